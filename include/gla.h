@@ -1,0 +1,146 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) gated linear attention library, libgla_amd.so.
+ *
+ * Operations (all per batch row b and head h, tokens t = 0..L-1):
+ *
+ *   GLA  (gated linear attention; GLA visual companion "Gated Linear Attention for Efficient
+ *         Long Sequences", cards "Core move" and "Step-by-step memory update"; MS-GLA summary,
+ *         section 2.1 "Linear Attention and Gated Linear Attention (GLA)"):
+ *         alpha_t = exp(g_t) per key channel (the forget gate scales the rows of the memory)
+ *         S_t = Diag(alpha_t) S_{t-1} + k_t^T v_t,   o_t = q_t S_t,   S_{-1} = h0 (or 0),
+ *         ht = S_{L-1}.  Computed chunkwise (same section: sequential inter-chunk updates,
+ *         parallel intra-chunk computation) with chunk size C; the result does not depend on C
+ *         beyond rounding.
+ *   GSA  (gated slot attention; "Gated Slot Attention for Efficient Linear-Time Sequence
+ *         Modeling": abstract, and research-map summary "Approach"): m slots with per-slot
+ *         forget gates alpha_t = exp(g_t), write weights w_t = 1 - alpha_t;
+ *         pass 1 (slot keys):   S1_t = S1_{t-1} Diag(alpha_t) + k_t^T w_t,  z_t = q_t S1_t
+ *         p_t = softmax(z_t) over the m slots
+ *         pass 2 (slot values): S2_t = Diag(alpha_t) S2_{t-1} + w_t^T v_t,  o_t = p_t S2_t
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are device pointers (HIP device memory of the current device), contiguous,
+ *     row-major, last dimension fastest.  Shapes are given next to each argument.
+ *   - dtype (gla_dtype) is the element type of q, k, v, g, o, do_, dq, dk, dv (all the same).
+ *     States (h0, ht, state, hk*, hv*, dh*) and gate gradients dg are always float32.
+ *     Internal accumulation is float32; bf16 operands feed bf16 matrix cores.
+ *   - Ownership: the caller owns every buffer.  The library never allocates device memory;
+ *     scratch space is the caller's `workspace` of at least the size the matching
+ *     *_workspace_bytes() query returns (its contents on entry do not matter).
+ *   - Synchrony: arguments are validated on the host before anything is enqueued.  On any
+ *     error the call returns a non-zero gla_status and enqueues nothing, so no output is
+ *     touched.  On success all work is enqueued on `stream` (a hipStream_t, NULL = the null
+ *     stream) and the call returns at once; outputs are valid once the stream is synchronised.
+ *   - Errors are reported only through the return value; the library never prints or aborts.
+ *     GLA_ERR_HIP means a launch failed (hipGetLastError); faults inside kernels surface at
+ *     the caller's next synchronisation.
+ *   - Outputs must not overlap inputs or each other (GLA_ERR_ALIAS), except `state` of
+ *     gla_decode_step, which is updated in place.
+ *   - Supported sizes: B, H >= 1; L >= 1 (any value; the last chunk may be partial);
+ *     C in {16, 32, 64, 128}; Dk and m multiples of 16 up to 256; Dv a multiple of 16 up to
+ *     512.  Other values return GLA_ERR_UNSUPPORTED (shape errors such as L < 1 return
+ *     GLA_ERR_SHAPE).
+ *   - Results are deterministic: no floating-point atomics are used, so two runs on the same
+ *     inputs give bitwise-identical outputs.
+ *   - The library is reentrant and keeps no mutable global state.
+ */
+#ifndef GLA_AMD_GLA_H
+#define GLA_AMD_GLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_NULL_ARG = 1,    /* a required pointer is NULL                               */
+  GLA_ERR_SHAPE = 2,       /* a size is < 1                                           */
+  GLA_ERR_DTYPE = 3,       /* dtype is not a gla_dtype value                          */
+  GLA_ERR_UNSUPPORTED = 4, /* C, Dk, Dv or m outside the supported set                */
+  GLA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the query returned       */
+  GLA_ERR_ALIAS = 6,       /* an output overlaps an input or another output           */
+  GLA_ERR_HIP = 7          /* a HIP launch failed                                     */
+} gla_status;
+
+typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+
+/* Version of this ABI (incremented on any incompatible change). */
+int gla_abi_version(void);
+
+/* Static, human-readable text for a status code (unknown codes give "unknown status"). */
+const char* gla_status_str(int status);
+
+/* ---------------------------------------------------------------- GLA forward ----------
+ * Bytes of workspace gla_fwd needs for these sizes (0 if the sizes are unsupported). */
+size_t gla_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype);
+
+/* Chunkwise GLA forward.
+ *   q, k, g : [B,H,L,Dk] dtype  (g = log of the forget gate, any real; normally <= 0)
+ *   v       : [B,H,L,Dv] dtype
+ *   h0      : [B,H,Dk,Dv] float32 initial state, or NULL for zeros
+ *   o       : [B,H,L,Dv] dtype   output
+ *   ht      : [B,H,Dk,Dv] float32 final state, or NULL to skip it */
+int gla_fwd(const void* q, const void* k, const void* v, const void* g, const float* h0,
+            void* o, float* ht,
+            int B, int H, int L, int Dk, int Dv, int C, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- GLA backward ---------
+ * Gradients of sum(o * do_) + sum(ht * dht).  gla_bwd recomputes what it needs from the
+ * forward inputs (no saved activations).
+ *   q, k, v, g, h0 : as in gla_fwd (h0 NULL = zeros)
+ *   do_  : [B,H,L,Dv] dtype   gradient of o
+ *   dht  : [B,H,Dk,Dv] float32 gradient of ht, or NULL for zero
+ *   dq, dk : [B,H,L,Dk] dtype;  dv : [B,H,L,Dv] dtype
+ *   dg   : [B,H,L,Dk] float32  gradient of the log gates
+ *   dh0  : [B,H,Dk,Dv] float32 gradient of h0, or NULL to skip it */
+size_t gla_bwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype);
+int gla_bwd(const void* q, const void* k, const void* v, const void* g, const float* h0,
+            const void* do_, const float* dht,
+            void* dq, void* dk, void* dv, float* dg, float* dh0,
+            int B, int H, int L, int Dk, int Dv, int C, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- GLA decode -----------
+ * One recurrent inference step per (batch, head): the O(1)-memory form of the recurrence
+ * (MS-GLA summary, section 1; GSA abstract: efficient recurrent inference).
+ *   q, k, g : [B,H,Dk] dtype;  v : [B,H,Dv] dtype
+ *   state   : [B,H,Dk,Dv] float32, read and overwritten with Diag(exp g) state + k^T v
+ *   o       : [B,H,Dv] dtype = q state (after the update)
+ * Needs no workspace.  Dk up to 256 and Dv up to 512, multiples of 16. */
+int gla_decode_step(const void* q, const void* k, const void* v, const void* g,
+                    float* state, void* o,
+                    int B, int H, int Dk, int Dv, int dtype, void* stream);
+
+/* ---------------------------------------------------------------- GSA forward ----------
+ *   q, k : [B,H,L,Dk] dtype;  v : [B,H,L,Dv] dtype;  g : [B,H,L,m] dtype slot log-gates
+ *   hk0  : [B,H,Dk,m] float32 initial pass-1 state or NULL;  hv0 : [B,H,m,Dv] or NULL
+ *   o    : [B,H,L,Dv] dtype
+ *   hkt, hvt : final states (same shapes as hk0, hv0) or NULL to skip */
+size_t gsa_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype);
+int gsa_fwd(const void* q, const void* k, const void* v, const void* g,
+            const float* hk0, const float* hv0,
+            void* o, float* hkt, float* hvt,
+            int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- GSA backward ---------
+ * Gradients of sum(o * do_) + sum(hkt * dhkt) + sum(hvt * dhvt).
+ *   do_ : [B,H,L,Dv] dtype;  dhkt [B,H,Dk,m], dhvt [B,H,m,Dv] float32 or NULL (= zero)
+ *   dq, dk : [B,H,L,Dk] dtype;  dv : [B,H,L,Dv] dtype;  dg : [B,H,L,m] float32
+ *   dhk0, dhv0 : gradients of hk0, hv0 (float32) or NULL to skip */
+size_t gsa_bwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype);
+int gsa_bwd(const void* q, const void* k, const void* v, const void* g,
+            const float* hk0, const float* hv0,
+            const void* do_, const float* dhkt, const float* dhvt,
+            void* dq, void* dk, void* dv, float* dg, float* dhk0, float* dhv0,
+            int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_AMD_GLA_H */

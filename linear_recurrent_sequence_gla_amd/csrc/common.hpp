@@ -1,0 +1,127 @@
+// common.hpp -- gfx950 building blocks shared by the GLA / GSA kernels.
+//
+// Matrix-core tile convention used everywhere (one wave = 64 lanes, lane = 16*grp + col):
+//   D[16x16] += X[16 x 32] * Y[32 x 16]^T-style contraction, written as
+//   D[m][n] += sum_k X[m][k] * Y[n][k]
+//   X fragment: lane holds X[m = col][k in kset(grp)], 8 values
+//   Y fragment: lane holds Y[n = col][k in kset(grp)], 8 values
+//   D accumulator (f32x4): lane holds D[m = 4*grp + e][n = col], e = 0..3
+// kset(grp) is any fixed set of 8 k-indices per lane group, as long as X and Y use the same
+// sets; the plain choice is {8*grp .. 8*grp+7}.  The "split" choice
+// {4*grp + 0..3} U {16 + 4*grp + 0..3} lets two stacked accumulator blocks be fed back as a Y
+// fragment without moving data between lanes.
+//
+// bf16: one v_mfma_f32_16x16x32_bf16 per fragment pair.
+// fp32: eight v_mfma_f32_16x16x4_f32, the e-th taking element e of each fragment (in that
+//       instruction lane group grp contributes k-index kset(grp)[e]).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x8 v; };
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], acc, 0, 0, 0);
+}
+
+// 8 consecutive elements p[0..7] (p 16-byte aligned).
+__device__ __forceinline__ Frag<bf16> ld8(const bf16* p) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+__device__ __forceinline__ Frag<float> ld8(const float* p) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  Frag<float> f;
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+// split set: p[0..3] and p[16..19] (p 8-byte aligned for bf16, 16-byte for fp32).
+__device__ __forceinline__ Frag<bf16> ld8_split(const bf16* p) {
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+  Frag<bf16> f;
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+__device__ __forceinline__ Frag<float> ld8_split(const float* p) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 16);
+  Frag<float> f;
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+// 8 elements down a column: p[0], p[ld], ..., p[7*ld].
+template <typename T>
+__device__ __forceinline__ Frag<T> ld8_col(const T* p, int ld) {
+  Frag<T> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = p[e * ld];
+  return f;
+}
+// Split-set fragment taken from two stacked accumulator blocks (rows 4*grp+e of block a and
+// of block b): the Y operand of a contraction over the accumulator's row index.
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_from_acc(const f32x4& a, const f32x4& b) {
+  Frag<T> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = from_f32<T>(a[e]);
+    f.v[4 + e] = from_f32<T>(b[e]);
+  }
+  return f;
+}
+
+// 16-byte vector of T for coalesced copies.
+template <typename T> struct V16;
+template <> struct V16<bf16> { static constexpr int N = 8; typedef bf16x8 type; };
+template <> struct V16<float> { static constexpr int N = 4; typedef f32x4 type; };
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Block-wide max of a non-negative value (256 threads); `red` holds >= 8 floats of LDS.
+__device__ __forceinline__ float block_max256(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return r;
+}
+
+// Map a flat block index so that consecutive "logical" indices land on the same XCD
+// (blocks are dispatched round-robin over the 8 XCDs; each XCD has its own L2).
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  if (nblocks % 8 != 0) return bid;
+  const int per = nblocks / 8;
+  return (bid % 8) * per + bid / 8;
+}
+
+}  // namespace gla

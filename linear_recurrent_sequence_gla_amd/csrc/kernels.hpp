@@ -1,0 +1,62 @@
+// kernels.hpp -- launch interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace gla {
+
+// Per-chunk operands written by the chunk-preparation kernel, all chunk-padded so that the
+// consumers need no bounds checks: CP = padded chunk rows, DKP = padded key width.
+struct ChunkOps {
+  void* Qs;     // [BH][N][CP][DKP]  q * 2^{b}            (T)
+  void* QsT;    // [BH][N][DKP][CP]  same, transposed      (T) or nullptr
+  void* KdT;    // [BH][N][DKP][CP]  (k * 2^{Gamma - b})^T (T)
+  void* A;      // [BH][N][CP][CP]   masked intra-chunk scores (T)
+  float* Gam;   // [BH][N][DKP]      chunk log2-decay Gamma (f32)
+};
+
+struct FwdParams {
+  const void *q, *k, *v, *g;
+  const float* h0;
+  void* o;
+  float* ht;
+  int BH, L, Dk, Dv, C, N;
+  ChunkOps ops;
+};
+
+struct BwdParams {
+  const void *q, *k, *v, *g, *do_;
+  const float *h0, *dht;
+  void *dq, *dk, *dv;
+  float *dg, *dh0;
+  int BH, L, Dk, Dv, C, N;
+  ChunkOps ops;
+  void* Hs;       // [BH][N][DKP][DvP] state at chunk starts (T)
+  void* dHs;      // [BH][N][DKP][DvP] state gradient at chunk ends (T)
+  float* carry;   // [BH][N][NT][DKP]  partial sum_j dH*H at chunk ends, per Dv tile
+};
+
+struct DecodeParams {
+  const void *q, *k, *v, *g;
+  float* state;
+  void* o;
+  int BH, Dk, Dv;
+};
+
+// Padded sizes shared by host and kernels.
+constexpr int kDvTile = 64;                       // Dv columns per walk workgroup
+inline int pad_dk(int Dk) { return Dk <= 32 ? 32 : Dk <= 64 ? 64 : Dk <= 128 ? 128 : 256; }
+inline int pad_c(int C) { return C <= 32 ? 32 : C; }
+inline int pad_dv(int Dv) { return (Dv + kDvTile - 1) / kDvTile * kDvTile; }
+
+template <typename T, int DKP, int CP>
+hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s);
+template <typename T, int DKP, int CP>
+hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s);
+template <typename T>
+hipError_t launch_gla_decode(const DecodeParams& p, hipStream_t s);
+
+// LDS bytes the preparation kernel needs (0 = does not fit the 160 KB of a CU).
+size_t prep_lds_bytes(int esize, int DKP, int CP);
+
+}  // namespace gla

@@ -1,0 +1,192 @@
+"""GPU parity of the GLA forward and decode (through the C ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import gla_decode_step as ref_decode
+from oracle import gla_recurrent_fwd
+from tests.helpers import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gla():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_recurrent_sequence_gla_amd as m
+    m.lib()
+    return m
+
+
+def run_fwd(gla, x, C, dtype, want_ht=True):
+    o, ht = gla.gla_fwd(dev(x["q"], dtype), dev(x["k"], dtype), dev(x["v"], dtype), dev(x["g"], dtype),
+                        C=C, h0=dev(x["h0"]), output_final_state=want_ht)
+    return host(o), (host(ht) if ht is not None else None)
+
+
+def check_fwd(gla, w, x, units=None):
+    o, ht = run_fwd(gla, x, w.C, w.dtype)
+    sel = (slice(None), slice(None)) if units is None else units
+    h0 = None if x["h0"] is None else x["h0"][sel]
+    ro, rh = gla_recurrent_fwd(x["q"][sel], x["k"][sel], x["v"][sel], x["g"][sel], h0)
+    print(f"[{w.name}] B={w.B} H={w.H} L={x['q'].shape[2]} Dk={w.Dk} Dv={w.Dv} C={w.C} {w.dtype}", flush=True)
+    assert_close("o", o[sel], ro, w.dtype)
+    assert_close("ht", ht[sel], rh, w.dtype)
+
+
+def test_tiny_fp32_config(gla):
+    """The tiny fp32 workload: B=1, H=1, L=64, Dk=Dv=16, C=16, zero initial state."""
+    w = W.WORKLOADS["tiny_f32"]
+    check_fwd(gla, w, W.gla_inputs(w, with_grad=False))
+
+
+SHAPES = [
+    # (B, H, L, Dk, Dv, C, dtype, h0)
+    (2, 2, 150, 64, 64, 64, "bf16", True),
+    (1, 3, 200, 128, 256, 64, "bf16", False),
+    (2, 1, 77, 16, 48, 16, "bf16", True),
+    (1, 2, 130, 32, 80, 32, "bf16", True),
+    (1, 2, 300, 128, 128, 128, "bf16", True),
+    (1, 1, 129, 256, 512, 64, "bf16", True),
+    (1, 1, 100, 256, 64, 32, "bf16", False),
+    (1, 2, 1, 128, 64, 64, "bf16", True),       # single token
+    (1, 2, 64, 128, 64, 64, "bf16", True),      # exactly one chunk
+    (2, 2, 90, 48, 32, 16, "f32", True),
+    (1, 2, 70, 128, 96, 64, "f32", True),
+    (1, 1, 140, 64, 64, 128, "f32", False),
+    (1, 1, 66, 256, 32, 32, "f32", True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes(gla, shape):
+    B, H, L, Dk, Dv, C, dt, h0 = shape
+    w = W.GlaWorkload("sweep", B, H, L, Dk, Dv, C, dt, 77 + L + Dk, h0=h0, gate_law="iid")
+    check_fwd(gla, w, W.gla_inputs(w, with_grad=False))
+
+
+@pytest.mark.parametrize("C", [16, 32, 64, 128])
+def test_chunk_size_independence(gla, C):
+    """Same inputs, every chunk size: each result matches the oracle (and so each other)."""
+    w = W.GlaWorkload("chunks", 1, 2, 333, 128, 64, C, "bf16", 5, h0=True)
+    check_fwd(gla, w, W.gla_inputs(w, with_grad=False))
+
+
+@pytest.mark.parametrize("gval", [0.0, -30.0, -3.0])
+def test_extreme_gates(gla, gval):
+    """g = 0 (ungated), g = -30 (memoryless; exercises the sub-chunked safe path), g = -3."""
+    w = W.GlaWorkload("gates", 1, 2, 150, 64, 64, 64, "bf16", 9, h0=True)
+    x = W.gla_inputs(w, with_grad=False)
+    x["g"] = np.full_like(x["g"], gval)
+    check_fwd(gla, w, x)
+
+
+def test_mixed_safe_and_fast_chunks(gla):
+    """Some chunks far beyond the span limit, others not, in one call."""
+    w = W.GlaWorkload("mixed", 1, 2, 256, 64, 64, 64, "bf16", 10, h0=True)
+    x = W.gla_inputs(w, with_grad=False)
+    x["g"][:, :, 64:128] = -2.0
+    x["g"][:, 1, 200:210, :7] = -40.0
+    check_fwd(gla, w, x)
+
+
+def test_large_negative_gate_is_finite(gla):
+    w = W.GlaWorkload("neg", 1, 1, 100, 32, 32, 32, "bf16", 11, h0=True)
+    x = W.gla_inputs(w, with_grad=False)
+    x["g"][:] = -1e4
+    check_fwd(gla, w, x)
+
+
+@pytest.mark.parametrize("name,units", [
+    ("gla_340m", (np.array([0, 7]), np.array([0, 3]))),
+    ("gla_1p3b", (np.array([2]), np.array([1]))),
+    ("gla_long", (np.array([0]), np.array([2]))),
+])
+def test_full_size_configs_sampled(gla, name, units):
+    """Full-size workloads, launched exactly as the benchmark does; the oracle checks sampled
+    (batch, head) units (units are independent, so this is exact for those outputs)."""
+    w = W.WORKLOADS[name]
+    x = W.gla_inputs(w, with_grad=False)
+    b, h = units
+    check_fwd(gla, w, x, units=(b[:, None], h[None, :]))
+
+
+def test_deterministic(gla):
+    import torch
+    w = W.GlaWorkload("det", 2, 2, 500, 128, 256, 64, "bf16", 12, h0=True)
+    x = W.gla_inputs(w, with_grad=False)
+    args = [dev(x[n], "bf16") for n in ("q", "k", "v", "g")]
+    o1, h1 = gla.gla_fwd(*args, C=64, h0=dev(x["h0"]))
+    o2, h2 = gla.gla_fwd(*args, C=64, h0=dev(x["h0"]))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_state_chaining(gla):
+    """fwd over [0, L) equals fwd over [0, L1) then [L1, L) from the carried state, L1 unaligned."""
+    w = W.GlaWorkload("chain", 1, 2, 300, 64, 64, 64, "bf16", 13, h0=True)
+    x = W.gla_inputs(w, with_grad=False)
+    L1 = 101
+    full_o, full_h = run_fwd(gla, x, 64, "bf16")
+    a = {n: (x[n][:, :, :L1] if n in "qkvg" else x[n]) for n in ("q", "k", "v", "g", "h0")}
+    o1, h1 = run_fwd(gla, a, 64, "bf16")
+    b = {n: x[n][:, :, L1:] for n in ("q", "k", "v", "g")}
+    b["h0"] = h1.astype(np.float32)
+    o2, h2 = run_fwd(gla, b, 64, "bf16")
+    ro, rh = gla_recurrent_fwd(x["q"], x["k"], x["v"], x["g"], x["h0"])
+    assert_close("o chained", np.concatenate([o1, o2], axis=2), ro, "bf16")
+    assert_close("ht chained", h2, rh, "bf16")
+
+
+def test_decode_matches_oracle_and_forward(gla):
+    """Decode steps: each step's output and the final state match the oracle's steps, and the
+    T-step result equals the forward over the same T tokens."""
+    import torch
+    w = W.WORKLOADS["decode"]
+    T = 40
+    d = W.decode_inputs(w, T=T, B=8)
+    state = dev(d["state"])
+    S = d["state"].astype(np.float64)
+    outs = []
+    for t in range(T):
+        o = gla.gla_decode_step(dev(d["q"][t], "bf16"), dev(d["k"][t], "bf16"), dev(d["v"][t], "bf16"),
+                                dev(d["g"][t], "bf16"), state)
+        ro, S = ref_decode(d["q"][t], d["k"][t], d["v"][t], d["g"][t], S)
+        outs.append(host(o))
+        assert_close(f"o[{t}]", host(o), ro, "bf16")
+    assert_close("state", host(state), S, "bf16")
+    # decode == forward over the same tokens (the forward sees [B,H,T,D])
+    perm = lambda a: np.ascontiguousarray(np.transpose(a, (1, 2, 0, 3)))
+    fo, fh = gla.gla_fwd(dev(perm(d["q"]), "bf16"), dev(perm(d["k"]), "bf16"), dev(perm(d["v"]), "bf16"),
+                         dev(perm(d["g"]), "bf16"), C=16, h0=dev(d["state"]))
+    torch.cuda.synchronize()
+    assert_close("decode vs fwd o", np.stack(outs, axis=2), host(fo), "bf16")
+    assert_close("decode vs fwd state", host(state), host(fh), "bf16")
+
+
+def test_decode_full_size_sampled(gla):
+    """The decode workload's full batch (64 x 4, Dk=128, Dv=256), a few steps, all units."""
+    w = W.WORKLOADS["decode"]
+    d = W.decode_inputs(w, T=3)
+    state = dev(d["state"])
+    S = d["state"].astype(np.float64)
+    for t in range(3):
+        o = gla.gla_decode_step(dev(d["q"][t], "bf16"), dev(d["k"][t], "bf16"), dev(d["v"][t], "bf16"),
+                                dev(d["g"][t], "bf16"), state)
+        ro, S = ref_decode(d["q"][t], d["k"][t], d["v"][t], d["g"][t], S)
+        assert_close(f"o[{t}]", host(o), ro, "bf16")
+    assert_close("state", host(state), S, "bf16")
+
+
+def test_decode_fp32(gla):
+    w = W.DecodeWorkload("dec32", 5, 2, 3, 48, 32, "f32", 21)
+    d = W.decode_inputs(w)
+    state = dev(d["state"])
+    S = d["state"].astype(np.float64)
+    for t in range(w.T):
+        o = gla.gla_decode_step(dev(d["q"][t]), dev(d["k"][t]), dev(d["v"][t]), dev(d["g"][t]), state)
+        ro, S = ref_decode(d["q"][t], d["k"][t], d["v"][t], d["g"][t], S)
+        assert_close(f"o[{t}]", host(o), ro, "f32")
+    assert_close("state", host(state), S, "f32")
