@@ -38,8 +38,10 @@
  *     gla_decode_step, which is updated in place.
  *   - Supported sizes: B, H >= 1; L >= 1 (any value; the last chunk may be partial);
  *     C in {16, 32, 64, 128}; Dk and m multiples of 16 up to 256; Dv a multiple of 16 up to
- *     512.  Other values return GLA_ERR_UNSUPPORTED (shape errors such as L < 1 return
- *     GLA_ERR_SHAPE).
+ *     512; B*H <= 65535; every tensor 16-byte aligned.  Chunk tiles must fit a CU's LDS:
+ *     bf16 excludes Dk > 128 with C = 128; float32 (a parity dtype) excludes C = 128 and
+ *     Dk > 128 with C = 64.  Other values return GLA_ERR_UNSUPPORTED (shape errors such as
+ *     L < 1 return GLA_ERR_SHAPE).
  *   - Results are deterministic: no floating-point atomics are used, so two runs on the same
  *     inputs give bitwise-identical outputs.
  *   - The library is reentrant and keeps no mutable global state.

@@ -39,7 +39,7 @@ int check_dims(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
   if (Dk % 16 != 0 || Dk > 256 || Dv % 16 != 0 || Dv > 512) return GLA_ERR_UNSUPPORTED;
   const int DKP = pad_dk(Dk), CP = pad_c(C);
   if (DKP == 256 && CP == 128) return GLA_ERR_UNSUPPORTED;   // chunk tile exceeds LDS
-  if (prep_lds_bytes(esize_of(dtype), DKP, CP) == 0) return GLA_ERR_UNSUPPORTED;
+  if (!fwd_config_fits(esize_of(dtype), DKP, CP)) return GLA_ERR_UNSUPPORTED;
   // element counts must fit the kernels' 64-bit offsets and int row indices
   if ((int64_t)B * H > 65535) return GLA_ERR_UNSUPPORTED;   // grid y-dimension of the chunk kernels
   if ((int64_t)B * H > INT32_MAX / 2 || (int64_t)L * Dv > INT32_MAX / 2 || (int64_t)L * Dk > INT32_MAX / 2)
@@ -161,8 +161,9 @@ const char* gla_status_str(int s) {
     case GLA_ERR_DTYPE: return "GLA_ERR_DTYPE: dtype must be GLA_F32 (0) or GLA_BF16 (1)";
     case GLA_ERR_UNSUPPORTED:
       return "GLA_ERR_UNSUPPORTED: C must be 16/32/64/128, Dk and m multiples of 16 up to 256, "
-             "Dv a multiple of 16 up to 512, B*H <= 65535, 16-byte aligned tensors (Dk > 128 "
-             "with C = 128 is not supported)";
+             "Dv a multiple of 16 up to 512, B*H <= 65535, 16-byte aligned tensors; tiles that "
+             "exceed a CU's LDS are not supported (bf16: Dk > 128 with C = 128; fp32: C = 128, "
+             "or Dk > 128 with C = 64)";
     case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE: workspace NULL or smaller than the query returned";
     case GLA_ERR_ALIAS: return "GLA_ERR_ALIAS: an output overlaps an input, another output or the workspace";
     case GLA_ERR_HIP: return "GLA_ERR_HIP: a HIP kernel launch failed";
@@ -201,6 +202,7 @@ int gla_fwd(const void* q, const void* k, const void* v, const void* g, const fl
 
 size_t gla_bwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
   if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
+  if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return 0;
   return bwd_layout(B, H, L, Dk, Dv, C, dtype).total;
 }
 
@@ -210,6 +212,7 @@ int gla_bwd(const void* q, const void* k, const void* v, const void* g, const fl
             void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_dims(B, H, L, Dk, Dv, C, dtype);
   if (st != GLA_OK) return st;
+  if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return GLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !g || !do_ || !dq || !dk || !dv || !dg) return GLA_ERR_NULL_ARG;
   if (!all_aligned({q, k, v, g, h0, do_, dht, dq, dk, dv, dg, dh0, workspace})) return GLA_ERR_UNSUPPORTED;
   const BwdLayout lay = bwd_layout(B, H, L, Dk, Dv, C, dtype);

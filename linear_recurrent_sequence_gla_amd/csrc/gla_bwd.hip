@@ -1,8 +1,801 @@
-// gla_bwd.hip -- chunkwise GLA backward (work in progress).
+// gla_bwd.hip -- chunkwise GLA backward on gfx950.
+//
+// Gradients of sum(o * do) + sum(ht * dht), recomputing everything from the forward inputs.
+// With Qs = q 2^b, Ks = k 2^-b, Kd = k 2^{Gamma-b} (prep.hpp), H_n the state at the start of
+// chunk n and dH_{n+1} the gradient of the state at its end, per chunk:
+//   dA  = mask(dO V^T)
+//   dq  = 2^b     * (dA Ks + dO H_n^T)
+//   dk  = 2^-b    * (dA^T Qs) + 2^{Gamma-b} * (V dH_{n+1}^T)
+//   dv  = A^T dO + Kd dH_{n+1}
+//   dH_n = Diag(2^{Gamma_n}) dH_{n+1} + Qs_n^T dO_n,   dH_N = dht,  dh0 = dH_0
+// The gate gradient.  q_t only appears as q_t 2^{G_t} and k_t only as k_t 2^{-G_t} (G the
+// prefix sum of g), so dg_t = sum_{s >= t} (q_s dq_s - k_s dk_s) (+ rowsum(dht * ht)).  Taken
+// literally that sum cancels: its diagonal intra-chunk terms (q_s dA_ss k_s - k_s dA_ss q_s)
+// and the state-update terms cancel exactly in exact arithmetic, and when the true dg is
+// small (strong forgetting, a tiny initial state) the rounding left over from those
+// cancelling O(1) terms would dominate.  The kernels therefore evaluate the same quantity
+// with every exactly-cancelling pair removed.  For t in chunk n:
+//   dg_t = sum_{s >= t, s in n} (q_s dq^nd_s - k_s dk'_s)  +  sum_{c < t, c in n} k_c B_c  +  Z_n
+// where dq^nd = dq minus its diagonal term (dA_ss k_s), dk' = the strictly-upper intra part
+// of dk, B_c = 2^{Gamma - b_c} (V dH_{n+1}^T)_c (the inter part of dk), and
+// Z_n = 2^{Gamma_n} rowsum(dH_{n+1} * H_n) is the gradient through the chunk's state decay
+// (everything beyond the chunk is folded into dH_{n+1}).  Every surviving term carries the
+// decay factors that contain alpha_t, so its rounding scales with dg itself.  The reverse
+// state walk emits Z_n per chunk; the chunk kernel does the two in-chunk prefix sums.
+//
+// Launches:
+//   1. gla_prep_kernel (also writes QsT)                      grid N x BH
+//   2. gla_bwd_walk: forward walk storing H_n, then reverse walk storing dH_{n+1} and Z_n,
+//      state slice in fp32 MFMA accumulators                    grid ceil(Dv/64) * BH
+//   3. gla_bwd_chunk: dA, dq, dk (+ dv when the whole key width fits one workgroup) on MFMA
+//      over 64-column slices of Dv, then an element-wise epilogue (gate scaling, diagonal
+//      terms, the two in-chunk prefix sums of dg, Z_n) with 16-byte stores
+//                                                              grid N x BH x (Dk slices)
+//   4. gla_bwd_dv (only when dv did not fit step 3)           grid N x BH x ceil(Dv/64)
+// Intra-chunk terms use the factorised form only on chunks whose gate span passes the same
+// check as the forward; other chunks form them exactly, element by element, in fp32.
 #include "prep.hpp"
+
 namespace gla {
+
+// ======================================================================= state walk
 template <typename T, int DKP, int CP>
-hipError_t launch_gla_bwd(const BwdParams&, hipStream_t) { return hipErrorNotSupported; }
+struct BwdWalkCfg {
+  static constexpr int V = 16 / (int)sizeof(T);
+  static constexpr int LDA = CP + V, LDV = kDvTile + V;
+  static constexpr size_t KT = (size_t)DKP * LDA * sizeof(T);   // KdT (forward) / QsT (reverse)
+  static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);    // V (forward) / dO (reverse)
+  static constexpr size_t HT = (size_t)DKP * LDV * sizeof(T);   // state tile (out / in)
+  static constexpr size_t BYTES = KT + VT + 2 * HT + (size_t)DKP * 4 + (size_t)4 * DKP * 4;
+  static constexpr int NK = DKP * CP / V, NV = CP * kDvTile / V, NH = DKP * kDvTile / V;
+  static constexpr int PKd = (NK + 255) / 256, PV = (NV + 255) / 256, PH = (NH + 255) / 256;
+};
+
+template <typename T, int DKP, int CP>
+struct BwdWalkStage {
+  using W = BwdWalkCfg<T, DKP, CP>;
+  typedef typename V16<T>::type VT;
+  VT kt[W::PKd], v[W::PV], h[W::PH];
+  f32x4 gam;
+
+  // mat: dense [DKP][CP] chunk matrix; src: [L][Dv] rows of this (b,h); htile: [DKP][DVP]
+  // state tile already offset to this workgroup's columns, or nullptr.
+  __device__ __forceinline__ void load(const T* mat, const T* src, int row0, int len, int Dv, int tile,
+                                       const float* gam_chunk, const T* htile, int DVP) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < W::PKd; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < W::NK) kt[m] = *reinterpret_cast<const VT*>(mat + (size_t)idx * W::V);
+    }
+    constexpr int PER_ROW = kDvTile / W::V;
+#pragma unroll
+    for (int m = 0; m < W::PV; ++m) {
+      const int idx = tid + 256 * m;
+      const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
+      const int j = tile * kDvTile + c;
+      v[m] = (idx < W::NV && r < len && j < Dv) ? *reinterpret_cast<const VT*>(src + (size_t)(row0 + r) * Dv + j)
+                                                : zero_vec<T>();
+    }
+    if (htile) {
+#pragma unroll
+      for (int m = 0; m < W::PH; ++m) {
+        const int idx = tid + 256 * m;
+        const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
+        if (idx < W::NH) h[m] = *reinterpret_cast<const VT*>(htile + (size_t)r * DVP + c);
+      }
+    }
+    if (tid < DKP / 4) gam = *reinterpret_cast<const f32x4*>(gam_chunk + 4 * tid);
+  }
+
+  __device__ __forceinline__ void store(T* sKT, T* sV, T* sHi, float* sG, bool with_h) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < W::PKd; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < W::NK) {
+        const int r = idx / (CP / W::V), c = (idx - r * (CP / W::V)) * W::V;
+        *reinterpret_cast<VT*>(sKT + r * W::LDA + c) = kt[m];
+      }
+    }
+    constexpr int PER_ROW = kDvTile / W::V;
+#pragma unroll
+    for (int m = 0; m < W::PV; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < W::NV) {
+        const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
+        *reinterpret_cast<VT*>(sV + r * W::LDV + c) = v[m];
+      }
+    }
+    if (with_h) {
+#pragma unroll
+      for (int m = 0; m < W::PH; ++m) {
+        const int idx = tid + 256 * m;
+        if (idx < W::NH) {
+          const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
+          *reinterpret_cast<VT*>(sHi + r * W::LDV + c) = h[m];
+        }
+      }
+    }
+    if (tid < DKP / 4) *reinterpret_cast<f32x4*>(sG + 4 * tid) = gam;
+  }
+};
+
+// Copy an LDS [DKP][64] tile to the state workspace (row stride DVP, already offset).
+template <typename T, int DKP>
+__device__ __forceinline__ void state_tile_out(T* dst, const T* src, int lds, int DVP) {
+  constexpr int V = V16<T>::N;
+  typedef typename V16<T>::type VT;
+  constexpr int PER_ROW = kDvTile / V;
+  for (int idx = threadIdx.x; idx < DKP * PER_ROW; idx += 256) {
+    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+    *reinterpret_cast<VT*>(dst + (size_t)r * DVP + c) = *reinterpret_cast<const VT*>(src + r * lds + c);
+  }
+}
+
+template <typename T, int DKP, int CP>
+__global__ __launch_bounds__(256) void gla_bwd_walk(BwdParams p, int ntile) {
+  using W = BwdWalkCfg<T, DKP, CP>;
+  constexpr int LDA = W::LDA, LDV = W::LDV;
+  constexpr int NCB = CP / 32, NIB = DKP / 16;
+  __shared__ __attribute__((aligned(16))) char smem[W::BYTES];
+  T* sKT = reinterpret_cast<T*>(smem);
+  T* sV = reinterpret_cast<T*>(smem + W::KT);
+  T* sHo = reinterpret_cast<T*>(smem + W::KT + W::VT);
+  T* sHi = reinterpret_cast<T*>(smem + W::KT + W::VT + W::HT);
+  float* sG = reinterpret_cast<float*>(smem + W::KT + W::VT + 2 * W::HT);
+  float* sRed = sG + DKP;
+
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = lin % ntile, bh = lin / ntile;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int Dv = p.Dv, Dk = p.Dk, L = p.L, C = p.C, N = p.N;
+  const int DVP = ntile * kDvTile;
+  const int j = tile * kDvTile + 16 * wave + col;
+  const bool jv = j < Dv;
+  const T* vg = reinterpret_cast<const T*>(p.v) + (size_t)bh * L * Dv;
+  const T* dog = reinterpret_cast<const T*>(p.do_) + (size_t)bh * L * Dv;
+  T* Hs = reinterpret_cast<T*>(p.Hs) + (size_t)bh * N * DKP * DVP + tile * kDvTile;
+  T* dHs = reinterpret_cast<T*>(p.dHs) + (size_t)bh * N * DKP * DVP + tile * kDvTile;
+  const T* KdT = reinterpret_cast<const T*>(p.ops.KdT) + (size_t)bh * N * DKP * CP;
+  const T* QsT = reinterpret_cast<const T*>(p.ops.QsT) + (size_t)bh * N * DKP * CP;
+  const float* Gam = p.ops.Gam + (size_t)bh * N * DKP;
+
+  f32x4 H[NIB];
+#pragma unroll
+  for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * ib + 4 * grp + e;
+      H[ib][e] = (p.h0 && jv && i < Dk) ? p.h0[((size_t)bh * Dk + i) * Dv + j] : 0.f;
+    }
+  }
+
+  // ---- forward: store H_n (n = 0..N-1), end with H = H_N = ht
+  BwdWalkStage<T, DKP, CP> st;
+  st.load(KdT, vg, 0, min(C, L), Dv, tile, Gam, nullptr, DVP);
+  st.store(sKT, sV, sHi, sG, false);
+  __syncthreads();
+  for (int n = 0; n < N; ++n) {
+    if (n + 1 < N) {
+      const int r1 = (n + 1) * C;
+      st.load(KdT + (size_t)(n + 1) * DKP * CP, vg, r1, min(C, L - r1), Dv, tile, Gam + (size_t)(n + 1) * DKP,
+              nullptr, DVP);
+    }
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sHo[(16 * ib + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(H[ib][e]);
+    }
+    Frag<T> Yv[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_col(sV + (32 * cb + 8 * grp) * LDV + 16 * wave + col, LDV);
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) H[ib][e] *= fast_exp2(sG[16 * ib + 4 * grp + e]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+      for (int ib = 0; ib < NIB; ++ib) mma(H[ib], ld8(sKT + (16 * ib + col) * LDA + 32 * cb + 8 * grp), Yv[cb]);
+    }
+    __syncthreads();
+    state_tile_out<T, DKP>(Hs + (size_t)n * DKP * DVP, sHo, LDV, DVP);
+    if (n + 1 < N) st.store(sKT, sV, sHi, sG, false);
+    __syncthreads();
+  }
+  __threadfence();     // the H_n tiles are read back below by this workgroup
+  __syncthreads();
+
+  // ---- reverse: for n = N-1..0 emit dH_{n+1} and Z_n = 2^{Gamma_n} rowsum(dH_{n+1} * H_n),
+  //      then dH_n = Diag(2^{Gamma_n}) dH_{n+1} + QsT_n dO_n
+  f32x4 dH[NIB];
+#pragma unroll
+  for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * ib + 4 * grp + e;
+      dH[ib][e] = (p.dht && jv && i < Dk) ? p.dht[((size_t)bh * Dk + i) * Dv + j] : 0.f;
+    }
+  }
+  {
+    const int r1 = (N - 1) * C;
+    st.load(QsT + (size_t)(N - 1) * DKP * CP, dog, r1, L - r1, Dv, tile, Gam + (size_t)(N - 1) * DKP,
+            Hs + (size_t)(N - 1) * DKP * DVP, DVP);
+    st.store(sKT, sV, sHi, sG, true);
+  }
+  __syncthreads();
+  for (int n = N - 1; n >= 0; --n) {
+    if (n > 0) {
+      const int r1 = (n - 1) * C;
+      st.load(QsT + (size_t)(n - 1) * DKP * CP, dog, r1, C, Dv, tile, Gam + (size_t)(n - 1) * DKP,
+              Hs + (size_t)(n - 1) * DKP * DVP, DVP);
+    }
+    // Z partial over this lane's column, then over the 16 columns of the wave
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * ib + 4 * grp + e;
+        float x = dH[ib][e] * to_f32(sHi[i * LDV + 16 * wave + col]);
+        x += __shfl_xor(x, 1, 64);
+        x += __shfl_xor(x, 2, 64);
+        x += __shfl_xor(x, 4, 64);
+        x += __shfl_xor(x, 8, 64);
+        if (col == 0) sRed[wave * DKP + i] = x * fast_exp2(sG[i]);
+        sHo[i * LDV + 16 * wave + col] = from_f32<T>(dH[ib][e]);
+      }
+    }
+    Frag<T> Yd[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) Yd[cb] = ld8_col(sV + (32 * cb + 8 * grp) * LDV + 16 * wave + col, LDV);
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dH[ib][e] *= fast_exp2(sG[16 * ib + 4 * grp + e]);
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+      for (int ib = 0; ib < NIB; ++ib) mma(dH[ib], ld8(sKT + (16 * ib + col) * LDA + 32 * cb + 8 * grp), Yd[cb]);
+    }
+    __syncthreads();
+    for (int i = tid; i < DKP; i += 256)
+      p.carry[(((size_t)bh * N + n) * ntile + tile) * DKP + i] =
+          sRed[i] + sRed[DKP + i] + sRed[2 * DKP + i] + sRed[3 * DKP + i];
+    state_tile_out<T, DKP>(dHs + (size_t)n * DKP * DVP, sHo, LDV, DVP);
+    if (n > 0) st.store(sKT, sV, sHi, sG, true);
+    __syncthreads();
+  }
+  if (p.dh0 && jv) {
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * ib + 4 * grp + e;
+        if (i < Dk) p.dh0[((size_t)bh * Dk + i) * Dv + j] = dH[ib][e];
+      }
+    }
+  }
+}
+
+// ======================================================================= chunk gradients
+// LDS phases of the chunk kernel:
+//   front   sdA [CP][CP] (written after the Dv loop, read to the end), diagonal of dA (fp32)
+//   phase 1 (Dv loop)    sQs, sKs (+ sKd, sA with dv) and the double Dv slice tiles
+//   phase 3 (epilogue)   three fp32 [CP][DKS] gradient tiles and, on the exact path, b
+constexpr size_t chunk_bwd_bytes(int es, int DKS, int CP, bool dv, int nseg) {
+  const size_t V = 16 / es;
+  const size_t LDQ = DKS + V, LDC = CP + V, LDV = kDvTile + V, LDF = DKS + 4;
+  const size_t QT = CP * LDQ * es, CT = CP * LDC * es, VT = CP * LDV * es, HT = DKS * LDV * es;
+  const size_t FT = CP * LDF * 4;
+  const size_t ph1 = 2 * QT + (dv ? QT + CT : 0) + 2 * VT + 2 * HT + (dv ? VT : 0);
+  const size_t ph3 = 3 * FT + (size_t)CP * DKS * 4;
+  return CT + (ph1 > ph3 ? ph1 : ph3) + (size_t)(2 * nseg * DKS + 2 * DKS + CP + 8) * 4;
+}
+
+template <typename T, int DKS, int CP, bool WITH_DV>
+struct BwdChunkCfg {
+  using M = ChunkMap<T, DKS, CP>;
+  static constexpr int V = 16 / (int)sizeof(T);
+  static constexpr int LDQ = DKS + V, LDC = CP + V, LDV = kDvTile + V, LDF = DKS + 4;
+  static constexpr size_t QT = (size_t)CP * LDQ * sizeof(T);
+  static constexpr size_t CT = (size_t)CP * LDC * sizeof(T);
+  static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
+  static constexpr size_t HT = (size_t)DKS * LDV * sizeof(T);
+  static constexpr size_t FT = (size_t)CP * LDF * 4;
+  static constexpr size_t PH1 = 2 * QT + (WITH_DV ? QT + CT : 0) + 2 * VT + 2 * HT + (WITH_DV ? VT : 0);
+  static constexpr size_t PH3 = 3 * FT + (size_t)CP * DKS * 4;
+  static constexpr size_t MAIN = CT + cmax(PH1, PH3);
+  static constexpr size_t BYTES = chunk_bwd_bytes(sizeof(T), DKS, CP, WITH_DV, M::NSEG);
+  static constexpr int NV = CP * kDvTile / V, NH = DKS * kDvTile / V;
+  static constexpr int PV = (NV + 255) / 256, PH = (NH + 255) / 256;
+};
+
+template <typename T, int DKS, int CP, bool WITH_DV>
+struct SliceStage {
+  using Cf = BwdChunkCfg<T, DKS, CP, WITH_DV>;
+  typedef typename V16<T>::type VT;
+  VT dov[Cf::PV], vv[Cf::PV], hv[Cf::PH], dhv[Cf::PH];
+
+  // dog/vg: rows of this chunk ([len][Dv]); hs/dhs: [DKS rows][DVP] state tiles of this chunk
+  __device__ __forceinline__ void load(const T* dog, const T* vg, const T* hs, const T* dhs, int len, int Dv,
+                                       int DVP, int js, int kvalid) {
+    const int tid = threadIdx.x;
+    constexpr int PER_ROW = kDvTile / Cf::V;
+#pragma unroll
+    for (int m = 0; m < Cf::PV; ++m) {
+      const int idx = tid + 256 * m;
+      const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
+      const int jj = js * kDvTile + c;
+      const bool ok = idx < Cf::NV && r < len && jj < Dv;
+      dov[m] = ok ? *reinterpret_cast<const VT*>(dog + (size_t)r * Dv + jj) : zero_vec<T>();
+      vv[m] = ok ? *reinterpret_cast<const VT*>(vg + (size_t)r * Dv + jj) : zero_vec<T>();
+    }
+#pragma unroll
+    for (int m = 0; m < Cf::PH; ++m) {
+      const int idx = tid + 256 * m;
+      const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
+      const bool ok = idx < Cf::NH && r < kvalid;
+      const size_t off = (size_t)r * DVP + js * kDvTile + c;
+      hv[m] = ok ? *reinterpret_cast<const VT*>(hs + off) : zero_vec<T>();
+      dhv[m] = ok ? *reinterpret_cast<const VT*>(dhs + off) : zero_vec<T>();
+    }
+  }
+  __device__ __forceinline__ void store(T* sdO, T* sV, T* sH, T* sdH) const {
+    const int tid = threadIdx.x;
+    constexpr int PER_ROW = kDvTile / Cf::V;
+#pragma unroll
+    for (int m = 0; m < Cf::PV; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < Cf::NV) {
+        const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
+        *reinterpret_cast<VT*>(sdO + r * Cf::LDV + c) = dov[m];
+        *reinterpret_cast<VT*>(sV + r * Cf::LDV + c) = vv[m];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < Cf::PH; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < Cf::NH) {
+        const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
+        *reinterpret_cast<VT*>(sH + r * Cf::LDV + c) = hv[m];
+        *reinterpret_cast<VT*>(sdH + r * Cf::LDV + c) = dhv[m];
+      }
+    }
+  }
+};
+
+template <typename T, int DKS, int CP, bool WITH_DV>
+__global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int ntile) {
+  using Cf = BwdChunkCfg<T, DKS, CP, WITH_DV>;
+  using M = ChunkMap<T, DKS, CP>;
+  constexpr int V = M::V, RPS = M::RPS, NSEG = M::NSEG;
+  constexpr int LDQ = Cf::LDQ, LDC = Cf::LDC, LDV = Cf::LDV, LDF = Cf::LDF;
+  constexpr int NBR = CP / 16, NIB = DKS / 16, NJB = kDvTile / 16;
+  constexpr int NA_BLK = NBR * NBR, NQ_BLK = NBR * NIB, NV_BLK = NBR * NJB;
+  constexpr int PA = (NA_BLK + 3) / 4, PQ = (NQ_BLK + 3) / 4, PVb = (NV_BLK + 3) / 4;
+  typedef typename V16<T>::type VT;
+  __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
+  T* sdA = reinterpret_cast<T*>(smem);                            // strictly lower dA
+  char* rmain = smem + Cf::CT;
+  // phase 1
+  T* sQs = reinterpret_cast<T*>(rmain);
+  T* sKs = sQs + CP * LDQ;
+  T* sKd = sKs + CP * LDQ;                                        // WITH_DV only
+  T* sA = sKd + (WITH_DV ? CP * LDQ : 0);                         // WITH_DV only
+  T* sdO = sA + (WITH_DV ? CP * LDC : 0);
+  T* sV = sdO + CP * LDV;
+  T* sH = sV + CP * LDV;
+  T* sdH = sH + DKS * LDV;
+  T* sdV = sdH + DKS * LDV;                                       // WITH_DV only
+  // phase 3 (aliases phase 1)
+  float* sDQ = reinterpret_cast<float*>(rmain);                   // dq^nd / 2^b
+  float* sDK = sDQ + CP * LDF;                                    // dk'  / 2^-b (fast path)
+  float* sDKI = sDK + CP * LDF;                                   // V dH^T
+  float* sB = sDKI + CP * LDF;                                    // b (exact path)
+  float* segtot = reinterpret_cast<float*>(smem + Cf::MAIN);      // [2][NSEG][DKS]
+  float* sGam = segtot + 2 * NSEG * DKS;
+  float* sZ = sGam + DKS;
+  float* sDiag = sZ + DKS;
+  float* red = sDiag + CP;
+
+  const int n = blockIdx.x, bh = blockIdx.y, ch0 = blockIdx.z * DKS;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int Dk = p.Dk, Dv = p.Dv, L = p.L, N = p.N;
+  const int DVP = ntile * kDvTile;
+  const int row0 = n * p.C;
+  const int len = min(p.C, L - row0);
+  const int kvalid = min(DKS, Dk - ch0);
+  const size_t chunk = (size_t)bh * N + n;
+  const size_t qbase = ((size_t)bh * L + row0) * Dk + ch0;
+  const T* qg = reinterpret_cast<const T*>(p.q) + qbase;
+  const T* kg = reinterpret_cast<const T*>(p.k) + qbase;
+  const T* dog = reinterpret_cast<const T*>(p.do_) + ((size_t)bh * L + row0) * Dv;
+  const T* vg = reinterpret_cast<const T*>(p.v) + ((size_t)bh * L + row0) * Dv;
+  const T* hs = reinterpret_cast<const T*>(p.Hs) + (chunk * DKP + ch0) * DVP;
+  const T* dhs = reinterpret_cast<const T*>(p.dHs) + (chunk * DKP + ch0) * DVP;
+
+  // Z_n = sum over Dv tiles of 2^Gamma rowsum(dH_{n+1} * H_n)
+  for (int i = tid; i < DKS; i += 256) {
+    float z = 0.f;
+    for (int t = 0; t < ntile; ++t) z += p.carry[(chunk * ntile + t) * DKP + ch0 + i];
+    sZ[i] = z;
+  }
+  ChunkScan<T, DKS, CP> cs;
+  const float maxb = cs.run(qg, kg, reinterpret_cast<const T*>(p.g) + qbase, Dk, Dk - ch0, len, segtot, sGam, red);
+  const bool fast = maxb <= kSpanLimit;
+  const int c0 = cs.cg * V, r0 = cs.seg * RPS;
+
+  SliceStage<T, DKS, CP, WITH_DV> st;
+  st.load(dog, vg, hs, dhs, len, Dv, DVP, 0, kvalid);
+
+  if (cs.active) {
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const int r = r0 + u;
+      VT qh, kh, kd;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        qh[e] = from_f32<T>(fast ? cs.qv[u][e] * fast_exp2(cs.b[u][e]) : 0.f);
+        kh[e] = from_f32<T>(fast ? cs.kv[u][e] * fast_exp2(-cs.b[u][e]) : 0.f);
+        if constexpr (WITH_DV) kd[e] = from_f32<T>(cs.kv[u][e] * fast_exp2(sGam[c0 + e] - cs.b[u][e]));
+      }
+      *reinterpret_cast<VT*>(sQs + r * LDQ + c0) = qh;
+      *reinterpret_cast<VT*>(sKs + r * LDQ + c0) = kh;
+      if constexpr (WITH_DV) *reinterpret_cast<VT*>(sKd + r * LDQ + c0) = kd;
+    }
+  }
+  if constexpr (WITH_DV) tile_in_dense<T>(sA, reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP, CP, CP, LDC);
+  st.store(sdO, sV, sH, sdH);
+  __syncthreads();
+
+  f32x4 accA[PA], accQ[PQ], accK[PQ], accKI[PQ];
+#pragma unroll
+  for (int s = 0; s < PA; ++s) accA[s] = zero4();
+#pragma unroll
+  for (int s = 0; s < PQ; ++s) accQ[s] = accK[s] = accKI[s] = zero4();
+
+  for (int js = 0; js < ntile; ++js) {
+    if (js + 1 < ntile) st.load(dog, vg, hs, dhs, len, Dv, DVP, js + 1, kvalid);
+#pragma unroll
+    for (int s = 0; s < PA; ++s) {       // dA += dO V^T
+      const int blk = wave + 4 * s;
+      if (blk < NA_BLK) {
+        const int rb = blk / NBR, cb = blk % NBR;
+#pragma unroll
+        for (int kb = 0; kb < kDvTile / 32; ++kb)
+          mma(accA[s], ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp), ld8(sV + (16 * cb + col) * LDV + 32 * kb + 8 * grp));
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < PQ; ++s) {       // dQ += dO H^T ; dKI += V dH^T
+      const int blk = wave + 4 * s;
+      if (blk < NQ_BLK) {
+        const int rb = blk / NIB, ib = blk % NIB;
+#pragma unroll
+        for (int kb = 0; kb < kDvTile / 32; ++kb) {
+          mma(accQ[s], ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp), ld8(sH + (16 * ib + col) * LDV + 32 * kb + 8 * grp));
+          mma(accKI[s], ld8(sV + (16 * rb + col) * LDV + 32 * kb + 8 * grp), ld8(sdH + (16 * ib + col) * LDV + 32 * kb + 8 * grp));
+        }
+      }
+    }
+    if constexpr (WITH_DV) {             // dV = A^T dO + Kd dH for this slice
+#pragma unroll
+      for (int s = 0; s < PVb; ++s) {
+        const int blk = wave + 4 * s;
+        if (blk < NV_BLK) {
+          const int cb = blk / NJB, jb = blk % NJB;
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kr = 0; kr < CP / 32; ++kr)
+            mma(acc, ld8_col(sA + (32 * kr + 8 * grp) * LDC + 16 * cb + col, LDC),
+                ld8_col(sdO + (32 * kr + 8 * grp) * LDV + 16 * jb + col, LDV));
+#pragma unroll
+          for (int ki = 0; ki < DKS / 32; ++ki)
+            mma(acc, ld8(sKd + (16 * cb + col) * LDQ + 32 * ki + 8 * grp),
+                ld8_col(sdH + (32 * ki + 8 * grp) * LDV + 16 * jb + col, LDV));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sdV[(16 * cb + 4 * grp + e) * LDV + 16 * jb + col] = from_f32<T>(acc[e]);
+        }
+      }
+    }
+    __syncthreads();
+    if constexpr (WITH_DV) {
+      T* dvg = reinterpret_cast<T*>(p.dv) + ((size_t)bh * L + row0) * Dv;
+      constexpr int PER_ROW = kDvTile / V;
+      for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
+        const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+        const int jj = js * kDvTile + c;
+        if (r < len && jj < Dv)
+          *reinterpret_cast<VT*>(dvg + (size_t)r * Dv + jj) = *reinterpret_cast<const VT*>(sdV + r * LDV + c);
+      }
+    }
+    if (js + 1 < ntile) st.store(sdO, sV, sH, sdH);
+    __syncthreads();
+  }
+
+  // strictly lower dA -> LDS, its diagonal kept apart in fp32
+#pragma unroll
+  for (int s = 0; s < PA; ++s) {
+    const int blk = wave + 4 * s;
+    if (blk < NA_BLK) {
+      const int rb = blk / NBR, cb = blk % NBR;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
+        sdA[r * LDC + c] = from_f32<T>(c < r ? accA[s][e] : 0.f);
+        if (c == r) sDiag[r] = accA[s][e];
+      }
+    }
+  }
+  __syncthreads();
+  if (fast) {                            // off-diagonal intra terms on MFMA
+#pragma unroll
+    for (int s = 0; s < PQ; ++s) {
+      const int blk = wave + 4 * s;
+      if (blk < NQ_BLK) {
+        const int rb = blk / NIB, ib = blk % NIB;
+#pragma unroll
+        for (int kc = 0; kc < CP / 32; ++kc) {
+          mma(accQ[s], ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp),
+              ld8_col(sKs + (32 * kc + 8 * grp) * LDQ + 16 * ib + col, LDQ));
+          mma(accK[s], ld8_col(sdA + (32 * kc + 8 * grp) * LDC + 16 * rb + col, LDC),
+              ld8_col(sQs + (32 * kc + 8 * grp) * LDQ + 16 * ib + col, LDQ));
+        }
+      }
+    }
+  }
+  __syncthreads();                       // phase-1 tiles are dead from here on
+#pragma unroll
+  for (int s = 0; s < PQ; ++s) {
+    const int blk = wave + 4 * s;
+    if (blk < NQ_BLK) {
+      const int rb = blk / NIB, ib = blk % NIB;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int o = (16 * rb + 4 * grp + e) * LDF + 16 * ib + col;
+        sDQ[o] = accQ[s][e];
+        sDK[o] = accK[s][e];
+        sDKI[o] = accKI[s][e];
+      }
+    }
+  }
+  if (!fast && cs.active) {
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) sB[(r0 + u) * DKS + c0 + e] = cs.b[u][e];
+    }
+  }
+  __syncthreads();
+
+  // ---- epilogue: dq, dk; dg from the two in-chunk prefix sums and Z
+  float up[RPS][V], uk[RPS][V];          // q dq^nd - k dk'  (suffix-summed) ; k B (prefix-summed)
+  if (cs.active) {
+    T* dqg = reinterpret_cast<T*>(p.dq) + qbase;
+    T* dkg = reinterpret_cast<T*>(p.dk) + qbase;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const int r = r0 + u;
+      const float dgn = sDiag[r];
+      VT dqv, dkv;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const int i = c0 + e;
+        const float bb = cs.b[u][e];
+        float dqn, dkp;
+        if (fast) {
+          dqn = sDQ[r * LDF + i] * fast_exp2(bb);
+          dkp = sDK[r * LDF + i] * fast_exp2(-bb);
+        } else {
+          // exact off-diagonal intra terms: every exponent b_r - b_c has r > c
+          float iq = 0.f, ik = 0.f;
+          const int cend = c0 < kvalid ? len : 0;          // padded channels: q = k = 0
+          for (int c = 0; c < cend; ++c) {
+            if (c < r) iq += to_f32(sdA[r * LDC + c]) * to_f32(kg[(size_t)c * Dk + i]) * fast_exp2(bb - sB[c * DKS + i]);
+            if (c > r) ik += to_f32(sdA[c * LDC + r]) * to_f32(qg[(size_t)c * Dk + i]) * fast_exp2(sB[c * DKS + i] - bb);
+          }
+          dqn = sDQ[r * LDF + i] * fast_exp2(bb) + iq;
+          dkp = ik;
+        }
+        const float bk = sDKI[r * LDF + i] * fast_exp2(sGam[i] - bb);
+        const float qv = cs.qv[u][e], kv = cs.kv[u][e];
+        dqv[e] = from_f32<T>(dqn + dgn * kv);
+        dkv[e] = from_f32<T>(dkp + dgn * qv + bk);
+        up[u][e] = qv * dqn - kv * dkp;
+        uk[u][e] = kv * bk;
+      }
+      if (r < len && c0 < kvalid) {
+        *reinterpret_cast<VT*>(dqg + (size_t)r * Dk + c0) = dqv;
+        *reinterpret_cast<VT*>(dkg + (size_t)r * Dk + c0) = dkv;
+      }
+    }
+    // in-segment scans: inclusive suffix of up, exclusive prefix of uk
+    float sp[V], sk[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) sp[e] = sk[e] = 0.f;
+#pragma unroll
+    for (int u = RPS - 1; u >= 0; --u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        sp[e] += up[u][e];
+        up[u][e] = sp[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float x = uk[u][e];
+        uk[u][e] = sk[e];
+        sk[e] += x;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      segtot[cs.seg * DKS + c0 + e] = sp[e];
+      segtot[(NSEG + cs.seg) * DKS + c0 + e] = sk[e];
+    }
+  }
+  __syncthreads();
+  if (cs.active) {
+    float add[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) add[e] = sZ[c0 + e];
+    for (int s2 = cs.seg + 1; s2 < NSEG; ++s2) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) add[e] += segtot[s2 * DKS + c0 + e];
+    }
+    for (int s2 = 0; s2 < cs.seg; ++s2) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) add[e] += segtot[(NSEG + s2) * DKS + c0 + e];
+    }
+    float* dgg = p.dg + qbase;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const int r = r0 + u;
+      if (r < len && c0 < kvalid) {
+#pragma unroll
+        for (int e = 0; e < V; e += 4) {
+          f32x4 w;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) w[x] = up[u][e + x] + uk[u][e + x] + add[e + x];
+          *reinterpret_cast<f32x4*>(dgg + (size_t)r * Dk + c0 + e) = w;
+        }
+      }
+    }
+  }
+}
+
+// ======================================================================= dv (separate)
+template <typename T, int DKP, int CP>
+struct BwdDvCfg {
+  static constexpr int V = 16 / (int)sizeof(T);
+  static constexpr int LDC = CP + V, LDV = kDvTile + V;
+  static constexpr size_t AT = (size_t)CP * LDC * sizeof(T);
+  static constexpr size_t KT = (size_t)DKP * LDC * sizeof(T);
+  static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
+  static constexpr size_t HT = (size_t)DKP * LDV * sizeof(T);
+  static constexpr size_t BYTES = AT + KT + 2 * VT + HT;
+};
+
+template <typename T, int DKP, int CP>
+__global__ __launch_bounds__(256) void gla_bwd_dv(BwdParams p, int ntile) {
+  using Cf = BwdDvCfg<T, DKP, CP>;
+  constexpr int V = Cf::V, LDC = Cf::LDC, LDV = Cf::LDV;
+  constexpr int NBR = CP / 16;
+  typedef typename V16<T>::type VT;
+  __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
+  T* sA = reinterpret_cast<T*>(smem);
+  T* sKdT = reinterpret_cast<T*>(smem + Cf::AT);
+  T* sdO = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT);
+  T* sdV = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT + Cf::VT);
+  T* sdH = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT + 2 * Cf::VT);
+
+  const int n = blockIdx.x, bh = blockIdx.y, js = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int Dv = p.Dv, L = p.L, N = p.N;
+  const int DVP = ntile * kDvTile;
+  const int row0 = n * p.C, len = min(p.C, L - row0);
+  const size_t chunk = (size_t)bh * N + n;
+  tile_in_dense<T>(sA, reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP, CP, CP, LDC);
+  tile_in_dense<T>(sKdT, reinterpret_cast<const T*>(p.ops.KdT) + chunk * DKP * CP, DKP, CP, LDC);
+  const T* dhs = reinterpret_cast<const T*>(p.dHs) + chunk * DKP * DVP + js * kDvTile;
+  const T* dog = reinterpret_cast<const T*>(p.do_) + ((size_t)bh * L + row0) * Dv;
+  constexpr int PER_ROW = kDvTile / V;
+  for (int idx = tid; idx < DKP * PER_ROW; idx += 256) {
+    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+    *reinterpret_cast<VT*>(sdH + r * LDV + c) = *reinterpret_cast<const VT*>(dhs + (size_t)r * DVP + c);
+  }
+  for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
+    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+    const int jj = js * kDvTile + c;
+    *reinterpret_cast<VT*>(sdO + r * LDV + c) =
+        (r < len && jj < Dv) ? *reinterpret_cast<const VT*>(dog + (size_t)r * Dv + jj) : zero_vec<T>();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int cb = 0; cb < NBR; ++cb) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int kr = 0; kr < CP / 32; ++kr)
+      mma(acc, ld8_col(sA + (32 * kr + 8 * grp) * LDC + 16 * cb + col, LDC),
+          ld8_col(sdO + (32 * kr + 8 * grp) * LDV + 16 * wave + col, LDV));
+#pragma unroll
+    for (int ki = 0; ki < DKP / 32; ++ki)
+      mma(acc, ld8_col(sKdT + (32 * ki + 8 * grp) * LDC + 16 * cb + col, LDC),
+          ld8_col(sdH + (32 * ki + 8 * grp) * LDV + 16 * wave + col, LDV));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sdV[(16 * cb + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(acc[e]);
+  }
+  __syncthreads();
+  T* dvg = reinterpret_cast<T*>(p.dv) + ((size_t)bh * L + row0) * Dv;
+  for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
+    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+    const int jj = js * kDvTile + c;
+    if (r < len && jj < Dv)
+      *reinterpret_cast<VT*>(dvg + (size_t)r * Dv + jj) = *reinterpret_cast<const VT*>(sdV + r * LDV + c);
+  }
+}
+
+// ======================================================================= plan + launch
+// Key-width slice of the chunk kernel: the whole key width with dv fused when it fits the
+// LDS of a CU, otherwise slices of at most 128 channels with dv in its own kernel.
+template <typename T, int DKP, int CP>
+struct BwdPlan {
+  static constexpr int es = sizeof(T);
+  static constexpr int nseg(int dks) { return imin(256 / (dks / (16 / es)), CP); }
+  static constexpr bool fits(int dks, bool dv) { return chunk_bwd_bytes(es, dks, CP, dv, nseg(dks)) <= kMaxLds; }
+  static constexpr bool FUSED = fits(DKP, true);
+  static constexpr int DKS = FUSED ? DKP
+                           : (DKP >= 128 && fits(128, false)) ? 128
+                           : (DKP >= 64 && fits(64, false)) ? 64 : 32;
+  static constexpr bool OK = (FUSED || fits(DKS, false)) && PrepCfg<T, DKP, CP>::BYTES <= kMaxLds &&
+                             BwdWalkCfg<T, DKP, CP>::BYTES <= kMaxLds &&
+                             (FUSED || BwdDvCfg<T, DKP, CP>::BYTES <= kMaxLds);
+};
+
+template <typename T, int DKP, int CP>
+hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
+  using P = BwdPlan<T, DKP, CP>;
+  if constexpr (!P::OK) {
+    return hipErrorNotSupported;
+  } else {
+    PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N};
+    hipError_t e = launch_prep<T, DKP, CP, true>(pp, p.BH, s);
+    if (e != hipSuccess) return e;
+    const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
+    hipLaunchKernelGGL((gla_bwd_walk<T, DKP, CP>), dim3(ntile * p.BH), dim3(256), 0, s, p, ntile);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED>), dim3(p.N, p.BH, DKP / P::DKS), dim3(256), 0, s,
+                       p, DKP, ntile);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if constexpr (!P::FUSED) {
+      hipLaunchKernelGGL((gla_bwd_dv<T, DKP, CP>), dim3(p.N, p.BH, ntile), dim3(256), 0, s, p, ntile);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+}
+
+bool bwd_config_fits(int esize, int DKP, int CP) {
+  bool ok = false;
+#define GLA_BFIT_CASE(TT, D, C_) \
+  if (esize == (int)sizeof(TT) && DKP == D && CP == C_) ok = BwdPlan<TT, D, C_>::OK;
+#define GLA_BFIT_ALL(TT)                                                                 \
+  GLA_BFIT_CASE(TT, 32, 32) GLA_BFIT_CASE(TT, 32, 64) GLA_BFIT_CASE(TT, 32, 128)           \
+  GLA_BFIT_CASE(TT, 64, 32) GLA_BFIT_CASE(TT, 64, 64) GLA_BFIT_CASE(TT, 64, 128)           \
+  GLA_BFIT_CASE(TT, 128, 32) GLA_BFIT_CASE(TT, 128, 64) GLA_BFIT_CASE(TT, 128, 128)        \
+  GLA_BFIT_CASE(TT, 256, 32) GLA_BFIT_CASE(TT, 256, 64)
+  GLA_BFIT_ALL(bf16)
+  GLA_BFIT_ALL(float)
+#undef GLA_BFIT_ALL
+#undef GLA_BFIT_CASE
+  return ok;
+}
+
 #define GLA_BWD_INST(TT, D, C_) template hipError_t launch_gla_bwd<TT, D, C_>(const BwdParams&, hipStream_t);
 #define GLA_BWD_INST_T(TT)                                                     \
   GLA_BWD_INST(TT, 32, 32) GLA_BWD_INST(TT, 32, 64) GLA_BWD_INST(TT, 32, 128)  \
@@ -11,4 +804,5 @@ hipError_t launch_gla_bwd(const BwdParams&, hipStream_t) { return hipErrorNotSup
   GLA_BWD_INST(TT, 256, 32) GLA_BWD_INST(TT, 256, 64)
 GLA_BWD_INST_T(bf16)
 GLA_BWD_INST_T(float)
+
 }  // namespace gla

@@ -18,15 +18,116 @@
 
 namespace gla {
 
+// LDS layout and prefetch shape of the walk (one chunk's operands).
+template <typename T, int DKP, int CP>
+struct WalkCfg {
+  static constexpr int V = 16 / (int)sizeof(T);
+  static constexpr int LDQ = DKP + V, LDA = CP + V, LDV = kDvTile + V;
+  static constexpr size_t QT = (size_t)CP * LDQ * sizeof(T);
+  static constexpr size_t AT = (size_t)CP * LDA * sizeof(T);
+  static constexpr size_t KT = (size_t)DKP * LDA * sizeof(T);
+  static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
+  static constexpr size_t BYTES = QT + AT + KT + 2 * VT + DKP * 4;
+  // 16-byte vectors per chunk and per thread
+  static constexpr int NQ = CP * DKP / V, NA = CP * CP / V, NK = DKP * CP / V, NV = CP * kDvTile / V;
+  static constexpr int PQ = (NQ + 255) / 256, PA = (NA + 255) / 256, PKd = (NK + 255) / 256, PV = (NV + 255) / 256;
+};
+
+// One chunk's walk operands in flight between global memory and LDS.
+template <typename T, int DKP, int CP>
+struct WalkStage {
+  using W = WalkCfg<T, DKP, CP>;
+  typedef typename V16<T>::type VT;
+  VT q[W::PQ], a[W::PA], kd[W::PKd], v[W::PV];
+  f32x4 gam;
+
+  __device__ __forceinline__ void load(const FwdParams& p, int bh, int n, int tile) {
+    const int tid = threadIdx.x;
+    const size_t chunk = (size_t)bh * p.N + n;
+    const T* Qc = reinterpret_cast<const T*>(p.ops.Qs) + chunk * CP * DKP;
+    const T* Ac = reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP;
+    const T* Kc = reinterpret_cast<const T*>(p.ops.KdT) + chunk * DKP * CP;
+#pragma unroll
+    for (int m = 0; m < W::PQ; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < W::NQ) q[m] = *reinterpret_cast<const VT*>(Qc + (size_t)idx * W::V);
+    }
+#pragma unroll
+    for (int m = 0; m < W::PA; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < W::NA) a[m] = *reinterpret_cast<const VT*>(Ac + (size_t)idx * W::V);
+    }
+#pragma unroll
+    for (int m = 0; m < W::PKd; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < W::NK) kd[m] = *reinterpret_cast<const VT*>(Kc + (size_t)idx * W::V);
+    }
+    const int row0 = n * p.C, len = min(p.C, p.L - row0);
+    const T* vg = reinterpret_cast<const T*>(p.v) + ((size_t)bh * p.L + row0) * p.Dv;
+    constexpr int PER_ROW = kDvTile / W::V;
+#pragma unroll
+    for (int m = 0; m < W::PV; ++m) {
+      const int idx = tid + 256 * m;
+      const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
+      const int j = tile * kDvTile + c;
+      v[m] = (idx < W::NV && r < len && j < p.Dv) ? *reinterpret_cast<const VT*>(vg + (size_t)r * p.Dv + j)
+                                                  : zero_vec<T>();
+    }
+    if (tid < DKP / 4) gam = *reinterpret_cast<const f32x4*>(p.ops.Gam + chunk * DKP + 4 * tid);
+  }
+
+  __device__ __forceinline__ void store(T* sQ, T* sA, T* sK, T* sV, float* sG) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < W::PQ; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < W::NQ) {
+        const int r = idx / (DKP / W::V), c = (idx - r * (DKP / W::V)) * W::V;
+        *reinterpret_cast<VT*>(sQ + r * W::LDQ + c) = q[m];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < W::PA; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < W::NA) {
+        const int r = idx / (CP / W::V), c = (idx - r * (CP / W::V)) * W::V;
+        *reinterpret_cast<VT*>(sA + r * W::LDA + c) = a[m];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < W::PKd; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < W::NK) {
+        const int r = idx / (CP / W::V), c = (idx - r * (CP / W::V)) * W::V;
+        *reinterpret_cast<VT*>(sK + r * W::LDA + c) = kd[m];
+      }
+    }
+    constexpr int PER_ROW = kDvTile / W::V;
+#pragma unroll
+    for (int m = 0; m < W::PV; ++m) {
+      const int idx = tid + 256 * m;
+      if (idx < W::NV) {
+        const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
+        *reinterpret_cast<VT*>(sV + r * W::LDV + c) = v[m];
+      }
+    }
+    if (tid < DKP / 4) *reinterpret_cast<f32x4*>(sG + 4 * tid) = gam;
+  }
+};
+
 template <typename T, int DKP, int CP>
 __global__ __launch_bounds__(256) void gla_fwd_walk(FwdParams p, int ntile) {
-  constexpr int PV = 16 / (int)sizeof(T);
-  constexpr int LDV = kDvTile + PV;
+  using W = WalkCfg<T, DKP, CP>;
+  constexpr int LDQ = W::LDQ, LDA = W::LDA, LDV = W::LDV;
   constexpr int NBR = CP / 16, NKB = DKP / 32, NCB = CP / 32, NIB = DKP / 16;
-  constexpr int V = V16<T>::N;
   typedef typename V16<T>::type VT;
-  __shared__ __attribute__((aligned(16))) T sV[CP * LDV];
-  __shared__ float sG[DKP];
+  __shared__ __attribute__((aligned(16))) char smem[W::BYTES];
+  T* sQ = reinterpret_cast<T*>(smem);
+  T* sA = reinterpret_cast<T*>(smem + W::QT);
+  T* sK = reinterpret_cast<T*>(smem + W::QT + W::AT);
+  T* sV = reinterpret_cast<T*>(smem + W::QT + W::AT + W::KT);
+  T* sO = reinterpret_cast<T*>(smem + W::QT + W::AT + W::KT + W::VT);
+  float* sG = reinterpret_cast<float*>(smem + W::QT + W::AT + W::KT + 2 * W::VT);
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = lin % ntile, bh = lin / ntile;
@@ -44,29 +145,17 @@ __global__ __launch_bounds__(256) void gla_fwd_walk(FwdParams p, int ntile) {
       H[ib][e] = (p.h0 && jv && i < p.Dk) ? p.h0[((size_t)bh * p.Dk + i) * Dv + j] : 0.f;
     }
   }
-  const T* vg = reinterpret_cast<const T*>(p.v) + (size_t)bh * L * Dv;
   T* og = reinterpret_cast<T*>(p.o) + (size_t)bh * L * Dv;
 
+  WalkStage<T, DKP, CP> st;
+  st.load(p, bh, 0, tile);
+  st.store(sQ, sA, sK, sV, sG);
+  __syncthreads();
+
   for (int n = 0; n < N; ++n) {
+    if (n + 1 < N) st.load(p, bh, n + 1, tile);     // in flight during this chunk's math
     const int row0 = n * C;
     const int len = min(C, L - row0);
-    const size_t chunk = (size_t)bh * N + n;
-    // stage the V tile [CP][64] (zero outside the chunk and past Dv)
-    constexpr int PER_ROW = kDvTile / V;
-    for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
-      const int r = idx / PER_ROW, cv = (idx - r * PER_ROW) * V;
-      const int jj = tile * kDvTile + cv;
-      VT val;
-      if (r < len && jj < Dv) {
-        val = *reinterpret_cast<const VT*>(vg + (size_t)(row0 + r) * Dv + jj);
-      } else {
-#pragma unroll
-        for (int e = 0; e < V; ++e) val[e] = from_f32<T>(0.f);
-      }
-      *reinterpret_cast<VT*>(sV + r * LDV + cv) = val;
-    }
-    if (tid < DKP) sG[tid] = p.ops.Gam[chunk * DKP + tid];
-    __syncthreads();
 
     Frag<T> Yv[NCB];
 #pragma unroll
@@ -76,29 +165,21 @@ __global__ __launch_bounds__(256) void gla_fwd_walk(FwdParams p, int ntile) {
     f32x4 O[NBR];
 #pragma unroll
     for (int rb = 0; rb < NBR; ++rb) O[rb] = zero4();
-    const T* Qc = reinterpret_cast<const T*>(p.ops.Qs) + chunk * CP * DKP;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const Frag<T> Yh = frag_from_acc<T>(H[2 * kb], H[2 * kb + 1]);
 #pragma unroll
-      for (int rb = 0; rb < NBR; ++rb)
-        mma(O[rb], ld8_split(Qc + (16 * rb + col) * DKP + 32 * kb + 4 * grp), Yh);
+      for (int rb = 0; rb < NBR; ++rb) mma(O[rb], ld8_split(sQ + (16 * rb + col) * LDQ + 32 * kb + 4 * grp), Yh);
     }
-    const T* Ac = reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-      for (int rb = 0; rb < NBR; ++rb) mma(O[rb], ld8(Ac + (16 * rb + col) * CP + 32 * cb + 8 * grp), Yv[cb]);
+      for (int rb = 0; rb < NBR; ++rb) mma(O[rb], ld8(sA + (16 * rb + col) * LDA + 32 * cb + 8 * grp), Yv[cb]);
     }
-    if (jv) {
 #pragma unroll
-      for (int rb = 0; rb < NBR; ++rb) {
+    for (int rb = 0; rb < NBR; ++rb) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * rb + 4 * grp + e;
-          if (r < len) og[(size_t)(row0 + r) * Dv + j] = from_f32<T>(O[rb][e]);
-        }
-      }
+      for (int e = 0; e < 4; ++e) sO[(16 * rb + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(O[rb][e]);
     }
 
     // H <- Diag(2^Gamma) H + KdT V
@@ -107,12 +188,21 @@ __global__ __launch_bounds__(256) void gla_fwd_walk(FwdParams p, int ntile) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) H[ib][e] *= fast_exp2(sG[16 * ib + 4 * grp + e]);
     }
-    const T* Kc = reinterpret_cast<const T*>(p.ops.KdT) + chunk * DKP * CP;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-      for (int ib = 0; ib < NIB; ++ib) mma(H[ib], ld8(Kc + (16 * ib + col) * CP + 32 * cb + 8 * grp), Yv[cb]);
+      for (int ib = 0; ib < NIB; ++ib) mma(H[ib], ld8(sK + (16 * ib + col) * LDA + 32 * cb + 8 * grp), Yv[cb]);
     }
+    __syncthreads();   // chunk n's LDS operands consumed, sO complete
+
+    constexpr int PER_ROW = kDvTile / W::V;
+    for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
+      const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
+      const int jj = tile * kDvTile + c;
+      if (r < len && jj < Dv)
+        *reinterpret_cast<VT*>(og + (size_t)(row0 + r) * Dv + jj) = *reinterpret_cast<const VT*>(sO + r * LDV + c);
+    }
+    if (n + 1 < N) st.store(sQ, sA, sK, sV, sG);
     __syncthreads();
   }
   if (p.ht && jv) {
@@ -129,28 +219,33 @@ __global__ __launch_bounds__(256) void gla_fwd_walk(FwdParams p, int ntile) {
 
 template <typename T, int DKP, int CP>
 hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
-  PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N};
-  hipError_t e = launch_prep<T, DKP, CP, false>(pp, p.BH, s);
-  if (e != hipSuccess) return e;
-  const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
-  hipLaunchKernelGGL((gla_fwd_walk<T, DKP, CP>), dim3(ntile * p.BH), dim3(256), 0, s, p, ntile);
-  return hipGetLastError();
+  if constexpr (PrepCfg<T, DKP, CP>::BYTES > kMaxLds || WalkCfg<T, DKP, CP>::BYTES > kMaxLds) {
+    return hipErrorNotSupported;
+  } else {
+    PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N};
+    hipError_t e = launch_prep<T, DKP, CP, false>(pp, p.BH, s);
+    if (e != hipSuccess) return e;
+    const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
+    hipLaunchKernelGGL((gla_fwd_walk<T, DKP, CP>), dim3(ntile * p.BH), dim3(256), 0, s, p, ntile);
+    return hipGetLastError();
+  }
 }
 
-size_t prep_lds_bytes(int esize, int DKP, int CP) {
-  size_t b = 0;
-#define GLA_PREP_CASE(TT, D, C_)                                              \
-  if (esize == (int)sizeof(TT) && DKP == D && CP == C_) b = PrepCfg<TT, D, C_>::BYTES;
-#define GLA_PREP_ALL(TT)                                                       \
-  GLA_PREP_CASE(TT, 32, 32) GLA_PREP_CASE(TT, 32, 64) GLA_PREP_CASE(TT, 32, 128) \
-  GLA_PREP_CASE(TT, 64, 32) GLA_PREP_CASE(TT, 64, 64) GLA_PREP_CASE(TT, 64, 128) \
-  GLA_PREP_CASE(TT, 128, 32) GLA_PREP_CASE(TT, 128, 64) GLA_PREP_CASE(TT, 128, 128) \
-  GLA_PREP_CASE(TT, 256, 32) GLA_PREP_CASE(TT, 256, 64) GLA_PREP_CASE(TT, 256, 128)
-  GLA_PREP_ALL(bf16)
-  GLA_PREP_ALL(float)
-#undef GLA_PREP_ALL
-#undef GLA_PREP_CASE
-  return b <= 160 * 1024 ? b : 0;
+bool fwd_config_fits(int esize, int DKP, int CP) {
+  bool ok = false;
+#define GLA_FIT_CASE(TT, D, C_)                                                       \
+  if (esize == (int)sizeof(TT) && DKP == D && CP == C_)                               \
+    ok = PrepCfg<TT, D, C_>::BYTES <= kMaxLds && WalkCfg<TT, D, C_>::BYTES <= kMaxLds;
+#define GLA_FIT_ALL(TT)                                                                \
+  GLA_FIT_CASE(TT, 32, 32) GLA_FIT_CASE(TT, 32, 64) GLA_FIT_CASE(TT, 32, 128)           \
+  GLA_FIT_CASE(TT, 64, 32) GLA_FIT_CASE(TT, 64, 64) GLA_FIT_CASE(TT, 64, 128)           \
+  GLA_FIT_CASE(TT, 128, 32) GLA_FIT_CASE(TT, 128, 64) GLA_FIT_CASE(TT, 128, 128)        \
+  GLA_FIT_CASE(TT, 256, 32) GLA_FIT_CASE(TT, 256, 64)
+  GLA_FIT_ALL(bf16)
+  GLA_FIT_ALL(float)
+#undef GLA_FIT_ALL
+#undef GLA_FIT_CASE
+  return ok;
 }
 
 #define GLA_FWD_INST(TT, D, C_) template hipError_t launch_gla_fwd<TT, D, C_>(const FwdParams&, hipStream_t);

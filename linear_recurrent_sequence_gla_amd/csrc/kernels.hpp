@@ -56,7 +56,11 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s);
 template <typename T>
 hipError_t launch_gla_decode(const DecodeParams& p, hipStream_t s);
 
-// LDS bytes the preparation kernel needs (0 = does not fit the 160 KB of a CU).
-size_t prep_lds_bytes(int esize, int DKP, int CP);
+constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
+
+// Whether every kernel of the forward fits the LDS of a CU for this (dtype size, DKP, CP).
+bool fwd_config_fits(int esize, int DKP, int CP);
+// Same for the backward kernels.
+bool bwd_config_fits(int esize, int DKP, int CP);
 
 }  // namespace gla

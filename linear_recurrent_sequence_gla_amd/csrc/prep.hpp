@@ -29,6 +29,11 @@
 // carried as X = hi + lo (hi = bf16(X), lo = bf16(X - hi)) and the product uses
 // hi.hi^T + hi.lo^T + lo.hi^T (three MFMAs), good to about 2^-17 per term.  The score
 // product is a small share of the chunk's matrix work, so this costs little.
+//
+// Memory access: every thread owns V = 16/sizeof(T) adjacent key channels of a few chunk
+// rows, loads its q, k, g vectors with 16-byte accesses issued together, and scans its rows
+// locally; segment totals are combined through LDS.  Qs leaves straight from registers with
+// 16-byte stores; KdT and A are staged in LDS so their stores are 16-byte and coalesced.
 #pragma once
 #include "common.hpp"
 #include "kernels.hpp"
@@ -44,26 +49,39 @@ struct PrepParams {
 };
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+constexpr int imin(int a, int b) { return a < b ? a : b; }
+
+// Thread -> (channel group, row segment) map for the element-wise phase of a chunk.
+template <typename T, int DKP, int CP>
+struct ChunkMap {
+  static constexpr int V = 16 / (int)sizeof(T);        // channels per thread (one 16-byte vector)
+  static constexpr int NCG = DKP / V;                  // channel groups
+  static constexpr int NSEG = imin(256 / NCG, CP);     // row segments
+  static constexpr int RPS = CP / NSEG;                // rows per segment
+  static constexpr int ACTIVE = NCG * NSEG;            // threads with work (<= 256)
+};
 
 template <typename T, int DKP, int CP>
 struct PrepCfg {
-  static constexpr int TPC = 256 / DKP;          // threads per key channel
-  static constexpr int RPT = CP / TPC;           // chunk rows per thread
-  static constexpr int PK = 16 / (int)sizeof(T); // 16-byte row padding, in elements
-  static constexpr int LDQ = DKP + PK;           // row stride of the [CP][DKP] tiles
-  static constexpr int LDC = CP + PK;            // row stride of the [DKP][CP] tile
-  static constexpr int LDP = 32 + PK;            // row stride of the safe-path slice tiles
-  static constexpr int NB = CP / 16;             // 16-row sub-chunks per chunk
-  static constexpr int NP = NB * (NB - 1) / 2;   // off-diagonal sub-block pairs
-  static constexpr int PPW = (NP + 3) / 4;       // pairs per wave
-  // bf16 operands of the score product are split hi + lo ("Precision of A"); fp32 is not split
-  static constexpr bool SPLIT = sizeof(T) == 2;
+  using M = ChunkMap<T, DKP, CP>;
+  static constexpr int PK = 16 / (int)sizeof(T);       // 16-byte row padding, in elements
+  static constexpr int LDQ = DKP + PK;                 // row stride of the [CP][DKP] tiles
+  static constexpr int LDC = CP + PK;                  // row stride of [DKP][CP] and [CP][CP] tiles
+  static constexpr int LDP = 32 + PK;                  // row stride of the safe-path slice tiles
+  static constexpr int NB = CP / 16;                   // 16-row sub-chunks per chunk
+  static constexpr int NP = NB * (NB - 1) / 2;         // off-diagonal sub-block pairs
+  static constexpr int PPW = (NP + 3) / 4;             // pairs per wave
+  static constexpr bool SPLIT = sizeof(T) == 2;        // hi/lo operands ("Precision of A")
   static constexpr size_t TILE = (size_t)CP * LDQ * sizeof(T);
-  static constexpr size_t R1 = TILE;
-  static constexpr size_t SAFE = (size_t)3 * CP * 33 * 4 + (size_t)(SPLIT ? 2 : 1) * (CP + 16) * LDP * sizeof(T);
-  static constexpr size_t R2 = cmax(cmax((SPLIT ? 3 : 1) * TILE, (size_t)DKP * LDC * sizeof(T)), SAFE);
-  static constexpr size_t MISC = (size_t)(TPC * DKP + DKP + 8) * 4;
-  static constexpr size_t BYTES = R1 + R2 + MISC;
+  static constexpr size_t KDT = (size_t)DKP * LDC * sizeof(T);
+  static constexpr size_t ATILE = (size_t)CP * LDC * sizeof(T);
+  // fast path: sQ, sK (+ sQl, sKl); after the score product the same bytes hold KdT and A
+  static constexpr size_t FAST = (SPLIT ? 4 : 2) * TILE;
+  static constexpr size_t SAFE = TILE + (size_t)3 * CP * 33 * 4 +
+                                 (size_t)(SPLIT ? 2 : 1) * (CP + 16) * LDP * sizeof(T);
+  static constexpr size_t MAIN = cmax(cmax(FAST, SAFE), TILE + KDT + ATILE);
+  static constexpr size_t MISC = (size_t)(M::NSEG * DKP + DKP + 8) * 4;
+  static constexpr size_t BYTES = MAIN + MISC;
 };
 
 // Copy a [rows][cols] tile (LDS row stride lds) to dense global memory, 16 bytes per access.
@@ -75,6 +93,17 @@ __device__ __forceinline__ void tile_out(T* __restrict__ dst, const T* src, int 
   for (int idx = threadIdx.x; idx < rows * per_row; idx += blockDim.x) {
     const int r = idx / per_row, c = (idx - r * per_row) * V;
     *reinterpret_cast<VT*>(dst + (size_t)r * cols + c) = *reinterpret_cast<const VT*>(src + r * lds + c);
+  }
+}
+// Copy a dense global [rows][cols] tile into LDS (row stride lds), 16 bytes per access.
+template <typename T>
+__device__ __forceinline__ void tile_in_dense(T* dst, const T* __restrict__ src, int rows, int cols, int lds) {
+  constexpr int V = V16<T>::N;
+  typedef typename V16<T>::type VT;
+  const int per_row = cols / V;
+  for (int idx = threadIdx.x; idx < rows * per_row; idx += blockDim.x) {
+    const int r = idx / per_row, c = (idx - r * per_row) * V;
+    *reinterpret_cast<VT*>(dst + r * lds + c) = *reinterpret_cast<const VT*>(src + (size_t)r * cols + c);
   }
 }
 // Copy the transpose of a [rows][cols] LDS tile to dense global [cols][rows].
@@ -98,107 +127,196 @@ __device__ __forceinline__ void pair_decode(int p, int& x, int& y) {
   y = p - (x * (x - 1)) / 2;
 }
 
+template <typename T>
+__device__ __forceinline__ typename V16<T>::type zero_vec() {
+  typename V16<T>::type z;
+#pragma unroll
+  for (int e = 0; e < V16<T>::N; ++e) z[e] = from_f32<T>(0.f);
+  return z;
+}
+
+// Chunk-local gate scan for the thread's (channel group, row segment): loads g, q, k
+// vectors (16-byte, all issued before first use), keeps b (log2 units) and the raw q and k
+// of its rows and channels, publishes Gamma in sGam and returns the block-wide max |b|.
+// Must be called by all 256 threads.
+template <typename T, int DKP, int CP>
+struct ChunkScan {
+  using M = ChunkMap<T, DKP, CP>;
+  static constexpr int V = M::V, RPS = M::RPS;
+  float b[RPS][V];
+  float qv[RPS][V];
+  float kv[RPS][V];
+  int cg, seg;
+  bool active;
+
+  // ld: row stride of q, k, g (elements); width: valid channels from the base pointer
+  __device__ __forceinline__ float run(const T* qg, const T* kg, const T* gg, int ld, int width, int len,
+                                       float* segtot, float* sGam, float* red) {
+    typedef typename V16<T>::type VT;
+    const int tid = threadIdx.x;
+    cg = tid % M::NCG;
+    seg = tid / M::NCG;
+    active = tid < M::ACTIVE;
+    const bool chv = active && cg * V < width;
+    VT gvec[RPS], qvec[RPS], kvec[RPS];
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const int r = seg * RPS + u;
+      const bool ok = chv && r < len;
+      const size_t off = (size_t)r * ld + cg * V;
+      gvec[u] = ok ? *reinterpret_cast<const VT*>(gg + off) : zero_vec<T>();
+      qvec[u] = ok ? *reinterpret_cast<const VT*>(qg + off) : zero_vec<T>();
+      kvec[u] = ok ? *reinterpret_cast<const VT*>(kg + off) : zero_vec<T>();
+    }
+    float run_[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) run_[e] = 0.f;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        run_[e] += to_f32(gvec[u][e]) * kLog2e;
+        b[u][e] = run_[e];
+        qv[u][e] = to_f32(qvec[u][e]);
+        kv[u][e] = to_f32(kvec[u][e]);
+      }
+    }
+    if (active) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) segtot[seg * DKP + cg * V + e] = run_[e];
+    }
+    __syncthreads();
+    float mx = 0.f;
+    if (active) {
+      float pre[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) pre[e] = 0.f;
+      for (int s = 0; s < seg; ++s) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) pre[e] += segtot[s * DKP + cg * V + e];
+      }
+#pragma unroll
+      for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          b[u][e] += pre[e];
+          mx = fmaxf(mx, fabsf(b[u][e]));
+        }
+      }
+      if (seg == M::NSEG - 1) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) sGam[cg * V + e] = b[RPS - 1][e];
+      }
+    }
+    return block_max256(mx, red);   // also makes sGam visible to all threads
+  }
+};
+
 template <typename T, int DKP, int CP, bool WANT_QST>
 __global__ __launch_bounds__(256) void gla_prep_kernel(PrepParams p) {
   using Cfg = PrepCfg<T, DKP, CP>;
-  constexpr int TPC = Cfg::TPC, RPT = Cfg::RPT, LDQ = Cfg::LDQ, LDC = Cfg::LDC, LDP = Cfg::LDP;
+  using M = ChunkMap<T, DKP, CP>;
+  constexpr int V = M::V, RPS = M::RPS;
+  constexpr int LDQ = Cfg::LDQ, LDC = Cfg::LDC, LDP = Cfg::LDP;
   constexpr int NB = Cfg::NB, NP = Cfg::NP, PPW = Cfg::PPW;
+  typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
-  T* sQ = reinterpret_cast<T*>(smem);
-  char* r2 = smem + Cfg::R1;
-  float* segtot = reinterpret_cast<float*>(r2 + Cfg::R2);
-  float* sGam = segtot + TPC * DKP;
+  float* segtot = reinterpret_cast<float*>(smem + Cfg::MAIN);
+  float* sGam = segtot + M::NSEG * DKP;
   float* red = sGam + DKP;
 
   const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int row0 = n * p.C;
   const int len = min(p.C, p.L - row0);
   const int Dk = p.Dk;
-  const int ch = tid % DKP, seg = tid / DKP, r0 = seg * RPT;
-  const bool chv = ch < Dk;
   const size_t base = ((size_t)bh * p.L + row0) * Dk;
-  const T* qg = reinterpret_cast<const T*>(p.q) + base;
-  const T* kg = reinterpret_cast<const T*>(p.k) + base;
-  const T* gg = reinterpret_cast<const T*>(p.g) + base;
   const size_t chunk = (size_t)bh * p.N + n;
 
-  // ---- chunk-local prefix sum of the gates (log2 units), segment-wise then combined
-  float b[RPT];
-  float run = 0.f;
-#pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const int r = r0 + u;
-    const float gv = (chv && r < len) ? to_f32(gg[(size_t)r * Dk + ch]) * kLog2e : 0.f;
-    run += gv;
-    b[u] = run;
-  }
-  segtot[seg * DKP + ch] = run;
-  __syncthreads();
-  float pre = 0.f;
-  for (int s = 0; s < seg; ++s) pre += segtot[s * DKP + ch];
-  float mx = 0.f;
-#pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    b[u] += pre;
-    mx = fmaxf(mx, fabsf(b[u]));
-  }
-  if (seg == TPC - 1) sGam[ch] = b[RPT - 1];
-  const bool fast = block_max256(mx, red) <= kSpanLimit;   // also publishes sGam
+  ChunkScan<T, DKP, CP> cs;
+  const float maxb = cs.run(reinterpret_cast<const T*>(p.q) + base, reinterpret_cast<const T*>(p.k) + base,
+                            reinterpret_cast<const T*>(p.g) + base, Dk, Dk, len, segtot, sGam, red);
+  const bool fast = maxb <= kSpanLimit;
+  const int c0 = cs.cg * V, r0 = cs.seg * RPS;
 
-  // ---- Qs = q 2^b (and Ks = k 2^-b on the fast path), with bf16 lo parts
-  T* sK = reinterpret_cast<T*>(r2);
+  // LDS regions: [0, TILE) sQ; then fast: sK, sQl, sKl; safe: its scratch
+  T* sQ = reinterpret_cast<T*>(smem);
+  T* sK = sQ + CP * LDQ;
   T* sQl = sK + CP * LDQ;
   T* sKl = sQl + CP * LDQ;
+  T* Qg = reinterpret_cast<T*>(p.ops.Qs) + chunk * CP * DKP;
+
+  // ---- Qs = q 2^b (global + LDS), Ks = k 2^-b (fast path), bf16 lo parts
+  if (cs.active) {
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const int r = r0 + u;
-    const bool rv = chv && r < len;
-    const float qv = rv ? to_f32(qg[(size_t)r * Dk + ch]) : 0.f;
-    const float qs = qv * fast_exp2(b[u]);
-    const T qh = from_f32<T>(qs);
-    sQ[r * LDQ + ch] = qh;
-    if (fast) {
-      const float kv = rv ? to_f32(kg[(size_t)r * Dk + ch]) : 0.f;
-      const float ks = kv * fast_exp2(-b[u]);
-      const T kh = from_f32<T>(ks);
-      sK[r * LDQ + ch] = kh;
-      if constexpr (Cfg::SPLIT) {
-        sQl[r * LDQ + ch] = from_f32<T>(qs - to_f32(qh));
-        sKl[r * LDQ + ch] = from_f32<T>(ks - to_f32(kh));
+    for (int u = 0; u < RPS; ++u) {
+      const int r = r0 + u;
+      VT qh, ql, kh, kl;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float qs = cs.qv[u][e] * fast_exp2(cs.b[u][e]);
+        qh[e] = from_f32<T>(qs);
+        ql[e] = from_f32<T>(qs - to_f32(qh[e]));
+        const float ks = fast ? cs.kv[u][e] * fast_exp2(-cs.b[u][e]) : 0.f;
+        kh[e] = from_f32<T>(ks);
+        kl[e] = from_f32<T>(ks - to_f32(kh[e]));
+      }
+      *reinterpret_cast<VT*>(sQ + r * LDQ + c0) = qh;
+      *reinterpret_cast<VT*>(Qg + (size_t)r * DKP + c0) = qh;
+      if (fast) {
+        *reinterpret_cast<VT*>(sK + r * LDQ + c0) = kh;
+        if constexpr (Cfg::SPLIT) {
+          *reinterpret_cast<VT*>(sQl + r * LDQ + c0) = ql;
+          *reinterpret_cast<VT*>(sKl + r * LDQ + c0) = kl;
+        }
       }
     }
   }
   __syncthreads();
-  tile_out<T>(reinterpret_cast<T*>(p.ops.Qs) + chunk * CP * DKP, sQ, CP, DKP, LDQ);
   if constexpr (WANT_QST) tile_out_t<T>(reinterpret_cast<T*>(p.ops.QsT) + chunk * CP * DKP, sQ, CP, DKP, LDQ);
 
-  // ---- intra-chunk scores A
-  T* Ag = reinterpret_cast<T*>(p.ops.A) + chunk * CP * CP;
+  // ---- intra-chunk scores A, kept in registers until the LDS operands are released
   const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  constexpr int NBLK = NB * NB;
+  constexpr int BPW = (NBLK + 3) / 4;        // score blocks per wave
+  f32x4 accA[BPW];
+#pragma unroll
+  for (int s = 0; s < BPW; ++s) accA[s] = zero4();
+  T* sKdT = reinterpret_cast<T*>(smem + Cfg::TILE);
+  T* sA = reinterpret_cast<T*>(smem + Cfg::TILE + Cfg::KDT);
   if (fast) {
-    for (int blk = wave; blk < NB * NB; blk += 4) {
+#pragma unroll
+    for (int s = 0; s < BPW; ++s) {
+      const int blk = wave + 4 * s;
       const int rb = blk / NB, cb = blk % NB;
-      f32x4 acc = zero4();
-      if (cb <= rb) {
+      if (blk < NBLK && cb <= rb) {
 #pragma unroll
         for (int kb = 0; kb < DKP / 32; ++kb) {
           const int oq = (16 * rb + col) * LDQ + 32 * kb + 8 * grp, ok = (16 * cb + col) * LDQ + 32 * kb + 8 * grp;
           const Frag<T> qh = ld8(sQ + oq), kh = ld8(sK + ok);
-          mma(acc, qh, kh);
+          mma(accA[s], qh, kh);
           if constexpr (Cfg::SPLIT) {
-            mma(acc, qh, ld8(sKl + ok));
-            mma(acc, ld8(sQl + oq), kh);
+            mma(accA[s], qh, ld8(sKl + ok));
+            mma(accA[s], ld8(sQl + oq), kh);
           }
         }
       }
+    }
+    __syncthreads();   // score operands released: KdT and A reuse their bytes
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
-        Ag[r * CP + c] = from_f32<T>(c <= r ? acc[e] : 0.f);
+    for (int s = 0; s < BPW; ++s) {
+      const int blk = wave + 4 * s;
+      if (blk < NBLK) {
+        const int rb = blk / NB, cb = blk % NB;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
+          sA[r * LDC + c] = from_f32<T>(c <= r ? accA[s][e] : 0.f);
+        }
       }
     }
   } else {
-    float* sqf = reinterpret_cast<float*>(r2);
+    // safe path scratch lives after sQ
+    float* sqf = reinterpret_cast<float*>(smem + Cfg::TILE);
     float* skf = sqf + CP * 33;
     float* sbs = skf + CP * 33;
     T* sQp = reinterpret_cast<T*>(sbs + CP * 33);
@@ -214,15 +332,17 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(PrepParams p) {
     const int rr = tid >> 4, cc = tid & 15;
     for (int sl = 0; sl < DKP / 32; ++sl) {
       __syncthreads();
-      if (ch >= 32 * sl && ch < 32 * sl + 32) {
+      if (cs.active && c0 >= 32 * sl && c0 < 32 * sl + 32) {
 #pragma unroll
-        for (int u = 0; u < RPT; ++u) sbs[(r0 + u) * 33 + ch - 32 * sl] = b[u];
-      }
-      for (int e = tid; e < CP * 32; e += 256) {
-        const int r = e >> 5, ii = e & 31, c2 = 32 * sl + ii;
-        const bool v = c2 < Dk && r < len;
-        sqf[r * 33 + ii] = v ? to_f32(qg[(size_t)r * Dk + c2]) : 0.f;
-        skf[r * 33 + ii] = v ? to_f32(kg[(size_t)r * Dk + c2]) : 0.f;
+        for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const int r = r0 + u, ii = c0 - 32 * sl + e;
+            sbs[r * 33 + ii] = cs.b[u][e];
+            sqf[r * 33 + ii] = cs.qv[u][e];
+            skf[r * 33 + ii] = cs.kv[u][e];
+          }
+        }
       }
       __syncthreads();
       // diagonal sub-blocks, element by element: exponent b_r - b_c <= 0 for c <= r
@@ -276,6 +396,7 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(PrepParams p) {
         }
       }
     }
+    __syncthreads();   // safe-path scratch released: KdT and A reuse its bytes
 #pragma unroll
     for (int s = 0; s < PPW; ++s) {
       const int pidx = wave + 4 * s;
@@ -283,39 +404,44 @@ __global__ __launch_bounds__(256) void gla_prep_kernel(PrepParams p) {
         int x, y;
         pair_decode(pidx, x, y);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Ag[(16 * x + 4 * grp + e) * CP + 16 * y + col] = from_f32<T>(acc_off[s][e]);
+        for (int e = 0; e < 4; ++e) sA[(16 * x + 4 * grp + e) * LDC + 16 * y + col] = from_f32<T>(acc_off[s][e]);
       }
     }
-    for (int blk = wave; blk < NB * NB; blk += 4) {
+    for (int blk = wave; blk < NBLK; blk += 4) {
       const int rb = blk / NB, cb = blk % NB;
       if (cb > rb) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Ag[(16 * rb + 4 * grp + e) * CP + 16 * cb + col] = from_f32<T>(0.f);
+        for (int e = 0; e < 4; ++e) sA[(16 * rb + 4 * grp + e) * LDC + 16 * cb + col] = from_f32<T>(0.f);
       }
     }
 #pragma unroll
-    for (int x = 0; x < NB; ++x) Ag[(16 * x + rr) * CP + 16 * x + cc] = from_f32<T>(cc <= rr ? acc_d[x] : 0.f);
+    for (int x = 0; x < NB; ++x) sA[(16 * x + rr) * LDC + 16 * x + cc] = from_f32<T>(cc <= rr ? acc_d[x] : 0.f);
   }
-  __syncthreads();
 
-  // ---- KdT = (k 2^{Gamma - b})^T
-  T* sKdT = reinterpret_cast<T*>(r2);
-  const float gam = sGam[ch];
+  // ---- KdT = (k 2^{Gamma - b})^T into LDS
+  if (cs.active) {
 #pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const int r = r0 + u;
-    const float kv = (chv && r < len) ? to_f32(kg[(size_t)r * Dk + ch]) : 0.f;
-    sKdT[ch * LDC + r] = from_f32<T>(kv * fast_exp2(gam - b[u]));
+    for (int e = 0; e < V; ++e) {
+      const float gam = sGam[c0 + e];
+#pragma unroll
+      for (int u = 0; u < RPS; ++u)
+        sKdT[(c0 + e) * LDC + r0 + u] = from_f32<T>(cs.kv[u][e] * fast_exp2(gam - cs.b[u][e]));
+    }
   }
   __syncthreads();
   tile_out<T>(reinterpret_cast<T*>(p.ops.KdT) + chunk * DKP * CP, sKdT, DKP, CP, LDC);
+  tile_out<T>(reinterpret_cast<T*>(p.ops.A) + chunk * CP * CP, sA, CP, CP, LDC);
   if (tid < DKP) p.ops.Gam[chunk * DKP + tid] = sGam[tid];
 }
 
 template <typename T, int DKP, int CP, bool WANT_QST>
 hipError_t launch_prep(const PrepParams& p, int BH, hipStream_t s) {
-  hipLaunchKernelGGL((gla_prep_kernel<T, DKP, CP, WANT_QST>), dim3(p.N, BH), dim3(256), 0, s, p);
-  return hipGetLastError();
+  if constexpr (PrepCfg<T, DKP, CP>::BYTES > kMaxLds) {
+    return hipErrorNotSupported;
+  } else {
+    hipLaunchKernelGGL((gla_prep_kernel<T, DKP, CP, WANT_QST>), dim3(p.N, BH), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
 }
 
 }  // namespace gla

@@ -55,7 +55,7 @@ SHAPES = [
     (1, 2, 64, 128, 64, 64, "bf16", True),      # exactly one chunk
     (2, 2, 90, 48, 32, 16, "f32", True),
     (1, 2, 70, 128, 96, 64, "f32", True),
-    (1, 1, 140, 64, 64, 128, "f32", False),
+    (1, 1, 140, 64, 64, 64, "f32", False),
     (1, 1, 66, 256, 32, 32, "f32", True),
 ]
 
