@@ -1,0 +1,415 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise GLA operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
+
+One step is one pass of the training hot path over one batch of the 340M-layer workload
+(B=8, H=4, L=2048, Dk=128, Dv=256, chunk C=64, bf16 inputs, fp32 accumulation): gla_fwd
+(chunk preparation + state walk) then gla_bwd (chunk preparation, state walks, chunk
+gradients) on inputs already resident in HBM, outputs and workspaces preallocated.  The
+timed region is exactly K steps between two device synchronisations; per-kernel durations
+come from HIP events the library records at its own kernel boundaries on the same stream.
+
+Prints ONE JSON line: tokens/s (B*L per step), % of bf16 MFMA peak at the algorithmic flop
+count, the roofline of the dominant kernel, the fp64 oracle timed on this host's cores on a
+bounded sample, and extra measurements of the other paths (decode step, gated slot
+attention).  Inputs are synthetic and seeded (see workloads/).
+
+Helper mode (summaries of rocprofv3 output, written under profiles/):
+    python bench.py --summarize-stats <kernel_stats.csv> --title T --cmd C --out F
+    python bench.py --summarize-pmc <counter_collection.csv> --kernel K --calib-bytes N ...
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402  (seeded input generators; no operator arithmetic)
+
+PEAK_BF16_FLOPS = 2516.6e12          # 256 CU x 2.4 GHz x 4096 flop/clk (dense bf16 MFMA)
+PEAK_HBM_BYTES = 8.0e12              # HBM3E
+WORKLOAD = "gla_340m"
+METRIC = "GLA fwd+bwd tokens/s and % bf16 MFMA peak at H=4 Dk=128 Dv=256 L=2048"
+CSRC = os.path.join(ROOT, "linear_recurrent_sequence_gla_amd", "csrc")
+PMC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+# ----------------------------------------------------------------------------- accounting
+def algorithmic(B, H, L, Dk, Dv, C, s=2):
+    """Algorithmic flops and bytes of one forward and one backward (per token-head figures,
+    times B*H*L token-heads).  Flops: the causal intra-chunk block incl. the diagonal, the
+    inter-chunk output and the state update (forward); three times the intra work on the key
+    side, twice on the value side, plus 10 Dk Dv (state recompute, reverse state pass and the
+    inter-chunk gradient products) for the backward.  Bytes: each operator input and output
+    once (q, k, g, v read, o written; + do read, dq, dk, dv written, dg written in fp32)."""
+    u = B * H * L
+    ff = (C + 1) * (Dk + Dv) + 4 * Dk * Dv
+    fb = 3 * (C + 1) * Dk + 2 * (C + 1) * Dv + 10 * Dk * Dv
+    bf = s * (3 * Dk + 2 * Dv)
+    bb = s * (3 * Dk + 2 * Dv) + s * (2 * Dk + Dv) + 4 * Dk
+    return {"flops_fwd": u * ff, "flops_bwd": u * fb, "bytes_fwd": u * bf, "bytes_bwd": u * bb,
+            "units": u}
+
+
+def kernel_alg_bytes(B, H, L, Dk, Dv, s=2):
+    """Per-launch algorithmic bytes of each kernel: the operator tensors it reads or writes,
+    each counted once (per token-head figure x B*H*L).  Workspace traffic is design overhead
+    and is not counted here (it shows up in the measured HBM traffic)."""
+    u = B * H * L
+    return {
+        "fwd.prep": u * s * 3 * Dk,                            # q, k, g
+        "fwd.walk": u * s * 2 * Dv,                            # v in, o out
+        "bwd.prep": u * s * 3 * Dk,                            # q, k, g
+        "bwd.walk": u * s * 2 * Dv,                            # v, do
+        "bwd.chunk": u * (s * (3 * Dk + 2 * Dv) + s * (2 * Dk + Dv) + 4 * Dk),  # all but h0/dh0
+        "bwd.dv": u * s * 2 * Dv,                              # do in, dv out
+    }
+
+
+def csrc_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def _oracle_row(args):
+    """fwd + bwd of the fp64 oracle on one batch row (all heads, full length)."""
+    q, k, v, g, do = args
+    from oracle import gla_recurrent_bwd, gla_recurrent_fwd
+    t0 = time.perf_counter()
+    gla_recurrent_fwd(q, k, v, g)
+    gla_recurrent_bwd(q, k, v, g, do)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(x, B, L, max_workers=8):
+    """The oracle as it stands, on this host's cores: one worker process per batch row of the
+    same 340M-shape batch, one BLAS/OpenMP thread each.  Returns tokens/s of that batch."""
+    import multiprocessing as mp
+    workers = max(1, min(max_workers, B, len(os.sched_getaffinity(0))))
+    rows = [tuple(x[n][b:b + 1] for n in ("q", "k", "v", "g", "do")) for b in range(B)]
+    saved = {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for v in saved:
+        os.environ[v] = "1"
+    try:
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(workers) as pool:
+            pool.map(_oracle_row, rows[:workers])            # warm the workers (imports)
+            t0 = time.perf_counter()
+            per = pool.map(_oracle_row, rows)
+            wall = time.perf_counter() - t0
+    finally:
+        for v, val in saved.items():
+            if val is None:
+                os.environ.pop(v, None)
+            else:
+                os.environ[v] = val
+    return {"value": B * L / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"the full 340M-shape batch (B={B}, H=4, L={L}) fwd+bwd, one process per batch "
+                      f"row on {workers} cores, fp64 NumPy, wall {wall:.1f} s "
+                      f"(one row on one core: {np.mean(per):.1f} s)"}
+
+
+# ----------------------------------------------------------------------------- GPU legs
+def _events(torch, n):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()                                           # created on first record
+    return evs
+
+
+def _handles(evs):
+    import ctypes
+    arr = (ctypes.c_void_p * len(evs))(*[e.cuda_event for e in evs])
+    return arr
+
+
+def run_gla(torch, m, steps, warmup):
+    w = W.WORKLOADS[WORKLOAD]
+    B, H, L, Dk, Dv, C = w.B, w.H, w.L, w.Dk, w.Dv, w.C
+    x = W.gla_inputs(w)
+    dt = torch.bfloat16
+    d = {n: torch.from_numpy(x[n]).to("cuda", dt).contiguous() for n in ("q", "k", "v", "g", "do")}
+    o = torch.empty(B, H, L, Dv, device="cuda", dtype=dt)
+    ht = torch.empty(B, H, Dk, Dv, device="cuda", dtype=torch.float32)
+    dq = torch.empty(B, H, L, Dk, device="cuda", dtype=dt)
+    dk = torch.empty_like(dq)
+    dv = torch.empty(B, H, L, Dv, device="cuda", dtype=dt)
+    dg = torch.empty(B, H, L, Dk, device="cuda", dtype=torch.float32)
+    lib = m.lib()
+    wsf = torch.empty(lib.gla_fwd_workspace_bytes(B, H, L, Dk, Dv, C, 1), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(lib.gla_bwd_workspace_bytes(B, H, L, Dk, Dv, C, 1), dtype=torch.uint8, device="cuda")
+    nb = lib.gla_bwd_launch_count(B, H, L, Dk, Dv, C, 1)
+    P = lambda t: None if t is None else __import__("ctypes").c_void_p(t.data_ptr())
+    stream = __import__("ctypes").c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step(evf=None, evb=None):
+        if evf is None:
+            m._check(lib.gla_fwd(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(o), P(ht),
+                                 B, H, L, Dk, Dv, C, 1, P(wsf), wsf.numel(), stream))
+            m._check(lib.gla_bwd(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(d["do"]), None,
+                                 P(dq), P(dk), P(dv), P(dg), None, B, H, L, Dk, Dv, C, 1, P(wsb), wsb.numel(),
+                                 stream))
+        else:
+            m._check(lib.gla_fwd_profiled(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(o), P(ht),
+                                          B, H, L, Dk, Dv, C, 1, P(wsf), wsf.numel(), stream, evf, 3))
+            m._check(lib.gla_bwd_profiled(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(d["do"]), None,
+                                          P(dq), P(dk), P(dv), P(dg), None, B, H, L, Dk, Dv, C, 1, P(wsb),
+                                          wsb.numel(), stream, evb, 5))
+
+    for _ in range(warmup):
+        step()
+    ef = [_events(torch, 3) for _ in range(steps)]
+    eb = [_events(torch, 5) for _ in range(steps)]
+    hf = [_handles(e) for e in ef]
+    hb = [_handles(e) for e in eb]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(steps):
+        step(hf[k], hb[k])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    names_f = ["fwd.prep", "fwd.walk"]
+    names_b = ["bwd.prep", "bwd.walk", "bwd.chunk", "bwd.dv"][:nb]
+    kt = {}
+    for i, nme in enumerate(names_f):
+        kt[nme] = float(np.mean([ef[k][i].elapsed_time(ef[k][i + 1]) for k in range(steps)]))
+    for i, nme in enumerate(names_b):
+        kt[nme] = float(np.mean([eb[k][i].elapsed_time(eb[k][i + 1]) for k in range(steps)]))
+    return {"w": w, "x": x, "ms": ms, "kernel_ms": kt}
+
+
+def run_decode(torch, m, steps=256):
+    """Back-to-back decode steps on the decode workload (B=64, H=4, Dk=128, Dv=256)."""
+    w = W.WORKLOADS["decode"]
+    T = min(steps, w.T)
+    dd = W.decode_inputs(w, T=T)
+    dt = torch.bfloat16
+    qs = torch.from_numpy(dd["q"]).to("cuda", dt)
+    ks = torch.from_numpy(dd["k"]).to("cuda", dt)
+    vs = torch.from_numpy(dd["v"]).to("cuda", dt)
+    gs = torch.from_numpy(dd["g"]).to("cuda", dt)
+    state = torch.from_numpy(dd["state"]).to("cuda")
+    o = torch.empty(w.B, w.H, w.Dv, device="cuda", dtype=dt)
+    for t in range(8):
+        m.gla_decode_step(qs[t], ks[t], vs[t], gs[t], state, out=o)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for t in range(T):
+        m.gla_decode_step(qs[t], ks[t], vs[t], gs[t], state, out=o)
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1e3 / T
+    BH = w.B * w.H
+    nbytes = BH * (2 * w.Dk * w.Dv * 4 + 2 * (3 * w.Dk + 2 * w.Dv))   # state in+out, q k g v o
+    return {"workload": f"decode B={w.B} H={w.H} Dk={w.Dk} Dv={w.Dv} fp32 state, {T} steps back to back",
+            "us_per_step": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
+            "frac_hbm": round(nbytes / us / 1e3 / (PEAK_HBM_BYTES / 1e9), 4),
+            "note": "the 33.6 MB state fits the 256 MB Infinity Cache, so back-to-back steps can "
+                    "exceed what HBM alone would give"}
+
+
+def run_gsa(torch, m, steps=10, warmup=3):
+    w = W.WORKLOADS["gsa_340m"]
+    lib = m.lib()
+    if lib.gsa_fwd_workspace_bytes(w.B, w.H, w.L, w.Dk, w.Dv, w.m, w.C, 1) == 0:
+        return None
+    x = W.gsa_inputs(w)
+    dt = torch.bfloat16
+    d = {n: torch.from_numpy(x[n]).to("cuda", dt).contiguous() for n in ("q", "k", "v", "g", "do")}
+    for _ in range(warmup):
+        m.gsa_fwd(d["q"], d["k"], d["v"], d["g"], C=w.C)
+        m.gsa_bwd(d["q"], d["k"], d["v"], d["g"], d["do"], C=w.C)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        m.gsa_fwd(d["q"], d["k"], d["v"], d["g"], C=w.C)
+        m.gsa_bwd(d["q"], d["k"], d["v"], d["g"], d["do"], C=w.C)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    return {"workload": f"gsa B={w.B} H={w.H} L={w.L} Dk={w.Dk} Dv={w.Dv} m={w.m} C={w.C} fwd+bwd",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / ms * 1e3, 1)}
+
+
+# ----------------------------------------------------------------------------- summaries
+def summarize_stats(path, title, cmd, out):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    lines = [f"# {title}", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | calls | avg (us) | total (us) | % |", "|---|---|---|---|---|"]
+    for r in rows:
+        nm = r["Name"]
+        short = nm.split("(")[0]
+        if len(short) > 70:
+            short = short[:70] + "..."
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['TotalDurationNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def summarize_pmc(paths, kernel_sub, calib_sub, calib_bytes, cmd, out_json, out_md):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the kernels whose name contains kernel_sub,
+    scaled by what the same counters read for a copy kernel of known size (calib_sub)."""
+    import csv
+    vals = {}
+    for p in paths:
+        for r in csv.DictReader(open(p)):
+            name, ctr, v = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+            key = "kernel" if kernel_sub in name else ("calib" if calib_sub in name else None)
+            if key:
+                vals.setdefault((key, ctr), []).append(v)
+    res = {}
+    for ctr, label in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
+        kk = vals.get(("kernel", ctr))
+        cc = vals.get(("calib", ctr))
+        if not kk or not cc:
+            continue
+        factor = calib_bytes / (np.median(cc) * 1024.0)       # known bytes / counted bytes
+        res[label] = {"kib_per_dispatch": float(np.median(kk)), "calib_kib": float(np.median(cc)),
+                      "scale": float(factor), "bytes": float(np.median(kk) * 1024.0 * factor)}
+    summary = {"kernel": kernel_sub, "csrc_hash": csrc_hash(), "command": cmd, **res}
+    if "read" in res and "write" in res:
+        summary["traffic_bytes"] = res["read"]["bytes"] + res["write"]["bytes"]
+    json.dump(summary, open(out_json, "w"), indent=1)
+    lines = [f"# HBM traffic of `{kernel_sub}` (rocprofv3 counters)", "", "Commands:", "", "```", cmd, "```", "",
+             f"Copy calibration: a plain device copy of {calib_bytes / 1e6:.1f} MB read + write.", "",
+             "| counter | KiB/dispatch | copy KiB | scale | bytes/dispatch |", "|---|---|---|---|---|"]
+    for label, r in res.items():
+        lines.append(f"| {label} | {r['kib_per_dispatch']:.0f} | {r['calib_kib']:.0f} | {r['scale']:.3f} | "
+                     f"{r['bytes'] / 1e6:.1f} MB |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def traffic_for(kernel):
+    """Counter-measured HBM bytes per launch of `kernel`, if taken on the current sources."""
+    try:
+        s = json.load(open(PMC_FILE))
+    except (OSError, ValueError):
+        return None
+    if s.get("kernel") != kernel or s.get("csrc_hash") != csrc_hash():
+        return None
+    return s.get("traffic_bytes")
+
+
+KERNEL_SYMBOLS = {"fwd.prep": "gla_prep_kernel", "fwd.walk": "gla_fwd_walk", "bwd.prep": "gla_prep_kernel",
+                  "bwd.walk": "gla_bwd_walk", "bwd.chunk": "gla_bwd_chunk", "bwd.dv": "gla_bwd_dv"}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--copy-calib-mb", type=float, default=0.0,
+                    help="also run one plain device copy of this many MB (counter calibration)")
+    ap.add_argument("--summarize-stats")
+    ap.add_argument("--summarize-pmc", nargs="+")
+    ap.add_argument("--title", default="")
+    ap.add_argument("--cmd", default="")
+    ap.add_argument("--out", default="")
+    ap.add_argument("--out-json", default="")
+    ap.add_argument("--kernel", default="gla_bwd_walk")
+    ap.add_argument("--calib-kernel", default="copy")
+    ap.add_argument("--calib-bytes", type=float, default=0.0)
+    args = ap.parse_args()
+
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.title, args.cmd, args.out)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.kernel, args.calib_kernel, args.calib_bytes, args.cmd,
+                      args.out_json, args.out)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the operator's work is per batch-row and head and "
+              f"needs no communication); --gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_recurrent_sequence_gla_amd as m
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    m.lib()
+
+    if args.copy_calib_mb > 0:
+        nb = int(args.copy_calib_mb * 1e6) // 16 * 16
+        a = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    r = run_gla(torch, m, args.steps, args.warmup)
+    w = r["w"]
+    B, H, L, Dk, Dv, C = w.B, w.H, w.L, w.Dk, w.Dv, w.C
+    alg = algorithmic(B, H, L, Dk, Dv, C)
+    ms = r["ms"]
+    flops = alg["flops_fwd"] + alg["flops_bwd"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    kt = r["kernel_ms"]
+    dom = max(kt, key=kt.get)
+    kb = kernel_alg_bytes(B, H, L, Dk, Dv)[dom]
+    achieved = kb / (kt[dom] * 1e-3) / 1e9
+    traffic = traffic_for(KERNEL_SYMBOLS[dom])
+    out = {
+        "metric": METRIC,
+        "value": round(B * L / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: GLA fwd+bwd, B={B} H={H} L={L} Dk={Dk} Dv={Dv} C={C}, bf16 "
+                               "inputs, fp32 accumulation, no initial state",
+                   "B": B, "H": H, "L": L, "Dk": Dk, "Dv": Dv, "C": C},
+        "pct_bf16_mfma_peak": round(100 * tflops * 1e12 / PEAK_BF16_FLOPS, 3),
+        "tflops": round(tflops, 3),
+        "pct_hbm_roofline_step": round(100 * (alg["bytes_fwd"] + alg["bytes_bwd"]) / (ms * 1e-3) / PEAK_HBM_BYTES, 3),
+        "kernel_us": {k: round(v * 1e3, 2) for k, v in kt.items()},
+        "roofline": {"kernel": KERNEL_SYMBOLS[dom] + f" ({dom})", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s", "frac": round(achieved / (PEAK_HBM_BYTES / 1e9), 4),
+                     "traffic": traffic},
+    }
+    if not args.no_extras:
+        ex = {"decode": run_decode(torch, m)}
+        g = run_gsa(torch, m)
+        if g is not None:
+            ex["gsa"] = g
+        out["extras"] = ex
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(r["x"], B, L)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

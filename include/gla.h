@@ -105,6 +105,26 @@ int gla_bwd(const void* q, const void* k, const void* v, const void* g, const fl
             int B, int H, int L, int Dk, int Dv, int C, int dtype,
             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- profiling ------------
+ * Same as gla_fwd / gla_bwd, and additionally records caller-created hipEvent_t handles on
+ * `stream` at kernel boundaries: events[0] before the first kernel, events[i] after the i-th
+ * (gla_fwd launches 2 kernels: chunk preparation, state walk; gla_bwd launches
+ * gla_bwd_launch_count() kernels: chunk preparation, state walk, chunk gradients, and a
+ * value-gradient kernel when the key width is split).  nevents must be at least 3 (forward)
+ * or 5 (backward), else GLA_ERR_NULL_ARG.  The events are owned by the caller and are only
+ * recorded, never created, synchronised or destroyed.  Used to time individual kernels. */
+int gla_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                     void* o, float* ht,
+                     int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream, void** events, int nevents);
+int gla_bwd_profiled(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                     const void* do_, const float* dht,
+                     void* dq, void* dk, void* dv, float* dg, float* dh0,
+                     int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream, void** events, int nevents);
+/* Number of kernels gla_bwd launches for these sizes (0 if unsupported). */
+int gla_bwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype);
+
 /* ---------------------------------------------------------------- GLA decode -----------
  * One recurrent inference step per (batch, head): the O(1)-memory form of the recurrence
  * (MS-GLA summary, section 1; GSA abstract: efficient recurrent inference).

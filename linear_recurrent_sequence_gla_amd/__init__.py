@@ -45,6 +45,9 @@ _SIGS = {
     "gla_fwd": (_I, [_P] * 7 + [_I] * 7 + [_P, _Z, _P]),
     "gla_bwd_workspace_bytes": (_Z, [_I] * 7),
     "gla_bwd": (_I, [_P] * 12 + [_I] * 7 + [_P, _Z, _P]),
+    "gla_fwd_profiled": (_I, [_P] * 7 + [_I] * 7 + [_P, _Z, _P, _P, _I]),
+    "gla_bwd_profiled": (_I, [_P] * 12 + [_I] * 7 + [_P, _Z, _P, _P, _I]),
+    "gla_bwd_launch_count": (_I, [_I] * 7),
     "gla_decode_step": (_I, [_P] * 6 + [_I] * 5 + [_P]),
     "gsa_fwd_workspace_bytes": (_Z, [_I] * 8),
     "gsa_fwd": (_I, [_P] * 9 + [_I] * 8 + [_P, _Z, _P]),

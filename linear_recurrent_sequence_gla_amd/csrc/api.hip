@@ -176,9 +176,19 @@ size_t gla_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int d
   return fwd_ws_bytes(B, H, L, Dk, Dv, C, dtype);
 }
 
-int gla_fwd(const void* q, const void* k, const void* v, const void* g, const float* h0,
-            void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype,
-            void* workspace, size_t workspace_bytes, void* stream) {
+size_t gla_bwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
+  if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return 0;
+  return bwd_layout(B, H, L, Dk, Dv, C, dtype).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(const void* q, const void* k, const void* v, const void* g, const float* h0,
+             void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+             void* workspace, size_t workspace_bytes, void* stream, LaunchEvents ev) {
   int st = check_dims(B, H, L, Dk, Dv, C, dtype);
   if (st != GLA_OK) return st;
   if (!q || !k || !v || !g || !o) return GLA_ERR_NULL_ARG;
@@ -196,20 +206,15 @@ int gla_fwd(const void* q, const void* k, const void* v, const void* g, const fl
   p.q = q; p.k = k; p.v = v; p.g = g; p.h0 = h0; p.o = o; p.ht = ht;
   p.BH = (int)BH; p.L = L; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
   p.ops = carve_ops(static_cast<char*>(workspace), ops_layout(BH, N, CP, DKP, es, false), false);
+  p.events = ev;
   if (dispatch_fwd(dtype, DKP, CP, p, static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
 }
 
-size_t gla_bwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
-  if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
-  if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return 0;
-  return bwd_layout(B, H, L, Dk, Dv, C, dtype).total;
-}
-
-int gla_bwd(const void* q, const void* k, const void* v, const void* g, const float* h0,
-            const void* do_, const float* dht, void* dq, void* dk, void* dv, float* dg,
-            float* dh0, int B, int H, int L, int Dk, int Dv, int C, int dtype,
-            void* workspace, size_t workspace_bytes, void* stream) {
+int bwd_impl(const void* q, const void* k, const void* v, const void* g, const float* h0,
+             const void* do_, const float* dht, void* dq, void* dk, void* dv, float* dg,
+             float* dh0, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+             void* workspace, size_t workspace_bytes, void* stream, LaunchEvents ev) {
   int st = check_dims(B, H, L, Dk, Dv, C, dtype);
   if (st != GLA_OK) return st;
   if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return GLA_ERR_UNSUPPORTED;
@@ -234,8 +239,50 @@ int gla_bwd(const void* q, const void* k, const void* v, const void* g, const fl
   p.Hs = ws + lay.hs;
   p.dHs = ws + lay.dhs;
   p.carry = reinterpret_cast<float*>(ws + lay.carry);
+  p.events = ev;
   if (dispatch_bwd(dtype, DKP, CP, p, static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gla_fwd(const void* q, const void* k, const void* v, const void* g, const float* h0,
+            void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(q, k, v, g, h0, o, ht, B, H, L, Dk, Dv, C, dtype, workspace, workspace_bytes, stream,
+                  LaunchEvents{nullptr, 0});
+}
+
+int gla_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                     void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream, void** events, int nevents) {
+  if (!events || nevents < GLA_FWD_LAUNCHES + 1) return GLA_ERR_NULL_ARG;
+  return fwd_impl(q, k, v, g, h0, o, ht, B, H, L, Dk, Dv, C, dtype, workspace, workspace_bytes, stream,
+                  LaunchEvents{events, nevents});
+}
+
+int gla_bwd(const void* q, const void* k, const void* v, const void* g, const float* h0,
+            const void* do_, const float* dht, void* dq, void* dk, void* dv, float* dg,
+            float* dh0, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, g, h0, do_, dht, dq, dk, dv, dg, dh0, B, H, L, Dk, Dv, C, dtype, workspace,
+                  workspace_bytes, stream, LaunchEvents{nullptr, 0});
+}
+
+int gla_bwd_profiled(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                     const void* do_, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                     float* dh0, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream, void** events, int nevents) {
+  if (!events || nevents < GLA_BWD_MAX_LAUNCHES + 1) return GLA_ERR_NULL_ARG;
+  return bwd_impl(q, k, v, g, h0, do_, dht, dq, dk, dv, dg, dh0, B, H, L, Dk, Dv, C, dtype, workspace,
+                  workspace_bytes, stream, LaunchEvents{events, nevents});
+}
+
+int gla_bwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
+  return bwd_launch_count(esize_of(dtype), pad_dk(Dk), pad_c(C));
 }
 
 int gla_decode_step(const void* q, const void* k, const void* v, const void* g, float* state,

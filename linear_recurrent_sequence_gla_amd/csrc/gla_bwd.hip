@@ -764,20 +764,41 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
     return hipErrorNotSupported;
   } else {
     PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N};
+    record_event(p.events, 0, s);
     hipError_t e = launch_prep<T, DKP, CP, true>(pp, p.BH, s);
     if (e != hipSuccess) return e;
+    record_event(p.events, 1, s);
     const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
     hipLaunchKernelGGL((gla_bwd_walk<T, DKP, CP>), dim3(ntile * p.BH), dim3(256), 0, s, p, ntile);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    record_event(p.events, 2, s);
     hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED>), dim3(p.N, p.BH, DKP / P::DKS), dim3(256), 0, s,
                        p, DKP, ntile);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    record_event(p.events, 3, s);
     if constexpr (!P::FUSED) {
       hipLaunchKernelGGL((gla_bwd_dv<T, DKP, CP>), dim3(p.N, p.BH, ntile), dim3(256), 0, s, p, ntile);
       if ((e = hipGetLastError()) != hipSuccess) return e;
+      record_event(p.events, 4, s);
     }
     return hipSuccess;
   }
+}
+
+int bwd_launch_count(int esize, int DKP, int CP) {
+  int c = 0;
+#define GLA_BCNT_CASE(TT, D, C_) \
+  if (esize == (int)sizeof(TT) && DKP == D && CP == C_) c = BwdPlan<TT, D, C_>::FUSED ? 3 : 4;
+#define GLA_BCNT_ALL(TT)                                                                 \
+  GLA_BCNT_CASE(TT, 32, 32) GLA_BCNT_CASE(TT, 32, 64) GLA_BCNT_CASE(TT, 32, 128)           \
+  GLA_BCNT_CASE(TT, 64, 32) GLA_BCNT_CASE(TT, 64, 64) GLA_BCNT_CASE(TT, 64, 128)           \
+  GLA_BCNT_CASE(TT, 128, 32) GLA_BCNT_CASE(TT, 128, 64) GLA_BCNT_CASE(TT, 128, 128)        \
+  GLA_BCNT_CASE(TT, 256, 32) GLA_BCNT_CASE(TT, 256, 64)
+  GLA_BCNT_ALL(bf16)
+  GLA_BCNT_ALL(float)
+#undef GLA_BCNT_ALL
+#undef GLA_BCNT_CASE
+  return c;
 }
 
 bool bwd_config_fits(int esize, int DKP, int CP) {

@@ -223,10 +223,13 @@ hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
     return hipErrorNotSupported;
   } else {
     PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N};
+    record_event(p.events, 0, s);
     hipError_t e = launch_prep<T, DKP, CP, false>(pp, p.BH, s);
     if (e != hipSuccess) return e;
+    record_event(p.events, 1, s);
     const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
     hipLaunchKernelGGL((gla_fwd_walk<T, DKP, CP>), dim3(ntile * p.BH), dim3(256), 0, s, p, ntile);
+    record_event(p.events, 2, s);
     return hipGetLastError();
   }
 }

@@ -15,6 +15,16 @@ struct ChunkOps {
   float* Gam;   // [BH][N][DKP]      chunk log2-decay Gamma (f32)
 };
 
+// Optional launch-boundary events (profiling): events[0] is recorded before the first
+// kernel and events[i] after the i-th kernel, on the launch stream; nullptr = none.
+struct LaunchEvents {
+  void** ev;
+  int n;
+};
+inline void record_event(const LaunchEvents& e, int i, hipStream_t s) {
+  if (e.ev && i < e.n && e.ev[i]) (void)hipEventRecord(static_cast<hipEvent_t>(e.ev[i]), s);
+}
+
 struct FwdParams {
   const void *q, *k, *v, *g;
   const float* h0;
@@ -22,6 +32,7 @@ struct FwdParams {
   float* ht;
   int BH, L, Dk, Dv, C, N;
   ChunkOps ops;
+  LaunchEvents events;
 };
 
 struct BwdParams {
@@ -33,7 +44,8 @@ struct BwdParams {
   ChunkOps ops;
   void* Hs;       // [BH][N][DKP][DvP] state at chunk starts (T)
   void* dHs;      // [BH][N][DKP][DvP] state gradient at chunk ends (T)
-  float* carry;   // [BH][N][NT][DKP]  partial sum_j dH*H at chunk ends, per Dv tile
+  float* carry;   // [BH][N][NT][DKP]  partial Z_n = 2^Gamma sum_j dH_{n+1} H_n, per Dv tile
+  LaunchEvents events;
 };
 
 struct DecodeParams {
@@ -57,6 +69,11 @@ template <typename T>
 hipError_t launch_gla_decode(const DecodeParams& p, hipStream_t s);
 
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
+
+// Kernel launches per call (for the profiled entry points).
+constexpr int GLA_FWD_LAUNCHES = 2;
+constexpr int GLA_BWD_MAX_LAUNCHES = 4;
+int bwd_launch_count(int esize, int DKP, int CP);
 
 // Whether every kernel of the forward fits the LDS of a CU for this (dtype size, DKP, CP).
 bool fwd_config_fits(int esize, int DKP, int CP);

@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is launched).
+
+Every call here fails validation before any launch, so it runs without a GPU: the library
+loads, exports every symbol include/gla.h declares, returns the documented status codes, and
+computes workspace sizes.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    m = pytest.importorskip("linear_recurrent_sequence_gla_amd")
+    if not os.path.exists(m.lib_path):
+        pytest.skip("library not built")
+    return m.lib()
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "gla.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\*|int|size_t)\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    import linear_recurrent_sequence_gla_amd as m
+    syms = header_symbols()
+    assert len(syms) >= 12, syms
+    for s in syms:
+        assert hasattr(lib, s), f"{s} declared in gla.h but not exported"
+    assert set(syms) == set(m.EXPORTED_SYMBOLS), (set(syms) ^ set(m.EXPORTED_SYMBOLS))
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gla_abi_version() >= 1
+    for code in range(8):
+        s = lib.gla_status_str(code).decode()
+        assert s.startswith("GLA_"), s
+    assert lib.gla_status_str(99).decode() == "unknown status"
+
+
+NOP = [None] * 7
+
+
+def fwd(lib, B=1, H=1, L=64, Dk=16, Dv=16, C=16, dt=1, ptrs=None, ws=None, wsb=0):
+    p = ptrs if ptrs is not None else NOP
+    return lib.gla_fwd(*p, B, H, L, Dk, Dv, C, dt, ws, wsb, None)
+
+
+def test_dtype_shape_unsupported(lib):
+    assert fwd(lib, dt=5) == 3                        # GLA_ERR_DTYPE
+    assert fwd(lib, L=0) == 2                         # GLA_ERR_SHAPE
+    assert fwd(lib, B=0) == 2
+    assert fwd(lib, C=48) == 4                        # GLA_ERR_UNSUPPORTED
+    assert fwd(lib, Dk=24) == 4
+    assert fwd(lib, Dk=512) == 4
+    assert fwd(lib, Dv=520) == 4
+    assert fwd(lib, Dk=256, C=128) == 4               # LDS limit (bf16)
+    assert fwd(lib, Dk=64, C=128, dt=0) == 4          # LDS limit (fp32)
+    assert fwd(lib, B=70000) == 4                     # grid limit
+
+
+def test_null_workspace_alias(lib):
+    a = ctypes.c_void_p(0x10000000)
+    b = ctypes.c_void_p(0x20000000)
+    assert fwd(lib) == 1                              # NULL pointers
+    ptrs = [a, ctypes.c_void_p(0x11000000), ctypes.c_void_p(0x12000000), ctypes.c_void_p(0x13000000), None, b, None]
+    need = lib.gla_fwd_workspace_bytes(1, 1, 64, 16, 16, 16, 1)
+    assert need > 0
+    assert fwd(lib, ptrs=ptrs, ws=None, wsb=0) == 5   # no workspace
+    assert fwd(lib, ptrs=ptrs, ws=ctypes.c_void_p(0x30000000), wsb=need - 1) == 5
+    alias = list(ptrs)
+    alias[5] = ctypes.c_void_p(0x10000000 + 64)       # o overlaps q
+    assert fwd(lib, ptrs=alias, ws=ctypes.c_void_p(0x30000000), wsb=need) == 6
+    wsalias = ctypes.c_void_p(0x20000000 + 32)        # workspace overlaps o
+    assert fwd(lib, ptrs=ptrs, ws=wsalias, wsb=need) == 6
+    mis = list(ptrs)
+    mis[0] = ctypes.c_void_p(0x10000000 + 2)          # misaligned q
+    assert fwd(lib, ptrs=mis, ws=ctypes.c_void_p(0x30000000), wsb=need) == 4
+
+
+def test_workspace_sizes(lib):
+    # forward: Qs, KdT (C x Dk each, bf16), A (C x C), Gamma (fp32) per chunk, 256-byte aligned
+    B, H, L, Dk, Dv, C = 8, 4, 2048, 128, 256, 64
+    N = L // C
+    expect = 2 * (B * H * N * C * Dk * 2) + B * H * N * C * C * 2 + B * H * N * Dk * 4
+    assert lib.gla_fwd_workspace_bytes(B, H, L, Dk, Dv, C, 1) == expect
+    assert lib.gla_bwd_workspace_bytes(B, H, L, Dk, Dv, C, 1) > expect
+    assert lib.gla_fwd_workspace_bytes(1, 1, 64, 16, 16, 48, 1) == 0
+    assert lib.gla_bwd_launch_count(B, H, L, Dk, Dv, C, 1) == 3
+    assert lib.gla_bwd_launch_count(4, 4, 4096, 256, 512, 64, 1) == 4
+
+
+def test_decode_validation(lib):
+    assert lib.gla_decode_step(*[None] * 6, 1, 1, 16, 16, 7, None) == 3
+    assert lib.gla_decode_step(*[None] * 6, 1, 1, 16, 16, 1, None) == 1
+    assert lib.gla_decode_step(*[None] * 6, 1, 1, 20, 16, 1, None) == 4
+    p = [ctypes.c_void_p(0x10000000 + i * 0x1000000) for i in range(6)]
+    p[5] = ctypes.c_void_p(0x10000000 + 16)             # o overlaps q
+    assert lib.gla_decode_step(*p, 1, 1, 16, 16, 1, None) == 6
+
+
+def test_profiled_needs_events(lib):
+    assert lib.gla_fwd_profiled(*NOP, 1, 1, 64, 16, 16, 16, 1, None, 0, None, None, 0) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    import linear_recurrent_sequence_gla_amd as m
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "lib_path", "/nonexistent/libgla_amd.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        m.lib()
