@@ -71,7 +71,8 @@ def kernel_alg_bytes(B, H, L, Dk, Dv, s=2):
         "fwd.prep": u * s * 3 * Dk,                            # q, k, g
         "fwd.walk": u * s * 2 * Dv,                            # v in, o out
         "bwd.prep": u * s * 3 * Dk,                            # q, k, g
-        "bwd.walk": u * s * 2 * Dv,                            # v, do
+        "bwd.walk_fwd": u * s * Dv,                            # v
+        "bwd.walk_rev": u * s * Dv,                            # do
         "bwd.chunk": u * (s * (3 * Dk + 2 * Dv) + s * (2 * Dk + Dv) + 4 * Dk),  # all but h0/dh0
         "bwd.dv": u * s * 2 * Dv,                              # do in, dv out
     }
@@ -170,12 +171,12 @@ def run_gla(torch, m, steps, warmup):
                                           B, H, L, Dk, Dv, C, 1, P(wsf), wsf.numel(), stream, evf, 3))
             m._check(lib.gla_bwd_profiled(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(d["do"]), None,
                                           P(dq), P(dk), P(dv), P(dg), None, B, H, L, Dk, Dv, C, 1, P(wsb),
-                                          wsb.numel(), stream, evb, 5))
+                                          wsb.numel(), stream, evb, 6))
 
     for _ in range(warmup):
         step()
     ef = [_events(torch, 3) for _ in range(steps)]
-    eb = [_events(torch, 5) for _ in range(steps)]
+    eb = [_events(torch, 6) for _ in range(steps)]
     hf = [_handles(e) for e in ef]
     hb = [_handles(e) for e in eb]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -187,7 +188,7 @@ def run_gla(torch, m, steps, warmup):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     names_f = ["fwd.prep", "fwd.walk"]
-    names_b = ["bwd.prep", "bwd.walk", "bwd.chunk", "bwd.dv"][:nb]
+    names_b = ["bwd.prep", "bwd.walk_fwd", "bwd.walk_rev", "bwd.chunk", "bwd.dv"][:nb]
     kt = {}
     for i, nme in enumerate(names_f):
         kt[nme] = float(np.mean([ef[k][i].elapsed_time(ef[k][i + 1]) for k in range(steps)]))
@@ -312,7 +313,8 @@ def traffic_for(kernel):
 
 
 KERNEL_SYMBOLS = {"fwd.prep": "gla_prep_kernel", "fwd.walk": "gla_fwd_walk", "bwd.prep": "gla_prep_kernel",
-                  "bwd.walk": "gla_bwd_walk", "bwd.chunk": "gla_bwd_chunk", "bwd.dv": "gla_bwd_dv"}
+                  "bwd.walk_fwd": "walk_store", "bwd.walk_rev": "walk_reverse", "bwd.chunk": "gla_bwd_chunk",
+                  "bwd.dv": "gla_bwd_dv"}
 
 
 # ----------------------------------------------------------------------------- main
@@ -331,7 +333,7 @@ def main():
     ap.add_argument("--cmd", default="")
     ap.add_argument("--out", default="")
     ap.add_argument("--out-json", default="")
-    ap.add_argument("--kernel", default="gla_bwd_walk")
+    ap.add_argument("--kernel", default="walk_reverse")
     ap.add_argument("--calib-kernel", default="copy")
     ap.add_argument("--calib-bytes", type=float, default=0.0)
     args = ap.parse_args()

@@ -109,9 +109,9 @@ int gla_bwd(const void* q, const void* k, const void* v, const void* g, const fl
  * Same as gla_fwd / gla_bwd, and additionally records caller-created hipEvent_t handles on
  * `stream` at kernel boundaries: events[0] before the first kernel, events[i] after the i-th
  * (gla_fwd launches 2 kernels: chunk preparation, state walk; gla_bwd launches
- * gla_bwd_launch_count() kernels: chunk preparation, state walk, chunk gradients, and a
- * value-gradient kernel when the key width is split).  nevents must be at least 3 (forward)
- * or 5 (backward), else GLA_ERR_NULL_ARG.  The events are owned by the caller and are only
+ * gla_bwd_launch_count() kernels: chunk preparation, forward state walk, reverse state walk,
+ * chunk gradients, and a value-gradient kernel when the key width is split).  nevents must
+ * be at least 3 (forward) or 6 (backward), else GLA_ERR_NULL_ARG.  The events are owned by the caller and are only
  * recorded, never created, synchronised or destroyed.  Used to time individual kernels. */
 int gla_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const float* h0,
                      void* o, float* ht,
@@ -137,6 +137,8 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g,
                     int B, int H, int Dk, int Dv, int dtype, void* stream);
 
 /* ---------------------------------------------------------------- GSA forward ----------
+ * Supported: C in {16, 32, 64}; m a multiple of 16 up to 64; Dk a multiple of 16 up to 256;
+ * Dv a multiple of 16 up to 512 (others: GLA_ERR_UNSUPPORTED).
  *   q, k : [B,H,L,Dk] dtype;  v : [B,H,L,Dv] dtype;  g : [B,H,L,m] dtype slot log-gates
  *   hk0  : [B,H,Dk,m] float32 initial pass-1 state or NULL;  hv0 : [B,H,m,Dv] or NULL
  *   o    : [B,H,L,Dv] dtype

@@ -308,3 +308,157 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
 }
 
 }  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------- gated slot attention
+int check_gsa(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, bool bwd) {
+  if (dtype != GLA_F32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;
+  if (B < 1 || H < 1 || L < 1 || Dk < 1 || Dv < 1 || m < 1 || C < 1) return GLA_ERR_SHAPE;
+  if (C != 16 && C != 32 && C != 64) return GLA_ERR_UNSUPPORTED;
+  if (m % 16 != 0 || m > 64 || Dk % 16 != 0 || Dk > 256 || Dv % 16 != 0 || Dv > 512) return GLA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H > 65535 || (int64_t)L * Dv > INT32_MAX / 2 || (int64_t)L * Dk > INT32_MAX / 2)
+    return GLA_ERR_UNSUPPORTED;
+  const int es = esize_of(dtype), MP = pad_dk(m), CP = pad_c(C);
+  if (!gsa_config_fits(es, MP, CP) || !fwd_config_fits(es, MP, CP)) return GLA_ERR_UNSUPPORTED;
+  if (bwd && !bwd_config_fits(es, MP, CP)) return GLA_ERR_UNSUPPORTED;
+  return GLA_OK;
+}
+
+struct GsaLayout {
+  size_t W, P, Pf, dP, dW2, dg2, dZ, WdT, Gam, S1s, dS1s, dZsT, Z1, ops2base, Hs2, dHs2, carry2, total;
+  OpsLayout ops2;
+};
+
+GsaLayout gsa_layout(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, bool bwd) {
+  const size_t BH = (size_t)B * H, es = esize_of(dtype), MP = pad_dk(m), CP = pad_c(C);
+  const size_t N = (L + C - 1) / C, DkP = pad_dv(Dk), DvP = pad_dv(Dv);
+  const size_t tok = BH * L * m;
+  GsaLayout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
+  l.W = take(tok * es);
+  l.P = take(tok * es);
+  l.WdT = take(BH * N * MP * CP * es);
+  l.Gam = take(BH * N * MP * 4);
+  l.S1s = take(BH * N * MP * DkP * es);
+  if (bwd) {
+    l.Pf = take(tok * 4);
+    l.dP = take(tok * es);
+    l.dW2 = take(tok * es);
+    l.dg2 = take(tok * 4);
+    l.dZ = take(tok * 4);
+    l.dS1s = take(BH * N * MP * DkP * es);
+    l.dZsT = take(BH * N * MP * CP * es);
+    l.Z1 = take(BH * N * (DkP / kDvTile) * MP * 4);
+  }
+  l.ops2 = ops_layout(BH, N, CP, MP, es, bwd);
+  l.ops2base = take(l.ops2.total);
+  if (bwd) {
+    l.Hs2 = take(BH * N * MP * DvP * es);
+    l.dHs2 = take(BH * N * MP * DvP * es);
+    l.carry2 = take(BH * N * (DvP / kDvTile) * MP * 4);
+  }
+  l.total = off;
+  return l;
+}
+
+GsaParams gsa_params(const GsaLayout& l, char* ws, int B, int H, int L, int Dk, int Dv, int m, int C, bool bwd) {
+  GsaParams p{};
+  p.BH = B * H; p.L = L; p.Dk = Dk; p.DkP = pad_dv(Dk); p.Dv = Dv; p.m = m; p.C = C; p.N = (L + C - 1) / C;
+  p.W = ws + l.W; p.P = ws + l.P; p.WdT = ws + l.WdT; p.Gam = reinterpret_cast<float*>(ws + l.Gam);
+  p.S1s = ws + l.S1s;
+  if (bwd) {
+    p.Pf = reinterpret_cast<float*>(ws + l.Pf);
+    p.dP = ws + l.dP; p.dW2 = ws + l.dW2;
+    p.dg2 = reinterpret_cast<float*>(ws + l.dg2); p.dZ = reinterpret_cast<float*>(ws + l.dZ);
+    p.dS1s = ws + l.dS1s; p.dZsT = ws + l.dZsT; p.Z1 = reinterpret_cast<float*>(ws + l.Z1);
+    p.Hs2 = ws + l.Hs2; p.dHs2 = ws + l.dHs2; p.carry2 = reinterpret_cast<float*>(ws + l.carry2);
+  }
+  p.ops2 = carve_ops(ws + l.ops2base, l.ops2, bwd);
+  return p;
+}
+
+#define GSA_DISPATCH(LAUNCH, TT, MP, CP, ...)                                                   \
+  do {                                                                                         \
+    if (MP == 32 && CP == 32) return LAUNCH<TT, 32, 32>(__VA_ARGS__);                          \
+    if (MP == 32 && CP == 64) return LAUNCH<TT, 32, 64>(__VA_ARGS__);                          \
+    if (MP == 64 && CP == 32) return LAUNCH<TT, 64, 32>(__VA_ARGS__);                          \
+    if (MP == 64 && CP == 64) return LAUNCH<TT, 64, 64>(__VA_ARGS__);                          \
+  } while (0)
+
+hipError_t dispatch_gsa(bool bwd, int dtype, int MP, int CP, const GsaParams& p, hipStream_t s) {
+  if (bwd) {
+    if (dtype == GLA_BF16) GSA_DISPATCH(launch_gsa_bwd, bf16, MP, CP, p, s);
+    else GSA_DISPATCH(launch_gsa_bwd, float, MP, CP, p, s);
+  } else {
+    if (dtype == GLA_BF16) GSA_DISPATCH(launch_gsa_fwd, bf16, MP, CP, p, s);
+    else GSA_DISPATCH(launch_gsa_fwd, float, MP, CP, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gsa_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype) {
+  if (check_gsa(B, H, L, Dk, Dv, m, C, dtype, false) != GLA_OK) return 0;
+  return gsa_layout(B, H, L, Dk, Dv, m, C, dtype, false).total;
+}
+
+size_t gsa_bwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype) {
+  if (check_gsa(B, H, L, Dk, Dv, m, C, dtype, true) != GLA_OK) return 0;
+  return gsa_layout(B, H, L, Dk, Dv, m, C, dtype, true).total;
+}
+
+int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
+            void* o, float* hkt, float* hvt, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gsa(B, H, L, Dk, Dv, m, C, dtype, false);
+  if (st != GLA_OK) return st;
+  if (!q || !k || !v || !g || !o) return GLA_ERR_NULL_ARG;
+  if (!all_aligned({q, k, v, g, hk0, hv0, o, hkt, hvt, workspace})) return GLA_ERR_UNSUPPORTED;
+  const GsaLayout lay = gsa_layout(B, H, L, Dk, Dv, m, C, dtype, false);
+  if (!workspace || workspace_bytes < lay.total) return GLA_ERR_WORKSPACE;
+  const size_t es = esize_of(dtype), BH = (size_t)B * H;
+  const size_t nk = BH * L * Dk * es, nv = BH * L * Dv * es, ng = BH * L * m * es;
+  const size_t sk = BH * Dk * m * 4, sv = BH * m * Dv * 4;
+  const Range ins[] = {{q, nk}, {k, nk}, {v, nv}, {g, ng}, {hk0, hk0 ? sk : 0}, {hv0, hv0 ? sv : 0}};
+  const Range outs[] = {{o, nv}, {hkt, hkt ? sk : 0}, {hvt, hvt ? sv : 0}, {workspace, lay.total}};
+  if (any_alias(outs, 4, ins, 6)) return GLA_ERR_ALIAS;
+  GsaParams p = gsa_params(lay, static_cast<char*>(workspace), B, H, L, Dk, Dv, m, C, false);
+  p.q = q; p.k = k; p.v = v; p.g = g; p.hk0 = hk0; p.hv0 = hv0; p.o = o; p.hkt = hkt; p.hvt = hvt;
+  if (dispatch_gsa(false, dtype, pad_dk(m), pad_c(C), p, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
+            const void* do_, const float* dhkt, const float* dhvt, void* dq, void* dk, void* dv, float* dg,
+            float* dhk0, float* dhv0, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
+            void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gsa(B, H, L, Dk, Dv, m, C, dtype, true);
+  if (st != GLA_OK) return st;
+  if (!q || !k || !v || !g || !do_ || !dq || !dk || !dv || !dg) return GLA_ERR_NULL_ARG;
+  if (!all_aligned({q, k, v, g, hk0, hv0, do_, dhkt, dhvt, dq, dk, dv, dg, dhk0, dhv0, workspace}))
+    return GLA_ERR_UNSUPPORTED;
+  const GsaLayout lay = gsa_layout(B, H, L, Dk, Dv, m, C, dtype, true);
+  if (!workspace || workspace_bytes < lay.total) return GLA_ERR_WORKSPACE;
+  const size_t es = esize_of(dtype), BH = (size_t)B * H;
+  const size_t nk = BH * L * Dk * es, nv = BH * L * Dv * es, ng = BH * L * m * es;
+  const size_t sk = BH * Dk * m * 4, sv = BH * m * Dv * 4;
+  const Range ins[] = {{q, nk}, {k, nk}, {v, nv}, {g, ng}, {hk0, hk0 ? sk : 0}, {hv0, hv0 ? sv : 0},
+                       {do_, nv}, {dhkt, dhkt ? sk : 0}, {dhvt, dhvt ? sv : 0}};
+  const Range outs[] = {{dq, nk}, {dk, nk}, {dv, nv}, {dg, BH * L * m * 4}, {dhk0, dhk0 ? sk : 0},
+                        {dhv0, dhv0 ? sv : 0}, {workspace, lay.total}};
+  if (any_alias(outs, 7, ins, 9)) return GLA_ERR_ALIAS;
+  GsaParams p = gsa_params(lay, static_cast<char*>(workspace), B, H, L, Dk, Dv, m, C, true);
+  p.q = q; p.k = k; p.v = v; p.g = g; p.do_ = do_; p.hk0 = hk0; p.hv0 = hv0; p.dhkt = dhkt; p.dhvt = dhvt;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dhk0 = dhk0; p.dhv0 = dhv0;
+  if (dispatch_gsa(true, dtype, pad_dk(m), pad_c(C), p, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+}  // extern "C"

@@ -97,6 +97,38 @@ __device__ __forceinline__ Frag<T> frag_from_acc(const f32x4& a, const f32x4& b)
   return f;
 }
 
+// An operand carried as hi + lo (hi = T(x), lo = T(x - hi)); for fp32 the lo part is zero
+// and unused.  mma3 forms hi.hi + hi.lo + lo.hi, about 2^-17 per term for bf16.
+template <typename T>
+struct HiLo {
+  Frag<T> hi, lo;
+};
+template <typename T>
+__device__ __forceinline__ HiLo<T> hilo(const float (&x)[8]) {
+  HiLo<T> r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    r.hi.v[e] = from_f32<T>(x[e]);
+    r.lo.v[e] = from_f32<T>(x[e] - to_f32(r.hi.v[e]));
+  }
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ void mma3(f32x4& acc, const HiLo<T>& a, const HiLo<T>& b) {
+  mma(acc, a.hi, b.hi);
+  if constexpr (sizeof(T) == 2) {
+    mma(acc, a.hi, b.lo);
+    mma(acc, a.lo, b.hi);
+  }
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_of(const float (&x)[8]) {
+  Frag<T> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = from_f32<T>(x[e]);
+  return f;
+}
+
 // 16-byte vector of T for coalesced copies.
 template <typename T> struct V16;
 template <> struct V16<bf16> { static constexpr int N = 8; typedef bf16x8 type; };

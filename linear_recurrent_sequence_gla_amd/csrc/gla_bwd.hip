@@ -25,260 +25,19 @@
 //
 // Launches:
 //   1. gla_prep_kernel (also writes QsT)                      grid N x BH
-//   2. gla_bwd_walk: forward walk storing H_n, then reverse walk storing dH_{n+1} and Z_n,
-//      state slice in fp32 MFMA accumulators                    grid ceil(Dv/64) * BH
-//   3. gla_bwd_chunk: dA, dq, dk (+ dv when the whole key width fits one workgroup) on MFMA
+//   2. walk_store: forward state walk storing H_n               grid ceil(Dv/64) * BH
+//   3. walk_reverse: reverse walk storing dH_{n+1} and Z_n       grid ceil(Dv/64) * BH
+//      (walks.hpp; state slices in fp32 MFMA accumulators)
+//   4. gla_bwd_chunk: dA, dq, dk (+ dv when the whole key width fits one workgroup) on MFMA
 //      over 64-column slices of Dv, then an element-wise epilogue (gate scaling, diagonal
 //      terms, the two in-chunk prefix sums of dg, Z_n) with 16-byte stores
 //                                                              grid N x BH x (Dk slices)
-//   4. gla_bwd_dv (only when dv did not fit step 3)           grid N x BH x ceil(Dv/64)
+//   5. gla_bwd_dv (only when dv did not fit step 4)           grid N x BH x ceil(Dv/64)
 // Intra-chunk terms use the factorised form only on chunks whose gate span passes the same
 // check as the forward; other chunks form them exactly, element by element, in fp32.
-#include "prep.hpp"
+#include "walks.hpp"
 
 namespace gla {
-
-// ======================================================================= state walk
-template <typename T, int DKP, int CP>
-struct BwdWalkCfg {
-  static constexpr int V = 16 / (int)sizeof(T);
-  static constexpr int LDA = CP + V, LDV = kDvTile + V;
-  static constexpr size_t KT = (size_t)DKP * LDA * sizeof(T);   // KdT (forward) / QsT (reverse)
-  static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);    // V (forward) / dO (reverse)
-  static constexpr size_t HT = (size_t)DKP * LDV * sizeof(T);   // state tile (out / in)
-  static constexpr size_t BYTES = KT + VT + 2 * HT + (size_t)DKP * 4 + (size_t)4 * DKP * 4;
-  static constexpr int NK = DKP * CP / V, NV = CP * kDvTile / V, NH = DKP * kDvTile / V;
-  static constexpr int PKd = (NK + 255) / 256, PV = (NV + 255) / 256, PH = (NH + 255) / 256;
-};
-
-template <typename T, int DKP, int CP>
-struct BwdWalkStage {
-  using W = BwdWalkCfg<T, DKP, CP>;
-  typedef typename V16<T>::type VT;
-  VT kt[W::PKd], v[W::PV], h[W::PH];
-  f32x4 gam;
-
-  // mat: dense [DKP][CP] chunk matrix; src: [L][Dv] rows of this (b,h); htile: [DKP][DVP]
-  // state tile already offset to this workgroup's columns, or nullptr.
-  __device__ __forceinline__ void load(const T* mat, const T* src, int row0, int len, int Dv, int tile,
-                                       const float* gam_chunk, const T* htile, int DVP) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int m = 0; m < W::PKd; ++m) {
-      const int idx = tid + 256 * m;
-      if (idx < W::NK) kt[m] = *reinterpret_cast<const VT*>(mat + (size_t)idx * W::V);
-    }
-    constexpr int PER_ROW = kDvTile / W::V;
-#pragma unroll
-    for (int m = 0; m < W::PV; ++m) {
-      const int idx = tid + 256 * m;
-      const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
-      const int j = tile * kDvTile + c;
-      v[m] = (idx < W::NV && r < len && j < Dv) ? *reinterpret_cast<const VT*>(src + (size_t)(row0 + r) * Dv + j)
-                                                : zero_vec<T>();
-    }
-    if (htile) {
-#pragma unroll
-      for (int m = 0; m < W::PH; ++m) {
-        const int idx = tid + 256 * m;
-        const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
-        if (idx < W::NH) h[m] = *reinterpret_cast<const VT*>(htile + (size_t)r * DVP + c);
-      }
-    }
-    if (tid < DKP / 4) gam = *reinterpret_cast<const f32x4*>(gam_chunk + 4 * tid);
-  }
-
-  __device__ __forceinline__ void store(T* sKT, T* sV, T* sHi, float* sG, bool with_h) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int m = 0; m < W::PKd; ++m) {
-      const int idx = tid + 256 * m;
-      if (idx < W::NK) {
-        const int r = idx / (CP / W::V), c = (idx - r * (CP / W::V)) * W::V;
-        *reinterpret_cast<VT*>(sKT + r * W::LDA + c) = kt[m];
-      }
-    }
-    constexpr int PER_ROW = kDvTile / W::V;
-#pragma unroll
-    for (int m = 0; m < W::PV; ++m) {
-      const int idx = tid + 256 * m;
-      if (idx < W::NV) {
-        const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
-        *reinterpret_cast<VT*>(sV + r * W::LDV + c) = v[m];
-      }
-    }
-    if (with_h) {
-#pragma unroll
-      for (int m = 0; m < W::PH; ++m) {
-        const int idx = tid + 256 * m;
-        if (idx < W::NH) {
-          const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
-          *reinterpret_cast<VT*>(sHi + r * W::LDV + c) = h[m];
-        }
-      }
-    }
-    if (tid < DKP / 4) *reinterpret_cast<f32x4*>(sG + 4 * tid) = gam;
-  }
-};
-
-// Copy an LDS [DKP][64] tile to the state workspace (row stride DVP, already offset).
-template <typename T, int DKP>
-__device__ __forceinline__ void state_tile_out(T* dst, const T* src, int lds, int DVP) {
-  constexpr int V = V16<T>::N;
-  typedef typename V16<T>::type VT;
-  constexpr int PER_ROW = kDvTile / V;
-  for (int idx = threadIdx.x; idx < DKP * PER_ROW; idx += 256) {
-    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
-    *reinterpret_cast<VT*>(dst + (size_t)r * DVP + c) = *reinterpret_cast<const VT*>(src + r * lds + c);
-  }
-}
-
-template <typename T, int DKP, int CP>
-__global__ __launch_bounds__(256) void gla_bwd_walk(BwdParams p, int ntile) {
-  using W = BwdWalkCfg<T, DKP, CP>;
-  constexpr int LDA = W::LDA, LDV = W::LDV;
-  constexpr int NCB = CP / 32, NIB = DKP / 16;
-  __shared__ __attribute__((aligned(16))) char smem[W::BYTES];
-  T* sKT = reinterpret_cast<T*>(smem);
-  T* sV = reinterpret_cast<T*>(smem + W::KT);
-  T* sHo = reinterpret_cast<T*>(smem + W::KT + W::VT);
-  T* sHi = reinterpret_cast<T*>(smem + W::KT + W::VT + W::HT);
-  float* sG = reinterpret_cast<float*>(smem + W::KT + W::VT + 2 * W::HT);
-  float* sRed = sG + DKP;
-
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = lin % ntile, bh = lin / ntile;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  const int Dv = p.Dv, Dk = p.Dk, L = p.L, C = p.C, N = p.N;
-  const int DVP = ntile * kDvTile;
-  const int j = tile * kDvTile + 16 * wave + col;
-  const bool jv = j < Dv;
-  const T* vg = reinterpret_cast<const T*>(p.v) + (size_t)bh * L * Dv;
-  const T* dog = reinterpret_cast<const T*>(p.do_) + (size_t)bh * L * Dv;
-  T* Hs = reinterpret_cast<T*>(p.Hs) + (size_t)bh * N * DKP * DVP + tile * kDvTile;
-  T* dHs = reinterpret_cast<T*>(p.dHs) + (size_t)bh * N * DKP * DVP + tile * kDvTile;
-  const T* KdT = reinterpret_cast<const T*>(p.ops.KdT) + (size_t)bh * N * DKP * CP;
-  const T* QsT = reinterpret_cast<const T*>(p.ops.QsT) + (size_t)bh * N * DKP * CP;
-  const float* Gam = p.ops.Gam + (size_t)bh * N * DKP;
-
-  f32x4 H[NIB];
-#pragma unroll
-  for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * ib + 4 * grp + e;
-      H[ib][e] = (p.h0 && jv && i < Dk) ? p.h0[((size_t)bh * Dk + i) * Dv + j] : 0.f;
-    }
-  }
-
-  // ---- forward: store H_n (n = 0..N-1), end with H = H_N = ht
-  BwdWalkStage<T, DKP, CP> st;
-  st.load(KdT, vg, 0, min(C, L), Dv, tile, Gam, nullptr, DVP);
-  st.store(sKT, sV, sHi, sG, false);
-  __syncthreads();
-  for (int n = 0; n < N; ++n) {
-    if (n + 1 < N) {
-      const int r1 = (n + 1) * C;
-      st.load(KdT + (size_t)(n + 1) * DKP * CP, vg, r1, min(C, L - r1), Dv, tile, Gam + (size_t)(n + 1) * DKP,
-              nullptr, DVP);
-    }
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sHo[(16 * ib + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(H[ib][e]);
-    }
-    Frag<T> Yv[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_col(sV + (32 * cb + 8 * grp) * LDV + 16 * wave + col, LDV);
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) H[ib][e] *= fast_exp2(sG[16 * ib + 4 * grp + e]);
-    }
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-      for (int ib = 0; ib < NIB; ++ib) mma(H[ib], ld8(sKT + (16 * ib + col) * LDA + 32 * cb + 8 * grp), Yv[cb]);
-    }
-    __syncthreads();
-    state_tile_out<T, DKP>(Hs + (size_t)n * DKP * DVP, sHo, LDV, DVP);
-    if (n + 1 < N) st.store(sKT, sV, sHi, sG, false);
-    __syncthreads();
-  }
-  __threadfence();     // the H_n tiles are read back below by this workgroup
-  __syncthreads();
-
-  // ---- reverse: for n = N-1..0 emit dH_{n+1} and Z_n = 2^{Gamma_n} rowsum(dH_{n+1} * H_n),
-  //      then dH_n = Diag(2^{Gamma_n}) dH_{n+1} + QsT_n dO_n
-  f32x4 dH[NIB];
-#pragma unroll
-  for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * ib + 4 * grp + e;
-      dH[ib][e] = (p.dht && jv && i < Dk) ? p.dht[((size_t)bh * Dk + i) * Dv + j] : 0.f;
-    }
-  }
-  {
-    const int r1 = (N - 1) * C;
-    st.load(QsT + (size_t)(N - 1) * DKP * CP, dog, r1, L - r1, Dv, tile, Gam + (size_t)(N - 1) * DKP,
-            Hs + (size_t)(N - 1) * DKP * DVP, DVP);
-    st.store(sKT, sV, sHi, sG, true);
-  }
-  __syncthreads();
-  for (int n = N - 1; n >= 0; --n) {
-    if (n > 0) {
-      const int r1 = (n - 1) * C;
-      st.load(QsT + (size_t)(n - 1) * DKP * CP, dog, r1, C, Dv, tile, Gam + (size_t)(n - 1) * DKP,
-              Hs + (size_t)(n - 1) * DKP * DVP, DVP);
-    }
-    // Z partial over this lane's column, then over the 16 columns of the wave
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * ib + 4 * grp + e;
-        float x = dH[ib][e] * to_f32(sHi[i * LDV + 16 * wave + col]);
-        x += __shfl_xor(x, 1, 64);
-        x += __shfl_xor(x, 2, 64);
-        x += __shfl_xor(x, 4, 64);
-        x += __shfl_xor(x, 8, 64);
-        if (col == 0) sRed[wave * DKP + i] = x * fast_exp2(sG[i]);
-        sHo[i * LDV + 16 * wave + col] = from_f32<T>(dH[ib][e]);
-      }
-    }
-    Frag<T> Yd[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) Yd[cb] = ld8_col(sV + (32 * cb + 8 * grp) * LDV + 16 * wave + col, LDV);
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dH[ib][e] *= fast_exp2(sG[16 * ib + 4 * grp + e]);
-    }
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-      for (int ib = 0; ib < NIB; ++ib) mma(dH[ib], ld8(sKT + (16 * ib + col) * LDA + 32 * cb + 8 * grp), Yd[cb]);
-    }
-    __syncthreads();
-    for (int i = tid; i < DKP; i += 256)
-      p.carry[(((size_t)bh * N + n) * ntile + tile) * DKP + i] =
-          sRed[i] + sRed[DKP + i] + sRed[2 * DKP + i] + sRed[3 * DKP + i];
-    state_tile_out<T, DKP>(dHs + (size_t)n * DKP * DVP, sHo, LDV, DVP);
-    if (n > 0) st.store(sKT, sV, sHi, sG, true);
-    __syncthreads();
-  }
-  if (p.dh0 && jv) {
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * ib + 4 * grp + e;
-        if (i < Dk) p.dh0[((size_t)bh * Dk + i) * Dv + j] = dH[ib][e];
-      }
-    }
-  }
-}
 
 // ======================================================================= chunk gradients
 // LDS phases of the chunk kernel:
@@ -753,7 +512,7 @@ struct BwdPlan {
                            : (DKP >= 128 && fits(128, false)) ? 128
                            : (DKP >= 64 && fits(64, false)) ? 64 : 32;
   static constexpr bool OK = (FUSED || fits(DKS, false)) && PrepCfg<T, DKP, CP>::BYTES <= kMaxLds &&
-                             BwdWalkCfg<T, DKP, CP>::BYTES <= kMaxLds &&
+                             WalkIOCfg<T, DKP, CP>::BYTES <= kMaxLds &&
                              (FUSED || BwdDvCfg<T, DKP, CP>::BYTES <= kMaxLds);
 };
 
@@ -769,17 +528,20 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     record_event(p.events, 1, s);
     const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
-    hipLaunchKernelGGL((gla_bwd_walk<T, DKP, CP>), dim3(ntile * p.BH), dim3(256), 0, s, p, ntile);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, nullptr, nullptr, p.h0, nullptr, p.Dk, p.Dv, p.L, p.C, p.N, 0};
+    if ((e = launch_walk_store<T, DKP, CP>(wf, p.BH, s)) != hipSuccess) return e;
     record_event(p.events, 2, s);
+    WalkIO wr{p.ops.QsT, p.do_, p.ops.Gam, p.dHs, p.Hs, p.carry, p.dht, p.dh0, p.Dk, p.Dv, p.L, p.C, p.N, 0};
+    if ((e = launch_walk_reverse<T, DKP, CP>(wr, p.BH, s)) != hipSuccess) return e;
+    record_event(p.events, 3, s);
     hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED>), dim3(p.N, p.BH, DKP / P::DKS), dim3(256), 0, s,
                        p, DKP, ntile);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    record_event(p.events, 3, s);
+    record_event(p.events, 4, s);
     if constexpr (!P::FUSED) {
       hipLaunchKernelGGL((gla_bwd_dv<T, DKP, CP>), dim3(p.N, p.BH, ntile), dim3(256), 0, s, p, ntile);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      record_event(p.events, 4, s);
+      record_event(p.events, 5, s);
     }
     return hipSuccess;
   }
@@ -788,7 +550,7 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
 int bwd_launch_count(int esize, int DKP, int CP) {
   int c = 0;
 #define GLA_BCNT_CASE(TT, D, C_) \
-  if (esize == (int)sizeof(TT) && DKP == D && CP == C_) c = BwdPlan<TT, D, C_>::FUSED ? 3 : 4;
+  if (esize == (int)sizeof(TT) && DKP == D && CP == C_) c = BwdPlan<TT, D, C_>::FUSED ? 4 : 5;
 #define GLA_BCNT_ALL(TT)                                                                 \
   GLA_BCNT_CASE(TT, 32, 32) GLA_BCNT_CASE(TT, 32, 64) GLA_BCNT_CASE(TT, 32, 128)           \
   GLA_BCNT_CASE(TT, 64, 32) GLA_BCNT_CASE(TT, 64, 64) GLA_BCNT_CASE(TT, 64, 128)           \

@@ -1,0 +1,731 @@
+// gsa.hip -- gated slot attention (GSA) on gfx950: two GLA passes linked by a softmax.
+//
+// GSA ("Gated Slot Attention for Efficient Linear-Time Sequence Modeling": abstract and the
+// research-map summary, "Approach") keeps m slot memories per head with a data-dependent
+// forget gate per slot.  With alpha_t = exp(g_t) (g_t in R^m) and write weights
+// w_t = 1 - alpha_t:
+//   pass 1 (slot keys, decay on the slot axis)  S1_t = S1_{t-1} Diag(alpha_t) + k_t^T w_t,
+//                                               z_t = q_t S1_t
+//   p_t = softmax(z_t) over the m slots
+//   pass 2 (slot values, row-gated GLA)          S2_t = Diag(alpha_t) S2_{t-1} + w_t^T v_t,
+//                                               o_t = p_t S2_t
+// Pass 2 is exactly GLA with queries p, keys w, values v and the same gates, so it runs on the
+// GLA kernels (gla_fwd.hip / gla_bwd.hip) with p and w materialised as [B,H,L,m] tensors.  Pass
+// 1 runs here.  Its transposed state S1^T [m x Dk] is row-gated (keys w, values k), so it
+// rides the generic state walks of walks.hpp.  In chunk form (b = chunk-local log2 prefix sum
+// of g, E = 2^b, Ei = 2^-b, Eg = 2^{Gamma-b}, QK = mask(Q K^T) with c <= r):
+//   Z = E * (QK (W*Ei) + Q S1_n)                                    (then P = softmax(Z))
+//   dQK = mask((dZ*E)(W*Ei)^T),  dq = dQK K + (dZ*E) S1_n^T
+//   dk  = dQK^T Q + (W*Eg) dS1_{n+1}^T
+//   dW1 = Ei*(QK^T (dZ*E)) + Eg*(K dS1_{n+1})
+// with the same gate-span check as GLA: chunks with |b| > 32 form the intra-chunk terms
+// exactly, element by element.  Operands whose dot products can cancel (QK, dZ) go through
+// hi/lo bf16 splits.  The gate gradient is assembled without exactly-cancelling pairs:
+//   dg_t = sum_{r>=t}(dZ_r Znd_r - W_r dW1'_r) + sum_{c<t} W_c B1_c + Z1_n      (pass 1)
+//        + [pass-2 gate gradient from the GLA backward]
+//        - alpha_t (dW1_t + dW2_t)                                  (w = 1 - alpha)
+// where Znd is Z without its diagonal term QK_rr W_r, dW1' the strictly-upper intra part of
+// dW1, B1 = Eg*(K dS1_{n+1}) and Z1_n = 2^Gamma colsum(dS1_{n+1} * S1_n).
+#include "walks.hpp"
+
+namespace gla {
+
+template <typename T, int MP, int CP>
+struct GsaCfg {
+  using M = ChunkMap<T, MP, CP>;
+  static constexpr int V = 16 / (int)sizeof(T);
+  static constexpr int LDF = MP + 4;            // fp32 [CP][MP] tiles
+  static constexpr int LDQK = CP + 4;           // fp32 [CP][CP] tiles
+  static constexpr int LDS = kDvTile + V;       // 64-wide T slices
+  static constexpr int LDM = MP + V;            // T [CP][MP] staging
+  static constexpr int LDC = CP + V;            // T [MP][CP] tiles
+  static constexpr int NRB = CP / 16, NSB = MP / 16;
+  static constexpr size_t FT = (size_t)CP * LDF * 4;
+  static constexpr size_t QKT = (size_t)CP * LDQK * 4;
+  static constexpr size_t ST_C = (size_t)CP * LDS * sizeof(T);
+  static constexpr size_t ST_M = (size_t)MP * LDS * sizeof(T);
+  // gsa_p: sB, sW, sQK, then slices (q, k, S1^T) aliased by the P staging tile
+  static constexpr size_t P_BYTES = 2 * FT + QKT + cmax(2 * ST_C + ST_M, (size_t)CP * LDM * sizeof(T)) +
+                                    (size_t)(M::NSEG * MP + MP + 8) * 4;
+  // gsa_pass1_bwd: sB, sW, sdZ, then {sdQK + slices} aliased by {sQK + three fp32 tiles}
+  static constexpr size_t B_REGION = cmax(QKT + 4 * ST_C + 2 * ST_M, QKT + 3 * FT);
+  static constexpr size_t B_BYTES = 3 * FT + B_REGION + (size_t)(2 * M::NSEG * MP + 2 * MP + 8) * 4;
+};
+
+// ----------------------------------------------------------------------------- prep
+// Per chunk: b, Gamma (log2 units), w = -expm1(g) written as a [L][m] tensor (the keys of
+// pass 2), and WdT = (w * 2^{Gamma-b})^T, the decayed write weights both state walks consume.
+template <typename T, int MP, int CP>
+__global__ __launch_bounds__(256) void gsa_prep_kernel(GsaParams p) {
+  using M = ChunkMap<T, MP, CP>;
+  constexpr int V = M::V, RPS = M::RPS, LDC = CP + V;
+  typedef typename V16<T>::type VT;
+  __shared__ __attribute__((aligned(16))) T sWdT[MP * LDC];
+  __shared__ float segtot[M::NSEG * MP];
+  __shared__ float sGam[MP];
+  __shared__ float red[8];
+  const int n = blockIdx.x, bh = blockIdx.y, m = p.m;
+  const int row0 = n * p.C, len = min(p.C, p.L - row0);
+  const size_t gbase = ((size_t)bh * p.L + row0) * m;
+  const size_t chunk = (size_t)bh * p.N + n;
+  const T* gg = reinterpret_cast<const T*>(p.g) + gbase;
+  ChunkScan<T, MP, CP, false> cs;
+  cs.run(gg, gg, gg, m, m, len, segtot, sGam, red);
+  const int c0 = cs.cg * V, r0 = cs.seg * RPS;
+  if (cs.active) {
+    T* Wg = reinterpret_cast<T*>(p.W) + gbase;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const int r = r0 + u;
+      VT wv;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float w = -expm1f(cs.qv[u][e]);
+        wv[e] = from_f32<T>(w);
+        sWdT[(c0 + e) * LDC + r] = from_f32<T>(w * fast_exp2(sGam[c0 + e] - cs.b[u][e]));
+      }
+      if (r < len && c0 < m) *reinterpret_cast<VT*>(Wg + (size_t)r * m + c0) = wv;
+    }
+  }
+  __syncthreads();
+  tile_out<T>(reinterpret_cast<T*>(p.WdT) + chunk * MP * CP, sWdT, MP, CP, LDC);
+  if (threadIdx.x < MP) p.Gam[chunk * MP + threadIdx.x] = sGam[threadIdx.x];
+}
+
+// Stage a [rows][64] slice of a row-major [*, ld] tensor (rows < nrows, columns < ncols
+// valid, zero elsewhere) into LDS with row stride lds.
+template <typename T>
+__device__ __forceinline__ void slice_in(T* dst, int lds, const T* src, size_t ld, int rows, int nrows, int col0,
+                                         int ncols) {
+  constexpr int V = V16<T>::N;
+  typedef typename V16<T>::type VT;
+  constexpr int PER_ROW = kDvTile / V;
+  for (int idx = threadIdx.x; idx < rows * PER_ROW; idx += 256) {
+    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+    const int cc = col0 + c;
+    *reinterpret_cast<VT*>(dst + r * lds + c) =
+        (r < nrows && cc < ncols) ? *reinterpret_cast<const VT*>(src + (size_t)r * ld + cc) : zero_vec<T>();
+  }
+}
+
+// ----------------------------------------------------------------------------- pass 1 forward
+// Z = E * (QK (W Ei) + Q S1_n), P = softmax_slots(Z), written as the [L][m] queries of pass 2.
+template <typename T, int MP, int CP>
+__global__ __launch_bounds__(256) void gsa_p_kernel(GsaParams p) {
+  using G = GsaCfg<T, MP, CP>;
+  using M = ChunkMap<T, MP, CP>;
+  constexpr int V = M::V, RPS = M::RPS;
+  constexpr int LDF = G::LDF, LDQK = G::LDQK, LDS = G::LDS, LDM = G::LDM, NRB = G::NRB, NSB = G::NSB;
+  typedef typename V16<T>::type VT;
+  __shared__ __attribute__((aligned(16))) char smem[G::P_BYTES];
+  float* sB = reinterpret_cast<float*>(smem);
+  float* sW = sB + CP * LDF;                  // Ws = W 2^-b (fast) or W (exact path)
+  float* sQK = sW + CP * LDF;
+  T* sq = reinterpret_cast<T*>(smem + 2 * G::FT + G::QKT);
+  T* sk = sq + CP * LDS;
+  T* sS1 = sk + CP * LDS;
+  T* sP = sq;                                 // after the slice loop
+  float* segtot = reinterpret_cast<float*>(smem + G::P_BYTES - (size_t)(M::NSEG * MP + MP + 8) * 4);
+  float* sGam = segtot + M::NSEG * MP;
+  float* red = sGam + MP;
+
+  const int n = blockIdx.x, bh = blockIdx.y, m = p.m, Dk = p.Dk;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int row0 = n * p.C, len = min(p.C, p.L - row0);
+  const size_t chunk = (size_t)bh * p.N + n;
+  const size_t gbase = ((size_t)bh * p.L + row0) * m;
+  const T* gg = reinterpret_cast<const T*>(p.g) + gbase;
+  ChunkScan<T, MP, CP, false> cs;
+  const bool fast = cs.run(gg, gg, gg, m, m, len, segtot, sGam, red) <= kSpanLimit;
+  if (cs.active) {
+    const int c0 = cs.cg * V, r0 = cs.seg * RPS;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float bb = cs.b[u][e];
+        const float w = -expm1f(cs.qv[u][e]);
+        sB[(r0 + u) * LDF + c0 + e] = bb;
+        sW[(r0 + u) * LDF + c0 + e] = fast ? w * fast_exp2(-bb) : w;
+      }
+    }
+  }
+  const int rb = wave;                        // this wave's 16 chunk rows
+  const bool rbv = rb < NRB;
+  f32x4 accQK[NRB], accZe[NSB];
+#pragma unroll
+  for (int c = 0; c < NRB; ++c) accQK[c] = zero4();
+#pragma unroll
+  for (int s = 0; s < NSB; ++s) accZe[s] = zero4();
+  const T* qg = reinterpret_cast<const T*>(p.q) + ((size_t)bh * p.L + row0) * Dk;
+  const T* kg = reinterpret_cast<const T*>(p.k) + ((size_t)bh * p.L + row0) * Dk;
+  const int DkP = p.DkP;
+  const T* s1 = reinterpret_cast<const T*>(p.S1s) + chunk * MP * DkP;
+  for (int ds = 0; ds < DkP / kDvTile; ++ds) {
+    __syncthreads();
+    slice_in<T>(sq, LDS, qg, Dk, CP, len, ds * kDvTile, Dk);
+    slice_in<T>(sk, LDS, kg, Dk, CP, len, ds * kDvTile, Dk);
+    slice_in<T>(sS1, LDS, s1, DkP, MP, MP, ds * kDvTile, DkP);
+    __syncthreads();
+    if (rbv) {
+#pragma unroll
+      for (int kb = 0; kb < kDvTile / 32; ++kb) {
+        const Frag<T> X = ld8(sq + (16 * rb + col) * LDS + 32 * kb + 8 * grp);
+#pragma unroll
+        for (int cb = 0; cb < NRB; ++cb)
+          if (cb <= rb) mma(accQK[cb], X, ld8(sk + (16 * cb + col) * LDS + 32 * kb + 8 * grp));
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) mma(accZe[sb], X, ld8(sS1 + (16 * sb + col) * LDS + 32 * kb + 8 * grp));
+      }
+    }
+  }
+  if (rbv) {
+#pragma unroll
+    for (int cb = 0; cb < NRB; ++cb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
+        sQK[r * LDQK + c] = c <= r ? accQK[cb][e] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  float z[NSB][4];
+#pragma unroll
+  for (int sb = 0; sb < NSB; ++sb) z[sb][0] = z[sb][1] = z[sb][2] = z[sb][3] = 0.f;
+  if (rbv) {
+    if (fast) {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kc = 0; kc < CP / 32; ++kc) {
+          float xa[8], xb[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xa[e] = sQK[(16 * rb + col) * LDQK + 32 * kc + 8 * grp + e];
+            xb[e] = sW[(32 * kc + 8 * grp + e) * LDF + 16 * sb + col];
+          }
+          mma3(acc, hilo<T>(xa), hilo<T>(xb));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rb + 4 * grp + e, s = 16 * sb + col;
+          z[sb][e] = fast_exp2(sB[r * LDF + s]) * (acc[e] + accZe[sb][e]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rb + 4 * grp + e, s = 16 * sb + col;
+          const float br = sB[r * LDF + s];
+          float zi = 0.f;
+          for (int c = 0; c <= r; ++c) zi += sQK[r * LDQK + c] * sW[c * LDF + s] * fast_exp2(br - sB[c * LDF + s]);
+          z[sb][e] = zi + fast_exp2(br) * accZe[sb][e];
+        }
+      }
+    }
+  }
+  __syncthreads();   // sP aliases the slice tiles: every wave is past its last slice read
+  if (rbv) {
+    // softmax over the m valid slots of each row (rows spread over e, slots over sb and col)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+        if (16 * sb + col < m) mx = fmaxf(mx, z[sb][e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 4, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 8, 64));
+      float ex[NSB], sum = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        ex[sb] = (16 * sb + col < m) ? fast_exp2((z[sb][e] - mx) * kLog2e) : 0.f;
+        sum += ex[sb];
+      }
+      sum += __shfl_xor(sum, 1, 64);
+      sum += __shfl_xor(sum, 2, 64);
+      sum += __shfl_xor(sum, 4, 64);
+      sum += __shfl_xor(sum, 8, 64);
+      const float inv = 1.f / sum;
+      const int r = 16 * rb + 4 * grp + e;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        const float pr = ex[sb] * inv;
+        sP[r * LDM + 16 * sb + col] = from_f32<T>(pr);
+        if (p.Pf && r < len && 16 * sb + col < m) p.Pf[gbase + (size_t)r * m + 16 * sb + col] = pr;
+      }
+    }
+  }
+  __syncthreads();
+  T* Pg = reinterpret_cast<T*>(p.P) + gbase;
+  constexpr int PER_ROW = MP / V;
+  for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
+    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+    if (r < len && c < m) *reinterpret_cast<VT*>(Pg + (size_t)r * m + c) = *reinterpret_cast<const VT*>(sP + r * LDM + c);
+  }
+}
+
+// ----------------------------------------------------------------------------- softmax backward
+// dZ = P (dP - <dP, P>) per row, written in fp32, and (dZ * 2^b)^T per chunk for the pass-1
+// reverse walk.
+template <typename T, int MP, int CP>
+__global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
+  using M = ChunkMap<T, MP, CP>;
+  constexpr int V = M::V, RPS = M::RPS, LDC = CP + V;
+  typedef typename V16<T>::type VT;
+  __shared__ __attribute__((aligned(16))) T sT[MP * LDC];
+  __shared__ float segtot[M::NSEG * MP];
+  __shared__ float sGam[MP];
+  __shared__ float red[8];
+  __shared__ float rpart[M::NCG * CP];
+  const int n = blockIdx.x, bh = blockIdx.y, m = p.m;
+  const int row0 = n * p.C, len = min(p.C, p.L - row0);
+  const size_t gbase = ((size_t)bh * p.L + row0) * m;
+  const size_t chunk = (size_t)bh * p.N + n;
+  const T* gg = reinterpret_cast<const T*>(p.g) + gbase;
+  ChunkScan<T, MP, CP, false> cs;
+  cs.run(gg, gg, gg, m, m, len, segtot, sGam, red);
+  const int c0 = cs.cg * V, r0 = cs.seg * RPS;
+  float pv[RPS][V], dpv[RPS][V];
+  if (cs.active) {
+    const float* Pg = p.Pf + gbase;     // fp32 softmax: its Jacobian keeps sum_s dZ = 0
+    const T* dPg = reinterpret_cast<const T*>(p.dP) + gbase;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const int r = r0 + u;
+      const bool ok = r < len && c0 < m;
+      const VT b = ok ? *reinterpret_cast<const VT*>(dPg + (size_t)r * m + c0) : zero_vec<T>();
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        pv[u][e] = ok ? Pg[(size_t)r * m + c0 + e] : 0.f;
+        dpv[u][e] = to_f32(b[e]);
+        s += pv[u][e] * dpv[u][e];
+      }
+      rpart[cs.cg * CP + r] = s;
+    }
+  }
+  __syncthreads();
+  if (cs.active) {
+    float* dZg = p.dZ + gbase;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const int r = r0 + u;
+      float rs = 0.f;
+      for (int c = 0; c < M::NCG; ++c) rs += rpart[c * CP + r];
+      float dz[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        dz[e] = pv[u][e] * (dpv[u][e] - rs);
+        sT[(c0 + e) * LDC + r] = from_f32<T>(dz[e] * fast_exp2(cs.b[u][e]));
+      }
+      if (r < len && c0 < m) {
+#pragma unroll
+        for (int e = 0; e < V; e += 4)
+          *reinterpret_cast<f32x4*>(dZg + (size_t)r * m + c0 + e) = f32x4{dz[e], dz[e + 1], dz[e + 2], dz[e + 3]};
+      }
+    }
+  }
+  __syncthreads();
+  tile_out<T>(reinterpret_cast<T*>(p.dZsT) + chunk * MP * CP, sT, MP, CP, LDC);
+}
+
+// ----------------------------------------------------------------------------- pass 1 backward
+template <typename T, int MP, int CP>
+__global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk) {
+  using G = GsaCfg<T, MP, CP>;
+  using M = ChunkMap<T, MP, CP>;
+  constexpr int V = M::V, RPS = M::RPS, NSEG = M::NSEG;
+  constexpr int LDF = G::LDF, LDQK = G::LDQK, LDS = G::LDS, NRB = G::NRB, NSB = G::NSB;
+  typedef typename V16<T>::type VT;
+  __shared__ __attribute__((aligned(16))) char smem[G::B_BYTES];
+  float* sB = reinterpret_cast<float*>(smem);
+  float* sW = sB + CP * LDF;
+  float* sdZ = sW + CP * LDF;
+  char* reg = smem + 3 * G::FT;
+  float* sdQK = reinterpret_cast<float*>(reg);             // during the slice loop
+  T* sq = reinterpret_cast<T*>(reg + G::QKT);
+  T* sk = sq + CP * LDS;
+  T* sS1 = sk + CP * LDS;
+  T* sdS1 = sS1 + MP * LDS;
+  T* sDQ = sdS1 + MP * LDS;
+  T* sDK = sDQ + CP * LDS;
+  float* sQK = reinterpret_cast<float*>(reg);              // after the slice loop
+  float* sU = sQK + CP * LDQK;
+  float* sY = sU + CP * LDF;
+  float* sD = sY + CP * LDF;
+  float* segtot = reinterpret_cast<float*>(smem + 3 * G::FT + G::B_REGION);
+  float* sGam = segtot + 2 * NSEG * MP;
+  float* sZ1 = sGam + MP;
+  float* red = sZ1 + MP;
+
+  const int n = blockIdx.x, bh = blockIdx.y, m = p.m, Dk = p.Dk, DkP = p.DkP;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int row0 = n * p.C, len = min(p.C, p.L - row0);
+  const size_t chunk = (size_t)bh * p.N + n;
+  const size_t gbase = ((size_t)bh * p.L + row0) * m;
+  const size_t kbase = ((size_t)bh * p.L + row0) * Dk;
+  const T* gg = reinterpret_cast<const T*>(p.g) + gbase;
+
+  for (int s = tid; s < MP; s += 256) {
+    float z = 0.f;
+    for (int t = 0; t < ntk; ++t) z += p.Z1[(chunk * ntk + t) * MP + s];
+    sZ1[s] = z;
+  }
+  ChunkScan<T, MP, CP, false> cs;
+  const bool fast = cs.run(gg, gg, gg, m, m, len, segtot, sGam, red) <= kSpanLimit;
+  const int c0 = cs.cg * V, r0 = cs.seg * RPS;
+  if (cs.active) {
+    const float* dZg = p.dZ + gbase;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const int r = r0 + u;
+      const bool ok = r < len && c0 < m;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        sB[r * LDF + c0 + e] = cs.b[u][e];
+        sW[r * LDF + c0 + e] = -expm1f(cs.qv[u][e]);
+        sdZ[r * LDF + c0 + e] = ok ? dZg[(size_t)r * m + c0 + e] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  const int rb = wave;
+  const bool rbv = rb < NRB;
+
+  // ---- dQK = mask_{c<=r}((dZ E)(W Ei)^T)
+  if (rbv) {
+#pragma unroll
+    for (int cb = 0; cb < NRB; ++cb) {
+      f32x4 acc = zero4();
+      if (cb <= rb) {
+        if (fast) {
+#pragma unroll
+          for (int ks = 0; ks < MP / 32; ++ks) {
+            float xa[8], xb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int s = 32 * ks + 8 * grp + e;
+              const int r = 16 * rb + col, c = 16 * cb + col;
+              xa[e] = sdZ[r * LDF + s] * fast_exp2(sB[r * LDF + s]);
+              xb[e] = sW[c * LDF + s] * fast_exp2(-sB[c * LDF + s]);
+            }
+            mma3(acc, hilo<T>(xa), hilo<T>(xb));
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
+            float x = 0.f;
+            if (c <= r)
+              for (int s = 0; s < m; ++s)
+                x += sdZ[r * LDF + s] * sW[c * LDF + s] * fast_exp2(sB[r * LDF + s] - sB[c * LDF + s]);
+            acc[e] = x;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
+        float x = c <= r ? acc[e] : 0.f;
+        if (c == r) {
+          // diagonal: sum_s dZ w = -sum_s dZ alpha, since sum_s dZ = 0 (softmax Jacobian);
+          // the right-hand form scales with alpha instead of cancelling
+          x = 0.f;
+          for (int s = 0; s < m; ++s) x -= sdZ[r * LDF + s] * (1.f - sW[r * LDF + s]);
+        }
+        sdQK[r * LDQK + c] = x;
+      }
+    }
+  }
+
+  // ---- Dk slices: QK, Ze, B1 accumulate; dq, dk slices written
+  f32x4 accQK[NRB], accZe[NSB], accB1[NSB];
+#pragma unroll
+  for (int c = 0; c < NRB; ++c) accQK[c] = zero4();
+#pragma unroll
+  for (int s = 0; s < NSB; ++s) accZe[s] = accB1[s] = zero4();
+  const T* qg = reinterpret_cast<const T*>(p.q) + kbase;
+  const T* kg = reinterpret_cast<const T*>(p.k) + kbase;
+  const T* s1 = reinterpret_cast<const T*>(p.S1s) + chunk * MP * DkP;
+  const T* ds1 = reinterpret_cast<const T*>(p.dS1s) + chunk * MP * DkP;
+  T* dqg = reinterpret_cast<T*>(p.dq) + kbase;
+  T* dkg = reinterpret_cast<T*>(p.dk) + kbase;
+  for (int ds = 0; ds < DkP / kDvTile; ++ds) {
+    __syncthreads();
+    slice_in<T>(sq, LDS, qg, Dk, CP, len, ds * kDvTile, Dk);
+    slice_in<T>(sk, LDS, kg, Dk, CP, len, ds * kDvTile, Dk);
+    slice_in<T>(sS1, LDS, s1, DkP, MP, MP, ds * kDvTile, DkP);
+    slice_in<T>(sdS1, LDS, ds1, DkP, MP, MP, ds * kDvTile, DkP);
+    __syncthreads();
+    if (rbv) {
+#pragma unroll
+      for (int kb = 0; kb < kDvTile / 32; ++kb) {
+        const Frag<T> Xq = ld8(sq + (16 * rb + col) * LDS + 32 * kb + 8 * grp);
+        const Frag<T> Xk = ld8(sk + (16 * rb + col) * LDS + 32 * kb + 8 * grp);
+#pragma unroll
+        for (int cb = 0; cb < NRB; ++cb)
+          if (cb <= rb) mma(accQK[cb], Xq, ld8(sk + (16 * cb + col) * LDS + 32 * kb + 8 * grp));
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) {
+          mma(accZe[sb], Xq, ld8(sS1 + (16 * sb + col) * LDS + 32 * kb + 8 * grp));
+          mma(accB1[sb], Xk, ld8(sdS1 + (16 * sb + col) * LDS + 32 * kb + 8 * grp));
+        }
+      }
+      // dq slice = dQK K + (dZ E) S1^T ; dk slice = dQK^T Q + (W Eg) dS1^T
+#pragma unroll
+      for (int ib = 0; ib < kDvTile / 16; ++ib) {
+        f32x4 aq = zero4(), ak = zero4();
+#pragma unroll
+        for (int kc = 0; kc < CP / 32; ++kc) {
+          float xa[8], xt[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xa[e] = sdQK[(16 * rb + col) * LDQK + 32 * kc + 8 * grp + e];
+            xt[e] = sdQK[(32 * kc + 8 * grp + e) * LDQK + 16 * rb + col];
+          }
+          mma(aq, frag_of<T>(xa), ld8_col(sk + (32 * kc + 8 * grp) * LDS + 16 * ib + col, LDS));
+          mma(ak, frag_of<T>(xt), ld8_col(sq + (32 * kc + 8 * grp) * LDS + 16 * ib + col, LDS));
+        }
+#pragma unroll
+        for (int ks = 0; ks < MP / 32; ++ks) {
+          float xa[8], xw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int s = 32 * ks + 8 * grp + e, r = 16 * rb + col;
+            xa[e] = sdZ[r * LDF + s] * fast_exp2(sB[r * LDF + s]);
+            xw[e] = sW[r * LDF + s] * fast_exp2(sGam[s] - sB[r * LDF + s]);
+          }
+          mma(aq, frag_of<T>(xa), ld8_col(sS1 + (32 * ks + 8 * grp) * LDS + 16 * ib + col, LDS));
+          mma(ak, frag_of<T>(xw), ld8_col(sdS1 + (32 * ks + 8 * grp) * LDS + 16 * ib + col, LDS));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sDQ[(16 * rb + 4 * grp + e) * LDS + 16 * ib + col] = from_f32<T>(aq[e]);
+          sDK[(16 * rb + 4 * grp + e) * LDS + 16 * ib + col] = from_f32<T>(ak[e]);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int PER_ROW = kDvTile / V;
+    for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
+      const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+      const int cc = ds * kDvTile + c;
+      if (r < len && cc < Dk) {
+        *reinterpret_cast<VT*>(dqg + (size_t)r * Dk + cc) = *reinterpret_cast<const VT*>(sDQ + r * LDS + c);
+        *reinterpret_cast<VT*>(dkg + (size_t)r * Dk + cc) = *reinterpret_cast<const VT*>(sDK + r * LDS + c);
+      }
+    }
+  }
+  __syncthreads();   // slices and dQK dead: sQK and the dg tiles take their bytes
+  if (rbv) {
+#pragma unroll
+    for (int cb = 0; cb < NRB; ++cb) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
+        sQK[r * LDQK + c] = c <= r ? accQK[cb][e] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- per element (rows of this wave): Znd, dW1', B1 -> u, y, dW1 total
+  if (rbv) {
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      f32x4 zi = zero4(), w1 = zero4();
+      if (fast) {
+#pragma unroll
+        for (int kc = 0; kc < CP / 32; ++kc) {
+          float xa[8], xb[8], xt[8], xd[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kk = 32 * kc + 8 * grp + e, r = 16 * rb + col, s = 16 * sb + col;
+            xa[e] = kk < r ? sQK[r * LDQK + kk] : 0.f;                      // QK' row r
+            xb[e] = sW[kk * LDF + s] * fast_exp2(-sB[kk * LDF + s]);       // (W Ei)[c][s]
+            xt[e] = kk > r ? sQK[kk * LDQK + r] : 0.f;                      // QK'^T row c = r
+            xd[e] = sdZ[kk * LDF + s] * fast_exp2(sB[kk * LDF + s]);       // (dZ E)[r'][s]
+          }
+          mma3(zi, hilo<T>(xa), hilo<T>(xb));
+          mma3(w1, hilo<T>(xt), hilo<T>(xd));
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * grp + e, s = 16 * sb + col;
+        const float br = sB[r * LDF + s];
+        float zip, dw1p;
+        if (fast) {
+          zip = fast_exp2(br) * zi[e];
+          dw1p = fast_exp2(-br) * w1[e];
+        } else {
+          zip = 0.f;
+          dw1p = 0.f;
+          for (int c = 0; c < r; ++c) zip += sQK[r * LDQK + c] * sW[c * LDF + s] * fast_exp2(br - sB[c * LDF + s]);
+          for (int c = r + 1; c < CP; ++c)
+            dw1p += sQK[c * LDQK + r] * sdZ[c * LDF + s] * fast_exp2(sB[c * LDF + s] - br);
+        }
+        const float znd = zip + fast_exp2(br) * accZe[sb][e];
+        const float b1 = fast_exp2(sGam[s] - br) * accB1[sb][e];
+        const float dz = sdZ[r * LDF + s], w = sW[r * LDF + s];
+        sU[r * LDF + s] = dz * znd - w * dw1p;
+        sY[r * LDF + s] = w * b1;
+        sD[r * LDF + s] = dw1p + sQK[r * LDQK + r] * dz + b1;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- dg: in-chunk suffix of u, exclusive prefix of y, Z1, pass-2 part, -alpha dW
+  float up[RPS][V], yk[RPS][V];
+  if (cs.active) {
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        up[u][e] = sU[(r0 + u) * LDF + c0 + e];
+        yk[u][e] = sY[(r0 + u) * LDF + c0 + e];
+      }
+    }
+    float sp[V], sk2[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) sp[e] = sk2[e] = 0.f;
+#pragma unroll
+    for (int u = RPS - 1; u >= 0; --u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        sp[e] += up[u][e];
+        up[u][e] = sp[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const float x = yk[u][e];
+        yk[u][e] = sk2[e];
+        sk2[e] += x;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      segtot[cs.seg * MP + c0 + e] = sp[e];
+      segtot[(NSEG + cs.seg) * MP + c0 + e] = sk2[e];
+    }
+  }
+  __syncthreads();
+  if (cs.active) {
+    float add[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) add[e] = sZ1[c0 + e];
+    for (int s2 = cs.seg + 1; s2 < NSEG; ++s2) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) add[e] += segtot[s2 * MP + c0 + e];
+    }
+    for (int s2 = 0; s2 < cs.seg; ++s2) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) add[e] += segtot[(NSEG + s2) * MP + c0 + e];
+    }
+    const T* dW2g = reinterpret_cast<const T*>(p.dW2) + gbase;
+    const float* dg2g = p.dg2 + gbase;
+    float* dgg = p.dg + gbase;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const int r = r0 + u;
+      if (r < len && c0 < m) {
+        const VT w2 = *reinterpret_cast<const VT*>(dW2g + (size_t)r * m + c0);
+#pragma unroll
+        for (int e = 0; e < V; e += 4) {
+          const f32x4 g2 = *reinterpret_cast<const f32x4*>(dg2g + (size_t)r * m + c0 + e);
+          f32x4 o;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const float alpha = fast_exp2(cs.qv[u][e + x] * kLog2e);
+            const float dwt = sD[r * LDF + c0 + e + x] + to_f32(w2[e + x]);
+            o[x] = up[u][e + x] + yk[u][e + x] + add[e + x] + g2[x] - alpha * dwt;
+          }
+          *reinterpret_cast<f32x4*>(dgg + (size_t)r * m + c0 + e) = o;
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------- launchers
+template <typename T, int MP, int CP>
+constexpr bool gsa_fits() {
+  return GsaCfg<T, MP, CP>::P_BYTES <= kMaxLds && GsaCfg<T, MP, CP>::B_BYTES <= kMaxLds &&
+         WalkIOCfg<T, MP, CP>::BYTES <= kMaxLds;
+}
+
+template <typename T, int MP, int CP>
+hipError_t launch_gsa_fwd(const GsaParams& p, hipStream_t s) {
+  if constexpr (!gsa_fits<T, MP, CP>()) {
+    return hipErrorNotSupported;
+  } else {
+    hipError_t e;
+    hipLaunchKernelGGL((gsa_prep_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    WalkIO w1{p.WdT, p.k, p.Gam, p.S1s, nullptr, nullptr, p.hk0, p.hkt, p.m, p.Dk, p.L, p.C, p.N, 1};
+    if ((e = launch_walk_store<T, MP, CP>(w1, p.BH, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    FwdParams f;
+    f.q = p.P; f.k = p.W; f.v = p.v; f.g = p.g; f.h0 = p.hv0; f.o = p.o; f.ht = p.hvt;
+    f.BH = p.BH; f.L = p.L; f.Dk = p.m; f.Dv = p.Dv; f.C = p.C; f.N = p.N;
+    f.ops = p.ops2; f.events = LaunchEvents{nullptr, 0};
+    return launch_gla_fwd<T, MP, CP>(f, s);
+  }
+}
+
+template <typename T, int MP, int CP>
+hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
+  if constexpr (!gsa_fits<T, MP, CP>()) {
+    return hipErrorNotSupported;
+  } else {
+    hipError_t e;
+    hipLaunchKernelGGL((gsa_prep_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    WalkIO w1{p.WdT, p.k, p.Gam, p.S1s, nullptr, nullptr, p.hk0, nullptr, p.m, p.Dk, p.L, p.C, p.N, 1};
+    if ((e = launch_walk_store<T, MP, CP>(w1, p.BH, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    BwdParams b;
+    b.q = p.P; b.k = p.W; b.v = p.v; b.g = p.g; b.do_ = p.do_; b.h0 = p.hv0; b.dht = p.dhvt;
+    b.dq = p.dP; b.dk = p.dW2; b.dv = p.dv; b.dg = p.dg2; b.dh0 = p.dhv0;
+    b.BH = p.BH; b.L = p.L; b.Dk = p.m; b.Dv = p.Dv; b.C = p.C; b.N = p.N;
+    b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.carry = p.carry2; b.events = LaunchEvents{nullptr, 0};
+    if ((e = launch_gla_bwd<T, MP, CP>(b, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL((gsa_dz_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    WalkIO w1r{p.dZsT, p.q, p.Gam, p.dS1s, p.S1s, p.Z1, p.dhkt, p.dhk0, p.m, p.Dk, p.L, p.C, p.N, 1};
+    if ((e = launch_walk_reverse<T, MP, CP>(w1r, p.BH, s)) != hipSuccess) return e;
+    const int ntk = p.DkP / kDvTile;
+    hipLaunchKernelGGL((gsa_pass1_bwd_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p, ntk);
+    return hipGetLastError();
+  }
+}
+
+bool gsa_config_fits(int esize, int MP, int CP) {
+  bool ok = false;
+#define GSA_FIT(TT, M_, C_) \
+  if (esize == (int)sizeof(TT) && MP == M_ && CP == C_) ok = gsa_fits<TT, M_, C_>();
+  GSA_FIT(bf16, 32, 32) GSA_FIT(bf16, 32, 64) GSA_FIT(bf16, 64, 32) GSA_FIT(bf16, 64, 64)
+  GSA_FIT(float, 32, 32) GSA_FIT(float, 32, 64) GSA_FIT(float, 64, 32) GSA_FIT(float, 64, 64)
+#undef GSA_FIT
+  return ok;
+}
+
+#define GSA_INST(TT, M_, C_)                                                          \
+  template hipError_t launch_gsa_fwd<TT, M_, C_>(const GsaParams&, hipStream_t); \
+  template hipError_t launch_gsa_bwd<TT, M_, C_>(const GsaParams&, hipStream_t);
+GSA_INST(bf16, 32, 32) GSA_INST(bf16, 32, 64) GSA_INST(bf16, 64, 32) GSA_INST(bf16, 64, 64)
+GSA_INST(float, 32, 32) GSA_INST(float, 32, 64) GSA_INST(float, 64, 32) GSA_INST(float, 64, 64)
+
+}  // namespace gla

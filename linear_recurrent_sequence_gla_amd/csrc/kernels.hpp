@@ -48,6 +48,34 @@ struct BwdParams {
   LaunchEvents events;
 };
 
+// Gated slot attention: pass 1 runs on its own kernels, pass 2 on the GLA kernels.
+struct GsaParams {
+  const void *q, *k, *v, *g, *do_;
+  const float *hk0, *hv0, *dhkt, *dhvt;
+  void* o;
+  float *hkt, *hvt;
+  void *dq, *dk, *dv;
+  float *dg, *dhk0, *dhv0;
+  int BH, L, Dk, DkP, Dv, m, C, N;
+  // workspace
+  void* W;        // [BH][L][m] write weights 1 - exp(g)   (keys of pass 2)   (T)
+  void* P;        // [BH][L][m] slot softmax              (queries of pass 2) (T)
+  float* Pf;      // [BH][L][m] the same softmax in fp32 (backward only, for its Jacobian)
+  void* dP;       // [BH][L][m] gradient of P (backward)                       (T)
+  void* dW2;      // [BH][L][m] pass-2 gradient of W (backward)                (T)
+  float* dg2;     // [BH][L][m] pass-2 decay gradient (backward)
+  float* dZ;      // [BH][L][m] gradient of the softmax input (backward)
+  void* WdT;      // [BH][N][MP][CP] (W 2^{Gamma-b})^T                         (T)
+  float* Gam;     // [BH][N][MP]
+  void* S1s;      // [BH][N][MP][DkP] pass-1 state S1^T at chunk starts        (T)
+  void* dS1s;     // [BH][N][MP][DkP] its gradient at chunk ends (backward)    (T)
+  void* dZsT;     // [BH][N][MP][CP] (dZ 2^b)^T (backward)                     (T)
+  float* Z1;      // [BH][N][DkP/64][MP] pass-1 decay gradient partials (backward)
+  ChunkOps ops2;  // pass-2 GLA chunk operands
+  void *Hs2, *dHs2;
+  float* carry2;
+};
+
 struct DecodeParams {
   const void *q, *k, *v, *g;
   float* state;
@@ -70,9 +98,15 @@ hipError_t launch_gla_decode(const DecodeParams& p, hipStream_t s);
 
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 
+template <typename T, int MP, int CP>
+hipError_t launch_gsa_fwd(const GsaParams& p, hipStream_t s);
+template <typename T, int MP, int CP>
+hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s);
+bool gsa_config_fits(int esize, int MP, int CP);
+
 // Kernel launches per call (for the profiled entry points).
 constexpr int GLA_FWD_LAUNCHES = 2;
-constexpr int GLA_BWD_MAX_LAUNCHES = 4;
+constexpr int GLA_BWD_MAX_LAUNCHES = 5;
 int bwd_launch_count(int esize, int DKP, int CP);
 
 // Whether every kernel of the forward fits the LDS of a CU for this (dtype size, DKP, CP).

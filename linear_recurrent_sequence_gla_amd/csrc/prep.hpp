@@ -139,7 +139,8 @@ __device__ __forceinline__ typename V16<T>::type zero_vec() {
 // vectors (16-byte, all issued before first use), keeps b (log2 units) and the raw q and k
 // of its rows and channels, publishes Gamma in sGam and returns the block-wide max |b|.
 // Must be called by all 256 threads.
-template <typename T, int DKP, int CP>
+// With LOAD_QK = false only g is loaded, and qv holds the raw gate values instead of q.
+template <typename T, int DKP, int CP, bool LOAD_QK = true>
 struct ChunkScan {
   using M = ChunkMap<T, DKP, CP>;
   static constexpr int V = M::V, RPS = M::RPS;
@@ -165,8 +166,13 @@ struct ChunkScan {
       const bool ok = chv && r < len;
       const size_t off = (size_t)r * ld + cg * V;
       gvec[u] = ok ? *reinterpret_cast<const VT*>(gg + off) : zero_vec<T>();
-      qvec[u] = ok ? *reinterpret_cast<const VT*>(qg + off) : zero_vec<T>();
-      kvec[u] = ok ? *reinterpret_cast<const VT*>(kg + off) : zero_vec<T>();
+      if constexpr (LOAD_QK) {
+        qvec[u] = ok ? *reinterpret_cast<const VT*>(qg + off) : zero_vec<T>();
+        kvec[u] = ok ? *reinterpret_cast<const VT*>(kg + off) : zero_vec<T>();
+      } else {
+        qvec[u] = gvec[u];
+        kvec[u] = zero_vec<T>();
+      }
     }
     float run_[V];
 #pragma unroll

@@ -92,8 +92,8 @@ def test_workspace_sizes(lib):
     assert lib.gla_fwd_workspace_bytes(B, H, L, Dk, Dv, C, 1) == expect
     assert lib.gla_bwd_workspace_bytes(B, H, L, Dk, Dv, C, 1) > expect
     assert lib.gla_fwd_workspace_bytes(1, 1, 64, 16, 16, 48, 1) == 0
-    assert lib.gla_bwd_launch_count(B, H, L, Dk, Dv, C, 1) == 3
-    assert lib.gla_bwd_launch_count(4, 4, 4096, 256, 512, 64, 1) == 4
+    assert lib.gla_bwd_launch_count(B, H, L, Dk, Dv, C, 1) == 4
+    assert lib.gla_bwd_launch_count(4, 4, 4096, 256, 512, 64, 1) == 5
 
 
 def test_decode_validation(lib):

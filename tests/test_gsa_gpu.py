@@ -1,0 +1,145 @@
+"""GPU parity of gated slot attention (two passes on the GPU) against the fp64 oracle, which
+evaluates the slot memories directly, token by token."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import gsa_recurrent_bwd, gsa_recurrent_fwd
+from tests.helpers import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gla():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_recurrent_sequence_gla_amd as m
+    m.lib()
+    return m
+
+
+def check_gsa(gla, w, x, units=None, with_state=True, with_dstate=True):
+    dt = w.dtype
+    args = [dev(x[n], dt) for n in ("q", "k", "v", "g")]
+    hk0 = dev(x["hk0"]) if with_state else None
+    hv0 = dev(x["hv0"]) if with_state else None
+    o, hkt, hvt = gla.gsa_fwd(*args, C=w.C, hk0=hk0, hv0=hv0)
+    dq, dk, dv, dg, dhk0, dhv0 = gla.gsa_bwd(*args, dev(x["do"], dt), C=w.C, hk0=hk0, hv0=hv0,
+                                             dhkt=dev(x["dhkt"]) if with_dstate else None,
+                                             dhvt=dev(x["dhvt"]) if with_dstate else None, want_dh0=True)
+    sel = (slice(None), slice(None)) if units is None else units
+    s0 = (lambda a: None if (a is None or not with_state) else a[sel])
+    ro, rhk, rhv = gsa_recurrent_fwd(x["q"][sel], x["k"][sel], x["v"][sel], x["g"][sel], s0(x["hk0"]), s0(x["hv0"]))
+    rb = gsa_recurrent_bwd(x["q"][sel], x["k"][sel], x["v"][sel], x["g"][sel], x["do"][sel], s0(x["hk0"]),
+                           s0(x["hv0"]), x["dhkt"][sel] if with_dstate else None,
+                           x["dhvt"][sel] if with_dstate else None)
+    print(f"[{w.name}] B={w.B} H={w.H} L={x['q'].shape[2]} Dk={w.Dk} Dv={w.Dv} m={w.m} C={w.C} {dt} "
+          f"h0={with_state} dht={with_dstate}", flush=True)
+    assert_close("o", host(o)[sel], ro, dt)
+    assert_close("hkt", host(hkt)[sel], rhk, dt)
+    assert_close("hvt", host(hvt)[sel], rhv, dt)
+    assert_close("dq", host(dq)[sel], rb["dq"], dt)
+    assert_close("dk", host(dk)[sel], rb["dk"], dt)
+    assert_close("dv", host(dv)[sel], rb["dv"], dt)
+    assert_close("dg", host(dg)[sel], rb["dg"], dt)
+    assert_close("dhk0", host(dhk0)[sel], rb["dhk0"], dt)
+    assert_close("dhv0", host(dhv0)[sel], rb["dhv0"], dt)
+
+
+SHAPES = [
+    # (B, H, L, Dk, Dv, m, C, dtype, h0, dht)
+    (1, 2, 150, 64, 64, 32, 64, "bf16", True, True),
+    (2, 1, 77, 32, 48, 16, 16, "bf16", True, True),
+    (1, 2, 130, 128, 128, 64, 32, "bf16", False, False),
+    (1, 1, 200, 96, 160, 48, 64, "bf16", True, True),
+    (1, 2, 1, 64, 64, 64, 64, "bf16", True, True),
+    (1, 2, 64, 128, 128, 64, 64, "bf16", True, False),
+    (1, 1, 90, 256, 64, 32, 32, "bf16", True, True),
+    (2, 1, 70, 32, 32, 32, 16, "f32", True, True),
+    (1, 2, 100, 64, 96, 64, 32, "f32", True, True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_small_shapes(gla, shape):
+    B, H, L, Dk, Dv, m, C, dt, h0, dht = shape
+    w = W.GsaWorkload("sweep", B, H, L, Dk, Dv, m, C, dt, 300 + L + m, h0=True)
+    check_gsa(gla, w, W.gsa_inputs(w), with_state=h0, with_dstate=dht)
+
+
+@pytest.mark.parametrize("gval", [-3.0, -30.0])
+def test_extreme_gates(gla, gval):
+    """Strong forgetting on every other slot (normal gates on the rest): every chunk fails the
+    span check and takes the exact intra-chunk path, while the slots still differ."""
+    w = W.GsaWorkload("gates", 1, 2, 150, 64, 64, 32, 64, "bf16", 31, h0=True)
+    x = W.gsa_inputs(w)
+    x["g"][..., ::2] = gval
+    check_gsa(gla, w, x)
+
+
+def test_identical_slots_degenerate(gla):
+    """The same gate g = -30 on every slot makes all slots identical: z is uniform, the
+    softmax gradient vanishes, and dq, dk, dg are analytically ~1e-13 of the gradient scale.
+    Check the outputs that stay O(1) to the bound and the vanishing ones against the scale."""
+    w = W.GsaWorkload("degenerate", 1, 2, 150, 64, 64, 32, 64, "bf16", 35, h0=True)
+    x = W.gsa_inputs(w)
+    x["g"] = np.full_like(x["g"], -30.0)
+    args = [dev(x[n], "bf16") for n in ("q", "k", "v", "g")]
+    hk0, hv0 = dev(x["hk0"]), dev(x["hv0"])
+    o, hkt, hvt = gla.gsa_fwd(*args, C=64, hk0=hk0, hv0=hv0)
+    dq, dk, dv, dg, _, dhv0 = gla.gsa_bwd(*args, dev(x["do"], "bf16"), C=64, hk0=hk0, hv0=hv0,
+                                          dhkt=dev(x["dhkt"]), dhvt=dev(x["dhvt"]), want_dh0=True)
+    ro, rhk, rhv = gsa_recurrent_fwd(x["q"], x["k"], x["v"], x["g"], x["hk0"], x["hv0"])
+    rb = gsa_recurrent_bwd(x["q"], x["k"], x["v"], x["g"], x["do"], x["hk0"], x["hv0"], x["dhkt"], x["dhvt"])
+    assert_close("o", host(o), ro, "bf16")
+    assert_close("hvt", host(hvt), rhv, "bf16")
+    assert_close("dv", host(dv), rb["dv"], "bf16")
+    assert_close("dhv0", host(dhv0), rb["dhv0"], "bf16")
+    scale = np.max(np.abs(rb["dv"]))
+    for name, t in (("dq", dq), ("dk", dk), ("dg", dg)):
+        e = np.max(np.abs(host(t) - rb[name])) / scale
+        print(f"  {name}: max|d| / max|dv_ref| = {e:.3e}", flush=True)
+        assert e <= 1e-2, name
+
+
+def test_open_gates_zero_state_gives_zero(gla):
+    """g = 0 means w = 0: with zero initial memories nothing is ever written, so o = 0."""
+    import torch
+    w = W.GsaWorkload("open", 1, 2, 100, 64, 64, 32, 64, "bf16", 32)
+    x = W.gsa_inputs(w, with_grad=False)
+    o, hkt, hvt = gla.gsa_fwd(dev(x["q"], "bf16"), dev(x["k"], "bf16"), dev(x["v"], "bf16"),
+                              dev(np.zeros_like(x["g"]), "bf16"), C=64)
+    torch.cuda.synchronize()
+    assert float(o.abs().max()) == 0.0 and float(hkt.abs().max()) == 0.0 and float(hvt.abs().max()) == 0.0
+
+
+def test_mixed_chunks(gla):
+    w = W.GsaWorkload("mixed", 1, 2, 256, 64, 64, 64, 64, "bf16", 33, h0=True)
+    x = W.gsa_inputs(w)
+    x["g"][:, :, 64:128] = -2.0
+    x["g"][:, 1, 200:210, :5] = -40.0
+    check_gsa(gla, w, x)
+
+
+def test_full_size_config_sampled(gla):
+    """The GSA workload (B=8, H=4, L=2048, Dk=Dv=128, m=64, C=64), sampled units."""
+    w = W.WORKLOADS["gsa_340m"]
+    x = W.gsa_inputs(w)
+    units = (np.array([0, 5])[:, None], np.array([1, 3])[None, :])
+    check_gsa(gla, w, x, units=units, with_state=False, with_dstate=False)
+
+
+def test_deterministic(gla):
+    import torch
+    w = W.GsaWorkload("det", 2, 2, 300, 64, 64, 64, 64, "bf16", 34)
+    x = W.gsa_inputs(w)
+    args = [dev(x[n], "bf16") for n in ("q", "k", "v", "g", "do")]
+    a = gla.gsa_bwd(*args, C=64)
+    b = gla.gsa_bwd(*args, C=64)
+    fa = gla.gsa_fwd(*args[:4], C=64)
+    fb = gla.gsa_fwd(*args[:4], C=64)
+    torch.cuda.synchronize()
+    assert all(torch.equal(s, t) for s, t in zip(a[:4], b[:4]))
+    assert all(torch.equal(s, t) for s, t in zip(fa, fb))
