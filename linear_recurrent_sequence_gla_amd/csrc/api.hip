@@ -131,18 +131,17 @@ size_t fwd_ws_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
 
 struct BwdLayout {
   OpsLayout ops;
-  size_t hs, dhs, carry, total;
+  size_t hs, dhs, total;
 };
 
 BwdLayout bwd_layout(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
   const size_t BH = (size_t)B * H, CP = pad_c(C), DKP = pad_dk(Dk), N = (L + C - 1) / C;
-  const size_t es = esize_of(dtype), DVP = pad_dv(Dv), NT = DVP / kDvTile;
+  const size_t es = esize_of(dtype), DVP = pad_dv(Dv);
   BwdLayout l;
   l.ops = ops_layout(BH, N, CP, DKP, es, true);
   size_t off = l.ops.total;
   l.hs = off;    off += align_up(BH * N * DKP * DVP * es);
   l.dhs = off;   off += align_up(BH * N * DKP * DVP * es);
-  l.carry = off; off += align_up(BH * N * NT * DKP * 4);
   l.total = off;
   return l;
 }
@@ -238,7 +237,6 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* g, const f
   p.ops = carve_ops(ws, lay.ops, true);
   p.Hs = ws + lay.hs;
   p.dHs = ws + lay.dhs;
-  p.carry = reinterpret_cast<float*>(ws + lay.carry);
   p.events = ev;
   if (dispatch_bwd(dtype, DKP, CP, p, static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
@@ -326,7 +324,7 @@ int check_gsa(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, bool
 }
 
 struct GsaLayout {
-  size_t W, P, Pf, dP, dW2, dg2, dZ, WdT, Gam, S1s, dS1s, dZsT, Z1, ops2base, Hs2, dHs2, carry2, total;
+  size_t W, P, Pf, dP, dW2, dg2, dZ, WdT, Gam, S1s, dS1s, dZsT, ops2base, Hs2, dHs2, total;
   OpsLayout ops2;
 };
 
@@ -350,14 +348,12 @@ GsaLayout gsa_layout(int B, int H, int L, int Dk, int Dv, int m, int C, int dtyp
     l.dZ = take(tok * 4);
     l.dS1s = take(BH * N * MP * DkP * es);
     l.dZsT = take(BH * N * MP * CP * es);
-    l.Z1 = take(BH * N * (DkP / kDvTile) * MP * 4);
   }
   l.ops2 = ops_layout(BH, N, CP, MP, es, bwd);
   l.ops2base = take(l.ops2.total);
   if (bwd) {
     l.Hs2 = take(BH * N * MP * DvP * es);
     l.dHs2 = take(BH * N * MP * DvP * es);
-    l.carry2 = take(BH * N * (DvP / kDvTile) * MP * 4);
   }
   l.total = off;
   return l;
@@ -372,8 +368,8 @@ GsaParams gsa_params(const GsaLayout& l, char* ws, int B, int H, int L, int Dk, 
     p.Pf = reinterpret_cast<float*>(ws + l.Pf);
     p.dP = ws + l.dP; p.dW2 = ws + l.dW2;
     p.dg2 = reinterpret_cast<float*>(ws + l.dg2); p.dZ = reinterpret_cast<float*>(ws + l.dZ);
-    p.dS1s = ws + l.dS1s; p.dZsT = ws + l.dZsT; p.Z1 = reinterpret_cast<float*>(ws + l.Z1);
-    p.Hs2 = ws + l.Hs2; p.dHs2 = ws + l.dHs2; p.carry2 = reinterpret_cast<float*>(ws + l.carry2);
+    p.dS1s = ws + l.dS1s; p.dZsT = ws + l.dZsT;
+    p.Hs2 = ws + l.Hs2; p.dHs2 = ws + l.dHs2;
   }
   p.ops2 = carve_ops(ws + l.ops2base, l.ops2, bwd);
   return p;

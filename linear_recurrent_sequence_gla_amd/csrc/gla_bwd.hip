@@ -20,17 +20,18 @@
 // of dk, B_c = 2^{Gamma - b_c} (V dH_{n+1}^T)_c (the inter part of dk), and
 // Z_n = 2^{Gamma_n} rowsum(dH_{n+1} * H_n) is the gradient through the chunk's state decay
 // (everything beyond the chunk is folded into dH_{n+1}).  Every surviving term carries the
-// decay factors that contain alpha_t, so its rounding scales with dg itself.  The reverse
-// state walk emits Z_n per chunk; the chunk kernel does the two in-chunk prefix sums.
+// decay factors that contain alpha_t, so its rounding scales with dg itself.  The chunk
+// kernel forms Z_n from the H_n and dH_{n+1} tiles it stages anyway, and does the two
+// in-chunk prefix sums.
 //
 // Launches:
 //   1. gla_prep_kernel (also writes QsT)                      grid N x BH
 //   2. walk_store: forward state walk storing H_n               grid ceil(Dv/64) * BH
-//   3. walk_reverse: reverse walk storing dH_{n+1} and Z_n       grid ceil(Dv/64) * BH
+//   3. walk_reverse: reverse walk storing dH_{n+1}              grid ceil(Dv/64) * BH
 //      (walks.hpp; state slices in fp32 MFMA accumulators)
 //   4. gla_bwd_chunk: dA, dq, dk (+ dv when the whole key width fits one workgroup) on MFMA
 //      over 64-column slices of Dv, then an element-wise epilogue (gate scaling, diagonal
-//      terms, the two in-chunk prefix sums of dg, Z_n) with 16-byte stores
+//      terms, Z_n, the two in-chunk prefix sums of dg) with 16-byte stores
 //                                                              grid N x BH x (Dk slices)
 //   5. gla_bwd_dv (only when dv did not fit step 4)           grid N x BH x ceil(Dv/64)
 // Intra-chunk terms use the factorised form only on chunks whose gate span passes the same
@@ -100,6 +101,14 @@ struct SliceStage {
       const size_t off = (size_t)r * DVP + js * kDvTile + c;
       hv[m] = ok ? *reinterpret_cast<const VT*>(hs + off) : zero_vec<T>();
       dhv[m] = ok ? *reinterpret_cast<const VT*>(dhs + off) : zero_vec<T>();
+    }
+  }
+  // z[m] += this thread's share of rowsum(H * dH) for the state tile it stages
+  __device__ __forceinline__ void zdot(float (&z)[Cf::PH]) const {
+#pragma unroll
+    for (int m = 0; m < Cf::PH; ++m) {
+#pragma unroll
+      for (int e = 0; e < Cf::V; ++e) z[m] += to_f32(hv[m][e]) * to_f32(dhv[m][e]);
     }
   }
   __device__ __forceinline__ void store(T* sdO, T* sV, T* sH, T* sdH) const {
@@ -176,12 +185,6 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
   const T* hs = reinterpret_cast<const T*>(p.Hs) + (chunk * DKP + ch0) * DVP;
   const T* dhs = reinterpret_cast<const T*>(p.dHs) + (chunk * DKP + ch0) * DVP;
 
-  // Z_n = sum over Dv tiles of 2^Gamma rowsum(dH_{n+1} * H_n)
-  for (int i = tid; i < DKS; i += 256) {
-    float z = 0.f;
-    for (int t = 0; t < ntile; ++t) z += p.carry[(chunk * ntile + t) * DKP + ch0 + i];
-    sZ[i] = z;
-  }
   ChunkScan<T, DKS, CP> cs;
   const float maxb = cs.run(qg, kg, reinterpret_cast<const T*>(p.g) + qbase, Dk, Dk - ch0, len, segtot, sGam, red);
   const bool fast = maxb <= kSpanLimit;
@@ -207,6 +210,10 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
     }
   }
   if constexpr (WITH_DV) tile_in_dense<T>(sA, reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP, CP, CP, LDC);
+  float zp[Cf::PH];
+#pragma unroll
+  for (int m = 0; m < Cf::PH; ++m) zp[m] = 0.f;
+  st.zdot(zp);
   st.store(sdO, sV, sH, sdH);
   __syncthreads();
 
@@ -271,8 +278,22 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
           *reinterpret_cast<VT*>(dvg + (size_t)r * Dv + jj) = *reinterpret_cast<const VT*>(sdV + r * LDV + c);
       }
     }
-    if (js + 1 < ntile) st.store(sdO, sV, sH, sdH);
+    if (js + 1 < ntile) {
+      st.zdot(zp);
+      st.store(sdO, sV, sH, sdH);
+    }
     __syncthreads();
+  }
+  {  // Z_n = 2^Gamma rowsum(dH_{n+1} * H_n): reduce over the lanes that staged one state row
+    constexpr int PER_ROW = kDvTile / V;
+#pragma unroll
+    for (int m = 0; m < Cf::PH; ++m) {
+      float z = zp[m];
+#pragma unroll
+      for (int off = 1; off < PER_ROW; off <<= 1) z += __shfl_xor(z, off, 64);
+      const int idx = tid + 256 * m, r = idx / PER_ROW;
+      if (idx < Cf::NH && idx % PER_ROW == 0) sZ[r] = r < kvalid ? z * fast_exp2(sGam[r]) : 0.f;
+    }
   }
 
   // strictly lower dA -> LDS, its diagonal kept apart in fp32
@@ -528,10 +549,10 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     record_event(p.events, 1, s);
     const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
-    WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, nullptr, nullptr, p.h0, nullptr, p.Dk, p.Dv, p.L, p.C, p.N, 0};
+    WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, nullptr, p.Dk, p.Dv, p.L, p.C, p.N, 0};
     if ((e = launch_walk_store<T, DKP, CP>(wf, p.BH, s)) != hipSuccess) return e;
     record_event(p.events, 2, s);
-    WalkIO wr{p.ops.QsT, p.do_, p.ops.Gam, p.dHs, p.Hs, p.carry, p.dht, p.dh0, p.Dk, p.Dv, p.L, p.C, p.N, 0};
+    WalkIO wr{p.ops.QsT, p.do_, p.ops.Gam, p.dHs, p.dht, p.dh0, p.Dk, p.Dv, p.L, p.C, p.N, 0};
     if ((e = launch_walk_reverse<T, DKP, CP>(wr, p.BH, s)) != hipSuccess) return e;
     record_event(p.events, 3, s);
     hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED>), dim3(p.N, p.BH, DKP / P::DKS), dim3(256), 0, s,

@@ -372,11 +372,6 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
   const size_t kbase = ((size_t)bh * p.L + row0) * Dk;
   const T* gg = reinterpret_cast<const T*>(p.g) + gbase;
 
-  for (int s = tid; s < MP; s += 256) {
-    float z = 0.f;
-    for (int t = 0; t < ntk; ++t) z += p.Z1[(chunk * ntk + t) * MP + s];
-    sZ1[s] = z;
-  }
   ChunkScan<T, MP, CP, false> cs;
   const bool fast = cs.run(gg, gg, gg, m, m, len, segtot, sGam, red) <= kSpanLimit;
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
@@ -456,13 +451,22 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
   const T* ds1 = reinterpret_cast<const T*>(p.dS1s) + chunk * MP * DkP;
   T* dqg = reinterpret_cast<T*>(p.dq) + kbase;
   T* dkg = reinterpret_cast<T*>(p.dk) + kbase;
-  for (int ds = 0; ds < DkP / kDvTile; ++ds) {
+  float z1 = 0.f;                        // this thread's share of colsum(dS1 * S1): slot tid/4
+  const int zs = tid >> 2, zq = tid & 3;
+  for (int ds = 0; ds < ntk; ++ds) {
     __syncthreads();
     slice_in<T>(sq, LDS, qg, Dk, CP, len, ds * kDvTile, Dk);
     slice_in<T>(sk, LDS, kg, Dk, CP, len, ds * kDvTile, Dk);
     slice_in<T>(sS1, LDS, s1, DkP, MP, MP, ds * kDvTile, DkP);
     slice_in<T>(sdS1, LDS, ds1, DkP, MP, MP, ds * kDvTile, DkP);
     __syncthreads();
+    if (zs < MP) {
+#pragma unroll
+      for (int c = 0; c < kDvTile / 4; ++c) {
+        const int o = zs * LDS + zq * (kDvTile / 4) + c;
+        z1 += to_f32(sS1[o]) * to_f32(sdS1[o]);
+      }
+    }
     if (rbv) {
 #pragma unroll
       for (int kb = 0; kb < kDvTile / 32; ++kb) {
@@ -522,6 +526,10 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
       }
     }
   }
+  // Z1_n = 2^Gamma colsum(dS1_{n+1} * S1_n), one slot per four lanes
+  z1 += __shfl_xor(z1, 1, 64);
+  z1 += __shfl_xor(z1, 2, 64);
+  if (zq == 0 && zs < MP) sZ1[zs] = zs < m ? z1 * fast_exp2(sGam[zs]) : 0.f;
   __syncthreads();   // slices and dQK dead: sQK and the dg tiles take their bytes
   if (rbv) {
 #pragma unroll
@@ -672,7 +680,7 @@ hipError_t launch_gsa_fwd(const GsaParams& p, hipStream_t s) {
     hipError_t e;
     hipLaunchKernelGGL((gsa_prep_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    WalkIO w1{p.WdT, p.k, p.Gam, p.S1s, nullptr, nullptr, p.hk0, p.hkt, p.m, p.Dk, p.L, p.C, p.N, 1};
+    WalkIO w1{p.WdT, p.k, p.Gam, p.S1s, p.hk0, p.hkt, p.m, p.Dk, p.L, p.C, p.N, 1};
     if ((e = launch_walk_store<T, MP, CP>(w1, p.BH, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -692,7 +700,7 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
     hipError_t e;
     hipLaunchKernelGGL((gsa_prep_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    WalkIO w1{p.WdT, p.k, p.Gam, p.S1s, nullptr, nullptr, p.hk0, nullptr, p.m, p.Dk, p.L, p.C, p.N, 1};
+    WalkIO w1{p.WdT, p.k, p.Gam, p.S1s, p.hk0, nullptr, p.m, p.Dk, p.L, p.C, p.N, 1};
     if ((e = launch_walk_store<T, MP, CP>(w1, p.BH, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -700,11 +708,11 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
     b.q = p.P; b.k = p.W; b.v = p.v; b.g = p.g; b.do_ = p.do_; b.h0 = p.hv0; b.dht = p.dhvt;
     b.dq = p.dP; b.dk = p.dW2; b.dv = p.dv; b.dg = p.dg2; b.dh0 = p.dhv0;
     b.BH = p.BH; b.L = p.L; b.Dk = p.m; b.Dv = p.Dv; b.C = p.C; b.N = p.N;
-    b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.carry = p.carry2; b.events = LaunchEvents{nullptr, 0};
+    b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.events = LaunchEvents{nullptr, 0};
     if ((e = launch_gla_bwd<T, MP, CP>(b, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((gsa_dz_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    WalkIO w1r{p.dZsT, p.q, p.Gam, p.dS1s, p.S1s, p.Z1, p.dhkt, p.dhk0, p.m, p.Dk, p.L, p.C, p.N, 1};
+    WalkIO w1r{p.dZsT, p.q, p.Gam, p.dS1s, p.dhkt, p.dhk0, p.m, p.Dk, p.L, p.C, p.N, 1};
     if ((e = launch_walk_reverse<T, MP, CP>(w1r, p.BH, s)) != hipSuccess) return e;
     const int ntk = p.DkP / kDvTile;
     hipLaunchKernelGGL((gsa_pass1_bwd_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p, ntk);

@@ -44,7 +44,6 @@ struct BwdParams {
   ChunkOps ops;
   void* Hs;       // [BH][N][DKP][DvP] state at chunk starts (T)
   void* dHs;      // [BH][N][DKP][DvP] state gradient at chunk ends (T)
-  float* carry;   // [BH][N][NT][DKP]  partial Z_n = 2^Gamma sum_j dH_{n+1} H_n, per Dv tile
   LaunchEvents events;
 };
 
@@ -70,10 +69,8 @@ struct GsaParams {
   void* S1s;      // [BH][N][MP][DkP] pass-1 state S1^T at chunk starts        (T)
   void* dS1s;     // [BH][N][MP][DkP] its gradient at chunk ends (backward)    (T)
   void* dZsT;     // [BH][N][MP][CP] (dZ 2^b)^T (backward)                     (T)
-  float* Z1;      // [BH][N][DkP/64][MP] pass-1 decay gradient partials (backward)
   ChunkOps ops2;  // pass-2 GLA chunk operands
   void *Hs2, *dHs2;
-  float* carry2;
 };
 
 struct DecodeParams {

@@ -5,7 +5,6 @@
 //   walk_store    S_0 = init;  for n = 0..N-1:  store S_n (bf16/T),
 //                              S_{n+1} = Diag(2^{Gamma_n}) S_n + M_n X_n ;  fin = S_N
 //   walk_reverse  D_N = init;  for n = N-1..0:  store D_{n+1},
-//                              Z_n += 2^{Gamma_n} rowsum(D_{n+1} * S_n)   (this tile's share),
 //                              D_n = Diag(2^{Gamma_n}) D_{n+1} + M_n X_n ;  fin = D_0
 //
 // with M_n = mat[n] a per-chunk [SP][CP] matrix (the decayed keys transposed for the forward
@@ -26,8 +25,6 @@ struct WalkIO {
   const void* src;     // [BH][L][Ds] token tensor (T)
   const float* gam;    // [BH][N][SP] chunk log2-decay per state row
   void* states;        // [BH][N][SP][DsP] stored states / state gradients (T)
-  const void* hin;     // reverse only: [BH][N][SP][DsP] chunk-start states (T)
-  float* zout;         // reverse only: [BH][N][NT][SP] partial Z_n per 64-column tile
   const float* init;   // fp32 [BH][rows][Ds] (or [BH][Ds][rows] when trans) or nullptr (= 0)
   float* fin;          // fp32, same layout, or nullptr (= not written)
   int rows, Ds, L, C, N, trans;
@@ -40,7 +37,7 @@ struct WalkIOCfg {
   static constexpr size_t KT = (size_t)SP * LDA * sizeof(T);
   static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
   static constexpr size_t HT = (size_t)SP * LDV * sizeof(T);
-  static constexpr size_t BYTES = KT + VT + 2 * HT + (size_t)SP * 4 + (size_t)4 * SP * 4;
+  static constexpr size_t BYTES = KT + VT + HT + (size_t)SP * 4;
   static constexpr int NK = SP * CP / V, NV = CP * kDvTile / V, NH = SP * kDvTile / V;
   static constexpr int PKd = (NK + 255) / 256, PV = (NV + 255) / 256, PH = (NH + 255) / 256;
 };
@@ -49,13 +46,12 @@ template <typename T, int SP, int CP>
 struct WalkIOStage {
   using W = WalkIOCfg<T, SP, CP>;
   typedef typename V16<T>::type VT;
-  VT kt[W::PKd], v[W::PV], h[W::PH];
+  VT kt[W::PKd], v[W::PV];
   f32x4 gam;
 
-  // mat: [SP][CP] of this chunk; src: [L][Ds] of this (b,h); htile: [SP][DsP] tile at this
-  // workgroup's columns, or nullptr.
+  // mat: [SP][CP] of this chunk; src: [L][Ds] of this (b,h).
   __device__ __forceinline__ void load(const T* mat, const T* src, int row0, int len, int Ds, int tile,
-                                       const float* gam_chunk, const T* htile, int DsP) {
+                                       const float* gam_chunk) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < W::PKd; ++m) {
@@ -71,18 +67,10 @@ struct WalkIOStage {
       v[m] = (idx < W::NV && r < len && j < Ds) ? *reinterpret_cast<const VT*>(src + (size_t)(row0 + r) * Ds + j)
                                                 : zero_vec<T>();
     }
-    if (htile) {
-#pragma unroll
-      for (int m = 0; m < W::PH; ++m) {
-        const int idx = tid + 256 * m;
-        const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
-        if (idx < W::NH) h[m] = *reinterpret_cast<const VT*>(htile + (size_t)r * DsP + c);
-      }
-    }
     if (tid < SP / 4) gam = *reinterpret_cast<const f32x4*>(gam_chunk + 4 * tid);
   }
 
-  __device__ __forceinline__ void store(T* sKT, T* sV, T* sHi, float* sG, bool with_h) const {
+  __device__ __forceinline__ void store(T* sKT, T* sV, float* sG) const {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < W::PKd; ++m) {
@@ -99,16 +87,6 @@ struct WalkIOStage {
       if (idx < W::NV) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
         *reinterpret_cast<VT*>(sV + r * W::LDV + c) = v[m];
-      }
-    }
-    if (with_h) {
-#pragma unroll
-      for (int m = 0; m < W::PH; ++m) {
-        const int idx = tid + 256 * m;
-        if (idx < W::NH) {
-          const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
-          *reinterpret_cast<VT*>(sHi + r * W::LDV + c) = h[m];
-        }
       }
     }
     if (tid < SP / 4) *reinterpret_cast<f32x4*>(sG + 4 * tid) = gam;
@@ -160,8 +138,7 @@ __global__ __launch_bounds__(256) void walk_store(WalkIO w, int ntile) {
   T* sKT = reinterpret_cast<T*>(smem);
   T* sV = reinterpret_cast<T*>(smem + W::KT);
   T* sHo = reinterpret_cast<T*>(smem + W::KT + W::VT);
-  T* sHi = reinterpret_cast<T*>(smem + W::KT + W::VT + W::HT);
-  float* sG = reinterpret_cast<float*>(smem + W::KT + W::VT + 2 * W::HT);
+  float* sG = reinterpret_cast<float*>(smem + W::KT + W::VT + W::HT);
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = lin % ntile, bh = lin / ntile;
@@ -185,14 +162,13 @@ __global__ __launch_bounds__(256) void walk_store(WalkIO w, int ntile) {
     }
   }
   WalkIOStage<T, SP, CP> st;
-  st.load(mat, src, 0, min(C, L), Ds, tile, gam, nullptr, DsP);
-  st.store(sKT, sV, sHi, sG, false);
+  st.load(mat, src, 0, min(C, L), Ds, tile, gam);
+  st.store(sKT, sV, sG);
   __syncthreads();
   for (int n = 0; n < N; ++n) {
     if (n + 1 < N) {
       const int r1 = (n + 1) * C;
-      st.load(mat + (size_t)(n + 1) * SP * CP, src, r1, min(C, L - r1), Ds, tile, gam + (size_t)(n + 1) * SP,
-              nullptr, DsP);
+      st.load(mat + (size_t)(n + 1) * SP * CP, src, r1, min(C, L - r1), Ds, tile, gam + (size_t)(n + 1) * SP);
     }
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) {
@@ -202,7 +178,7 @@ __global__ __launch_bounds__(256) void walk_store(WalkIO w, int ntile) {
     walk_step<T, SP, CP>(S, sKT, sV, sG);
     __syncthreads();
     state_tile_out<T, SP>(out + (size_t)n * SP * DsP, sHo, LDV, DsP);
-    if (n + 1 < N) st.store(sKT, sV, sHi, sG, false);
+    if (n + 1 < N) st.store(sKT, sV, sG);
     __syncthreads();
   }
   if (w.fin && jv) {
@@ -225,9 +201,7 @@ __global__ __launch_bounds__(256) void walk_reverse(WalkIO w, int ntile) {
   T* sKT = reinterpret_cast<T*>(smem);
   T* sV = reinterpret_cast<T*>(smem + W::KT);
   T* sHo = reinterpret_cast<T*>(smem + W::KT + W::VT);
-  T* sHi = reinterpret_cast<T*>(smem + W::KT + W::VT + W::HT);
-  float* sG = reinterpret_cast<float*>(smem + W::KT + W::VT + 2 * W::HT);
-  float* sRed = sG + SP;
+  float* sG = reinterpret_cast<float*>(smem + W::KT + W::VT + W::HT);
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = lin % ntile, bh = lin / ntile;
@@ -239,7 +213,6 @@ __global__ __launch_bounds__(256) void walk_reverse(WalkIO w, int ntile) {
   const T* src = reinterpret_cast<const T*>(w.src) + (size_t)bh * L * Ds;
   const T* mat = reinterpret_cast<const T*>(w.mat) + (size_t)bh * N * SP * CP;
   const float* gam = w.gam + (size_t)bh * N * SP;
-  const T* hin = reinterpret_cast<const T*>(w.hin) + (size_t)bh * N * SP * DsP + tile * kDvTile;
   T* out = reinterpret_cast<T*>(w.states) + (size_t)bh * N * SP * DsP + tile * kDvTile;
 
   f32x4 D[NIB];
@@ -254,38 +227,24 @@ __global__ __launch_bounds__(256) void walk_reverse(WalkIO w, int ntile) {
   WalkIOStage<T, SP, CP> st;
   {
     const int r1 = (N - 1) * C;
-    st.load(mat + (size_t)(N - 1) * SP * CP, src, r1, L - r1, Ds, tile, gam + (size_t)(N - 1) * SP,
-            hin + (size_t)(N - 1) * SP * DsP, DsP);
-    st.store(sKT, sV, sHi, sG, true);
+    st.load(mat + (size_t)(N - 1) * SP * CP, src, r1, L - r1, Ds, tile, gam + (size_t)(N - 1) * SP);
+    st.store(sKT, sV, sG);
   }
   __syncthreads();
   for (int n = N - 1; n >= 0; --n) {
     if (n > 0) {
       const int r1 = (n - 1) * C;
-      st.load(mat + (size_t)(n - 1) * SP * CP, src, r1, C, Ds, tile, gam + (size_t)(n - 1) * SP,
-              hin + (size_t)(n - 1) * SP * DsP, DsP);
+      st.load(mat + (size_t)(n - 1) * SP * CP, src, r1, C, Ds, tile, gam + (size_t)(n - 1) * SP);
     }
-    // Z partial: 2^Gamma * sum over this tile's 64 columns of D_{n+1} * S_n
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * ib + 4 * grp + e;
-        float x = D[ib][e] * to_f32(sHi[i * LDV + 16 * wave + col]);
-        x += __shfl_xor(x, 1, 64);
-        x += __shfl_xor(x, 2, 64);
-        x += __shfl_xor(x, 4, 64);
-        x += __shfl_xor(x, 8, 64);
-        if (col == 0) sRed[wave * SP + i] = x * fast_exp2(sG[i]);
-        sHo[i * LDV + 16 * wave + col] = from_f32<T>(D[ib][e]);
-      }
+      for (int e = 0; e < 4; ++e) sHo[(16 * ib + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(D[ib][e]);
     }
     walk_step<T, SP, CP>(D, sKT, sV, sG);
     __syncthreads();
-    for (int i = tid; i < SP; i += 256)
-      w.zout[(((size_t)bh * N + n) * ntile + tile) * SP + i] = sRed[i] + sRed[SP + i] + sRed[2 * SP + i] + sRed[3 * SP + i];
     state_tile_out<T, SP>(out + (size_t)n * SP * DsP, sHo, LDV, DsP);
-    if (n > 0) st.store(sKT, sV, sHi, sG, true);
+    if (n > 0) st.store(sKT, sV, sG);
     __syncthreads();
   }
   if (w.fin && jv) {
