@@ -272,13 +272,15 @@ def summarize_pmc(paths, kernel_sub, calib_sub, calib_bytes, cmd, out_json, out_
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the kernels whose name contains kernel_sub,
     scaled by what the same counters read for a copy kernel of known size (calib_sub)."""
     import csv
-    vals = {}
+    vals, every = {}, {}
     for p in paths:
         for r in csv.DictReader(open(p)):
             name, ctr, v = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
             key = "kernel" if kernel_sub in name else ("calib" if calib_sub in name else None)
             if key:
                 vals.setdefault((key, ctr), []).append(v)
+            if name.startswith("_ZN3gla"):
+                every.setdefault(name, {}).setdefault(ctr, []).append(v)
     res = {}
     for ctr, label in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
         kk = vals.get(("kernel", ctr))
@@ -298,6 +300,14 @@ def summarize_pmc(paths, kernel_sub, calib_sub, calib_bytes, cmd, out_json, out_
     for label, r in res.items():
         lines.append(f"| {label} | {r['kib_per_dispatch']:.0f} | {r['calib_kib']:.0f} | {r['scale']:.3f} | "
                      f"{r['bytes'] / 1e6:.1f} MB |")
+    if "read" in res and "write" in res:
+        lines += ["", "Every kernel of the library in the same runs (scaled the same way):", "",
+                  "| kernel | read MB | write MB |", "|---|---|---|"]
+        for name, c in every.items():
+            if "FETCH_SIZE" in c and "WRITE_SIZE" in c:
+                rd = np.median(c["FETCH_SIZE"]) * 1024.0 * res["read"]["scale"] / 1e6
+                wr = np.median(c["WRITE_SIZE"]) * 1024.0 * res["write"]["scale"] / 1e6
+                lines.append(f"| `{name[:70]}` | {rd:.1f} | {wr:.1f} |")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
