@@ -4,11 +4,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
 
 One step is one pass of the training hot path over one batch of the 340M-layer workload
-(B=8, H=4, L=2048, Dk=128, Dv=256, chunk C=64, bf16 inputs, fp32 accumulation): gla_fwd
-(chunk preparation + state walk) then gla_bwd (chunk preparation, state walks, chunk
-gradients) on inputs already resident in HBM, outputs and workspaces preallocated.  The
-timed region is exactly K steps between two device synchronisations; per-kernel durations
-come from HIP events the library records at its own kernel boundaries on the same stream.
+(B=8, H=4, L=2048, Dk=128, Dv=256, chunk C=64, bf16 inputs, fp32 accumulation): the forward
+(gla_fwd_save: chunk preparation + state walk, keeping the chunk operands and chunk-start
+states) then the backward (gla_bwd_saved: reverse state walk + chunk gradients) on inputs
+already resident in HBM, outputs and buffers preallocated.  The timed region is exactly K
+steps between two device synchronisations; per-kernel durations come from HIP events the
+library records at its own kernel boundaries on the same stream.
 
 Prints ONE JSON line: tokens/s (B*L per step), % of bf16 MFMA peak at the algorithmic flop
 count, the roofline of the dominant kernel, the fp64 oracle timed on this host's cores on a
@@ -70,7 +71,7 @@ def kernel_alg_bytes(B, H, L, Dk, Dv, s=2):
     return {
         "fwd.prep": u * s * 3 * Dk,                            # q, k, g
         "fwd.walk": u * s * 2 * Dv,                            # v in, o out
-        "bwd.prep": u * s * 3 * Dk,                            # q, k, g
+        "bwd.prep": u * s * 3 * Dk,                            # q, k, g (self-contained backward)
         "bwd.walk_fwd": u * s * Dv,                            # v
         "bwd.walk_rev": u * s * Dv,                            # do
         "bwd.chunk": u * (s * (3 * Dk + 2 * Dv) + s * (2 * Dk + Dv) + 4 * Dk),  # all but h0/dh0
@@ -153,30 +154,23 @@ def run_gla(torch, m, steps, warmup):
     dv = torch.empty(B, H, L, Dv, device="cuda", dtype=dt)
     dg = torch.empty(B, H, L, Dk, device="cuda", dtype=torch.float32)
     lib = m.lib()
-    wsf = torch.empty(lib.gla_fwd_workspace_bytes(B, H, L, Dk, Dv, C, 1), dtype=torch.uint8, device="cuda")
-    wsb = torch.empty(lib.gla_bwd_workspace_bytes(B, H, L, Dk, Dv, C, 1), dtype=torch.uint8, device="cuda")
-    nb = lib.gla_bwd_launch_count(B, H, L, Dk, Dv, C, 1)
+    sv = torch.empty(lib.gla_saved_bytes(B, H, L, Dk, Dv, C, 1), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(lib.gla_bwd_saved_workspace_bytes(B, H, L, Dk, Dv, C, 1), dtype=torch.uint8, device="cuda")
+    nb = lib.gla_bwd_launch_count(B, H, L, Dk, Dv, C, 1) - 2      # the saved backward skips two
     P = lambda t: None if t is None else __import__("ctypes").c_void_p(t.data_ptr())
     stream = __import__("ctypes").c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def step(evf=None, evb=None):
-        if evf is None:
-            m._check(lib.gla_fwd(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(o), P(ht),
-                                 B, H, L, Dk, Dv, C, 1, P(wsf), wsf.numel(), stream))
-            m._check(lib.gla_bwd(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(d["do"]), None,
-                                 P(dq), P(dk), P(dv), P(dg), None, B, H, L, Dk, Dv, C, 1, P(wsb), wsb.numel(),
-                                 stream))
-        else:
-            m._check(lib.gla_fwd_profiled(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(o), P(ht),
-                                          B, H, L, Dk, Dv, C, 1, P(wsf), wsf.numel(), stream, evf, 3))
-            m._check(lib.gla_bwd_profiled(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(d["do"]), None,
-                                          P(dq), P(dk), P(dv), P(dg), None, B, H, L, Dk, Dv, C, 1, P(wsb),
-                                          wsb.numel(), stream, evb, 6))
+        m._check(lib.gla_fwd_save(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(o), P(ht),
+                                  B, H, L, Dk, Dv, C, 1, P(sv), sv.numel(), stream, evf, 3 if evf else 0))
+        m._check(lib.gla_bwd_saved(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(d["do"]), None,
+                                   P(dq), P(dk), P(dv), P(dg), None, B, H, L, Dk, Dv, C, 1, P(sv), sv.numel(),
+                                   P(wsb), wsb.numel(), stream, evb, 4 if evb else 0))
 
     for _ in range(warmup):
         step()
     ef = [_events(torch, 3) for _ in range(steps)]
-    eb = [_events(torch, 6) for _ in range(steps)]
+    eb = [_events(torch, 4) for _ in range(steps)]                 # room for the most launches
     hf = [_handles(e) for e in ef]
     hb = [_handles(e) for e in eb]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -188,7 +182,7 @@ def run_gla(torch, m, steps, warmup):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     names_f = ["fwd.prep", "fwd.walk"]
-    names_b = ["bwd.prep", "bwd.walk_fwd", "bwd.walk_rev", "bwd.chunk", "bwd.dv"][:nb]
+    names_b = ["bwd.walk_rev", "bwd.chunk", "bwd.dv"][:nb]
     kt = {}
     for i, nme in enumerate(names_f):
         kt[nme] = float(np.mean([ef[k][i].elapsed_time(ef[k][i + 1]) for k in range(steps)]))
@@ -401,8 +395,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{WORKLOAD}: GLA fwd+bwd, B={B} H={H} L={L} Dk={Dk} Dv={Dv} C={C}, bf16 "
-                               "inputs, fp32 accumulation, no initial state",
+        "config": {"workload": f"{WORKLOAD}: GLA fwd+bwd (forward keeps chunk operands and states for the "
+                               f"backward), B={B} H={H} L={L} Dk={Dk} Dv={Dv} C={C}, bf16 inputs, fp32 "
+                               "accumulation, no initial state",
                    "B": B, "H": H, "L": L, "Dk": Dk, "Dv": Dv, "C": C},
         "pct_bf16_mfma_peak": round(100 * tflops * 1e12 / PEAK_BF16_FLOPS, 3),
         "tflops": round(tflops, 3),

@@ -125,6 +125,42 @@ int gla_bwd_profiled(const void* q, const void* k, const void* v, const void* g,
 /* Number of kernels gla_bwd launches for these sizes (0 if unsupported). */
 int gla_bwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype);
 
+/* ---------------------------------------------------------------- GLA saved activations --
+ * A training step runs the forward and then the backward on the same q, k, v, g, h0.  The
+ * backward needs the per-chunk operands (decayed queries and keys, Gamma, the intra-chunk
+ * scores) and the state at every chunk start; gla_bwd recomputes them (one preparation and
+ * one forward state walk), which gla_fwd_save / gla_bwd_saved avoid by keeping them:
+ *
+ *   gla_fwd_save   computes exactly what gla_fwd computes (o, ht) and also leaves the chunk
+ *                  operands and the chunk-start states H_n (the sequential inter-chunk state
+ *                  of the chunkwise form, MS-GLA summary section 2.1) in `saved`.
+ *   gla_bwd_saved  computes exactly what gla_bwd computes, reading them from `saved`.
+ *
+ * saved: device buffer of at least gla_saved_bytes() bytes, owned by the caller; its contents
+ *   on entry to gla_fwd_save do not matter, and gla_bwd_saved only reads it.  It is valid
+ *   for the q, k, g, h0, C and dtype of the gla_fwd_save call that filled it; passing other
+ *   inputs to gla_bwd_saved gives undefined results (the library cannot check this).  The
+ *   states take B*H*ceil(L/C)*pad(Dk)*pad(Dv) elements of dtype (pad(Dv) = Dv rounded up to
+ *   64, pad(Dk) = 32, 64, 128 or 256), about 130 MB at B=8, H=4, L=2048, Dk=128, Dv=256.
+ * workspace (gla_bwd_saved): at least gla_bwd_saved_workspace_bytes() bytes.
+ * events / nevents: optional (NULL, 0) launch-boundary events as for gla_*_profiled:
+ *   gla_fwd_save launches 2 kernels (nevents >= 3), gla_bwd_saved launches
+ *   gla_bwd_launch_count() - 2 kernels (nevents >= 4).
+ * Sizes, dtypes, alignment and errors as for gla_bwd (the saved path supports the sizes the
+ * backward supports); `saved` must not overlap any input or output (GLA_ERR_ALIAS). */
+size_t gla_saved_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype);
+size_t gla_bwd_saved_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype);
+int gla_fwd_save(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                 void* o, float* ht,
+                 int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                 void* saved, size_t saved_bytes, void* stream, void** events, int nevents);
+int gla_bwd_saved(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                  const void* do_, const float* dht,
+                  void* dq, void* dk, void* dv, float* dg, float* dh0,
+                  int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                  const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                  void* stream, void** events, int nevents);
+
 /* ---------------------------------------------------------------- GLA decode -----------
  * One recurrent inference step per (batch, head): the O(1)-memory form of the recurrence
  * (MS-GLA summary, section 1; GSA abstract: efficient recurrent inference).

@@ -7,6 +7,9 @@ or PyTorch fallback: if the library is missing or cannot be loaded every call ra
 Entry points (same names as the C ABI):
     gla_fwd(q, k, v, g, C=64, h0=None, output_final_state=True) -> (o, ht)
     gla_bwd(q, k, v, g, do, C=64, h0=None, dht=None, want_dh0=False) -> (dq, dk, dv, dg, dh0)
+    gla_fwd_save(q, k, v, g, C=64, h0=None, output_final_state=True) -> (o, ht, saved)
+    gla_bwd_saved(q, k, v, g, do, saved, C=64, h0=None, dht=None, want_dh0=False)
+        -> (dq, dk, dv, dg, dh0)             (saved: what gla_fwd_save left for these inputs)
     gla_decode_step(q, k, v, g, state) -> o                     (state updated in place)
     gsa_fwd(q, k, v, g, C=64, hk0=None, hv0=None, output_final_state=True) -> (o, hkt, hvt)
     gsa_bwd(q, k, v, g, do, C=64, hk0=None, hv0=None, dhkt=None, dhvt=None, want_dh0=False)
@@ -22,7 +25,8 @@ from typing import Optional
 import torch  # imported first so the library binds to the HIP runtime torch already loaded
 
 __all__ = [
-    "lib", "lib_path", "GlaError", "gla_fwd", "gla_bwd", "gla_decode_step", "gsa_fwd", "gsa_bwd",
+    "lib", "lib_path", "GlaError", "gla_fwd", "gla_bwd", "gla_fwd_save", "gla_bwd_saved", "gla_decode_step",
+    "gsa_fwd", "gsa_bwd", "gla_saved_bytes", "gla_bwd_saved_workspace_bytes",
     "gla_fwd_workspace_bytes", "gla_bwd_workspace_bytes", "gsa_fwd_workspace_bytes",
     "gsa_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
@@ -48,6 +52,10 @@ _SIGS = {
     "gla_fwd_profiled": (_I, [_P] * 7 + [_I] * 7 + [_P, _Z, _P, _P, _I]),
     "gla_bwd_profiled": (_I, [_P] * 12 + [_I] * 7 + [_P, _Z, _P, _P, _I]),
     "gla_bwd_launch_count": (_I, [_I] * 7),
+    "gla_saved_bytes": (_Z, [_I] * 7),
+    "gla_bwd_saved_workspace_bytes": (_Z, [_I] * 7),
+    "gla_fwd_save": (_I, [_P] * 7 + [_I] * 7 + [_P, _Z, _P, _P, _I]),
+    "gla_bwd_saved": (_I, [_P] * 12 + [_I] * 7 + [_P, _Z, _P, _Z, _P, _P, _I]),
     "gla_decode_step": (_I, [_P] * 6 + [_I] * 5 + [_P]),
     "gsa_fwd_workspace_bytes": (_Z, [_I] * 8),
     "gsa_fwd": (_I, [_P] * 9 + [_I] * 8 + [_P, _Z, _P]),
@@ -143,6 +151,14 @@ def gla_bwd_workspace_bytes(B, H, L, Dk, Dv, C, dtype) -> int:
     return int(lib().gla_bwd_workspace_bytes(B, H, L, Dk, Dv, C, _DT[dtype]))
 
 
+def gla_saved_bytes(B, H, L, Dk, Dv, C, dtype) -> int:
+    return int(lib().gla_saved_bytes(B, H, L, Dk, Dv, C, _DT[dtype]))
+
+
+def gla_bwd_saved_workspace_bytes(B, H, L, Dk, Dv, C, dtype) -> int:
+    return int(lib().gla_bwd_saved_workspace_bytes(B, H, L, Dk, Dv, C, _DT[dtype]))
+
+
 def gsa_fwd_workspace_bytes(B, H, L, Dk, Dv, m, C, dtype) -> int:
     return int(lib().gsa_fwd_workspace_bytes(B, H, L, Dk, Dv, m, C, _DT[dtype]))
 
@@ -198,6 +214,60 @@ def gla_bwd(q, k, v, g, do, C: int = 64, h0=None, dht=None, want_dh0: bool = Fal
     _check(L_.gla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(do), _ptr(dht),
                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dh0),
                       B, H, L, Dk, Dv, C, _DT[dt], _ptr(ws), ws.numel(), _stream(dev)))
+    return dq, dk, dv, dg, dh0
+
+
+def gla_fwd_save(q, k, v, g, C: int = 64, h0=None, output_final_state: bool = True, *,
+                 out=None, ht_out=None, saved=None):
+    """gla_fwd that also keeps the chunk operands and chunk-start states for gla_bwd_saved.
+    Returns (o, ht, saved)."""
+    B, H, L, Dk, Dv, dev, dt = _common(q, k, v, g)
+    if h0 is not None:
+        _need(h0, "h0", (B, H, Dk, Dv), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, H, L, Dv), dtype=dt, device=dev)
+    _need(o, "out", (B, H, L, Dv), dt, dev)
+    ht = None
+    if output_final_state:
+        ht = ht_out if ht_out is not None else torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+        _need(ht, "ht_out", (B, H, Dk, Dv), torch.float32, dev)
+    L_ = lib()
+    nbytes = L_.gla_saved_bytes(B, H, L, Dk, Dv, C, _DT[dt])
+    if nbytes == 0:
+        _check(L_.gla_fwd_save(*([None] * 7), B, H, L, Dk, Dv, C, _DT[dt], None, 0, None, None, 0))
+    sv = _workspace(nbytes, dev, saved)
+    _check(L_.gla_fwd_save(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(o), _ptr(ht),
+                           B, H, L, Dk, Dv, C, _DT[dt], _ptr(sv), sv.numel(), _stream(dev), None, 0))
+    return o, ht, sv
+
+
+def gla_bwd_saved(q, k, v, g, do, saved, C: int = 64, h0=None, dht=None, want_dh0: bool = False, *,
+                  workspace=None, outs=None):
+    """gla_bwd reusing what gla_fwd_save left in `saved` for the same q, k, v, g, h0 and C."""
+    B, H, L, Dk, Dv, dev, dt = _common(q, k, v, g)
+    _need(do, "do", (B, H, L, Dv), dt, dev)
+    if h0 is not None:
+        _need(h0, "h0", (B, H, Dk, Dv), torch.float32, dev)
+    if dht is not None:
+        _need(dht, "dht", (B, H, Dk, Dv), torch.float32, dev)
+    if outs is None:
+        dq = torch.empty((B, H, L, Dk), dtype=dt, device=dev)
+        dk = torch.empty((B, H, L, Dk), dtype=dt, device=dev)
+        dv = torch.empty((B, H, L, Dv), dtype=dt, device=dev)
+        dg = torch.empty((B, H, L, Dk), dtype=torch.float32, device=dev)
+        dh0 = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if want_dh0 else None
+    else:
+        dq, dk, dv, dg, dh0 = outs
+    L_ = lib()
+    nbytes = L_.gla_bwd_saved_workspace_bytes(B, H, L, Dk, Dv, C, _DT[dt])
+    if nbytes == 0:
+        _check(L_.gla_bwd_saved(*([None] * 12), B, H, L, Dk, Dv, C, _DT[dt], None, 0, None, 0, None, None, 0))
+    if not isinstance(saved, torch.Tensor) or saved.device != dev:
+        raise ValueError(f"saved must be the tensor gla_fwd_save returned, on {dev}")
+    ws = _workspace(nbytes, dev, workspace)
+    _check(L_.gla_bwd_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(do), _ptr(dht),
+                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dh0),
+                            B, H, L, Dk, Dv, C, _DT[dt], _ptr(saved), saved.numel() * saved.element_size(),
+                            _ptr(ws), ws.numel(), _stream(dev), None, 0))
     return dq, dk, dv, dg, dh0
 
 

@@ -134,6 +134,28 @@ struct BwdLayout {
   size_t hs, dhs, total;
 };
 
+// What gla_fwd_save leaves for gla_bwd_saved: the chunk operands (with Qs^T) and the
+// chunk-start states.  The saved-state backward's own workspace holds only dH.
+struct SavedLayout {
+  OpsLayout ops;
+  size_t hs, total;
+};
+
+SavedLayout saved_layout(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  const size_t BH = (size_t)B * H, CP = pad_c(C), DKP = pad_dk(Dk), N = (L + C - 1) / C;
+  const size_t es = esize_of(dtype), DVP = pad_dv(Dv);
+  SavedLayout l;
+  l.ops = ops_layout(BH, N, CP, DKP, es, true);
+  l.hs = l.ops.total;
+  l.total = l.hs + align_up(BH * N * DKP * DVP * es);
+  return l;
+}
+
+size_t bwd_saved_ws_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  const size_t BH = (size_t)B * H, DKP = pad_dk(Dk), N = (L + C - 1) / C;
+  return align_up(BH * N * DKP * pad_dv(Dv) * esize_of(dtype));
+}
+
 BwdLayout bwd_layout(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
   const size_t BH = (size_t)B * H, CP = pad_c(C), DKP = pad_dk(Dk), N = (L + C - 1) / C;
   const size_t es = esize_of(dtype), DVP = pad_dv(Dv);
@@ -205,6 +227,34 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* g, const f
   p.q = q; p.k = k; p.v = v; p.g = g; p.h0 = h0; p.o = o; p.ht = ht;
   p.BH = (int)BH; p.L = L; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
   p.ops = carve_ops(static_cast<char*>(workspace), ops_layout(BH, N, CP, DKP, es, false), false);
+  p.Hs = nullptr;
+  p.events = ev;
+  if (dispatch_fwd(dtype, DKP, CP, p, static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+int fwd_save_impl(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                  void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                  void* saved, size_t saved_bytes, void* stream, LaunchEvents ev) {
+  int st = check_dims(B, H, L, Dk, Dv, C, dtype);
+  if (st != GLA_OK) return st;
+  if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return GLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !o) return GLA_ERR_NULL_ARG;
+  if (!all_aligned({q, k, v, g, h0, o, ht, saved})) return GLA_ERR_UNSUPPORTED;
+  const SavedLayout lay = saved_layout(B, H, L, Dk, Dv, C, dtype);
+  if (!saved || saved_bytes < lay.total) return GLA_ERR_WORKSPACE;
+  const size_t es = esize_of(dtype), BH = (size_t)B * H;
+  const size_t nk = BH * L * Dk * es, nv = BH * L * Dv * es, ns = BH * Dk * Dv * 4;
+  const Range ins[] = {{q, nk}, {k, nk}, {v, nv}, {g, nk}, {h0, h0 ? ns : 0}};
+  const Range outs[] = {{o, nv}, {ht, ht ? ns : 0}, {saved, lay.total}};
+  if (any_alias(outs, 3, ins, 5)) return GLA_ERR_ALIAS;
+
+  const int DKP = pad_dk(Dk), CP = pad_c(C), N = (L + C - 1) / C;
+  FwdParams p;
+  p.q = q; p.k = k; p.v = v; p.g = g; p.h0 = h0; p.o = o; p.ht = ht;
+  p.BH = (int)BH; p.L = L; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
+  p.ops = carve_ops(static_cast<char*>(saved), lay.ops, true);
+  p.Hs = static_cast<char*>(saved) + lay.hs;
   p.events = ev;
   if (dispatch_fwd(dtype, DKP, CP, p, static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
@@ -237,6 +287,44 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* g, const f
   p.ops = carve_ops(ws, lay.ops, true);
   p.Hs = ws + lay.hs;
   p.dHs = ws + lay.dhs;
+  p.saved = false;
+  p.events = ev;
+  if (dispatch_bwd(dtype, DKP, CP, p, static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+int bwd_saved_impl(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                   const void* do_, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                   float* dh0, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                   const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                   void* stream, LaunchEvents ev) {
+  int st = check_dims(B, H, L, Dk, Dv, C, dtype);
+  if (st != GLA_OK) return st;
+  if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return GLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !do_ || !dq || !dk || !dv || !dg) return GLA_ERR_NULL_ARG;
+  if (!all_aligned({q, k, v, g, h0, do_, dht, dq, dk, dv, dg, dh0, saved, workspace})) return GLA_ERR_UNSUPPORTED;
+  const SavedLayout lay = saved_layout(B, H, L, Dk, Dv, C, dtype);
+  if (!saved || saved_bytes < lay.total) return GLA_ERR_WORKSPACE;
+  const size_t wsb = bwd_saved_ws_bytes(B, H, L, Dk, Dv, C, dtype);
+  if (!workspace || workspace_bytes < wsb) return GLA_ERR_WORKSPACE;
+  const size_t es = esize_of(dtype), BH = (size_t)B * H;
+  const size_t nk = BH * L * Dk * es, nv = BH * L * Dv * es, ns = BH * Dk * Dv * 4;
+  const Range ins[] = {{q, nk},   {k, nk},           {v, nv},   {g, nk},
+                       {h0, h0 ? ns : 0}, {do_, nv}, {dht, dht ? ns : 0}, {saved, lay.total}};
+  const Range outs[] = {{dq, nk}, {dk, nk}, {dv, nv}, {dg, BH * L * Dk * 4}, {dh0, dh0 ? ns : 0},
+                        {workspace, wsb}};
+  if (any_alias(outs, 6, ins, 8)) return GLA_ERR_ALIAS;
+
+  const int DKP = pad_dk(Dk), CP = pad_c(C), N = (L + C - 1) / C;
+  BwdParams p;
+  p.q = q; p.k = k; p.v = v; p.g = g; p.do_ = do_; p.h0 = h0; p.dht = dht;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dh0 = dh0;
+  p.BH = (int)BH; p.L = L; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
+  char* sv = const_cast<char*>(static_cast<const char*>(saved));   // read only on this path
+  p.ops = carve_ops(sv, lay.ops, true);
+  p.Hs = sv + lay.hs;
+  p.dHs = workspace;
+  p.saved = true;
   p.events = ev;
   if (dispatch_bwd(dtype, DKP, CP, p, static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
@@ -276,6 +364,36 @@ int gla_bwd_profiled(const void* q, const void* k, const void* v, const void* g,
   if (!events || nevents < GLA_BWD_MAX_LAUNCHES + 1) return GLA_ERR_NULL_ARG;
   return bwd_impl(q, k, v, g, h0, do_, dht, dq, dk, dv, dg, dh0, B, H, L, Dk, Dv, C, dtype, workspace,
                   workspace_bytes, stream, LaunchEvents{events, nevents});
+}
+
+size_t gla_saved_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
+  if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return 0;
+  return saved_layout(B, H, L, Dk, Dv, C, dtype).total;
+}
+
+size_t gla_bwd_saved_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
+  if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return 0;
+  return bwd_saved_ws_bytes(B, H, L, Dk, Dv, C, dtype);
+}
+
+int gla_fwd_save(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                 void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                 void* saved, size_t saved_bytes, void* stream, void** events, int nevents) {
+  if (events && nevents < GLA_FWD_LAUNCHES + 1) return GLA_ERR_NULL_ARG;
+  return fwd_save_impl(q, k, v, g, h0, o, ht, B, H, L, Dk, Dv, C, dtype, saved, saved_bytes, stream,
+                       LaunchEvents{events, events ? nevents : 0});
+}
+
+int gla_bwd_saved(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                  const void* do_, const float* dht, void* dq, void* dk, void* dv, float* dg,
+                  float* dh0, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                  const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                  void* stream, void** events, int nevents) {
+  if (events && nevents < GLA_BWD_MAX_LAUNCHES - 1) return GLA_ERR_NULL_ARG;
+  return bwd_saved_impl(q, k, v, g, h0, do_, dht, dq, dk, dv, dg, dh0, B, H, L, Dk, Dv, C, dtype, saved,
+                        saved_bytes, workspace, workspace_bytes, stream, LaunchEvents{events, events ? nevents : 0});
 }
 
 int gla_bwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype) {

@@ -42,17 +42,21 @@ namespace gla {
 
 // ======================================================================= chunk gradients
 // LDS phases of the chunk kernel:
-//   front   sdA [CP][CP] (written after the Dv loop, read to the end), diagonal of dA (fp32)
-//   phase 1 (Dv loop)    sQs, sKs (+ sKd, sA with dv) and the double Dv slice tiles
-//   phase 3 (epilogue)   three fp32 [CP][DKS] gradient tiles and, on the exact path, b
+//   front   sdA, sdA^T [CP][CP] (written after the Dv loop, read to the end), diag of dA (fp32)
+//   phase 1 (Dv loop)    sKd, sA (with dv) and the Dv slice tiles dO, V, H, dH (+ dV)
+//   phase 2 (intra)      Qs^T, Ks^T [DKS][CP] for the intra-chunk products
+//   phase 3 (epilogue)   three fp32 [CP][DKS] gradient tiles; on the exact path b takes the
+//                        place of the (unused) intra dk tile
 constexpr size_t chunk_bwd_bytes(int es, int DKS, int CP, bool dv, int nseg) {
   const size_t V = 16 / es;
   const size_t LDQ = DKS + V, LDC = CP + V, LDV = kDvTile + V, LDF = DKS + 4;
   const size_t QT = CP * LDQ * es, CT = CP * LDC * es, VT = CP * LDV * es, HT = DKS * LDV * es;
-  const size_t FT = CP * LDF * 4;
-  const size_t ph1 = 2 * QT + (dv ? QT + CT : 0) + 2 * VT + 2 * HT + (dv ? VT : 0);
-  const size_t ph3 = 3 * FT + (size_t)CP * DKS * 4;
-  return CT + (ph1 > ph3 ? ph1 : ph3) + (size_t)(2 * nseg * DKS + 2 * DKS + CP + 8) * 4;
+  const size_t TT = DKS * LDC * es, FT = CP * LDF * 4;
+  const size_t ph1 = (dv ? QT + CT : 0) + 2 * VT + 2 * HT + (dv ? VT : 0);
+  const size_t ph2 = 2 * TT;
+  const size_t ph3 = 3 * FT;
+  const size_t mx = ph1 > ph2 ? (ph1 > ph3 ? ph1 : ph3) : (ph2 > ph3 ? ph2 : ph3);
+  return 2 * CT + mx + (size_t)(2 * nseg * DKS + 2 * DKS + CP + 8) * 4;
 }
 
 template <typename T, int DKS, int CP, bool WITH_DV>
@@ -64,20 +68,27 @@ struct BwdChunkCfg {
   static constexpr size_t CT = (size_t)CP * LDC * sizeof(T);
   static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
   static constexpr size_t HT = (size_t)DKS * LDV * sizeof(T);
+  static constexpr size_t TT = (size_t)DKS * LDC * sizeof(T);
   static constexpr size_t FT = (size_t)CP * LDF * 4;
-  static constexpr size_t PH1 = 2 * QT + (WITH_DV ? QT + CT : 0) + 2 * VT + 2 * HT + (WITH_DV ? VT : 0);
-  static constexpr size_t PH3 = 3 * FT + (size_t)CP * DKS * 4;
-  static constexpr size_t MAIN = CT + cmax(PH1, PH3);
+  static constexpr size_t PH1 = (WITH_DV ? QT + CT : 0) + 2 * VT + 2 * HT + (WITH_DV ? VT : 0);
+  static constexpr size_t PH2 = 2 * TT;
+  static constexpr size_t PH3 = 3 * FT;
+  static constexpr size_t MAIN = 2 * CT + cmax(cmax(PH1, PH2), PH3);
   static constexpr size_t BYTES = chunk_bwd_bytes(sizeof(T), DKS, CP, WITH_DV, M::NSEG);
   static constexpr int NV = CP * kDvTile / V, NH = DKS * kDvTile / V;
   static constexpr int PV = (NV + 255) / 256, PH = (NH + 255) / 256;
 };
 
+// One 64-column Dv slice of dO, V (chunk rows) and of H_n, dH_{n+1} (key rows) in flight.
+// Loads are unconditional from clamped in-bounds addresses; each vector's validity is kept
+// beside it and applied once the data is used, so no branch or register rewrite touches a
+// load in flight and the next slice's loads overlap the current slice's matrix work.
 template <typename T, int DKS, int CP, bool WITH_DV>
 struct SliceStage {
   using Cf = BwdChunkCfg<T, DKS, CP, WITH_DV>;
   typedef typename V16<T>::type VT;
   VT dov[Cf::PV], vv[Cf::PV], hv[Cf::PH], dhv[Cf::PH];
+  bool vok[Cf::PV], hok[Cf::PH];
 
   // dog/vg: rows of this chunk ([len][Dv]); hs/dhs: [DKS rows][DVP] state tiles of this chunk
   __device__ __forceinline__ void load(const T* dog, const T* vg, const T* hs, const T* dhs, int len, int Dv,
@@ -89,26 +100,29 @@ struct SliceStage {
       const int idx = tid + 256 * m;
       const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
       const int jj = js * kDvTile + c;
-      const bool ok = idx < Cf::NV && r < len && jj < Dv;
-      dov[m] = ok ? *reinterpret_cast<const VT*>(dog + (size_t)r * Dv + jj) : zero_vec<T>();
-      vv[m] = ok ? *reinterpret_cast<const VT*>(vg + (size_t)r * Dv + jj) : zero_vec<T>();
+      vok[m] = idx < Cf::NV && r < len && jj < Dv;
+      const size_t off = (size_t)min(r, len - 1) * Dv + min(jj, Dv - Cf::V);
+      dov[m] = *reinterpret_cast<const VT*>(dog + off);
+      vv[m] = *reinterpret_cast<const VT*>(vg + off);
     }
 #pragma unroll
     for (int m = 0; m < Cf::PH; ++m) {
       const int idx = tid + 256 * m;
       const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
-      const bool ok = idx < Cf::NH && r < kvalid;
-      const size_t off = (size_t)r * DVP + js * kDvTile + c;
-      hv[m] = ok ? *reinterpret_cast<const VT*>(hs + off) : zero_vec<T>();
-      dhv[m] = ok ? *reinterpret_cast<const VT*>(dhs + off) : zero_vec<T>();
+      hok[m] = idx < Cf::NH && r < kvalid;
+      const size_t off = (size_t)min(r, kvalid - 1) * DVP + js * kDvTile + c;
+      hv[m] = *reinterpret_cast<const VT*>(hs + off);
+      dhv[m] = *reinterpret_cast<const VT*>(dhs + off);
     }
   }
   // z[m] += this thread's share of rowsum(H * dH) for the state tile it stages
   __device__ __forceinline__ void zdot(float (&z)[Cf::PH]) const {
 #pragma unroll
     for (int m = 0; m < Cf::PH; ++m) {
+      float t = 0.f;
 #pragma unroll
-      for (int e = 0; e < Cf::V; ++e) z[m] += to_f32(hv[m][e]) * to_f32(dhv[m][e]);
+      for (int e = 0; e < Cf::V; ++e) t += to_f32(hv[m][e]) * to_f32(dhv[m][e]);
+      z[m] += hok[m] ? t : 0.f;
     }
   }
   __device__ __forceinline__ void store(T* sdO, T* sV, T* sH, T* sdH) const {
@@ -119,8 +133,8 @@ struct SliceStage {
       const int idx = tid + 256 * m;
       if (idx < Cf::NV) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
-        *reinterpret_cast<VT*>(sdO + r * Cf::LDV + c) = dov[m];
-        *reinterpret_cast<VT*>(sV + r * Cf::LDV + c) = vv[m];
+        *reinterpret_cast<VT*>(sdO + r * Cf::LDV + c) = vok[m] ? dov[m] : zero_vec<T>();
+        *reinterpret_cast<VT*>(sV + r * Cf::LDV + c) = vok[m] ? vv[m] : zero_vec<T>();
       }
     }
 #pragma unroll
@@ -128,8 +142,30 @@ struct SliceStage {
       const int idx = tid + 256 * m;
       if (idx < Cf::NH) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
-        *reinterpret_cast<VT*>(sH + r * Cf::LDV + c) = hv[m];
-        *reinterpret_cast<VT*>(sdH + r * Cf::LDV + c) = dhv[m];
+        *reinterpret_cast<VT*>(sH + r * Cf::LDV + c) = hok[m] ? hv[m] : zero_vec<T>();
+        *reinterpret_cast<VT*>(sdH + r * Cf::LDV + c) = hok[m] ? dhv[m] : zero_vec<T>();
+      }
+    }
+  }
+};
+
+// The chunk's A tile [CP][CP] in flight to LDS (16-byte vectors, issued early).
+template <typename T, int CP>
+struct ATileStage {
+  static constexpr int V = 16 / (int)sizeof(T), N = CP * CP / V, P = (N + 255) / 256;
+  typedef typename V16<T>::type VT;
+  VT a[P];
+  __device__ __forceinline__ void load(const T* src) {
+#pragma unroll
+    for (int m = 0; m < P; ++m) a[m] = *reinterpret_cast<const VT*>(src + (size_t)min((int)threadIdx.x + 256 * m, N - 1) * V);
+  }
+  __device__ __forceinline__ void store(T* dst, int lds) const {
+#pragma unroll
+    for (int m = 0; m < P; ++m) {
+      const int idx = threadIdx.x + 256 * m;
+      if (idx < N) {
+        const int r = idx / (CP / V), c = (idx - r * (CP / V)) * V;
+        *reinterpret_cast<VT*>(dst + r * lds + c) = a[m];
       }
     }
   }
@@ -147,22 +183,24 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
   T* sdA = reinterpret_cast<T*>(smem);                            // strictly lower dA
-  char* rmain = smem + Cf::CT;
+  T* sdAT = sdA + CP * LDC;                                       // its transpose
+  char* rmain = smem + 2 * Cf::CT;
   // phase 1
-  T* sQs = reinterpret_cast<T*>(rmain);
-  T* sKs = sQs + CP * LDQ;
-  T* sKd = sKs + CP * LDQ;                                        // WITH_DV only
+  T* sKd = reinterpret_cast<T*>(rmain);                           // WITH_DV only
   T* sA = sKd + (WITH_DV ? CP * LDQ : 0);                         // WITH_DV only
   T* sdO = sA + (WITH_DV ? CP * LDC : 0);
   T* sV = sdO + CP * LDV;
   T* sH = sV + CP * LDV;
   T* sdH = sH + DKS * LDV;
   T* sdV = sdH + DKS * LDV;                                       // WITH_DV only
-  // phase 3 (aliases phase 1)
+  // phase 2 (aliases phase 1)
+  T* sQsT = reinterpret_cast<T*>(rmain);                          // (q 2^b)^T  [DKS][CP]
+  T* sKsT = sQsT + DKS * LDC;                                     // (k 2^-b)^T
+  // phase 3 (aliases phases 1 and 2)
   float* sDQ = reinterpret_cast<float*>(rmain);                   // dq^nd / 2^b
   float* sDK = sDQ + CP * LDF;                                    // dk'  / 2^-b (fast path)
   float* sDKI = sDK + CP * LDF;                                   // V dH^T
-  float* sB = sDKI + CP * LDF;                                    // b (exact path)
+  float* sB = sDK;                                                // b [CP][DKS] (exact path)
   float* segtot = reinterpret_cast<float*>(smem + Cf::MAIN);      // [2][NSEG][DKS]
   float* sGam = segtot + 2 * NSEG * DKS;
   float* sZ = sGam + DKS;
@@ -185,31 +223,30 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
   const T* hs = reinterpret_cast<const T*>(p.Hs) + (chunk * DKP + ch0) * DVP;
   const T* dhs = reinterpret_cast<const T*>(p.dHs) + (chunk * DKP + ch0) * DVP;
 
+  // every independent load goes out before the first wait: q, k, g of the chunk, the first
+  // Dv slice and (with dv) the chunk's A tile
   ChunkScan<T, DKS, CP> cs;
-  const float maxb = cs.run(qg, kg, reinterpret_cast<const T*>(p.g) + qbase, Dk, Dk - ch0, len, segtot, sGam, red);
+  cs.load(qg, kg, reinterpret_cast<const T*>(p.g) + qbase, Dk, Dk - ch0, len);
+  SliceStage<T, DKS, CP, WITH_DV> st;
+  st.load(dog, vg, hs, dhs, len, Dv, DVP, 0, kvalid);
+  ATileStage<T, CP> at;
+  if constexpr (WITH_DV) at.load(reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP);
+  const float maxb = cs.finish(segtot, sGam, red);
   const bool fast = maxb <= kSpanLimit;
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
 
-  SliceStage<T, DKS, CP, WITH_DV> st;
-  st.load(dog, vg, hs, dhs, len, Dv, DVP, 0, kvalid);
-
-  if (cs.active) {
+  if constexpr (WITH_DV) {
+    if (cs.active) {
 #pragma unroll
-    for (int u = 0; u < RPS; ++u) {
-      const int r = r0 + u;
-      VT qh, kh, kd;
+      for (int u = 0; u < RPS; ++u) {
+        VT kd;
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        qh[e] = from_f32<T>(fast ? cs.qv[u][e] * fast_exp2(cs.b[u][e]) : 0.f);
-        kh[e] = from_f32<T>(fast ? cs.kv[u][e] * fast_exp2(-cs.b[u][e]) : 0.f);
-        if constexpr (WITH_DV) kd[e] = from_f32<T>(cs.kv[u][e] * fast_exp2(sGam[c0 + e] - cs.b[u][e]));
+        for (int e = 0; e < V; ++e) kd[e] = from_f32<T>(cs.kv[u][e] * fast_exp2(sGam[c0 + e] - cs.b[u][e]));
+        *reinterpret_cast<VT*>(sKd + (r0 + u) * LDQ + c0) = kd;
       }
-      *reinterpret_cast<VT*>(sQs + r * LDQ + c0) = qh;
-      *reinterpret_cast<VT*>(sKs + r * LDQ + c0) = kh;
-      if constexpr (WITH_DV) *reinterpret_cast<VT*>(sKd + r * LDQ + c0) = kd;
     }
+    at.store(sA, LDC);
   }
-  if constexpr (WITH_DV) tile_in_dense<T>(sA, reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP, CP, CP, LDC);
   float zp[Cf::PH];
 #pragma unroll
   for (int m = 0; m < Cf::PH; ++m) zp[m] = 0.f;
@@ -224,7 +261,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
   for (int s = 0; s < PQ; ++s) accQ[s] = accK[s] = accKI[s] = zero4();
 
   for (int js = 0; js < ntile; ++js) {
-    if (js + 1 < ntile) st.load(dog, vg, hs, dhs, len, Dv, DVP, js + 1, kvalid);
+    st.load(dog, vg, hs, dhs, len, Dv, DVP, min(js + 1, ntile - 1), kvalid);   // last: harmless reload
 #pragma unroll
     for (int s = 0; s < PA; ++s) {       // dA += dO V^T
       const int blk = wave + 4 * s;
@@ -296,7 +333,8 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
     }
   }
 
-  // strictly lower dA -> LDS, its diagonal kept apart in fp32
+  // strictly lower dA and its transpose -> LDS, the diagonal kept apart in fp32; on the
+  // factorised path also Qs^T and Ks^T (the phase-1 tiles are dead here)
 #pragma unroll
   for (int s = 0; s < PA; ++s) {
     const int blk = wave + 4 * s;
@@ -305,8 +343,20 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
-        sdA[r * LDC + c] = from_f32<T>(c < r ? accA[s][e] : 0.f);
+        const T x = from_f32<T>(c < r ? accA[s][e] : 0.f);
+        sdA[r * LDC + c] = x;
+        sdAT[c * LDC + r] = x;
         if (c == r) sDiag[r] = accA[s][e];
+      }
+    }
+  }
+  if (fast && cs.active) {
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        sQsT[(c0 + e) * LDC + r0 + u] = from_f32<T>(cs.qv[u][e] * fast_exp2(cs.b[u][e]));
+        sKsT[(c0 + e) * LDC + r0 + u] = from_f32<T>(cs.kv[u][e] * fast_exp2(-cs.b[u][e]));
       }
     }
   }
@@ -320,9 +370,9 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
 #pragma unroll
         for (int kc = 0; kc < CP / 32; ++kc) {
           mma(accQ[s], ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp),
-              ld8_col(sKs + (32 * kc + 8 * grp) * LDQ + 16 * ib + col, LDQ));
-          mma(accK[s], ld8_col(sdA + (32 * kc + 8 * grp) * LDC + 16 * rb + col, LDC),
-              ld8_col(sQs + (32 * kc + 8 * grp) * LDQ + 16 * ib + col, LDQ));
+              ld8(sKsT + (16 * ib + col) * LDC + 32 * kc + 8 * grp));
+          mma(accK[s], ld8(sdAT + (16 * rb + col) * LDC + 32 * kc + 8 * grp),
+              ld8(sQsT + (16 * ib + col) * LDC + 32 * kc + 8 * grp));
         }
       }
     }
@@ -337,7 +387,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
       for (int e = 0; e < 4; ++e) {
         const int o = (16 * rb + 4 * grp + e) * LDF + 16 * ib + col;
         sDQ[o] = accQ[s][e];
-        sDK[o] = accK[s][e];
+        if (fast) sDK[o] = accK[s][e];
         sDKI[o] = accKI[s][e];
       }
     }
@@ -533,7 +583,7 @@ struct BwdPlan {
                            : (DKP >= 128 && fits(128, false)) ? 128
                            : (DKP >= 64 && fits(64, false)) ? 64 : 32;
   static constexpr bool OK = (FUSED || fits(DKS, false)) && PrepCfg<T, DKP, CP>::BYTES <= kMaxLds &&
-                             WalkIOCfg<T, DKP, CP>::BYTES <= kMaxLds &&
+                             walk_fits<T, DKP, CP>() &&
                              (FUSED || BwdDvCfg<T, DKP, CP>::BYTES <= kMaxLds);
 };
 
@@ -543,26 +593,29 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
   if constexpr (!P::OK) {
     return hipErrorNotSupported;
   } else {
-    PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N};
-    record_event(p.events, 0, s);
-    hipError_t e = launch_prep<T, DKP, CP, true>(pp, p.BH, s);
-    if (e != hipSuccess) return e;
-    record_event(p.events, 1, s);
+    hipError_t e;
+    int ev = 0;
+    record_event(p.events, ev++, s);
     const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
-    WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, nullptr, p.Dk, p.Dv, p.L, p.C, p.N, 0};
-    if ((e = launch_walk_store<T, DKP, CP>(wf, p.BH, s)) != hipSuccess) return e;
-    record_event(p.events, 2, s);
+    if (!p.saved) {   // recompute the chunk operands and the forward states
+      PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N};
+      if ((e = launch_prep<T, DKP, CP, true>(pp, p.BH, s)) != hipSuccess) return e;
+      record_event(p.events, ev++, s);
+      WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, nullptr, p.Dk, p.Dv, p.L, p.C, p.N, 0};
+      if ((e = launch_walk_store<T, DKP, CP>(wf, p.BH, s)) != hipSuccess) return e;
+      record_event(p.events, ev++, s);
+    }
     WalkIO wr{p.ops.QsT, p.do_, p.ops.Gam, p.dHs, p.dht, p.dh0, p.Dk, p.Dv, p.L, p.C, p.N, 0};
     if ((e = launch_walk_reverse<T, DKP, CP>(wr, p.BH, s)) != hipSuccess) return e;
-    record_event(p.events, 3, s);
+    record_event(p.events, ev++, s);
     hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED>), dim3(p.N, p.BH, DKP / P::DKS), dim3(256), 0, s,
                        p, DKP, ntile);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    record_event(p.events, 4, s);
+    record_event(p.events, ev++, s);
     if constexpr (!P::FUSED) {
       hipLaunchKernelGGL((gla_bwd_dv<T, DKP, CP>), dim3(p.N, p.BH, ntile), dim3(256), 0, s, p, ntile);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      record_event(p.events, 5, s);
+      record_event(p.events, ev++, s);
     }
     return hipSuccess;
   }

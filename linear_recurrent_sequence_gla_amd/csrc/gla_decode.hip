@@ -4,47 +4,64 @@
 // step the whole fp32 state is read and written once, so the kernel is a pure HBM stream:
 // 0.5 flop per byte.  One workgroup per (batch*head, 64 value columns): 16 lanes cover 64
 // contiguous columns with 16-byte accesses (256 bytes per state row) and 16 row groups walk
-// the key rows; q.S is reduced over the row groups in LDS.  No matrix cores: a rank-1 update
-// plus a vector-matrix product has nothing to contract.
+// the key rows, eight rows per thread per pass.  The state rows of the first pass are loaded
+// before q, k and the decay go through LDS, so the barrier that publishes them overlaps the
+// state stream; q.S is reduced over the row groups in LDS at the end.  No matrix cores: a
+// rank-1 update plus a vector-matrix product has nothing to contract.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace gla {
 
+template <typename T> struct V4;
+template <> struct V4<bf16> { typedef bf16x4 type; };
+template <> struct V4<float> { typedef f32x4 type; };
+
 template <typename T>
 __global__ __launch_bounds__(256) void gla_decode_kernel(DecodeParams p, int ntile) {
+  constexpr int RPP = 8;                       // rows per thread per pass
   __shared__ float sq[256], sk[256], sa[256];
   __shared__ f32x4 sred[16][16];
   const int tile = blockIdx.x % ntile, bh = blockIdx.x / ntile;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int Dk = p.Dk, Dv = p.Dv;
-  const T* q = reinterpret_cast<const T*>(p.q) + (size_t)bh * Dk;
-  const T* k = reinterpret_cast<const T*>(p.k) + (size_t)bh * Dk;
-  const T* g = reinterpret_cast<const T*>(p.g) + (size_t)bh * Dk;
-  for (int i = tid; i < Dk; i += 256) {
-    sq[i] = to_f32(q[i]);
-    sk[i] = to_f32(k[i]);
-    sa[i] = fast_exp2(to_f32(g[i]) * kLog2e);
+  const int j = tile * 64 + 4 * tx;
+  const bool jok = j < Dv;
+  const int jc = min(j, Dv - 4);               // in-bounds column for lanes past Dv
+  float* S = p.state + (size_t)bh * Dk * Dv + jc;
+
+  f32x4 s[RPP];
+#pragma unroll
+  for (int m = 0; m < RPP; ++m) s[m] = *reinterpret_cast<const f32x4*>(S + (size_t)min(ty + 16 * m, Dk - 1) * Dv);
+  const typename V4<T>::type vr =
+      *reinterpret_cast<const typename V4<T>::type*>(reinterpret_cast<const T*>(p.v) + (size_t)bh * Dv + jc);
+  if (tid < Dk) {
+    const size_t o = (size_t)bh * Dk + tid;
+    sq[tid] = to_f32(reinterpret_cast<const T*>(p.q)[o]);
+    sk[tid] = to_f32(reinterpret_cast<const T*>(p.k)[o]);
+    sa[tid] = fast_exp2(to_f32(reinterpret_cast<const T*>(p.g)[o]) * kLog2e);
   }
   __syncthreads();
-  const int j = tile * 64 + 4 * tx;
+
   f32x4 acc = zero4();
-  if (j < Dv) {
-    const T* v = reinterpret_cast<const T*>(p.v) + (size_t)bh * Dv + j;
-    f32x4 vv;
+  for (int base = 0; base < Dk; base += 16 * RPP) {
+    if (base > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vv[e] = to_f32(v[e]);
-    float* S = p.state + (size_t)bh * Dk * Dv + j;
-#pragma unroll 4
-    for (int i = ty; i < Dk; i += 16) {
-      f32x4 s = *reinterpret_cast<const f32x4*>(S + (size_t)i * Dv);
-      const float a = sa[i], kv = sk[i], qv = sq[i];
+      for (int m = 0; m < RPP; ++m)
+        s[m] = *reinterpret_cast<const f32x4*>(S + (size_t)min(base + ty + 16 * m, Dk - 1) * Dv);
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[e] = a * s[e] + kv * vv[e];
-        acc[e] += qv * s[e];
+    for (int m = 0; m < RPP; ++m) {
+      const int i = base + ty + 16 * m;
+      if (i < Dk) {
+        const float a = sa[i], kv = sk[i], qv = sq[i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[m][e] = a * s[m][e] + kv * to_f32(vr[e]);
+          acc[e] += qv * s[m][e];
+        }
+        if (jok) *reinterpret_cast<f32x4*>(S + (size_t)i * Dv) = s[m];
       }
-      *reinterpret_cast<f32x4*>(S + (size_t)i * Dv) = s;
     }
   }
   sred[ty][tx] = acc;

@@ -18,7 +18,9 @@
 
 namespace gla {
 
-// LDS layout and prefetch shape of the walk (one chunk's operands).
+// LDS layout and prefetch shape of the walk.  One stage holds one chunk's operands; the
+// stages (and the output staging tile) are double-buffered when two fit a CU's LDS, so a step
+// needs one barrier, else single-buffered with two barriers per step.
 template <typename T, int DKP, int CP>
 struct WalkCfg {
   static constexpr int V = 16 / (int)sizeof(T);
@@ -27,18 +29,27 @@ struct WalkCfg {
   static constexpr size_t AT = (size_t)CP * LDA * sizeof(T);
   static constexpr size_t KT = (size_t)DKP * LDA * sizeof(T);
   static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
-  static constexpr size_t BYTES = QT + AT + KT + 2 * VT + DKP * 4;
+  static constexpr size_t GT = (size_t)DKP * 4;
+  static constexpr size_t STAGE = QT + AT + KT + VT + GT;
+  static constexpr size_t OT = (size_t)CP * LDV * sizeof(T);
+  static constexpr int NB = 2 * (STAGE + OT) <= kMaxLds ? 2 : 1;
+  static constexpr size_t BYTES = NB * (STAGE + OT);
   // 16-byte vectors per chunk and per thread
   static constexpr int NQ = CP * DKP / V, NA = CP * CP / V, NK = DKP * CP / V, NV = CP * kDvTile / V;
   static constexpr int PQ = (NQ + 255) / 256, PA = (NA + 255) / 256, PKd = (NK + 255) / 256, PV = (NV + 255) / 256;
+  static constexpr int R = 2;   // chunks whose operands are in flight ahead of the one in use
 };
 
-// One chunk's walk operands in flight between global memory and LDS.
+// One chunk's walk operands in flight between global memory and LDS.  Loads are issued
+// unconditionally from clamped, in-bounds addresses, with the validity of each value vector
+// kept beside it and applied when the registers are written to LDS; no branch or register
+// rewrite touches a load in flight, so several chunks' loads can stay outstanding.
 template <typename T, int DKP, int CP>
 struct WalkStage {
   using W = WalkCfg<T, DKP, CP>;
   typedef typename V16<T>::type VT;
   VT q[W::PQ], a[W::PA], kd[W::PKd], v[W::PV];
+  bool vok[W::PV];
   f32x4 gam;
 
   __device__ __forceinline__ void load(const FwdParams& p, int bh, int n, int tile) {
@@ -48,20 +59,12 @@ struct WalkStage {
     const T* Ac = reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP;
     const T* Kc = reinterpret_cast<const T*>(p.ops.KdT) + chunk * DKP * CP;
 #pragma unroll
-    for (int m = 0; m < W::PQ; ++m) {
-      const int idx = tid + 256 * m;
-      if (idx < W::NQ) q[m] = *reinterpret_cast<const VT*>(Qc + (size_t)idx * W::V);
-    }
+    for (int m = 0; m < W::PQ; ++m) q[m] = *reinterpret_cast<const VT*>(Qc + (size_t)min(tid + 256 * m, W::NQ - 1) * W::V);
 #pragma unroll
-    for (int m = 0; m < W::PA; ++m) {
-      const int idx = tid + 256 * m;
-      if (idx < W::NA) a[m] = *reinterpret_cast<const VT*>(Ac + (size_t)idx * W::V);
-    }
+    for (int m = 0; m < W::PA; ++m) a[m] = *reinterpret_cast<const VT*>(Ac + (size_t)min(tid + 256 * m, W::NA - 1) * W::V);
 #pragma unroll
-    for (int m = 0; m < W::PKd; ++m) {
-      const int idx = tid + 256 * m;
-      if (idx < W::NK) kd[m] = *reinterpret_cast<const VT*>(Kc + (size_t)idx * W::V);
-    }
+    for (int m = 0; m < W::PKd; ++m)
+      kd[m] = *reinterpret_cast<const VT*>(Kc + (size_t)min(tid + 256 * m, W::NK - 1) * W::V);
     const int row0 = n * p.C, len = min(p.C, p.L - row0);
     const T* vg = reinterpret_cast<const T*>(p.v) + ((size_t)bh * p.L + row0) * p.Dv;
     constexpr int PER_ROW = kDvTile / W::V;
@@ -70,10 +73,10 @@ struct WalkStage {
       const int idx = tid + 256 * m;
       const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
       const int j = tile * kDvTile + c;
-      v[m] = (idx < W::NV && r < len && j < p.Dv) ? *reinterpret_cast<const VT*>(vg + (size_t)r * p.Dv + j)
-                                                  : zero_vec<T>();
+      vok[m] = idx < W::NV && r < len && j < p.Dv;
+      v[m] = *reinterpret_cast<const VT*>(vg + (size_t)min(r, len - 1) * p.Dv + min(j, p.Dv - W::V));
     }
-    if (tid < DKP / 4) gam = *reinterpret_cast<const f32x4*>(p.ops.Gam + chunk * DKP + 4 * tid);
+    gam = *reinterpret_cast<const f32x4*>(p.ops.Gam + chunk * DKP + 4 * (tid % (DKP / 4)));
   }
 
   __device__ __forceinline__ void store(T* sQ, T* sA, T* sK, T* sV, float* sG) const {
@@ -108,7 +111,7 @@ struct WalkStage {
       const int idx = tid + 256 * m;
       if (idx < W::NV) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
-        *reinterpret_cast<VT*>(sV + r * W::LDV + c) = v[m];
+        *reinterpret_cast<VT*>(sV + r * W::LDV + c) = vok[m] ? v[m] : zero_vec<T>();
       }
     }
     if (tid < DKP / 4) *reinterpret_cast<f32x4*>(sG + 4 * tid) = gam;
@@ -118,16 +121,17 @@ struct WalkStage {
 template <typename T, int DKP, int CP>
 __global__ __launch_bounds__(256) void gla_fwd_walk(FwdParams p, int ntile) {
   using W = WalkCfg<T, DKP, CP>;
-  constexpr int LDQ = W::LDQ, LDA = W::LDA, LDV = W::LDV;
+  constexpr int LDQ = W::LDQ, LDA = W::LDA, LDV = W::LDV, R = W::R, NB = W::NB;
   constexpr int NBR = CP / 16, NKB = DKP / 32, NCB = CP / 32, NIB = DKP / 16;
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[W::BYTES];
-  T* sQ = reinterpret_cast<T*>(smem);
-  T* sA = reinterpret_cast<T*>(smem + W::QT);
-  T* sK = reinterpret_cast<T*>(smem + W::QT + W::AT);
-  T* sV = reinterpret_cast<T*>(smem + W::QT + W::AT + W::KT);
-  T* sO = reinterpret_cast<T*>(smem + W::QT + W::AT + W::KT + W::VT);
-  float* sG = reinterpret_cast<float*>(smem + W::QT + W::AT + W::KT + 2 * W::VT);
+  auto base = [&](int b) { return smem + (NB == 2 ? b : 0) * (W::STAGE + W::OT); };
+  auto sQ = [&](int b) { return reinterpret_cast<T*>(base(b)); };
+  auto sA = [&](int b) { return reinterpret_cast<T*>(base(b) + W::QT); };
+  auto sK = [&](int b) { return reinterpret_cast<T*>(base(b) + W::QT + W::AT); };
+  auto sV = [&](int b) { return reinterpret_cast<T*>(base(b) + W::QT + W::AT + W::KT); };
+  auto sG = [&](int b) { return reinterpret_cast<float*>(base(b) + W::QT + W::AT + W::KT + W::VT); };
+  auto sO = [&](int b) { return reinterpret_cast<T*>(base(b) + W::STAGE); };
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = lin % ntile, bh = lin / ntile;
@@ -145,65 +149,92 @@ __global__ __launch_bounds__(256) void gla_fwd_walk(FwdParams p, int ntile) {
       H[ib][e] = (p.h0 && jv && i < p.Dk) ? p.h0[((size_t)bh * p.Dk + i) * Dv + j] : 0.f;
     }
   }
+  __builtin_amdgcn_s_waitcnt(0);                   // initial state in before the pipeline starts
   T* og = reinterpret_cast<T*>(p.o) + (size_t)bh * L * Dv;
 
-  WalkStage<T, DKP, CP> st;
-  st.load(p, bh, 0, tile);
-  st.store(sQ, sA, sK, sV, sG);
+  WalkStage<T, DKP, CP> st[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) st[r].load(p, bh, min(r, N - 1), tile);
+  st[0].store(sQ(0), sA(0), sK(0), sV(0), sG(0));
   __syncthreads();
 
-  for (int n = 0; n < N; ++n) {
-    if (n + 1 < N) st.load(p, bh, n + 1, tile);     // in flight during this chunk's math
-    const int row0 = n * C;
-    const int len = min(C, L - row0);
+  for (int k0 = 0; k0 < N; k0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int n = k0 + r;
+      if (n < N) {
+        const int b = n & 1, row0 = n * C, len = min(C, L - row0);
+        st[r].load(p, bh, min(n + R, N - 1), tile);   // st[r] (chunk n) is already in LDS
+        if (p.Hs) {   // H_n for a later backward, straight from the accumulators
+          T* hs = reinterpret_cast<T*>(p.Hs) + ((size_t)bh * N + n) * DKP * (ntile * kDvTile) + j;
+#pragma unroll
+          for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hs[(size_t)(16 * ib + 4 * grp + e) * (ntile * kDvTile)] = from_f32<T>(H[ib][e]);
+          }
+        }
+        const T* q_ = sQ(b);
+        const T* a_ = sA(b);
+        const T* k_ = sK(b);
+        const T* v_ = sV(b);
+        const float* g_ = sG(b);
+        T* o_ = sO(b);
 
-    Frag<T> Yv[NCB];
+        Frag<T> Yv[NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_col(sV + (32 * cb + 8 * grp) * LDV + 16 * wave + col, LDV);
+        for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_col(v_ + (32 * cb + 8 * grp) * LDV + 16 * wave + col, LDV);
 
-    // O = Qs H + A V
-    f32x4 O[NBR];
+        // O = Qs H + A V
+        f32x4 O[NBR];
 #pragma unroll
-    for (int rb = 0; rb < NBR; ++rb) O[rb] = zero4();
+        for (int rb = 0; rb < NBR; ++rb) O[rb] = zero4();
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const Frag<T> Yh = frag_from_acc<T>(H[2 * kb], H[2 * kb + 1]);
+        for (int kb = 0; kb < NKB; ++kb) {
+          const Frag<T> Yh = frag_from_acc<T>(H[2 * kb], H[2 * kb + 1]);
 #pragma unroll
-      for (int rb = 0; rb < NBR; ++rb) mma(O[rb], ld8_split(sQ + (16 * rb + col) * LDQ + 32 * kb + 4 * grp), Yh);
-    }
+          for (int rb = 0; rb < NBR; ++rb) mma(O[rb], ld8_split(q_ + (16 * rb + col) * LDQ + 32 * kb + 4 * grp), Yh);
+        }
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+        for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-      for (int rb = 0; rb < NBR; ++rb) mma(O[rb], ld8(sA + (16 * rb + col) * LDA + 32 * cb + 8 * grp), Yv[cb]);
-    }
+          for (int rb = 0; rb < NBR; ++rb) mma(O[rb], ld8(a_ + (16 * rb + col) * LDA + 32 * cb + 8 * grp), Yv[cb]);
+        }
 #pragma unroll
-    for (int rb = 0; rb < NBR; ++rb) {
+        for (int rb = 0; rb < NBR; ++rb) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sO[(16 * rb + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(O[rb][e]);
-    }
+          for (int e = 0; e < 4; ++e) o_[(16 * rb + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(O[rb][e]);
+        }
 
-    // H <- Diag(2^Gamma) H + KdT V
+        // H <- Diag(2^Gamma) H + KdT V
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
+        for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) H[ib][e] *= fast_exp2(sG[16 * ib + 4 * grp + e]);
+          for (int e = 0; e < 4; ++e) H[ib][e] *= fast_exp2(g_[16 * ib + 4 * grp + e]);
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+          for (int ib = 0; ib < NIB; ++ib) mma(H[ib], ld8(k_ + (16 * ib + col) * LDA + 32 * cb + 8 * grp), Yv[cb]);
+        }
+        if constexpr (NB == 2) {
+          st[(r + 1) % R].store(sQ(b ^ 1), sA(b ^ 1), sK(b ^ 1), sV(b ^ 1), sG(b ^ 1));
+          __syncthreads();   // chunk n+1 staged, chunk n's tiles consumed, O complete
+        } else {
+          __syncthreads();   // chunk n's tiles consumed, O complete
+          st[(r + 1) % R].store(sQ(0), sA(0), sK(0), sV(0), sG(0));
+        }
+        constexpr int PER_ROW = kDvTile / W::V;
+#pragma unroll
+        for (int m = 0; m < (CP * PER_ROW + 255) / 256; ++m) {
+          const int idx = tid + 256 * m;
+          const int rr = idx / PER_ROW, c = (idx - rr * PER_ROW) * W::V;
+          const int jj = tile * kDvTile + c;
+          if (idx < CP * PER_ROW && rr < len && jj < Dv)
+            *reinterpret_cast<VT*>(og + (size_t)(row0 + rr) * Dv + jj) = *reinterpret_cast<const VT*>(o_ + rr * LDV + c);
+        }
+        if constexpr (NB == 1) __syncthreads();   // chunk n+1 staged, O copied out
+      }
     }
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-      for (int ib = 0; ib < NIB; ++ib) mma(H[ib], ld8(sK + (16 * ib + col) * LDA + 32 * cb + 8 * grp), Yv[cb]);
-    }
-    __syncthreads();   // chunk n's LDS operands consumed, sO complete
-
-    constexpr int PER_ROW = kDvTile / W::V;
-    for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
-      const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
-      const int jj = tile * kDvTile + c;
-      if (r < len && jj < Dv)
-        *reinterpret_cast<VT*>(og + (size_t)(row0 + r) * Dv + jj) = *reinterpret_cast<const VT*>(sO + r * LDV + c);
-    }
-    if (n + 1 < N) st.store(sQ, sA, sK, sV, sG);
-    __syncthreads();
   }
   if (p.ht && jv) {
 #pragma unroll
@@ -224,7 +255,7 @@ hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
   } else {
     PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N};
     record_event(p.events, 0, s);
-    hipError_t e = launch_prep<T, DKP, CP, false>(pp, p.BH, s);
+    hipError_t e = p.ops.QsT ? launch_prep<T, DKP, CP, true>(pp, p.BH, s) : launch_prep<T, DKP, CP, false>(pp, p.BH, s);
     if (e != hipSuccess) return e;
     record_event(p.events, 1, s);
     const int ntile = (p.Dv + kDvTile - 1) / kDvTile;

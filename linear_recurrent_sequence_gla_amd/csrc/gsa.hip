@@ -669,7 +669,7 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
 template <typename T, int MP, int CP>
 constexpr bool gsa_fits() {
   return GsaCfg<T, MP, CP>::P_BYTES <= kMaxLds && GsaCfg<T, MP, CP>::B_BYTES <= kMaxLds &&
-         WalkIOCfg<T, MP, CP>::BYTES <= kMaxLds;
+         walk_fits<T, MP, CP>();
 }
 
 template <typename T, int MP, int CP>
@@ -687,7 +687,7 @@ hipError_t launch_gsa_fwd(const GsaParams& p, hipStream_t s) {
     FwdParams f;
     f.q = p.P; f.k = p.W; f.v = p.v; f.g = p.g; f.h0 = p.hv0; f.o = p.o; f.ht = p.hvt;
     f.BH = p.BH; f.L = p.L; f.Dk = p.m; f.Dv = p.Dv; f.C = p.C; f.N = p.N;
-    f.ops = p.ops2; f.events = LaunchEvents{nullptr, 0};
+    f.ops = p.ops2; f.Hs = nullptr; f.events = LaunchEvents{nullptr, 0};
     return launch_gla_fwd<T, MP, CP>(f, s);
   }
 }
@@ -708,7 +708,7 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
     b.q = p.P; b.k = p.W; b.v = p.v; b.g = p.g; b.do_ = p.do_; b.h0 = p.hv0; b.dht = p.dhvt;
     b.dq = p.dP; b.dk = p.dW2; b.dv = p.dv; b.dg = p.dg2; b.dh0 = p.dhv0;
     b.BH = p.BH; b.L = p.L; b.Dk = p.m; b.Dv = p.Dv; b.C = p.C; b.N = p.N;
-    b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.events = LaunchEvents{nullptr, 0};
+    b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.saved = false; b.events = LaunchEvents{nullptr, 0};
     if ((e = launch_gla_bwd<T, MP, CP>(b, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((gsa_dz_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -31,7 +31,8 @@ struct FwdParams {
   void* o;
   float* ht;
   int BH, L, Dk, Dv, C, N;
-  ChunkOps ops;
+  ChunkOps ops;   // ops.QsT != nullptr: the preparation also writes Qs^T (kept for a backward)
+  void* Hs;       // [BH][N][DKP][DvP] chunk-start states (T), written when not nullptr
   LaunchEvents events;
 };
 
@@ -44,6 +45,7 @@ struct BwdParams {
   ChunkOps ops;
   void* Hs;       // [BH][N][DKP][DvP] state at chunk starts (T)
   void* dHs;      // [BH][N][DKP][DvP] state gradient at chunk ends (T)
+  bool saved;     // ops (with QsT) and Hs were left by a forward: skip recomputing them
   LaunchEvents events;
 };
 
@@ -104,7 +106,7 @@ bool gsa_config_fits(int esize, int MP, int CP);
 // Kernel launches per call (for the profiled entry points).
 constexpr int GLA_FWD_LAUNCHES = 2;
 constexpr int GLA_BWD_MAX_LAUNCHES = 5;
-int bwd_launch_count(int esize, int DKP, int CP);
+int bwd_launch_count(int esize, int DKP, int CP);   // self-contained backward; 2 fewer when saved
 
 // Whether every kernel of the forward fits the LDS of a CU for this (dtype size, DKP, CP).
 bool fwd_config_fits(int esize, int DKP, int CP);

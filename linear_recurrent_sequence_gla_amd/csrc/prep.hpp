@@ -138,42 +138,45 @@ __device__ __forceinline__ typename V16<T>::type zero_vec() {
 // Chunk-local gate scan for the thread's (channel group, row segment): loads g, q, k
 // vectors (16-byte, all issued before first use), keeps b (log2 units) and the raw q and k
 // of its rows and channels, publishes Gamma in sGam and returns the block-wide max |b|.
-// Must be called by all 256 threads.
-// With LOAD_QK = false only g is loaded, and qv holds the raw gate values instead of q.
+// load() only issues the loads -- unconditionally, from clamped in-bounds addresses, with the
+// validity kept beside them -- so a kernel can put other independent loads in flight before
+// finish() consumes these.  run() is load() then finish().  finish() must be called by all
+// 256 threads.  With LOAD_QK = false only g is loaded, and qv holds the raw gate values.
 template <typename T, int DKP, int CP, bool LOAD_QK = true>
 struct ChunkScan {
   using M = ChunkMap<T, DKP, CP>;
   static constexpr int V = M::V, RPS = M::RPS;
+  typedef typename V16<T>::type VT;
   float b[RPS][V];
   float qv[RPS][V];
   float kv[RPS][V];
   int cg, seg;
   bool active;
+  VT gvec[RPS], qvec[RPS], kvec[RPS];
+  bool ok[RPS];
 
   // ld: row stride of q, k, g (elements); width: valid channels from the base pointer
-  __device__ __forceinline__ float run(const T* qg, const T* kg, const T* gg, int ld, int width, int len,
-                                       float* segtot, float* sGam, float* red) {
-    typedef typename V16<T>::type VT;
+  __device__ __forceinline__ void load(const T* qg, const T* kg, const T* gg, int ld, int width, int len) {
     const int tid = threadIdx.x;
     cg = tid % M::NCG;
     seg = tid / M::NCG;
     active = tid < M::ACTIVE;
     const bool chv = active && cg * V < width;
-    VT gvec[RPS], qvec[RPS], kvec[RPS];
+    const int cc = chv ? cg * V : 0;
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
       const int r = seg * RPS + u;
-      const bool ok = chv && r < len;
-      const size_t off = (size_t)r * ld + cg * V;
-      gvec[u] = ok ? *reinterpret_cast<const VT*>(gg + off) : zero_vec<T>();
+      ok[u] = chv && r < len;
+      const size_t off = (size_t)min(r, len - 1) * ld + cc;
+      gvec[u] = *reinterpret_cast<const VT*>(gg + off);
       if constexpr (LOAD_QK) {
-        qvec[u] = ok ? *reinterpret_cast<const VT*>(qg + off) : zero_vec<T>();
-        kvec[u] = ok ? *reinterpret_cast<const VT*>(kg + off) : zero_vec<T>();
-      } else {
-        qvec[u] = gvec[u];
-        kvec[u] = zero_vec<T>();
+        qvec[u] = *reinterpret_cast<const VT*>(qg + off);
+        kvec[u] = *reinterpret_cast<const VT*>(kg + off);
       }
     }
+  }
+
+  __device__ __forceinline__ float finish(float* segtot, float* sGam, float* red) {
     float run_[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) run_[e] = 0.f;
@@ -181,10 +184,16 @@ struct ChunkScan {
     for (int u = 0; u < RPS; ++u) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        run_[e] += to_f32(gvec[u][e]) * kLog2e;
+        const float gv = ok[u] ? to_f32(gvec[u][e]) : 0.f;
+        run_[e] += gv * kLog2e;
         b[u][e] = run_[e];
-        qv[u][e] = to_f32(qvec[u][e]);
-        kv[u][e] = to_f32(kvec[u][e]);
+        if constexpr (LOAD_QK) {
+          qv[u][e] = ok[u] ? to_f32(qvec[u][e]) : 0.f;
+          kv[u][e] = ok[u] ? to_f32(kvec[u][e]) : 0.f;
+        } else {
+          qv[u][e] = gv;
+          kv[u][e] = 0.f;
+        }
       }
     }
     if (active) {
@@ -216,10 +225,16 @@ struct ChunkScan {
     }
     return block_max256(mx, red);   // also makes sGam visible to all threads
   }
+
+  __device__ __forceinline__ float run(const T* qg, const T* kg, const T* gg, int ld, int width, int len,
+                                       float* segtot, float* sGam, float* red) {
+    load(qg, kg, gg, ld, width, len);
+    return finish(segtot, sGam, red);
+  }
 };
 
 template <typename T, int DKP, int CP, bool WANT_QST>
-__global__ __launch_bounds__(256) void gla_prep_kernel(PrepParams p) {
+__global__ __launch_bounds__(256, 2) void gla_prep_kernel(PrepParams p) {
   using Cfg = PrepCfg<T, DKP, CP>;
   using M = ChunkMap<T, DKP, CP>;
   constexpr int V = M::V, RPS = M::RPS;

@@ -1,11 +1,11 @@
-// walks.hpp -- the two sequential state walks shared by the GLA and GSA backward (and the
-// GSA forward).  Both carry one 64-column tile of a row-gated state S [SP rows][64] in fp32
+// walks.hpp -- the sequential state walks shared by the GLA and GSA backward (and the GSA
+// forward).  A walk carries a [RT rows][64 columns] tile of a row-gated state in fp32
 // matrix-core accumulators while stepping over the chunks of one (batch*head):
 //
-//   walk_store    S_0 = init;  for n = 0..N-1:  store S_n (bf16/T),
-//                              S_{n+1} = Diag(2^{Gamma_n}) S_n + M_n X_n ;  fin = S_N
-//   walk_reverse  D_N = init;  for n = N-1..0:  store D_{n+1},
-//                              D_n = Diag(2^{Gamma_n}) D_{n+1} + M_n X_n ;  fin = D_0
+//   forward walk   S_0 = init;  for n = 0..N-1:      store S_n,
+//                               S_{n+1} = Diag(2^{Gamma_n}) S_n + M_n X_n ;    fin = S_N
+//   reverse walk   D_N = init;  for n = N-1..0:      store D_{n+1} (at index n),
+//                               D_n = Diag(2^{Gamma_n}) D_{n+1} + M_n X_n ;    fin = D_0
 //
 // with M_n = mat[n] a per-chunk [SP][CP] matrix (the decayed keys transposed for the forward
 // walk, the decayed queries transposed for the reverse walk) and X_n the chunk's rows of a
@@ -13,8 +13,17 @@
 // GLA: rows = key channels.  GSA: rows = slots for both passes (pass 1 walks the transposed
 // slot-key memory, whose values are the keys).  The chunked structure -- sequential
 // inter-chunk updates, state written only at chunk boundaries -- is the chunkwise training
-// form of the MS-GLA summary (section 2.1).  The next chunk's operands are loaded into
-// registers while the current chunk is processed.
+// form of the MS-GLA summary (section 2.1).
+//
+// Both walks are one kernel.  Row i of the update needs only row i of M_n, so the state is
+// tiled over rows as well as columns: one workgroup per (row tile, 64-column tile, b*h).
+// Per chunk the walk's own arithmetic is tiny, so its speed is set by the latency of each
+// sequential step (LDS round trip, barrier, matrix-core chain) rather than by bandwidth.  A
+// step therefore takes a group of G chunks: the G products T_g = M_g X_g are independent and
+// go on the matrix cores back to back, and the sequential part is only the element-wise fold
+// S <- Diag(2^Gamma_g) S + T_g, which also yields each stored state.  Group operands are
+// loaded into registers kWalkDepth groups ahead of use and LDS is double-buffered, so a step
+// needs one barrier per G chunks.
 #pragma once
 #include "prep.hpp"
 
@@ -30,33 +39,68 @@ struct WalkIO {
   int rows, Ds, L, C, N, trans;
 };
 
-template <typename T, int SP, int CP>
+constexpr int kWalkDepth = 2;   // chunk groups whose operands are in flight ahead of use
+
+template <typename T, int RT, int CP, int G = 1>
 struct WalkIOCfg {
   static constexpr int V = 16 / (int)sizeof(T);
   static constexpr int LDA = CP + V, LDV = kDvTile + V;
-  static constexpr size_t KT = (size_t)SP * LDA * sizeof(T);
+  static constexpr size_t KT = (size_t)RT * LDA * sizeof(T);
   static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
-  static constexpr size_t HT = (size_t)SP * LDV * sizeof(T);
-  static constexpr size_t BYTES = KT + VT + HT + (size_t)SP * 4;
-  static constexpr int NK = SP * CP / V, NV = CP * kDvTile / V, NH = SP * kDvTile / V;
-  static constexpr int PKd = (NK + 255) / 256, PV = (NV + 255) / 256, PH = (NH + 255) / 256;
+  static constexpr size_t GT = (size_t)RT * 4;
+  static constexpr size_t SLOT = KT + VT + GT;            // one chunk's operands
+  static constexpr size_t STAGE = G * SLOT;               // one group's operands
+  static constexpr size_t HT = (size_t)RT * LDV * sizeof(T);
+  static constexpr size_t BYTES = 2 * STAGE + 2 * G * HT;
+  static constexpr int NK = RT * CP / V, NV = CP * kDvTile / V;
+  static constexpr int PKd = (NK + 255) / 256, PV = (NV + 255) / 256;
 };
 
+// Row tile RT (32 rows, at most SP; 16 if nothing fits) and group size G (4, 2 or 1 chunks):
+// the largest group whose double-buffered tiles leave room for two workgroups per CU (the
+// grid has two row tiles per 64 columns, so every workgroup is resident at once), else the
+// largest that fits at all.
 template <typename T, int SP, int CP>
+struct WalkPlan {
+  static constexpr int cand(int r) { return r < SP ? r : SP; }
+  template <int RT_>
+  static constexpr int group() {
+    return WalkIOCfg<T, RT_, CP, 4>::BYTES <= kMaxLds / 2   ? 4
+           : WalkIOCfg<T, RT_, CP, 2>::BYTES <= kMaxLds / 2 ? 2
+           : WalkIOCfg<T, RT_, CP, 2>::BYTES <= kMaxLds     ? 2
+                                                             : 1;
+  }
+  static constexpr int RT = WalkIOCfg<T, cand(32), CP, 1>::BYTES <= kMaxLds ? cand(32) : cand(16);
+  static constexpr int G = group<RT>();
+  static constexpr bool OK = WalkIOCfg<T, RT, CP, G>::BYTES <= kMaxLds;
+};
+template <typename T, int SP, int CP>
+constexpr bool walk_fits() {
+  return WalkPlan<T, SP, CP>::OK;
+}
+
+// One chunk's walk operands in flight between global memory and LDS.  Loads are issued
+// unconditionally from clamped, in-bounds addresses and the validity of each vector is kept
+// beside it; masking happens when the registers are written to LDS, after the data has
+// arrived.  This keeps branches and register rewrites away from loads in flight, so the
+// compiler can leave several chunks' loads outstanding.
+template <typename T, int RT, int CP>
 struct WalkIOStage {
-  using W = WalkIOCfg<T, SP, CP>;
+  using W = WalkIOCfg<T, RT, CP>;
   typedef typename V16<T>::type VT;
   VT kt[W::PKd], v[W::PV];
+  bool vok[W::PV];
   f32x4 gam;
 
-  // mat: [SP][CP] of this chunk; src: [L][Ds] of this (b,h).
+  // mat: [RT][CP] rows of this chunk's matrix (row stride CP); src: [L][Ds] of this (b,h);
+  // gam_chunk: this tile's RT decay values.
   __device__ __forceinline__ void load(const T* mat, const T* src, int row0, int len, int Ds, int tile,
                                        const float* gam_chunk) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < W::PKd; ++m) {
-      const int idx = tid + 256 * m;
-      if (idx < W::NK) kt[m] = *reinterpret_cast<const VT*>(mat + (size_t)idx * W::V);
+      const int idx = min(tid + 256 * m, W::NK - 1);
+      kt[m] = *reinterpret_cast<const VT*>(mat + (size_t)idx * W::V);
     }
     constexpr int PER_ROW = kDvTile / W::V;
 #pragma unroll
@@ -64,10 +108,11 @@ struct WalkIOStage {
       const int idx = tid + 256 * m;
       const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
       const int j = tile * kDvTile + c;
-      v[m] = (idx < W::NV && r < len && j < Ds) ? *reinterpret_cast<const VT*>(src + (size_t)(row0 + r) * Ds + j)
-                                                : zero_vec<T>();
+      vok[m] = idx < W::NV && r < len && j < Ds;
+      const int rr = min(r, len - 1), jj = min(j, Ds - W::V);
+      v[m] = *reinterpret_cast<const VT*>(src + (size_t)(row0 + rr) * Ds + jj);
     }
-    if (tid < SP / 4) gam = *reinterpret_cast<const f32x4*>(gam_chunk + 4 * tid);
+    gam = *reinterpret_cast<const f32x4*>(gam_chunk + 4 * (tid % (RT / 4)));
   }
 
   __device__ __forceinline__ void store(T* sKT, T* sV, float* sG) const {
@@ -86,22 +131,26 @@ struct WalkIOStage {
       const int idx = tid + 256 * m;
       if (idx < W::NV) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
-        *reinterpret_cast<VT*>(sV + r * W::LDV + c) = v[m];
+        *reinterpret_cast<VT*>(sV + r * W::LDV + c) = vok[m] ? v[m] : zero_vec<T>();
       }
     }
-    if (tid < SP / 4) *reinterpret_cast<f32x4*>(sG + 4 * tid) = gam;
+    if (tid < RT / 4) *reinterpret_cast<f32x4*>(sG + 4 * tid) = gam;
   }
 };
 
-// Copy an LDS [SP][64] tile to the state workspace (row stride DsP, already offset).
-template <typename T, int SP>
+// Copy an LDS [RT][64] tile to the state workspace (row stride DsP, already offset).
+template <typename T, int RT>
 __device__ __forceinline__ void state_tile_out(T* dst, const T* src, int lds, int DsP) {
   constexpr int V = V16<T>::N;
   typedef typename V16<T>::type VT;
   constexpr int PER_ROW = kDvTile / V;
-  for (int idx = threadIdx.x; idx < SP * PER_ROW; idx += 256) {
-    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
-    *reinterpret_cast<VT*>(dst + (size_t)r * DsP + c) = *reinterpret_cast<const VT*>(src + r * lds + c);
+#pragma unroll
+  for (int m = 0; m < (RT * PER_ROW + 255) / 256; ++m) {
+    const int idx = threadIdx.x + 256 * m;
+    if (idx < RT * PER_ROW) {
+      const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+      *reinterpret_cast<VT*>(dst + (size_t)r * DsP + c) = *reinterpret_cast<const VT*>(src + r * lds + c);
+    }
   }
 }
 
@@ -109,167 +158,146 @@ __device__ __forceinline__ size_t walk_state_index(const WalkIO& w, int bh, int 
   return w.trans ? ((size_t)bh * w.Ds + j) * w.rows + i : ((size_t)bh * w.rows + i) * w.Ds + j;
 }
 
-// S_{n+1} = Diag(2^Gamma) S_n + M_n X_n on the accumulators (X from LDS, M from LDS).
-template <typename T, int SP, int CP>
-__device__ __forceinline__ void walk_step(f32x4 (&S)[SP / 16], const T* sKT, const T* sV, const float* sG) {
-  using W = WalkIOCfg<T, SP, CP>;
+// T = M X on fresh accumulators (M and X from LDS): one chunk's state increment.
+template <typename T, int RT, int CP>
+__device__ __forceinline__ void walk_product(f32x4 (&Tm)[RT / 16], const T* sKT, const T* sV) {
+  using W = WalkIOCfg<T, RT, CP>;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  constexpr int NCB = CP / 32, NIB = SP / 16;
+  constexpr int NCB = CP / 32, NIB = RT / 16;
   Frag<T> Yv[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_col(sV + (32 * cb + 8 * grp) * W::LDV + 16 * wave + col, W::LDV);
 #pragma unroll
-  for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) S[ib][e] *= fast_exp2(sG[16 * ib + 4 * grp + e]);
-  }
+  for (int ib = 0; ib < NIB; ++ib) Tm[ib] = zero4();
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) mma(S[ib], ld8(sKT + (16 * ib + col) * W::LDA + 32 * cb + 8 * grp), Yv[cb]);
+    for (int ib = 0; ib < NIB; ++ib) mma(Tm[ib], ld8(sKT + (16 * ib + col) * W::LDA + 32 * cb + 8 * grp), Yv[cb]);
   }
 }
 
-template <typename T, int SP, int CP>
-__global__ __launch_bounds__(256) void walk_store(WalkIO w, int ntile) {
-  using W = WalkIOCfg<T, SP, CP>;
-  constexpr int LDV = W::LDV, NIB = SP / 16;
+// grid: ntile * (SP / RT) * BH workgroups of 256 threads; each wave owns 16 of the 64 columns.
+template <typename T, int SP, int RT, int CP, int G, bool REV>
+__global__ __launch_bounds__(256) void walk_kernel(WalkIO w, int ntile) {
+  using W = WalkIOCfg<T, RT, CP, G>;
+  constexpr int LDV = W::LDV, NIB = RT / 16, NRT = SP / RT, R = kWalkDepth;
   __shared__ __attribute__((aligned(16))) char smem[W::BYTES];
-  T* sKT = reinterpret_cast<T*>(smem);
-  T* sV = reinterpret_cast<T*>(smem + W::KT);
-  T* sHo = reinterpret_cast<T*>(smem + W::KT + W::VT);
-  float* sG = reinterpret_cast<float*>(smem + W::KT + W::VT + W::HT);
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = lin % ntile, bh = lin / ntile;
+  const int tile = lin % ntile, rt = (lin / ntile) % NRT, bh = lin / (ntile * NRT);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int Ds = w.Ds, L = w.L, C = w.C, N = w.N;
-  const int DsP = ntile * kDvTile;
+  const int NG = (N + G - 1) / G;
+  const int DsP = ntile * kDvTile, i0 = rt * RT;
   const int j = tile * kDvTile + 16 * wave + col;
   const bool jv = j < Ds;
   const T* src = reinterpret_cast<const T*>(w.src) + (size_t)bh * L * Ds;
-  const T* mat = reinterpret_cast<const T*>(w.mat) + (size_t)bh * N * SP * CP;
-  const float* gam = w.gam + (size_t)bh * N * SP;
-  T* out = reinterpret_cast<T*>(w.states) + (size_t)bh * N * SP * DsP + tile * kDvTile;
+  const T* mat = reinterpret_cast<const T*>(w.mat) + ((size_t)bh * N * SP + i0) * CP;
+  const float* gam = w.gam + (size_t)bh * N * SP + i0;
+  T* out = reinterpret_cast<T*>(w.states) + ((size_t)bh * N * SP + i0) * DsP + tile * kDvTile;
+
+  auto slot = [&](int b, int g) { return smem + b * W::STAGE + g * W::SLOT; };
+  auto sKT = [&](int b, int g) { return reinterpret_cast<T*>(slot(b, g)); };
+  auto sV = [&](int b, int g) { return reinterpret_cast<T*>(slot(b, g) + W::KT); };
+  auto sG = [&](int b, int g) { return reinterpret_cast<float*>(slot(b, g) + W::KT + W::VT); };
+  auto sHo = [&](int b, int g) { return reinterpret_cast<T*>(smem + 2 * W::STAGE + (b * G + g) * W::HT); };
+  auto chunk_of = [&](int k) { return REV ? N - 1 - k : k; };   // the k-th chunk visited
 
   f32x4 S[NIB];
 #pragma unroll
   for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = 16 * ib + 4 * grp + e;
+      const int i = i0 + 16 * ib + 4 * grp + e;
       S[ib][e] = (w.init && jv && i < w.rows) ? w.init[walk_state_index(w, bh, i, j)] : 0.f;
     }
   }
-  WalkIOStage<T, SP, CP> st;
-  st.load(mat, src, 0, min(C, L), Ds, tile, gam);
-  st.store(sKT, sV, sG);
+  __builtin_amdgcn_s_waitcnt(0);                   // initial state in before the pipeline starts
+
+  WalkIOStage<T, RT, CP> st[R][G];
+  auto load = [&](WalkIOStage<T, RT, CP> (&s)[G], int kg) {   // past the end: reload the last chunk
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int n = chunk_of(min(kg * G + g, N - 1)), row0 = n * C;
+      s[g].load(mat + (size_t)n * SP * CP, src, row0, min(C, L - row0), Ds, tile, gam + (size_t)n * SP);
+    }
+  };
+  auto store = [&](const WalkIOStage<T, RT, CP> (&s)[G], int b) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) s[g].store(sKT(b, g), sV(b, g), sG(b, g));
+  };
+#pragma unroll
+  for (int r = 0; r < R; ++r) load(st[r], r);
+  store(st[0], 0);
   __syncthreads();
-  for (int n = 0; n < N; ++n) {
-    if (n + 1 < N) {
-      const int r1 = (n + 1) * C;
-      st.load(mat + (size_t)(n + 1) * SP * CP, src, r1, min(C, L - r1), Ds, tile, gam + (size_t)(n + 1) * SP);
-    }
+
+  for (int q0 = 0; q0 < NG; q0 += R) {
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
+    for (int r = 0; r < R; ++r) {
+      const int kg = q0 + r;
+      if (kg < NG) {
+        const int b = kg & 1;
+        load(st[r], kg + R);                         // st[r] (group kg) is already in LDS
+        f32x4 Tm[G][NIB];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sHo[(16 * ib + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(S[ib][e]);
+        for (int g = 0; g < G; ++g) walk_product<T, RT, CP>(Tm[g], sKT(b, g), sV(b, g));
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (kg * G + g < N) {
+            T* ho = sHo(b, g);
+            const float* gg = sG(b, g);
+#pragma unroll
+            for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int ii = 16 * ib + 4 * grp + e;
+                ho[ii * LDV + 16 * wave + col] = from_f32<T>(S[ib][e]);
+                S[ib][e] = fast_exp2(gg[ii]) * S[ib][e] + Tm[g][ib][e];
+              }
+            }
+          }
+        }
+        store(st[(r + 1) % R], b ^ 1);
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const int k = kg * G + g;
+          if (k < N) state_tile_out<T, RT>(out + (size_t)chunk_of(k) * SP * DsP, sHo(b, g), LDV, DsP);
+        }
+      }
     }
-    walk_step<T, SP, CP>(S, sKT, sV, sG);
-    __syncthreads();
-    state_tile_out<T, SP>(out + (size_t)n * SP * DsP, sHo, LDV, DsP);
-    if (n + 1 < N) st.store(sKT, sV, sG);
-    __syncthreads();
   }
   if (w.fin && jv) {
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = 16 * ib + 4 * grp + e;
+        const int i = i0 + 16 * ib + 4 * grp + e;
         if (i < w.rows) w.fin[walk_state_index(w, bh, i, j)] = S[ib][e];
       }
     }
   }
 }
 
-template <typename T, int SP, int CP>
-__global__ __launch_bounds__(256) void walk_reverse(WalkIO w, int ntile) {
-  using W = WalkIOCfg<T, SP, CP>;
-  constexpr int LDV = W::LDV, NIB = SP / 16;
-  __shared__ __attribute__((aligned(16))) char smem[W::BYTES];
-  T* sKT = reinterpret_cast<T*>(smem);
-  T* sV = reinterpret_cast<T*>(smem + W::KT);
-  T* sHo = reinterpret_cast<T*>(smem + W::KT + W::VT);
-  float* sG = reinterpret_cast<float*>(smem + W::KT + W::VT + W::HT);
-
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int tile = lin % ntile, bh = lin / ntile;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  const int Ds = w.Ds, L = w.L, C = w.C, N = w.N;
-  const int DsP = ntile * kDvTile;
-  const int j = tile * kDvTile + 16 * wave + col;
-  const bool jv = j < Ds;
-  const T* src = reinterpret_cast<const T*>(w.src) + (size_t)bh * L * Ds;
-  const T* mat = reinterpret_cast<const T*>(w.mat) + (size_t)bh * N * SP * CP;
-  const float* gam = w.gam + (size_t)bh * N * SP;
-  T* out = reinterpret_cast<T*>(w.states) + (size_t)bh * N * SP * DsP + tile * kDvTile;
-
-  f32x4 D[NIB];
-#pragma unroll
-  for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * ib + 4 * grp + e;
-      D[ib][e] = (w.init && jv && i < w.rows) ? w.init[walk_state_index(w, bh, i, j)] : 0.f;
-    }
-  }
-  WalkIOStage<T, SP, CP> st;
-  {
-    const int r1 = (N - 1) * C;
-    st.load(mat + (size_t)(N - 1) * SP * CP, src, r1, L - r1, Ds, tile, gam + (size_t)(N - 1) * SP);
-    st.store(sKT, sV, sG);
-  }
-  __syncthreads();
-  for (int n = N - 1; n >= 0; --n) {
-    if (n > 0) {
-      const int r1 = (n - 1) * C;
-      st.load(mat + (size_t)(n - 1) * SP * CP, src, r1, C, Ds, tile, gam + (size_t)(n - 1) * SP);
-    }
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sHo[(16 * ib + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(D[ib][e]);
-    }
-    walk_step<T, SP, CP>(D, sKT, sV, sG);
-    __syncthreads();
-    state_tile_out<T, SP>(out + (size_t)n * SP * DsP, sHo, LDV, DsP);
-    if (n > 0) st.store(sKT, sV, sG);
-    __syncthreads();
-  }
-  if (w.fin && jv) {
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * ib + 4 * grp + e;
-        if (i < w.rows) w.fin[walk_state_index(w, bh, i, j)] = D[ib][e];
-      }
-    }
+template <typename T, int SP, int CP, bool REV>
+hipError_t launch_walk(const WalkIO& w, int BH, hipStream_t s) {
+  using P = WalkPlan<T, SP, CP>;
+  if constexpr (!P::OK) {
+    return hipErrorNotSupported;
+  } else {
+    const int ntile = (w.Ds + kDvTile - 1) / kDvTile;
+    hipLaunchKernelGGL((walk_kernel<T, SP, P::RT, CP, P::G, REV>), dim3(ntile * (SP / P::RT) * BH), dim3(256), 0, s,
+                       w, ntile);
+    return hipGetLastError();
   }
 }
-
 template <typename T, int SP, int CP>
 hipError_t launch_walk_store(const WalkIO& w, int BH, hipStream_t s) {
-  const int ntile = (w.Ds + kDvTile - 1) / kDvTile;
-  hipLaunchKernelGGL((walk_store<T, SP, CP>), dim3(ntile * BH), dim3(256), 0, s, w, ntile);
-  return hipGetLastError();
+  return launch_walk<T, SP, CP, false>(w, BH, s);
 }
 template <typename T, int SP, int CP>
 hipError_t launch_walk_reverse(const WalkIO& w, int BH, hipStream_t s) {
-  const int ntile = (w.Ds + kDvTile - 1) / kDvTile;
-  hipLaunchKernelGGL((walk_reverse<T, SP, CP>), dim3(ntile * BH), dim3(256), 0, s, w, ntile);
-  return hipGetLastError();
+  return launch_walk<T, SP, CP, true>(w, BH, s);
 }
 
 }  // namespace gla

@@ -96,6 +96,38 @@ def test_workspace_sizes(lib):
     assert lib.gla_bwd_launch_count(4, 4, 4096, 256, 512, 64, 1) == 5
 
 
+def test_saved_path_sizes_and_validation(lib):
+    # saved = the backward's chunk operands (with Qs^T) + chunk-start states; its workspace = dH
+    B, H, L, Dk, Dv, C = 8, 4, 2048, 128, 256, 64
+    N = L // C
+    ops = 3 * (B * H * N * C * Dk * 2) + B * H * N * C * C * 2 + B * H * N * Dk * 4
+    states = B * H * N * Dk * Dv * 2
+    assert lib.gla_saved_bytes(B, H, L, Dk, Dv, C, 1) == ops + states
+    assert lib.gla_bwd_saved_workspace_bytes(B, H, L, Dk, Dv, C, 1) == states
+    assert lib.gla_saved_bytes(1, 1, 64, 16, 16, 48, 1) == 0          # unsupported C
+    assert lib.gla_saved_bytes(1, 1, 64, 256, 64, 128, 1) == 0        # LDS limit
+    q, k, v, g, o = (ctypes.c_void_p(0x10000000 + i * 0x1000000) for i in range(5))
+    need = lib.gla_saved_bytes(1, 1, 64, 16, 16, 16, 1)
+    assert lib.gla_fwd_save(q, k, v, g, None, o, None, 1, 1, 64, 16, 16, 16, 1, None, 0, None, None, 0) == 5
+    assert lib.gla_fwd_save(q, k, v, g, None, o, None, 1, 1, 64, 16, 16, 16, 1,
+                            ctypes.c_void_p(0x30000000), need - 1, None, None, 0) == 5
+    assert lib.gla_fwd_save(q, k, v, g, None, o, None, 1, 1, 64, 16, 16, 16, 1,
+                            ctypes.c_void_p(0x10000000 + 256), need, None, None, 0) == 6   # saved overlaps q
+    assert lib.gla_fwd_save(None, k, v, g, None, o, None, 1, 1, 64, 16, 16, 16, 1,
+                            ctypes.c_void_p(0x30000000), need, None, None, 0) == 1
+    ev = (ctypes.c_void_p * 2)()
+    assert lib.gla_fwd_save(q, k, v, g, None, o, None, 1, 1, 64, 16, 16, 16, 1,
+                            ctypes.c_void_p(0x30000000), need, None, ev, 2) == 1            # too few events
+    d = [ctypes.c_void_p(0x40000000 + i * 0x1000000) for i in range(5)]
+    wsb = lib.gla_bwd_saved_workspace_bytes(1, 1, 64, 16, 16, 16, 1)
+    args = [q, k, v, g, None, o, None, d[0], d[1], d[2], d[3], None, 1, 1, 64, 16, 16, 16, 1]
+    assert lib.gla_bwd_saved(*args, ctypes.c_void_p(0x30000000), need, None, 0, None, None, 0) == 5
+    assert lib.gla_bwd_saved(*args, ctypes.c_void_p(0x30000000), need, d[4], wsb - 1, None, None, 0) == 5
+    assert lib.gla_bwd_saved(*args, ctypes.c_void_p(0x30000000), need,
+                             ctypes.c_void_p(0x30000000 + 512), wsb, None, None, 0) == 6     # workspace in saved
+    assert lib.gla_bwd_saved(*args, d[0], need, d[4], wsb, None, None, 0) == 6               # saved is dq
+
+
 def test_decode_validation(lib):
     assert lib.gla_decode_step(*[None] * 6, 1, 1, 16, 16, 7, None) == 3
     assert lib.gla_decode_step(*[None] * 6, 1, 1, 16, 16, 1, None) == 1
