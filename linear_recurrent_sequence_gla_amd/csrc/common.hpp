@@ -84,6 +84,33 @@ __device__ __forceinline__ Frag<T> ld8_col(const T* p, int ld) {
   for (int e = 0; e < 8; ++e) f.v[e] = p[e * ld];
   return f;
 }
+// The same column run of a row-major LDS tile, addressed by the corner of its 32 x 16 block:
+// lane (grp, col) gets blk[(8 * grp + e) * ld + col], e = 0..7 -- the k-run of a
+// matrix-core operand whose k index runs down the tile's rows.  For 16-bit types this is two
+// transposing LDS reads (ds_read_b64_tr_b16): within each 16-lane group, lane 4u+t receives
+// element t of the 4-element rows read by lanes u, u+4, u+8 and u+12, so lane j reads row
+// j / 4 of a 4-row slab at column 4 * (j % 4).  ld * sizeof(T) must be a multiple of 8.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+template <typename T>
+__device__ __forceinline__ Frag<T> ld8_colblk(const T* blk, int ld);
+template <>
+__device__ __forceinline__ Frag<bf16> ld8_colblk(const bf16* blk, int ld) {
+  typedef i16x4 __attribute__((address_space(3)))* lds_ptr;
+  const int lane = threadIdx.x & 63, grp = lane >> 4, j = lane & 15;
+  bf16* a = const_cast<bf16*>(blk) + (8 * grp + (j >> 2)) * ld + 4 * (j & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)a);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(a + 4 * ld));
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> ld8_colblk(const float* blk, int ld) {
+  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+  return ld8_col(blk + 8 * grp * ld + col, ld);
+}
+
 // Split-set fragment taken from two stacked accumulator blocks (rows 4*grp+e of block a and
 // of block b): the Y operand of a contraction over the accumulator's row index.
 template <typename T>

@@ -293,12 +293,12 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
           f32x4 acc = zero4();
 #pragma unroll
           for (int kr = 0; kr < CP / 32; ++kr)
-            mma(acc, ld8_col(sA + (32 * kr + 8 * grp) * LDC + 16 * cb + col, LDC),
-                ld8_col(sdO + (32 * kr + 8 * grp) * LDV + 16 * jb + col, LDV));
+            mma(acc, ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC),
+                ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV));
 #pragma unroll
           for (int ki = 0; ki < DKS / 32; ++ki)
             mma(acc, ld8(sKd + (16 * cb + col) * LDQ + 32 * ki + 8 * grp),
-                ld8_col(sdH + (32 * ki + 8 * grp) * LDV + 16 * jb + col, LDV));
+                ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV));
 #pragma unroll
           for (int e = 0; e < 4; ++e) sdV[(16 * cb + 4 * grp + e) * LDV + 16 * jb + col] = from_f32<T>(acc[e]);
         }
@@ -551,12 +551,12 @@ __global__ __launch_bounds__(256) void gla_bwd_dv(BwdParams p, int ntile) {
     f32x4 acc = zero4();
 #pragma unroll
     for (int kr = 0; kr < CP / 32; ++kr)
-      mma(acc, ld8_col(sA + (32 * kr + 8 * grp) * LDC + 16 * cb + col, LDC),
-          ld8_col(sdO + (32 * kr + 8 * grp) * LDV + 16 * wave + col, LDV));
+      mma(acc, ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC),
+          ld8_colblk(sdO + (32 * kr) * LDV + 16 * wave, LDV));
 #pragma unroll
     for (int ki = 0; ki < DKP / 32; ++ki)
-      mma(acc, ld8_col(sKdT + (32 * ki + 8 * grp) * LDC + 16 * cb + col, LDC),
-          ld8_col(sdH + (32 * ki + 8 * grp) * LDV + 16 * wave + col, LDV));
+      mma(acc, ld8_colblk(sKdT + (32 * ki) * LDC + 16 * cb, LDC),
+          ld8_colblk(sdH + (32 * ki) * LDV + 16 * wave, LDV));
 #pragma unroll
     for (int e = 0; e < 4; ++e) sdV[(16 * cb + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(acc[e]);
   }

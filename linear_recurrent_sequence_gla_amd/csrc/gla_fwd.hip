@@ -33,7 +33,11 @@ struct WalkCfg {
   static constexpr size_t STAGE = QT + AT + KT + VT + GT;
   static constexpr size_t OT = (size_t)CP * LDV * sizeof(T);
   static constexpr int NB = 2 * (STAGE + OT) <= kMaxLds ? 2 : 1;
-  static constexpr size_t BYTES = NB * (STAGE + OT);
+  // staging tile for the chunk-start states a saving forward writes (coalesced stores), when
+  // it fits beside the rest; otherwise the states leave straight from the accumulators
+  static constexpr size_t HT = (size_t)DKP * LDV * sizeof(T);
+  static constexpr bool HS_LDS = NB * (STAGE + OT) + HT <= kMaxLds;
+  static constexpr size_t BYTES = NB * (STAGE + OT) + (HS_LDS ? HT : 0);
   // 16-byte vectors per chunk and per thread
   static constexpr int NQ = CP * DKP / V, NA = CP * CP / V, NK = DKP * CP / V, NV = CP * kDvTile / V;
   static constexpr int PQ = (NQ + 255) / 256, PA = (NA + 255) / 256, PKd = (NK + 255) / 256, PV = (NV + 255) / 256;
@@ -132,6 +136,7 @@ __global__ __launch_bounds__(256) void gla_fwd_walk(FwdParams p, int ntile) {
   auto sV = [&](int b) { return reinterpret_cast<T*>(base(b) + W::QT + W::AT + W::KT); };
   auto sG = [&](int b) { return reinterpret_cast<float*>(base(b) + W::QT + W::AT + W::KT + W::VT); };
   auto sO = [&](int b) { return reinterpret_cast<T*>(base(b) + W::STAGE); };
+  T* sHs = reinterpret_cast<T*>(smem + NB * (W::STAGE + W::OT));   // HS_LDS only
 
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = lin % ntile, bh = lin / ntile;
@@ -165,12 +170,33 @@ __global__ __launch_bounds__(256) void gla_fwd_walk(FwdParams p, int ntile) {
       if (n < N) {
         const int b = n & 1, row0 = n * C, len = min(C, L - row0);
         st[r].load(p, bh, min(n + R, N - 1), tile);   // st[r] (chunk n) is already in LDS
-        if (p.Hs) {   // H_n for a later backward, straight from the accumulators
-          T* hs = reinterpret_cast<T*>(p.Hs) + ((size_t)bh * N + n) * DKP * (ntile * kDvTile) + j;
+        if (p.Hs) {   // H_n for a later backward
+          const int DvP = ntile * kDvTile;
+          T* hs = reinterpret_cast<T*>(p.Hs) + ((size_t)bh * N + n) * DKP * DvP + tile * kDvTile;
+          if constexpr (W::HS_LDS) {   // through LDS: one more barrier, 16-byte stores
 #pragma unroll
-          for (int ib = 0; ib < NIB; ++ib) {
+            for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hs[(size_t)(16 * ib + 4 * grp + e) * (ntile * kDvTile)] = from_f32<T>(H[ib][e]);
+              for (int e = 0; e < 4; ++e) sHs[(16 * ib + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(H[ib][e]);
+            }
+            __syncthreads();
+            constexpr int PER_ROW = kDvTile / W::V;
+#pragma unroll
+            for (int m = 0; m < (DKP * PER_ROW + 255) / 256; ++m) {
+              const int idx = tid + 256 * m;
+              if (idx < DKP * PER_ROW) {
+                const int rr = idx / PER_ROW, c = (idx - rr * PER_ROW) * W::V;
+                *reinterpret_cast<VT*>(hs + (size_t)rr * DvP + c) = *reinterpret_cast<const VT*>(sHs + rr * LDV + c);
+              }
+            }
+            // sHs is rewritten only after this step's closing barrier(s)
+          } else {
+#pragma unroll
+            for (int ib = 0; ib < NIB; ++ib) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                hs[(size_t)(16 * ib + 4 * grp + e) * DvP + 16 * wave + col] = from_f32<T>(H[ib][e]);
+            }
           }
         }
         const T* q_ = sQ(b);
@@ -182,7 +208,7 @@ __global__ __launch_bounds__(256) void gla_fwd_walk(FwdParams p, int ntile) {
 
         Frag<T> Yv[NCB];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_col(v_ + (32 * cb + 8 * grp) * LDV + 16 * wave + col, LDV);
+        for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_colblk(v_ + (32 * cb) * LDV + 16 * wave, LDV);
 
         // O = Qs H + A V
         f32x4 O[NBR];

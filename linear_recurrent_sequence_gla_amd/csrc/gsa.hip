@@ -493,8 +493,8 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
             xa[e] = sdQK[(16 * rb + col) * LDQK + 32 * kc + 8 * grp + e];
             xt[e] = sdQK[(32 * kc + 8 * grp + e) * LDQK + 16 * rb + col];
           }
-          mma(aq, frag_of<T>(xa), ld8_col(sk + (32 * kc + 8 * grp) * LDS + 16 * ib + col, LDS));
-          mma(ak, frag_of<T>(xt), ld8_col(sq + (32 * kc + 8 * grp) * LDS + 16 * ib + col, LDS));
+          mma(aq, frag_of<T>(xa), ld8_colblk(sk + (32 * kc) * LDS + 16 * ib, LDS));
+          mma(ak, frag_of<T>(xt), ld8_colblk(sq + (32 * kc) * LDS + 16 * ib, LDS));
         }
 #pragma unroll
         for (int ks = 0; ks < MP / 32; ++ks) {
@@ -505,8 +505,8 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
             xa[e] = sdZ[r * LDF + s] * fast_exp2(sB[r * LDF + s]);
             xw[e] = sW[r * LDF + s] * fast_exp2(sGam[s] - sB[r * LDF + s]);
           }
-          mma(aq, frag_of<T>(xa), ld8_col(sS1 + (32 * ks + 8 * grp) * LDS + 16 * ib + col, LDS));
-          mma(ak, frag_of<T>(xw), ld8_col(sdS1 + (32 * ks + 8 * grp) * LDS + 16 * ib + col, LDS));
+          mma(aq, frag_of<T>(xa), ld8_colblk(sS1 + (32 * ks) * LDS + 16 * ib, LDS));
+          mma(ak, frag_of<T>(xw), ld8_colblk(sdS1 + (32 * ks) * LDS + 16 * ib, LDS));
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

@@ -166,7 +166,7 @@ __device__ __forceinline__ void walk_product(f32x4 (&Tm)[RT / 16], const T* sKT,
   constexpr int NCB = CP / 32, NIB = RT / 16;
   Frag<T> Yv[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_col(sV + (32 * cb + 8 * grp) * W::LDV + 16 * wave + col, W::LDV);
+  for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_colblk(sV + (32 * cb) * W::LDV + 16 * wave, W::LDV);
 #pragma unroll
   for (int ib = 0; ib < NIB; ++ib) Tm[ib] = zero4();
 #pragma unroll
