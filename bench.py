@@ -70,7 +70,8 @@ def kernel_alg_bytes(B, H, L, Dk, Dv, s=2):
     u = B * H * L
     return {
         "fwd.prep": u * s * 3 * Dk,                            # q, k, g
-        "fwd.walk": u * s * 2 * Dv,                            # v in, o out
+        "fwd.walk": u * s * Dv,                                # v (states are workspace)
+        "fwd.out": u * s * 2 * Dv,                             # v in, o out
         "bwd.prep": u * s * 3 * Dk,                            # q, k, g (self-contained backward)
         "bwd.walk_fwd": u * s * Dv,                            # v
         "bwd.walk_rev": u * s * Dv,                            # do
@@ -162,14 +163,14 @@ def run_gla(torch, m, steps, warmup):
 
     def step(evf=None, evb=None):
         m._check(lib.gla_fwd_save(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(o), P(ht),
-                                  B, H, L, Dk, Dv, C, 1, P(sv), sv.numel(), stream, evf, 3 if evf else 0))
+                                  B, H, L, Dk, Dv, C, 1, P(sv), sv.numel(), stream, evf, 4 if evf else 0))
         m._check(lib.gla_bwd_saved(P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(d["do"]), None,
                                    P(dq), P(dk), P(dv), P(dg), None, B, H, L, Dk, Dv, C, 1, P(sv), sv.numel(),
                                    P(wsb), wsb.numel(), stream, evb, 4 if evb else 0))
 
     for _ in range(warmup):
         step()
-    ef = [_events(torch, 3) for _ in range(steps)]
+    ef = [_events(torch, 4) for _ in range(steps)]
     eb = [_events(torch, 4) for _ in range(steps)]                 # room for the most launches
     hf = [_handles(e) for e in ef]
     hb = [_handles(e) for e in eb]
@@ -181,7 +182,7 @@ def run_gla(torch, m, steps, warmup):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
-    names_f = ["fwd.prep", "fwd.walk"]
+    names_f = ["fwd.prep", "fwd.walk", "fwd.out"]
     names_b = ["bwd.walk_rev", "bwd.chunk", "bwd.dv"][:nb]
     kt = {}
     for i, nme in enumerate(names_f):
@@ -316,8 +317,9 @@ def traffic_for(kernel):
     return s.get("traffic_bytes")
 
 
-KERNEL_SYMBOLS = {"fwd.prep": "gla_prep_kernel", "fwd.walk": "gla_fwd_walk", "bwd.prep": "gla_prep_kernel",
-                  "bwd.walk_fwd": "walk_store", "bwd.walk_rev": "walk_reverse", "bwd.chunk": "gla_bwd_chunk",
+KERNEL_SYMBOLS = {"fwd.prep": "gla_prep_kernel", "fwd.walk": "walk_kernel", "fwd.out": "gla_fwd_out",
+                  "bwd.prep": "gla_prep_kernel",
+                  "bwd.walk_fwd": "walk_kernel", "bwd.walk_rev": "walk_kernel", "bwd.chunk": "gla_bwd_chunk",
                   "bwd.dv": "gla_bwd_dv"}
 
 

@@ -39,9 +39,10 @@
  *   - Supported sizes: B, H >= 1; L >= 1 (any value; the last chunk may be partial);
  *     C in {16, 32, 64, 128}; Dk and m multiples of 16 up to 256; Dv a multiple of 16 up to
  *     512; B*H <= 65535; every tensor 16-byte aligned.  Chunk tiles must fit a CU's LDS:
- *     bf16 excludes Dk > 128 with C = 128; float32 (a parity dtype) excludes C = 128 and
- *     Dk > 128 with C = 64.  Other values return GLA_ERR_UNSUPPORTED (shape errors such as
- *     L < 1 return GLA_ERR_SHAPE).
+ *     bf16 excludes Dk > 128 with C = 128; float32 (a parity dtype) excludes Dk > 128 with
+ *     C = 64, Dk > 64 with C = 128 and, for the backward, every Dk with C = 128.  Other
+ *     values return GLA_ERR_UNSUPPORTED (shape errors such as L < 1 return GLA_ERR_SHAPE);
+ *     a *_workspace_bytes() query returns 0 for them.
  *   - Results are deterministic: no floating-point atomics are used, so two runs on the same
  *     inputs give bitwise-identical outputs.
  *   - The library is reentrant and keeps no mutable global state.
@@ -108,10 +109,10 @@ int gla_bwd(const void* q, const void* k, const void* v, const void* g, const fl
 /* ---------------------------------------------------------------- profiling ------------
  * Same as gla_fwd / gla_bwd, and additionally records caller-created hipEvent_t handles on
  * `stream` at kernel boundaries: events[0] before the first kernel, events[i] after the i-th
- * (gla_fwd launches 2 kernels: chunk preparation, state walk; gla_bwd launches
+ * (gla_fwd launches 3 kernels: chunk preparation, state walk, chunk outputs; gla_bwd launches
  * gla_bwd_launch_count() kernels: chunk preparation, forward state walk, reverse state walk,
  * chunk gradients, and a value-gradient kernel when the key width is split).  nevents must
- * be at least 3 (forward) or 6 (backward), else GLA_ERR_NULL_ARG.  The events are owned by the caller and are only
+ * be at least 4 (forward) or 6 (backward), else GLA_ERR_NULL_ARG.  The events are owned by the caller and are only
  * recorded, never created, synchronised or destroyed.  Used to time individual kernels. */
 int gla_fwd_profiled(const void* q, const void* k, const void* v, const void* g, const float* h0,
                      void* o, float* ht,
@@ -144,7 +145,7 @@ int gla_bwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype);
  *   64, pad(Dk) = 32, 64, 128 or 256), about 130 MB at B=8, H=4, L=2048, Dk=128, Dv=256.
  * workspace (gla_bwd_saved): at least gla_bwd_saved_workspace_bytes() bytes.
  * events / nevents: optional (NULL, 0) launch-boundary events as for gla_*_profiled:
- *   gla_fwd_save launches 2 kernels (nevents >= 3), gla_bwd_saved launches
+ *   gla_fwd_save launches 3 kernels (nevents >= 4), gla_bwd_saved launches
  *   gla_bwd_launch_count() - 2 kernels (nevents >= 4).
  * Sizes, dtypes, alignment and errors as for gla_bwd (the saved path supports the sizes the
  * backward supports); `saved` must not overlap any input or output (GLA_ERR_ALIAS). */

@@ -123,10 +123,11 @@ hipError_t dispatch_bwd(int dtype, int DKP, int CP, const BwdParams& p, hipStrea
   return hipErrorInvalidValue;
 }
 
+// Forward workspace: the chunk operands, then the chunk-start states.
 size_t fwd_ws_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
-  (void)Dv;
   const size_t BH = (size_t)B * H, CP = pad_c(C), DKP = pad_dk(Dk), N = (L + C - 1) / C;
-  return ops_layout(BH, N, CP, DKP, esize_of(dtype), false).total;
+  const size_t es = esize_of(dtype);
+  return ops_layout(BH, N, CP, DKP, es, false).total + align_up(BH * N * DKP * pad_dv(Dv) * es);
 }
 
 struct BwdLayout {
@@ -226,8 +227,9 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* g, const f
   FwdParams p;
   p.q = q; p.k = k; p.v = v; p.g = g; p.h0 = h0; p.o = o; p.ht = ht;
   p.BH = (int)BH; p.L = L; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
-  p.ops = carve_ops(static_cast<char*>(workspace), ops_layout(BH, N, CP, DKP, es, false), false);
-  p.Hs = nullptr;
+  const OpsLayout ol = ops_layout(BH, N, CP, DKP, es, false);
+  p.ops = carve_ops(static_cast<char*>(workspace), ol, false);
+  p.Hs = static_cast<char*>(workspace) + ol.total;
   p.events = ev;
   if (dispatch_fwd(dtype, DKP, CP, p, static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;
@@ -469,8 +471,8 @@ GsaLayout gsa_layout(int B, int H, int L, int Dk, int Dv, int m, int C, int dtyp
   }
   l.ops2 = ops_layout(BH, N, CP, MP, es, bwd);
   l.ops2base = take(l.ops2.total);
+  l.Hs2 = take(BH * N * MP * DvP * es);
   if (bwd) {
-    l.Hs2 = take(BH * N * MP * DvP * es);
     l.dHs2 = take(BH * N * MP * DvP * es);
   }
   l.total = off;
@@ -487,9 +489,10 @@ GsaParams gsa_params(const GsaLayout& l, char* ws, int B, int H, int L, int Dk, 
     p.dP = ws + l.dP; p.dW2 = ws + l.dW2;
     p.dg2 = reinterpret_cast<float*>(ws + l.dg2); p.dZ = reinterpret_cast<float*>(ws + l.dZ);
     p.dS1s = ws + l.dS1s; p.dZsT = ws + l.dZsT;
-    p.Hs2 = ws + l.Hs2; p.dHs2 = ws + l.dHs2;
+    p.dHs2 = ws + l.dHs2;
   }
   p.ops2 = carve_ops(ws + l.ops2base, l.ops2, bwd);
+  p.Hs2 = ws + l.Hs2;
   return p;
 }
 

@@ -687,7 +687,7 @@ hipError_t launch_gsa_fwd(const GsaParams& p, hipStream_t s) {
     FwdParams f;
     f.q = p.P; f.k = p.W; f.v = p.v; f.g = p.g; f.h0 = p.hv0; f.o = p.o; f.ht = p.hvt;
     f.BH = p.BH; f.L = p.L; f.Dk = p.m; f.Dv = p.Dv; f.C = p.C; f.N = p.N;
-    f.ops = p.ops2; f.Hs = nullptr; f.events = LaunchEvents{nullptr, 0};
+    f.ops = p.ops2; f.Hs = p.Hs2; f.events = LaunchEvents{nullptr, 0};
     return launch_gla_fwd<T, MP, CP>(f, s);
   }
 }

@@ -32,7 +32,7 @@ struct FwdParams {
   float* ht;
   int BH, L, Dk, Dv, C, N;
   ChunkOps ops;   // ops.QsT != nullptr: the preparation also writes Qs^T (kept for a backward)
-  void* Hs;       // [BH][N][DKP][DvP] chunk-start states (T), written when not nullptr
+  void* Hs;       // [BH][N][DKP][DvP] chunk-start states (T), written by the state walk
   LaunchEvents events;
 };
 
@@ -104,7 +104,7 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s);
 bool gsa_config_fits(int esize, int MP, int CP);
 
 // Kernel launches per call (for the profiled entry points).
-constexpr int GLA_FWD_LAUNCHES = 2;
+constexpr int GLA_FWD_LAUNCHES = 3;
 constexpr int GLA_BWD_MAX_LAUNCHES = 5;
 int bwd_launch_count(int esize, int DKP, int CP);   // self-contained backward; 2 fewer when saved
 

@@ -61,7 +61,9 @@ def test_dtype_shape_unsupported(lib):
     assert fwd(lib, Dk=512) == 4
     assert fwd(lib, Dv=520) == 4
     assert fwd(lib, Dk=256, C=128) == 4               # LDS limit (bf16)
-    assert fwd(lib, Dk=64, C=128, dt=0) == 4          # LDS limit (fp32)
+    assert fwd(lib, Dk=128, C=128, dt=0) == 4         # LDS limit (fp32)
+    assert lib.gla_fwd_workspace_bytes(1, 1, 64, 64, 16, 128, 0) > 0        # fp32 forward fits
+    assert lib.gla_bwd_workspace_bytes(1, 1, 64, 64, 16, 128, 0) == 0       # its backward does not
     assert fwd(lib, B=70000) == 4                     # grid limit
 
 
@@ -85,10 +87,11 @@ def test_null_workspace_alias(lib):
 
 
 def test_workspace_sizes(lib):
-    # forward: Qs, KdT (C x Dk each, bf16), A (C x C), Gamma (fp32) per chunk, 256-byte aligned
+    # forward: Qs, KdT (C x Dk each, bf16), A (C x C), Gamma (fp32) per chunk, 256-byte
+    # aligned, then the chunk-start states (Dk x Dv bf16 per chunk)
     B, H, L, Dk, Dv, C = 8, 4, 2048, 128, 256, 64
     N = L // C
-    expect = 2 * (B * H * N * C * Dk * 2) + B * H * N * C * C * 2 + B * H * N * Dk * 4
+    expect = 2 * (B * H * N * C * Dk * 2) + B * H * N * C * C * 2 + B * H * N * Dk * 4 + B * H * N * Dk * Dv * 2
     assert lib.gla_fwd_workspace_bytes(B, H, L, Dk, Dv, C, 1) == expect
     assert lib.gla_bwd_workspace_bytes(B, H, L, Dk, Dv, C, 1) > expect
     assert lib.gla_fwd_workspace_bytes(1, 1, 64, 16, 16, 48, 1) == 0

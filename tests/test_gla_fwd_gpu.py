@@ -57,6 +57,7 @@ SHAPES = [
     (1, 2, 70, 128, 96, 64, "f32", True),
     (1, 1, 140, 64, 64, 64, "f32", False),
     (1, 1, 66, 256, 32, 32, "f32", True),
+    (1, 2, 300, 64, 80, 128, "f32", True),      # fp32 with C=128: forward only
 ]
 
 
