@@ -470,18 +470,15 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
     }
   }
   __syncthreads();
+  // later segments' suffix totals of u, earlier segments' prefix totals of y
+  for (int t = tid; t < 2 * DKS; t += 256)
+    seg_scan_channel<NSEG>(segtot + (t < DKS ? 0 : NSEG * DKS), DKS, t < DKS ? t : t - DKS, t < DKS);
+  __syncthreads();
   if (cs.active) {
     float add[V];
 #pragma unroll
-    for (int e = 0; e < V; ++e) add[e] = sZ[c0 + e];
-    for (int s2 = cs.seg + 1; s2 < NSEG; ++s2) {
-#pragma unroll
-      for (int e = 0; e < V; ++e) add[e] += segtot[s2 * DKS + c0 + e];
-    }
-    for (int s2 = 0; s2 < cs.seg; ++s2) {
-#pragma unroll
-      for (int e = 0; e < V; ++e) add[e] += segtot[(NSEG + s2) * DKS + c0 + e];
-    }
+    for (int e = 0; e < V; ++e)
+      add[e] = sZ[c0 + e] + segtot[cs.seg * DKS + c0 + e] + segtot[(NSEG + cs.seg) * DKS + c0 + e];
     float* dgg = p.dg + qbase;
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {

@@ -628,18 +628,16 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
     }
   }
   __syncthreads();
+  // later segments' suffix totals of u, earlier segments' prefix totals of y
+  for (int t = tid; t < 2 * MP; t += 256)
+    seg_scan_channel<NSEG>(segtot + (t < MP ? 0 : NSEG * MP), MP, t < MP ? t : t - MP, t < MP);
+  __syncthreads();
   if (cs.active) {
     float add[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) add[e] = sZ1[c0 + e];
-    for (int s2 = cs.seg + 1; s2 < NSEG; ++s2) {
 #pragma unroll
-      for (int e = 0; e < V; ++e) add[e] += segtot[s2 * MP + c0 + e];
-    }
-    for (int s2 = 0; s2 < cs.seg; ++s2) {
-#pragma unroll
-      for (int e = 0; e < V; ++e) add[e] += segtot[(NSEG + s2) * MP + c0 + e];
-    }
+    for (int e = 0; e < V; ++e) add[e] += segtot[cs.seg * MP + c0 + e] + segtot[(NSEG + cs.seg) * MP + c0 + e];
     const T* dW2g = reinterpret_cast<const T*>(p.dW2) + gbase;
     const float* dg2g = p.dg2 + gbase;
     float* dgg = p.dg + gbase;

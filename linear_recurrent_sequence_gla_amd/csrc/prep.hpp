@@ -135,6 +135,33 @@ __device__ __forceinline__ typename V16<T>::type zero_vec() {
   return z;
 }
 
+// In-place exclusive scan along the NSEG segment totals of each channel of an [NSEG][width]
+// array: prefix (sum over earlier segments) or suffix (sum over later segments).  One thread
+// per channel, all NSEG values read into registers first, so the cost is one LDS round trip
+// instead of a per-thread loop over segments.  The caller synchronises before and after.
+template <int NSEG>
+__device__ __forceinline__ void seg_scan_channel(float* a, int width, int ch, bool suffix) {
+  float v[NSEG];
+#pragma unroll
+  for (int s = 0; s < NSEG; ++s) v[s] = a[s * width + ch];
+  float run = 0.f;
+  if (suffix) {
+#pragma unroll
+    for (int s = NSEG - 1; s >= 0; --s) {
+      const float x = v[s];
+      a[s * width + ch] = run;
+      run += x;
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NSEG; ++s) {
+      const float x = v[s];
+      a[s * width + ch] = run;
+      run += x;
+    }
+  }
+}
+
 // Chunk-local gate scan for the thread's (channel group, row segment): loads g, q, k
 // vectors (16-byte, all issued before first use), keeps b (log2 units) and the raw q and k
 // of its rows and channels, publishes Gamma in sGam and returns the block-wide max |b|.
@@ -201,15 +228,13 @@ struct ChunkScan {
       for (int e = 0; e < V; ++e) segtot[seg * DKP + cg * V + e] = run_[e];
     }
     __syncthreads();
+    for (int ch = threadIdx.x; ch < DKP; ch += 256) seg_scan_channel<M::NSEG>(segtot, DKP, ch, false);
+    __syncthreads();
     float mx = 0.f;
     if (active) {
       float pre[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) pre[e] = 0.f;
-      for (int s = 0; s < seg; ++s) {
-#pragma unroll
-        for (int e = 0; e < V; ++e) pre[e] += segtot[s * DKP + cg * V + e];
-      }
+      for (int e = 0; e < V; ++e) pre[e] = segtot[seg * DKP + cg * V + e];
 #pragma unroll
       for (int u = 0; u < RPS; ++u) {
 #pragma unroll
