@@ -163,14 +163,17 @@ template <> struct V16<float> { static constexpr int N = 4; typedef f32x4 type; 
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Block-wide max of a non-negative value (256 threads); `red` holds >= 8 floats of LDS.
-__device__ __forceinline__ float block_max256(float v, float* red) {
+// Block-wide max of a non-negative value over NT threads; `red` holds >= NT/64 floats of LDS.
+template <int NT = 256>
+__device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) red[wave] = v;
   __syncthreads();
-  float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) r = fmaxf(r, red[w]);
   __syncthreads();
   return r;
 }

@@ -41,13 +41,17 @@
 namespace gla {
 
 // ======================================================================= chunk gradients
+// The chunk-gradient kernel runs 512 threads (8 waves): one workgroup fills a CU's LDS, and
+// two waves per SIMD let one wave's LDS and matrix-core latencies hide behind the other's.
+constexpr int kBwdThreads = 512;
+
 // LDS phases of the chunk kernel:
 //   front   sdA, sdA^T [CP][CP] (written after the Dv loop, read to the end), diag of dA (fp32)
 //   phase 1 (Dv loop)    sKd, sA (with dv) and the Dv slice tiles dO, V, H, dH (+ dV)
 //   phase 2 (intra)      Qs^T, Ks^T [DKS][CP] for the intra-chunk products
 //   phase 3 (epilogue)   three fp32 [CP][DKS] gradient tiles; on the exact path b takes the
 //                        place of the (unused) intra dk tile
-constexpr size_t chunk_bwd_bytes(int es, int DKS, int CP, bool dv, int nseg) {
+constexpr size_t chunk_bwd_bytes(int es, int DKS, int CP, bool dv, int nseg) {   // nseg for kBwdThreads
   const size_t V = 16 / es;
   const size_t LDQ = DKS + V, LDC = CP + V, LDV = kDvTile + V, LDF = DKS + 4;
   const size_t QT = CP * LDQ * es, CT = CP * LDC * es, VT = CP * LDV * es, HT = DKS * LDV * es;
@@ -61,7 +65,8 @@ constexpr size_t chunk_bwd_bytes(int es, int DKS, int CP, bool dv, int nseg) {
 
 template <typename T, int DKS, int CP, bool WITH_DV>
 struct BwdChunkCfg {
-  using M = ChunkMap<T, DKS, CP>;
+  static constexpr int NT = kBwdThreads;
+  using M = ChunkMap<T, DKS, CP, NT>;
   static constexpr int V = 16 / (int)sizeof(T);
   static constexpr int LDQ = DKS + V, LDC = CP + V, LDV = kDvTile + V, LDF = DKS + 4;
   static constexpr size_t QT = (size_t)CP * LDQ * sizeof(T);
@@ -76,7 +81,7 @@ struct BwdChunkCfg {
   static constexpr size_t MAIN = 2 * CT + cmax(cmax(PH1, PH2), PH3);
   static constexpr size_t BYTES = chunk_bwd_bytes(sizeof(T), DKS, CP, WITH_DV, M::NSEG);
   static constexpr int NV = CP * kDvTile / V, NH = DKS * kDvTile / V;
-  static constexpr int PV = (NV + 255) / 256, PH = (NH + 255) / 256;
+  static constexpr int PV = (NV + NT - 1) / NT, PH = (NH + NT - 1) / NT;
 };
 
 // One 64-column Dv slice of dO, V (chunk rows) and of H_n, dH_{n+1} (key rows) in flight.
@@ -97,7 +102,7 @@ struct SliceStage {
     constexpr int PER_ROW = kDvTile / Cf::V;
 #pragma unroll
     for (int m = 0; m < Cf::PV; ++m) {
-      const int idx = tid + 256 * m;
+      const int idx = tid + Cf::NT * m;
       const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
       const int jj = js * kDvTile + c;
       vok[m] = idx < Cf::NV && r < len && jj < Dv;
@@ -107,7 +112,7 @@ struct SliceStage {
     }
 #pragma unroll
     for (int m = 0; m < Cf::PH; ++m) {
-      const int idx = tid + 256 * m;
+      const int idx = tid + Cf::NT * m;
       const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
       hok[m] = idx < Cf::NH && r < kvalid;
       const size_t off = (size_t)min(r, kvalid - 1) * DVP + js * kDvTile + c;
@@ -130,7 +135,7 @@ struct SliceStage {
     constexpr int PER_ROW = kDvTile / Cf::V;
 #pragma unroll
     for (int m = 0; m < Cf::PV; ++m) {
-      const int idx = tid + 256 * m;
+      const int idx = tid + Cf::NT * m;
       if (idx < Cf::NV) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
         *reinterpret_cast<VT*>(sdO + r * Cf::LDV + c) = vok[m] ? dov[m] : zero_vec<T>();
@@ -139,7 +144,7 @@ struct SliceStage {
     }
 #pragma unroll
     for (int m = 0; m < Cf::PH; ++m) {
-      const int idx = tid + 256 * m;
+      const int idx = tid + Cf::NT * m;
       if (idx < Cf::NH) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * Cf::V;
         *reinterpret_cast<VT*>(sH + r * Cf::LDV + c) = hok[m] ? hv[m] : zero_vec<T>();
@@ -150,19 +155,19 @@ struct SliceStage {
 };
 
 // The chunk's A tile [CP][CP] in flight to LDS (16-byte vectors, issued early).
-template <typename T, int CP>
+template <typename T, int CP, int NT>
 struct ATileStage {
-  static constexpr int V = 16 / (int)sizeof(T), N = CP * CP / V, P = (N + 255) / 256;
+  static constexpr int V = 16 / (int)sizeof(T), N = CP * CP / V, P = (N + NT - 1) / NT;
   typedef typename V16<T>::type VT;
   VT a[P];
   __device__ __forceinline__ void load(const T* src) {
 #pragma unroll
-    for (int m = 0; m < P; ++m) a[m] = *reinterpret_cast<const VT*>(src + (size_t)min((int)threadIdx.x + 256 * m, N - 1) * V);
+    for (int m = 0; m < P; ++m) a[m] = *reinterpret_cast<const VT*>(src + (size_t)min((int)threadIdx.x + NT * m, N - 1) * V);
   }
   __device__ __forceinline__ void store(T* dst, int lds) const {
 #pragma unroll
     for (int m = 0; m < P; ++m) {
-      const int idx = threadIdx.x + 256 * m;
+      const int idx = threadIdx.x + NT * m;
       if (idx < N) {
         const int r = idx / (CP / V), c = (idx - r * (CP / V)) * V;
         *reinterpret_cast<VT*>(dst + r * lds + c) = a[m];
@@ -172,14 +177,15 @@ struct ATileStage {
 };
 
 template <typename T, int DKS, int CP, bool WITH_DV>
-__global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int ntile) {
+__global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DKP, int ntile) {
   using Cf = BwdChunkCfg<T, DKS, CP, WITH_DV>;
-  using M = ChunkMap<T, DKS, CP>;
+  constexpr int NT = Cf::NT, NW = NT / 64;
+  using M = ChunkMap<T, DKS, CP, NT>;
   constexpr int V = M::V, RPS = M::RPS, NSEG = M::NSEG;
   constexpr int LDQ = Cf::LDQ, LDC = Cf::LDC, LDV = Cf::LDV, LDF = Cf::LDF;
   constexpr int NBR = CP / 16, NIB = DKS / 16, NJB = kDvTile / 16;
   constexpr int NA_BLK = NBR * NBR, NQ_BLK = NBR * NIB, NV_BLK = NBR * NJB;
-  constexpr int PA = (NA_BLK + 3) / 4, PQ = (NQ_BLK + 3) / 4, PVb = (NV_BLK + 3) / 4;
+  constexpr int PA = (NA_BLK + NW - 1) / NW, PQ = (NQ_BLK + NW - 1) / NW, PVb = (NV_BLK + NW - 1) / NW;
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
   T* sdA = reinterpret_cast<T*>(smem);                            // strictly lower dA
@@ -225,11 +231,11 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
 
   // every independent load goes out before the first wait: q, k, g of the chunk, the first
   // Dv slice and (with dv) the chunk's A tile
-  ChunkScan<T, DKS, CP> cs;
+  ChunkScan<T, DKS, CP, true, NT> cs;
   cs.load(qg, kg, reinterpret_cast<const T*>(p.g) + qbase, Dk, Dk - ch0, len);
   SliceStage<T, DKS, CP, WITH_DV> st;
   st.load(dog, vg, hs, dhs, len, Dv, DVP, 0, kvalid);
-  ATileStage<T, CP> at;
+  ATileStage<T, CP, NT> at;
   if constexpr (WITH_DV) at.load(reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP);
   const float maxb = cs.finish(segtot, sGam, red);
   const bool fast = maxb <= kSpanLimit;
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
     st.load(dog, vg, hs, dhs, len, Dv, DVP, min(js + 1, ntile - 1), kvalid);   // last: harmless reload
 #pragma unroll
     for (int s = 0; s < PA; ++s) {       // dA += dO V^T
-      const int blk = wave + 4 * s;
+      const int blk = wave + NW * s;
       if (blk < NA_BLK) {
         const int rb = blk / NBR, cb = blk % NBR;
 #pragma unroll
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
     }
 #pragma unroll
     for (int s = 0; s < PQ; ++s) {       // dQ += dO H^T ; dKI += V dH^T
-      const int blk = wave + 4 * s;
+      const int blk = wave + NW * s;
       if (blk < NQ_BLK) {
         const int rb = blk / NIB, ib = blk % NIB;
 #pragma unroll
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
     if constexpr (WITH_DV) {             // dV = A^T dO + Kd dH for this slice
 #pragma unroll
       for (int s = 0; s < PVb; ++s) {
-        const int blk = wave + 4 * s;
+        const int blk = wave + NW * s;
         if (blk < NV_BLK) {
           const int cb = blk / NJB, jb = blk % NJB;
           f32x4 acc = zero4();
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
     if constexpr (WITH_DV) {
       T* dvg = reinterpret_cast<T*>(p.dv) + ((size_t)bh * L + row0) * Dv;
       constexpr int PER_ROW = kDvTile / V;
-      for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
+      for (int idx = tid; idx < CP * PER_ROW; idx += NT) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
         const int jj = js * kDvTile + c;
         if (r < len && jj < Dv)
@@ -328,7 +334,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
       float z = zp[m];
 #pragma unroll
       for (int off = 1; off < PER_ROW; off <<= 1) z += __shfl_xor(z, off, 64);
-      const int idx = tid + 256 * m, r = idx / PER_ROW;
+      const int idx = tid + NT * m, r = idx / PER_ROW;
       if (idx < Cf::NH && idx % PER_ROW == 0) sZ[r] = r < kvalid ? z * fast_exp2(sGam[r]) : 0.f;
     }
   }
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
   // factorised path also Qs^T and Ks^T (the phase-1 tiles are dead here)
 #pragma unroll
   for (int s = 0; s < PA; ++s) {
-    const int blk = wave + 4 * s;
+    const int blk = wave + NW * s;
     if (blk < NA_BLK) {
       const int rb = blk / NBR, cb = blk % NBR;
 #pragma unroll
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
   if (fast) {                            // off-diagonal intra terms on MFMA
 #pragma unroll
     for (int s = 0; s < PQ; ++s) {
-      const int blk = wave + 4 * s;
+      const int blk = wave + NW * s;
       if (blk < NQ_BLK) {
         const int rb = blk / NIB, ib = blk % NIB;
 #pragma unroll
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
   __syncthreads();                       // phase-1 tiles are dead from here on
 #pragma unroll
   for (int s = 0; s < PQ; ++s) {
-    const int blk = wave + 4 * s;
+    const int blk = wave + NW * s;
     if (blk < NQ_BLK) {
       const int rb = blk / NIB, ib = blk % NIB;
 #pragma unroll
@@ -471,7 +477,7 @@ __global__ __launch_bounds__(256) void gla_bwd_chunk(BwdParams p, int DKP, int n
   }
   __syncthreads();
   // later segments' suffix totals of u, earlier segments' prefix totals of y
-  for (int t = tid; t < 2 * DKS; t += 256)
+  for (int t = tid; t < 2 * DKS; t += NT)
     seg_scan_channel<NSEG>(segtot + (t < DKS ? 0 : NSEG * DKS), DKS, t < DKS ? t : t - DKS, t < DKS);
   __syncthreads();
   if (cs.active) {
@@ -573,7 +579,7 @@ __global__ __launch_bounds__(256) void gla_bwd_dv(BwdParams p, int ntile) {
 template <typename T, int DKP, int CP>
 struct BwdPlan {
   static constexpr int es = sizeof(T);
-  static constexpr int nseg(int dks) { return imin(256 / (dks / (16 / es)), CP); }
+  static constexpr int nseg(int dks) { return imin(kBwdThreads / (dks / (16 / es)), CP); }
   static constexpr bool fits(int dks, bool dv) { return chunk_bwd_bytes(es, dks, CP, dv, nseg(dks)) <= kMaxLds; }
   static constexpr bool FUSED = fits(DKP, true);
   static constexpr int DKS = FUSED ? DKP
@@ -605,7 +611,7 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
     WalkIO wr{p.ops.QsT, p.do_, p.ops.Gam, p.dHs, p.dht, p.dh0, p.Dk, p.Dv, p.L, p.C, p.N, 0};
     if ((e = launch_walk_reverse<T, DKP, CP>(wr, p.BH, s)) != hipSuccess) return e;
     record_event(p.events, ev++, s);
-    hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED>), dim3(p.N, p.BH, DKP / P::DKS), dim3(256), 0, s,
+    hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED>), dim3(p.N, p.BH, DKP / P::DKS), dim3(kBwdThreads), 0, s,
                        p, DKP, ntile);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     record_event(p.events, ev++, s);

@@ -51,14 +51,15 @@ struct PrepParams {
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 constexpr int imin(int a, int b) { return a < b ? a : b; }
 
-// Thread -> (channel group, row segment) map for the element-wise phase of a chunk.
-template <typename T, int DKP, int CP>
+// Thread -> (channel group, row segment) map for the element-wise phase of a chunk, for a
+// workgroup of NT threads.
+template <typename T, int DKP, int CP, int NT = 256>
 struct ChunkMap {
   static constexpr int V = 16 / (int)sizeof(T);        // channels per thread (one 16-byte vector)
   static constexpr int NCG = DKP / V;                  // channel groups
-  static constexpr int NSEG = imin(256 / NCG, CP);     // row segments
+  static constexpr int NSEG = imin(NT / NCG, CP);      // row segments
   static constexpr int RPS = CP / NSEG;                // rows per segment
-  static constexpr int ACTIVE = NCG * NSEG;            // threads with work (<= 256)
+  static constexpr int ACTIVE = NCG * NSEG;            // threads with work (<= NT)
 };
 
 template <typename T, int DKP, int CP>
@@ -168,10 +169,10 @@ __device__ __forceinline__ void seg_scan_channel(float* a, int width, int ch, bo
 // load() only issues the loads -- unconditionally, from clamped in-bounds addresses, with the
 // validity kept beside them -- so a kernel can put other independent loads in flight before
 // finish() consumes these.  run() is load() then finish().  finish() must be called by all
-// 256 threads.  With LOAD_QK = false only g is loaded, and qv holds the raw gate values.
-template <typename T, int DKP, int CP, bool LOAD_QK = true>
+// NT threads.  With LOAD_QK = false only g is loaded, and qv holds the raw gate values.
+template <typename T, int DKP, int CP, bool LOAD_QK = true, int NT = 256>
 struct ChunkScan {
-  using M = ChunkMap<T, DKP, CP>;
+  using M = ChunkMap<T, DKP, CP, NT>;
   static constexpr int V = M::V, RPS = M::RPS;
   typedef typename V16<T>::type VT;
   float b[RPS][V];
@@ -228,7 +229,7 @@ struct ChunkScan {
       for (int e = 0; e < V; ++e) segtot[seg * DKP + cg * V + e] = run_[e];
     }
     __syncthreads();
-    for (int ch = threadIdx.x; ch < DKP; ch += 256) seg_scan_channel<M::NSEG>(segtot, DKP, ch, false);
+    for (int ch = threadIdx.x; ch < DKP; ch += NT) seg_scan_channel<M::NSEG>(segtot, DKP, ch, false);
     __syncthreads();
     float mx = 0.f;
     if (active) {
@@ -248,7 +249,7 @@ struct ChunkScan {
         for (int e = 0; e < V; ++e) sGam[cg * V + e] = b[RPS - 1][e];
       }
     }
-    return block_max256(mx, red);   // also makes sGam visible to all threads
+    return block_max<NT>(mx, red);   // also makes sGam visible to all threads
   }
 
   __device__ __forceinline__ float run(const T* qg, const T* kg, const T* gg, int ld, int width, int len,
