@@ -19,31 +19,33 @@
 
 namespace gla {
 
-// LDS tiles of one output workgroup: Qs [CP][DKP], A [CP][CP], H_n [DKP][64], V [CP][64].
+// One output workgroup: O [CP rows][64 columns] of one chunk.  Wave w owns the 16-row blocks
+// w, w+4, ... of O across all 64 columns.  Its row operands (Qs, A rows) are loaded straight
+// from global memory into registers -- each row block is read by exactly one wave -- while the
+// column operands every wave shares (H_n [DKP][64], V [CP][64]) are staged in LDS and read
+// with transposing LDS reads.
 template <typename T, int DKP, int CP>
 struct OutCfg {
   static constexpr int V = 16 / (int)sizeof(T);
-  static constexpr int LDQ = DKP + V, LDA = CP + V, LDV = kDvTile + V;
-  static constexpr size_t QT = (size_t)CP * LDQ * sizeof(T);
-  static constexpr size_t AT = (size_t)CP * LDA * sizeof(T);
+  static constexpr int LDV = kDvTile + V;
   static constexpr size_t HT = (size_t)DKP * LDV * sizeof(T);
   static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
-  static constexpr size_t BYTES = QT + AT + HT + VT;
-  static constexpr int NQ = CP * DKP / V, NA = CP * CP / V, NH = DKP * kDvTile / V, NV = CP * kDvTile / V;
-  static constexpr int PQ = (NQ + 255) / 256, PA = (NA + 255) / 256, PH = (NH + 255) / 256, PV = (NV + 255) / 256;
+  static constexpr size_t OT = (size_t)CP * LDV * sizeof(T);
+  static constexpr size_t BYTES = HT + VT > OT ? HT + VT : OT;   // O staging reuses H, V
+  static constexpr int NH = DKP * kDvTile / V, NV = CP * kDvTile / V;
+  static constexpr int PH = (NH + 255) / 256, PV = (NV + 255) / 256;
+  static constexpr int NBR = CP / 16, RBW = (NBR + 3) / 4;       // row blocks, per wave
 };
 
 template <typename T, int DKP, int CP>
 __global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
   using W = OutCfg<T, DKP, CP>;
-  constexpr int LDQ = W::LDQ, LDA = W::LDA, LDV = W::LDV, V = W::V;
-  constexpr int NBR = CP / 16, NKB = DKP / 32, NCB = CP / 32;
+  constexpr int LDV = W::LDV, V = W::V, NBR = W::NBR, RBW = W::RBW;
+  constexpr int NKB = DKP / 32, NCB = CP / 32, NJB = kDvTile / 16;
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[W::BYTES];
-  T* sQ = reinterpret_cast<T*>(smem);
-  T* sA = reinterpret_cast<T*>(smem + W::QT);
-  T* sH = reinterpret_cast<T*>(smem + W::QT + W::AT);
-  T* sV = reinterpret_cast<T*>(smem + W::QT + W::AT + W::HT);
+  T* sH = reinterpret_cast<T*>(smem);
+  T* sV = reinterpret_cast<T*>(smem + W::HT);
 
   // the ntile value tiles of one chunk are consecutive, so they share an XCD's L2 for Qs, A
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -57,15 +59,12 @@ __global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
   const T* Hc = reinterpret_cast<const T*>(p.Hs) + chunk * DKP * DvP + tile * kDvTile;
   const T* vg = reinterpret_cast<const T*>(p.v) + ((size_t)bh * L + row0) * Dv;
 
-  // all loads first (16-byte vectors; value rows past the chunk end and columns past Dv are
-  // read from clamped addresses and zeroed when stored)
-  VT q[W::PQ], a[W::PA], h[W::PH], v[W::PV];
+  // all loads first: shared tiles (16-byte vectors; value rows past the chunk end and columns
+  // past Dv come from clamped addresses and are zeroed when stored), then this wave's row
+  // operands as matrix-core fragments
+  VT h[W::PH], v[W::PV];
   bool vok[W::PV];
   constexpr int PER_ROW = kDvTile / V;
-#pragma unroll
-  for (int m = 0; m < W::PQ; ++m) q[m] = *reinterpret_cast<const VT*>(Qc + (size_t)min(tid + 256 * m, W::NQ - 1) * V);
-#pragma unroll
-  for (int m = 0; m < W::PA; ++m) a[m] = *reinterpret_cast<const VT*>(Ac + (size_t)min(tid + 256 * m, W::NA - 1) * V);
 #pragma unroll
   for (int m = 0; m < W::PH; ++m) {
     const int idx = min(tid + 256 * m, W::NH - 1), r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
@@ -78,21 +77,14 @@ __global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
     vok[m] = idx < W::NV && r < len && j < Dv;
     v[m] = *reinterpret_cast<const VT*>(vg + (size_t)min(r, len - 1) * Dv + min(j, Dv - V));
   }
+  Frag<T> xq[RBW][NKB], xa[RBW][NCB];
 #pragma unroll
-  for (int m = 0; m < W::PQ; ++m) {
-    const int idx = tid + 256 * m;
-    if (idx < W::NQ) {
-      const int r = idx / (DKP / V), c = (idx - r * (DKP / V)) * V;
-      *reinterpret_cast<VT*>(sQ + r * LDQ + c) = q[m];
-    }
-  }
+  for (int s = 0; s < RBW; ++s) {
+    const int rb = min(wave + 4 * s, NBR - 1);
 #pragma unroll
-  for (int m = 0; m < W::PA; ++m) {
-    const int idx = tid + 256 * m;
-    if (idx < W::NA) {
-      const int r = idx / (CP / V), c = (idx - r * (CP / V)) * V;
-      *reinterpret_cast<VT*>(sA + r * LDA + c) = a[m];
-    }
+    for (int kb = 0; kb < NKB; ++kb) xq[s][kb] = ld8(Qc + (16 * rb + col) * DKP + 32 * kb + 8 * grp);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) xa[s][cb] = ld8(Ac + (16 * rb + col) * CP + 32 * cb + 8 * grp);
   }
 #pragma unroll
   for (int m = 0; m < W::PH; ++m) {
@@ -112,28 +104,40 @@ __global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
   }
   __syncthreads();
 
-  // O = Qs H + A V; each wave owns 16 of the 64 columns
-  f32x4 O[NBR];
+  // O = Qs H + A V
+  f32x4 O[RBW][NJB];
 #pragma unroll
-  for (int rb = 0; rb < NBR; ++rb) O[rb] = zero4();
+  for (int s = 0; s < RBW; ++s) {
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    const Frag<T> Yh = ld8_colblk(sH + (32 * kb) * LDV + 16 * wave, LDV);
-#pragma unroll
-    for (int rb = 0; rb < NBR; ++rb) mma(O[rb], ld8(sQ + (16 * rb + col) * LDQ + 32 * kb + 8 * grp), Yh);
+    for (int jb = 0; jb < NJB; ++jb) O[s][jb] = zero4();
   }
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const Frag<T> Yv = ld8_colblk(sV + (32 * cb) * LDV + 16 * wave, LDV);
+  for (int jb = 0; jb < NJB; ++jb) {
 #pragma unroll
-    for (int rb = 0; rb < NBR; ++rb) mma(O[rb], ld8(sA + (16 * rb + col) * LDA + 32 * cb + 8 * grp), Yv);
+    for (int kb = 0; kb < NKB; ++kb) {
+      const Frag<T> Yh = ld8_colblk(sH + (32 * kb) * LDV + 16 * jb, LDV);
+#pragma unroll
+      for (int s = 0; s < RBW; ++s) mma(O[s][jb], xq[s][kb], Yh);
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const Frag<T> Yv = ld8_colblk(sV + (32 * cb) * LDV + 16 * jb, LDV);
+#pragma unroll
+      for (int s = 0; s < RBW; ++s) mma(O[s][jb], xa[s][cb], Yv);
+    }
   }
-  __syncthreads();   // sQ and sA are free: stage O there for 16-byte stores
-  T* sO = sQ;
+  __syncthreads();   // H and V are consumed: stage O in their place for 16-byte stores
+  T* sO = reinterpret_cast<T*>(smem);
 #pragma unroll
-  for (int rb = 0; rb < NBR; ++rb) {
+  for (int s = 0; s < RBW; ++s) {
+    const int rb = wave + 4 * s;
+    if (rb < NBR) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sO[(16 * rb + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(O[rb][e]);
+      for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sO[(16 * rb + 4 * grp + e) * LDV + 16 * jb + col] = from_f32<T>(O[s][jb][e]);
+      }
+    }
   }
   __syncthreads();
   T* og = reinterpret_cast<T*>(p.o) + ((size_t)bh * L + row0) * Dv;
@@ -148,8 +152,7 @@ __global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
 
 template <typename T, int DKP, int CP>
 constexpr bool fwd_fits() {
-  return PrepCfg<T, DKP, CP>::BYTES <= kMaxLds && walk_fits<T, DKP, CP>() && OutCfg<T, DKP, CP>::BYTES <= kMaxLds &&
-         (size_t)CP * OutCfg<T, DKP, CP>::LDV * sizeof(T) <= OutCfg<T, DKP, CP>::QT + OutCfg<T, DKP, CP>::AT;
+  return PrepCfg<T, DKP, CP>::BYTES <= kMaxLds && walk_fits<T, DKP, CP>() && OutCfg<T, DKP, CP>::BYTES <= kMaxLds;
 }
 
 template <typename T, int DKP, int CP>
