@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["gsa_recurrent_fwd", "gsa_recurrent_bwd"]
+__all__ = ["gsa_recurrent_fwd", "gsa_recurrent_bwd", "gsa_decode_step"]
 
 
 def _f64(x):
@@ -119,3 +119,31 @@ def gsa_recurrent_bwd(q, k, v, g, do, hk0=None, hv0=None, dhkt=None, dhvt=None,
             dV = a[..., None] * dV
     return {"dq": dq, "dk": dk, "dv": dv, "dg": dg,
             "dhk0": np.swapaxes(dK, -1, -2), "dhv0": dV}
+
+
+def gsa_decode_step(q, k, v, g, hk, hv):
+    """One recurrent inference step of GSA on a single token per (batch, head): the bounded
+    slot memories make inference O(1) in memory per token (GSA abstract: efficient recurrent
+    inference with a compact state; research-map summary, "Approach").
+
+    q, k [B,H,Dk]; v [B,H,Dv]; g [B,H,m] slot log-gates; hk [B,H,Dk,m] (= Kmem^T);
+    hv [B,H,m,Dv] (= Vmem).  Written slot by slot from the slot-memory definition:
+        for each slot s:  Kmem[s] <- alpha_s Kmem[s] + w_s k,   Vmem[s] <- alpha_s Vmem[s] + w_s v,
+                          z_s = <Kmem[s], q>
+        p = softmax(z),  o = sum_s p_s Vmem[s].
+    Returns (o [B,H,Dv], hk_new [B,H,Dk,m], hv_new [B,H,m,Dv]), float64.
+    """
+    q, k, v, g, hk, hv = map(_f64, (q, k, v, g, hk, hv))
+    m = g.shape[-1]
+    hk = hk.copy()
+    hv = hv.copy()
+    z = np.empty(g.shape)
+    for s in range(m):
+        a = np.exp(g[..., s])[..., None]
+        w = -np.expm1(g[..., s])[..., None]
+        hk[..., :, s] = a * hk[..., :, s] + w * k
+        hv[..., s, :] = a * hv[..., s, :] + w * v
+        z[..., s] = np.sum(hk[..., :, s] * q, axis=-1)
+    p = _softmax(z)
+    o = np.einsum("bhs,bhsd->bhd", p, hv)
+    return o, hk, hv

@@ -8,7 +8,7 @@ the separately pinned GLA oracle, (b) closed forms for one slot and for frozen m
 import numpy as np
 import pytest
 
-from oracle import gla_recurrent_bwd, gla_recurrent_fwd, gsa_recurrent_bwd, gsa_recurrent_fwd
+from oracle import gla_recurrent_bwd, gla_recurrent_fwd, gsa_decode_step, gsa_recurrent_bwd, gsa_recurrent_fwd
 
 
 def rand_gsa(seed, B=1, H=2, L=19, Dk=4, Dv=3, m=5, h0=True):
@@ -170,3 +170,43 @@ def test_gate_gradient_identity():
     final = np.sum(dhkt * hkt, axis=-2) + np.sum(dhvt * hvt, axis=-1)      # [B,H,m]
     dg = rc + final[:, :, None, :] - np.exp(g) * (dw1 + dw2)
     np.testing.assert_allclose(ref["dg"], dg, rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("h0", [False, True])
+def test_decode_steps_equal_two_pass_forward(h0):
+    """P17: T single-token GSA decode steps reproduce the two-pass form (built from the
+    separately pinned GLA oracle): every output and both final memories."""
+    q, k, v, g, hk0, hv0 = rand_gsa(11, B=2, H=2, L=9, Dk=5, Dv=4, m=3, h0=h0)
+    o2, hkt2, hvt2, *_ = two_pass_forward(q, k, v, g, hk0, hv0)
+    B, H, L, Dk = q.shape
+    hk = np.zeros((B, H, Dk, 3)) if hk0 is None else hk0
+    hv = np.zeros((B, H, 3, 4)) if hv0 is None else hv0
+    for t in range(L):
+        ot, hk, hv = gsa_decode_step(q[:, :, t], k[:, :, t], v[:, :, t], g[:, :, t], hk, hv)
+        np.testing.assert_allclose(ot, o2[:, :, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(hk, hkt2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(hv, hvt2, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_step_closed_forms():
+    """P18: closed forms of one decode step.
+    (a) g = 0: alpha = 1, w = 0, the memories are unchanged and o = softmax(q hk) hv;
+    (b) g -> -inf: alpha = 0, w = 1, every slot is overwritten with the token, the slots are
+        equal, the softmax is uniform and o = v;
+    (c) m = 1: o = alpha hv + (1 - alpha) v whatever q and k are."""
+    q, k, v, g, hk0, hv0 = rand_gsa(12, L=1, Dk=6, Dv=5, m=4)
+    q, k, v, g = q[:, :, 0], k[:, :, 0], v[:, :, 0], g[:, :, 0]
+    o, hk, hv = gsa_decode_step(q, k, v, np.zeros_like(g), hk0, hv0)
+    np.testing.assert_array_equal(hk, hk0)
+    np.testing.assert_array_equal(hv, hv0)
+    z = (q[..., None, :] @ hk0)[..., 0, :]
+    np.testing.assert_allclose(o, (softmax(z)[..., None, :] @ hv0)[..., 0, :], rtol=1e-12, atol=1e-12)
+    o, hk, hv = gsa_decode_step(q, k, v, np.full_like(g, -800.0), hk0, hv0)
+    np.testing.assert_array_equal(hk, np.repeat(k[..., :, None], 4, axis=-1))
+    np.testing.assert_array_equal(hv, np.repeat(v[..., None, :], 4, axis=-2))
+    np.testing.assert_allclose(o, v, rtol=1e-12, atol=1e-12)
+    q1, k1, v1, g1, hk1, hv1 = rand_gsa(13, L=1, Dk=6, Dv=5, m=1)
+    o, _, hv = gsa_decode_step(q1[:, :, 0], k1[:, :, 0], v1[:, :, 0], g1[:, :, 0], hk1, hv1)
+    a = np.exp(g1[:, :, 0])
+    np.testing.assert_allclose(o, a * hv1[:, :, 0] + (1 - a) * v1[:, :, 0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(hv[:, :, 0], o, rtol=1e-12, atol=1e-12)
