@@ -192,30 +192,18 @@ def run_gla(torch, m, steps, warmup):
     return {"w": w, "x": x, "ms": ms, "kernel_ms": kt}
 
 
-def run_decode(torch, m, steps=256):
-    """Decode steps on the decode workload (B=64, H=4, Dk=128, Dv=256), fp32 state updated in
-    place.  The steps are captured once in a HIP graph and replayed, as a serving loop would run
-    them, so the figure is device time rather than host launch overhead; the graph's result is
-    checked bit for bit against the same steps launched one by one.  The one-by-one rate is
-    reported beside it."""
-    w = W.WORKLOADS["decode"]
-    T = min(steps, w.T)
-    dd = W.decode_inputs(w, T=T)
-    dt = torch.bfloat16
-    qs = torch.from_numpy(dd["q"]).to("cuda", dt)
-    ks = torch.from_numpy(dd["k"]).to("cuda", dt)
-    vs = torch.from_numpy(dd["v"]).to("cuda", dt)
-    gs = torch.from_numpy(dd["g"]).to("cuda", dt)
-    state0 = torch.from_numpy(dd["state"]).to("cuda")
-    state = state0.clone()
-    o = torch.empty(w.B, w.H, w.Dv, device="cuda", dtype=dt)
+def time_decode_chain(torch, run_all, states, T):
+    """Times T decode steps (run_all launches them, updating `states` in place) two ways: launched
+    one by one from Python, and captured once in a HIP graph and replayed, as a serving loop would
+    run them.  The replay's states and outputs must equal the one-by-one launches bit for bit.
+    Returns (us per step replayed, us per step launched one by one)."""
+    init = [t.clone() for t in states]
 
-    def run_all():
-        for t in range(T):
-            m.gla_decode_step(qs[t], ks[t], vs[t], gs[t], state, out=o)
+    def reset():
+        for t, t0 in zip(states, init):
+            t.copy_(t0)
 
-    # one by one (host launch overhead included)
-    run_all()
+    outs = run_all()                                          # warm
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
@@ -223,41 +211,88 @@ def run_decode(torch, m, steps=256):
     e.record()
     torch.cuda.synchronize()
     us_eager = s.elapsed_time(e) * 1e3 / T
-    # reference result of T steps from state0, launched one by one
-    state.copy_(state0)
-    run_all()
+    reset()
+    outs = run_all()
     torch.cuda.synchronize()
-    ref_state, ref_o = state.clone(), o.clone()
-    # the same T steps as one graph
+    ref = [t.clone() for t in list(states) + list(outs)]
     g = torch.cuda.CUDAGraph()
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
         with torch.cuda.graph(g, stream=cap):
-            run_all()
+            outs = run_all()
     torch.cuda.current_stream().wait_stream(cap)
-    state.copy_(state0)
+    reset()
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
-    if not (torch.equal(state, ref_state) and torch.equal(o, ref_o)):
+    if not all(torch.equal(a, b) for a, b in zip(list(states) + list(outs), ref)):
         raise RuntimeError("graph replay of the decode steps differs from launching them one by one")
-    g.replay()                                               # warm
+    g.replay()                                                # warm
     torch.cuda.synchronize()
     s.record()
     g.replay()
     e.record()
     torch.cuda.synchronize()
-    us = s.elapsed_time(e) * 1e3 / T
-    BH = w.B * w.H
-    nbytes = BH * (2 * w.Dk * w.Dv * 4 + 2 * (3 * w.Dk + 2 * w.Dv))   # state in+out, q k g v o
-    return {"workload": f"decode B={w.B} H={w.H} Dk={w.Dk} Dv={w.Dv} fp32 state, {T} steps replayed as one HIP "
-                        "graph (bitwise equal to launching them one by one)",
+    return s.elapsed_time(e) * 1e3 / T, us_eager
+
+
+def decode_line(workload, T, nbytes, us, us_eager, state_mb):
+    return {"workload": f"{workload}, {T} steps replayed as one HIP graph (bitwise equal to launching "
+                        "them one by one)",
             "us_per_step": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
             "frac_hbm": round(nbytes / us / 1e3 / (PEAK_HBM_BYTES / 1e9), 4),
             "us_per_step_launched_one_by_one": round(us_eager, 3),
-            "note": "the 33.6 MB state fits the 256 MB Infinity Cache, so back-to-back steps can "
-                    "exceed what HBM alone would give"}
+            "note": f"the {state_mb:.1f} MB state fits the 256 MB Infinity Cache, so back-to-back steps "
+                    "can exceed what HBM alone would give"}
+
+
+def run_decode(torch, m, steps=256):
+    """GLA decode steps on the decode workload (B=64, H=4, Dk=128, Dv=256), fp32 state updated in
+    place."""
+    w = W.WORKLOADS["decode"]
+    T = min(steps, w.T)
+    dd = W.decode_inputs(w, T=T)
+    dt = torch.bfloat16
+    qs, ks, vs, gs = (torch.from_numpy(dd[n]).to("cuda", dt) for n in ("q", "k", "v", "g"))
+    state = torch.from_numpy(dd["state"]).to("cuda")
+    o = torch.empty(w.B, w.H, w.Dv, device="cuda", dtype=dt)
+
+    def run_all():
+        for t in range(T):
+            m.gla_decode_step(qs[t], ks[t], vs[t], gs[t], state, out=o)
+        return [o]
+
+    us, us_eager = time_decode_chain(torch, run_all, [state], T)
+    BH = w.B * w.H
+    nbytes = BH * (2 * w.Dk * w.Dv * 4 + 2 * (3 * w.Dk + 2 * w.Dv))   # state in+out, q k g v o
+    return decode_line(f"decode B={w.B} H={w.H} Dk={w.Dk} Dv={w.Dv} fp32 state", T, nbytes, us, us_eager,
+                       BH * w.Dk * w.Dv * 4 / 1e6)
+
+
+def run_gsa_decode(torch, m, steps=256):
+    """GSA decode steps on the GSA decode workload (B=64, H=4, Dk=Dv=128, m=64), both fp32 slot
+    memories updated in place."""
+    w = W.WORKLOADS["gsa_decode"]
+    T = min(steps, w.T)
+    dd = W.gsa_decode_inputs(w, T=T)
+    dt = torch.bfloat16
+    qs, ks, vs, gs = (torch.from_numpy(dd[n]).to("cuda", dt) for n in ("q", "k", "v", "g"))
+    hk = torch.from_numpy(dd["hk"]).to("cuda")
+    hv = torch.from_numpy(dd["hv"]).to("cuda")
+    o = torch.empty(w.B, w.H, w.Dv, device="cuda", dtype=dt)
+
+    def run_all():
+        for t in range(T):
+            m.gsa_decode_step(qs[t], ks[t], vs[t], gs[t], hk, hv, out=o)
+        return [o]
+
+    us, us_eager = time_decode_chain(torch, run_all, [hk, hv], T)
+    BH = w.B * w.H
+    state = (w.Dk * w.m + w.m * w.Dv) * 4
+    nbytes = BH * (2 * state + 2 * (2 * w.Dk + w.m + 2 * w.Dv))     # memories in+out, q k g v o
+    return decode_line(f"gsa decode B={w.B} H={w.H} Dk={w.Dk} Dv={w.Dv} m={w.m} fp32 memories", T, nbytes,
+                       us, us_eager, BH * state / 1e6)
 
 
 def run_gsa(torch, m, steps=10, warmup=3):
@@ -447,7 +482,7 @@ def main():
                      "traffic": traffic},
     }
     if not args.no_extras:
-        ex = {"decode": run_decode(torch, m)}
+        ex = {"decode": run_decode(torch, m), "gsa_decode": run_gsa_decode(torch, m)}
         g = run_gsa(torch, m)
         if g is not None:
             ex["gsa"] = g

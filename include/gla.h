@@ -200,6 +200,24 @@ int gsa_bwd(const void* q, const void* k, const void* v, const void* g,
             int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- GSA decode -----------
+ * One recurrent inference step of gated slot attention per (batch, head): the fixed-size
+ * slot memories are updated with the token and read through a softmax over the m slots
+ * (GSA abstract: efficient recurrent inference; research-map summary, "Approach").
+ *   q, k : [B,H,Dk] dtype;  v : [B,H,Dv] dtype;  g : [B,H,m] dtype slot log-gates
+ *   hk   : [B,H,Dk,m] float32 slot keys (transposed), read and overwritten with
+ *          hk Diag(exp g) + k^T (1 - exp g)
+ *   hv   : [B,H,m,Dv] float32 slot values, read and overwritten with
+ *          Diag(exp g) hv + (1 - exp g)^T v
+ *   o    : [B,H,Dv] dtype = softmax(q hk) hv (after the update)
+ * The memories have the layout of gsa_fwd's hkt and hvt, so a prefill by gsa_fwd can be
+ * continued token by token.  Needs no workspace.  Dk up to 256, Dv up to 512 and m up to
+ * 256, multiples of 16.  hk and hv must overlap neither each other nor q, k, v, g; o must
+ * overlap nothing (GLA_ERR_ALIAS). */
+int gsa_decode_step(const void* q, const void* k, const void* v, const void* g,
+                    float* hk, float* hv, void* o,
+                    int B, int H, int Dk, int Dv, int m, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

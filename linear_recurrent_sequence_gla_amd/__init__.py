@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
         -> (dq, dk, dv, dg, dh0)             (saved: what gla_fwd_save left for these inputs)
     gla_decode_step(q, k, v, g, state) -> o                     (state updated in place)
     gsa_fwd(q, k, v, g, C=64, hk0=None, hv0=None, output_final_state=True) -> (o, hkt, hvt)
+    gsa_decode_step(q, k, v, g, hk, hv) -> o                    (hk, hv updated in place)
     gsa_bwd(q, k, v, g, do, C=64, hk0=None, hv0=None, dhkt=None, dhvt=None, want_dh0=False)
         -> (dq, dk, dv, dg, dhk0, dhv0)
 Layouts: q, k, g [B,H,L,Dk]; v, o, do [B,H,L,Dv] (all bf16 or all float32); states float32.
@@ -26,7 +27,7 @@ import torch  # imported first so the library binds to the HIP runtime torch alr
 
 __all__ = [
     "lib", "lib_path", "GlaError", "gla_fwd", "gla_bwd", "gla_fwd_save", "gla_bwd_saved", "gla_decode_step",
-    "gsa_fwd", "gsa_bwd", "gla_saved_bytes", "gla_bwd_saved_workspace_bytes",
+    "gsa_fwd", "gsa_bwd", "gsa_decode_step", "gla_saved_bytes", "gla_bwd_saved_workspace_bytes",
     "gla_fwd_workspace_bytes", "gla_bwd_workspace_bytes", "gsa_fwd_workspace_bytes",
     "gsa_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
 ]
@@ -61,6 +62,7 @@ _SIGS = {
     "gsa_fwd": (_I, [_P] * 9 + [_I] * 8 + [_P, _Z, _P]),
     "gsa_bwd_workspace_bytes": (_Z, [_I] * 8),
     "gsa_bwd": (_I, [_P] * 15 + [_I] * 8 + [_P, _Z, _P]),
+    "gsa_decode_step": (_I, [_P] * 7 + [_I] * 6 + [_P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -288,6 +290,28 @@ def gla_decode_step(q, k, v, g, state, *, out=None):
     _need(o, "out", (B, H, Dv), dt, dev)
     _check(lib().gla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state), _ptr(o),
                                  B, H, Dk, Dv, _DT[dt], _stream(dev)))
+    return o
+
+
+def gsa_decode_step(q, k, v, g, hk, hv, *, out=None):
+    """One GSA recurrent step: with a = exp(g), w = 1 - a per slot, hk <- hk Diag(a) + k^T w and
+    hv <- Diag(a) hv + w^T v (in place); returns o = softmax(q hk) hv.
+    q, k [B,H,Dk]; v [B,H,Dv]; g [B,H,m]; hk [B,H,Dk,m], hv [B,H,m,Dv] float32."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be [B,H,Dk]")
+    if q.dtype not in _DT:
+        raise TypeError("q, k, v, g must be torch.bfloat16 or torch.float32")
+    B, H, Dk = q.shape
+    dev, dt = q.device, q.dtype
+    Dv, m = v.shape[-1], g.shape[-1]
+    for t, n, s in ((q, "q", (B, H, Dk)), (k, "k", (B, H, Dk)), (g, "g", (B, H, m)), (v, "v", (B, H, Dv))):
+        _need(t, n, s, dt, dev)
+    _need(hk, "hk", (B, H, Dk, m), torch.float32, dev)
+    _need(hv, "hv", (B, H, m, Dv), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, H, Dv), dtype=dt, device=dev)
+    _need(o, "out", (B, H, Dv), dt, dev)
+    _check(lib().gsa_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(hk), _ptr(hv), _ptr(o),
+                                 B, H, Dk, Dv, m, _DT[dt], _stream(dev)))
     return o
 
 

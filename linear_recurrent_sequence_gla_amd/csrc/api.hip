@@ -425,6 +425,29 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
+int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, float* hk, float* hv,
+                    void* o, int B, int H, int Dk, int Dv, int m, int dtype, void* stream) {
+  if (dtype != GLA_F32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;
+  if (B < 1 || H < 1 || Dk < 1 || Dv < 1 || m < 1) return GLA_ERR_SHAPE;
+  if (Dk % 16 != 0 || Dk > 256 || Dv % 16 != 0 || Dv > 512 || m % 16 != 0 || m > 256)
+    return GLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !hk || !hv || !o) return GLA_ERR_NULL_ARG;
+  if ((int64_t)B * H > INT32_MAX) return GLA_ERR_UNSUPPORTED;
+  if (!all_aligned({q, k, v, g, hk, hv, o})) return GLA_ERR_UNSUPPORTED;
+  const size_t es = esize_of(dtype), BH = (size_t)B * H;
+  const Range ins[] = {{q, BH * Dk * es}, {k, BH * Dk * es}, {v, BH * Dv * es}, {g, BH * m * es},
+                       {hk, BH * Dk * m * 4}, {hv, BH * m * Dv * 4}};
+  const Range outs[] = {{o, BH * Dv * es}};
+  if (any_alias(outs, 1, ins, 6)) return GLA_ERR_ALIAS;
+  // the two in-place memories overlap neither the token inputs nor each other
+  const Range mem[] = {{hk, BH * Dk * m * 4}, {hv, BH * m * Dv * 4}};
+  if (any_alias(mem, 2, ins, 4)) return GLA_ERR_ALIAS;
+  GsaDecodeParams p{q, k, v, g, hk, hv, o, (int)BH, Dk, Dv, m};
+  hipError_t e = dtype == GLA_BF16 ? launch_gsa_decode<bf16>(p, static_cast<hipStream_t>(stream))
+                                   : launch_gsa_decode<float>(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
 }  // extern "C"
 
 namespace {

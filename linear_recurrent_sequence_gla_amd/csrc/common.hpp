@@ -161,6 +161,11 @@ template <typename T> struct V16;
 template <> struct V16<bf16> { static constexpr int N = 8; typedef bf16x8 type; };
 template <> struct V16<float> { static constexpr int N = 4; typedef f32x4 type; };
 
+// Four consecutive elements of T, for 8- or 16-byte vector accesses.
+template <typename T> struct Vec4;
+template <> struct Vec4<bf16> { typedef bf16x4 type; };
+template <> struct Vec4<float> { typedef f32x4 type; };
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Block-wide max of a non-negative value over NT threads; `red` holds >= NT/64 floats of LDS.

@@ -4,18 +4,15 @@
 // step the whole fp32 state is read and written once, so the kernel is a pure HBM stream:
 // 0.5 flop per byte.  One workgroup per (batch*head, 64 value columns): 16 lanes cover 64
 // contiguous columns with 16-byte accesses (256 bytes per state row) and 16 row groups walk
-// the key rows, eight rows per thread per pass.  The state rows of the first pass are loaded
-// before q, k and the decay go through LDS, so the barrier that publishes them overlaps the
-// state stream; q.S is reduced over the row groups in LDS at the end.  No matrix cores: a
-// rank-1 update plus a vector-matrix product has nothing to contract.
+// the key rows, eight rows per thread per pass.  q, k and the decay are requested first and the
+// state rows of the first pass right after, so the barrier that publishes the token's inputs
+// through LDS waits for those alone and overlaps the state stream; q.S is reduced over the
+// row groups in LDS at the end.  No matrix cores: a rank-1 update plus a vector-matrix product
+// has nothing to contract.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace gla {
-
-template <typename T> struct V4;
-template <> struct V4<bf16> { typedef bf16x4 type; };
-template <> struct V4<float> { typedef f32x4 type; };
 
 template <typename T>
 __global__ __launch_bounds__(256) void gla_decode_kernel(DecodeParams p, int ntile) {
@@ -30,16 +27,22 @@ __global__ __launch_bounds__(256) void gla_decode_kernel(DecodeParams p, int nti
   const int jc = min(j, Dv - 4);               // in-bounds column for lanes past Dv
   float* S = p.state + (size_t)bh * Dk * Dv + jc;
 
+  // the token's inputs are requested first (clamped, unconditionally): loads complete in issue
+  // order, so the wait before the barrier that publishes them does not cover the state rows
+  const size_t ot = (size_t)bh * Dk + min(tid, Dk - 1);
+  const T qt = reinterpret_cast<const T*>(p.q)[ot];
+  const T kt = reinterpret_cast<const T*>(p.k)[ot];
+  const T gt = reinterpret_cast<const T*>(p.g)[ot];
+  const typename Vec4<T>::type vr =
+      *reinterpret_cast<const typename Vec4<T>::type*>(reinterpret_cast<const T*>(p.v) + (size_t)bh * Dv + jc);
+  __builtin_amdgcn_sched_barrier(0);
   f32x4 s[RPP];
 #pragma unroll
   for (int m = 0; m < RPP; ++m) s[m] = *reinterpret_cast<const f32x4*>(S + (size_t)min(ty + 16 * m, Dk - 1) * Dv);
-  const typename V4<T>::type vr =
-      *reinterpret_cast<const typename V4<T>::type*>(reinterpret_cast<const T*>(p.v) + (size_t)bh * Dv + jc);
   if (tid < Dk) {
-    const size_t o = (size_t)bh * Dk + tid;
-    sq[tid] = to_f32(reinterpret_cast<const T*>(p.q)[o]);
-    sk[tid] = to_f32(reinterpret_cast<const T*>(p.k)[o]);
-    sa[tid] = fast_exp2(to_f32(reinterpret_cast<const T*>(p.g)[o]) * kLog2e);
+    sq[tid] = to_f32(qt);
+    sk[tid] = to_f32(kt);
+    sa[tid] = fast_exp2(to_f32(gt) * kLog2e);
   }
   __syncthreads();
 

@@ -95,6 +95,15 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s);
 template <typename T>
 hipError_t launch_gla_decode(const DecodeParams& p, hipStream_t s);
 
+struct GsaDecodeParams {
+  const void *q, *k, *v, *g;
+  float *hk, *hv;                 // [BH][Dk][m], [BH][m][Dv], updated in place
+  void* o;
+  int BH, Dk, Dv, m;
+};
+template <typename T>
+hipError_t launch_gsa_decode(const GsaDecodeParams& p, hipStream_t s);
+
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 
 template <typename T, int MP, int CP>

@@ -140,6 +140,28 @@ def test_decode_validation(lib):
     assert lib.gla_decode_step(*p, 1, 1, 16, 16, 1, None) == 6
 
 
+def test_gsa_decode_validation(lib):
+    N = [None] * 7
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 16, 7, None) == 3            # dtype
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 0, 1, None) == 2             # m < 1
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 16, 1, None) == 1            # null pointers
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 20, 1, None) == 4            # m not a multiple of 16
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 272, 1, None) == 4           # m > 256
+    assert lib.gsa_decode_step(*N, 1, 1, 272, 16, 16, 1, None) == 4           # Dk > 256
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 528, 16, 1, None) == 4          # Dv > 512
+    p = [ctypes.c_void_p(0x10000000 + i * 0x1000000) for i in range(7)]
+    assert lib.gsa_decode_step(*p[:6], ctypes.c_void_p(0x10000000 + 2), 1, 1, 16, 16, 16, 1, None) == 4  # misaligned
+    q = list(p)
+    q[6] = ctypes.c_void_p(0x10000000 + 16)                                  # o overlaps q
+    assert lib.gsa_decode_step(*q, 1, 1, 16, 16, 16, 1, None) == 6
+    q = list(p)
+    q[5] = ctypes.c_void_p(0x10000000 + 0x4000000 + 512)                     # hv overlaps hk
+    assert lib.gsa_decode_step(*q, 1, 1, 16, 16, 16, 1, None) == 6
+    q = list(p)
+    q[4] = ctypes.c_void_p(0x10000000 + 0x2000000)                           # hk is v
+    assert lib.gsa_decode_step(*q, 1, 1, 16, 16, 16, 1, None) == 6
+
+
 def test_profiled_needs_events(lib):
     assert lib.gla_fwd_profiled(*NOP, 1, 1, 64, 16, 16, 16, 1, None, 0, None, None, 0) == 1
 

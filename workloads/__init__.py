@@ -28,7 +28,7 @@ import numpy as np
 
 __all__ = [
     "round_bf16", "logsigmoid", "GlaWorkload", "GsaWorkload", "DecodeWorkload",
-    "gla_inputs", "gsa_inputs", "decode_inputs", "WORKLOADS",
+    "GsaDecodeWorkload", "gla_inputs", "gsa_inputs", "decode_inputs", "gsa_decode_inputs", "WORKLOADS",
 ]
 
 
@@ -95,6 +95,19 @@ class DecodeWorkload:
     bias_frac: float = 0.1
 
 
+@dataclasses.dataclass(frozen=True)
+class GsaDecodeWorkload:
+    name: str
+    T: int      # number of single-token steps
+    B: int
+    H: int
+    Dk: int
+    Dv: int
+    m: int
+    dtype: str
+    seed: int
+
+
 # The workloads named by the measurement plan (sizes from the pages' model shapes: the 340M
 # and 1.3B GLA layers, a 20K-token sequence, and GSA with 64 slots).
 WORKLOADS = {
@@ -104,6 +117,8 @@ WORKLOADS = {
     "gla_long": GlaWorkload("gla_long", 1, 4, 20480, 128, 256, 64, "bf16", 1004, bias_frac=0.1),
     "decode": DecodeWorkload("decode", 1024, 64, 4, 128, 256, "bf16", 1004),
     "gsa_340m": GsaWorkload("gsa_340m", 8, 4, 2048, 128, 128, 64, 64, "bf16", 1005),
+    # GSA recurrent inference at the GSA layer's dimensions with the decode batch
+    "gsa_decode": GsaDecodeWorkload("gsa_decode", 1024, 64, 4, 128, 128, 64, "bf16", 1006),
 }
 
 
@@ -220,3 +235,21 @@ def decode_inputs(w: DecodeWorkload, *, T: Optional[int] = None, B: Optional[int
     state = rng.standard_normal((B, H, Dk, Dv), dtype=np.float32) * np.float32(0.02)
     return {"q": _cast(q, w.dtype), "k": _cast(k, w.dtype), "v": _cast(v, w.dtype),
             "g": _cast(g, w.dtype), "state": state}
+
+
+def gsa_decode_inputs(w: GsaDecodeWorkload, *, T: Optional[int] = None, B: Optional[int] = None) -> dict:
+    """Pre-generated single-token GSA stream: q, k [T,B,H,Dk], v [T,B,H,Dv], g [T,B,H,m] slot
+    log-gates (the GSA law, logsigmoid(N(0, 1)) / 16); slot memories hk [B,H,Dk,m] and
+    hv [B,H,m,Dv] float32 ~ N(0, 0.02**2)."""
+    T = w.T if T is None else T
+    B = w.B if B is None else B
+    H, Dk, Dv, m = w.H, w.Dk, w.Dv, w.m
+    rng = np.random.Generator(np.random.PCG64(w.seed + 100))
+    q = rng.standard_normal((T, B, H, Dk), dtype=np.float32) * np.float32(Dk ** -0.5)
+    k = rng.standard_normal((T, B, H, Dk), dtype=np.float32)
+    v = rng.standard_normal((T, B, H, Dv), dtype=np.float32)
+    g = logsigmoid(rng.standard_normal((T, B, H, m), dtype=np.float32)) / np.float32(16.0)
+    hk = rng.standard_normal((B, H, Dk, m), dtype=np.float32) * np.float32(0.02)
+    hv = rng.standard_normal((B, H, m, Dv), dtype=np.float32) * np.float32(0.02)
+    return {"q": _cast(q, w.dtype), "k": _cast(k, w.dtype), "v": _cast(v, w.dtype),
+            "g": _cast(g, w.dtype), "hk": hk, "hv": hv}
