@@ -8,11 +8,13 @@
 //   z = q hk,  p = softmax(z) over the m slots,  o = p hv
 // Both fp32 memories are read and written once per step: an HBM stream at about 0.5 flop per
 // byte, like the GLA decode step, with nothing to contract on matrix cores.  The softmax
-// couples every slot, so one workgroup holds one (batch, head): 256 threads tile hk as
-// (row group, 4 slots) and hv as (row group, 4 columns), with 16-byte accesses.  The first
-// rows of both memories are requested before anything else; hv is updated and written back
-// before the softmax, since its update does not need p; z and o are reduced over the row
-// groups in LDS.  The softmax subtracts the maximum and normalises o once at the end.
+// couples every slot, so one workgroup holds one (batch, head), with 16-byte accesses: each
+// wave owns whole rows of hk and whole columns of hv.  The first rows of both memories are
+// requested before anything else; hv is updated and written back before the softmax, since
+// its update does not need p.  z is folded over a wave's rows by shuffles and over the waves
+// through LDS (one barrier); every wave then forms the softmax for itself, so o is folded
+// over rows by shuffles with no further barrier.  The softmax subtracts the maximum and
+// normalises o once at the end.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,22 +23,28 @@ namespace gla {
 constexpr int kGsaDecThreads = 256;
 constexpr int kGsaDecRows = 8;                 // rows per thread per pass, for each memory
 
+__device__ __forceinline__ int pow2_ceil(int x) { return x <= 1 ? 1 : 1 << (32 - __builtin_clz(x - 1)); }
+
 template <typename T>
 __global__ __launch_bounds__(kGsaDecThreads) void gsa_decode_kernel(GsaDecodeParams p) {
   constexpr int NT = kGsaDecThreads, R = kGsaDecRows, NW = NT / 64;
-  __shared__ float sq[256], sk[256], sa[256], sw[256], sp[256];
-  __shared__ float sred[4 * NT];               // partial sums of z or o: [row group][column]
-  __shared__ float swave[2 * NW];
+  __shared__ float sq[256], sk[256], sa[256], sw[256];
+  __shared__ float szp[NW][256];               // per-wave partial z
+  __shared__ float sp[NW][256];                // per-wave copy of exp(z - max)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, bh = blockIdx.x;
   const int Dk = p.Dk, Dv = p.Dv, m = p.m;
-  // hk: NSG groups of 4 slots x NRK row groups; lanes past NSG * NRK load but never store
-  const int NSG = m >> 2, NRK = NT / NSG;
-  const int sg = tid % NSG, rk = min(tid / NSG, NRK - 1);
-  const bool kact = tid < NSG * NRK;
-  // hv: NCG groups of 4 columns x NRV row groups
-  const int NCG = Dv >> 2, NRV = NT / NCG;
-  const int cg = tid % NCG, rv = min(tid / NCG, NRV - 1);
-  const bool vact = tid < NCG * NRV;
+  // hk: whole rows per wave.  NSGP (a power of two) lanes span the m/4 slot groups of a row, so
+  // a wave's row groups differ in the high lane bits and z folds over them by shuffles.
+  const int NSG = m >> 2, NSGP = pow2_ceil(NSG), NRK = NT / NSGP;
+  const int sgl = tid & (NSGP - 1), rk = tid / NSGP;
+  const bool kact = sgl < NSG;
+  const int sg = min(sgl, NSG - 1);
+  // hv: whole columns per wave.  CGW groups of 4 columns per wave (Dv/16 with four waves),
+  // padded to CGWP lanes; o folds over the wave's RVW row groups by shuffles.
+  const int CGW = (Dv >> 2) / NW, CGWP = pow2_ceil(CGW), RVW = 64 / CGWP;
+  const int cgl = lane & (CGWP - 1), rv = lane / CGWP;
+  const bool vact = cgl < CGW;
+  const int cg = wave * CGW + min(cgl, CGW - 1);
 
   // the token's inputs are requested first (from clamped addresses, unconditionally): loads
   // complete in issue order, so their wait then does not cover the memories' rows
@@ -52,7 +60,7 @@ __global__ __launch_bounds__(kGsaDecThreads) void gsa_decode_kernel(GsaDecodePar
 #pragma unroll
   for (int u = 0; u < R; ++u) hk[u] = *reinterpret_cast<const f32x4*>(HK + (size_t)min(rk + NRK * u, Dk - 1) * m);
 #pragma unroll
-  for (int u = 0; u < R; ++u) hv[u] = *reinterpret_cast<const f32x4*>(HV + (size_t)min(rv + NRV * u, m - 1) * Dv);
+  for (int u = 0; u < R; ++u) hv[u] = *reinterpret_cast<const f32x4*>(HV + (size_t)min(rv + RVW * u, m - 1) * Dv);
   if (tid < Dk) sq[tid] = to_f32(qt), sk[tid] = to_f32(kt);
   if (tid < m) {
     const float g = to_f32(gt);
@@ -92,7 +100,7 @@ __global__ __launch_bounds__(kGsaDecThreads) void gsa_decode_kernel(GsaDecodePar
   for (int e = 0; e < 4; ++e) vv[e] = to_f32(vt[e]);
 #pragma unroll
   for (int u = 0; u < R; ++u) {
-    const int s = rv + NRV * u;
+    const int s = rv + RVW * u;
     if (s < m) {
       const float a = sa[s], w = sw[s];
 #pragma unroll
@@ -100,57 +108,70 @@ __global__ __launch_bounds__(kGsaDecThreads) void gsa_decode_kernel(GsaDecodePar
       if (vact) *reinterpret_cast<f32x4*>(HV + (size_t)s * Dv) = hv[u];
     }
   }
-  if (kact) {
+  // z over the wave's rows, then over the waves through LDS
+  for (int off = NSGP; off < 64; off <<= 1) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sred[rk * m + 4 * sg + e] = zacc[e];
+    for (int e = 0; e < 4; ++e) zacc[e] += __shfl_xor(zacc[e], off, 64);
+  }
+  if (lane < NSGP && kact) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) szp[wave][4 * sg + e] = zacc[e];
   }
   __syncthreads();
 
-  // softmax over the m slots: thread s < m owns z_s
-  float z = -INFINITY;
-  if (tid < m) {
-    z = 0.f;
-    for (int r = 0; r < NRK; ++r) z += sred[r * m + tid];
+  // softmax over the m slots, computed by every wave for itself: lane holds slots lane + 64 j
+  float z[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int s = lane + 64 * j;
+    z[j] = -INFINITY;
+    if (s < m) {
+      z[j] = szp[0][s];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) z[j] += szp[w][s];
+    }
+    mx = fmaxf(mx, z[j]);
   }
-  float mx = z;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if (lane == 0) swave[wave] = mx;
-  __syncthreads();
-  mx = swave[0];
+  float sum = 0.f;
 #pragma unroll
-  for (int w = 1; w < NW; ++w) mx = fmaxf(mx, swave[w]);
-  const float ez = tid < m ? expf(z - mx) : 0.f;
-  if (tid < m) sp[tid] = ez;
-  float sum = ez;
+  for (int j = 0; j < 4; ++j) {
+    const int s = lane + 64 * j;
+    if (s < m) {
+      const float ez = expf(z[j] - mx);
+      sp[wave][s] = ez;
+      sum += ez;
+    }
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  if (lane == 0) swave[NW + wave] = sum;
-  __syncthreads();
-  sum = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) sum += swave[NW + w];
+  // the wave's own copy of p is read by other lanes of the same wave
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // o = (sum_s e_s hv[s, :]) / sum_s e_s
+  // o = (sum_s e_s hv[s, :]) / sum_s e_s over the wave's columns
   f32x4 oacc = zero4();
 #pragma unroll
   for (int u = 0; u < R; ++u) {
-    const int s = rv + NRV * u;
+    const int s = rv + RVW * u;
     if (s < m) {
-      const float ps = sp[s];
+      const float ps = sp[wave][s];
 #pragma unroll
       for (int e = 0; e < 4; ++e) oacc[e] += ps * hv[u][e];
     }
   }
-  for (int base = NRV * R; base < m; base += NRV * R) {
+  for (int base = RVW * R; base < m; base += RVW * R) {
 #pragma unroll
     for (int u = 0; u < R; ++u)
-      hv[u] = *reinterpret_cast<const f32x4*>(HV + (size_t)min(base + rv + NRV * u, m - 1) * Dv);
+      hv[u] = *reinterpret_cast<const f32x4*>(HV + (size_t)min(base + rv + RVW * u, m - 1) * Dv);
 #pragma unroll
     for (int u = 0; u < R; ++u) {
-      const int s = base + rv + NRV * u;
+      const int s = base + rv + RVW * u;
       if (s < m) {
-        const float a = sa[s], w = sw[s], ps = sp[s];
+        const float a = sa[s], w = sw[s], ps = sp[wave][s];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           hv[u][e] = a * hv[u][e] + w * vv[e];
@@ -160,21 +181,16 @@ __global__ __launch_bounds__(kGsaDecThreads) void gsa_decode_kernel(GsaDecodePar
       }
     }
   }
-  // sred's z partials were all read before the last barrier
-  if (vact) {
+  for (int off = CGWP; off < 64; off <<= 1) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sred[rv * Dv + 4 * cg + e] = oacc[e];
+    for (int e = 0; e < 4; ++e) oacc[e] += __shfl_xor(oacc[e], off, 64);
   }
-  __syncthreads();
-  if (tid < Dv) {
-    float o = 0.f;
-    for (int r = 0; r < NRV; ++r) o += sred[r * Dv + tid];
-    reinterpret_cast<T*>(p.o)[(size_t)bh * Dv + tid] = from_f32<T>(o / sum);
-  }
-  for (int j = tid + NT; j < Dv; j += NT) {
-    float o = 0.f;
-    for (int r = 0; r < NRV; ++r) o += sred[r * Dv + j];
-    reinterpret_cast<T*>(p.o)[(size_t)bh * Dv + j] = from_f32<T>(o / sum);
+  if (lane < CGWP && vact) {
+    const float inv = 1.f / sum;
+    typename Vec4<T>::type ov;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ov[e] = from_f32<T>(oacc[e] * inv);
+    *reinterpret_cast<typename Vec4<T>::type*>(reinterpret_cast<T*>(p.o) + (size_t)bh * Dv + 4 * cg) = ov;
   }
 }
 
