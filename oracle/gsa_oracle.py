@@ -15,6 +15,12 @@ two passes, so that a two-pass implementation is checked against a different for
     Vmem_t = Diag(alpha_t) Vmem_{t-1} + w_t^T v_t               (Vmem in R^{m x Dv})
     z_t = Kmem_t q_t^T,  p_t = softmax(z_t),  o_t = p_t Vmem_t
 
+The read-out nonlinearity between the two memories is softmax by default.  The GSA summary's
+ablations ("Measured effects": replacing the softmax) also run Swish, ReLU and ReLU^2 in its
+place, or none; those variants are read as the function applied to each slot score alone,
+with no normalisation over the slots (act = "swish": z * sigmoid(z); "relu": max(z, 0);
+"relu2": max(z, 0)^2; "none": z).
+
 Readings taken where the pages are silent: the slot write weight is the complement of the
 forget gate (w = 1 - alpha), the same weights write keys and values; softmax temperature is 1
 (max-subtracted, which is the same function); initial memories default to zero.  The states
@@ -25,7 +31,9 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["gsa_recurrent_fwd", "gsa_recurrent_bwd", "gsa_decode_step"]
+__all__ = ["gsa_recurrent_fwd", "gsa_recurrent_bwd", "gsa_decode_step", "ACTS"]
+
+ACTS = ("softmax", "swish", "relu", "relu2", "none")
 
 
 def _f64(x):
@@ -36,6 +44,41 @@ def _softmax(z):
     z = z - np.max(z, axis=-1, keepdims=True)
     e = np.exp(z)
     return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def _sigmoid(z):
+    return 0.5 * (1.0 + np.tanh(0.5 * z))
+
+
+def _read(z, act):
+    """Slot weights p from slot scores z (last axis = slots)."""
+    if act == "softmax":
+        return _softmax(z)
+    if act == "swish":
+        return z * _sigmoid(z)
+    if act == "relu":
+        return np.maximum(z, 0.0)
+    if act == "relu2":
+        return np.maximum(z, 0.0) ** 2
+    if act == "none":
+        return z.copy()
+    raise ValueError(f"unknown read-out {act!r}")
+
+
+def _read_bwd(z, p, dp, act):
+    """dLoss/dz from dLoss/dp through the read-out."""
+    if act == "softmax":
+        return p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
+    if act == "swish":
+        sg = _sigmoid(z)
+        return dp * sg * (1.0 + z * (1.0 - sg))
+    if act == "relu":
+        return dp * (z > 0)
+    if act == "relu2":
+        return dp * 2.0 * np.maximum(z, 0.0)
+    if act == "none":
+        return dp.copy()
+    raise ValueError(f"unknown read-out {act!r}")
 
 
 def _init(hk0, hv0, B, H, Dk, Dv, m):
@@ -52,7 +95,7 @@ def _step(Km, Vm, k_t, v_t, g_t):
     return Km, Vm
 
 
-def gsa_recurrent_fwd(q, k, v, g, hk0=None, hv0=None):
+def gsa_recurrent_fwd(q, k, v, g, hk0=None, hv0=None, act="softmax"):
     """Returns (o [B,H,L,Dv], hkt [B,H,Dk,m], hvt [B,H,m,Dv]) in float64."""
     q, k, v, g, hk0, hv0 = map(_f64, (q, k, v, g, hk0, hv0))
     B, H, L, Dk = q.shape
@@ -61,18 +104,19 @@ def gsa_recurrent_fwd(q, k, v, g, hk0=None, hv0=None):
     o = np.empty((B, H, L, Dv))
     for t in range(L):
         Km, Vm = _step(Km, Vm, k[:, :, t], v[:, :, t], g[:, :, t])
-        p = _softmax((Km @ q[:, :, t, :, None])[..., 0])                 # [B,H,m]
+        p = _read((Km @ q[:, :, t, :, None])[..., 0], act)               # [B,H,m]
         o[:, :, t] = (p[:, :, None, :] @ Vm)[:, :, 0, :]
     return o, np.swapaxes(Km, -1, -2), Vm
 
 
 def gsa_recurrent_bwd(q, k, v, g, do, hk0=None, hv0=None, dhkt=None, dhvt=None,
-                      checkpoint: int = 64):
+                      checkpoint: int = 64, act="softmax"):
     """Reverse-mode gradient of sum(o*do) + sum(hkt*dhkt) + sum(hvt*dhvt).
 
     Walks tokens from last to first carrying dK = dLoss/dKmem_t and dV = dLoss/dVmem_t.
     At token t (memories after the write: Km, Vm; before it: Km', Vm'):
-        dV  += p_t^T do_t;   dp = Vm do_t^T;   dz = p * (dp - <dp, p>)   (softmax backward)
+        dV  += p_t^T do_t;   dp = Vm do_t^T;   dz = p * (dp - <dp, p>)   (softmax backward;
+                                                  the other read-outs: dz = f'(z) dp)
         dK  += dz^T q_t;     dq_t = dz Km
         dk_t = w_t dK;       dv_t = w_t dV
         dw   = rowsum(dK * k_t) + rowsum(dV * v_t)
@@ -104,10 +148,11 @@ def gsa_recurrent_bwd(q, k, v, g, do, hk0=None, hv0=None, dhkt=None, dhvt=None,
         for t in range(t1 - 1, t0 - 1, -1):
             (Kb, Vb), (Ka, Va) = seg[t - t0], seg[t - t0 + 1]
             a = np.exp(g[:, :, t]); w = -np.expm1(g[:, :, t])
-            p = _softmax((Ka @ q[:, :, t, :, None])[..., 0])
+            z = (Ka @ q[:, :, t, :, None])[..., 0]
+            p = _read(z, act)
             dV = dV + p[..., None] * do[:, :, t, None, :]
             dp = (Va @ do[:, :, t, :, None])[..., 0]
-            dz = p * (dp - np.sum(dp * p, axis=-1, keepdims=True))
+            dz = _read_bwd(z, p, dp, act)
             dK = dK + dz[..., None] * q[:, :, t, None, :]
             dq[:, :, t] = (dz[:, :, None, :] @ Ka)[:, :, 0, :]
             dk[:, :, t] = (w[:, :, None, :] @ dK)[:, :, 0, :]
@@ -121,7 +166,7 @@ def gsa_recurrent_bwd(q, k, v, g, do, hk0=None, hv0=None, dhkt=None, dhvt=None,
             "dhk0": np.swapaxes(dK, -1, -2), "dhv0": dV}
 
 
-def gsa_decode_step(q, k, v, g, hk, hv):
+def gsa_decode_step(q, k, v, g, hk, hv, act="softmax"):
     """One recurrent inference step of GSA on a single token per (batch, head): the bounded
     slot memories make inference O(1) in memory per token (GSA abstract: efficient recurrent
     inference with a compact state; research-map summary, "Approach").
@@ -130,7 +175,7 @@ def gsa_decode_step(q, k, v, g, hk, hv):
     hv [B,H,m,Dv] (= Vmem).  Written slot by slot from the slot-memory definition:
         for each slot s:  Kmem[s] <- alpha_s Kmem[s] + w_s k,   Vmem[s] <- alpha_s Vmem[s] + w_s v,
                           z_s = <Kmem[s], q>
-        p = softmax(z),  o = sum_s p_s Vmem[s].
+        p = softmax(z) (or the read-out act),  o = sum_s p_s Vmem[s].
     Returns (o [B,H,Dv], hk_new [B,H,Dk,m], hv_new [B,H,m,Dv]), float64.
     """
     q, k, v, g, hk, hv = map(_f64, (q, k, v, g, hk, hv))
@@ -144,6 +189,6 @@ def gsa_decode_step(q, k, v, g, hk, hv):
         hk[..., :, s] = a * hk[..., :, s] + w * k
         hv[..., s, :] = a * hv[..., s, :] + w * v
         z[..., s] = np.sum(hk[..., :, s] * q, axis=-1)
-    p = _softmax(z)
+    p = _read(z, act)
     o = np.einsum("bhs,bhsd->bhd", p, hv)
     return o, hk, hv
