@@ -15,7 +15,7 @@
  *         Modeling": abstract, and research-map summary "Approach"): m slots with per-slot
  *         forget gates alpha_t = exp(g_t), write weights w_t = 1 - alpha_t;
  *         pass 1 (slot keys):   S1_t = S1_{t-1} Diag(alpha_t) + k_t^T w_t,  z_t = q_t S1_t
- *         p_t = softmax(z_t) over the m slots
+ *         p_t = softmax(z_t) over the m slots (or an element-wise read-out, gsa_act)
  *         pass 2 (slot values): S2_t = Diag(alpha_t) S2_{t-1} + w_t^T v_t,  o_t = p_t S2_t
  *
  * Conventions shared by every entry point
@@ -68,6 +68,19 @@ typedef enum {
 } gla_status;
 
 typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
+
+/* Read-out between GSA's two passes (argument `act` of the gsa_* entry points).  Softmax over
+ * the slots is GSA's own; the GSA summary's ablations ("Measured effects") replace it with
+ * Swish, ReLU or ReLU^2, or drop it.  The replacements act on each slot score z alone, with
+ * no normalisation over the slots:  SWISH p = z sigmoid(z);  RELU p = max(z, 0);
+ * RELU2 p = max(z, 0)^2;  NONE p = z.  Other values give GLA_ERR_UNSUPPORTED. */
+typedef enum {
+  GSA_ACT_SOFTMAX = 0,
+  GSA_ACT_SWISH = 1,
+  GSA_ACT_RELU = 2,
+  GSA_ACT_RELU2 = 3,
+  GSA_ACT_NONE = 4
+} gsa_act;
 
 /* Version of this ABI (incremented on any incompatible change). */
 int gla_abi_version(void);
@@ -175,7 +188,7 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g,
 
 /* ---------------------------------------------------------------- GSA forward ----------
  * Supported: C in {16, 32, 64}; m a multiple of 16 up to 64; Dk a multiple of 16 up to 256;
- * Dv a multiple of 16 up to 512 (others: GLA_ERR_UNSUPPORTED).
+ * Dv a multiple of 16 up to 512 (others: GLA_ERR_UNSUPPORTED).  act: a gsa_act value.
  *   q, k : [B,H,L,Dk] dtype;  v : [B,H,L,Dv] dtype;  g : [B,H,L,m] dtype slot log-gates
  *   hk0  : [B,H,Dk,m] float32 initial pass-1 state or NULL;  hv0 : [B,H,m,Dv] or NULL
  *   o    : [B,H,L,Dv] dtype
@@ -184,7 +197,7 @@ size_t gsa_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C
 int gsa_fwd(const void* q, const void* k, const void* v, const void* g,
             const float* hk0, const float* hv0,
             void* o, float* hkt, float* hvt,
-            int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
+            int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, int act,
             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- GSA backward ---------
@@ -197,7 +210,7 @@ int gsa_bwd(const void* q, const void* k, const void* v, const void* g,
             const float* hk0, const float* hv0,
             const void* do_, const float* dhkt, const float* dhvt,
             void* dq, void* dk, void* dv, float* dg, float* dhk0, float* dhv0,
-            int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
+            int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, int act,
             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------- GSA decode -----------
@@ -209,14 +222,15 @@ int gsa_bwd(const void* q, const void* k, const void* v, const void* g,
  *          hk Diag(exp g) + k^T (1 - exp g)
  *   hv   : [B,H,m,Dv] float32 slot values, read and overwritten with
  *          Diag(exp g) hv + (1 - exp g)^T v
- *   o    : [B,H,Dv] dtype = softmax(q hk) hv (after the update)
+ *   o    : [B,H,Dv] dtype = softmax(q hk) hv (after the update), or f(q hk) hv for the
+ *          element-wise read-outs (act: a gsa_act value)
  * The memories have the layout of gsa_fwd's hkt and hvt, so a prefill by gsa_fwd can be
  * continued token by token.  Needs no workspace.  Dk up to 256, Dv up to 512 and m up to
  * 256, multiples of 16.  hk and hv must overlap neither each other nor q, k, v, g; o must
  * overlap nothing (GLA_ERR_ALIAS). */
 int gsa_decode_step(const void* q, const void* k, const void* v, const void* g,
                     float* hk, float* hv, void* o,
-                    int B, int H, int Dk, int Dv, int m, int dtype, void* stream);
+                    int B, int H, int Dk, int Dv, int m, int dtype, int act, void* stream);
 
 #ifdef __cplusplus
 }

@@ -11,10 +11,12 @@ Entry points (same names as the C ABI):
     gla_bwd_saved(q, k, v, g, do, saved, C=64, h0=None, dht=None, want_dh0=False)
         -> (dq, dk, dv, dg, dh0)             (saved: what gla_fwd_save left for these inputs)
     gla_decode_step(q, k, v, g, state) -> o                     (state updated in place)
-    gsa_fwd(q, k, v, g, C=64, hk0=None, hv0=None, output_final_state=True) -> (o, hkt, hvt)
-    gsa_decode_step(q, k, v, g, hk, hv) -> o                    (hk, hv updated in place)
-    gsa_bwd(q, k, v, g, do, C=64, hk0=None, hv0=None, dhkt=None, dhvt=None, want_dh0=False)
-        -> (dq, dk, dv, dg, dhk0, dhv0)
+    gsa_fwd(q, k, v, g, C=64, hk0=None, hv0=None, output_final_state=True, act="softmax")
+        -> (o, hkt, hvt)
+    gsa_decode_step(q, k, v, g, hk, hv, act="softmax") -> o     (hk, hv updated in place)
+    gsa_bwd(q, k, v, g, do, C=64, hk0=None, hv0=None, dhkt=None, dhvt=None, want_dh0=False,
+            act="softmax") -> (dq, dk, dv, dg, dhk0, dhv0)
+    (act: the read-out between GSA's passes, one of GSA_ACTS)
 Layouts: q, k, g [B,H,L,Dk]; v, o, do [B,H,L,Dv] (all bf16 or all float32); states float32.
 """
 from __future__ import annotations
@@ -29,7 +31,7 @@ __all__ = [
     "lib", "lib_path", "GlaError", "gla_fwd", "gla_bwd", "gla_fwd_save", "gla_bwd_saved", "gla_decode_step",
     "gsa_fwd", "gsa_bwd", "gsa_decode_step", "gla_saved_bytes", "gla_bwd_saved_workspace_bytes",
     "gla_fwd_workspace_bytes", "gla_bwd_workspace_bytes", "gsa_fwd_workspace_bytes",
-    "gsa_bwd_workspace_bytes", "EXPORTED_SYMBOLS",
+    "gsa_bwd_workspace_bytes", "EXPORTED_SYMBOLS", "GSA_ACTS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +39,14 @@ lib_path = os.path.join(_HERE, "libgla_amd.so")
 
 GLA_F32, GLA_BF16 = 0, 1
 _DT = {torch.float32: GLA_F32, torch.bfloat16: GLA_BF16}
+# read-outs between GSA's two passes, in the order of gla.h's gsa_act values
+GSA_ACTS = ("softmax", "swish", "relu", "relu2", "none")
+
+
+def _act(act: str) -> int:
+    if act not in GSA_ACTS:
+        raise ValueError(f"act must be one of {GSA_ACTS}, not {act!r}")
+    return GSA_ACTS.index(act)
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -59,10 +69,10 @@ _SIGS = {
     "gla_bwd_saved": (_I, [_P] * 12 + [_I] * 7 + [_P, _Z, _P, _Z, _P, _P, _I]),
     "gla_decode_step": (_I, [_P] * 6 + [_I] * 5 + [_P]),
     "gsa_fwd_workspace_bytes": (_Z, [_I] * 8),
-    "gsa_fwd": (_I, [_P] * 9 + [_I] * 8 + [_P, _Z, _P]),
+    "gsa_fwd": (_I, [_P] * 9 + [_I] * 9 + [_P, _Z, _P]),
     "gsa_bwd_workspace_bytes": (_Z, [_I] * 8),
-    "gsa_bwd": (_I, [_P] * 15 + [_I] * 8 + [_P, _Z, _P]),
-    "gsa_decode_step": (_I, [_P] * 7 + [_I] * 6 + [_P]),
+    "gsa_bwd": (_I, [_P] * 15 + [_I] * 9 + [_P, _Z, _P]),
+    "gsa_decode_step": (_I, [_P] * 7 + [_I] * 7 + [_P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -293,9 +303,9 @@ def gla_decode_step(q, k, v, g, state, *, out=None):
     return o
 
 
-def gsa_decode_step(q, k, v, g, hk, hv, *, out=None):
+def gsa_decode_step(q, k, v, g, hk, hv, *, act: str = "softmax", out=None):
     """One GSA recurrent step: with a = exp(g), w = 1 - a per slot, hk <- hk Diag(a) + k^T w and
-    hv <- Diag(a) hv + w^T v (in place); returns o = softmax(q hk) hv.
+    hv <- Diag(a) hv + w^T v (in place); returns o = softmax(q hk) hv (or f(q hk) hv).
     q, k [B,H,Dk]; v [B,H,Dv]; g [B,H,m]; hk [B,H,Dk,m], hv [B,H,m,Dv] float32."""
     if not isinstance(q, torch.Tensor) or q.dim() != 3:
         raise ValueError("q must be [B,H,Dk]")
@@ -311,12 +321,12 @@ def gsa_decode_step(q, k, v, g, hk, hv, *, out=None):
     o = out if out is not None else torch.empty((B, H, Dv), dtype=dt, device=dev)
     _need(o, "out", (B, H, Dv), dt, dev)
     _check(lib().gsa_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(hk), _ptr(hv), _ptr(o),
-                                 B, H, Dk, Dv, m, _DT[dt], _stream(dev)))
+                                 B, H, Dk, Dv, m, _DT[dt], _act(act), _stream(dev)))
     return o
 
 
 def gsa_fwd(q, k, v, g, C: int = 64, hk0=None, hv0=None, output_final_state: bool = True, *,
-            workspace=None, out=None):
+            act: str = "softmax", workspace=None, out=None):
     """Gated slot attention forward; g [B,H,L,m].  Returns (o, hkt, hvt)."""
     B, H, L, Dk, Dv, dev, dt = _common(q, k, v, g, gate_width=True)
     m = g.shape[-1]
@@ -332,15 +342,15 @@ def gsa_fwd(q, k, v, g, C: int = 64, hk0=None, hv0=None, output_final_state: boo
     L_ = lib()
     nbytes = L_.gsa_fwd_workspace_bytes(B, H, L, Dk, Dv, m, C, _DT[dt])
     if nbytes == 0:
-        _check(L_.gsa_fwd(*([None] * 9), B, H, L, Dk, Dv, m, C, _DT[dt], None, 0, None))
+        _check(L_.gsa_fwd(*([None] * 9), B, H, L, Dk, Dv, m, C, _DT[dt], _act(act), None, 0, None))
     ws = _workspace(nbytes, dev, workspace)
     _check(L_.gsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(hk0), _ptr(hv0), _ptr(o), _ptr(hkt), _ptr(hvt),
-                      B, H, L, Dk, Dv, m, C, _DT[dt], _ptr(ws), ws.numel(), _stream(dev)))
+                      B, H, L, Dk, Dv, m, C, _DT[dt], _act(act), _ptr(ws), ws.numel(), _stream(dev)))
     return o, hkt, hvt
 
 
 def gsa_bwd(q, k, v, g, do, C: int = 64, hk0=None, hv0=None, dhkt=None, dhvt=None,
-            want_dh0: bool = False, *, workspace=None, outs=None):
+            want_dh0: bool = False, *, act: str = "softmax", workspace=None, outs=None):
     """Gradients of sum(o*do) + sum(hkt*dhkt) + sum(hvt*dhvt).
     Returns (dq, dk, dv, dg, dhk0-or-None, dhv0-or-None)."""
     B, H, L, Dk, Dv, dev, dt = _common(q, k, v, g, gate_width=True)
@@ -362,9 +372,9 @@ def gsa_bwd(q, k, v, g, do, C: int = 64, hk0=None, hv0=None, dhkt=None, dhvt=Non
     L_ = lib()
     nbytes = L_.gsa_bwd_workspace_bytes(B, H, L, Dk, Dv, m, C, _DT[dt])
     if nbytes == 0:
-        _check(L_.gsa_bwd(*([None] * 15), B, H, L, Dk, Dv, m, C, _DT[dt], None, 0, None))
+        _check(L_.gsa_bwd(*([None] * 15), B, H, L, Dk, Dv, m, C, _DT[dt], _act(act), None, 0, None))
     ws = _workspace(nbytes, dev, workspace)
     _check(L_.gsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(hk0), _ptr(hv0), _ptr(do), _ptr(dhkt), _ptr(dhvt),
                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dhk0), _ptr(dhv0),
-                      B, H, L, Dk, Dv, m, C, _DT[dt], _ptr(ws), ws.numel(), _stream(dev)))
+                      B, H, L, Dk, Dv, m, C, _DT[dt], _act(act), _ptr(ws), ws.numel(), _stream(dev)))
     return dq, dk, dv, dg, dhk0, dhv0

@@ -14,8 +14,10 @@ using namespace gla;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr size_t kAlign = 256;
+
+bool valid_act(int act) { return act >= GSA_ACT_SOFTMAX && act <= GSA_ACT_NONE; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -426,9 +428,10 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g, 
 }
 
 int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, float* hk, float* hv,
-                    void* o, int B, int H, int Dk, int Dv, int m, int dtype, void* stream) {
+                    void* o, int B, int H, int Dk, int Dv, int m, int dtype, int act, void* stream) {
   if (dtype != GLA_F32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;
   if (B < 1 || H < 1 || Dk < 1 || Dv < 1 || m < 1) return GLA_ERR_SHAPE;
+  if (!valid_act(act)) return GLA_ERR_UNSUPPORTED;
   if (Dk % 16 != 0 || Dk > 256 || Dv % 16 != 0 || Dv > 512 || m % 16 != 0 || m > 256)
     return GLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !g || !hk || !hv || !o) return GLA_ERR_NULL_ARG;
@@ -442,7 +445,7 @@ int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, 
   // the two in-place memories overlap neither the token inputs nor each other
   const Range mem[] = {{hk, BH * Dk * m * 4}, {hv, BH * m * Dv * 4}};
   if (any_alias(mem, 2, ins, 4)) return GLA_ERR_ALIAS;
-  GsaDecodeParams p{q, k, v, g, hk, hv, o, (int)BH, Dk, Dv, m};
+  GsaDecodeParams p{q, k, v, g, hk, hv, o, (int)BH, Dk, Dv, m, act};
   hipError_t e = dtype == GLA_BF16 ? launch_gsa_decode<bf16>(p, static_cast<hipStream_t>(stream))
                                    : launch_gsa_decode<float>(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
@@ -554,9 +557,10 @@ size_t gsa_bwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C
 
 int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
             void* o, float* hkt, float* hvt, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
-            void* workspace, size_t workspace_bytes, void* stream) {
+            int act, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_gsa(B, H, L, Dk, Dv, m, C, dtype, false);
   if (st != GLA_OK) return st;
+  if (!valid_act(act)) return GLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !g || !o) return GLA_ERR_NULL_ARG;
   if (!all_aligned({q, k, v, g, hk0, hv0, o, hkt, hvt, workspace})) return GLA_ERR_UNSUPPORTED;
   const GsaLayout lay = gsa_layout(B, H, L, Dk, Dv, m, C, dtype, false);
@@ -569,6 +573,7 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
   if (any_alias(outs, 4, ins, 6)) return GLA_ERR_ALIAS;
   GsaParams p = gsa_params(lay, static_cast<char*>(workspace), B, H, L, Dk, Dv, m, C, false);
   p.q = q; p.k = k; p.v = v; p.g = g; p.hk0 = hk0; p.hv0 = hv0; p.o = o; p.hkt = hkt; p.hvt = hvt;
+  p.act = act;
   if (dispatch_gsa(false, dtype, pad_dk(m), pad_c(C), p, static_cast<hipStream_t>(stream)) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;
@@ -577,9 +582,10 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
 int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
             const void* do_, const float* dhkt, const float* dhvt, void* dq, void* dk, void* dv, float* dg,
             float* dhk0, float* dhv0, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
-            void* workspace, size_t workspace_bytes, void* stream) {
+            int act, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_gsa(B, H, L, Dk, Dv, m, C, dtype, true);
   if (st != GLA_OK) return st;
+  if (!valid_act(act)) return GLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !g || !do_ || !dq || !dk || !dv || !dg) return GLA_ERR_NULL_ARG;
   if (!all_aligned({q, k, v, g, hk0, hv0, do_, dhkt, dhvt, dq, dk, dv, dg, dhk0, dhv0, workspace}))
     return GLA_ERR_UNSUPPORTED;
@@ -596,6 +602,7 @@ int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const fl
   GsaParams p = gsa_params(lay, static_cast<char*>(workspace), B, H, L, Dk, Dv, m, C, true);
   p.q = q; p.k = k; p.v = v; p.g = g; p.do_ = do_; p.hk0 = hk0; p.hv0 = hv0; p.dhkt = dhkt; p.dhvt = dhvt;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dhk0 = dhk0; p.dhv0 = dhv0;
+  p.act = act;
   if (dispatch_gsa(true, dtype, pad_dk(m), pad_c(C), p, static_cast<hipStream_t>(stream)) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;

@@ -1,4 +1,5 @@
-// gsa.hip -- gated slot attention (GSA) on gfx950: two GLA passes linked by a softmax.
+// gsa.hip -- gated slot attention (GSA) on gfx950: two GLA passes linked by a softmax (or by
+// one of the element-wise read-outs the GSA summary's ablations use in its place).
 //
 // GSA ("Gated Slot Attention for Efficient Linear-Time Sequence Modeling": abstract and the
 // research-map summary, "Approach") keeps m slot memories per head with a data-dependent
@@ -6,7 +7,7 @@
 // w_t = 1 - alpha_t:
 //   pass 1 (slot keys, decay on the slot axis)  S1_t = S1_{t-1} Diag(alpha_t) + k_t^T w_t,
 //                                               z_t = q_t S1_t
-//   p_t = softmax(z_t) over the m slots
+//   p_t = softmax(z_t) over the m slots  (or p_t = f(z_t) slot by slot: Swish, ReLU, ReLU^2, none)
 //   pass 2 (slot values, row-gated GLA)          S2_t = Diag(alpha_t) S2_{t-1} + w_t^T v_t,
 //                                               o_t = p_t S2_t
 // Pass 2 is exactly GLA with queries p, keys w, values v and the same gates, so it runs on the
@@ -229,7 +230,19 @@ __global__ __launch_bounds__(256) void gsa_p_kernel(GsaParams p) {
     }
   }
   __syncthreads();   // sP aliases the slice tiles: every wave is past its last slice read
-  if (rbv) {
+  if (rbv && p.act != kActSoftmax) {
+    // element-wise read-out; the backward keeps the scores Z, from which it forms f'(Z)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * rb + 4 * grp + e;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb) {
+        const bool ok = 16 * sb + col < m;
+        sP[r * LDM + 16 * sb + col] = from_f32<T>(ok ? gsa_read(z[sb][e], p.act) : 0.f);
+        if (p.Pf && r < len && ok) p.Pf[gbase + (size_t)r * m + 16 * sb + col] = z[sb][e];
+      }
+    }
+  } else if (rbv) {
     // softmax over the m valid slots of each row (rows spread over e, slots over sb and col)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -270,9 +283,9 @@ __global__ __launch_bounds__(256) void gsa_p_kernel(GsaParams p) {
   }
 }
 
-// ----------------------------------------------------------------------------- softmax backward
-// dZ = P (dP - <dP, P>) per row, written in fp32, and (dZ * 2^b)^T per chunk for the pass-1
-// reverse walk.
+// ----------------------------------------------------------------------------- read-out backward
+// dZ = P (dP - <dP, P>) per row for the softmax, dZ = f'(Z) dP for the element-wise read-outs;
+// written in fp32, and (dZ * 2^b)^T per chunk for the pass-1 reverse walk.
 template <typename T, int MP, int CP>
 __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
   using M = ChunkMap<T, MP, CP>;
@@ -293,7 +306,7 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
   float pv[RPS][V], dpv[RPS][V];
   if (cs.active) {
-    const float* Pg = p.Pf + gbase;     // fp32 softmax: its Jacobian keeps sum_s dZ = 0
+    const float* Pg = p.Pf + gbase;     // fp32 P (softmax: its Jacobian keeps sum_s dZ = 0) or Z
     const T* dPg = reinterpret_cast<const T*>(p.dP) + gbase;
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
@@ -321,7 +334,7 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
       float dz[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        dz[e] = pv[u][e] * (dpv[u][e] - rs);
+        dz[e] = p.act == kActSoftmax ? pv[u][e] * (dpv[u][e] - rs) : gsa_read_grad(pv[u][e], dpv[u][e], p.act);
         sT[(c0 + e) * LDC + r] = from_f32<T>(dz[e] * fast_exp2(cs.b[u][e]));
       }
       if (r < len && c0 < m) {
@@ -429,10 +442,14 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
         const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
         float x = c <= r ? acc[e] : 0.f;
         if (c == r) {
-          // diagonal: sum_s dZ w = -sum_s dZ alpha, since sum_s dZ = 0 (softmax Jacobian);
-          // the right-hand form scales with alpha instead of cancelling
+          // diagonal: sum_s dZ w, in fp32.  For the softmax it equals -sum_s dZ alpha, since
+          // sum_s dZ = 0 (its Jacobian); that form scales with alpha instead of cancelling
           x = 0.f;
-          for (int s = 0; s < m; ++s) x -= sdZ[r * LDF + s] * (1.f - sW[r * LDF + s]);
+          if (p.act == kActSoftmax) {
+            for (int s = 0; s < m; ++s) x -= sdZ[r * LDF + s] * (1.f - sW[r * LDF + s]);
+          } else {
+            for (int s = 0; s < m; ++s) x += sdZ[r * LDF + s] * sW[r * LDF + s];
+          }
         }
         sdQK[r * LDQK + c] = x;
       }

@@ -5,7 +5,7 @@
 // (batch, head), with alpha = exp(g) and w = -expm1(g) = 1 - alpha (one value per slot):
 //   hk[:, s] <- alpha_s hk[:, s] + w_s k       (slot keys, stored transposed: [Dk][m])
 //   hv[s, :] <- alpha_s hv[s, :] + w_s v       (slot values: [m][Dv])
-//   z = q hk,  p = softmax(z) over the m slots,  o = p hv
+//   z = q hk,  p = softmax(z) over the m slots (or an element-wise read-out),  o = p hv
 // Both fp32 memories are read and written once per step: an HBM stream at about 0.5 flop per
 // byte, like the GLA decode step, with nothing to contract on matrix cores.  The softmax
 // couples every slot, so one workgroup holds one (batch, head), with 16-byte accesses: each
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kGsaDecThreads) void gsa_decode_kernel(GsaDecodePar
   }
   __syncthreads();
 
-  // softmax over the m slots, computed by every wave for itself: lane holds slots lane + 64 j
+  // read-out over the m slots, computed by every wave for itself: lane holds slots lane + 64 j
   float z[4];
   float mx = -INFINITY;
 #pragma unroll
@@ -133,26 +133,36 @@ __global__ __launch_bounds__(kGsaDecThreads) void gsa_decode_kernel(GsaDecodePar
     }
     mx = fmaxf(mx, z[j]);
   }
+  float sum = 1.f;
+  if (p.act == kActSoftmax) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  float sum = 0.f;
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    sum = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int s = lane + 64 * j;
-    if (s < m) {
-      const float ez = expf(z[j] - mx);
-      sp[wave][s] = ez;
-      sum += ez;
+    for (int j = 0; j < 4; ++j) {
+      const int s = lane + 64 * j;
+      if (s < m) {
+        const float ez = expf(z[j] - mx);
+        sp[wave][s] = ez;
+        sum += ez;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = lane + 64 * j;
+      if (s < m) sp[wave][s] = gsa_read(z[j], p.act);
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
   // the wave's own copy of p is read by other lanes of the same wave
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // o = (sum_s e_s hv[s, :]) / sum_s e_s over the wave's columns
+  // o = (sum_s e_s hv[s, :]) / sum_s e_s over the wave's columns (sum = 1 for the element-wise
+  // read-outs, whose weights are not normalised)
   f32x4 oacc = zero4();
 #pragma unroll
   for (int u = 0; u < R; ++u) {

@@ -58,10 +58,12 @@ struct GsaParams {
   void *dq, *dk, *dv;
   float *dg, *dhk0, *dhv0;
   int BH, L, Dk, DkP, Dv, m, C, N;
+  int act;        // read-out between the passes (GsaAct)
   // workspace
   void* W;        // [BH][L][m] write weights 1 - exp(g)   (keys of pass 2)   (T)
   void* P;        // [BH][L][m] slot softmax              (queries of pass 2) (T)
-  float* Pf;      // [BH][L][m] the same softmax in fp32 (backward only, for its Jacobian)
+  float* Pf;      // [BH][L][m] fp32, backward only: the softmax P (its Jacobian needs P) or,
+                  // for the element-wise read-outs, the scores Z (their derivative needs Z)
   void* dP;       // [BH][L][m] gradient of P (backward)                       (T)
   void* dW2;      // [BH][L][m] pass-2 gradient of W (backward)                (T)
   float* dg2;     // [BH][L][m] pass-2 decay gradient (backward)
@@ -95,11 +97,39 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s);
 template <typename T>
 hipError_t launch_gla_decode(const DecodeParams& p, hipStream_t s);
 
+// Read-out between GSA's two passes.  Softmax over the slots is the method's own; the GSA
+// summary's ablations ("Measured effects") also replace it with Swish, ReLU or ReLU^2, or drop
+// it, each applied to every slot score alone.  Values match gla.h's GSA_ACT_* constants.
+enum GsaAct { kActSoftmax = 0, kActSwish = 1, kActRelu = 2, kActRelu2 = 3, kActNone = 4 };
+
+// p = f(z) for the element-wise read-outs
+__device__ __forceinline__ float gsa_read(float z, int act) {
+  switch (act) {
+    case kActSwish: return z / (1.f + __expf(-z));
+    case kActRelu: return fmaxf(z, 0.f);
+    case kActRelu2: { const float r = fmaxf(z, 0.f); return r * r; }
+    default: return z;
+  }
+}
+
+// dLoss/dz = f'(z) dLoss/dp for the element-wise read-outs
+__device__ __forceinline__ float gsa_read_grad(float z, float dp, int act) {
+  switch (act) {
+    case kActSwish: {
+      const float sg = 1.f / (1.f + __expf(-z));
+      return dp * (sg + z * sg * (1.f - sg));
+    }
+    case kActRelu: return z > 0.f ? dp : 0.f;
+    case kActRelu2: return z > 0.f ? 2.f * z * dp : 0.f;
+    default: return dp;
+  }
+}
+
 struct GsaDecodeParams {
   const void *q, *k, *v, *g;
   float *hk, *hv;                 // [BH][Dk][m], [BH][m][Dv], updated in place
   void* o;
-  int BH, Dk, Dv, m;
+  int BH, Dk, Dv, m, act;
 };
 template <typename T>
 hipError_t launch_gsa_decode(const GsaDecodeParams& p, hipStream_t s);

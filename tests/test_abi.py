@@ -142,24 +142,26 @@ def test_decode_validation(lib):
 
 def test_gsa_decode_validation(lib):
     N = [None] * 7
-    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 16, 7, None) == 3            # dtype
-    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 0, 1, None) == 2             # m < 1
-    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 16, 1, None) == 1            # null pointers
-    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 20, 1, None) == 4            # m not a multiple of 16
-    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 272, 1, None) == 4           # m > 256
-    assert lib.gsa_decode_step(*N, 1, 1, 272, 16, 16, 1, None) == 4           # Dk > 256
-    assert lib.gsa_decode_step(*N, 1, 1, 16, 528, 16, 1, None) == 4          # Dv > 512
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 16, 7, 0, None) == 3            # dtype
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 0, 1, 0, None) == 2             # m < 1
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 16, 1, 0, None) == 1            # null pointers
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 20, 1, 0, None) == 4            # m not a multiple of 16
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 272, 1, 0, None) == 4           # m > 256
+    assert lib.gsa_decode_step(*N, 1, 1, 272, 16, 16, 1, 0, None) == 4           # Dk > 256
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 528, 16, 1, 0, None) == 4          # Dv > 512
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 16, 1, 5, None) == 4          # act not a gsa_act
+    assert lib.gsa_decode_step(*N, 1, 1, 16, 16, 16, 1, -1, None) == 4
     p = [ctypes.c_void_p(0x10000000 + i * 0x1000000) for i in range(7)]
-    assert lib.gsa_decode_step(*p[:6], ctypes.c_void_p(0x10000000 + 2), 1, 1, 16, 16, 16, 1, None) == 4  # misaligned
+    assert lib.gsa_decode_step(*p[:6], ctypes.c_void_p(0x10000000 + 2), 1, 1, 16, 16, 16, 1, 0, None) == 4  # misaligned
     q = list(p)
     q[6] = ctypes.c_void_p(0x10000000 + 16)                                  # o overlaps q
-    assert lib.gsa_decode_step(*q, 1, 1, 16, 16, 16, 1, None) == 6
+    assert lib.gsa_decode_step(*q, 1, 1, 16, 16, 16, 1, 0, None) == 6
     q = list(p)
     q[5] = ctypes.c_void_p(0x10000000 + 0x4000000 + 512)                     # hv overlaps hk
-    assert lib.gsa_decode_step(*q, 1, 1, 16, 16, 16, 1, None) == 6
+    assert lib.gsa_decode_step(*q, 1, 1, 16, 16, 16, 1, 0, None) == 6
     q = list(p)
     q[4] = ctypes.c_void_p(0x10000000 + 0x2000000)                           # hk is v
-    assert lib.gsa_decode_step(*q, 1, 1, 16, 16, 16, 1, None) == 6
+    assert lib.gsa_decode_step(*q, 1, 1, 16, 16, 16, 1, 0, None) == 6
 
 
 def test_profiled_needs_events(lib):
@@ -172,3 +174,11 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(m, "lib_path", "/nonexistent/libgla_amd.so")
     with pytest.raises(RuntimeError, match="no fallback"):
         m.lib()
+
+
+def test_gsa_read_out_validation(lib):
+    """An act outside gsa_act is rejected before the pointers are looked at; every valid act
+    gets as far as the null-pointer check."""
+    for act, want in ((-1, 4), (5, 4), (0, 1), (1, 1), (2, 1), (3, 1), (4, 1)):
+        assert lib.gsa_fwd(*[None] * 9, 1, 1, 64, 16, 16, 16, 16, 1, act, None, 0, None) == want
+        assert lib.gsa_bwd(*[None] * 15, 1, 1, 64, 16, 16, 16, 16, 1, act, None, 0, None) == want

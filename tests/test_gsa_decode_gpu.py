@@ -22,7 +22,7 @@ def gla():
     return m
 
 
-def run_chain(gla, d, dt, T):
+def run_chain(gla, d, dt, T, act="softmax"):
     """T steps on the GPU and in the oracle; returns both sides' outputs and final memories."""
     import torch
     hk, hv = dev(d["hk"]), dev(d["hv"])
@@ -30,9 +30,9 @@ def run_chain(gla, d, dt, T):
     outs, routs = [], []
     for t in range(T):
         o = gla.gsa_decode_step(dev(d["q"][t], dt), dev(d["k"][t], dt), dev(d["v"][t], dt), dev(d["g"][t], dt),
-                                hk, hv)
+                                hk, hv, act=act)
         outs.append(o)
-        ro, rk, rv = ref_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], rk, rv)
+        ro, rk, rv = ref_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], rk, rv, act=act)
         routs.append(ro)
     torch.cuda.synchronize()
     return np.stack([host(o) for o in outs]), np.stack(routs), host(hk), rk, host(hv), rv
@@ -61,6 +61,21 @@ def test_steps_match_oracle(gla, shape):
     o, ro, hk, rk, hv, rv = run_chain(gla, d, dt, w.T)
     assert_close("o", o, ro, dt)
     # the memories are float32 whatever the token dtype: hold them to the fp32 bound
+    assert_close("hk", hk, rk, "f32")
+    assert_close("hv", hv, rv, "f32")
+
+
+@pytest.mark.parametrize("act", ["swish", "relu", "relu2", "none"])
+@pytest.mark.parametrize("shape", [(2, 3, 128, 128, 64, "bf16"), (1, 2, 48, 80, 48, "f32"),
+                                   (1, 1, 32, 48, 256, "bf16")], ids=lambda s: "x".join(map(str, s)))
+def test_read_outs(gla, shape, act):
+    """The element-wise read-outs in place of the softmax (o is continuous in z for all)."""
+    B, H, Dk, Dv, m, dt = shape
+    w = W.GsaDecodeWorkload("gsa-dec-act", 4, B, H, Dk, Dv, m, dt, 620 + Dk + m)
+    d = W.gsa_decode_inputs(w)
+    print(f"[gsa decode] B={B} H={H} Dk={Dk} Dv={Dv} m={m} {dt} act={act}", flush=True)
+    o, ro, hk, rk, hv, rv = run_chain(gla, d, dt, w.T, act)
+    assert_close("o", o, ro, dt)
     assert_close("hk", hk, rk, "f32")
     assert_close("hv", hv, rv, "f32")
 

@@ -20,26 +20,29 @@ def gla():
     return m
 
 
-def check_gsa(gla, w, x, units=None, with_state=True, with_dstate=True):
+def check_gsa(gla, w, x, units=None, with_state=True, with_dstate=True, act="softmax", backward=True):
     dt = w.dtype
     args = [dev(x[n], dt) for n in ("q", "k", "v", "g")]
     hk0 = dev(x["hk0"]) if with_state else None
     hv0 = dev(x["hv0"]) if with_state else None
-    o, hkt, hvt = gla.gsa_fwd(*args, C=w.C, hk0=hk0, hv0=hv0)
-    dq, dk, dv, dg, dhk0, dhv0 = gla.gsa_bwd(*args, dev(x["do"], dt), C=w.C, hk0=hk0, hv0=hv0,
-                                             dhkt=dev(x["dhkt"]) if with_dstate else None,
-                                             dhvt=dev(x["dhvt"]) if with_dstate else None, want_dh0=True)
+    o, hkt, hvt = gla.gsa_fwd(*args, C=w.C, hk0=hk0, hv0=hv0, act=act)
     sel = (slice(None), slice(None)) if units is None else units
     s0 = (lambda a: None if (a is None or not with_state) else a[sel])
-    ro, rhk, rhv = gsa_recurrent_fwd(x["q"][sel], x["k"][sel], x["v"][sel], x["g"][sel], s0(x["hk0"]), s0(x["hv0"]))
-    rb = gsa_recurrent_bwd(x["q"][sel], x["k"][sel], x["v"][sel], x["g"][sel], x["do"][sel], s0(x["hk0"]),
-                           s0(x["hv0"]), x["dhkt"][sel] if with_dstate else None,
-                           x["dhvt"][sel] if with_dstate else None)
+    ro, rhk, rhv = gsa_recurrent_fwd(x["q"][sel], x["k"][sel], x["v"][sel], x["g"][sel], s0(x["hk0"]), s0(x["hv0"]),
+                                     act=act)
     print(f"[{w.name}] B={w.B} H={w.H} L={x['q'].shape[2]} Dk={w.Dk} Dv={w.Dv} m={w.m} C={w.C} {dt} "
-          f"h0={with_state} dht={with_dstate}", flush=True)
+          f"h0={with_state} dht={with_dstate} act={act}", flush=True)
     assert_close("o", host(o)[sel], ro, dt)
     assert_close("hkt", host(hkt)[sel], rhk, dt)
     assert_close("hvt", host(hvt)[sel], rhv, dt)
+    if not backward:
+        return
+    dq, dk, dv, dg, dhk0, dhv0 = gla.gsa_bwd(*args, dev(x["do"], dt), C=w.C, hk0=hk0, hv0=hv0,
+                                             dhkt=dev(x["dhkt"]) if with_dstate else None,
+                                             dhvt=dev(x["dhvt"]) if with_dstate else None, want_dh0=True, act=act)
+    rb = gsa_recurrent_bwd(x["q"][sel], x["k"][sel], x["v"][sel], x["g"][sel], x["do"][sel], s0(x["hk0"]),
+                           s0(x["hv0"]), x["dhkt"][sel] if with_dstate else None,
+                           x["dhvt"][sel] if with_dstate else None, act=act)
     assert_close("dq", host(dq)[sel], rb["dq"], dt)
     assert_close("dk", host(dk)[sel], rb["dk"], dt)
     assert_close("dv", host(dv)[sel], rb["dv"], dt)
@@ -143,3 +146,66 @@ def test_deterministic(gla):
     torch.cuda.synchronize()
     assert all(torch.equal(s, t) for s, t in zip(a[:4], b[:4]))
     assert all(torch.equal(s, t) for s, t in zip(fa, fb))
+
+
+# ---------------------------------------------------------------- read-outs other than softmax
+def slot_scores(q, k, g, hk0):
+    """z_t[s] = <Kmem_t[s], q_t> with the slot keys written token by token (test-side helper,
+    used only to check that every score is well away from ReLU's kink)."""
+    B, H, L, Dk = q.shape
+    m = g.shape[-1]
+    K = np.zeros((B, H, Dk, m)) if hk0 is None else hk0.astype(np.float64).copy()
+    z = np.empty((B, H, L, m))
+    for t in range(L):
+        a = np.exp(g[:, :, t].astype(np.float64))
+        K = K * a[:, :, None, :] + k[:, :, t, :, None] * (1.0 - a)[:, :, None, :]
+        z[:, :, t] = np.einsum("bhi,bhis->bhs", q[:, :, t], K)
+    return z
+
+
+READ_OUT_SHAPES = [
+    # (B, H, L, Dk, Dv, m, C, dtype)
+    (1, 2, 150, 64, 64, 32, 64, "bf16"),
+    (2, 1, 77, 32, 48, 16, 16, "bf16"),
+    (1, 1, 130, 128, 128, 64, 32, "bf16"),
+    (1, 2, 100, 64, 96, 64, 32, "f32"),
+]
+
+
+@pytest.mark.parametrize("act", ["swish", "relu2", "none"])
+@pytest.mark.parametrize("shape", READ_OUT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_read_outs(gla, shape, act):
+    """Swish, ReLU^2 and no read-out, forward and backward (their derivatives are continuous)."""
+    B, H, L, Dk, Dv, m, C, dt = shape
+    w = W.GsaWorkload("read-out", B, H, L, Dk, Dv, m, C, dt, 500 + L + m, h0=True)
+    check_gsa(gla, w, W.gsa_inputs(w), act=act)
+
+
+@pytest.mark.parametrize("shape", READ_OUT_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_relu_forward(gla, shape):
+    """ReLU read-out, forward on the general inputs (the output is continuous in z)."""
+    B, H, L, Dk, Dv, m, C, dt = shape
+    w = W.GsaWorkload("relu", B, H, L, Dk, Dv, m, C, dt, 520 + L + m, h0=True)
+    check_gsa(gla, w, W.gsa_inputs(w), act="relu", backward=False)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_relu_backward_clear_margin(gla, dt):
+    """ReLU's derivative jumps at z = 0, and the two sides compute z in different precision, so
+    the backward is compared where every score is decided: initial slot keys carry a strong
+    signed component along key channel 0 that q_t reads with weight 1, gates are close to 0
+    (the keys persist) and every |z| is asserted to stay above 0.5, far beyond either side's
+    rounding of z."""
+    w = W.GsaWorkload("relu-margin", 1, 2, 150, 64, 64, 32, 64, dt, 541, h0=True)
+    x = W.gsa_inputs(w)
+    rng = np.random.default_rng(542)
+    sign = np.where(rng.random(w.m) < 0.5, -1.0, 1.0).astype(np.float32)
+    x["hk0"][:, :, 0, :] = 3.0 * sign
+    x["q"][:, :, :, 0] = 1.0
+    x["g"] = (x["g"] / 400.0).astype(np.float32)
+    if dt == "bf16":
+        x["g"] = W.round_bf16(x["g"])
+    z = slot_scores(x["q"], x["k"], x["g"], x["hk0"])
+    print(f"  min |z| = {np.min(np.abs(z)):.3f}", flush=True)
+    assert np.min(np.abs(z)) > 0.5
+    check_gsa(gla, w, x, act="relu")
