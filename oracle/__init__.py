@@ -14,3 +14,4 @@ from .gla_oracle import (  # noqa: F401
     gla_recurrent_fwd, gla_recurrent_bwd, gla_decode_step, gla_chunkwise_fwd,
 )
 from .gsa_oracle import ACTS as GSA_ACTS, gsa_decode_step, gsa_recurrent_bwd, gsa_recurrent_fwd  # noqa: F401
+from .msgla_oracle import msgla_fwd  # noqa: F401
