@@ -232,6 +232,35 @@ int gsa_decode_step(const void* q, const void* k, const void* v, const void* g,
                     float* hk, float* hv, void* o,
                     int B, int H, int Dk, int Dv, int m, int dtype, int act, void* stream);
 
+/* ---------------------------------------------------------------- MS-GLA front end -----
+ * Multi-scale GLA over head groups (MS-GLA summary, sections 3.1 to 3.4).  Group i holds heads
+ * heads[0] + ... + heads[i-1] .. + heads[i] - 1 (consecutive, sum(heads) = H) at temporal scale
+ * scales[i]:
+ *   pooling: non-overlapping averages of scales[i] tokens of q, k, g and v of those heads (the
+ *            trailing partial block averages only its real tokens), ceil(L / scales[i]) pooled
+ *            tokens;
+ *   branch:  GLA (as gla_fwd, chunk size C) on the pooled sequence, from h0's slice;
+ *   hold:    token t reads the pooled output of block (t + 1) / scales[i] - 1 (integer
+ *            division), the latest block whose tokens it has all seen, and zeros before the
+ *            first block completes;
+ *   fusion:  o[b,h,t,:] = w[b,t,i] * held[b,h,t,:] for the group i of head h.
+ *   q, k, g : [B,H,L,Dk] dtype;  v : [B,H,L,Dv] dtype
+ *   h0      : [B,H,Dk,Dv] float32 initial state of every head's branch, or NULL (zeros)
+ *   w       : [B,L,ngroups] float32 fusion weights (4-byte aligned), or NULL (all 1)
+ *   o       : [B,H,L,Dv] dtype
+ *   ht      : [B,H,Dk,Dv] float32, each branch's state after its last pooled token, or NULL
+ *   ngroups : 1 .. 8;  scales, heads: HOST arrays of ngroups ints (1 <= scales[i] <= 65536,
+ *             heads[i] >= 1)
+ * Every group's pooled shape must be supported by gla_fwd (same C, Dk, Dv rules).  Bad group
+ * arrays give GLA_ERR_SHAPE (counts) or GLA_ERR_UNSUPPORTED (ngroups, scales). */
+size_t msgla_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                                 int ngroups, const int* scales, const int* heads);
+int msgla_fwd(const void* q, const void* k, const void* v, const void* g,
+              const float* h0, const float* w, void* o, float* ht,
+              int B, int H, int L, int Dk, int Dv, int C, int dtype,
+              int ngroups, const int* scales, const int* heads,
+              void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,8 @@ Entry points (same names as the C ABI):
     gsa_bwd(q, k, v, g, do, C=64, hk0=None, hv0=None, dhkt=None, dhvt=None, want_dh0=False,
             act="softmax") -> (dq, dk, dv, dg, dhk0, dhv0)
     (act: the read-out between GSA's passes, one of GSA_ACTS)
+    msgla_fwd(q, k, v, g, scales, heads, w=None, C=64, h0=None, output_final_state=True)
+        -> (o, ht)                         (multi-scale GLA over head groups; w [B,L,groups])
 Layouts: q, k, g [B,H,L,Dk]; v, o, do [B,H,L,Dv] (all bf16 or all float32); states float32.
 """
 from __future__ import annotations
@@ -31,7 +33,7 @@ __all__ = [
     "lib", "lib_path", "GlaError", "gla_fwd", "gla_bwd", "gla_fwd_save", "gla_bwd_saved", "gla_decode_step",
     "gsa_fwd", "gsa_bwd", "gsa_decode_step", "gla_saved_bytes", "gla_bwd_saved_workspace_bytes",
     "gla_fwd_workspace_bytes", "gla_bwd_workspace_bytes", "gsa_fwd_workspace_bytes",
-    "gsa_bwd_workspace_bytes", "EXPORTED_SYMBOLS", "GSA_ACTS",
+    "gsa_bwd_workspace_bytes", "EXPORTED_SYMBOLS", "GSA_ACTS", "msgla_fwd", "msgla_fwd_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +75,8 @@ _SIGS = {
     "gsa_bwd_workspace_bytes": (_Z, [_I] * 8),
     "gsa_bwd": (_I, [_P] * 15 + [_I] * 9 + [_P, _Z, _P]),
     "gsa_decode_step": (_I, [_P] * 7 + [_I] * 7 + [_P]),
+    "msgla_fwd_workspace_bytes": (_Z, [_I] * 8 + [_P, _P]),
+    "msgla_fwd": (_I, [_P] * 8 + [_I] * 8 + [_P, _P, _P, _Z, _P]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -378,3 +382,40 @@ def gsa_bwd(q, k, v, g, do, C: int = 64, hk0=None, hv0=None, dhkt=None, dhvt=Non
                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dhk0), _ptr(dhv0),
                       B, H, L, Dk, Dv, m, C, _DT[dt], _act(act), _ptr(ws), ws.numel(), _stream(dev)))
     return dq, dk, dv, dg, dhk0, dhv0
+
+
+def _groups(scales, heads):
+    scales, heads = [int(x) for x in scales], [int(x) for x in heads]
+    if len(scales) != len(heads):
+        raise ValueError("scales and heads need one entry per head group")
+    n = len(scales)
+    return n, (ctypes.c_int * n)(*scales), (ctypes.c_int * n)(*heads)
+
+
+def msgla_fwd_workspace_bytes(B, H, L, Dk, Dv, C, dtype, scales, heads) -> int:
+    n, sc, hd = _groups(scales, heads)
+    return lib().msgla_fwd_workspace_bytes(B, H, L, Dk, Dv, C, _DT[dtype], n, sc, hd)
+
+
+def msgla_fwd(q, k, v, g, scales, heads, w=None, C: int = 64, h0=None, output_final_state: bool = True, *,
+              workspace=None, out=None):
+    """Multi-scale GLA: head group i (heads[i] consecutive heads) runs GLA on its q, k, g, v
+    average-pooled over blocks of scales[i] tokens; token t takes its group's pooled output of
+    block (t+1)//s - 1 (zeros before the first block completes), times w[b, t, i].
+    Returns (o [B,H,L,Dv], ht [B,H,Dk,Dv] or None)."""
+    B, H, L, Dk, Dv, dev, dt = _common(q, k, v, g)
+    n, sc, hd = _groups(scales, heads)
+    if h0 is not None:
+        _need(h0, "h0", (B, H, Dk, Dv), torch.float32, dev)
+    if w is not None:
+        _need(w, "w", (B, L, n), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, H, L, Dv), dtype=dt, device=dev)
+    ht = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev) if output_final_state else None
+    L_ = lib()
+    nbytes = L_.msgla_fwd_workspace_bytes(B, H, L, Dk, Dv, C, _DT[dt], n, sc, hd)
+    if nbytes == 0:
+        _check(L_.msgla_fwd(*([None] * 8), B, H, L, Dk, Dv, C, _DT[dt], n, sc, hd, None, 0, None))
+    ws = _workspace(nbytes, dev, workspace)
+    _check(L_.msgla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(w), _ptr(o), _ptr(ht),
+                        B, H, L, Dk, Dv, C, _DT[dt], n, sc, hd, _ptr(ws), ws.numel(), _stream(dev)))
+    return o, ht

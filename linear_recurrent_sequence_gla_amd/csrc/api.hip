@@ -4,6 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <initializer_list>
 
 #include "../../include/gla.h"
@@ -455,6 +456,58 @@ int gsa_decode_step(const void* q, const void* k, const void* v, const void* g, 
 
 namespace {
 
+// ---------------------------------------------------------------- MS-GLA front end
+struct MsglaLayout {
+  size_t pooled[kMsMaxGroups];   // per group: pooled q, k, g, then v
+  size_t op[kMsMaxGroups];       // per group: pooled GLA outputs
+  size_t h0g, htg;               // one group's initial / final states (reused group by group)
+  size_t gla;                    // one group's GLA forward workspace (reused group by group)
+  size_t total;
+};
+
+int pooled_len(int L, int s) { return (L + s - 1) / s; }
+
+int check_msgla(int B, int H, int L, int Dk, int Dv, int C, int dtype, int ngroups, const int* scales,
+                const int* heads) {
+  int st = check_dims(B, H, L, Dk, Dv, C, dtype);
+  if (st != GLA_OK) return st;
+  if (ngroups < 1 || ngroups > kMsMaxGroups) return GLA_ERR_UNSUPPORTED;
+  if (!scales || !heads) return GLA_ERR_NULL_ARG;
+  int total = 0;
+  for (int i = 0; i < ngroups; ++i) {
+    if (scales[i] < 1 || heads[i] < 1) return GLA_ERR_SHAPE;
+    if (scales[i] > 65536) return GLA_ERR_UNSUPPORTED;
+    total += heads[i];
+    if (total > H) return GLA_ERR_SHAPE;
+    if ((st = check_dims(B, heads[i], pooled_len(L, scales[i]), Dk, Dv, C, dtype)) != GLA_OK) return st;
+  }
+  return total == H ? GLA_OK : GLA_ERR_SHAPE;
+}
+
+MsglaLayout msgla_layout(int B, int L, int Dk, int Dv, int C, int dtype, int ngroups, const int* scales,
+                         const int* heads) {
+  MsglaLayout l{};
+  const size_t es = esize_of(dtype);
+  size_t off = 0, smax = 0, gmax = 0;
+  for (int i = 0; i < ngroups; ++i) {
+    const size_t rows = (size_t)B * heads[i] * pooled_len(L, scales[i]);
+    l.pooled[i] = off;
+    off += 3 * align_up(rows * Dk * es) + align_up(rows * Dv * es);
+    l.op[i] = off;
+    off += align_up(rows * Dv * es);
+    smax = std::max(smax, (size_t)B * heads[i] * Dk * Dv * 4);
+    gmax = std::max(gmax, fwd_ws_bytes(B, heads[i], pooled_len(L, scales[i]), Dk, Dv, C, dtype));
+  }
+  l.h0g = off;
+  off += align_up(smax);
+  l.htg = off;
+  off += align_up(smax);
+  l.gla = off;
+  off += gmax;
+  l.total = off;
+  return l;
+}
+
 // ---------------------------------------------------------------- gated slot attention
 int check_gsa(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, bool bwd) {
   if (dtype != GLA_F32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;
@@ -606,6 +659,78 @@ int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const fl
   if (dispatch_gsa(true, dtype, pad_dk(m), pad_c(C), p, static_cast<hipStream_t>(stream)) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;
+}
+
+
+size_t msgla_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype, int ngroups,
+                                 const int* scales, const int* heads) {
+  if (check_msgla(B, H, L, Dk, Dv, C, dtype, ngroups, scales, heads) != GLA_OK) return 0;
+  return msgla_layout(B, L, Dk, Dv, C, dtype, ngroups, scales, heads).total;
+}
+
+int msgla_fwd(const void* q, const void* k, const void* v, const void* g, const float* h0, const float* w,
+              void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype, int ngroups,
+              const int* scales, const int* heads, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_msgla(B, H, L, Dk, Dv, C, dtype, ngroups, scales, heads);
+  if (st != GLA_OK) return st;
+  if (!q || !k || !v || !g || !o) return GLA_ERR_NULL_ARG;
+  if (!all_aligned({q, k, v, g, h0, o, ht, workspace}) || (reinterpret_cast<uintptr_t>(w) & 3))
+    return GLA_ERR_UNSUPPORTED;
+  const MsglaLayout lay = msgla_layout(B, L, Dk, Dv, C, dtype, ngroups, scales, heads);
+  if (!workspace || workspace_bytes < lay.total) return GLA_ERR_WORKSPACE;
+  const size_t es = esize_of(dtype), BH = (size_t)B * H;
+  const size_t nk = BH * L * Dk * es, nv = BH * L * Dv * es, ns = BH * Dk * Dv * 4;
+  const Range ins[] = {{q, nk}, {k, nk}, {v, nv}, {g, nk}, {h0, h0 ? ns : 0},
+                       {w, w ? (size_t)B * L * ngroups * 4 : 0}};
+  const Range outs[] = {{o, nv}, {ht, ht ? ns : 0}, {workspace, lay.total}};
+  if (any_alias(outs, 3, ins, 6)) return GLA_ERR_ALIAS;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  MsglaParams mp{};
+  mp.q = q; mp.k = k; mp.v = v; mp.g = g; mp.w = w; mp.o = o;
+  mp.B = B; mp.H = H; mp.L = L; mp.Dk = Dk; mp.Dv = Dv; mp.ngroups = ngroups;
+  int hbeg = 0;
+  for (int i = 0; i < ngroups; ++i) {
+    const size_t rows = (size_t)B * heads[i] * pooled_len(L, scales[i]);
+    MsglaGroup& G = mp.grp[i];
+    G.h0 = hbeg; G.nh = heads[i]; G.s = scales[i];
+    G.qp = ws + lay.pooled[i];
+    G.kp = static_cast<char*>(G.qp) + align_up(rows * Dk * es);
+    G.gp = static_cast<char*>(G.kp) + align_up(rows * Dk * es);
+    G.vp = static_cast<char*>(G.gp) + align_up(rows * Dk * es);
+    G.op = ws + lay.op[i];
+    hbeg += heads[i];
+  }
+  hipError_t e = dtype == GLA_BF16 ? launch_msgla_pool<bf16>(mp, hs) : launch_msgla_pool<float>(mp, hs);
+  if (e != hipSuccess) return GLA_ERR_HIP;
+
+  // one GLA forward per head group on its pooled sequence; the group's heads are a strided
+  // slice of [B][H], so its states are gathered into / scattered from contiguous buffers
+  float* h0g = reinterpret_cast<float*>(ws + lay.h0g);
+  float* htg = reinterpret_cast<float*>(ws + lay.htg);
+  const size_t head_bytes = (size_t)Dk * Dv * 4;
+  for (int i = 0; i < ngroups; ++i) {
+    const MsglaGroup& G = mp.grp[i];
+    const int Ls = pooled_len(L, G.s), N = (Ls + C - 1) / C, DKP = pad_dk(Dk), CP = pad_c(C);
+    if (h0 && hipMemcpy2DAsync(h0g, G.nh * head_bytes, h0 + (size_t)G.h0 * Dk * Dv, (size_t)H * head_bytes,
+                               G.nh * head_bytes, B, hipMemcpyDeviceToDevice, hs) != hipSuccess)
+      return GLA_ERR_HIP;
+    FwdParams p;
+    p.q = G.qp; p.k = G.kp; p.v = G.vp; p.g = G.gp; p.h0 = h0 ? h0g : nullptr;
+    p.o = G.op; p.ht = ht ? htg : nullptr;
+    p.BH = B * G.nh; p.L = Ls; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
+    const OpsLayout ol = ops_layout((size_t)p.BH, N, CP, DKP, es, false);
+    p.ops = carve_ops(ws + lay.gla, ol, false);
+    p.Hs = ws + lay.gla + ol.total;
+    p.events = LaunchEvents{nullptr, 0};
+    if (dispatch_fwd(dtype, DKP, CP, p, hs) != hipSuccess) return GLA_ERR_HIP;
+    if (ht && hipMemcpy2DAsync(ht + (size_t)G.h0 * Dk * Dv, (size_t)H * head_bytes, htg, G.nh * head_bytes,
+                               G.nh * head_bytes, B, hipMemcpyDeviceToDevice, hs) != hipSuccess)
+      return GLA_ERR_HIP;
+  }
+  e = dtype == GLA_BF16 ? launch_msgla_hold<bf16>(mp, hs) : launch_msgla_hold<float>(mp, hs);
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -134,6 +134,25 @@ struct GsaDecodeParams {
 template <typename T>
 hipError_t launch_gsa_decode(const GsaDecodeParams& p, hipStream_t s);
 
+// MS-GLA front end: head groups, one per temporal scale
+constexpr int kMsMaxGroups = 8;
+struct MsglaGroup {
+  int h0, nh, s;                  // first head, number of heads, pooling scale
+  void *qp, *kp, *gp, *vp;        // pooled inputs [B][nh][ceil(L/s)][Dk or Dv] (T)
+  void* op;                       // pooled GLA outputs [B][nh][ceil(L/s)][Dv] (T)
+};
+struct MsglaParams {
+  const void *q, *k, *v, *g;      // [B][H][L][Dk or Dv] (T)
+  const float* w;                 // [B][L][ngroups] fusion weights, or null for 1
+  void* o;                        // [B][H][L][Dv] (T)
+  int B, H, L, Dk, Dv, ngroups;
+  MsglaGroup grp[kMsMaxGroups];
+};
+template <typename T>
+hipError_t launch_msgla_pool(const MsglaParams& p, hipStream_t s);
+template <typename T>
+hipError_t launch_msgla_hold(const MsglaParams& p, hipStream_t s);
+
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 
 template <typename T, int MP, int CP>

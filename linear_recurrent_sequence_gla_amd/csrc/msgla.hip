@@ -1,0 +1,130 @@
+// msgla.hip -- the multi-scale GLA (MS-GLA) front end: temporal pooling per head group, and
+// the causal hold with per-token fusion weights.  Between the two, each group's pooled
+// sequence runs through the GLA forward kernels unchanged (MS-GLA summary, section 3.4: static,
+// non-overlapping pooling keeps each branch a contiguous, shorter GLA sequence).
+//
+//   pooling (section 3.1): block j of group scale s averages tokens j*s .. min(j*s+s, L) - 1
+//       of q, k, g and v (a trailing partial block averages only its real tokens), for the
+//       group's heads, into contiguous [B][heads][ceil(L/s)][D] tensors;
+//   hold and fusion (section 3.3): token t takes the pooled output of block (t+1)/s - 1, the
+//       latest block it has fully seen (zero before the first completes), times the caller's
+//       weight w[b][t][group].
+//
+// Both kernels are plain HBM streams with 16-byte accesses and fp32 arithmetic; nothing here
+// contracts, so there is no matrix-core work.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace gla {
+
+constexpr int kMsRowsPerBlock = 16;     // pooled rows per pooling workgroup
+constexpr int kMsTokPerBlock = 16;      // tokens per hold workgroup
+
+// head group of head h (groups hold consecutive heads, in order)
+__device__ __forceinline__ int ms_group_of(const MsglaParams& p, int h) {
+  int gi = 0;
+#pragma unroll 1
+  while (gi + 1 < p.ngroups && h >= p.grp[gi + 1].h0) ++gi;
+  return gi;
+}
+
+// grid (ceil(L / kMsRowsPerBlock), B*H); the blocks past a group's pooled length return
+template <typename T>
+__global__ __launch_bounds__(256) void msgla_pool_kernel(MsglaParams p) {
+  typedef typename V16<T>::type VT;
+  constexpr int V = V16<T>::N;
+  const int bh = blockIdx.y, b = bh / p.H, h = bh - b * p.H;
+  const int gi = ms_group_of(p, h);
+  const MsglaGroup& G = p.grp[gi];
+  const int s = G.s, Ls = (p.L + s - 1) / s, hl = h - G.h0;
+  const int j0 = blockIdx.x * kMsRowsPerBlock;
+  if (j0 >= Ls) return;
+  const int nk = p.Dk / V, nv = p.Dv / V, per_row = 3 * nk + nv;
+  const size_t src_k = (size_t)bh * p.L * p.Dk, src_v = (size_t)bh * p.L * p.Dv;
+  const size_t dst_row = (size_t)(b * G.nh + hl) * Ls;
+  const int rows = min(kMsRowsPerBlock, Ls - j0);
+  for (int idx = threadIdx.x; idx < rows * per_row; idx += 256) {
+    const int r = idx / per_row, c = idx - r * per_row;
+    const int j = j0 + r;
+    const int t0 = j * s, cnt = min(s, p.L - t0);
+    const T* src;
+    T* dst;
+    int col, D;
+    if (c < 3 * nk) {
+      const int which = c / nk;
+      col = (c - which * nk) * V;
+      D = p.Dk;
+      src = reinterpret_cast<const T*>(which == 0 ? p.q : which == 1 ? p.k : p.g) + src_k;
+      dst = reinterpret_cast<T*>(which == 0 ? G.qp : which == 1 ? G.kp : G.gp) + dst_row * p.Dk;
+    } else {
+      col = (c - 3 * nk) * V;
+      D = p.Dv;
+      src = reinterpret_cast<const T*>(p.v) + src_v;
+      dst = reinterpret_cast<T*>(G.vp) + dst_row * p.Dv;
+    }
+    float acc[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = 0.f;
+    for (int u = 0; u < cnt; ++u) {
+      const VT x = *reinterpret_cast<const VT*>(src + (size_t)(t0 + u) * D + col);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += to_f32(x[e]);
+    }
+    const float inv = 1.f / (float)cnt;
+    VT y;
+#pragma unroll
+    for (int e = 0; e < V; ++e) y[e] = from_f32<T>(cnt == 1 ? acc[e] : acc[e] * inv);
+    *reinterpret_cast<VT*>(dst + (size_t)j * D + col) = y;
+  }
+}
+
+// grid (ceil(L / kMsTokPerBlock), B*H)
+template <typename T>
+__global__ __launch_bounds__(256) void msgla_hold_kernel(MsglaParams p) {
+  typedef typename V16<T>::type VT;
+  constexpr int V = V16<T>::N;
+  const int bh = blockIdx.y, b = bh / p.H, h = bh - b * p.H;
+  const int gi = ms_group_of(p, h);
+  const MsglaGroup& G = p.grp[gi];
+  const int s = G.s, Ls = (p.L + s - 1) / s, hl = h - G.h0;
+  const int nv = p.Dv / V;
+  const int t0 = blockIdx.x * kMsTokPerBlock, toks = min(kMsTokPerBlock, p.L - t0);
+  const T* op = reinterpret_cast<const T*>(G.op) + (size_t)(b * G.nh + hl) * Ls * p.Dv;
+  T* o = reinterpret_cast<T*>(p.o) + (size_t)bh * p.L * p.Dv;
+  for (int idx = threadIdx.x; idx < toks * nv; idx += 256) {
+    const int r = idx / nv, col = (idx - r * nv) * V;
+    const int t = t0 + r, j = (t + 1) / s - 1;
+    const float wt = p.w ? p.w[((size_t)b * p.L + t) * p.ngroups + gi] : 1.f;
+    VT y;
+    if (j >= 0) {
+      const VT x = *reinterpret_cast<const VT*>(op + (size_t)j * p.Dv + col);
+#pragma unroll
+      for (int e = 0; e < V; ++e) y[e] = from_f32<T>(wt * to_f32(x[e]));
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) y[e] = from_f32<T>(0.f);
+    }
+    *reinterpret_cast<VT*>(o + (size_t)t * p.Dv + col) = y;
+  }
+}
+
+template <typename T>
+hipError_t launch_msgla_pool(const MsglaParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((msgla_pool_kernel<T>), dim3((p.L + kMsRowsPerBlock - 1) / kMsRowsPerBlock, p.B * p.H),
+                     dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_msgla_hold(const MsglaParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((msgla_hold_kernel<T>), dim3((p.L + kMsTokPerBlock - 1) / kMsTokPerBlock, p.B * p.H),
+                     dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template hipError_t launch_msgla_pool<bf16>(const MsglaParams&, hipStream_t);
+template hipError_t launch_msgla_pool<float>(const MsglaParams&, hipStream_t);
+template hipError_t launch_msgla_hold<bf16>(const MsglaParams&, hipStream_t);
+template hipError_t launch_msgla_hold<float>(const MsglaParams&, hipStream_t);
+
+}  // namespace gla

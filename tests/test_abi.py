@@ -182,3 +182,20 @@ def test_gsa_read_out_validation(lib):
     for act, want in ((-1, 4), (5, 4), (0, 1), (1, 1), (2, 1), (3, 1), (4, 1)):
         assert lib.gsa_fwd(*[None] * 9, 1, 1, 64, 16, 16, 16, 16, 1, act, None, 0, None) == want
         assert lib.gsa_bwd(*[None] * 15, 1, 1, 64, 16, 16, 16, 16, 1, act, None, 0, None) == want
+
+
+def test_msgla_validation(lib):
+    """Group arrays are checked before anything else is looked at."""
+    I = lambda *xs: (ctypes.c_int * len(xs))(*xs)
+    N = [None] * 8
+    args = lambda n, sc, hd: (*N, 1, 4, 64, 64, 64, 64, 1, n, sc, hd, None, 0, None)
+    assert lib.msgla_fwd(*args(3, I(1, 2, 4), I(2, 1, 1))) == 1                 # valid groups, null tensors
+    assert lib.msgla_fwd(*args(0, I(1), I(4))) == 4                             # no group
+    assert lib.msgla_fwd(*args(9, I(*[1] * 9), I(*[1] * 9))) == 4               # more than 8 groups
+    assert lib.msgla_fwd(*args(2, I(1, 2), I(2, 1))) == 2                       # heads sum to 3, not 4
+    assert lib.msgla_fwd(*args(2, I(1, 2), I(3, 2))) == 2                       # heads sum to 5
+    assert lib.msgla_fwd(*args(2, I(0, 2), I(2, 2))) == 2                       # scale 0
+    assert lib.msgla_fwd(*args(2, I(1, 70000), I(2, 2))) == 4                   # scale too large
+    assert lib.msgla_fwd(*N, 1, 4, 64, 64, 64, 64, 1, 1, None, I(4), None, 0, None) == 1
+    assert lib.msgla_fwd_workspace_bytes(1, 4, 64, 64, 64, 64, 1, 2, I(1, 2), I(2, 1)) == 0
+    assert lib.msgla_fwd_workspace_bytes(1, 4, 64, 64, 64, 64, 1, 2, I(1, 2), I(2, 2)) > 0
