@@ -319,6 +319,43 @@ def run_gsa(torch, m, steps=10, warmup=3):
             "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / ms * 1e3, 1)}
 
 
+def run_msgla(torch, m, steps=10, warmup=3):
+    """MS-GLA {1, 2, 4} forward on the 340M-layer shape, head budget split 2/1/1, with fusion
+    weights; plain gla_fwd on the same inputs is timed beside it."""
+    w = W.WORKLOADS["gla_340m"]
+    x = W.gla_inputs(w, with_grad=False)
+    dt = torch.bfloat16
+    d = {n: torch.from_numpy(x[n]).to("cuda", dt).contiguous() for n in ("q", "k", "v", "g")}
+    wts = torch.full((w.B, w.L, 3), 1.0 / 3.0, device="cuda")
+    scales, heads = [1, 2, 4], [2, 1, 1]
+    ws = torch.empty(m.msgla_fwd_workspace_bytes(w.B, w.H, w.L, w.Dk, w.Dv, w.C, dt, scales, heads),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty(w.B, w.H, w.L, w.Dv, device="cuda", dtype=dt)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps
+
+    ms = timed(lambda: m.msgla_fwd(d["q"], d["k"], d["v"], d["g"], scales, heads, wts, C=w.C,
+                                   output_final_state=False, workspace=ws, out=o))
+    ws2 = torch.empty(m.gla_fwd_workspace_bytes(w.B, w.H, w.L, w.Dk, w.Dv, w.C, dt), dtype=torch.uint8,
+                      device="cuda")
+    ms_gla = timed(lambda: m.gla_fwd(d["q"], d["k"], d["v"], d["g"], C=w.C, output_final_state=False, out=o,
+                                     workspace=ws2))
+    return {"workload": f"ms-gla scales (1,2,4) heads (2,1,1) B={w.B} H={w.H} L={w.L} Dk={w.Dk} Dv={w.Dv} "
+                        f"C={w.C} forward",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / ms * 1e3, 1),
+            "gla_fwd_ms_same_inputs": round(ms_gla, 4)}
+
+
 # ----------------------------------------------------------------------------- summaries
 def summarize_stats(path, title, cmd, out):
     import csv
@@ -486,6 +523,7 @@ def main():
         g = run_gsa(torch, m)
         if g is not None:
             ex["gsa"] = g
+        ex["msgla"] = run_msgla(torch, m)
         out["extras"] = ex
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(r["x"], B, L)
