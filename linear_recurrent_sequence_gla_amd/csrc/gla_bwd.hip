@@ -412,6 +412,39 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   if (cs.active) {
     T* dqg = reinterpret_cast<T*>(p.dq) + qbase;
     T* dkg = reinterpret_cast<T*>(p.dk) + qbase;
+    // dq^nd and dk' per element; the path test is uniform and kept outside the element loops
+    // so that the fast path's LDS reads issue together
+    float dqn[RPS][V], dkp[RPS][V];
+    if (fast) {
+#pragma unroll
+      for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const int o = (r0 + u) * LDF + c0 + e;
+          dqn[u][e] = sDQ[o] * fast_exp2(cs.b[u][e]);
+          dkp[u][e] = sDK[o] * fast_exp2(-cs.b[u][e]);
+        }
+      }
+    } else {
+      // exact off-diagonal intra terms: every exponent b_r - b_c has r > c
+      const int cend = c0 < kvalid ? len : 0;            // padded channels: q = k = 0
+#pragma unroll
+      for (int u = 0; u < RPS; ++u) {
+        const int r = r0 + u;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const int i = c0 + e;
+          const float bb = cs.b[u][e];
+          float iq = 0.f, ik = 0.f;
+          for (int c = 0; c < cend; ++c) {
+            if (c < r) iq += to_f32(sdA[r * LDC + c]) * to_f32(kg[(size_t)c * Dk + i]) * fast_exp2(bb - sB[c * DKS + i]);
+            if (c > r) ik += to_f32(sdA[c * LDC + r]) * to_f32(qg[(size_t)c * Dk + i]) * fast_exp2(sB[c * DKS + i] - bb);
+          }
+          dqn[u][e] = sDQ[r * LDF + i] * fast_exp2(bb) + iq;
+          dkp[u][e] = ik;
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
       const int r = r0 + u;
@@ -421,26 +454,11 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
       for (int e = 0; e < V; ++e) {
         const int i = c0 + e;
         const float bb = cs.b[u][e];
-        float dqn, dkp;
-        if (fast) {
-          dqn = sDQ[r * LDF + i] * fast_exp2(bb);
-          dkp = sDK[r * LDF + i] * fast_exp2(-bb);
-        } else {
-          // exact off-diagonal intra terms: every exponent b_r - b_c has r > c
-          float iq = 0.f, ik = 0.f;
-          const int cend = c0 < kvalid ? len : 0;          // padded channels: q = k = 0
-          for (int c = 0; c < cend; ++c) {
-            if (c < r) iq += to_f32(sdA[r * LDC + c]) * to_f32(kg[(size_t)c * Dk + i]) * fast_exp2(bb - sB[c * DKS + i]);
-            if (c > r) ik += to_f32(sdA[c * LDC + r]) * to_f32(qg[(size_t)c * Dk + i]) * fast_exp2(sB[c * DKS + i] - bb);
-          }
-          dqn = sDQ[r * LDF + i] * fast_exp2(bb) + iq;
-          dkp = ik;
-        }
         const float bk = sDKI[r * LDF + i] * fast_exp2(sGam[i] - bb);
         const float qv = cs.qv[u][e], kv = cs.kv[u][e];
-        dqv[e] = from_f32<T>(dqn + dgn * kv);
-        dkv[e] = from_f32<T>(dkp + dgn * qv + bk);
-        up[u][e] = qv * dqn - kv * dkp;
+        dqv[e] = from_f32<T>(dqn[u][e] + dgn * kv);
+        dkv[e] = from_f32<T>(dkp[u][e] + dgn * qv + bk);
+        up[u][e] = qv * dqn[u][e] - kv * dkp[u][e];
         uk[u][e] = kv * bk;
       }
       if (r < len && c0 < kvalid) {

@@ -23,8 +23,12 @@
 // go on the matrix cores back to back, and the sequential part is only the element-wise fold
 // S <- Diag(2^Gamma_g) S + T_g, which also yields each stored state.  Group operands are
 // loaded into registers kWalkDepth groups ahead of use and LDS is double-buffered, so a step
-// needs one barrier per G chunks.
+// needs one barrier per G chunks.  The accumulators hold the transposed tile (the product is
+// formed as X^T M^T): a lane then owns four consecutive columns of one state row, so it needs
+// one decay factor per row and stages each stored state with one 8-byte LDS write per 16-row
+// block; the staged tile leaves in full 128-byte rows.
 #pragma once
+#include <type_traits>
 #include "prep.hpp"
 
 namespace gla {
@@ -50,7 +54,7 @@ struct WalkIOCfg {
   static constexpr size_t GT = (size_t)RT * 4;
   static constexpr size_t SLOT = KT + VT + GT;            // one chunk's operands
   static constexpr size_t STAGE = G * SLOT;               // one group's operands
-  static constexpr size_t HT = (size_t)RT * LDV * sizeof(T);
+  static constexpr size_t HT = (size_t)RT * LDV * sizeof(T);   // one staged state tile
   static constexpr size_t BYTES = 2 * STAGE + 2 * G * HT;
   static constexpr int NK = RT * CP / V, NV = CP * kDvTile / V;
   static constexpr int PKd = (NK + 255) / 256, PV = (NV + 255) / 256;
@@ -158,7 +162,8 @@ __device__ __forceinline__ size_t walk_state_index(const WalkIO& w, int bh, int 
   return w.trans ? ((size_t)bh * w.Ds + j) * w.rows + i : ((size_t)bh * w.rows + i) * w.Ds + j;
 }
 
-// T = M X on fresh accumulators (M and X from LDS): one chunk's state increment.
+// T^T = X^T M^T on fresh accumulators (M and X from LDS): one chunk's state increment, with
+// lane (col, grp) of wave w holding T[16 ib + col][16 w + 4 grp + e] in Tm[ib][e].
 template <typename T, int RT, int CP>
 __device__ __forceinline__ void walk_product(f32x4 (&Tm)[RT / 16], const T* sKT, const T* sV) {
   using W = WalkIOCfg<T, RT, CP>;
@@ -172,7 +177,7 @@ __device__ __forceinline__ void walk_product(f32x4 (&Tm)[RT / 16], const T* sKT,
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) mma(Tm[ib], ld8(sKT + (16 * ib + col) * W::LDA + 32 * cb + 8 * grp), Yv[cb]);
+    for (int ib = 0; ib < NIB; ++ib) mma(Tm[ib], Yv[cb], ld8(sKT + (16 * ib + col) * W::LDA + 32 * cb + 8 * grp));
   }
 }
 
@@ -189,8 +194,8 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkIO w, int ntile) {
   const int Ds = w.Ds, L = w.L, C = w.C, N = w.N;
   const int NG = (N + G - 1) / G;
   const int DsP = ntile * kDvTile, i0 = rt * RT;
-  const int j = tile * kDvTile + 16 * wave + col;
-  const bool jv = j < Ds;
+  const int j0 = tile * kDvTile + 16 * wave + 4 * grp;     // this lane's four columns
+  typedef typename Vec4<T>::type V4T;
   const T* src = reinterpret_cast<const T*>(w.src) + (size_t)bh * L * Ds;
   const T* mat = reinterpret_cast<const T*>(w.mat) + ((size_t)bh * N * SP + i0) * CP;
   const float* gam = w.gam + (size_t)bh * N * SP + i0;
@@ -208,8 +213,8 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkIO w, int ntile) {
   for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = i0 + 16 * ib + 4 * grp + e;
-      S[ib][e] = (w.init && jv && i < w.rows) ? w.init[walk_state_index(w, bh, i, j)] : 0.f;
+      const int i = i0 + 16 * ib + col, j = j0 + e;
+      S[ib][e] = (w.init && j < Ds && i < w.rows) ? w.init[walk_state_index(w, bh, i, j)] : 0.f;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);                   // initial state in before the pipeline starts
@@ -231,49 +236,65 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkIO w, int ntile) {
   store(st[0], 0);
   __syncthreads();
 
-  for (int q0 = 0; q0 < NG; q0 += R) {
+  // One chunk group: its products from LDS, the sequential fold (which stages each state in
+  // LDS), the next group's operands into the other LDS buffer, one barrier, the states out.  CHECK guards
+  // the ragged end; the bulk of the walk runs unguarded, so the compiler can count the loads
+  // and stores in flight exactly and never waits on the prefetch it has just issued.
+  auto body = [&](auto rc, int kg, auto cc) {
+    constexpr int r = decltype(rc)::value;
+    constexpr bool CHECK = decltype(cc)::value;
+    const int b = kg & 1;
+    load(st[r], kg + R);                         // st[r] (group kg) is already in LDS
+    f32x4 Tm[G][NIB];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int kg = q0 + r;
-      if (kg < NG) {
-        const int b = kg & 1;
-        load(st[r], kg + R);                         // st[r] (group kg) is already in LDS
-        f32x4 Tm[G][NIB];
+    for (int g = 0; g < G; ++g) walk_product<T, RT, CP>(Tm[g], sKT(b, g), sV(b, g));
 #pragma unroll
-        for (int g = 0; g < G; ++g) walk_product<T, RT, CP>(Tm[g], sKT(b, g), sV(b, g));
+    for (int g = 0; g < G; ++g) {
+      const int k = kg * G + g;
+      if (!CHECK || k < N) {
+        const float* gg = sG(b, g);
+        T* ho = sHo(b, g) + col * LDV + 16 * wave + 4 * grp;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if (kg * G + g < N) {
-            T* ho = sHo(b, g);
-            const float* gg = sG(b, g);
+        for (int ib = 0; ib < NIB; ++ib) {
+          V4T hv;
+          const float dec = fast_exp2(gg[16 * ib + col]);
 #pragma unroll
-            for (int ib = 0; ib < NIB; ++ib) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int ii = 16 * ib + 4 * grp + e;
-                ho[ii * LDV + 16 * wave + col] = from_f32<T>(S[ib][e]);
-                S[ib][e] = fast_exp2(gg[ii]) * S[ib][e] + Tm[g][ib][e];
-              }
-            }
+          for (int e = 0; e < 4; ++e) {
+            hv[e] = from_f32<T>(S[ib][e]);
+            S[ib][e] = dec * S[ib][e] + Tm[g][ib][e];
           }
-        }
-        store(st[(r + 1) % R], b ^ 1);
-        __syncthreads();
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const int k = kg * G + g;
-          if (k < N) state_tile_out<T, RT>(out + (size_t)chunk_of(k) * SP * DsP, sHo(b, g), LDV, DsP);
+          *reinterpret_cast<V4T*>(ho + 16 * ib * LDV) = hv;
         }
       }
     }
+    store(st[(r + 1) % R], b ^ 1);
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int k = kg * G + g;
+      if (!CHECK || k < N) state_tile_out<T, RT>(out + (size_t)chunk_of(k) * SP * DsP, sHo(b, g), LDV, DsP);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  static_assert(R == 2, "the walk pipeline alternates two register stages");
+  const int full = (N / G) / R * R;              // groups walked without bounds checks
+  int kg = 0;
+  for (; kg < full; kg += R) {
+    body(I0{}, kg, std::false_type{});
+    body(I1{}, kg + 1, std::false_type{});
   }
-  if (w.fin && jv) {
+  for (; kg < NG; kg += R) {
+    body(I0{}, kg, std::true_type{});
+    if (kg + 1 < NG) body(I1{}, kg + 1, std::true_type{});
+  }
+  if (w.fin) {
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = i0 + 16 * ib + 4 * grp + e;
-        if (i < w.rows) w.fin[walk_state_index(w, bh, i, j)] = S[ib][e];
+        const int i = i0 + 16 * ib + col, j = j0 + e;
+        if (i < w.rows && j < Ds) w.fin[walk_state_index(w, bh, i, j)] = S[ib][e];
       }
     }
   }
