@@ -46,21 +46,21 @@ namespace gla {
 constexpr int kBwdThreads = 512;
 
 // LDS phases of the chunk kernel:
-//   front   sdA, sdA^T [CP][CP] (written after the Dv loop, read to the end), diag of dA (fp32)
+//   front   sdA [CP][CP] (written after the Dv loop, read to the end), diag of dA (fp32)
 //   phase 1 (Dv loop)    sKd, sA (with dv) and the Dv slice tiles dO, V, H, dH (+ dV)
-//   phase 2 (intra)      Qs^T, Ks^T [DKS][CP] for the intra-chunk products
+//   phase 2 (intra)      Qs, Ks [CP][DKS] for the intra-chunk products
 //   phase 3 (epilogue)   three fp32 [CP][DKS] gradient tiles; on the exact path b takes the
 //                        place of the (unused) intra dk tile
 constexpr size_t chunk_bwd_bytes(int es, int DKS, int CP, bool dv, int nseg) {   // nseg for kBwdThreads
   const size_t V = 16 / es;
   const size_t LDQ = DKS + V, LDC = CP + V, LDV = kDvTile + V, LDF = DKS + 4;
   const size_t QT = CP * LDQ * es, CT = CP * LDC * es, VT = CP * LDV * es, HT = DKS * LDV * es;
-  const size_t TT = DKS * LDC * es, FT = CP * LDF * 4;
+  const size_t FT = CP * LDF * 4;
   const size_t ph1 = (dv ? QT + CT : 0) + 2 * VT + 2 * HT + (dv ? VT : 0);
-  const size_t ph2 = 2 * TT;
+  const size_t ph2 = 2 * QT;
   const size_t ph3 = 3 * FT;
   const size_t mx = ph1 > ph2 ? (ph1 > ph3 ? ph1 : ph3) : (ph2 > ph3 ? ph2 : ph3);
-  return 2 * CT + mx + (size_t)(2 * nseg * DKS + 2 * DKS + CP + 8) * 4;
+  return CT + mx + (size_t)(2 * nseg * DKS + 2 * DKS + CP + 8) * 4;
 }
 
 template <typename T, int DKS, int CP, bool WITH_DV>
@@ -73,12 +73,11 @@ struct BwdChunkCfg {
   static constexpr size_t CT = (size_t)CP * LDC * sizeof(T);
   static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
   static constexpr size_t HT = (size_t)DKS * LDV * sizeof(T);
-  static constexpr size_t TT = (size_t)DKS * LDC * sizeof(T);
   static constexpr size_t FT = (size_t)CP * LDF * 4;
   static constexpr size_t PH1 = (WITH_DV ? QT + CT : 0) + 2 * VT + 2 * HT + (WITH_DV ? VT : 0);
-  static constexpr size_t PH2 = 2 * TT;
+  static constexpr size_t PH2 = 2 * QT;
   static constexpr size_t PH3 = 3 * FT;
-  static constexpr size_t MAIN = 2 * CT + cmax(cmax(PH1, PH2), PH3);
+  static constexpr size_t MAIN = CT + cmax(cmax(PH1, PH2), PH3);
   static constexpr size_t BYTES = chunk_bwd_bytes(sizeof(T), DKS, CP, WITH_DV, M::NSEG);
   static constexpr int NV = CP * kDvTile / V, NH = DKS * kDvTile / V;
   static constexpr int PV = (NV + NT - 1) / NT, PH = (NH + NT - 1) / NT;
@@ -189,8 +188,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
   T* sdA = reinterpret_cast<T*>(smem);                            // strictly lower dA
-  T* sdAT = sdA + CP * LDC;                                       // its transpose
-  char* rmain = smem + 2 * Cf::CT;
+  char* rmain = smem + Cf::CT;
   // phase 1
   T* sKd = reinterpret_cast<T*>(rmain);                           // WITH_DV only
   T* sA = sKd + (WITH_DV ? CP * LDQ : 0);                         // WITH_DV only
@@ -200,8 +198,8 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   T* sdH = sH + DKS * LDV;
   T* sdV = sdH + DKS * LDV;                                       // WITH_DV only
   // phase 2 (aliases phase 1)
-  T* sQsT = reinterpret_cast<T*>(rmain);                          // (q 2^b)^T  [DKS][CP]
-  T* sKsT = sQsT + DKS * LDC;                                     // (k 2^-b)^T
+  T* sQs = reinterpret_cast<T*>(rmain);                           // q 2^b   [CP][DKS]
+  T* sKs = sQs + CP * LDQ;                                        // k 2^-b
   // phase 3 (aliases phases 1 and 2)
   float* sDQ = reinterpret_cast<float*>(rmain);                   // dq^nd / 2^b
   float* sDK = sDQ + CP * LDF;                                    // dk'  / 2^-b (fast path)
@@ -339,8 +337,9 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
     }
   }
 
-  // strictly lower dA and its transpose -> LDS, the diagonal kept apart in fp32; on the
-  // factorised path also Qs^T and Ks^T (the phase-1 tiles are dead here)
+  // strictly lower dA -> LDS, the diagonal kept apart in fp32; on the factorised path also
+  // Qs and Ks (the phase-1 tiles are dead here).  The intra products read dA^T, Qs^T and Ks^T
+  // as column runs of these tiles through transposing LDS reads.
 #pragma unroll
   for (int s = 0; s < PA; ++s) {
     const int blk = wave + NW * s;
@@ -351,7 +350,6 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
         const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
         const T x = from_f32<T>(c < r ? accA[s][e] : 0.f);
         sdA[r * LDC + c] = x;
-        sdAT[c * LDC + r] = x;
         if (c == r) sDiag[r] = accA[s][e];
       }
     }
@@ -359,11 +357,14 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   if (fast && cs.active) {
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
+      VT qs, ks;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        sQsT[(c0 + e) * LDC + r0 + u] = from_f32<T>(cs.qv[u][e] * fast_exp2(cs.b[u][e]));
-        sKsT[(c0 + e) * LDC + r0 + u] = from_f32<T>(cs.kv[u][e] * fast_exp2(-cs.b[u][e]));
+        qs[e] = from_f32<T>(cs.qv[u][e] * fast_exp2(cs.b[u][e]));
+        ks[e] = from_f32<T>(cs.kv[u][e] * fast_exp2(-cs.b[u][e]));
       }
+      *reinterpret_cast<VT*>(sQs + (r0 + u) * LDQ + c0) = qs;
+      *reinterpret_cast<VT*>(sKs + (r0 + u) * LDQ + c0) = ks;
     }
   }
   __syncthreads();
@@ -376,9 +377,9 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
 #pragma unroll
         for (int kc = 0; kc < CP / 32; ++kc) {
           mma(accQ[s], ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp),
-              ld8(sKsT + (16 * ib + col) * LDC + 32 * kc + 8 * grp));
-          mma(accK[s], ld8(sdAT + (16 * rb + col) * LDC + 32 * kc + 8 * grp),
-              ld8(sQsT + (16 * ib + col) * LDC + 32 * kc + 8 * grp));
+              ld8_colblk(sKs + (32 * kc) * LDQ + 16 * ib, LDQ));
+          mma(accK[s], ld8_colblk(sdA + (32 * kc) * LDC + 16 * rb, LDC),
+              ld8_colblk(sQs + (32 * kc) * LDQ + 16 * ib, LDQ));
         }
       }
     }
