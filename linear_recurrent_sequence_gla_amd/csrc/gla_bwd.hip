@@ -258,6 +258,9 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   st.store(sdO, sV, sH, sdH);
   __syncthreads();
 
+  // accA holds dA blocks as they are; accQ, accK, accKI hold their blocks transposed (the
+  // products are formed with the operands swapped), so a lane owns four consecutive channels of
+  // one row and moves them with a single 16-byte LDS write
   f32x4 accA[PA], accQ[PQ], accK[PQ], accKI[PQ];
 #pragma unroll
   for (int s = 0; s < PA; ++s) accA[s] = zero4();
@@ -283,8 +286,8 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
         const int rb = blk / NIB, ib = blk % NIB;
 #pragma unroll
         for (int kb = 0; kb < kDvTile / 32; ++kb) {
-          mma(accQ[s], ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp), ld8(sH + (16 * ib + col) * LDV + 32 * kb + 8 * grp));
-          mma(accKI[s], ld8(sV + (16 * rb + col) * LDV + 32 * kb + 8 * grp), ld8(sdH + (16 * ib + col) * LDV + 32 * kb + 8 * grp));
+          mma(accQ[s], ld8(sH + (16 * ib + col) * LDV + 32 * kb + 8 * grp), ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
+          mma(accKI[s], ld8(sdH + (16 * ib + col) * LDV + 32 * kb + 8 * grp), ld8(sV + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
         }
       }
     }
@@ -376,10 +379,10 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
         const int rb = blk / NIB, ib = blk % NIB;
 #pragma unroll
         for (int kc = 0; kc < CP / 32; ++kc) {
-          mma(accQ[s], ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp),
-              ld8_colblk(sKs + (32 * kc) * LDQ + 16 * ib, LDQ));
-          mma(accK[s], ld8_colblk(sdA + (32 * kc) * LDC + 16 * rb, LDC),
-              ld8_colblk(sQs + (32 * kc) * LDQ + 16 * ib, LDQ));
+          mma(accQ[s], ld8_colblk(sKs + (32 * kc) * LDQ + 16 * ib, LDQ),
+              ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp));
+          mma(accK[s], ld8_colblk(sQs + (32 * kc) * LDQ + 16 * ib, LDQ),
+              ld8_colblk(sdA + (32 * kc) * LDC + 16 * rb, LDC));
         }
       }
     }
@@ -390,13 +393,10 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
     const int blk = wave + NW * s;
     if (blk < NQ_BLK) {
       const int rb = blk / NIB, ib = blk % NIB;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int o = (16 * rb + 4 * grp + e) * LDF + 16 * ib + col;
-        sDQ[o] = accQ[s][e];
-        if (fast) sDK[o] = accK[s][e];
-        sDKI[o] = accKI[s][e];
-      }
+      const int o = (16 * rb + col) * LDF + 16 * ib + 4 * grp;   // four consecutive channels
+      *reinterpret_cast<f32x4*>(sDQ + o) = accQ[s];
+      if (fast) *reinterpret_cast<f32x4*>(sDK + o) = accK[s];
+      *reinterpret_cast<f32x4*>(sDKI + o) = accKI[s];
     }
   }
   if (!fast && cs.active) {
