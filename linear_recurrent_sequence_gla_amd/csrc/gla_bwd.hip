@@ -258,9 +258,9 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   st.store(sdO, sV, sH, sdH);
   __syncthreads();
 
-  // accA holds dA blocks as they are; accQ, accK, accKI hold their blocks transposed (the
-  // products are formed with the operands swapped), so a lane owns four consecutive channels of
-  // one row and moves them with a single 16-byte LDS write
+  // The accumulators hold their blocks transposed (the products are formed with the operands
+  // swapped), so a lane owns four consecutive columns of one row and moves them to LDS with a
+  // single 8- or 16-byte write
   f32x4 accA[PA], accQ[PQ], accK[PQ], accKI[PQ];
 #pragma unroll
   for (int s = 0; s < PA; ++s) accA[s] = zero4();
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
         const int rb = blk / NBR, cb = blk % NBR;
 #pragma unroll
         for (int kb = 0; kb < kDvTile / 32; ++kb)
-          mma(accA[s], ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp), ld8(sV + (16 * cb + col) * LDV + 32 * kb + 8 * grp));
+          mma(accA[s], ld8(sV + (16 * cb + col) * LDV + 32 * kb + 8 * grp), ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
       }
     }
 #pragma unroll
@@ -300,14 +300,17 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
           f32x4 acc = zero4();
 #pragma unroll
           for (int kr = 0; kr < CP / 32; ++kr)
-            mma(acc, ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC),
-                ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV));
+            mma(acc, ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV),
+                ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC));
 #pragma unroll
           for (int ki = 0; ki < DKS / 32; ++ki)
-            mma(acc, ld8(sKd + (16 * cb + col) * LDQ + 32 * ki + 8 * grp),
-                ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV));
+            mma(acc, ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV),
+                ld8(sKd + (16 * cb + col) * LDQ + 32 * ki + 8 * grp));
+          // transposed block: this lane holds dV[16 cb + col][16 jb + 4 grp + e]
+          typename Vec4<T>::type dv4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sdV[(16 * cb + 4 * grp + e) * LDV + 16 * jb + col] = from_f32<T>(acc[e]);
+          for (int e = 0; e < 4; ++e) dv4[e] = from_f32<T>(acc[e]);
+          *reinterpret_cast<typename Vec4<T>::type*>(sdV + (16 * cb + col) * LDV + 16 * jb + 4 * grp) = dv4;
         }
       }
     }
@@ -348,13 +351,16 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
     const int blk = wave + NW * s;
     if (blk < NA_BLK) {
       const int rb = blk / NBR, cb = blk % NBR;
+      // transposed block: this lane holds dA[16 rb + col][16 cb + 4 grp + e]
+      const int r = 16 * rb + col;
+      typename Vec4<T>::type a4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
-        const T x = from_f32<T>(c < r ? accA[s][e] : 0.f);
-        sdA[r * LDC + c] = x;
+        const int c = 16 * cb + 4 * grp + e;
+        a4[e] = from_f32<T>(c < r ? accA[s][e] : 0.f);
         if (c == r) sDiag[r] = accA[s][e];
       }
+      *reinterpret_cast<typename Vec4<T>::type*>(sdA + r * LDC + 16 * cb + 4 * grp) = a4;
     }
   }
   if (fast && cs.active) {
