@@ -236,6 +236,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   ATileStage<T, CP, NT> at;
   if constexpr (WITH_DV) at.load(reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP);
   const float maxb = cs.finish(segtot, sGam, red);
+  cs.kvals();                            // q is converted after the Dv loop, where it is first needed
   const bool fast = maxb <= kSpanLimit;
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
 
@@ -342,6 +343,8 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
       if (idx < Cf::NH && idx % PER_ROW == 0) sZ[r] = r < kvalid ? z * fast_exp2(sGam[r]) : 0.f;
     }
   }
+
+  cs.qvals();
 
   // strictly lower dA -> LDS, the diagonal kept apart in fp32; on the factorised path also
   // Qs and Ks (the phase-1 tiles are dead here).  The intra products read dA^T, Qs^T and Ks^T

@@ -163,13 +163,14 @@ __device__ __forceinline__ void seg_scan_channel(float* a, int width, int ch, bo
   }
 }
 
-// Chunk-local gate scan for the thread's (channel group, row segment): loads g, q, k
-// vectors (16-byte, all issued before first use), keeps b (log2 units) and the raw q and k
-// of its rows and channels, publishes Gamma in sGam and returns the block-wide max |b|.
+// Chunk-local gate scan for the thread's (channel group, row segment): loads g, k, q
+// vectors (16-byte, all issued before first use, g first), keeps b (log2 units) and the raw q
+// and k of its rows and channels, publishes Gamma in sGam and returns the block-wide max |b|.
 // load() only issues the loads -- unconditionally, from clamped in-bounds addresses, with the
 // validity kept beside them -- so a kernel can put other independent loads in flight before
-// finish() consumes these.  run() is load() then finish().  finish() must be called by all
-// NT threads.  With LOAD_QK = false only g is loaded, and qv holds the raw gate values.
+// finish() consumes the gates; kvals() and qvals() convert k and q when they are needed.
+// run() is load(), finish(), kvals() and qvals().  finish() must be called by all NT threads.
+// With LOAD_QK = false only g is loaded, and qv holds the raw gate values.
 template <typename T, int DKP, int CP, bool LOAD_QK = true, int NT = 256>
 struct ChunkScan {
   using M = ChunkMap<T, DKP, CP, NT>;
@@ -191,15 +192,40 @@ struct ChunkScan {
     active = tid < M::ACTIVE;
     const bool chv = active && cg * V < width;
     const int cc = chv ? cg * V : 0;
+    // g first: the scan needs only the gates, and loads complete in issue order
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
       const int r = seg * RPS + u;
       ok[u] = chv && r < len;
-      const size_t off = (size_t)min(r, len - 1) * ld + cc;
-      gvec[u] = *reinterpret_cast<const VT*>(gg + off);
-      if constexpr (LOAD_QK) {
-        qvec[u] = *reinterpret_cast<const VT*>(qg + off);
-        kvec[u] = *reinterpret_cast<const VT*>(kg + off);
+      gvec[u] = *reinterpret_cast<const VT*>(gg + (size_t)min(r, len - 1) * ld + cc);
+    }
+    if constexpr (LOAD_QK) {
+#pragma unroll
+      for (int u = 0; u < RPS; ++u)
+        kvec[u] = *reinterpret_cast<const VT*>(kg + (size_t)min(seg * RPS + u, len - 1) * ld + cc);
+#pragma unroll
+      for (int u = 0; u < RPS; ++u)
+        qvec[u] = *reinterpret_cast<const VT*>(qg + (size_t)min(seg * RPS + u, len - 1) * ld + cc);
+    }
+  }
+
+  // k and q as fp32 (zero outside the chunk and the channel range); separate from finish() so
+  // that the scan does not wait for them
+  __device__ __forceinline__ void kvals() {
+    if constexpr (LOAD_QK) {
+#pragma unroll
+      for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) kv[u][e] = ok[u] ? to_f32(kvec[u][e]) : 0.f;
+      }
+    }
+  }
+  __device__ __forceinline__ void qvals() {
+    if constexpr (LOAD_QK) {
+#pragma unroll
+      for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) qv[u][e] = ok[u] ? to_f32(qvec[u][e]) : 0.f;
       }
     }
   }
@@ -215,10 +241,7 @@ struct ChunkScan {
         const float gv = ok[u] ? to_f32(gvec[u][e]) : 0.f;
         run_[e] += gv * kLog2e;
         b[u][e] = run_[e];
-        if constexpr (LOAD_QK) {
-          qv[u][e] = ok[u] ? to_f32(qvec[u][e]) : 0.f;
-          kv[u][e] = ok[u] ? to_f32(kvec[u][e]) : 0.f;
-        } else {
+        if constexpr (!LOAD_QK) {
           qv[u][e] = gv;
           kv[u][e] = 0.f;
         }
@@ -255,7 +278,10 @@ struct ChunkScan {
   __device__ __forceinline__ float run(const T* qg, const T* kg, const T* gg, int ld, int width, int len,
                                        float* segtot, float* sGam, float* red) {
     load(qg, kg, gg, ld, width, len);
-    return finish(segtot, sGam, red);
+    const float mx = finish(segtot, sGam, red);
+    kvals();
+    qvals();
+    return mx;
   }
 };
 
