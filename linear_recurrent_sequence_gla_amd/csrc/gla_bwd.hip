@@ -53,7 +53,7 @@ constexpr int kBwdThreads = 512;
 //                        place of the (unused) intra dk tile
 constexpr size_t chunk_bwd_bytes(int es, int DKS, int CP, bool dv, int nseg) {   // nseg for kBwdThreads
   const size_t V = 16 / es;
-  const size_t LDQ = DKS + V, LDC = CP + V, LDV = kDvTile + V, LDF = DKS + 4;
+  const size_t LDQ = DKS + 2 * V, LDC = CP + 2 * V, LDV = kDvTile + 2 * V, LDF = DKS + 4;
   const size_t QT = CP * LDQ * es, CT = CP * LDC * es, VT = CP * LDV * es, HT = DKS * LDV * es;
   const size_t FT = CP * LDF * 4;
   const size_t ph1 = (dv ? QT + CT : 0) + 2 * VT + 2 * HT + (dv ? VT : 0);
@@ -68,7 +68,9 @@ struct BwdChunkCfg {
   static constexpr int NT = kBwdThreads;
   using M = ChunkMap<T, DKS, CP, NT>;
   static constexpr int V = 16 / (int)sizeof(T);
-  static constexpr int LDQ = DKS + V, LDC = CP + V, LDV = kDvTile + V, LDF = DKS + 4;
+  // 32-byte row pads: the four rows a transposing LDS read touches per 16 lanes then fall in
+  // disjoint bank windows, which the 16-byte pads of the other kernels do not give here
+  static constexpr int LDQ = DKS + 2 * V, LDC = CP + 2 * V, LDV = kDvTile + 2 * V, LDF = DKS + 4;
   static constexpr size_t QT = (size_t)CP * LDQ * sizeof(T);
   static constexpr size_t CT = (size_t)CP * LDC * sizeof(T);
   static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
