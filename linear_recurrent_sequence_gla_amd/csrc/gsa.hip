@@ -45,12 +45,14 @@ struct GsaCfg {
   static constexpr size_t QKT = (size_t)CP * LDQK * 4;
   static constexpr size_t ST_C = (size_t)CP * LDS * sizeof(T);
   static constexpr size_t ST_M = (size_t)MP * LDS * sizeof(T);
-  // gsa_p: sB, sW, sQK, then slices (q, k, S1^T) aliased by the P staging tile
-  static constexpr size_t P_BYTES = 2 * FT + QKT + cmax(2 * ST_C + ST_M, (size_t)CP * LDM * sizeof(T)) +
-                                    (size_t)(M::NSEG * MP + MP + 8) * 4;
-  // gsa_pass1_bwd: sB, sW, sdZ, then {sdQK + slices} aliased by {sQK + three fp32 tiles}
+  // gsa_p: sB, sW, then the slices (q, k, S1^T), which sQK and the P staging tile replace
+  // once the Dk loop is done.  Under 80 KB for bf16, so that two workgroups share a CU.
+  static constexpr size_t P_REGION = cmax(2 * ST_C + ST_M, QKT + (size_t)CP * LDM * sizeof(T));
+  static constexpr size_t P_BYTES = 2 * FT + P_REGION + (size_t)(M::NSEG * MP + MP + 8) * 4;
+  // gsa_pass1_bwd: sB, sW, sdZ, then {sdQK + slices} aliased by {sQK + three fp32 tiles}; the
+  // tail holds the scan totals, Gamma, Z1, the block-max scratch and the dQK diagonal
   static constexpr size_t B_REGION = cmax(QKT + 4 * ST_C + 2 * ST_M, QKT + 3 * FT);
-  static constexpr size_t B_BYTES = 3 * FT + B_REGION + (size_t)(2 * M::NSEG * MP + 2 * MP + 8) * 4;
+  static constexpr size_t B_BYTES = 3 * FT + B_REGION + (size_t)(2 * M::NSEG * MP + 2 * MP + 8 + CP) * 4;
 };
 
 // ----------------------------------------------------------------------------- prep
@@ -93,26 +95,37 @@ __global__ __launch_bounds__(256) void gsa_prep_kernel(GsaParams p) {
   if (threadIdx.x < MP) p.Gam[chunk * MP + threadIdx.x] = sGam[threadIdx.x];
 }
 
-// Stage a [rows][64] slice of a row-major [*, ld] tensor (rows < nrows, columns < ncols
-// valid, zero elsewhere) into LDS with row stride lds.
-template <typename T>
-__device__ __forceinline__ void slice_in(T* dst, int lds, const T* src, size_t ld, int rows, int nrows, int col0,
-                                         int ncols) {
-  constexpr int V = V16<T>::N;
+// A [ROWS][64] column slice of a row-major [*, ld] tensor held in registers, 16 bytes per
+// vector, vector j of thread t covering row (t + 256 j) / 8 (bf16; / 16 for fp32).  Rows
+// < nrows and columns < ncols are valid.  load() clamps its addresses into that range, so its
+// loads are unconditional and can be issued one slice ahead of their use; store() writes the
+// slice into LDS with zeros outside the valid range.
+template <typename T, int ROWS>
+struct SliceRegs {
+  static constexpr int V = V16<T>::N, PER_ROW = kDvTile / V, N = ROWS * PER_ROW / 256;
+  static_assert(N >= 1 && ROWS * PER_ROW % 256 == 0, "slice rows");
   typedef typename V16<T>::type VT;
-  constexpr int PER_ROW = kDvTile / V;
-  for (int idx = threadIdx.x; idx < rows * PER_ROW; idx += 256) {
-    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
-    const int cc = col0 + c;
-    *reinterpret_cast<VT*>(dst + r * lds + c) =
-        (r < nrows && cc < ncols) ? *reinterpret_cast<const VT*>(src + (size_t)r * ld + cc) : zero_vec<T>();
+  VT x[N];
+  __device__ __forceinline__ void load(const T* src, size_t ld, int nrows, int col0, int ncols) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = threadIdx.x + 256 * j, r = idx / PER_ROW, c = col0 + (idx % PER_ROW) * V;
+      x[j] = *reinterpret_cast<const VT*>(src + (size_t)min(r, nrows - 1) * ld + min(c, ncols - V));
+    }
   }
-}
+  __device__ __forceinline__ void store(T* dst, int lds, int nrows, int col0, int ncols) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int idx = threadIdx.x + 256 * j, r = idx / PER_ROW, c = (idx % PER_ROW) * V;
+      *reinterpret_cast<VT*>(dst + r * lds + c) = (r < nrows && col0 + c < ncols) ? x[j] : zero_vec<T>();
+    }
+  }
+};
 
 // ----------------------------------------------------------------------------- pass 1 forward
 // Z = E * (QK (W Ei) + Q S1_n), P = softmax_slots(Z), written as the [L][m] queries of pass 2.
 template <typename T, int MP, int CP>
-__global__ __launch_bounds__(256) void gsa_p_kernel(GsaParams p) {
+__global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
   using G = GsaCfg<T, MP, CP>;
   using M = ChunkMap<T, MP, CP>;
   constexpr int V = M::V, RPS = M::RPS;
@@ -121,23 +134,34 @@ __global__ __launch_bounds__(256) void gsa_p_kernel(GsaParams p) {
   __shared__ __attribute__((aligned(16))) char smem[G::P_BYTES];
   float* sB = reinterpret_cast<float*>(smem);
   float* sW = sB + CP * LDF;                  // Ws = W 2^-b (fast) or W (exact path)
-  float* sQK = sW + CP * LDF;
-  T* sq = reinterpret_cast<T*>(smem + 2 * G::FT + G::QKT);
+  char* reg = smem + 2 * G::FT;
+  T* sq = reinterpret_cast<T*>(reg);          // during the Dk loop
   T* sk = sq + CP * LDS;
   T* sS1 = sk + CP * LDS;
-  T* sP = sq;                                 // after the slice loop
-  float* segtot = reinterpret_cast<float*>(smem + G::P_BYTES - (size_t)(M::NSEG * MP + MP + 8) * 4);
+  float* sQK = reinterpret_cast<float*>(reg);  // after it
+  T* sP = reinterpret_cast<T*>(reg + G::QKT);
+  float* segtot = reinterpret_cast<float*>(smem + 2 * G::FT + G::P_REGION);
   float* sGam = segtot + M::NSEG * MP;
   float* red = sGam + MP;
 
-  const int n = blockIdx.x, bh = blockIdx.y, m = p.m, Dk = p.Dk;
+  const int n = blockIdx.x, bh = blockIdx.y, m = p.m, Dk = p.Dk, DkP = p.DkP;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int row0 = n * p.C, len = min(p.C, p.L - row0);
   const size_t chunk = (size_t)bh * p.N + n;
   const size_t gbase = ((size_t)bh * p.L + row0) * m;
   const T* gg = reinterpret_cast<const T*>(p.g) + gbase;
+  const T* qg = reinterpret_cast<const T*>(p.q) + ((size_t)bh * p.L + row0) * Dk;
+  const T* kg = reinterpret_cast<const T*>(p.k) + ((size_t)bh * p.L + row0) * Dk;
+  const T* s1 = reinterpret_cast<const T*>(p.S1s) + chunk * MP * DkP;
   ChunkScan<T, MP, CP, false> cs;
-  const bool fast = cs.run(gg, gg, gg, m, m, len, segtot, sGam, red) <= kSpanLimit;
+  cs.load(gg, gg, gg, m, m, len);
+  // the first Dk slice is in flight while the gates are scanned
+  SliceRegs<T, CP> rq, rk;
+  SliceRegs<T, MP> rs;
+  rq.load(qg, Dk, len, 0, Dk);
+  rk.load(kg, Dk, len, 0, Dk);
+  rs.load(s1, DkP, MP, 0, DkP);
+  const bool fast = cs.finish(segtot, sGam, red) <= kSpanLimit;
   if (cs.active) {
     const int c0 = cs.cg * V, r0 = cs.seg * RPS;
 #pragma unroll
@@ -158,15 +182,17 @@ __global__ __launch_bounds__(256) void gsa_p_kernel(GsaParams p) {
   for (int c = 0; c < NRB; ++c) accQK[c] = zero4();
 #pragma unroll
   for (int s = 0; s < NSB; ++s) accZe[s] = zero4();
-  const T* qg = reinterpret_cast<const T*>(p.q) + ((size_t)bh * p.L + row0) * Dk;
-  const T* kg = reinterpret_cast<const T*>(p.k) + ((size_t)bh * p.L + row0) * Dk;
-  const int DkP = p.DkP;
-  const T* s1 = reinterpret_cast<const T*>(p.S1s) + chunk * MP * DkP;
-  for (int ds = 0; ds < DkP / kDvTile; ++ds) {
+  const int nds = DkP / kDvTile;
+  for (int ds = 0; ds < nds; ++ds) {
     __syncthreads();
-    slice_in<T>(sq, LDS, qg, Dk, CP, len, ds * kDvTile, Dk);
-    slice_in<T>(sk, LDS, kg, Dk, CP, len, ds * kDvTile, Dk);
-    slice_in<T>(sS1, LDS, s1, DkP, MP, MP, ds * kDvTile, DkP);
+    rq.store(sq, LDS, len, ds * kDvTile, Dk);
+    rk.store(sk, LDS, len, ds * kDvTile, Dk);
+    rs.store(sS1, LDS, MP, ds * kDvTile, DkP);
+    if (ds + 1 < nds) {
+      rq.load(qg, Dk, len, (ds + 1) * kDvTile, Dk);
+      rk.load(kg, Dk, len, (ds + 1) * kDvTile, Dk);
+      rs.load(s1, DkP, MP, (ds + 1) * kDvTile, DkP);
+    }
     __syncthreads();
     if (rbv) {
 #pragma unroll
@@ -180,6 +206,7 @@ __global__ __launch_bounds__(256) void gsa_p_kernel(GsaParams p) {
       }
     }
   }
+  __syncthreads();   // sQK and sP take the slices' bytes
   if (rbv) {
 #pragma unroll
     for (int cb = 0; cb < NRB; ++cb) {
@@ -229,7 +256,6 @@ __global__ __launch_bounds__(256) void gsa_p_kernel(GsaParams p) {
       }
     }
   }
-  __syncthreads();   // sP aliases the slice tiles: every wave is past its last slice read
   if (rbv && p.act != kActSoftmax) {
     // element-wise read-out; the backward keeps the scores Z, from which it forms f'(Z)
 #pragma unroll
@@ -353,22 +379,24 @@ template <typename T, int MP, int CP>
 __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk) {
   using G = GsaCfg<T, MP, CP>;
   using M = ChunkMap<T, MP, CP>;
-  constexpr int V = M::V, RPS = M::RPS, NSEG = M::NSEG;
+  constexpr int V = M::V, RPS = M::RPS, NSEG = M::NSEG, NCG = M::NCG;
   constexpr int LDF = G::LDF, LDQK = G::LDQK, LDS = G::LDS, NRB = G::NRB, NSB = G::NSB;
   typedef typename V16<T>::type VT;
+  using SC = SliceRegs<T, CP>;
+  using SM = SliceRegs<T, MP>;
   __shared__ __attribute__((aligned(16))) char smem[G::B_BYTES];
   float* sB = reinterpret_cast<float*>(smem);
   float* sW = sB + CP * LDF;
   float* sdZ = sW + CP * LDF;
   char* reg = smem + 3 * G::FT;
-  float* sdQK = reinterpret_cast<float*>(reg);             // during the slice loop
+  float* sdQK = reinterpret_cast<float*>(reg);             // until the Dk loop
   T* sq = reinterpret_cast<T*>(reg + G::QKT);
   T* sk = sq + CP * LDS;
   T* sS1 = sk + CP * LDS;
   T* sdS1 = sS1 + MP * LDS;
   T* sDQ = sdS1 + MP * LDS;
   T* sDK = sDQ + CP * LDS;
-  float* sQK = reinterpret_cast<float*>(reg);              // after the slice loop
+  float* sQK = reinterpret_cast<float*>(reg);              // after the Dk loop
   float* sU = sQK + CP * LDQK;
   float* sY = sU + CP * LDF;
   float* sD = sY + CP * LDF;
@@ -376,6 +404,7 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
   float* sGam = segtot + 2 * NSEG * MP;
   float* sZ1 = sGam + MP;
   float* red = sZ1 + MP;
+  float* sDiag = red + 8;
 
   const int n = blockIdx.x, bh = blockIdx.y, m = p.m, Dk = p.Dk, DkP = p.DkP;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
@@ -384,29 +413,82 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
   const size_t gbase = ((size_t)bh * p.L + row0) * m;
   const size_t kbase = ((size_t)bh * p.L + row0) * Dk;
   const T* gg = reinterpret_cast<const T*>(p.g) + gbase;
+  const T* qg = reinterpret_cast<const T*>(p.q) + kbase;
+  const T* kg = reinterpret_cast<const T*>(p.k) + kbase;
+  const T* s1 = reinterpret_cast<const T*>(p.S1s) + chunk * MP * DkP;
+  const T* ds1 = reinterpret_cast<const T*>(p.dS1s) + chunk * MP * DkP;
+  T* dqg = reinterpret_cast<T*>(p.dq) + kbase;
+  T* dkg = reinterpret_cast<T*>(p.dk) + kbase;
 
   ChunkScan<T, MP, CP, false> cs;
-  const bool fast = cs.run(gg, gg, gg, m, m, len, segtot, sGam, red) <= kSpanLimit;
+  cs.load(gg, gg, gg, m, m, len);
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
+  // dZ in the scan's layout and the first Dk slice: in flight while the gates are scanned
+  f32x4 dzv[RPS][V / 4];
+  {
+    const int cc = (cs.active && c0 < m) ? c0 : 0;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const float* src = p.dZ + gbase + (size_t)min(r0 + u, len - 1) * m + cc;
+#pragma unroll
+      for (int e4 = 0; e4 < V / 4; ++e4) dzv[u][e4] = *reinterpret_cast<const f32x4*>(src + 4 * e4);
+    }
+  }
+  SC rq, rk;
+  SM rs, rd;
+  rq.load(qg, Dk, len, 0, Dk);
+  rk.load(kg, Dk, len, 0, Dk);
+  rs.load(s1, DkP, MP, 0, DkP);
+  rd.load(ds1, DkP, MP, 0, DkP);
+  const bool fast = cs.finish(segtot, sGam, red) <= kSpanLimit;
+  // diagonal of dQK, sum_s dZ w per row.  For the softmax it equals -sum_s dZ alpha, since
+  // sum_s dZ = 0 (its Jacobian); that form scales with alpha instead of cancelling.
+  float dsum[RPS];
+#pragma unroll
+  for (int u = 0; u < RPS; ++u) dsum[u] = 0.f;
   if (cs.active) {
-    const float* dZg = p.dZ + gbase;
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
       const int r = r0 + u;
       const bool ok = r < len && c0 < m;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
+        const float w = -expm1f(cs.qv[u][e]);
+        const float dz = ok ? dzv[u][e >> 2][e & 3] : 0.f;
         sB[r * LDF + c0 + e] = cs.b[u][e];
-        sW[r * LDF + c0 + e] = -expm1f(cs.qv[u][e]);
-        sdZ[r * LDF + c0 + e] = ok ? dZg[(size_t)r * m + c0 + e] : 0.f;
+        sW[r * LDF + c0 + e] = w;
+        sdZ[r * LDF + c0 + e] = dz;
+        dsum[u] += p.act == kActSoftmax ? -dz * (1.f - w) : dz * w;
       }
     }
+  }
+#pragma unroll
+  for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+    for (int o = 1; o < NCG; o <<= 1) dsum[u] += __shfl_xor(dsum[u], o, 64);
+  }
+  if (cs.active && cs.cg == 0) {
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) sDiag[r0 + u] = dsum[u];
   }
   __syncthreads();
   const int rb = wave;
   const bool rbv = rb < NRB;
 
-  // ---- dQK = mask_{c<=r}((dZ E)(W Ei)^T)
+  // (dZ E) on this lane's operand row 16 rb + col: the row operand of dQK and of dq's state term
+  float dze[MP / 32][8];
+  if (rbv) {
+#pragma unroll
+    for (int ks = 0; ks < MP / 32; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 16 * rb + col, s = 32 * ks + 8 * grp + e;
+        dze[ks][e] = sdZ[r * LDF + s] * fast_exp2(sB[r * LDF + s]);
+      }
+    }
+  }
+
+  // ---- dQK = mask_{c<=r}((dZ E)(W Ei)^T), with the diagonal from sDiag
   if (rbv) {
 #pragma unroll
     for (int cb = 0; cb < NRB; ++cb) {
@@ -415,22 +497,20 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
         if (fast) {
 #pragma unroll
           for (int ks = 0; ks < MP / 32; ++ks) {
-            float xa[8], xb[8];
+            float xb[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int s = 32 * ks + 8 * grp + e;
-              const int r = 16 * rb + col, c = 16 * cb + col;
-              xa[e] = sdZ[r * LDF + s] * fast_exp2(sB[r * LDF + s]);
+              const int s = 32 * ks + 8 * grp + e, c = 16 * cb + col;
               xb[e] = sW[c * LDF + s] * fast_exp2(-sB[c * LDF + s]);
             }
-            mma3(acc, hilo<T>(xa), hilo<T>(xb));
+            mma3(acc, hilo<T>(dze[ks]), hilo<T>(xb));
           }
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
             float x = 0.f;
-            if (c <= r)
+            if (c < r)
               for (int s = 0; s < m; ++s)
                 x += sdZ[r * LDF + s] * sW[c * LDF + s] * fast_exp2(sB[r * LDF + s] - sB[c * LDF + s]);
             acc[e] = x;
@@ -440,50 +520,68 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
-        float x = c <= r ? acc[e] : 0.f;
-        if (c == r) {
-          // diagonal: sum_s dZ w, in fp32.  For the softmax it equals -sum_s dZ alpha, since
-          // sum_s dZ = 0 (its Jacobian); that form scales with alpha instead of cancelling
-          x = 0.f;
-          if (p.act == kActSoftmax) {
-            for (int s = 0; s < m; ++s) x -= sdZ[r * LDF + s] * (1.f - sW[r * LDF + s]);
-          } else {
-            for (int s = 0; s < m; ++s) x += sdZ[r * LDF + s] * sW[r * LDF + s];
-          }
-        }
-        sdQK[r * LDQK + c] = x;
+        sdQK[r * LDQK + c] = c < r ? acc[e] : c == r ? sDiag[r] : 0.f;
       }
     }
   }
+  __syncthreads();
 
-  // ---- Dk slices: QK, Ze, B1 accumulate; dq, dk slices written
+  // Operands that stay fixed over the Dk slices, built once: dQK rows and columns, dZ E and
+  // W Eg (Eg = 2^{Gamma-b}), all on this wave's 16 rows
+  Frag<T> fA[CP / 32], fT[CP / 32], fZ[MP / 32], fG[MP / 32];
+  if (rbv) {
+#pragma unroll
+    for (int kc = 0; kc < CP / 32; ++kc) {
+      float xa[8], xt[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xa[e] = sdQK[(16 * rb + col) * LDQK + 32 * kc + 8 * grp + e];
+        xt[e] = sdQK[(32 * kc + 8 * grp + e) * LDQK + 16 * rb + col];
+      }
+      fA[kc] = frag_of<T>(xa);
+      fT[kc] = frag_of<T>(xt);
+    }
+#pragma unroll
+    for (int ks = 0; ks < MP / 32; ++ks) {
+      float xw[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int s = 32 * ks + 8 * grp + e, r = 16 * rb + col;
+        xw[e] = sW[r * LDF + s] * fast_exp2(sGam[s] - sB[r * LDF + s]);
+      }
+      fZ[ks] = frag_of<T>(dze[ks]);
+      fG[ks] = frag_of<T>(xw);
+    }
+  }
+
+  // ---- Dk slices: QK, Ze, B1 accumulate; dq, dk slices written; the next slice is loaded
+  // while this one is used
   f32x4 accQK[NRB], accZe[NSB], accB1[NSB];
 #pragma unroll
   for (int c = 0; c < NRB; ++c) accQK[c] = zero4();
 #pragma unroll
   for (int s = 0; s < NSB; ++s) accZe[s] = accB1[s] = zero4();
-  const T* qg = reinterpret_cast<const T*>(p.q) + kbase;
-  const T* kg = reinterpret_cast<const T*>(p.k) + kbase;
-  const T* s1 = reinterpret_cast<const T*>(p.S1s) + chunk * MP * DkP;
-  const T* ds1 = reinterpret_cast<const T*>(p.dS1s) + chunk * MP * DkP;
-  T* dqg = reinterpret_cast<T*>(p.dq) + kbase;
-  T* dkg = reinterpret_cast<T*>(p.dk) + kbase;
-  float z1 = 0.f;                        // this thread's share of colsum(dS1 * S1): slot tid/4
-  const int zs = tid >> 2, zq = tid & 3;
+  float z1[SM::N];                       // partial colsum(dS1 * S1) over this thread's slice rows
+#pragma unroll
+  for (int j = 0; j < SM::N; ++j) z1[j] = 0.f;
   for (int ds = 0; ds < ntk; ++ds) {
     __syncthreads();
-    slice_in<T>(sq, LDS, qg, Dk, CP, len, ds * kDvTile, Dk);
-    slice_in<T>(sk, LDS, kg, Dk, CP, len, ds * kDvTile, Dk);
-    slice_in<T>(sS1, LDS, s1, DkP, MP, MP, ds * kDvTile, DkP);
-    slice_in<T>(sdS1, LDS, ds1, DkP, MP, MP, ds * kDvTile, DkP);
-    __syncthreads();
-    if (zs < MP) {
+    rq.store(sq, LDS, len, ds * kDvTile, Dk);
+    rk.store(sk, LDS, len, ds * kDvTile, Dk);
+    rs.store(sS1, LDS, MP, ds * kDvTile, DkP);
+    rd.store(sdS1, LDS, MP, ds * kDvTile, DkP);
 #pragma unroll
-      for (int c = 0; c < kDvTile / 4; ++c) {
-        const int o = zs * LDS + zq * (kDvTile / 4) + c;
-        z1 += to_f32(sS1[o]) * to_f32(sdS1[o]);
-      }
+    for (int j = 0; j < SM::N; ++j) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) z1[j] += to_f32(rs.x[j][e]) * to_f32(rd.x[j][e]);
     }
+    if (ds + 1 < ntk) {
+      rq.load(qg, Dk, len, (ds + 1) * kDvTile, Dk);
+      rk.load(kg, Dk, len, (ds + 1) * kDvTile, Dk);
+      rs.load(s1, DkP, MP, (ds + 1) * kDvTile, DkP);
+      rd.load(ds1, DkP, MP, (ds + 1) * kDvTile, DkP);
+    }
+    __syncthreads();
     if (rbv) {
 #pragma unroll
       for (int kb = 0; kb < kDvTile / 32; ++kb) {
@@ -504,26 +602,13 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
         f32x4 aq = zero4(), ak = zero4();
 #pragma unroll
         for (int kc = 0; kc < CP / 32; ++kc) {
-          float xa[8], xt[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            xa[e] = sdQK[(16 * rb + col) * LDQK + 32 * kc + 8 * grp + e];
-            xt[e] = sdQK[(32 * kc + 8 * grp + e) * LDQK + 16 * rb + col];
-          }
-          mma(aq, frag_of<T>(xa), ld8_colblk(sk + (32 * kc) * LDS + 16 * ib, LDS));
-          mma(ak, frag_of<T>(xt), ld8_colblk(sq + (32 * kc) * LDS + 16 * ib, LDS));
+          mma(aq, fA[kc], ld8_colblk(sk + (32 * kc) * LDS + 16 * ib, LDS));
+          mma(ak, fT[kc], ld8_colblk(sq + (32 * kc) * LDS + 16 * ib, LDS));
         }
 #pragma unroll
         for (int ks = 0; ks < MP / 32; ++ks) {
-          float xa[8], xw[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int s = 32 * ks + 8 * grp + e, r = 16 * rb + col;
-            xa[e] = sdZ[r * LDF + s] * fast_exp2(sB[r * LDF + s]);
-            xw[e] = sW[r * LDF + s] * fast_exp2(sGam[s] - sB[r * LDF + s]);
-          }
-          mma(aq, frag_of<T>(xa), ld8_colblk(sS1 + (32 * ks) * LDS + 16 * ib, LDS));
-          mma(ak, frag_of<T>(xw), ld8_colblk(sdS1 + (32 * ks) * LDS + 16 * ib, LDS));
+          mma(aq, fZ[ks], ld8_colblk(sS1 + (32 * ks) * LDS + 16 * ib, LDS));
+          mma(ak, fG[ks], ld8_colblk(sdS1 + (32 * ks) * LDS + 16 * ib, LDS));
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -543,10 +628,28 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
       }
     }
   }
-  // Z1_n = 2^Gamma colsum(dS1_{n+1} * S1_n), one slot per four lanes
-  z1 += __shfl_xor(z1, 1, 64);
-  z1 += __shfl_xor(z1, 2, 64);
-  if (zq == 0 && zs < MP) sZ1[zs] = zs < m ? z1 * fast_exp2(sGam[zs]) : 0.f;
+  // the pass-2 gradients the gate gradient adds at the end, fetched while the rest runs
+  VT w2v[RPS];
+  f32x4 g2v[RPS][V / 4];
+  {
+    const int cc = (cs.active && c0 < m) ? c0 : 0;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const size_t off = gbase + (size_t)min(r0 + u, len - 1) * m + cc;
+      w2v[u] = *reinterpret_cast<const VT*>(reinterpret_cast<const T*>(p.dW2) + off);
+#pragma unroll
+      for (int e4 = 0; e4 < V / 4; ++e4) g2v[u][e4] = *reinterpret_cast<const f32x4*>(p.dg2 + off + 4 * e4);
+    }
+  }
+  // Z1_n = 2^Gamma colsum(dS1_{n+1} * S1_n): slot row (tid + 256 j) / PER_ROW, summed over the
+  // PER_ROW consecutive lanes that share it
+#pragma unroll
+  for (int j = 0; j < SM::N; ++j) {
+#pragma unroll
+    for (int o = 1; o < SM::PER_ROW; o <<= 1) z1[j] += __shfl_xor(z1[j], o, 64);
+    const int idx = tid + 256 * j, zs = idx / SM::PER_ROW;
+    if (idx % SM::PER_ROW == 0) sZ1[zs] = zs < m ? z1[j] * fast_exp2(sGam[zs]) : 0.f;
+  }
   __syncthreads();   // slices and dQK dead: sQK and the dg tiles take their bytes
   if (rbv) {
 #pragma unroll
@@ -655,22 +758,19 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
     for (int e = 0; e < V; ++e) add[e] = sZ1[c0 + e];
 #pragma unroll
     for (int e = 0; e < V; ++e) add[e] += segtot[cs.seg * MP + c0 + e] + segtot[(NSEG + cs.seg) * MP + c0 + e];
-    const T* dW2g = reinterpret_cast<const T*>(p.dW2) + gbase;
-    const float* dg2g = p.dg2 + gbase;
     float* dgg = p.dg + gbase;
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
       const int r = r0 + u;
       if (r < len && c0 < m) {
-        const VT w2 = *reinterpret_cast<const VT*>(dW2g + (size_t)r * m + c0);
 #pragma unroll
         for (int e = 0; e < V; e += 4) {
-          const f32x4 g2 = *reinterpret_cast<const f32x4*>(dg2g + (size_t)r * m + c0 + e);
+          const f32x4 g2 = g2v[u][e >> 2];
           f32x4 o;
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const float alpha = fast_exp2(cs.qv[u][e + x] * kLog2e);
-            const float dwt = sD[r * LDF + c0 + e + x] + to_f32(w2[e + x]);
+            const float dwt = sD[r * LDF + c0 + e + x] + to_f32(w2v[u][e + x]);
             o[x] = up[u][e + x] + yk[u][e + x] + add[e + x] + g2[x] - alpha * dwt;
           }
           *reinterpret_cast<f32x4*>(dgg + (size_t)r * m + c0 + e) = o;
