@@ -124,7 +124,7 @@ struct WalkIOStage {
 #pragma unroll
     for (int m = 0; m < W::PKd; ++m) {
       const int idx = tid + 256 * m;
-      if (idx < W::NK) {
+      if (W::NK % 256 == 0 || idx < W::NK) {
         const int r = idx / (CP / W::V), c = (idx - r * (CP / W::V)) * W::V;
         *reinterpret_cast<VT*>(sKT + r * W::LDA + c) = kt[m];
       }
@@ -133,7 +133,7 @@ struct WalkIOStage {
 #pragma unroll
     for (int m = 0; m < W::PV; ++m) {
       const int idx = tid + 256 * m;
-      if (idx < W::NV) {
+      if (W::NV % 256 == 0 || idx < W::NV) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
         *reinterpret_cast<VT*>(sV + r * W::LDV + c) = vok[m] ? v[m] : zero_vec<T>();
       }
@@ -151,7 +151,9 @@ __device__ __forceinline__ void state_tile_out(T* dst, const T* src, int lds, in
 #pragma unroll
   for (int m = 0; m < (RT * PER_ROW + 255) / 256; ++m) {
     const int idx = threadIdx.x + 256 * m;
-    if (idx < RT * PER_ROW) {
+    // a guard only where the tile does not divide evenly: a store the compiler must treat as
+    // optional would make it wait for the stores before it at the next operand wait
+    if (RT * PER_ROW % 256 == 0 || idx < RT * PER_ROW) {
       const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
       *reinterpret_cast<VT*>(dst + (size_t)r * DsP + c) = *reinterpret_cast<const VT*>(src + r * lds + c);
     }
@@ -280,9 +282,17 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkIO w, int ntile) {
   static_assert(R == 2, "the walk pipeline alternates two register stages");
   const int full = (N / G) / R * R;              // groups walked without bounds checks
   int kg = 0;
-  for (; kg < full; kg += R) {
-    body(I0{}, kg, std::false_type{});
-    body(I1{}, kg + 1, std::false_type{});
+  // The first pair runs ahead of the loop, and the loop is reached only through it: every path
+  // into a group's operand wait then has the previous group's state stores between that
+  // group's loads and the wait, so the compiler's count leaves those stores in flight instead
+  // of waiting for them.
+  if (full >= R) {
+    body(I0{}, 0, std::false_type{});
+    body(I1{}, 1, std::false_type{});
+    for (kg = R; kg < full; kg += R) {
+      body(I0{}, kg, std::false_type{});
+      body(I1{}, kg + 1, std::false_type{});
+    }
   }
   for (; kg < NG; kg += R) {
     body(I0{}, kg, std::true_type{});
