@@ -28,6 +28,7 @@
 // one decay factor per row and stages each stored state with one 8-byte LDS write per 16-row
 // block; the staged tile leaves in full 128-byte rows.
 #pragma once
+#include <atomic>
 #include <type_traits>
 #include "prep.hpp"
 
@@ -77,7 +78,26 @@ struct WalkPlan {
   static constexpr int RT = WalkIOCfg<T, cand(32), CP, 1>::BYTES <= kMaxLds ? cand(32) : cand(16);
   static constexpr int G = group<RT>();
   static constexpr bool OK = WalkIOCfg<T, RT, CP, G>::BYTES <= kMaxLds;
+  // 64-row tiles, two chunks per group, one workgroup per CU: each chunk's source rows are
+  // then fetched by half as many workgroups.  Worth it only while the grid still gives every
+  // CU a workgroup; below that, more and smaller tiles shorten each sequential step.
+  static constexpr bool WIDE = OK && RT == 32 && SP % 64 == 0 && WalkIOCfg<T, 64, CP, 2>::BYTES <= kMaxLds;
 };
+
+// Compute units of the current device, cached per device id.
+inline int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 template <typename T, int SP, int CP>
 constexpr bool walk_fits() {
   return WalkPlan<T, SP, CP>::OK;
@@ -317,6 +337,14 @@ hipError_t launch_walk(const WalkIO& w, int BH, hipStream_t s) {
     return hipErrorNotSupported;
   } else {
     const int ntile = (w.Ds + kDvTile - 1) / kDvTile;
+    if constexpr (P::WIDE) {
+      const int cus = device_cu_count();
+      if (cus > 0 && ntile * (SP / 64) * BH >= cus) {
+        hipLaunchKernelGGL((walk_kernel<T, SP, 64, CP, 2, REV>), dim3(ntile * (SP / 64) * BH), dim3(256), 0, s, w,
+                           ntile);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL((walk_kernel<T, SP, P::RT, CP, P::G, REV>), dim3(ntile * (SP / P::RT) * BH), dim3(256), 0, s,
                        w, ntile);
     return hipGetLastError();
