@@ -45,7 +45,8 @@
  *     a *_workspace_bytes() query returns 0 for them.
  *   - Results are deterministic: no floating-point atomics are used, so two runs on the same
  *     inputs give bitwise-identical outputs.
- *   - The library is reentrant and keeps no mutable global state.
+ *   - The library is reentrant.  Its only global state is the compute-unit count of each
+ *     device it has run on (read once; it picks the state walks' tile height).
  */
 #ifndef GLA_AMD_GLA_H
 #define GLA_AMD_GLA_H
@@ -252,7 +253,10 @@ int gsa_decode_step(const void* q, const void* k, const void* v, const void* g,
  *   ngroups : 1 .. 8;  scales, heads: HOST arrays of ngroups ints (1 <= scales[i] <= 65536,
  *             heads[i] >= 1)
  * Every group's pooled shape must be supported by gla_fwd (same C, Dk, Dv rules).  Bad group
- * arrays give GLA_ERR_SHAPE (counts) or GLA_ERR_UNSUPPORTED (ngroups, scales). */
+ * arrays give GLA_ERR_SHAPE (counts) or GLA_ERR_UNSUPPORTED (ngroups, scales).
+ * The groups' GLA forwards run together, each kernel launched once for all groups, each
+ * group with its own workspace slice.  A scale-1 group reads q, k, v and g in place; other
+ * groups read pooled copies in the workspace. */
 size_t msgla_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype,
                                  int ngroups, const int* scales, const int* heads);
 int msgla_fwd(const void* q, const void* k, const void* v, const void* g,

@@ -120,6 +120,12 @@ hipError_t dispatch_fwd(int dtype, int DKP, int CP, const FwdParams& p, hipStrea
   return hipErrorInvalidValue;
 }
 
+hipError_t dispatch_fwd_batches(int dtype, int DKP, int CP, const FwdParams* ps, int nb, hipStream_t s) {
+  if (dtype == GLA_BF16) GLA_DISPATCH_DKCP(launch_gla_fwd_batches, bf16, DKP, CP, ps, nb, s);
+  else GLA_DISPATCH_DKCP(launch_gla_fwd_batches, float, DKP, CP, ps, nb, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t dispatch_bwd(int dtype, int DKP, int CP, const BwdParams& p, hipStream_t s) {
   if (dtype == GLA_BF16) GLA_DISPATCH_DKCP(launch_gla_bwd, bf16, DKP, CP, p, s);
   else GLA_DISPATCH_DKCP(launch_gla_bwd, float, DKP, CP, p, s);
@@ -458,10 +464,11 @@ namespace {
 
 // ---------------------------------------------------------------- MS-GLA front end
 struct MsglaLayout {
-  size_t pooled[kMsMaxGroups];   // per group: pooled q, k, g, then v
-  size_t op[kMsMaxGroups];       // per group: pooled GLA outputs
-  size_t h0g, htg;               // one group's initial / final states (reused group by group)
-  size_t gla;                    // one group's GLA forward workspace (reused group by group)
+  size_t pooled[kMsMaxGroups];   // per group: pooled q, k, g, then v (none at scale 1)
+  size_t op[kMsMaxGroups];       // per group: GLA outputs on the pooled sequence
+  size_t h0g[kMsMaxGroups];      // per group: initial / final states, gathered from and
+  size_t htg[kMsMaxGroups];      //   scattered to the group's heads of h0 / ht
+  size_t gla[kMsMaxGroups];      // per group: GLA forward workspace (the groups run together)
   size_t total;
 };
 
@@ -488,22 +495,21 @@ MsglaLayout msgla_layout(int B, int L, int Dk, int Dv, int C, int dtype, int ngr
                          const int* heads) {
   MsglaLayout l{};
   const size_t es = esize_of(dtype);
-  size_t off = 0, smax = 0, gmax = 0;
+  size_t off = 0;
   for (int i = 0; i < ngroups; ++i) {
     const size_t rows = (size_t)B * heads[i] * pooled_len(L, scales[i]);
+    const size_t st = align_up((size_t)B * heads[i] * Dk * Dv * 4);
     l.pooled[i] = off;
-    off += 3 * align_up(rows * Dk * es) + align_up(rows * Dv * es);
+    if (scales[i] > 1) off += 3 * align_up(rows * Dk * es) + align_up(rows * Dv * es);
     l.op[i] = off;
     off += align_up(rows * Dv * es);
-    smax = std::max(smax, (size_t)B * heads[i] * Dk * Dv * 4);
-    gmax = std::max(gmax, fwd_ws_bytes(B, heads[i], pooled_len(L, scales[i]), Dk, Dv, C, dtype));
+    l.h0g[i] = off;
+    off += st;
+    l.htg[i] = off;
+    off += st;
+    l.gla[i] = off;
+    off += align_up(fwd_ws_bytes(B, heads[i], pooled_len(L, scales[i]), Dk, Dv, C, dtype));
   }
-  l.h0g = off;
-  off += align_up(smax);
-  l.htg = off;
-  off += align_up(smax);
-  l.gla = off;
-  off += gmax;
   l.total = off;
   return l;
 }
@@ -691,42 +697,65 @@ int msgla_fwd(const void* q, const void* k, const void* v, const void* g, const 
   mp.q = q; mp.k = k; mp.v = v; mp.g = g; mp.w = w; mp.o = o;
   mp.B = B; mp.H = H; mp.L = L; mp.Dk = Dk; mp.Dv = Dv; mp.ngroups = ngroups;
   int hbeg = 0;
+  bool pooled = false;
+  mp.pooled_heads = 0;
+  mp.max_pooled_len = 0;
   for (int i = 0; i < ngroups; ++i) {
     const size_t rows = (size_t)B * heads[i] * pooled_len(L, scales[i]);
     MsglaGroup& G = mp.grp[i];
     G.h0 = hbeg; G.nh = heads[i]; G.s = scales[i];
-    G.qp = ws + lay.pooled[i];
-    G.kp = static_cast<char*>(G.qp) + align_up(rows * Dk * es);
-    G.gp = static_cast<char*>(G.kp) + align_up(rows * Dk * es);
-    G.vp = static_cast<char*>(G.gp) + align_up(rows * Dk * es);
+    if (G.s > 1) {
+      G.qp = ws + lay.pooled[i];
+      G.kp = static_cast<char*>(G.qp) + align_up(rows * Dk * es);
+      G.gp = static_cast<char*>(G.kp) + align_up(rows * Dk * es);
+      G.vp = static_cast<char*>(G.gp) + align_up(rows * Dk * es);
+      pooled = true;
+      mp.pooled_heads += G.nh;
+      mp.max_pooled_len = std::max(mp.max_pooled_len, pooled_len(L, G.s));
+    }
     G.op = ws + lay.op[i];
     hbeg += heads[i];
   }
-  hipError_t e = dtype == GLA_BF16 ? launch_msgla_pool<bf16>(mp, hs) : launch_msgla_pool<float>(mp, hs);
-  if (e != hipSuccess) return GLA_ERR_HIP;
+  hipError_t e = hipSuccess;
+  if (pooled && (e = dtype == GLA_BF16 ? launch_msgla_pool<bf16>(mp, hs) : launch_msgla_pool<float>(mp, hs)) !=
+                    hipSuccess)
+    return GLA_ERR_HIP;
 
-  // one GLA forward per head group on its pooled sequence; the group's heads are a strided
-  // slice of [B][H], so its states are gathered into / scattered from contiguous buffers
-  float* h0g = reinterpret_cast<float*>(ws + lay.h0g);
-  float* htg = reinterpret_cast<float*>(ws + lay.htg);
+  // The head groups' GLA forwards on their pooled sequences (scale 1: on the caller's tensors,
+  // through a strided view of the group's heads), all groups in each of three launches, so the
+  // small groups fill the CUs the large one leaves idle.  A group's heads are a strided slice
+  // of [B][H]: its states are gathered into / scattered from contiguous buffers.
   const size_t head_bytes = (size_t)Dk * Dv * 4;
+  const int DKP = pad_dk(Dk), CP = pad_c(C);
+  FwdParams ps[kMsMaxGroups];
   for (int i = 0; i < ngroups; ++i) {
     const MsglaGroup& G = mp.grp[i];
-    const int Ls = pooled_len(L, G.s), N = (Ls + C - 1) / C, DKP = pad_dk(Dk), CP = pad_c(C);
+    float* h0g = reinterpret_cast<float*>(ws + lay.h0g[i]);
+    float* htg = reinterpret_cast<float*>(ws + lay.htg[i]);
+    const int Ls = pooled_len(L, G.s), N = (Ls + C - 1) / C;
     if (h0 && hipMemcpy2DAsync(h0g, G.nh * head_bytes, h0 + (size_t)G.h0 * Dk * Dv, (size_t)H * head_bytes,
                                G.nh * head_bytes, B, hipMemcpyDeviceToDevice, hs) != hipSuccess)
       return GLA_ERR_HIP;
-    FwdParams p;
-    p.q = G.qp; p.k = G.kp; p.v = G.vp; p.g = G.gp; p.h0 = h0 ? h0g : nullptr;
+    FwdParams& p = ps[i];
+    if (G.s == 1) {
+      p.q = q; p.k = k; p.v = v; p.g = g;
+      p.in = SeqView{G.nh, H, G.h0};
+    } else {
+      p.q = G.qp; p.k = G.kp; p.v = G.vp; p.g = G.gp;
+    }
+    p.h0 = h0 ? h0g : nullptr;
     p.o = G.op; p.ht = ht ? htg : nullptr;
     p.BH = B * G.nh; p.L = Ls; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
     const OpsLayout ol = ops_layout((size_t)p.BH, N, CP, DKP, es, false);
-    p.ops = carve_ops(ws + lay.gla, ol, false);
-    p.Hs = ws + lay.gla + ol.total;
+    p.ops = carve_ops(ws + lay.gla[i], ol, false);
+    p.Hs = ws + lay.gla[i] + ol.total;
     p.events = LaunchEvents{nullptr, 0};
-    if (dispatch_fwd(dtype, DKP, CP, p, hs) != hipSuccess) return GLA_ERR_HIP;
-    if (ht && hipMemcpy2DAsync(ht + (size_t)G.h0 * Dk * Dv, (size_t)H * head_bytes, htg, G.nh * head_bytes,
-                               G.nh * head_bytes, B, hipMemcpyDeviceToDevice, hs) != hipSuccess)
+  }
+  if (dispatch_fwd_batches(dtype, DKP, CP, ps, ngroups, hs) != hipSuccess) return GLA_ERR_HIP;
+  for (int i = 0; i < ngroups && ht; ++i) {
+    const MsglaGroup& G = mp.grp[i];
+    if (hipMemcpy2DAsync(ht + (size_t)G.h0 * Dk * Dv, (size_t)H * head_bytes, ws + lay.htg[i], G.nh * head_bytes,
+                         G.nh * head_bytes, B, hipMemcpyDeviceToDevice, hs) != hipSuccess)
       return GLA_ERR_HIP;
   }
   e = dtype == GLA_BF16 ? launch_msgla_hold<bf16>(mp, hs) : launch_msgla_hold<float>(mp, hs);

@@ -38,7 +38,7 @@ struct OutCfg {
 };
 
 template <typename T, int DKP, int CP>
-__global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
+__device__ __forceinline__ void fwd_out_block(const FwdParams& p, int ntile, int lin) {
   using W = OutCfg<T, DKP, CP>;
   constexpr int LDV = W::LDV, V = W::V, NBR = W::NBR, RBW = W::RBW;
   constexpr int NKB = DKP / 32, NCB = CP / 32, NJB = kDvTile / 16;
@@ -47,8 +47,6 @@ __global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
   T* sH = reinterpret_cast<T*>(smem);
   T* sV = reinterpret_cast<T*>(smem + W::HT);
 
-  // the ntile value tiles of one chunk are consecutive, so they share an XCD's L2 for Qs, A
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = lin % ntile, n = (lin / ntile) % p.N, bh = lin / (ntile * p.N);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int Dv = p.Dv, L = p.L, DvP = ntile * kDvTile;
@@ -57,7 +55,7 @@ __global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
   const T* Qc = reinterpret_cast<const T*>(p.ops.Qs) + chunk * CP * DKP;
   const T* Ac = reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP;
   const T* Hc = reinterpret_cast<const T*>(p.Hs) + chunk * DKP * DvP + tile * kDvTile;
-  const T* vg = reinterpret_cast<const T*>(p.v) + ((size_t)bh * L + row0) * Dv;
+  const T* vg = reinterpret_cast<const T*>(p.v) + ((size_t)p.in(bh) * L + row0) * Dv;
 
   // all loads first: shared tiles (16-byte vectors; value rows past the chunk end and columns
   // past Dv come from clamped addresses and are zeroed when stored), then this wave's row
@@ -150,6 +148,20 @@ __global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
   }
 }
 
+// grid ntile * N * BH; the ntile value tiles of one chunk are consecutive after the XCD
+// remapping, so they share an XCD's L2 for Qs and A
+template <typename T, int DKP, int CP>
+__global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
+  fwd_out_block<T, DKP, CP>(p, ntile, xcd_remap(blockIdx.x, gridDim.x));
+}
+
+// several batches in one launch (see Batches): batch i owns blocks first[i] .. first[i+1] - 1
+template <typename T, int DKP, int CP>
+__global__ __launch_bounds__(256) void gla_fwd_out_batches(Batches<FwdParams> b, int ntile) {
+  const int gi = b.find(blockIdx.x);
+  fwd_out_block<T, DKP, CP>(b.p[gi], ntile, blockIdx.x - b.first[gi]);
+}
+
 template <typename T, int DKP, int CP>
 constexpr bool fwd_fits() {
   return PrepCfg<T, DKP, CP>::BYTES <= kMaxLds && walk_fits<T, DKP, CP>() && OutCfg<T, DKP, CP>::BYTES <= kMaxLds;
@@ -160,12 +172,12 @@ hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
   if constexpr (!fwd_fits<T, DKP, CP>()) {
     return hipErrorNotSupported;
   } else {
-    PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N};
+    PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N, p.in};
     record_event(p.events, 0, s);
     hipError_t e = p.ops.QsT ? launch_prep<T, DKP, CP, true>(pp, p.BH, s) : launch_prep<T, DKP, CP, false>(pp, p.BH, s);
     if (e != hipSuccess) return e;
     record_event(p.events, 1, s);
-    WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, p.ht, p.Dk, p.Dv, p.L, p.C, p.N, 0};
+    WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, p.ht, p.Dk, p.Dv, p.L, p.C, p.N, 0, p.in};
     if ((e = launch_walk_store<T, DKP, CP>(wf, p.BH, s)) != hipSuccess) return e;
     record_event(p.events, 2, s);
     const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
@@ -173,6 +185,40 @@ hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     record_event(p.events, 3, s);
     return hipSuccess;
+  }
+}
+
+// The forward of nb independent batches (same T, Dk, Dv, C; each with its own inputs, sequence
+// view, workspace and outputs) with three launches in all.
+template <typename T, int DKP, int CP>
+hipError_t launch_gla_fwd_batches(const FwdParams* ps, int nb, hipStream_t s) {
+  if constexpr (!fwd_fits<T, DKP, CP>()) {
+    return hipErrorNotSupported;
+  } else {
+    if (nb < 1 || nb > kMaxBatches) return hipErrorInvalidValue;
+    Batches<PrepParams> bp{};
+    Batches<WalkIO> bw{};
+    Batches<FwdParams> bo{};
+    bp.n = bw.n = bo.n = nb;
+    int BH[kMaxBatches], maxN = 0;
+    const int ntile = (ps[0].Dv + kDvTile - 1) / kDvTile;
+    bp.first[0] = bo.first[0] = 0;
+    for (int i = 0; i < nb; ++i) {
+      const FwdParams& p = ps[i];
+      if (p.ops.QsT || p.Dk != ps[0].Dk || p.Dv != ps[0].Dv || p.C != ps[0].C) return hipErrorInvalidValue;
+      bp.p[i] = PrepParams{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N, p.in};
+      bw.p[i] = WalkIO{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, p.ht, p.Dk, p.Dv, p.L, p.C, p.N, 0, p.in};
+      bo.p[i] = p;
+      BH[i] = p.BH;
+      maxN = p.N > maxN ? p.N : maxN;
+      bp.first[i + 1] = bp.first[i] + p.BH;
+      bo.first[i + 1] = bo.first[i] + ntile * p.N * p.BH;
+    }
+    hipError_t e;
+    if ((e = launch_prep_batches<T, DKP, CP, false>(bp, maxN, s)) != hipSuccess) return e;
+    if ((e = launch_walk_store_batches<T, DKP, CP>(bw, BH, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL((gla_fwd_out_batches<T, DKP, CP>), dim3(bo.first[nb]), dim3(256), 0, s, bo, ntile);
+    return hipGetLastError();
   }
 }
 
@@ -193,7 +239,9 @@ bool fwd_config_fits(int esize, int DKP, int CP) {
   return ok;
 }
 
-#define GLA_FWD_INST(TT, D, C_) template hipError_t launch_gla_fwd<TT, D, C_>(const FwdParams&, hipStream_t);
+#define GLA_FWD_INST(TT, D, C_)                                                     \
+  template hipError_t launch_gla_fwd<TT, D, C_>(const FwdParams&, hipStream_t); \
+  template hipError_t launch_gla_fwd_batches<TT, D, C_>(const FwdParams*, int, hipStream_t);
 #define GLA_FWD_INST_T(TT)                                                     \
   GLA_FWD_INST(TT, 32, 32) GLA_FWD_INST(TT, 32, 64) GLA_FWD_INST(TT, 32, 128)  \
   GLA_FWD_INST(TT, 64, 32) GLA_FWD_INST(TT, 64, 64) GLA_FWD_INST(TT, 64, 128)  \

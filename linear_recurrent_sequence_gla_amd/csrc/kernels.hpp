@@ -5,6 +5,34 @@
 
 namespace gla {
 
+// Which input sequence the bh-th sequence of a launch reads: (bh / n) * stride + off + bh % n.
+// The default is the contiguous [BH] batch itself.  With n = nh, stride = H, off = h0 a launch
+// over B * nh sequences reads heads h0 .. h0 + nh - 1 of caller tensors laid out [B][H][L][D]
+// in place (the multi-scale front end runs its scale-1 head group this way).  Only the token
+// inputs (q, k, g, v) are read through it; workspaces and outputs stay indexed by bh.
+struct SeqView {
+  int n = 1, stride = 1, off = 0;
+  __host__ __device__ int operator()(int bh) const { return (bh / n) * stride + off + bh % n; }
+};
+
+// Up to kMaxBatches independent sequence batches with the same widths and chunk size, run by
+// one launch per kernel: batch i owns blocks first[i] .. first[i + 1] - 1 of the launch's
+// batch axis (its sequences for the preparation kernel, its blocks for the others).  The
+// multi-scale front end runs its head groups this way, so that the small groups fill the CUs
+// the large one leaves idle.
+constexpr int kMaxBatches = 8;
+template <typename P>
+struct Batches {
+  P p[kMaxBatches];
+  int first[kMaxBatches + 1];
+  int n;
+  __host__ __device__ int find(int i) const {
+    int g = 0;
+    while (g + 1 < n && i >= first[g + 1]) ++g;
+    return g;
+  }
+};
+
 // Per-chunk operands written by the chunk-preparation kernel, all chunk-padded so that the
 // consumers need no bounds checks: CP = padded chunk rows, DKP = padded key width.
 struct ChunkOps {
@@ -34,6 +62,7 @@ struct FwdParams {
   ChunkOps ops;   // ops.QsT != nullptr: the preparation also writes Qs^T (kept for a backward)
   void* Hs;       // [BH][N][DKP][DvP] chunk-start states (T), written by the state walk
   LaunchEvents events;
+  SeqView in;     // input sequences read by the launch
 };
 
 struct BwdParams {
@@ -93,6 +122,8 @@ inline int pad_dv(int Dv) { return (Dv + kDvTile - 1) / kDvTile * kDvTile; }
 template <typename T, int DKP, int CP>
 hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s);
 template <typename T, int DKP, int CP>
+hipError_t launch_gla_fwd_batches(const FwdParams* ps, int nb, hipStream_t s);
+template <typename T, int DKP, int CP>
 hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s);
 template <typename T>
 hipError_t launch_gla_decode(const DecodeParams& p, hipStream_t s);
@@ -136,6 +167,7 @@ hipError_t launch_gsa_decode(const GsaDecodeParams& p, hipStream_t s);
 
 // MS-GLA front end: head groups, one per temporal scale
 constexpr int kMsMaxGroups = 8;
+static_assert(kMsMaxGroups <= kMaxBatches, "the head groups run as one batched launch");
 struct MsglaGroup {
   int h0, nh, s;                  // first head, number of heads, pooling scale
   void *qp, *kp, *gp, *vp;        // pooled inputs [B][nh][ceil(L/s)][Dk or Dv] (T)
@@ -146,6 +178,8 @@ struct MsglaParams {
   const float* w;                 // [B][L][ngroups] fusion weights, or null for 1
   void* o;                        // [B][H][L][Dv] (T)
   int B, H, L, Dk, Dv, ngroups;
+  int pooled_heads;               // heads in groups with scale > 1
+  int max_pooled_len;             // longest pooled sequence among those groups
   MsglaGroup grp[kMsMaxGroups];
 };
 template <typename T>

@@ -5,7 +5,8 @@
 //
 //   pooling (section 3.1): block j of group scale s averages tokens j*s .. min(j*s+s, L) - 1
 //       of q, k, g and v (a trailing partial block averages only its real tokens), for the
-//       group's heads, into contiguous [B][heads][ceil(L/s)][D] tensors;
+//       group's heads, into contiguous [B][heads][ceil(L/s)][D] tensors (scale 1 is the
+//       identity: those heads are read in place, through a strided sequence view);
 //   hold and fusion (section 3.3): token t takes the pooled output of block (t+1)/s - 1, the
 //       latest block it has fully seen (zero before the first completes), times the caller's
 //       weight w[b][t][group].
@@ -17,8 +18,9 @@
 
 namespace gla {
 
-constexpr int kMsRowsPerBlock = 16;     // pooled rows per pooling workgroup
+constexpr int kMsRowsPerBlock = 4;      // pooled rows per pooling workgroup
 constexpr int kMsTokPerBlock = 16;      // tokens per hold workgroup
+constexpr int kMsUnroll = 4;            // tokens whose loads are in flight together
 
 // head group of head h (groups hold consecutive heads, in order)
 __device__ __forceinline__ int ms_group_of(const MsglaParams& p, int h) {
@@ -28,15 +30,22 @@ __device__ __forceinline__ int ms_group_of(const MsglaParams& p, int h) {
   return gi;
 }
 
-// grid (ceil(L / kMsRowsPerBlock), B*H); the blocks past a group's pooled length return
+// grid (ceil(max pooled length / kMsRowsPerBlock), B * pooled heads): only the groups with a
+// scale above 1 are pooled; blocks past their group's pooled length return
 template <typename T>
 __global__ __launch_bounds__(256) void msgla_pool_kernel(MsglaParams p) {
   typedef typename V16<T>::type VT;
   constexpr int V = V16<T>::N;
-  const int bh = blockIdx.y, b = bh / p.H, h = bh - b * p.H;
-  const int gi = ms_group_of(p, h);
+  const int b = blockIdx.y / p.pooled_heads;
+  int k = blockIdx.y - b * p.pooled_heads, gi = 0;
+#pragma unroll 1
+  for (; gi < p.ngroups; ++gi) {            // the k-th pooled head, in head order
+    if (p.grp[gi].s == 1) continue;
+    if (k < p.grp[gi].nh) break;
+    k -= p.grp[gi].nh;
+  }
   const MsglaGroup& G = p.grp[gi];
-  const int s = G.s, Ls = (p.L + s - 1) / s, hl = h - G.h0;
+  const int s = G.s, Ls = (p.L + s - 1) / s, hl = k, h = G.h0 + hl, bh = b * p.H + h;
   const int j0 = blockIdx.x * kMsRowsPerBlock;
   if (j0 >= Ls) return;
   const int nk = p.Dk / V, nv = p.Dv / V, per_row = 3 * nk + nv;
@@ -65,10 +74,19 @@ __global__ __launch_bounds__(256) void msgla_pool_kernel(MsglaParams p) {
     float acc[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) acc[e] = 0.f;
-    for (int u = 0; u < cnt; ++u) {
-      const VT x = *reinterpret_cast<const VT*>(src + (size_t)(t0 + u) * D + col);
+    // kMsUnroll tokens' loads issued together, from rows clamped into the block
+    for (int u0 = 0; u0 < cnt; u0 += kMsUnroll) {
+      VT x[kMsUnroll];
 #pragma unroll
-      for (int e = 0; e < V; ++e) acc[e] += to_f32(x[e]);
+      for (int u = 0; u < kMsUnroll; ++u)
+        x[u] = *reinterpret_cast<const VT*>(src + (size_t)(t0 + min(u0 + u, cnt - 1)) * D + col);
+#pragma unroll
+      for (int u = 0; u < kMsUnroll; ++u) {
+        if (u0 + u < cnt) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) acc[e] += to_f32(x[u][e]);
+        }
+      }
     }
     const float inv = 1.f / (float)cnt;
     VT y;
@@ -110,7 +128,9 @@ __global__ __launch_bounds__(256) void msgla_hold_kernel(MsglaParams p) {
 
 template <typename T>
 hipError_t launch_msgla_pool(const MsglaParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((msgla_pool_kernel<T>), dim3((p.L + kMsRowsPerBlock - 1) / kMsRowsPerBlock, p.B * p.H),
+  if (p.pooled_heads == 0) return hipSuccess;
+  hipLaunchKernelGGL((msgla_pool_kernel<T>),
+                     dim3((p.max_pooled_len + kMsRowsPerBlock - 1) / kMsRowsPerBlock, p.B * p.pooled_heads),
                      dim3(256), 0, s, p);
   return hipGetLastError();
 }

@@ -46,6 +46,7 @@ struct PrepParams {
   const void *q, *k, *g;
   ChunkOps ops;
   int L, Dk, C, N;
+  SeqView in;     // input sequences of q, k, g
 };
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
@@ -286,7 +287,7 @@ struct ChunkScan {
 };
 
 template <typename T, int DKP, int CP, bool WANT_QST>
-__global__ __launch_bounds__(256, 2) void gla_prep_kernel(PrepParams p) {
+__device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh) {
   using Cfg = PrepCfg<T, DKP, CP>;
   using M = ChunkMap<T, DKP, CP>;
   constexpr int V = M::V, RPS = M::RPS;
@@ -298,11 +299,11 @@ __global__ __launch_bounds__(256, 2) void gla_prep_kernel(PrepParams p) {
   float* sGam = segtot + M::NSEG * DKP;
   float* red = sGam + DKP;
 
-  const int n = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
   const int row0 = n * p.C;
   const int len = min(p.C, p.L - row0);
   const int Dk = p.Dk;
-  const size_t base = ((size_t)bh * p.L + row0) * Dk;
+  const size_t base = ((size_t)p.in(bh) * p.L + row0) * Dk;
   const size_t chunk = (size_t)bh * p.N + n;
 
   ChunkScan<T, DKP, CP> cs;
@@ -507,12 +508,38 @@ __global__ __launch_bounds__(256, 2) void gla_prep_kernel(PrepParams p) {
   if (tid < DKP) p.ops.Gam[chunk * DKP + tid] = sGam[tid];
 }
 
+// grid (N, BH): chunk n of sequence bh
+template <typename T, int DKP, int CP, bool WANT_QST>
+__global__ __launch_bounds__(256, 2) void gla_prep_kernel(PrepParams p) {
+  prep_chunk<T, DKP, CP, WANT_QST>(p, blockIdx.x, blockIdx.y);
+}
+
+// grid (max N, total sequences): blockIdx.y runs over the batches' sequences back to back;
+// blocks past a batch's own chunk count return at once
+template <typename T, int DKP, int CP, bool WANT_QST>
+__global__ __launch_bounds__(256, 2) void gla_prep_batches(Batches<PrepParams> b) {
+  const int gi = b.find(blockIdx.y);
+  const PrepParams& p = b.p[gi];
+  if ((int)blockIdx.x >= p.N) return;
+  prep_chunk<T, DKP, CP, WANT_QST>(p, blockIdx.x, blockIdx.y - b.first[gi]);
+}
+
 template <typename T, int DKP, int CP, bool WANT_QST>
 hipError_t launch_prep(const PrepParams& p, int BH, hipStream_t s) {
   if constexpr (PrepCfg<T, DKP, CP>::BYTES > kMaxLds) {
     return hipErrorNotSupported;
   } else {
     hipLaunchKernelGGL((gla_prep_kernel<T, DKP, CP, WANT_QST>), dim3(p.N, BH), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+}
+
+template <typename T, int DKP, int CP, bool WANT_QST>
+hipError_t launch_prep_batches(const Batches<PrepParams>& b, int maxN, hipStream_t s) {
+  if constexpr (PrepCfg<T, DKP, CP>::BYTES > kMaxLds) {
+    return hipErrorNotSupported;
+  } else {
+    hipLaunchKernelGGL((gla_prep_batches<T, DKP, CP, WANT_QST>), dim3(maxN, b.first[b.n]), dim3(256), 0, s, b);
     return hipGetLastError();
   }
 }

@@ -42,11 +42,12 @@ struct WalkIO {
   const float* init;   // fp32 [BH][rows][Ds] (or [BH][Ds][rows] when trans) or nullptr (= 0)
   float* fin;          // fp32, same layout, or nullptr (= not written)
   int rows, Ds, L, C, N, trans;
+  SeqView in;          // input sequences of src
 };
 
 constexpr int kWalkDepth = 2;   // chunk groups whose operands are in flight ahead of use
 
-template <typename T, int RT, int CP, int G = 1>
+template <typename T, int RT, int CP, int G = 1, int NT = 256>
 struct WalkIOCfg {
   static constexpr int V = 16 / (int)sizeof(T);
   static constexpr int LDA = CP + V, LDV = kDvTile + V;
@@ -58,7 +59,7 @@ struct WalkIOCfg {
   static constexpr size_t HT = (size_t)RT * LDV * sizeof(T);   // one staged state tile
   static constexpr size_t BYTES = 2 * STAGE + 2 * G * HT;
   static constexpr int NK = RT * CP / V, NV = CP * kDvTile / V;
-  static constexpr int PKd = (NK + 255) / 256, PV = (NV + 255) / 256;
+  static constexpr int PKd = (NK + NT - 1) / NT, PV = (NV + NT - 1) / NT;   // vectors per thread
 };
 
 // Row tile RT (32 rows, at most SP; 16 if nothing fits) and group size G (4, 2 or 1 chunks):
@@ -78,9 +79,10 @@ struct WalkPlan {
   static constexpr int RT = WalkIOCfg<T, cand(32), CP, 1>::BYTES <= kMaxLds ? cand(32) : cand(16);
   static constexpr int G = group<RT>();
   static constexpr bool OK = WalkIOCfg<T, RT, CP, G>::BYTES <= kMaxLds;
-  // 64-row tiles, two chunks per group, one workgroup per CU: each chunk's source rows are
-  // then fetched by half as many workgroups.  Worth it only while the grid still gives every
-  // CU a workgroup; below that, more and smaller tiles shorten each sequential step.
+  // 64-row tiles of 8 waves (two 32-row halves sharing each chunk's source rows), two chunks
+  // per group, one workgroup per CU: each source row is fetched by half as many workgroups.
+  // Worth it only while the grid still gives every CU a workgroup; below that, more and
+  // smaller tiles shorten each sequential step.
   static constexpr bool WIDE = OK && RT == 32 && SP % 64 == 0 && WalkIOCfg<T, 64, CP, 2>::BYTES <= kMaxLds;
 };
 
@@ -108,9 +110,9 @@ constexpr bool walk_fits() {
 // beside it; masking happens when the registers are written to LDS, after the data has
 // arrived.  This keeps branches and register rewrites away from loads in flight, so the
 // compiler can leave several chunks' loads outstanding.
-template <typename T, int RT, int CP>
+template <typename T, int RT, int CP, int NT>
 struct WalkIOStage {
-  using W = WalkIOCfg<T, RT, CP>;
+  using W = WalkIOCfg<T, RT, CP, 1, NT>;
   typedef typename V16<T>::type VT;
   VT kt[W::PKd], v[W::PV];
   bool vok[W::PV];
@@ -123,13 +125,13 @@ struct WalkIOStage {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < W::PKd; ++m) {
-      const int idx = min(tid + 256 * m, W::NK - 1);
+      const int idx = min(tid + NT * m, W::NK - 1);
       kt[m] = *reinterpret_cast<const VT*>(mat + (size_t)idx * W::V);
     }
     constexpr int PER_ROW = kDvTile / W::V;
 #pragma unroll
     for (int m = 0; m < W::PV; ++m) {
-      const int idx = tid + 256 * m;
+      const int idx = tid + NT * m;
       const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
       const int j = tile * kDvTile + c;
       vok[m] = idx < W::NV && r < len && j < Ds;
@@ -143,8 +145,8 @@ struct WalkIOStage {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < W::PKd; ++m) {
-      const int idx = tid + 256 * m;
-      if (W::NK % 256 == 0 || idx < W::NK) {
+      const int idx = tid + NT * m;
+      if (W::NK % NT == 0 || idx < W::NK) {
         const int r = idx / (CP / W::V), c = (idx - r * (CP / W::V)) * W::V;
         *reinterpret_cast<VT*>(sKT + r * W::LDA + c) = kt[m];
       }
@@ -152,8 +154,8 @@ struct WalkIOStage {
     constexpr int PER_ROW = kDvTile / W::V;
 #pragma unroll
     for (int m = 0; m < W::PV; ++m) {
-      const int idx = tid + 256 * m;
-      if (W::NV % 256 == 0 || idx < W::NV) {
+      const int idx = tid + NT * m;
+      if (W::NV % NT == 0 || idx < W::NV) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * W::V;
         *reinterpret_cast<VT*>(sV + r * W::LDV + c) = vok[m] ? v[m] : zero_vec<T>();
       }
@@ -163,17 +165,17 @@ struct WalkIOStage {
 };
 
 // Copy an LDS [RT][64] tile to the state workspace (row stride DsP, already offset).
-template <typename T, int RT>
+template <typename T, int RT, int NT>
 __device__ __forceinline__ void state_tile_out(T* dst, const T* src, int lds, int DsP) {
   constexpr int V = V16<T>::N;
   typedef typename V16<T>::type VT;
   constexpr int PER_ROW = kDvTile / V;
 #pragma unroll
-  for (int m = 0; m < (RT * PER_ROW + 255) / 256; ++m) {
-    const int idx = threadIdx.x + 256 * m;
+  for (int m = 0; m < (RT * PER_ROW + NT - 1) / NT; ++m) {
+    const int idx = threadIdx.x + NT * m;
     // a guard only where the tile does not divide evenly: a store the compiler must treat as
     // optional would make it wait for the stores before it at the next operand wait
-    if (RT * PER_ROW % 256 == 0 || idx < RT * PER_ROW) {
+    if (RT * PER_ROW % NT == 0 || idx < RT * PER_ROW) {
       const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
       *reinterpret_cast<VT*>(dst + (size_t)r * DsP + c) = *reinterpret_cast<const VT*>(src + r * lds + c);
     }
@@ -184,41 +186,47 @@ __device__ __forceinline__ size_t walk_state_index(const WalkIO& w, int bh, int 
   return w.trans ? ((size_t)bh * w.Ds + j) * w.rows + i : ((size_t)bh * w.rows + i) * w.Ds + j;
 }
 
-// T^T = X^T M^T on fresh accumulators (M and X from LDS): one chunk's state increment, with
-// lane (col, grp) of wave w holding T[16 ib + col][16 w + 4 grp + e] in Tm[ib][e].
-template <typename T, int RT, int CP>
-__device__ __forceinline__ void walk_product(f32x4 (&Tm)[RT / 16], const T* sKT, const T* sV) {
+// T^T = X^T M^T on fresh accumulators (M and X from LDS): one chunk's state increment over
+// the RW rows from row ri and the 16 columns from cj, with lane (col, grp) holding
+// T[ri + 16 ib + col][cj + 4 grp + e] in Tm[ib][e].
+template <typename T, int RT, int CP, int RW>
+__device__ __forceinline__ void walk_product(f32x4 (&Tm)[RW / 16], const T* sKT, const T* sV, int ri, int cj) {
   using W = WalkIOCfg<T, RT, CP>;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  constexpr int NCB = CP / 32, NIB = RT / 16;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  constexpr int NCB = CP / 32, NIB = RW / 16;
   Frag<T> Yv[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_colblk(sV + (32 * cb) * W::LDV + 16 * wave, W::LDV);
+  for (int cb = 0; cb < NCB; ++cb) Yv[cb] = ld8_colblk(sV + (32 * cb) * W::LDV + cj, W::LDV);
 #pragma unroll
   for (int ib = 0; ib < NIB; ++ib) Tm[ib] = zero4();
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) mma(Tm[ib], Yv[cb], ld8(sKT + (16 * ib + col) * W::LDA + 32 * cb + 8 * grp));
+    for (int ib = 0; ib < NIB; ++ib)
+      mma(Tm[ib], Yv[cb], ld8(sKT + (ri + 16 * ib + col) * W::LDA + 32 * cb + 8 * grp));
   }
 }
 
-// grid: ntile * (SP / RT) * BH workgroups of 256 threads; each wave owns 16 of the 64 columns.
-template <typename T, int SP, int RT, int CP, int G, bool REV>
-__global__ __launch_bounds__(256) void walk_kernel(WalkIO w, int ntile) {
-  using W = WalkIOCfg<T, RT, CP, G>;
-  constexpr int LDV = W::LDV, NIB = RT / 16, NRT = SP / RT, R = kWalkDepth;
+// grid: ntile * (SP / RT) * BH workgroups of 64 NW threads.  Wave w owns columns 16 (w % 4)
+// .. +15 of the 64 and rows RW (w / 4) .. +RW-1 of the RT, RW = 4 RT / NW.
+template <typename T, int SP, int RT, int CP, int G, bool REV, int NW>
+__device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
+  constexpr int NT = 64 * NW, RW = RT * 4 / NW;
+  static_assert(NW == 4 || NW == 8, "four column waves, one or two row groups");
+  using W = WalkIOCfg<T, RT, CP, G, NT>;
+  using Stage = WalkIOStage<T, RT, CP, NT>;
+  constexpr int LDV = W::LDV, NIB = RW / 16, NRT = SP / RT, R = kWalkDepth;
   __shared__ __attribute__((aligned(16))) char smem[W::BYTES];
 
-  const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int tile = lin % ntile, rt = (lin / ntile) % NRT, bh = lin / (ntile * NRT);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int cw = 16 * (wave & 3), ri = RW * (wave >> 2);    // this wave's columns and rows
   const int Ds = w.Ds, L = w.L, C = w.C, N = w.N;
   const int NG = (N + G - 1) / G;
   const int DsP = ntile * kDvTile, i0 = rt * RT;
-  const int j0 = tile * kDvTile + 16 * wave + 4 * grp;     // this lane's four columns
+  const int j0 = tile * kDvTile + cw + 4 * grp;             // this lane's four columns
   typedef typename Vec4<T>::type V4T;
-  const T* src = reinterpret_cast<const T*>(w.src) + (size_t)bh * L * Ds;
+  const T* src = reinterpret_cast<const T*>(w.src) + (size_t)w.in(bh) * L * Ds;
   const T* mat = reinterpret_cast<const T*>(w.mat) + ((size_t)bh * N * SP + i0) * CP;
   const float* gam = w.gam + (size_t)bh * N * SP + i0;
   T* out = reinterpret_cast<T*>(w.states) + ((size_t)bh * N * SP + i0) * DsP + tile * kDvTile;
@@ -235,21 +243,21 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkIO w, int ntile) {
   for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = i0 + 16 * ib + col, j = j0 + e;
+      const int i = i0 + ri + 16 * ib + col, j = j0 + e;
       S[ib][e] = (w.init && j < Ds && i < w.rows) ? w.init[walk_state_index(w, bh, i, j)] : 0.f;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);                   // initial state in before the pipeline starts
 
-  WalkIOStage<T, RT, CP> st[R][G];
-  auto load = [&](WalkIOStage<T, RT, CP> (&s)[G], int kg) {   // past the end: reload the last chunk
+  Stage st[R][G];
+  auto load = [&](Stage (&s)[G], int kg) {   // past the end: reload the last chunk
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int n = chunk_of(min(kg * G + g, N - 1)), row0 = n * C;
       s[g].load(mat + (size_t)n * SP * CP, src, row0, min(C, L - row0), Ds, tile, gam + (size_t)n * SP);
     }
   };
-  auto store = [&](const WalkIOStage<T, RT, CP> (&s)[G], int b) {
+  auto store = [&](const Stage (&s)[G], int b) {
 #pragma unroll
     for (int g = 0; g < G; ++g) s[g].store(sKT(b, g), sV(b, g), sG(b, g));
   };
@@ -269,17 +277,17 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkIO w, int ntile) {
     load(st[r], kg + R);                         // st[r] (group kg) is already in LDS
     f32x4 Tm[G][NIB];
 #pragma unroll
-    for (int g = 0; g < G; ++g) walk_product<T, RT, CP>(Tm[g], sKT(b, g), sV(b, g));
+    for (int g = 0; g < G; ++g) walk_product<T, RT, CP, RW>(Tm[g], sKT(b, g), sV(b, g), ri, cw);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int k = kg * G + g;
       if (!CHECK || k < N) {
         const float* gg = sG(b, g);
-        T* ho = sHo(b, g) + col * LDV + 16 * wave + 4 * grp;
+        T* ho = sHo(b, g) + (ri + col) * LDV + cw + 4 * grp;
 #pragma unroll
         for (int ib = 0; ib < NIB; ++ib) {
           V4T hv;
-          const float dec = fast_exp2(gg[16 * ib + col]);
+          const float dec = fast_exp2(gg[ri + 16 * ib + col]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             hv[e] = from_f32<T>(S[ib][e]);
@@ -294,7 +302,7 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkIO w, int ntile) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int k = kg * G + g;
-      if (!CHECK || k < N) state_tile_out<T, RT>(out + (size_t)chunk_of(k) * SP * DsP, sHo(b, g), LDV, DsP);
+      if (!CHECK || k < N) state_tile_out<T, RT, NT>(out + (size_t)chunk_of(k) * SP * DsP, sHo(b, g), LDV, DsP);
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -323,11 +331,23 @@ __global__ __launch_bounds__(256) void walk_kernel(WalkIO w, int ntile) {
     for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int i = i0 + 16 * ib + col, j = j0 + e;
+        const int i = i0 + ri + 16 * ib + col, j = j0 + e;
         if (i < w.rows && j < Ds) w.fin[walk_state_index(w, bh, i, j)] = S[ib][e];
       }
     }
   }
+}
+
+template <typename T, int SP, int RT, int CP, int G, bool REV, int NW>
+__global__ __launch_bounds__(64 * NW) void walk_kernel(WalkIO w, int ntile) {
+  walk_tile<T, SP, RT, CP, G, REV, NW>(w, ntile, xcd_remap(blockIdx.x, gridDim.x));
+}
+
+// several batches in one launch (see Batches): batch i owns blocks first[i] .. first[i+1] - 1
+template <typename T, int SP, int RT, int CP, int G, bool REV, int NW>
+__global__ __launch_bounds__(64 * NW) void walk_batches(Batches<WalkIO> b, int ntile) {
+  const int gi = b.find(blockIdx.x);
+  walk_tile<T, SP, RT, CP, G, REV, NW>(b.p[gi], ntile, blockIdx.x - b.first[gi]);
 }
 
 template <typename T, int SP, int CP, bool REV>
@@ -340,13 +360,28 @@ hipError_t launch_walk(const WalkIO& w, int BH, hipStream_t s) {
     if constexpr (P::WIDE) {
       const int cus = device_cu_count();
       if (cus > 0 && ntile * (SP / 64) * BH >= cus) {
-        hipLaunchKernelGGL((walk_kernel<T, SP, 64, CP, 2, REV>), dim3(ntile * (SP / 64) * BH), dim3(256), 0, s, w,
-                           ntile);
+        hipLaunchKernelGGL((walk_kernel<T, SP, 64, CP, 2, REV, 8>), dim3(ntile * (SP / 64) * BH), dim3(512), 0, s,
+                           w, ntile);
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((walk_kernel<T, SP, P::RT, CP, P::G, REV>), dim3(ntile * (SP / P::RT) * BH), dim3(256), 0, s,
-                       w, ntile);
+    hipLaunchKernelGGL((walk_kernel<T, SP, P::RT, CP, P::G, REV, 4>), dim3(ntile * (SP / P::RT) * BH), dim3(256), 0,
+                       s, w, ntile);
+    return hipGetLastError();
+  }
+}
+// b.p[i] with BH[i] sequences each; the launch sets b.first
+template <typename T, int SP, int CP>
+hipError_t launch_walk_store_batches(Batches<WalkIO> b, const int* BH, hipStream_t s) {
+  using P = WalkPlan<T, SP, CP>;
+  if constexpr (!P::OK) {
+    return hipErrorNotSupported;
+  } else {
+    const int ntile = (b.p[0].Ds + kDvTile - 1) / kDvTile;
+    b.first[0] = 0;
+    for (int i = 0; i < b.n; ++i) b.first[i + 1] = b.first[i] + ntile * (SP / P::RT) * BH[i];
+    hipLaunchKernelGGL((walk_batches<T, SP, P::RT, CP, P::G, false, 4>), dim3(b.first[b.n]), dim3(256), 0, s, b,
+                       ntile);
     return hipGetLastError();
   }
 }

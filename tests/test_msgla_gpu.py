@@ -50,6 +50,7 @@ SHAPES = [
     (1, 4, 200, 64, 64, 32, "f32", (1, 2, 4, 8), (1, 1, 1, 1), True, True),
     (1, 2, 10, 64, 64, 16, "bf16", (1, 16), (1, 1), True, True),        # a scale longer than L
     (2, 5, 257, 128, 128, 64, "bf16", (4, 1), (3, 2), False, True),      # coarse group first
+    (2, 5, 190, 64, 128, 64, "bf16", (2, 1, 4), (1, 3, 1), True, True),  # in-place group in the middle
 ]
 
 
@@ -62,8 +63,8 @@ def test_small_shapes(gla, shape):
 
 
 def test_single_group_at_scale_one_is_gla_fwd(gla):
-    """One group at scale 1 with no weights is gla_fwd itself, bit for bit: the gather copies
-    exactly and the hold multiplies by 1."""
+    """One group at scale 1 with no weights is gla_fwd itself, bit for bit: the group reads the
+    inputs in place and the hold multiplies by 1."""
     import torch
     w = W.GlaWorkload("msgla-id", 2, 3, 200, 64, 128, 64, "bf16", 711, h0=True, gate_law="iid")
     x = W.gla_inputs(w, with_grad=False)
