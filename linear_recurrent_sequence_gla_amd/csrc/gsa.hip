@@ -95,29 +95,33 @@ __global__ __launch_bounds__(256) void gsa_prep_kernel(GsaParams p) {
   if (threadIdx.x < MP) p.Gam[chunk * MP + threadIdx.x] = sGam[threadIdx.x];
 }
 
-// A [ROWS][64] column slice of a row-major [*, ld] tensor held in registers, 16 bytes per
-// vector, vector j of thread t covering row (t + 256 j) / 8 (bf16; / 16 for fp32).  Rows
-// < nrows and columns < ncols are valid.  load() clamps its addresses into that range, so its
-// loads are unconditional and can be issued one slice ahead of their use; store() writes the
-// slice into LDS with zeros outside the valid range.
-template <typename T, int ROWS>
+// A [ROWS][64] column slice of a row-major [*, ld] tensor held in registers by NT threads,
+// 16 bytes per vector: vector j of thread t is item t + NT j, row item / 8 (bf16; / 16 for
+// fp32).  Rows < nrows and columns < ncols are valid.  load() clamps its addresses into that
+// range, so its loads are unconditional and can be issued one slice ahead of their use;
+// store() writes the slice into LDS with zeros outside the valid range.
+template <typename T, int ROWS, int NT = 256>
 struct SliceRegs {
-  static constexpr int V = V16<T>::N, PER_ROW = kDvTile / V, N = ROWS * PER_ROW / 256;
-  static_assert(N >= 1 && ROWS * PER_ROW % 256 == 0, "slice rows");
+  static constexpr int V = V16<T>::N, PER_ROW = kDvTile / V, ITEMS = ROWS * PER_ROW;
+  static constexpr int N = (ITEMS + NT - 1) / NT;
   typedef typename V16<T>::type VT;
   VT x[N];
+  // item j of this thread exists (always, when the items divide evenly over the threads)
+  __device__ __forceinline__ static bool has(int j) { return ITEMS % NT == 0 || (int)threadIdx.x + NT * j < ITEMS; }
   __device__ __forceinline__ void load(const T* src, size_t ld, int nrows, int col0, int ncols) {
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const int idx = threadIdx.x + 256 * j, r = idx / PER_ROW, c = col0 + (idx % PER_ROW) * V;
+      const int idx = min((int)threadIdx.x + NT * j, ITEMS - 1), r = idx / PER_ROW;
+      const int c = col0 + (idx % PER_ROW) * V;
       x[j] = *reinterpret_cast<const VT*>(src + (size_t)min(r, nrows - 1) * ld + min(c, ncols - V));
     }
   }
   __device__ __forceinline__ void store(T* dst, int lds, int nrows, int col0, int ncols) const {
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const int idx = threadIdx.x + 256 * j, r = idx / PER_ROW, c = (idx % PER_ROW) * V;
-      *reinterpret_cast<VT*>(dst + r * lds + c) = (r < nrows && col0 + c < ncols) ? x[j] : zero_vec<T>();
+      const int idx = threadIdx.x + NT * j, r = idx / PER_ROW, c = (idx % PER_ROW) * V;
+      if (has(j))
+        *reinterpret_cast<VT*>(dst + r * lds + c) = (r < nrows && col0 + c < ncols) ? x[j] : zero_vec<T>();
     }
   }
 };
@@ -375,15 +379,22 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
 }
 
 // ----------------------------------------------------------------------------- pass 1 backward
+// Eight waves: the two waves (rb, 0) and (rb, 1) of 16-row block rb split its column blocks by
+// parity, so each holds half the accumulators and a CU runs two waves per SIMD.  The scans
+// keep the 256-thread layout (the upper 256 threads sit them out).
+constexpr int kP1Threads = 512;
+
 template <typename T, int MP, int CP>
-__global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk) {
+__global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, int ntk) {
   using G = GsaCfg<T, MP, CP>;
   using M = ChunkMap<T, MP, CP>;
+  constexpr int NT = kP1Threads;
   constexpr int V = M::V, RPS = M::RPS, NSEG = M::NSEG, NCG = M::NCG;
   constexpr int LDF = G::LDF, LDQK = G::LDQK, LDS = G::LDS, NRB = G::NRB, NSB = G::NSB;
+  constexpr int NRH = (NRB + 1) / 2, NSH = NSB / 2, NIH = kDvTile / 32;   // column blocks per half
   typedef typename V16<T>::type VT;
-  using SC = SliceRegs<T, CP>;
-  using SM = SliceRegs<T, MP>;
+  using SC = SliceRegs<T, CP, NT>;
+  using SM = SliceRegs<T, MP, NT>;
   __shared__ __attribute__((aligned(16))) char smem[G::B_BYTES];
   float* sB = reinterpret_cast<float*>(smem);
   float* sW = sB + CP * LDF;
@@ -472,7 +483,7 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
     for (int u = 0; u < RPS; ++u) sDiag[r0 + u] = dsum[u];
   }
   __syncthreads();
-  const int rb = wave;
+  const int rb = wave & 3, hf = wave >> 2;   // row block; which parity of column blocks
   const bool rbv = rb < NRB;
 
   // (dZ E) on this lane's operand row 16 rb + col: the row operand of dQK and of dq's state term
@@ -491,7 +502,9 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
   // ---- dQK = mask_{c<=r}((dZ E)(W Ei)^T), with the diagonal from sDiag
   if (rbv) {
 #pragma unroll
-    for (int cb = 0; cb < NRB; ++cb) {
+    for (int ch = 0; ch < NRH; ++ch) {
+      const int cb = 2 * ch + hf;
+      if (cb >= NRB) break;
       f32x4 acc = zero4();
       if (cb <= rb) {
         if (fast) {
@@ -556,11 +569,11 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
 
   // ---- Dk slices: QK, Ze, B1 accumulate; dq, dk slices written; the next slice is loaded
   // while this one is used
-  f32x4 accQK[NRB], accZe[NSB], accB1[NSB];
+  f32x4 accQK[NRH], accZe[NSH], accB1[NSH];   // column blocks 2 i + hf
 #pragma unroll
-  for (int c = 0; c < NRB; ++c) accQK[c] = zero4();
+  for (int c = 0; c < NRH; ++c) accQK[c] = zero4();
 #pragma unroll
-  for (int s = 0; s < NSB; ++s) accZe[s] = accB1[s] = zero4();
+  for (int s = 0; s < NSH; ++s) accZe[s] = accB1[s] = zero4();
   float z1[SM::N];                       // partial colsum(dS1 * S1) over this thread's slice rows
 #pragma unroll
   for (int j = 0; j < SM::N; ++j) z1[j] = 0.f;
@@ -572,8 +585,10 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
     rd.store(sdS1, LDS, MP, ds * kDvTile, DkP);
 #pragma unroll
     for (int j = 0; j < SM::N; ++j) {
+      if (SM::has(j)) {
 #pragma unroll
-      for (int e = 0; e < V; ++e) z1[j] += to_f32(rs.x[j][e]) * to_f32(rd.x[j][e]);
+        for (int e = 0; e < V; ++e) z1[j] += to_f32(rs.x[j][e]) * to_f32(rd.x[j][e]);
+      }
     }
     if (ds + 1 < ntk) {
       rq.load(qg, Dk, len, (ds + 1) * kDvTile, Dk);
@@ -588,17 +603,21 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
         const Frag<T> Xq = ld8(sq + (16 * rb + col) * LDS + 32 * kb + 8 * grp);
         const Frag<T> Xk = ld8(sk + (16 * rb + col) * LDS + 32 * kb + 8 * grp);
 #pragma unroll
-        for (int cb = 0; cb < NRB; ++cb)
-          if (cb <= rb) mma(accQK[cb], Xq, ld8(sk + (16 * cb + col) * LDS + 32 * kb + 8 * grp));
+        for (int ch = 0; ch < NRH; ++ch) {
+          const int cb = 2 * ch + hf;
+          if (cb <= rb) mma(accQK[ch], Xq, ld8(sk + (16 * cb + col) * LDS + 32 * kb + 8 * grp));
+        }
 #pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) {
-          mma(accZe[sb], Xq, ld8(sS1 + (16 * sb + col) * LDS + 32 * kb + 8 * grp));
-          mma(accB1[sb], Xk, ld8(sdS1 + (16 * sb + col) * LDS + 32 * kb + 8 * grp));
+        for (int sh = 0; sh < NSH; ++sh) {
+          const int sb = 2 * sh + hf;
+          mma(accZe[sh], Xq, ld8(sS1 + (16 * sb + col) * LDS + 32 * kb + 8 * grp));
+          mma(accB1[sh], Xk, ld8(sdS1 + (16 * sb + col) * LDS + 32 * kb + 8 * grp));
         }
       }
       // dq slice = dQK K + (dZ E) S1^T ; dk slice = dQK^T Q + (W Eg) dS1^T
 #pragma unroll
-      for (int ib = 0; ib < kDvTile / 16; ++ib) {
+      for (int ih = 0; ih < NIH; ++ih) {
+        const int ib = 2 * ih + hf;
         f32x4 aq = zero4(), ak = zero4();
 #pragma unroll
         for (int kc = 0; kc < CP / 32; ++kc) {
@@ -619,7 +638,7 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
     }
     __syncthreads();
     constexpr int PER_ROW = kDvTile / V;
-    for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
+    for (int idx = tid; idx < CP * PER_ROW; idx += NT) {
       const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
       const int cc = ds * kDvTile + c;
       if (r < len && cc < Dk) {
@@ -641,23 +660,25 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
       for (int e4 = 0; e4 < V / 4; ++e4) g2v[u][e4] = *reinterpret_cast<const f32x4*>(p.dg2 + off + 4 * e4);
     }
   }
-  // Z1_n = 2^Gamma colsum(dS1_{n+1} * S1_n): slot row (tid + 256 j) / PER_ROW, summed over the
+  // Z1_n = 2^Gamma colsum(dS1_{n+1} * S1_n): slot row (tid + NT j) / PER_ROW, summed over the
   // PER_ROW consecutive lanes that share it
 #pragma unroll
   for (int j = 0; j < SM::N; ++j) {
 #pragma unroll
     for (int o = 1; o < SM::PER_ROW; o <<= 1) z1[j] += __shfl_xor(z1[j], o, 64);
-    const int idx = tid + 256 * j, zs = idx / SM::PER_ROW;
-    if (idx % SM::PER_ROW == 0) sZ1[zs] = zs < m ? z1[j] * fast_exp2(sGam[zs]) : 0.f;
+    const int idx = tid + NT * j, zs = idx / SM::PER_ROW;
+    if (SM::has(j) && idx % SM::PER_ROW == 0) sZ1[zs] = zs < m ? z1[j] * fast_exp2(sGam[zs]) : 0.f;
   }
   __syncthreads();   // slices and dQK dead: sQK and the dg tiles take their bytes
   if (rbv) {
 #pragma unroll
-    for (int cb = 0; cb < NRB; ++cb) {
+    for (int ch = 0; ch < NRH; ++ch) {
+      const int cb = 2 * ch + hf;
+      if (cb >= NRB) break;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
-        sQK[r * LDQK + c] = c <= r ? accQK[cb][e] : 0.f;
+        sQK[r * LDQK + c] = c <= r ? accQK[ch][e] : 0.f;
       }
     }
   }
@@ -666,7 +687,8 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
   // ---- per element (rows of this wave): Znd, dW1', B1 -> u, y, dW1 total
   if (rbv) {
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
+    for (int sh = 0; sh < NSH; ++sh) {
+      const int sb = 2 * sh + hf;
       f32x4 zi = zero4(), w1 = zero4();
       if (fast) {
 #pragma unroll
@@ -699,8 +721,8 @@ __global__ __launch_bounds__(256) void gsa_pass1_bwd_kernel(GsaParams p, int ntk
           for (int c = r + 1; c < CP; ++c)
             dw1p += sQK[c * LDQK + r] * sdZ[c * LDF + s] * fast_exp2(sB[c * LDF + s] - br);
         }
-        const float znd = zip + fast_exp2(br) * accZe[sb][e];
-        const float b1 = fast_exp2(sGam[s] - br) * accB1[sb][e];
+        const float znd = zip + fast_exp2(br) * accZe[sh][e];
+        const float b1 = fast_exp2(sGam[s] - br) * accB1[sh][e];
         const float dz = sdZ[r * LDF + s], w = sW[r * LDF + s];
         sU[r * LDF + s] = dz * znd - w * dw1p;
         sY[r * LDF + s] = w * b1;
@@ -830,7 +852,7 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
     WalkIO w1r{p.dZsT, p.q, p.Gam, p.dS1s, p.dhkt, p.dhk0, p.m, p.Dk, p.L, p.C, p.N, 1};
     if ((e = launch_walk_reverse<T, MP, CP>(w1r, p.BH, s)) != hipSuccess) return e;
     const int ntk = p.DkP / kDvTile;
-    hipLaunchKernelGGL((gsa_pass1_bwd_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p, ntk);
+    hipLaunchKernelGGL((gsa_pass1_bwd_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(kP1Threads), 0, s, p, ntk);
     return hipGetLastError();
   }
 }
