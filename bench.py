@@ -300,6 +300,8 @@ def run_gsa_decode(torch, m, steps=256):
 
 
 def run_gsa(torch, m, steps=10, warmup=3):
+    """GSA fwd+bwd at its workload: gsa_fwd_save then gsa_bwd_saved (the training-step form, as
+    for GLA), with the recomputing gsa_fwd + gsa_bwd timed beside it."""
     w = W.WORKLOADS["gsa_340m"]
     lib = m.lib()
     if lib.gsa_fwd_workspace_bytes(w.B, w.H, w.L, w.Dk, w.Dv, w.m, w.C, 1) == 0:
@@ -307,20 +309,41 @@ def run_gsa(torch, m, steps=10, warmup=3):
     x = W.gsa_inputs(w)
     dt = torch.bfloat16
     d = {n: torch.from_numpy(x[n]).to("cuda", dt).contiguous() for n in ("q", "k", "v", "g", "do")}
-    for _ in range(warmup):
-        m.gsa_fwd(d["q"], d["k"], d["v"], d["g"], C=w.C)
-        m.gsa_bwd(d["q"], d["k"], d["v"], d["g"], d["do"], C=w.C)
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
-        m.gsa_fwd(d["q"], d["k"], d["v"], d["g"], C=w.C)
-        m.gsa_bwd(d["q"], d["k"], d["v"], d["g"], d["do"], C=w.C)
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / steps
-    return {"workload": f"gsa B={w.B} H={w.H} L={w.L} Dk={w.Dk} Dv={w.Dv} m={w.m} C={w.C} fwd+bwd",
-            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / ms * 1e3, 1)}
+    args = (d["q"], d["k"], d["v"], d["g"])
+    saved = torch.empty(m.gsa_saved_bytes(w.B, w.H, w.L, w.Dk, w.Dv, w.m, w.C, dt), dtype=torch.uint8,
+                        device="cuda")
+    ws = torch.empty(m.gsa_bwd_saved_workspace_bytes(w.B, w.H, w.L, w.Dk, w.Dv, w.m, w.C, dt),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty(w.B, w.H, w.L, w.Dv, device="cuda", dtype=dt)
+    outs = (torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]),
+            torch.empty(w.B, w.H, w.L, w.m, device="cuda"), None, None)
+
+    def saved_step():
+        m.gsa_fwd_save(*args, C=w.C, output_final_state=False, saved=saved, out=o)
+        m.gsa_bwd_saved(*args, d["do"], saved, C=w.C, workspace=ws, outs=outs)
+
+    def recompute_step():
+        m.gsa_fwd(*args, C=w.C)
+        m.gsa_bwd(*args, d["do"], C=w.C)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps
+
+    ms = timed(saved_step)
+    ms_re = timed(recompute_step)
+    return {"workload": f"gsa B={w.B} H={w.H} L={w.L} Dk={w.Dk} Dv={w.Dv} m={w.m} C={w.C} fwd+bwd "
+                        "(gsa_fwd_save + gsa_bwd_saved)",
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / ms * 1e3, 1),
+            "recomputing_ms_per_step": round(ms_re, 4)}
 
 
 def run_msgla(torch, m, steps=10, warmup=3):

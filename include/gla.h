@@ -214,6 +214,36 @@ int gsa_bwd(const void* q, const void* k, const void* v, const void* g,
             int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, int act,
             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- GSA saved activations --
+ * As for GLA: gsa_bwd recomputes the forward's intermediate tensors (the write weights
+ * w = 1 - exp(g), the pass-1 chunk operands and chunk-start states, the read-out p and its
+ * float32 copy, pass 2's chunk operands and chunk-start states), which gsa_fwd_save /
+ * gsa_bwd_saved avoid by keeping them:
+ *   gsa_fwd_save   computes exactly what gsa_fwd computes and also leaves them in `saved`;
+ *   gsa_bwd_saved  computes exactly what gsa_bwd computes, reading them from `saved`.
+ * saved: device buffer of at least gsa_saved_bytes() bytes, owned by the caller; its contents
+ *   on entry to gsa_fwd_save do not matter, and gsa_bwd_saved only reads it.  It is valid for
+ *   the q, k, g, hk0, hv0, C, dtype and act of the gsa_fwd_save call that filled it; passing
+ *   other inputs to gsa_bwd_saved gives undefined results (the library cannot check this).
+ *   NULL saved in gsa_bwd_saved: GLA_ERR_NULL_ARG.
+ * workspace (gsa_bwd_saved): at least gsa_bwd_saved_workspace_bytes() bytes.
+ * Sizes, dtypes, alignment and errors as for gsa_bwd (the saved path supports the sizes the
+ * backward supports); `saved` must not overlap any input or output (GLA_ERR_ALIAS). */
+size_t gsa_saved_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype);
+size_t gsa_bwd_saved_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype);
+int gsa_fwd_save(const void* q, const void* k, const void* v, const void* g,
+                 const float* hk0, const float* hv0,
+                 void* o, float* hkt, float* hvt,
+                 int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, int act,
+                 void* saved, size_t saved_bytes, void* stream);
+int gsa_bwd_saved(const void* q, const void* k, const void* v, const void* g,
+                  const float* hk0, const float* hv0,
+                  const void* do_, const float* dhkt, const float* dhvt,
+                  void* dq, void* dk, void* dv, float* dg, float* dhk0, float* dhv0,
+                  int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, int act,
+                  const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                  void* stream);
+
 /* ---------------------------------------------------------------- GSA decode -----------
  * One recurrent inference step of gated slot attention per (batch, head): the fixed-size
  * slot memories are updated with the token and read through a softmax over the m slots

@@ -34,6 +34,7 @@ __all__ = [
     "gsa_fwd", "gsa_bwd", "gsa_decode_step", "gla_saved_bytes", "gla_bwd_saved_workspace_bytes",
     "gla_fwd_workspace_bytes", "gla_bwd_workspace_bytes", "gsa_fwd_workspace_bytes",
     "gsa_bwd_workspace_bytes", "EXPORTED_SYMBOLS", "GSA_ACTS", "msgla_fwd", "msgla_fwd_workspace_bytes",
+    "gsa_fwd_save", "gsa_bwd_saved", "gsa_saved_bytes", "gsa_bwd_saved_workspace_bytes",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +75,10 @@ _SIGS = {
     "gsa_fwd": (_I, [_P] * 9 + [_I] * 9 + [_P, _Z, _P]),
     "gsa_bwd_workspace_bytes": (_Z, [_I] * 8),
     "gsa_bwd": (_I, [_P] * 15 + [_I] * 9 + [_P, _Z, _P]),
+    "gsa_saved_bytes": (_Z, [_I] * 8),
+    "gsa_bwd_saved_workspace_bytes": (_Z, [_I] * 8),
+    "gsa_fwd_save": (_I, [_P] * 9 + [_I] * 9 + [_P, _Z, _P]),
+    "gsa_bwd_saved": (_I, [_P] * 15 + [_I] * 9 + [_P, _Z, _P, _Z, _P]),
     "gsa_decode_step": (_I, [_P] * 7 + [_I] * 7 + [_P]),
     "msgla_fwd_workspace_bytes": (_Z, [_I] * 8 + [_P, _P]),
     "msgla_fwd": (_I, [_P] * 8 + [_I] * 8 + [_P, _P, _P, _Z, _P]),
@@ -381,6 +386,75 @@ def gsa_bwd(q, k, v, g, do, C: int = 64, hk0=None, hv0=None, dhkt=None, dhvt=Non
     _check(L_.gsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(hk0), _ptr(hv0), _ptr(do), _ptr(dhkt), _ptr(dhvt),
                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dhk0), _ptr(dhv0),
                       B, H, L, Dk, Dv, m, C, _DT[dt], _act(act), _ptr(ws), ws.numel(), _stream(dev)))
+    return dq, dk, dv, dg, dhk0, dhv0
+
+
+def gsa_saved_bytes(B, H, L, Dk, Dv, m, C, dtype) -> int:
+    return int(lib().gsa_saved_bytes(B, H, L, Dk, Dv, m, C, _DT[dtype]))
+
+
+def gsa_bwd_saved_workspace_bytes(B, H, L, Dk, Dv, m, C, dtype) -> int:
+    return int(lib().gsa_bwd_saved_workspace_bytes(B, H, L, Dk, Dv, m, C, _DT[dtype]))
+
+
+def gsa_fwd_save(q, k, v, g, C: int = 64, hk0=None, hv0=None, output_final_state: bool = True, *,
+                 act: str = "softmax", saved=None, out=None):
+    """gsa_fwd that also keeps the forward's intermediate tensors for gsa_bwd_saved.
+    Returns (o, hkt, hvt, saved)."""
+    B, H, L, Dk, Dv, dev, dt = _common(q, k, v, g, gate_width=True)
+    m = g.shape[-1]
+    if hk0 is not None:
+        _need(hk0, "hk0", (B, H, Dk, m), torch.float32, dev)
+    if hv0 is not None:
+        _need(hv0, "hv0", (B, H, m, Dv), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, H, L, Dv), dtype=dt, device=dev)
+    hkt = hvt = None
+    if output_final_state:
+        hkt = torch.empty((B, H, Dk, m), dtype=torch.float32, device=dev)
+        hvt = torch.empty((B, H, m, Dv), dtype=torch.float32, device=dev)
+    L_ = lib()
+    nbytes = L_.gsa_saved_bytes(B, H, L, Dk, Dv, m, C, _DT[dt])
+    if nbytes == 0:
+        _check(L_.gsa_fwd_save(*([None] * 9), B, H, L, Dk, Dv, m, C, _DT[dt], _act(act), None, 0, None))
+    sv = _workspace(nbytes, dev, saved)
+    _check(L_.gsa_fwd_save(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(hk0), _ptr(hv0), _ptr(o), _ptr(hkt),
+                           _ptr(hvt), B, H, L, Dk, Dv, m, C, _DT[dt], _act(act), _ptr(sv), sv.numel(),
+                           _stream(dev)))
+    return o, hkt, hvt, sv
+
+
+def gsa_bwd_saved(q, k, v, g, do, saved, C: int = 64, hk0=None, hv0=None, dhkt=None, dhvt=None,
+                  want_dh0: bool = False, *, act: str = "softmax", workspace=None, outs=None):
+    """gsa_bwd reusing what gsa_fwd_save left in `saved` for the same q, k, g, hk0, hv0, C and act.
+    Returns (dq, dk, dv, dg, dhk0-or-None, dhv0-or-None)."""
+    B, H, L, Dk, Dv, dev, dt = _common(q, k, v, g, gate_width=True)
+    m = g.shape[-1]
+    _need(do, "do", (B, H, L, Dv), dt, dev)
+    for t, n, s in ((hk0, "hk0", (B, H, Dk, m)), (hv0, "hv0", (B, H, m, Dv)),
+                    (dhkt, "dhkt", (B, H, Dk, m)), (dhvt, "dhvt", (B, H, m, Dv))):
+        if t is not None:
+            _need(t, n, s, torch.float32, dev)
+    if outs is None:
+        dq = torch.empty((B, H, L, Dk), dtype=dt, device=dev)
+        dk = torch.empty((B, H, L, Dk), dtype=dt, device=dev)
+        dv = torch.empty((B, H, L, Dv), dtype=dt, device=dev)
+        dg = torch.empty((B, H, L, m), dtype=torch.float32, device=dev)
+        dhk0 = torch.empty((B, H, Dk, m), dtype=torch.float32, device=dev) if want_dh0 else None
+        dhv0 = torch.empty((B, H, m, Dv), dtype=torch.float32, device=dev) if want_dh0 else None
+    else:
+        dq, dk, dv, dg, dhk0, dhv0 = outs
+    L_ = lib()
+    nbytes = L_.gsa_bwd_saved_workspace_bytes(B, H, L, Dk, Dv, m, C, _DT[dt])
+    if nbytes == 0:
+        _check(L_.gsa_bwd_saved(*([None] * 15), B, H, L, Dk, Dv, m, C, _DT[dt], _act(act), None, 0, None, 0,
+                                None))
+    if not isinstance(saved, torch.Tensor) or saved.device != dev:
+        raise ValueError(f"saved must be the tensor gsa_fwd_save returned, on {dev}")
+    ws = _workspace(nbytes, dev, workspace)
+    _check(L_.gsa_bwd_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(hk0), _ptr(hv0), _ptr(do), _ptr(dhkt),
+                            _ptr(dhvt), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dhk0), _ptr(dhv0),
+                            B, H, L, Dk, Dv, m, C, _DT[dt], _act(act), _ptr(saved),
+                            saved.numel() * saved.element_size(), _ptr(ws), ws.numel(), _stream(dev)))
     return dq, dk, dv, dg, dhk0, dhv0
 
 

@@ -15,7 +15,7 @@ using namespace gla;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr size_t kAlign = 256;
 
 bool valid_act(int act) { return act >= GSA_ACT_SOFTMAX && act <= GSA_ACT_NONE; }
@@ -533,51 +533,65 @@ struct GsaLayout {
   OpsLayout ops2;
 };
 
-GsaLayout gsa_layout(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, bool bwd) {
+// Parts of the GSA device memory.  FWD: the forward's own tensors.  SAVED: those plus what only
+// the backward reads (the fp32 read-out Pf, pass 2's Qs^T operand) -- what gsa_fwd_save leaves
+// for gsa_bwd_saved.  GRAD: the backward's gradient buffers.  gsa_bwd keeps SAVED and GRAD in
+// one workspace.
+enum { kGsaFwd = 1, kGsaSaved = 2, kGsaGrad = 4 };
+
+GsaLayout gsa_layout_of(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, int parts) {
   const size_t BH = (size_t)B * H, es = esize_of(dtype), MP = pad_dk(m), CP = pad_c(C);
   const size_t N = (L + C - 1) / C, DkP = pad_dv(Dk), DvP = pad_dv(Dv);
   const size_t tok = BH * L * m;
+  const bool fwd = parts & (kGsaFwd | kGsaSaved), saved = parts & kGsaSaved, grad = parts & kGsaGrad;
   GsaLayout l{};
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
-  l.W = take(tok * es);
-  l.P = take(tok * es);
-  l.WdT = take(BH * N * MP * CP * es);
-  l.Gam = take(BH * N * MP * 4);
-  l.S1s = take(BH * N * MP * DkP * es);
-  if (bwd) {
-    l.Pf = take(tok * 4);
+  if (fwd) {
+    l.W = take(tok * es);
+    l.P = take(tok * es);
+    l.WdT = take(BH * N * MP * CP * es);
+    l.Gam = take(BH * N * MP * 4);
+    l.S1s = take(BH * N * MP * DkP * es);
+    if (saved) l.Pf = take(tok * 4);
+    l.ops2 = ops_layout(BH, N, CP, MP, es, saved);
+    l.ops2base = take(l.ops2.total);
+    l.Hs2 = take(BH * N * MP * DvP * es);
+  }
+  if (grad) {
     l.dP = take(tok * es);
     l.dW2 = take(tok * es);
     l.dg2 = take(tok * 4);
     l.dZ = take(tok * 4);
     l.dS1s = take(BH * N * MP * DkP * es);
     l.dZsT = take(BH * N * MP * CP * es);
-  }
-  l.ops2 = ops_layout(BH, N, CP, MP, es, bwd);
-  l.ops2base = take(l.ops2.total);
-  l.Hs2 = take(BH * N * MP * DvP * es);
-  if (bwd) {
     l.dHs2 = take(BH * N * MP * DvP * es);
   }
   l.total = off;
   return l;
 }
 
-GsaParams gsa_params(const GsaLayout& l, char* ws, int B, int H, int L, int Dk, int Dv, int m, int C, bool bwd) {
+GsaLayout gsa_layout(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, bool bwd) {
+  return gsa_layout_of(B, H, L, Dk, Dv, m, C, dtype, bwd ? (kGsaSaved | kGsaGrad) : kGsaFwd);
+}
+
+// lf/fb: the forward tensors (FWD or SAVED layout) and their base; lg/gb: the gradient buffers
+// (GRAD layout) and their base, or null for a forward
+GsaParams gsa_params(const GsaLayout& lf, char* fb, bool saved, const GsaLayout& lg, char* gb, int B, int H, int L,
+                     int Dk, int Dv, int m, int C) {
   GsaParams p{};
   p.BH = B * H; p.L = L; p.Dk = Dk; p.DkP = pad_dv(Dk); p.Dv = Dv; p.m = m; p.C = C; p.N = (L + C - 1) / C;
-  p.W = ws + l.W; p.P = ws + l.P; p.WdT = ws + l.WdT; p.Gam = reinterpret_cast<float*>(ws + l.Gam);
-  p.S1s = ws + l.S1s;
-  if (bwd) {
-    p.Pf = reinterpret_cast<float*>(ws + l.Pf);
-    p.dP = ws + l.dP; p.dW2 = ws + l.dW2;
-    p.dg2 = reinterpret_cast<float*>(ws + l.dg2); p.dZ = reinterpret_cast<float*>(ws + l.dZ);
-    p.dS1s = ws + l.dS1s; p.dZsT = ws + l.dZsT;
-    p.dHs2 = ws + l.dHs2;
+  p.W = fb + lf.W; p.P = fb + lf.P; p.WdT = fb + lf.WdT; p.Gam = reinterpret_cast<float*>(fb + lf.Gam);
+  p.S1s = fb + lf.S1s;
+  if (saved) p.Pf = reinterpret_cast<float*>(fb + lf.Pf);
+  p.ops2 = carve_ops(fb + lf.ops2base, lf.ops2, saved);
+  p.Hs2 = fb + lf.Hs2;
+  if (gb) {
+    p.dP = gb + lg.dP; p.dW2 = gb + lg.dW2;
+    p.dg2 = reinterpret_cast<float*>(gb + lg.dg2); p.dZ = reinterpret_cast<float*>(gb + lg.dZ);
+    p.dS1s = gb + lg.dS1s; p.dZsT = gb + lg.dZsT;
+    p.dHs2 = gb + lg.dHs2;
   }
-  p.ops2 = carve_ops(ws + l.ops2base, l.ops2, bwd);
-  p.Hs2 = ws + l.Hs2;
   return p;
 }
 
@@ -614,23 +628,39 @@ size_t gsa_bwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C
   return gsa_layout(B, H, L, Dk, Dv, m, C, dtype, true).total;
 }
 
-int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
-            void* o, float* hkt, float* hvt, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
-            int act, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_gsa(B, H, L, Dk, Dv, m, C, dtype, false);
+size_t gsa_saved_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype) {
+  if (check_gsa(B, H, L, Dk, Dv, m, C, dtype, true) != GLA_OK) return 0;
+  return gsa_layout_of(B, H, L, Dk, Dv, m, C, dtype, kGsaSaved).total;
+}
+
+size_t gsa_bwd_saved_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype) {
+  if (check_gsa(B, H, L, Dk, Dv, m, C, dtype, true) != GLA_OK) return 0;
+  return gsa_layout_of(B, H, L, Dk, Dv, m, C, dtype, kGsaGrad).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+// gsa_fwd (saving = false: workspace of the FWD layout) and gsa_fwd_save (saving = true: `mem`
+// is the caller's saved buffer, SAVED layout)
+int gsa_fwd_impl(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
+                 void* o, float* hkt, float* hvt, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
+                 int act, void* mem, size_t mem_bytes, void* stream, bool saving) {
+  int st = check_gsa(B, H, L, Dk, Dv, m, C, dtype, saving);
   if (st != GLA_OK) return st;
   if (!valid_act(act)) return GLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !g || !o) return GLA_ERR_NULL_ARG;
-  if (!all_aligned({q, k, v, g, hk0, hv0, o, hkt, hvt, workspace})) return GLA_ERR_UNSUPPORTED;
-  const GsaLayout lay = gsa_layout(B, H, L, Dk, Dv, m, C, dtype, false);
-  if (!workspace || workspace_bytes < lay.total) return GLA_ERR_WORKSPACE;
+  if (!all_aligned({q, k, v, g, hk0, hv0, o, hkt, hvt, mem})) return GLA_ERR_UNSUPPORTED;
+  const GsaLayout lay = gsa_layout_of(B, H, L, Dk, Dv, m, C, dtype, saving ? kGsaSaved : kGsaFwd);
+  if (!mem || mem_bytes < lay.total) return GLA_ERR_WORKSPACE;
   const size_t es = esize_of(dtype), BH = (size_t)B * H;
   const size_t nk = BH * L * Dk * es, nv = BH * L * Dv * es, ng = BH * L * m * es;
   const size_t sk = BH * Dk * m * 4, sv = BH * m * Dv * 4;
   const Range ins[] = {{q, nk}, {k, nk}, {v, nv}, {g, ng}, {hk0, hk0 ? sk : 0}, {hv0, hv0 ? sv : 0}};
-  const Range outs[] = {{o, nv}, {hkt, hkt ? sk : 0}, {hvt, hvt ? sv : 0}, {workspace, lay.total}};
+  const Range outs[] = {{o, nv}, {hkt, hkt ? sk : 0}, {hvt, hvt ? sv : 0}, {mem, lay.total}};
   if (any_alias(outs, 4, ins, 6)) return GLA_ERR_ALIAS;
-  GsaParams p = gsa_params(lay, static_cast<char*>(workspace), B, H, L, Dk, Dv, m, C, false);
+  GsaParams p = gsa_params(lay, static_cast<char*>(mem), saving, lay, nullptr, B, H, L, Dk, Dv, m, C);
   p.q = q; p.k = k; p.v = v; p.g = g; p.hk0 = hk0; p.hv0 = hv0; p.o = o; p.hkt = hkt; p.hvt = hvt;
   p.act = act;
   if (dispatch_gsa(false, dtype, pad_dk(m), pad_c(C), p, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -638,35 +668,80 @@ int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const fl
   return GLA_OK;
 }
 
-int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
-            const void* do_, const float* dhkt, const float* dhvt, void* dq, void* dk, void* dv, float* dg,
-            float* dhk0, float* dhv0, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
-            int act, void* workspace, size_t workspace_bytes, void* stream) {
+// gsa_bwd (saved = null: `workspace` holds SAVED then GRAD, and the forward tensors are
+// recomputed) and gsa_bwd_saved (saved: what gsa_fwd_save left; workspace: GRAD)
+int gsa_bwd_impl(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
+                 const void* do_, const float* dhkt, const float* dhvt, void* dq, void* dk, void* dv, float* dg,
+                 float* dhk0, float* dhv0, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, int act,
+                 const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_gsa(B, H, L, Dk, Dv, m, C, dtype, true);
   if (st != GLA_OK) return st;
   if (!valid_act(act)) return GLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !g || !do_ || !dq || !dk || !dv || !dg) return GLA_ERR_NULL_ARG;
-  if (!all_aligned({q, k, v, g, hk0, hv0, do_, dhkt, dhvt, dq, dk, dv, dg, dhk0, dhv0, workspace}))
+  if (!all_aligned({q, k, v, g, hk0, hv0, do_, dhkt, dhvt, dq, dk, dv, dg, dhk0, dhv0, workspace, saved}))
     return GLA_ERR_UNSUPPORTED;
-  const GsaLayout lay = gsa_layout(B, H, L, Dk, Dv, m, C, dtype, true);
-  if (!workspace || workspace_bytes < lay.total) return GLA_ERR_WORKSPACE;
+  const bool use_saved = saved != nullptr;
+  const GsaLayout ls = gsa_layout_of(B, H, L, Dk, Dv, m, C, dtype, kGsaSaved);
+  const GsaLayout lg = gsa_layout_of(B, H, L, Dk, Dv, m, C, dtype, kGsaGrad);
+  const GsaLayout lw = use_saved ? lg : gsa_layout(B, H, L, Dk, Dv, m, C, dtype, true);
+  if (use_saved && saved_bytes < ls.total) return GLA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < lw.total) return GLA_ERR_WORKSPACE;
   const size_t es = esize_of(dtype), BH = (size_t)B * H;
   const size_t nk = BH * L * Dk * es, nv = BH * L * Dv * es, ng = BH * L * m * es;
   const size_t sk = BH * Dk * m * 4, sv = BH * m * Dv * 4;
   const Range ins[] = {{q, nk}, {k, nk}, {v, nv}, {g, ng}, {hk0, hk0 ? sk : 0}, {hv0, hv0 ? sv : 0},
-                       {do_, nv}, {dhkt, dhkt ? sk : 0}, {dhvt, dhvt ? sv : 0}};
+                       {do_, nv}, {dhkt, dhkt ? sk : 0}, {dhvt, dhvt ? sv : 0}, {saved, use_saved ? ls.total : 0}};
   const Range outs[] = {{dq, nk}, {dk, nk}, {dv, nv}, {dg, BH * L * m * 4}, {dhk0, dhk0 ? sk : 0},
-                        {dhv0, dhv0 ? sv : 0}, {workspace, lay.total}};
-  if (any_alias(outs, 7, ins, 9)) return GLA_ERR_ALIAS;
-  GsaParams p = gsa_params(lay, static_cast<char*>(workspace), B, H, L, Dk, Dv, m, C, true);
+                        {dhv0, dhv0 ? sv : 0}, {workspace, lw.total}};
+  if (any_alias(outs, 7, ins, 10)) return GLA_ERR_ALIAS;
+  char* ws = static_cast<char*>(workspace);
+  // read only on the saved path
+  GsaParams p = use_saved ? gsa_params(ls, const_cast<char*>(static_cast<const char*>(saved)), true, lg, ws, B, H,
+                                       L, Dk, Dv, m, C)
+                          : gsa_params(lw, ws, true, lw, ws, B, H, L, Dk, Dv, m, C);
   p.q = q; p.k = k; p.v = v; p.g = g; p.do_ = do_; p.hk0 = hk0; p.hv0 = hv0; p.dhkt = dhkt; p.dhvt = dhvt;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dhk0 = dhk0; p.dhv0 = dhv0;
   p.act = act;
+  p.saved = use_saved ? 1 : 0;
   if (dispatch_gsa(true, dtype, pad_dk(m), pad_c(C), p, static_cast<hipStream_t>(stream)) != hipSuccess)
     return GLA_ERR_HIP;
   return GLA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int gsa_fwd(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
+            void* o, float* hkt, float* hvt, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
+            int act, void* workspace, size_t workspace_bytes, void* stream) {
+  return gsa_fwd_impl(q, k, v, g, hk0, hv0, o, hkt, hvt, B, H, L, Dk, Dv, m, C, dtype, act, workspace,
+                      workspace_bytes, stream, false);
+}
+
+int gsa_fwd_save(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
+                 void* o, float* hkt, float* hvt, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
+                 int act, void* saved, size_t saved_bytes, void* stream) {
+  return gsa_fwd_impl(q, k, v, g, hk0, hv0, o, hkt, hvt, B, H, L, Dk, Dv, m, C, dtype, act, saved, saved_bytes,
+                      stream, true);
+}
+
+int gsa_bwd(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
+            const void* do_, const float* dhkt, const float* dhvt, void* dq, void* dk, void* dv, float* dg,
+            float* dhk0, float* dhv0, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
+            int act, void* workspace, size_t workspace_bytes, void* stream) {
+  return gsa_bwd_impl(q, k, v, g, hk0, hv0, do_, dhkt, dhvt, dq, dk, dv, dg, dhk0, dhv0, B, H, L, Dk, Dv, m, C,
+                      dtype, act, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+int gsa_bwd_saved(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
+                  const void* do_, const float* dhkt, const float* dhvt, void* dq, void* dk, void* dv, float* dg,
+                  float* dhk0, float* dhv0, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, int act,
+                  const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!saved) return GLA_ERR_NULL_ARG;
+  return gsa_bwd_impl(q, k, v, g, hk0, hv0, do_, dhkt, dhvt, dq, dk, dv, dg, dhk0, dhv0, B, H, L, Dk, Dv, m, C,
+                      dtype, act, saved, saved_bytes, workspace, workspace_bytes, stream);
+}
 
 size_t msgla_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype, int ngroups,
                                  const int* scales, const int* heads) {

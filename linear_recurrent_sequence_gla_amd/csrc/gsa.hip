@@ -835,17 +835,19 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
     return hipErrorNotSupported;
   } else {
     hipError_t e;
-    hipLaunchKernelGGL((gsa_prep_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    WalkIO w1{p.WdT, p.k, p.Gam, p.S1s, p.hk0, nullptr, p.m, p.Dk, p.L, p.C, p.N, 1};
-    if ((e = launch_walk_store<T, MP, CP>(w1, p.BH, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!p.saved) {   // recompute the forward's tensors
+      hipLaunchKernelGGL((gsa_prep_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      WalkIO w1{p.WdT, p.k, p.Gam, p.S1s, p.hk0, nullptr, p.m, p.Dk, p.L, p.C, p.N, 1};
+      if ((e = launch_walk_store<T, MP, CP>(w1, p.BH, s)) != hipSuccess) return e;
+      hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     BwdParams b;
     b.q = p.P; b.k = p.W; b.v = p.v; b.g = p.g; b.do_ = p.do_; b.h0 = p.hv0; b.dht = p.dhvt;
     b.dq = p.dP; b.dk = p.dW2; b.dv = p.dv; b.dg = p.dg2; b.dh0 = p.dhv0;
     b.BH = p.BH; b.L = p.L; b.Dk = p.m; b.Dv = p.Dv; b.C = p.C; b.N = p.N;
-    b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.saved = false; b.events = LaunchEvents{nullptr, 0};
+    b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.saved = p.saved != 0; b.events = LaunchEvents{nullptr, 0};
     if ((e = launch_gla_bwd<T, MP, CP>(b, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((gsa_dz_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -88,6 +88,8 @@ struct GsaParams {
   float *dg, *dhk0, *dhv0;
   int BH, L, Dk, DkP, Dv, m, C, N;
   int act;        // read-out between the passes (GsaAct)
+  int saved;      // backward: W, P, Pf, WdT, Gam, S1s, ops2 (with QsT) and Hs2 were left by a
+                  // saving forward, so the backward does not recompute them
   // workspace
   void* W;        // [BH][L][m] write weights 1 - exp(g)   (keys of pass 2)   (T)
   void* P;        // [BH][L][m] slot softmax              (queries of pass 2) (T)

@@ -131,6 +131,33 @@ def test_saved_path_sizes_and_validation(lib):
     assert lib.gla_bwd_saved(*args, d[0], need, d[4], wsb, None, None, 0) == 6               # saved is dq
 
 
+def test_gsa_saved_path_sizes_and_validation(lib):
+    # saved = the backward's share of gsa_bwd's workspace; gsa_bwd_saved's workspace = the rest
+    B, H, L, Dk, Dv, m, C = 8, 4, 2048, 128, 128, 64, 64
+    sv = lib.gsa_saved_bytes(B, H, L, Dk, Dv, m, C, 1)
+    gw = lib.gsa_bwd_saved_workspace_bytes(B, H, L, Dk, Dv, m, C, 1)
+    assert sv > lib.gsa_fwd_workspace_bytes(B, H, L, Dk, Dv, m, C, 1) > 0
+    assert sv + gw == lib.gsa_bwd_workspace_bytes(B, H, L, Dk, Dv, m, C, 1)
+    assert lib.gsa_saved_bytes(1, 1, 64, 16, 16, 16, 48, 1) == 0       # unsupported C
+    q, k, v, g, o = (ctypes.c_void_p(0x10000000 + i * 0x1000000) for i in range(5))
+    need = lib.gsa_saved_bytes(1, 1, 64, 16, 16, 16, 16, 1)
+    base = [q, k, v, g, None, None, o, None, None, 1, 1, 64, 16, 16, 16, 16, 1, 0]
+    assert lib.gsa_fwd_save(*base, None, 0, None) == 5
+    assert lib.gsa_fwd_save(*base, ctypes.c_void_p(0x30000000), need - 1, None) == 5
+    assert lib.gsa_fwd_save(*base, ctypes.c_void_p(0x10000000 + 256), need, None) == 6    # saved overlaps q
+    assert lib.gsa_fwd_save(*base[:-1], 9, ctypes.c_void_p(0x30000000), need, None) == 4  # bad read-out
+    d = [ctypes.c_void_p(0x40000000 + i * 0x1000000) for i in range(5)]
+    wsb = lib.gsa_bwd_saved_workspace_bytes(1, 1, 64, 16, 16, 16, 16, 1)
+    args = [q, k, v, g, None, None, o, None, None, d[0], d[1], d[2], d[3], None, None,
+            1, 1, 64, 16, 16, 16, 16, 1, 0]
+    assert lib.gsa_bwd_saved(*args, None, need, d[4], wsb, None) == 1
+    assert lib.gsa_bwd_saved(*args, ctypes.c_void_p(0x30000000), need - 1, d[4], wsb, None) == 5
+    assert lib.gsa_bwd_saved(*args, ctypes.c_void_p(0x30000000), need, d[4], wsb - 1, None) == 5
+    assert lib.gsa_bwd_saved(*args, ctypes.c_void_p(0x30000000), need,
+                             ctypes.c_void_p(0x30000000 + 512), wsb, None) == 6            # workspace in saved
+    assert lib.gsa_bwd_saved(*args, d[0], need, d[4], wsb, None) == 6                     # saved is dq
+
+
 def test_decode_validation(lib):
     assert lib.gla_decode_step(*[None] * 6, 1, 1, 16, 16, 7, None) == 3
     assert lib.gla_decode_step(*[None] * 6, 1, 1, 16, 16, 1, None) == 1

@@ -20,26 +20,34 @@ def gla():
     return m
 
 
-def check_gsa(gla, w, x, units=None, with_state=True, with_dstate=True, act="softmax", backward=True):
+def check_gsa(gla, w, x, units=None, with_state=True, with_dstate=True, act="softmax", backward=True,
+              saved=False):
+    """saved: run gsa_fwd_save and gsa_bwd_saved instead of gsa_fwd and gsa_bwd."""
     dt = w.dtype
     args = [dev(x[n], dt) for n in ("q", "k", "v", "g")]
     hk0 = dev(x["hk0"]) if with_state else None
     hv0 = dev(x["hv0"]) if with_state else None
-    o, hkt, hvt = gla.gsa_fwd(*args, C=w.C, hk0=hk0, hv0=hv0, act=act)
+    if saved:
+        o, hkt, hvt, sv = gla.gsa_fwd_save(*args, C=w.C, hk0=hk0, hv0=hv0, act=act)
+    else:
+        o, hkt, hvt = gla.gsa_fwd(*args, C=w.C, hk0=hk0, hv0=hv0, act=act)
     sel = (slice(None), slice(None)) if units is None else units
     s0 = (lambda a: None if (a is None or not with_state) else a[sel])
     ro, rhk, rhv = gsa_recurrent_fwd(x["q"][sel], x["k"][sel], x["v"][sel], x["g"][sel], s0(x["hk0"]), s0(x["hv0"]),
                                      act=act)
     print(f"[{w.name}] B={w.B} H={w.H} L={x['q'].shape[2]} Dk={w.Dk} Dv={w.Dv} m={w.m} C={w.C} {dt} "
-          f"h0={with_state} dht={with_dstate} act={act}", flush=True)
+          f"h0={with_state} dht={with_dstate} act={act} saved={saved}", flush=True)
     assert_close("o", host(o)[sel], ro, dt)
     assert_close("hkt", host(hkt)[sel], rhk, dt)
     assert_close("hvt", host(hvt)[sel], rhv, dt)
     if not backward:
         return
-    dq, dk, dv, dg, dhk0, dhv0 = gla.gsa_bwd(*args, dev(x["do"], dt), C=w.C, hk0=hk0, hv0=hv0,
-                                             dhkt=dev(x["dhkt"]) if with_dstate else None,
-                                             dhvt=dev(x["dhvt"]) if with_dstate else None, want_dh0=True, act=act)
+    kw = dict(C=w.C, hk0=hk0, hv0=hv0, dhkt=dev(x["dhkt"]) if with_dstate else None,
+              dhvt=dev(x["dhvt"]) if with_dstate else None, want_dh0=True, act=act)
+    if saved:
+        dq, dk, dv, dg, dhk0, dhv0 = gla.gsa_bwd_saved(*args, dev(x["do"], dt), sv, **kw)
+    else:
+        dq, dk, dv, dg, dhk0, dhv0 = gla.gsa_bwd(*args, dev(x["do"], dt), **kw)
     rb = gsa_recurrent_bwd(x["q"][sel], x["k"][sel], x["v"][sel], x["g"][sel], x["do"][sel], s0(x["hk0"]),
                            s0(x["hv0"]), x["dhkt"][sel] if with_dstate else None,
                            x["dhvt"][sel] if with_dstate else None, act=act)
@@ -132,6 +140,36 @@ def test_full_size_config_sampled(gla):
     x = W.gsa_inputs(w)
     units = (np.array([0, 5])[:, None], np.array([1, 3])[None, :])
     check_gsa(gla, w, x, units=units, with_state=False, with_dstate=False)
+
+
+def test_full_size_config_sampled_saved_path(gla):
+    """The GSA workload through gsa_fwd_save / gsa_bwd_saved, as the benchmark runs it."""
+    w = W.WORKLOADS["gsa_340m"]
+    x = W.gsa_inputs(w)
+    units = (np.array([2, 7])[:, None], np.array([0, 2])[None, :])
+    check_gsa(gla, w, x, units=units, with_state=False, with_dstate=False, saved=True)
+
+
+@pytest.mark.parametrize("act", ["softmax", "swish", "relu2"])
+def test_saved_path_matches_recomputing_backward(gla, act):
+    """gsa_fwd_save and gsa_bwd_saved give gsa_fwd's outputs and gsa_bwd's gradients bit for
+    bit: what the saved backward reads is what the recomputing one rebuilds with the same
+    kernels from the same inputs."""
+    import torch
+    w = W.GsaWorkload("gsa-saved", 2, 2, 257, 64, 96, 48, 64, "bf16", 431, h0=True)
+    x = W.gsa_inputs(w)
+    args = [dev(x[n], "bf16") for n in ("q", "k", "v", "g")]
+    st = dict(C=64, hk0=dev(x["hk0"]), hv0=dev(x["hv0"]), act=act)
+    o, hkt, hvt, saved = gla.gsa_fwd_save(*args, **st)
+    ref = gla.gsa_fwd(*args, **st)
+    do, dhkt, dhvt = dev(x["do"], "bf16"), dev(x["dhkt"]), dev(x["dhvt"])
+    a = gla.gsa_bwd_saved(*args, do, saved, dhkt=dhkt, dhvt=dhvt, want_dh0=True, **st)
+    b = gla.gsa_bwd(*args, do, dhkt=dhkt, dhvt=dhvt, want_dh0=True, **st)
+    torch.cuda.synchronize()
+    for name, s_, t in zip(("o", "hkt", "hvt"), (o, hkt, hvt), ref):
+        assert torch.equal(s_, t), name
+    for name, s_, t in zip(("dq", "dk", "dv", "dg", "dhk0", "dhv0"), a, b):
+        assert torch.equal(s_, t), name
 
 
 def test_deterministic(gla):
