@@ -446,6 +446,44 @@ def summarize_pmc(paths, kernel_sub, calib_sub, calib_bytes, cmd, out_json, out_
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def summarize_mfma(paths, cmd, out, title):
+    """Matrix-core counters per library kernel from rocprofv3 --pmc MfmaUtil MfmaFlopsBF16:
+    busy share of the SIMDs' matrix cores, and executed bf16 MFMA flops over the dispatch's own
+    duration (hi/lo operand splits count every MFMA they issue)."""
+    import csv
+    per = {}
+    for p in paths:
+        for r in csv.DictReader(open(p)):
+            name = r["Kernel_Name"]
+            if not name.startswith("_ZN3gla"):
+                continue
+            d = per.setdefault(name, {"dur": {}, "ctr": {}})
+            did = r["Dispatch_Id"]
+            d["dur"][did] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            d["ctr"].setdefault(r["Counter_Name"], {})[did] = float(r["Counter_Value"])
+    lines = [f"# {title}", "", "Command:", "", "```", cmd, "```", "",
+             "MFMA busy: `MfmaUtil` (matrix-core busy cycles over active cycles of all SIMDs). "
+             "Executed bf16 flops: `MfmaFlopsBF16` (512 per MFMA MOP), over each dispatch's duration in "
+             f"the same run, against the {PEAK_BF16_FLOPS / 1e12:.0f} TFLOP/s dense bf16 peak. Medians over "
+             "dispatches.", "",
+             "| kernel | dispatches | avg (us) | MFMA busy % | executed bf16 TFLOP/s | % of peak |",
+             "|---|---|---|---|---|---|"]
+    for name, d in per.items():
+        util = d["ctr"].get("MfmaUtil", {})
+        fl = d["ctr"].get("MfmaFlopsBF16", {})
+        ids = [i for i in d["dur"] if i in fl]
+        if not ids:
+            continue
+        dur = float(np.median([d["dur"][i] for i in ids]))
+        tf = float(np.median([fl[i] / d["dur"][i] for i in ids])) / 1e12
+        u = float(np.median([util[i] for i in ids if i in util])) if util else float("nan")
+        short = name.split("(")[0]
+        short = short[:70] + "..." if len(short) > 70 else short
+        lines.append(f"| `{short}` | {len(ids)} | {dur * 1e6:.1f} | {u:.1f} | {tf:.1f} | "
+                     f"{100 * tf * 1e12 / PEAK_BF16_FLOPS:.2f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def traffic_for(kernel):
     """Counter-measured HBM bytes per launch of `kernel`, if taken on the current sources."""
     try:
@@ -477,6 +515,7 @@ def main():
                     help="run one extra workload alone and print its line (for profiling)")
     ap.add_argument("--summarize-stats")
     ap.add_argument("--summarize-pmc", nargs="+")
+    ap.add_argument("--summarize-mfma", nargs="+")
     ap.add_argument("--title", default="")
     ap.add_argument("--cmd", default="")
     ap.add_argument("--out", default="")
@@ -488,6 +527,9 @@ def main():
 
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.title, args.cmd, args.out)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma, args.cmd, args.out, args.title)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc, args.kernel, args.calib_kernel, args.calib_bytes, args.cmd,
@@ -505,14 +547,6 @@ def main():
         sys.exit(1)
     m.lib()
 
-    if args.only:
-        # one extra workload alone (for profiling it); prints its JSON object
-        fns = {"decode": lambda: run_decode(torch, m), "gsa_decode": lambda: run_gsa_decode(torch, m),
-               "gsa": lambda: run_gsa(torch, m, args.steps, args.warmup),
-               "msgla": lambda: run_msgla(torch, m, args.steps, args.warmup)}
-        print(json.dumps({args.only: fns[args.only]()}), flush=True)
-        return
-
     if args.copy_calib_mb > 0:
         nb = int(args.copy_calib_mb * 1e6) // 16 * 16
         a = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
@@ -521,6 +555,14 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         del a, b
+
+    if args.only:
+        # one extra workload alone (for profiling it); prints its JSON object
+        fns = {"decode": lambda: run_decode(torch, m), "gsa_decode": lambda: run_gsa_decode(torch, m),
+               "gsa": lambda: run_gsa(torch, m, args.steps, args.warmup),
+               "msgla": lambda: run_msgla(torch, m, args.steps, args.warmup)}
+        print(json.dumps({args.only: fns[args.only]()}), flush=True)
+        return
 
     r = run_gla(torch, m, args.steps, args.warmup)
     w = r["w"]
