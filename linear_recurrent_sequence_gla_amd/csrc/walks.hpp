@@ -82,8 +82,10 @@ struct WalkPlan {
   // 64-row tiles of 8 waves (two 32-row halves sharing each chunk's source rows), two chunks
   // per group, one workgroup per CU: each source row is fetched by half as many workgroups.
   // Worth it only while the grid still gives every CU a workgroup; below that, more and
-  // smaller tiles shorten each sequential step.
+  // smaller tiles shorten each sequential step: 16-row tiles when even the 32-row grid leaves
+  // CUs idle (few sequences).
   static constexpr bool WIDE = OK && RT == 32 && SP % 64 == 0 && WalkIOCfg<T, 64, CP, 2>::BYTES <= kMaxLds;
+  static constexpr bool NARROW = OK && RT == 32 && WalkIOCfg<T, 16, CP, 2>::BYTES <= kMaxLds;
 };
 
 // Compute units of the current device, cached per device id.
@@ -167,8 +169,11 @@ struct WalkIOStage {
 // Copy an LDS [RT][64] tile to the state workspace (row stride DsP, already offset).
 template <typename T, int RT, int NT>
 __device__ __forceinline__ void state_tile_out(T* dst, const T* src, int lds, int DsP) {
-  constexpr int V = V16<T>::N;
-  typedef typename V16<T>::type VT;
+  // 16-byte pieces, or 4-element (8-byte for bf16) pieces where a 16-row bf16 tile would
+  // leave half the threads without one
+  constexpr bool HALF = sizeof(T) == 2 && RT * kDvTile * (int)sizeof(T) < 16 * NT;
+  constexpr int V = HALF ? 4 : V16<T>::N;
+  typedef typename std::conditional<HALF, typename Vec4<T>::type, typename V16<T>::type>::type VT;
   constexpr int PER_ROW = kDvTile / V;
 #pragma unroll
   for (int m = 0; m < (RT * PER_ROW + NT - 1) / NT; ++m) {
@@ -362,6 +367,14 @@ hipError_t launch_walk(const WalkIO& w, int BH, hipStream_t s) {
       if (cus > 0 && ntile * (SP / 64) * BH >= cus) {
         hipLaunchKernelGGL((walk_kernel<T, SP, 64, CP, 2, REV, 8>), dim3(ntile * (SP / 64) * BH), dim3(512), 0, s,
                            w, ntile);
+        return hipGetLastError();
+      }
+    }
+    if constexpr (P::NARROW) {
+      const int cus = device_cu_count();
+      if (cus > 0 && ntile * (SP / 32) * BH < cus) {
+        hipLaunchKernelGGL((walk_kernel<T, SP, 16, CP, 2, REV, 4>), dim3(ntile * (SP / 16) * BH), dim3(256), 0, s, w,
+                           ntile);
         return hipGetLastError();
       }
     }

@@ -51,6 +51,7 @@ SHAPES = [
     (1, 2, 300, 128, 128, 128, "bf16", True),
     (1, 1, 129, 256, 512, 64, "bf16", True),
     (2, 4, 130, 256, 512, 64, "bf16", True),     # walk grid fills every CU at 64-row tiles
+    (4, 4, 150, 128, 256, 64, "bf16", True),     # ... at 32-row tiles (smaller shapes: 16-row)
     (1, 1, 100, 256, 64, 32, "bf16", False),
     (1, 2, 1, 128, 64, 64, "bf16", True),       # single token
     (1, 2, 64, 128, 64, 64, "bf16", True),      # exactly one chunk

@@ -54,6 +54,7 @@ SHAPES = [
     (1, 2, 300, 128, 128, 128, "bf16", True, True),
     (1, 1, 129, 256, 512, 64, "bf16", True, True),
     (2, 4, 130, 256, 512, 64, "bf16", True, True),   # 64-row walk tiles
+    (4, 4, 150, 128, 256, 64, "bf16", True, True),   # 32-row walk tiles
     (1, 2, 1, 128, 64, 64, "bf16", True, True),
     (2, 2, 90, 48, 32, 16, "f32", True, True),
     (1, 2, 70, 128, 96, 64, "f32", True, True),
