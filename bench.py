@@ -2,7 +2,7 @@
 """Benchmark of the chunkwise GLA operator on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-    python bench.py --only {decode,gsa_decode,gsa,msgla} [--steps K] [--warmup W]   (one extra, alone)
+    python bench.py --only {decode,gsa_decode,gsa,msgla,long_fwd} [--steps K] [--warmup W]   (one extra)
 
 One step is one pass of the training hot path over one batch of the 340M-layer workload
 (B=8, H=4, L=2048, Dk=128, Dv=256, chunk C=64, bf16 inputs, fp32 accumulation): the forward
@@ -347,6 +347,44 @@ def run_gsa(torch, m, steps=10, warmup=3):
             "recomputing_ms_per_step": round(ms_re, 4)}
 
 
+def run_long_fwd(torch, m, steps=10, warmup=3):
+    """The long-sequence forward (B=1, H=4, L=20480, Dk=128, Dv=256, C=64): few sequences, so
+    the sequential state walk over 320 chunks sets the time."""
+    w = W.WORKLOADS["gla_long"]
+    x = W.gla_inputs(w, with_grad=False)
+    dt = torch.bfloat16
+    d = {n: torch.from_numpy(x[n]).to("cuda", dt).contiguous() for n in ("q", "k", "v", "g")}
+    lib = m.lib()
+    ws = torch.empty(lib.gla_fwd_workspace_bytes(w.B, w.H, w.L, w.Dk, w.Dv, w.C, 1), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty(w.B, w.H, w.L, w.Dv, device="cuda", dtype=dt)
+    ht = torch.empty(w.B, w.H, w.Dk, w.Dv, device="cuda", dtype=torch.float32)
+    P = lambda t: __import__("ctypes").c_void_p(t.data_ptr())
+    stream = __import__("ctypes").c_void_p(torch.cuda.current_stream().cuda_stream)
+    evs = [_events(torch, 4) for _ in range(steps)]
+    hs = [_handles(e) for e in evs]
+
+    def fwd(h=None):
+        args = (P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), None, P(o), P(ht), w.B, w.H, w.L, w.Dk, w.Dv, w.C, 1,
+                P(ws), ws.numel(), stream)
+        m._check(lib.gla_fwd_profiled(*args, h, 4) if h else lib.gla_fwd(*args))
+
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for k in range(steps):
+        fwd(hs[k])
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    kt = {nme: round(float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)])) * 1e3, 2)
+          for i, nme in enumerate(("prep", "walk", "out"))}
+    return {"workload": f"gla_long forward B={w.B} H={w.H} L={w.L} Dk={w.Dk} Dv={w.Dv} C={w.C}, final state kept",
+            "ms": round(ms, 4), "tokens_per_s": round(w.B * w.L / ms * 1e3, 1), "kernel_us": kt}
+
+
 def run_msgla(torch, m, steps=10, warmup=3):
     """MS-GLA {1, 2, 4} forward on the 340M-layer shape, head budget split 2/1/1, with fusion
     weights; plain gla_fwd on the same inputs is timed beside it."""
@@ -511,7 +549,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-calib-mb", type=float, default=0.0,
                     help="also run one plain device copy of this many MB (counter calibration)")
-    ap.add_argument("--only", choices=["decode", "gsa_decode", "gsa", "msgla"],
+    ap.add_argument("--only", choices=["decode", "gsa_decode", "gsa", "msgla", "long_fwd"],
                     help="run one extra workload alone and print its line (for profiling)")
     ap.add_argument("--summarize-stats")
     ap.add_argument("--summarize-pmc", nargs="+")
@@ -559,6 +597,7 @@ def main():
     if args.only:
         # one extra workload alone (for profiling it); prints its JSON object
         fns = {"decode": lambda: run_decode(torch, m), "gsa_decode": lambda: run_gsa_decode(torch, m),
+               "long_fwd": lambda: run_long_fwd(torch, m, args.steps, args.warmup),
                "gsa": lambda: run_gsa(torch, m, args.steps, args.warmup),
                "msgla": lambda: run_msgla(torch, m, args.steps, args.warmup)}
         print(json.dumps({args.only: fns[args.only]()}), flush=True)
@@ -602,7 +641,8 @@ def main():
                      "traffic": traffic},
     }
     if not args.no_extras:
-        ex = {"decode": run_decode(torch, m), "gsa_decode": run_gsa_decode(torch, m)}
+        ex = {"decode": run_decode(torch, m), "gsa_decode": run_gsa_decode(torch, m),
+              "long_fwd": run_long_fwd(torch, m)}
         g = run_gsa(torch, m)
         if g is not None:
             ex["gsa"] = g
