@@ -133,10 +133,27 @@ hipError_t dispatch_bwd(int dtype, int DKP, int CP, const BwdParams& p, hipStrea
 }
 
 // Forward workspace: the chunk operands, then the chunk-start states.
+// Segments gla_fwd keeps room for, to split its state walk when there are few sequences
+// (walks.hpp, walk_segments): up to 8 while the 16-row walk grid is under 256 workgroups
+// and the sequence has at least 16 chunks, else none.
+int fwd_seg_max(int B, int H, int L, int Dk, int Dv, int C) {
+  const int64_t grid16 = (int64_t)((Dv + kDvTile - 1) / kDvTile) * (pad_dk(Dk) / 16) * B * H;
+  const int N = (L + C - 1) / C;
+  return (grid16 < 256 && N >= 16) ? std::min(8, N / 8) : 0;
+}
+
+size_t fwd_seg_bytes(int B, int H, int L, int Dk, int Dv, int C) {
+  const int S = fwd_seg_max(B, H, L, Dk, Dv, C);
+  if (S < 2) return 0;
+  const size_t BH = (size_t)B * H, DKP = pad_dk(Dk), N = (L + C - 1) / C;
+  return align_up((2 * BH * S * DKP * pad_dv(Dv) + BH * N * DKP + BH * S * DKP) * 4);
+}
+
 size_t fwd_ws_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
   const size_t BH = (size_t)B * H, CP = pad_c(C), DKP = pad_dk(Dk), N = (L + C - 1) / C;
   const size_t es = esize_of(dtype);
-  return ops_layout(BH, N, CP, DKP, es, false).total + align_up(BH * N * DKP * pad_dv(Dv) * es);
+  return ops_layout(BH, N, CP, DKP, es, false).total + align_up(BH * N * DKP * pad_dv(Dv) * es) +
+         fwd_seg_bytes(B, H, L, Dk, Dv, C);
 }
 
 struct BwdLayout {
@@ -239,6 +256,10 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* g, const f
   const OpsLayout ol = ops_layout(BH, N, CP, DKP, es, false);
   p.ops = carve_ops(static_cast<char*>(workspace), ol, false);
   p.Hs = static_cast<char*>(workspace) + ol.total;
+  if (fwd_seg_bytes(B, H, L, Dk, Dv, C) > 0) {
+    p.seg_ws = reinterpret_cast<float*>(static_cast<char*>(p.Hs) + align_up(BH * N * DKP * pad_dv(Dv) * es));
+    p.seg_max = fwd_seg_max(B, H, L, Dk, Dv, C);
+  }
   p.events = ev;
   if (dispatch_fwd(dtype, DKP, CP, p, static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
   return GLA_OK;

@@ -37,7 +37,8 @@ struct OutCfg {
   static constexpr int NBR = CP / 16, RBW = (NBR + 3) / 4;       // row blocks, per wave
 };
 
-template <typename T, int DKP, int CP>
+// SEGC: the states come from a segmented walk without their carried part (FwdParams::seg_carry)
+template <typename T, int DKP, int CP, bool SEGC = false>
 __device__ __forceinline__ void fwd_out_block(const FwdParams& p, int ntile, int lin) {
   using W = OutCfg<T, DKP, CP>;
   constexpr int LDV = W::LDV, V = W::V, NBR = W::NBR, RBW = W::RBW;
@@ -75,6 +76,23 @@ __device__ __forceinline__ void fwd_out_block(const FwdParams& p, int ntile, int
     vok[m] = idx < W::NV && r < len && j < Dv;
     v[m] = *reinterpret_cast<const VT*>(vg + (size_t)min(r, len - 1) * Dv + min(j, Dv - V));
   }
+  // a segmented walk stored this state without the part carried in from before its segment:
+  // its rows of X_s and the decay 2^{P_n} are fetched with the rest
+  f32x4 xc[SEGC ? W::PH : 1][V / 4];
+  float sc[SEGC ? W::PH : 1];
+  const bool carried = SEGC && n >= p.seg_len;
+  if constexpr (SEGC) {
+    const int sg = carried ? n / p.seg_len : 0;
+    const float* X = p.seg_carry + ((size_t)bh * p.seg_n + sg) * DKP * DvP + tile * kDvTile;
+    const float* Pn = p.seg_prefix + chunk * DKP;
+#pragma unroll
+    for (int m = 0; m < W::PH; ++m) {
+      const int idx = min(tid + 256 * m, W::NH - 1), r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+      sc[m] = Pn[r];
+#pragma unroll
+      for (int e4 = 0; e4 < V / 4; ++e4) xc[m][e4] = *reinterpret_cast<const f32x4*>(X + (size_t)r * DvP + c + 4 * e4);
+    }
+  }
   Frag<T> xq[RBW][NKB], xa[RBW][NCB];
 #pragma unroll
   for (int s = 0; s < RBW; ++s) {
@@ -83,6 +101,19 @@ __device__ __forceinline__ void fwd_out_block(const FwdParams& p, int ntile, int
     for (int kb = 0; kb < NKB; ++kb) xq[s][kb] = ld8(Qc + (16 * rb + col) * DKP + 32 * kb + 8 * grp);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) xa[s][cb] = ld8(Ac + (16 * rb + col) * CP + 32 * cb + 8 * grp);
+  }
+  if constexpr (SEGC) {
+    if (carried) {   // H_n += Diag(2^{P_n}) X_s
+#pragma unroll
+      for (int m = 0; m < W::PH; ++m) {
+        const float f = fast_exp2(sc[m]);
+#pragma unroll
+        for (int e4 = 0; e4 < V / 4; ++e4) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[m][4 * e4 + e] = from_f32<T>(to_f32(h[m][4 * e4 + e]) + f * xc[m][e4][e]);
+        }
+      }
+    }
   }
 #pragma unroll
   for (int m = 0; m < W::PH; ++m) {
@@ -150,9 +181,9 @@ __device__ __forceinline__ void fwd_out_block(const FwdParams& p, int ntile, int
 
 // grid ntile * N * BH; the ntile value tiles of one chunk are consecutive after the XCD
 // remapping, so they share an XCD's L2 for Qs and A
-template <typename T, int DKP, int CP>
+template <typename T, int DKP, int CP, bool SEGC = false>
 __global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
-  fwd_out_block<T, DKP, CP>(p, ntile, xcd_remap(blockIdx.x, gridDim.x));
+  fwd_out_block<T, DKP, CP, SEGC>(p, ntile, xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // several batches in one launch (see Batches): batch i owns blocks first[i] .. first[i+1] - 1
@@ -178,10 +209,30 @@ hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     record_event(p.events, 1, s);
     WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, p.ht, p.Dk, p.Dv, p.L, p.C, p.N, 0, p.in};
-    if ((e = launch_walk_store<T, DKP, CP>(wf, p.BH, s)) != hipSuccess) return e;
+    // few, long sequences: the walk runs in segments and the output kernel adds each state's
+    // carried part as it stages it (these states serve only that kernel)
+    const int nseg = p.seg_ws ? walk_segments<T, DKP, CP>(p.BH, p.Dv, p.N, p.seg_max) : 1;
+    FwdParams po = p;
+    if (nseg >= 2) {
+      const size_t part = (size_t)p.BH * p.seg_max * DKP * ((p.Dv + kDvTile - 1) / kDvTile * kDvTile);
+      float* prefix = p.seg_ws + 2 * part;
+      float* total = prefix + (size_t)p.BH * p.N * DKP;
+      if ((e = launch_walk_store_segmented<T, DKP, CP>(wf, p.BH, nseg, p.seg_ws, p.seg_ws + part, prefix, total, false,
+                                                       s)) != hipSuccess)
+        return e;
+      po.seg_carry = p.seg_ws + part;
+      po.seg_prefix = prefix;
+      po.seg_len = (p.N + nseg - 1) / nseg;
+      po.seg_n = nseg;
+    } else if ((e = launch_walk_store<T, DKP, CP>(wf, p.BH, s)) != hipSuccess) {
+      return e;
+    }
     record_event(p.events, 2, s);
     const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
-    hipLaunchKernelGGL((gla_fwd_out<T, DKP, CP>), dim3(ntile * p.N * p.BH), dim3(256), 0, s, p, ntile);
+    if (po.seg_carry)
+      hipLaunchKernelGGL((gla_fwd_out<T, DKP, CP, true>), dim3(ntile * p.N * p.BH), dim3(256), 0, s, po, ntile);
+    else
+      hipLaunchKernelGGL((gla_fwd_out<T, DKP, CP>), dim3(ntile * p.N * p.BH), dim3(256), 0, s, po, ntile);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     record_event(p.events, 3, s);
     return hipSuccess;

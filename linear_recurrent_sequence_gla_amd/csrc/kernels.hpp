@@ -63,6 +63,17 @@ struct FwdParams {
   void* Hs;       // [BH][N][DKP][DvP] chunk-start states (T), written by the state walk
   LaunchEvents events;
   SeqView in;     // input sequences read by the launch
+  // optional scratch for a segmented state walk (walks.hpp), room for seg_max segments:
+  // [BH][seg_max][DKP][DvP] fp32 twice, [BH][N][DKP] fp32, [BH][seg_max][DKP] fp32; null =
+  // never segment
+  float* seg_ws = nullptr;
+  int seg_max = 0;
+  // set by the launcher for the output kernel when the walk ran in seg_n segments of seg_len
+  // chunks and left the carried part out of the stored states: it adds Diag(2^{P_n}) X_s to
+  // H_n as it stages it (carry [BH][seg_n][DKP][DvP], prefix [BH][N][DKP], fp32)
+  const float* seg_carry = nullptr;
+  const float* seg_prefix = nullptr;
+  int seg_len = 0, seg_n = 0;
 };
 
 struct BwdParams {

@@ -43,6 +43,13 @@ struct WalkIO {
   float* fin;          // fp32, same layout, or nullptr (= not written)
   int rows, Ds, L, C, N, trans;
   SeqView in;          // input sequences of src
+  // Forward walks only: nseg > 1 splits the chunks into segments of seg_len chunks walked in
+  // parallel, the first from init and the others from zero.  Each segment then leaves its end
+  // state in seg_end ([BH][nseg][SP][DsP] fp32) instead of writing fin; the stored states of
+  // later segments lack the part carried in from before the segment (the segment kernels
+  // further down add it).
+  int nseg = 1, seg_len = 0;
+  float* seg_end = nullptr;
 };
 
 constexpr int kWalkDepth = 2;   // chunk groups whose operands are in flight ahead of use
@@ -223,25 +230,34 @@ __device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
   constexpr int LDV = W::LDV, NIB = RW / 16, NRT = SP / RT, R = kWalkDepth;
   __shared__ __attribute__((aligned(16))) char smem[W::BYTES];
 
+  int seg = 0;                                   // segment (the launch grid is nseg equal parts)
+  if (w.nseg > 1) {
+    const int per_seg = gridDim.x / w.nseg;
+    seg = lin / per_seg;
+    lin -= seg * per_seg;
+  }
   const int tile = lin % ntile, rt = (lin / ntile) % NRT, bh = lin / (ntile * NRT);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   const int cw = 16 * (wave & 3), ri = RW * (wave >> 2);    // this wave's columns and rows
-  const int Ds = w.Ds, L = w.L, C = w.C, N = w.N;
+  const int Ds = w.Ds, L = w.L, C = w.C, NT_ = w.N;
+  // this segment's chunks: c0 .. c0 + N - 1 (the whole sequence when not segmented)
+  const int c0 = w.nseg > 1 ? seg * w.seg_len : 0;
+  const int N = w.nseg > 1 ? min(w.seg_len, NT_ - c0) : NT_;
   const int NG = (N + G - 1) / G;
   const int DsP = ntile * kDvTile, i0 = rt * RT;
   const int j0 = tile * kDvTile + cw + 4 * grp;             // this lane's four columns
   typedef typename Vec4<T>::type V4T;
   const T* src = reinterpret_cast<const T*>(w.src) + (size_t)w.in(bh) * L * Ds;
-  const T* mat = reinterpret_cast<const T*>(w.mat) + ((size_t)bh * N * SP + i0) * CP;
-  const float* gam = w.gam + (size_t)bh * N * SP + i0;
-  T* out = reinterpret_cast<T*>(w.states) + ((size_t)bh * N * SP + i0) * DsP + tile * kDvTile;
+  const T* mat = reinterpret_cast<const T*>(w.mat) + ((size_t)bh * NT_ * SP + i0) * CP;
+  const float* gam = w.gam + (size_t)bh * NT_ * SP + i0;
+  T* out = reinterpret_cast<T*>(w.states) + ((size_t)bh * NT_ * SP + i0) * DsP + tile * kDvTile;
 
   auto slot = [&](int b, int g) { return smem + b * W::STAGE + g * W::SLOT; };
   auto sKT = [&](int b, int g) { return reinterpret_cast<T*>(slot(b, g)); };
   auto sV = [&](int b, int g) { return reinterpret_cast<T*>(slot(b, g) + W::KT); };
   auto sG = [&](int b, int g) { return reinterpret_cast<float*>(slot(b, g) + W::KT + W::VT); };
   auto sHo = [&](int b, int g) { return reinterpret_cast<T*>(smem + 2 * W::STAGE + (b * G + g) * W::HT); };
-  auto chunk_of = [&](int k) { return REV ? N - 1 - k : k; };   // the k-th chunk visited
+  auto chunk_of = [&](int k) { return REV ? N - 1 - k : c0 + k; };   // the k-th chunk visited
 
   f32x4 S[NIB];
 #pragma unroll
@@ -249,7 +265,7 @@ __device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = i0 + ri + 16 * ib + col, j = j0 + e;
-      S[ib][e] = (w.init && j < Ds && i < w.rows) ? w.init[walk_state_index(w, bh, i, j)] : 0.f;
+      S[ib][e] = (w.init && seg == 0 && j < Ds && i < w.rows) ? w.init[walk_state_index(w, bh, i, j)] : 0.f;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);                   // initial state in before the pipeline starts
@@ -331,7 +347,12 @@ __device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
     body(I0{}, kg, std::true_type{});
     if (kg + 1 < NG) body(I1{}, kg + 1, std::true_type{});
   }
-  if (w.fin) {
+  if (w.nseg > 1) {
+    float* e_out = w.seg_end + (((size_t)bh * w.nseg + seg) * SP + i0 + ri) * DsP;
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib)
+      *reinterpret_cast<f32x4*>(e_out + (size_t)(16 * ib + col) * DsP + j0) = S[ib];
+  } else if (w.fin) {
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) {
 #pragma unroll
@@ -401,6 +422,171 @@ hipError_t launch_walk_store_batches(Batches<WalkIO> b, const int* BH, hipStream
 template <typename T, int SP, int CP>
 hipError_t launch_walk_store(const WalkIO& w, int BH, hipStream_t s) {
   return launch_walk<T, SP, CP, false>(w, BH, s);
+}
+
+// ----------------------------------------------------------------------------- segmented walk
+// With few sequences the forward walk is a long chain of dependent steps on a fraction of the
+// CUs.  Splitting each sequence's chunks into segments walked in parallel, each from a zero
+// state (the first from the initial state), makes it nseg times shorter.  For chunk n of
+// segment s the true chunk-start state is
+//     H_n = H_n^seg + Diag(2^{P_n}) X_s,
+// with H_n^seg what the segment's own walk stored, P_n the log2-decay of the segment's chunks
+// before n (per row) and X_s the true state at the segment's start:
+//     X_1 = E_0,   X_{s+1} = Diag(2^{D_s}) X_s + E_s,   final state = X_nseg,
+// E_s being the segment's own end state and D_s its total log2-decay.  seg_prefix_kernel forms
+// P and D, seg_carry_kernel X and the final state, and seg_fixup_kernel adds the carried part
+// to the stored states.
+struct SegParams {
+  const float* gam;       // [BH][N][SP] chunk log2-decay per row
+  const float* seg_end;   // [BH][nseg][SP][DsP] each segment's own end state (fp32)
+  float* carry;           // [BH][nseg][SP][DsP] X_s (s >= 1)
+  float* prefix;          // [BH][N][SP] P_n
+  float* total;           // [BH][nseg][SP] D_s
+  void* states;           // [BH][N][SP][DsP] chunk-start states (T), fixed up in place
+  float* fin;             // [BH][rows][Ds] final state, or null
+  int N, nseg, seg_len, rows, Ds, DsP;
+};
+constexpr int kMaxSeg = 8;
+constexpr int kSegRounds = 16;     // 16-chunk rounds whose decay loads are in flight together
+
+// grid (BH, SP / 16, nseg): P_n for 16 rows over one segment, and D_s.  Thread (row r, lane l)
+// takes chunks l, l + 16, ... of the segment; each round of 16 chunks is scanned across the
+// 16 lanes of a row with shuffles.
+template <int SP>
+__global__ __launch_bounds__(256) void seg_prefix_kernel(SegParams q) {
+  const int bh = blockIdx.x, i = blockIdx.y * 16 + (threadIdx.x >> 4), sg = blockIdx.z, l = threadIdx.x & 15;
+  const int c0 = sg * q.seg_len, c1 = min(q.N, c0 + q.seg_len);
+  const float* gam = q.gam + (size_t)bh * q.N * SP + i;
+  float* pre = q.prefix + (size_t)bh * q.N * SP + i;
+  float run = 0.f;                                 // decay of the rounds before
+  for (int base = c0; base < c1; base += 16 * kSegRounds) {
+    float gv[kSegRounds];
+#pragma unroll
+    for (int t = 0; t < kSegRounds; ++t) {
+      const int n = base + 16 * t + l;
+      gv[t] = n < c1 ? gam[(size_t)n * SP] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < kSegRounds; ++t) {
+      float x = gv[t];                             // inclusive scan over the row's 16 lanes
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float y = __shfl_up(x, o, 16);
+        if (l >= o) x += y;
+      }
+      const int n = base + 16 * t + l;
+      if (n < c1) pre[(size_t)n * SP] = run + x - gv[t];
+      run += __shfl(x, 15, 16);
+    }
+  }
+  if (l == 0) q.total[((size_t)bh * q.nseg + sg) * SP + i] = run;
+}
+
+// grid (BH, SP / 16, DsP / 64): the carries for 16 rows and 64 columns, four columns a thread
+template <int SP>
+__global__ __launch_bounds__(256) void seg_carry_kernel(SegParams q) {
+  const int bh = blockIdx.x, i = blockIdx.y * 16 + (threadIdx.x >> 4);
+  const int j = blockIdx.z * 64 + 4 * (threadIdx.x & 15);
+  const size_t sstride = (size_t)SP * q.DsP;
+  const size_t e0 = ((size_t)bh * q.nseg * SP + i) * q.DsP + j;
+  f32x4 e[kMaxSeg];
+  float d[kMaxSeg];
+#pragma unroll
+  for (int sg = 0; sg < kMaxSeg; ++sg) {
+    if (sg < q.nseg) {
+      e[sg] = *reinterpret_cast<const f32x4*>(q.seg_end + e0 + sg * sstride);
+      d[sg] = fast_exp2(q.total[((size_t)bh * q.nseg + sg) * SP + i]);
+    }
+  }
+  f32x4 x = e[0];
+#pragma unroll
+  for (int sg = 1; sg < kMaxSeg; ++sg) {
+    if (sg < q.nseg) {
+      *reinterpret_cast<f32x4*>(q.carry + e0 + sg * sstride) = x;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) x[c] = d[sg] * x[c] + e[sg][c];
+    }
+  }
+  if (q.fin && i < q.rows) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (j + c < q.Ds) q.fin[((size_t)bh * q.rows + i) * q.Ds + j + c] = x[c];
+  }
+}
+
+// grid (N - seg_len, BH): chunk seg_len + blockIdx.x (segments 1 ..) of sequence bh
+template <typename T, int SP>
+__global__ __launch_bounds__(256) void seg_fixup_kernel(SegParams q) {
+  typedef typename V16<T>::type VT;
+  constexpr int V = V16<T>::N;
+  const int n = q.seg_len + blockIdx.x, bh = blockIdx.y, sg = n / q.seg_len;
+  T* h = reinterpret_cast<T*>(q.states) + ((size_t)bh * q.N + n) * SP * q.DsP;
+  const float* x = q.carry + ((size_t)bh * q.nseg + sg) * SP * q.DsP;
+  const float* pre = q.prefix + ((size_t)bh * q.N + n) * SP;
+  const int per_row = q.DsP / V;
+  for (int idx = threadIdx.x; idx < SP * per_row; idx += 256) {
+    const int i = idx / per_row, c = (idx - i * per_row) * V;
+    const float sc = fast_exp2(pre[i]);
+    VT hv = *reinterpret_cast<const VT*>(h + (size_t)i * q.DsP + c);
+#pragma unroll
+    for (int e4 = 0; e4 < V / 4; ++e4) {
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(x + (size_t)i * q.DsP + c + 4 * e4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hv[4 * e4 + e] = from_f32<T>(to_f32(hv[4 * e4 + e]) + sc * xv[e]);
+    }
+    *reinterpret_cast<VT*>(h + (size_t)i * q.DsP + c) = hv;
+  }
+}
+
+// Segments of a sequence for a forward walk of BH sequences of N chunks, given room for up to
+// seg_max: enough to give the CUs about two 16-row workgroups each, at least 8 chunks per
+// segment; 1 (no split) when the plain walk already fills the device.
+template <typename T, int SP, int CP>
+int walk_segments(int BH, int Ds, int N, int seg_max) {
+  using P = WalkPlan<T, SP, CP>;
+  if constexpr (!P::NARROW) {
+    return 1;
+  } else {
+    const int cus = device_cu_count();
+    const int grid16 = (Ds + kDvTile - 1) / kDvTile * (SP / 16) * BH;
+    if (cus <= 0 || seg_max < 2 || grid16 >= cus) return 1;
+    int ns = min(min(seg_max, kMaxSeg), max(1, 2 * cus / grid16));
+    ns = min(ns, N / 8);
+    if (ns < 2) return 1;
+    const int len = (N + ns - 1) / ns;
+    return (N + len - 1) / len;            // no empty trailing segment
+  }
+}
+
+// The forward walk in nseg segments (nseg from walk_segments, >= 2), then the decay prefixes,
+// the carries and the fix-up: w.states and w.fin end as the plain walk would leave them.
+// Scratch: seg_end and carry [BH][nseg][SP][DsP] fp32, prefix [BH][N][SP] fp32, total
+// [BH][nseg][SP] fp32.
+// fixup = false leaves the stored states without their carried part, for a consumer that adds
+// it itself (the forward's output kernel).
+template <typename T, int SP, int CP>
+hipError_t launch_walk_store_segmented(WalkIO w, int BH, int nseg, float* seg_end, float* carry, float* prefix,
+                                       float* total, bool fixup, hipStream_t s) {
+  using P = WalkPlan<T, SP, CP>;
+  if constexpr (!P::NARROW) {
+    return hipErrorNotSupported;
+  } else {
+    const int ntile = (w.Ds + kDvTile - 1) / kDvTile, DsP = ntile * kDvTile;
+    w.nseg = nseg;
+    w.seg_len = (w.N + nseg - 1) / nseg;
+    w.seg_end = seg_end;
+    hipLaunchKernelGGL((walk_kernel<T, SP, 16, CP, 2, false, 4>), dim3(ntile * (SP / 16) * BH * nseg), dim3(256), 0,
+                       s, w, ntile);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SegParams q{w.gam, seg_end, carry, prefix, total, w.states, w.fin, w.N, nseg, w.seg_len, w.rows, w.Ds, DsP};
+    hipLaunchKernelGGL((seg_prefix_kernel<SP>), dim3(BH, SP / 16, nseg), dim3(256), 0, s, q);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((seg_carry_kernel<SP>), dim3(BH, SP / 16, ntile), dim3(256), 0, s, q);
+    if ((e = hipGetLastError()) != hipSuccess || !fixup) return e;
+    hipLaunchKernelGGL((seg_fixup_kernel<T, SP>), dim3(w.N - w.seg_len, BH), dim3(256), 0, s, q);
+    return hipGetLastError();
+  }
 }
 template <typename T, int SP, int CP>
 hipError_t launch_walk_reverse(const WalkIO& w, int BH, hipStream_t s) {

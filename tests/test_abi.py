@@ -99,6 +99,18 @@ def test_workspace_sizes(lib):
     assert lib.gla_bwd_launch_count(4, 4, 4096, 256, 512, 64, 1) == 5
 
 
+def test_forward_workspace_keeps_room_for_a_segmented_walk(lib):
+    # few, long sequences: room for up to 8 walk segments (two fp32 [BH][8][Dk][Dv] carry
+    # buffers and the per-chunk decay prefixes); many sequences: none
+    B, H, L, Dk, Dv, C = 1, 4, 20480, 128, 256, 64
+    N = L // C
+    ops = 2 * (B * H * N * C * Dk * 2) + B * H * N * C * C * 2 + B * H * N * Dk * 4
+    states = B * H * N * Dk * Dv * 2
+    seg = (2 * B * H * 8 * Dk * Dv + B * H * N * Dk + B * H * 8 * Dk) * 4
+    assert lib.gla_fwd_workspace_bytes(B, H, L, Dk, Dv, C, 1) == ops + states + seg
+    assert lib.gla_fwd_workspace_bytes(8, 4, 2048, 128, 256, 64, 1) == lib.gla_saved_bytes(8, 4, 2048, 128, 256, 64, 1) - 8 * 4 * 32 * 64 * 128 * 2
+
+
 def test_saved_path_sizes_and_validation(lib):
     # saved = the backward's chunk operands (with Qs^T) + chunk-start states; its workspace = dH
     B, H, L, Dk, Dv, C = 8, 4, 2048, 128, 256, 64

@@ -60,6 +60,10 @@ SHAPES = [
     (1, 1, 140, 64, 64, 64, "f32", False),
     (1, 1, 66, 256, 32, 32, "f32", True),
     (1, 2, 300, 64, 80, 128, "f32", True),      # fp32 with C=128: forward only
+    # few sequences, many chunks: the state walk runs in parallel segments (4, 5 ragged, 2)
+    (1, 2, 2000, 64, 64, 64, "bf16", True),
+    (1, 1, 1500, 128, 96, 32, "bf16", True),
+    (1, 2, 1100, 64, 80, 64, "f32", True),
 ]
 
 
@@ -114,6 +118,27 @@ def test_full_size_configs_sampled(gla, name, units):
     x = W.gla_inputs(w, with_grad=False)
     b, h = units
     check_fwd(gla, w, x, units=(b[:, None], h[None, :]))
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 2000, 64, 64, 64), (1, 4, 3000, 128, 256, 64)])
+def test_segmented_walk_matches_plain_walk(gla, shape):
+    """gla_fwd splits the state walk of few, long sequences into segments and adds the carried
+    states afterwards; gla_fwd_save never splits.  Outputs and final states agree to rounding
+    (the fixed-up states are rounded to bf16 twice)."""
+    import torch
+    B, H, L, Dk, Dv, C = shape
+    w = W.GlaWorkload("seg", B, H, L, Dk, Dv, C, "bf16", 77, h0=True)
+    x = W.gla_inputs(w, with_grad=False)
+    q, k, v, g = (dev(x[n], "bf16") for n in ("q", "k", "v", "g"))
+    h0 = dev(x["h0"])
+    o1, ht1 = gla.gla_fwd(q, k, v, g, C=C, h0=h0)
+    o2, ht2, _ = gla.gla_fwd_save(q, k, v, g, C=C, h0=h0)
+    torch.cuda.synchronize()
+    for name, a, b in (("o", o1, o2), ("ht", ht1, ht2)):
+        a, b = host(a), host(b)
+        e = np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30)
+        print(f"  {name}: max|segmented - plain| / max|plain| = {e:.2e}", flush=True)
+        assert e <= 1e-2, name
 
 
 def test_deterministic(gla):
