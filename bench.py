@@ -319,9 +319,9 @@ def run_gsa(torch, m, steps=10, warmup=3):
     outs = (torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]),
             torch.empty(w.B, w.H, w.L, w.m, device="cuda"), None, None)
 
-    def saved_step():
-        m.gsa_fwd_save(*args, C=w.C, output_final_state=False, saved=saved, out=o)
-        m.gsa_bwd_saved(*args, d["do"], saved, C=w.C, workspace=ws, outs=outs)
+    def saved_step(act="softmax"):
+        m.gsa_fwd_save(*args, C=w.C, output_final_state=False, act=act, saved=saved, out=o)
+        m.gsa_bwd_saved(*args, d["do"], saved, C=w.C, act=act, workspace=ws, outs=outs)
 
     def recompute_step():
         m.gsa_fwd(*args, C=w.C)
@@ -341,10 +341,12 @@ def run_gsa(torch, m, steps=10, warmup=3):
 
     ms = timed(saved_step)
     ms_re = timed(recompute_step)
+    # the element-wise read-outs in place of the softmax (same saved-path step)
+    acts = {a: round(timed(lambda a=a: saved_step(a)), 4) for a in m.GSA_ACTS if a != "softmax"}
     return {"workload": f"gsa B={w.B} H={w.H} L={w.L} Dk={w.Dk} Dv={w.Dv} m={w.m} C={w.C} fwd+bwd "
                         "(gsa_fwd_save + gsa_bwd_saved)",
             "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.L / ms * 1e3, 1),
-            "recomputing_ms_per_step": round(ms_re, 4)}
+            "recomputing_ms_per_step": round(ms_re, 4), "read_out_ms_per_step": acts}
 
 
 def run_long_fwd(torch, m, steps=10, warmup=3):
