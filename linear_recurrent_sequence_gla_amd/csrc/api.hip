@@ -149,11 +149,12 @@ size_t fwd_seg_bytes(int B, int H, int L, int Dk, int Dv, int C) {
   return align_up((2 * BH * S * DKP * pad_dv(Dv) + BH * N * DKP + BH * S * DKP) * 4);
 }
 
-size_t fwd_ws_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+// seg: keep room for a segmented walk (gla_fwd); the batched forwards of MS-GLA never segment
+size_t fwd_ws_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype, bool seg = true) {
   const size_t BH = (size_t)B * H, CP = pad_c(C), DKP = pad_dk(Dk), N = (L + C - 1) / C;
   const size_t es = esize_of(dtype);
   return ops_layout(BH, N, CP, DKP, es, false).total + align_up(BH * N * DKP * pad_dv(Dv) * es) +
-         fwd_seg_bytes(B, H, L, Dk, Dv, C);
+         (seg ? fwd_seg_bytes(B, H, L, Dk, Dv, C) : 0);
 }
 
 struct BwdLayout {
@@ -529,7 +530,7 @@ MsglaLayout msgla_layout(int B, int L, int Dk, int Dv, int C, int dtype, int ngr
     l.htg[i] = off;
     off += st;
     l.gla[i] = off;
-    off += align_up(fwd_ws_bytes(B, heads[i], pooled_len(L, scales[i]), Dk, Dv, C, dtype));
+    off += align_up(fwd_ws_bytes(B, heads[i], pooled_len(L, scales[i]), Dk, Dv, C, dtype, false));
   }
   l.total = off;
   return l;
