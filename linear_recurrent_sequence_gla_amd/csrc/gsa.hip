@@ -332,22 +332,34 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
   const size_t chunk = (size_t)bh * p.N + n;
   const T* gg = reinterpret_cast<const T*>(p.g) + gbase;
   ChunkScan<T, MP, CP, false> cs;
-  cs.run(gg, gg, gg, m, m, len, segtot, sGam, red);
+  cs.load(gg, gg, gg, m, m, len);
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
+  // P (fp32: the softmax's Jacobian keeps sum_s dZ = 0; Z for the element-wise read-outs) and
+  // dP, from clamped rows, in flight while the gates are scanned
+  f32x4 pl[RPS][V / 4];
+  VT dl[RPS];
+  {
+    const int cc = (cs.active && c0 < m) ? c0 : 0;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const size_t off = gbase + (size_t)min(r0 + u, len - 1) * m + cc;
+#pragma unroll
+      for (int e4 = 0; e4 < V / 4; ++e4) pl[u][e4] = *reinterpret_cast<const f32x4*>(p.Pf + off + 4 * e4);
+      dl[u] = *reinterpret_cast<const VT*>(reinterpret_cast<const T*>(p.dP) + off);
+    }
+  }
+  cs.finish(segtot, sGam, red);
   float pv[RPS][V], dpv[RPS][V];
   if (cs.active) {
-    const float* Pg = p.Pf + gbase;     // fp32 P (softmax: its Jacobian keeps sum_s dZ = 0) or Z
-    const T* dPg = reinterpret_cast<const T*>(p.dP) + gbase;
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
       const int r = r0 + u;
       const bool ok = r < len && c0 < m;
-      const VT b = ok ? *reinterpret_cast<const VT*>(dPg + (size_t)r * m + c0) : zero_vec<T>();
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        pv[u][e] = ok ? Pg[(size_t)r * m + c0 + e] : 0.f;
-        dpv[u][e] = to_f32(b[e]);
+        pv[u][e] = ok ? pl[u][e >> 2][e & 3] : 0.f;
+        dpv[u][e] = ok ? to_f32(dl[u][e]) : 0.f;
         s += pv[u][e] * dpv[u][e];
       }
       rpart[cs.cg * CP + r] = s;
