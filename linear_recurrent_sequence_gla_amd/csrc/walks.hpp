@@ -30,6 +30,7 @@
 #pragma once
 #include <atomic>
 #include <type_traits>
+#include <utility>
 #include "prep.hpp"
 
 namespace gla {
@@ -194,6 +195,12 @@ __device__ __forceinline__ void state_tile_out(T* dst, const T* src, int lds, in
   }
 }
 
+// f(integral_constant<int, r>) for r = 0 .. R-1, unrolled at compile time
+template <typename F, int... r>
+__device__ __forceinline__ void for_each_stage(F&& f, std::integer_sequence<int, r...>) {
+  (f(std::integral_constant<int, r>{}), ...);
+}
+
 __device__ __forceinline__ size_t walk_state_index(const WalkIO& w, int bh, int i, int j) {
   return w.trans ? ((size_t)bh * w.Ds + j) * w.rows + i : ((size_t)bh * w.rows + i) * w.Ds + j;
 }
@@ -326,27 +333,25 @@ __device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
       if (!CHECK || k < N) state_tile_out<T, RT, NT>(out + (size_t)chunk_of(k) * SP * DsP, sHo(b, g), LDV, DsP);
     }
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  static_assert(R == 2, "the walk pipeline alternates two register stages");
+  // R consecutive groups, one per register stage (the r-th group in stage r)
+  auto round = [&](int kg0, auto cc) {
+    for_each_stage([&](auto rc) { body(rc, kg0 + decltype(rc)::value, cc); }, std::make_integer_sequence<int, R>{});
+  };
+  auto round_checked = [&](int kg0) {           // the ragged end: stop at the last group
+    for_each_stage([&](auto rc) { if (kg0 + decltype(rc)::value < NG) body(rc, kg0 + decltype(rc)::value, std::true_type{}); },
+                   std::make_integer_sequence<int, R>{});
+  };
   const int full = (N / G) / R * R;              // groups walked without bounds checks
   int kg = 0;
-  // The first pair runs ahead of the loop, and the loop is reached only through it: every path
+  // The first round runs ahead of the loop, and the loop is reached only through it: every path
   // into a group's operand wait then has the previous group's state stores between that
   // group's loads and the wait, so the compiler's count leaves those stores in flight instead
   // of waiting for them.
   if (full >= R) {
-    body(I0{}, 0, std::false_type{});
-    body(I1{}, 1, std::false_type{});
-    for (kg = R; kg < full; kg += R) {
-      body(I0{}, kg, std::false_type{});
-      body(I1{}, kg + 1, std::false_type{});
-    }
+    round(0, std::false_type{});
+    for (kg = R; kg < full; kg += R) round(kg, std::false_type{});
   }
-  for (; kg < NG; kg += R) {
-    body(I0{}, kg, std::true_type{});
-    if (kg + 1 < NG) body(I1{}, kg + 1, std::true_type{});
-  }
+  for (; kg < NG; kg += R) round_checked(kg);
   if (w.nseg > 1) {
     float* e_out = w.seg_end + (((size_t)bh * w.nseg + seg) * SP + i0 + ri) * DsP;
 #pragma unroll
