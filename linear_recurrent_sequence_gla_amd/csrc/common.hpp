@@ -92,12 +92,13 @@ __device__ __forceinline__ Frag<T> ld8_col(const T* p, int ld) {
 // j / 4 of a 4-row slab at column 4 * (j % 4).  ld * sizeof(T) must be a multiple of 8.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+// lane: this thread's lane in its wave (threadIdx.x & 63)
 template <typename T>
-__device__ __forceinline__ Frag<T> ld8_colblk(const T* blk, int ld);
+__device__ __forceinline__ Frag<T> ld8_colblk(const T* blk, int ld, int lane);
 template <>
-__device__ __forceinline__ Frag<bf16> ld8_colblk(const bf16* blk, int ld) {
+__device__ __forceinline__ Frag<bf16> ld8_colblk(const bf16* blk, int ld, int lane) {
   typedef i16x4 __attribute__((address_space(3)))* lds_ptr;
-  const int lane = threadIdx.x & 63, grp = lane >> 4, j = lane & 15;
+  const int grp = lane >> 4, j = lane & 15;
   bf16* a = const_cast<bf16*>(blk) + (8 * grp + (j >> 2)) * ld + 4 * (j & 3);
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)a);
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)(a + 4 * ld));
@@ -106,9 +107,23 @@ __device__ __forceinline__ Frag<bf16> ld8_colblk(const bf16* blk, int ld) {
   return f;
 }
 template <>
-__device__ __forceinline__ Frag<float> ld8_colblk(const float* blk, int ld) {
-  const int lane = threadIdx.x & 63, grp = lane >> 4, col = lane & 15;
+__device__ __forceinline__ Frag<float> ld8_colblk(const float* blk, int ld, int lane) {
+  const int grp = lane >> 4, col = lane & 15;
   return ld8_col(blk + 8 * grp * ld + col, ld);
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> ld8_colblk(const T* blk, int ld) {
+  return ld8_colblk(blk, ld, (int)threadIdx.x & 63);
+}
+
+// The thread's index through an opaque register move.  A kernel that loops over work items
+// takes it once per item, so that the compiler recomputes the per-lane LDS addresses derived
+// from it inside each item instead of hoisting them all out of the loop, where every one of
+// them would stay live across the whole loop body.
+__device__ __forceinline__ int opaque_thread_index() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t;
 }
 
 // Split-set fragment taken from two stacked accumulator blocks (rows 4*grp+e of block a and
@@ -170,11 +185,11 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Block-wide max of a non-negative value over NT threads; `red` holds >= NT/64 floats of LDS.
 template <int NT = 256>
-__device__ __forceinline__ float block_max(float v, float* red) {
+__device__ __forceinline__ float block_max(float v, float* red, int tid = threadIdx.x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  const int wave = tid >> 6;
+  if ((tid & 63) == 0) red[wave] = v;
   __syncthreads();
   float r = red[0];
 #pragma unroll

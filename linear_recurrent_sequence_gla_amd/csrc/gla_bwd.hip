@@ -98,8 +98,7 @@ struct SliceStage {
 
   // dog/vg: rows of this chunk ([len][Dv]); hs/dhs: [DKS rows][DVP] state tiles of this chunk
   __device__ __forceinline__ void load(const T* dog, const T* vg, const T* hs, const T* dhs, int len, int Dv,
-                                       int DVP, int js, int kvalid) {
-    const int tid = threadIdx.x;
+                                       int DVP, int js, int kvalid, int tid) {
     constexpr int PER_ROW = kDvTile / Cf::V;
 #pragma unroll
     for (int m = 0; m < Cf::PV; ++m) {
@@ -122,17 +121,16 @@ struct SliceStage {
     }
   }
   // z[m] += this thread's share of rowsum(H * dH) for the state tile it stages
-  __device__ __forceinline__ void zdot(float (&z)[Cf::PH]) const {
+  __device__ __forceinline__ void zdot(float (&z)[Cf::PH], bool take = true) const {
 #pragma unroll
     for (int m = 0; m < Cf::PH; ++m) {
       float t = 0.f;
 #pragma unroll
       for (int e = 0; e < Cf::V; ++e) t += to_f32(hv[m][e]) * to_f32(dhv[m][e]);
-      z[m] += hok[m] ? t : 0.f;
+      z[m] += hok[m] && take ? t : 0.f;
     }
   }
-  __device__ __forceinline__ void store(T* sdO, T* sV, T* sH, T* sdH) const {
-    const int tid = threadIdx.x;
+  __device__ __forceinline__ void store(T* sdO, T* sV, T* sH, T* sdH, int tid) const {
     constexpr int PER_ROW = kDvTile / Cf::V;
 #pragma unroll
     for (int m = 0; m < Cf::PV; ++m) {
@@ -161,14 +159,14 @@ struct ATileStage {
   static constexpr int V = 16 / (int)sizeof(T), N = CP * CP / V, P = (N + NT - 1) / NT;
   typedef typename V16<T>::type VT;
   VT a[P];
-  __device__ __forceinline__ void load(const T* src) {
+  __device__ __forceinline__ void load(const T* src, int tid) {
 #pragma unroll
-    for (int m = 0; m < P; ++m) a[m] = *reinterpret_cast<const VT*>(src + (size_t)min((int)threadIdx.x + NT * m, N - 1) * V);
+    for (int m = 0; m < P; ++m) a[m] = *reinterpret_cast<const VT*>(src + (size_t)min(tid + NT * m, N - 1) * V);
   }
-  __device__ __forceinline__ void store(T* dst, int lds) const {
+  __device__ __forceinline__ void store(T* dst, int lds, int tid) const {
 #pragma unroll
     for (int m = 0; m < P; ++m) {
-      const int idx = threadIdx.x + NT * m;
+      const int idx = tid + NT * m;
       if (idx < N) {
         const int r = idx / (CP / V), c = (idx - r * (CP / V)) * V;
         *reinterpret_cast<VT*>(dst + r * lds + c) = a[m];
@@ -177,8 +175,26 @@ struct ATileStage {
   }
 };
 
+// Where tile t of the chunk kernel lies: chunk fastest, then b*h, then the key-width slice
+// (the order a grid (N, BH, DKP / DKS) gives its blocks).
+struct BwdTile {
+  int n, bh, ch0, row0, len, kvalid;
+  size_t chunk, qbase, vbase;
+  __device__ __forceinline__ BwdTile(const BwdParams& p, int t, int DKS) {
+    n = t % p.N;
+    bh = t / p.N % p.BH;
+    ch0 = t / (p.N * p.BH) * DKS;
+    row0 = n * p.C;
+    len = min(p.C, p.L - row0);
+    kvalid = min(DKS, p.Dk - ch0);
+    chunk = (size_t)bh * p.N + n;
+    qbase = ((size_t)bh * p.L + row0) * p.Dk + ch0;
+    vbase = ((size_t)bh * p.L + row0) * p.Dv;
+  }
+};
+
 template <typename T, int DKS, int CP, bool WITH_DV>
-__global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DKP, int ntile) {
+__global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DKP, int ntile, int ntiles) {
   using Cf = BwdChunkCfg<T, DKS, CP, WITH_DV>;
   constexpr int NT = Cf::NT, NW = NT / 64;
   using M = ChunkMap<T, DKS, CP, NT>;
@@ -213,31 +229,39 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   float* sDiag = sZ + DKS;
   float* red = sDiag + CP;
 
-  const int n = blockIdx.x, bh = blockIdx.y, ch0 = blockIdx.z * DKS;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  const int Dk = p.Dk, Dv = p.Dv, L = p.L, N = p.N;
+  const int Dk = p.Dk, Dv = p.Dv, L = p.L;
   const int DVP = ntile * kDvTile;
-  const int row0 = n * p.C;
-  const int len = min(p.C, L - row0);
-  const int kvalid = min(DKS, Dk - ch0);
-  const size_t chunk = (size_t)bh * N + n;
-  const size_t qbase = ((size_t)bh * L + row0) * Dk + ch0;
+  int tid = threadIdx.x;
+
+  // The grid is persistent: workgroup w takes tiles w, w + gridDim.x, ...  A tile's q, k and
+  // g, which its gate scan waits for, go out during the previous tile's epilogue, which leaves
+  // HBM idle otherwise; the first tile's go out here.
+  ChunkScan<T, DKS, CP, true, NT> cs;
+  auto issue = [&](const BwdTile& u) {
+    cs.load(reinterpret_cast<const T*>(p.q) + u.qbase, reinterpret_cast<const T*>(p.k) + u.qbase,
+            reinterpret_cast<const T*>(p.g) + u.qbase, Dk, Dk - u.ch0, u.len, tid);
+  };
+  int t = blockIdx.x;
+  issue(BwdTile(p, t, DKS));
+  for (;;) {
+  tid = opaque_thread_index();           // per-lane addresses are formed anew for each tile
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const BwdTile tile(p, t, DKS);
+  const int tn = t + gridDim.x;                     // this workgroup's next tile
+  const int ch0 = tile.ch0, row0 = tile.row0, len = tile.len, kvalid = tile.kvalid;
+  const size_t chunk = tile.chunk, qbase = tile.qbase;
   const T* qg = reinterpret_cast<const T*>(p.q) + qbase;
   const T* kg = reinterpret_cast<const T*>(p.k) + qbase;
-  const T* dog = reinterpret_cast<const T*>(p.do_) + ((size_t)bh * L + row0) * Dv;
-  const T* vg = reinterpret_cast<const T*>(p.v) + ((size_t)bh * L + row0) * Dv;
+  const T* dog = reinterpret_cast<const T*>(p.do_) + tile.vbase;
+  const T* vg = reinterpret_cast<const T*>(p.v) + tile.vbase;
   const T* hs = reinterpret_cast<const T*>(p.Hs) + (chunk * DKP + ch0) * DVP;
   const T* dhs = reinterpret_cast<const T*>(p.dHs) + (chunk * DKP + ch0) * DVP;
-
-  // every independent load goes out before the first wait: q, k, g of the chunk, the first
-  // Dv slice and (with dv) the chunk's A tile
-  ChunkScan<T, DKS, CP, true, NT> cs;
-  cs.load(qg, kg, reinterpret_cast<const T*>(p.g) + qbase, Dk, Dk - ch0, len);
+  // the first Dv slice and (with dv) the chunk's A tile load while the gates are scanned
   SliceStage<T, DKS, CP, WITH_DV> st;
-  st.load(dog, vg, hs, dhs, len, Dv, DVP, 0, kvalid);
+  st.load(dog, vg, hs, dhs, len, Dv, DVP, 0, kvalid, tid);
   ATileStage<T, CP, NT> at;
-  if constexpr (WITH_DV) at.load(reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP);
-  const float maxb = cs.finish(segtot, sGam, red);
+  if constexpr (WITH_DV) at.load(reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP, tid);
+  const float maxb = cs.finish(segtot, sGam, red, tid);
   cs.kvals();                            // q is converted after the Dv loop, where it is first needed
   const bool fast = maxb <= kSpanLimit;
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
@@ -252,13 +276,13 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
         *reinterpret_cast<VT*>(sKd + (r0 + u) * LDQ + c0) = kd;
       }
     }
-    at.store(sA, LDC);
+    at.store(sA, LDC, tid);
   }
   float zp[Cf::PH];
 #pragma unroll
   for (int m = 0; m < Cf::PH; ++m) zp[m] = 0.f;
   st.zdot(zp);
-  st.store(sdO, sV, sH, sdH);
+  st.store(sdO, sV, sH, sdH, tid);
   __syncthreads();
 
   // The accumulators hold their blocks transposed (the products are formed with the operands
@@ -271,7 +295,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   for (int s = 0; s < PQ; ++s) accQ[s] = accK[s] = accKI[s] = zero4();
 
   for (int js = 0; js < ntile; ++js) {
-    st.load(dog, vg, hs, dhs, len, Dv, DVP, min(js + 1, ntile - 1), kvalid);   // last: harmless reload
+    st.load(dog, vg, hs, dhs, len, Dv, DVP, min(js + 1, ntile - 1), kvalid, tid);   // last: harmless reload
 #pragma unroll
     for (int s = 0; s < PA; ++s) {       // dA += dO V^T
       const int blk = wave + NW * s;
@@ -303,11 +327,11 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
           f32x4 acc = zero4();
 #pragma unroll
           for (int kr = 0; kr < CP / 32; ++kr)
-            mma(acc, ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV),
-                ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC));
+            mma(acc, ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV, lane),
+                ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC, lane));
 #pragma unroll
           for (int ki = 0; ki < DKS / 32; ++ki)
-            mma(acc, ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV),
+            mma(acc, ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV, lane),
                 ld8(sKd + (16 * cb + col) * LDQ + 32 * ki + 8 * grp));
           // transposed block: this lane holds dV[16 cb + col][16 jb + 4 grp + e]
           typename Vec4<T>::type dv4;
@@ -318,8 +342,16 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
       }
     }
     __syncthreads();
+    // The next slice is staged before this slice's dv leaves, and on every path: after the
+    // last slice the reloaded copy goes to LDS that the intra phase overwrites, and adds
+    // nothing to Z.  The wait for its loads is explicit and comes first (the only older
+    // memory operations are the previous slice's dv stores); left to the compiler, it sinks
+    // the Z sums below the dv stores and then waits for those stores as well.
+    __builtin_amdgcn_s_waitcnt(0);
+    st.zdot(zp, js + 1 < ntile);
+    st.store(sdO, sV, sH, sdH, tid);
     if constexpr (WITH_DV) {
-      T* dvg = reinterpret_cast<T*>(p.dv) + ((size_t)bh * L + row0) * Dv;
+      T* dvg = reinterpret_cast<T*>(p.dv) + tile.vbase;
       constexpr int PER_ROW = kDvTile / V;
       for (int idx = tid; idx < CP * PER_ROW; idx += NT) {
         const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
@@ -327,10 +359,6 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
         if (r < len && jj < Dv)
           *reinterpret_cast<VT*>(dvg + (size_t)r * Dv + jj) = *reinterpret_cast<const VT*>(sdV + r * LDV + c);
       }
-    }
-    if (js + 1 < ntile) {
-      st.zdot(zp);
-      st.store(sdO, sV, sH, sdH);
     }
     __syncthreads();
   }
@@ -390,10 +418,10 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
         const int rb = blk / NIB, ib = blk % NIB;
 #pragma unroll
         for (int kc = 0; kc < CP / 32; ++kc) {
-          mma(accQ[s], ld8_colblk(sKs + (32 * kc) * LDQ + 16 * ib, LDQ),
+          mma(accQ[s], ld8_colblk(sKs + (32 * kc) * LDQ + 16 * ib, LDQ, lane),
               ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp));
-          mma(accK[s], ld8_colblk(sQs + (32 * kc) * LDQ + 16 * ib, LDQ),
-              ld8_colblk(sdA + (32 * kc) * LDC + 16 * rb, LDC));
+          mma(accK[s], ld8_colblk(sQs + (32 * kc) * LDQ + 16 * ib, LDQ, lane),
+              ld8_colblk(sdA + (32 * kc) * LDC + 16 * rb, LDC, lane));
         }
       }
     }
@@ -417,6 +445,9 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
       for (int e = 0; e < V; ++e) sB[(r0 + u) * DKS + c0 + e] = cs.b[u][e];
     }
   }
+  // q, k and g of this tile are in registers as fp32 from here on: the next tile's go out
+  // (past the last tile, this tile's own again, so that no load is conditional)
+  issue(BwdTile(p, tn < ntiles ? tn : t, DKS));
   __syncthreads();
 
   // ---- epilogue: dq, dk; dg from the two in-chunk prefix sums and Z
@@ -530,6 +561,11 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
       }
     }
   }
+  if (tn >= ntiles) break;
+  t = tn;
+  __syncthreads();                       // the next tile's scan reuses segtot, sGam and red
+  }
+  __builtin_amdgcn_s_waitcnt(0);         // the last tile's repeated loads have landed
 }
 
 // ======================================================================= dv (separate)
@@ -604,6 +640,27 @@ __global__ __launch_bounds__(256) void gla_bwd_dv(BwdParams p, int ntile) {
 }
 
 // ======================================================================= plan + launch
+// Workgroups of the persistent chunk kernel that the device runs at once (CUs times the
+// workgroups one CU holds), cached per device; 0 cannot happen (at least one per CU).
+template <typename T, int DKS, int CP, bool WITH_DV>
+int bwd_chunk_slots() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gla_bwd_chunk<T, DKS, CP, WITH_DV>, kBwdThreads, 0) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int cus = device_cu_count();
+  const int n = (cus > 0 ? cus : 256) * per_cu;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 // Key-width slice of the chunk kernel: the whole key width with dv fused when it fits the
 // LDS of a CU, otherwise slices of at most 128 channels with dv in its own kernel.
 template <typename T, int DKP, int CP>
@@ -641,8 +698,9 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
     WalkIO wr{p.ops.QsT, p.do_, p.ops.Gam, p.dHs, p.dht, p.dh0, p.Dk, p.Dv, p.L, p.C, p.N, 0};
     if ((e = launch_walk_reverse<T, DKP, CP>(wr, p.BH, s)) != hipSuccess) return e;
     record_event(p.events, ev++, s);
-    hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED>), dim3(p.N, p.BH, DKP / P::DKS), dim3(kBwdThreads), 0, s,
-                       p, DKP, ntile);
+    const int ntiles = p.N * p.BH * (DKP / P::DKS);
+    hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED>), dim3(imin(ntiles, bwd_chunk_slots<T, P::DKS, CP, P::FUSED>())),
+                       dim3(kBwdThreads), 0, s, p, DKP, ntile, ntiles);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     record_event(p.events, ev++, s);
     if constexpr (!P::FUSED) {

@@ -186,8 +186,9 @@ struct ChunkScan {
   bool ok[RPS];
 
   // ld: row stride of q, k, g (elements); width: valid channels from the base pointer
-  __device__ __forceinline__ void load(const T* qg, const T* kg, const T* gg, int ld, int width, int len) {
-    const int tid = threadIdx.x;
+  // tid: the thread's index (threadIdx.x)
+  __device__ __forceinline__ void load(const T* qg, const T* kg, const T* gg, int ld, int width, int len,
+                                       int tid = threadIdx.x) {
     cg = tid % M::NCG;
     seg = tid / M::NCG;
     active = tid < M::ACTIVE;
@@ -231,7 +232,7 @@ struct ChunkScan {
     }
   }
 
-  __device__ __forceinline__ float finish(float* segtot, float* sGam, float* red) {
+  __device__ __forceinline__ float finish(float* segtot, float* sGam, float* red, int tid = threadIdx.x) {
     float run_[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) run_[e] = 0.f;
@@ -253,7 +254,7 @@ struct ChunkScan {
       for (int e = 0; e < V; ++e) segtot[seg * DKP + cg * V + e] = run_[e];
     }
     __syncthreads();
-    for (int ch = threadIdx.x; ch < DKP; ch += NT) seg_scan_channel<M::NSEG>(segtot, DKP, ch, false);
+    for (int ch = tid; ch < DKP; ch += NT) seg_scan_channel<M::NSEG>(segtot, DKP, ch, false);
     __syncthreads();
     float mx = 0.f;
     if (active) {
@@ -273,7 +274,7 @@ struct ChunkScan {
         for (int e = 0; e < V; ++e) sGam[cg * V + e] = b[RPS - 1][e];
       }
     }
-    return block_max<NT>(mx, red);   // also makes sGam visible to all threads
+    return block_max<NT>(mx, red, tid);   // also makes sGam visible to all threads
   }
 
   __device__ __forceinline__ float run(const T* qg, const T* kg, const T* gg, int ld, int width, int len,
