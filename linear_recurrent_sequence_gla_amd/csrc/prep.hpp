@@ -68,20 +68,20 @@ struct PrepCfg {
   using M = ChunkMap<T, DKP, CP>;
   static constexpr int PK = 16 / (int)sizeof(T);       // 16-byte row padding, in elements
   static constexpr int LDQ = DKP + PK;                 // row stride of the [CP][DKP] tiles
-  static constexpr int LDC = CP + PK;                  // row stride of [DKP][CP] and [CP][CP] tiles
+  static constexpr int LDC = CP + PK;                  // row stride of the [CP][CP] score tile
   static constexpr int LDP = 32 + PK;                  // row stride of the safe-path slice tiles
   static constexpr int NB = CP / 16;                   // 16-row sub-chunks per chunk
   static constexpr int NP = NB * (NB - 1) / 2;         // off-diagonal sub-block pairs
   static constexpr int PPW = (NP + 3) / 4;             // pairs per wave
   static constexpr bool SPLIT = sizeof(T) == 2;        // hi/lo operands ("Precision of A")
   static constexpr size_t TILE = (size_t)CP * LDQ * sizeof(T);
-  static constexpr size_t KDT = (size_t)DKP * LDC * sizeof(T);
+  static constexpr size_t KD = TILE;                   // Kd [CP][DKP], copied out transposed
   static constexpr size_t ATILE = (size_t)CP * LDC * sizeof(T);
   // fast path: sQ, sK (+ sQl, sKl); after the score product the same bytes hold KdT and A
   static constexpr size_t FAST = (SPLIT ? 4 : 2) * TILE;
   static constexpr size_t SAFE = TILE + (size_t)3 * CP * 33 * 4 +
                                  (size_t)(SPLIT ? 2 : 1) * (CP + 16) * LDP * sizeof(T);
-  static constexpr size_t MAIN = cmax(cmax(FAST, SAFE), TILE + KDT + ATILE);
+  static constexpr size_t MAIN = cmax(cmax(FAST, SAFE), TILE + KD + ATILE);
   static constexpr size_t MISC = (size_t)(M::NSEG * DKP + DKP + 8) * 4;
   static constexpr size_t BYTES = MAIN + MISC;
 };
@@ -108,18 +108,19 @@ __device__ __forceinline__ void tile_in_dense(T* dst, const T* __restrict__ src,
     *reinterpret_cast<VT*>(dst + r * lds + c) = *reinterpret_cast<const VT*>(src + (size_t)r * cols + c);
   }
 }
-// Copy the transpose of a [rows][cols] LDS tile to dense global [cols][rows].
-template <typename T>
+// Copy the transpose of a [rows][cols] LDS tile to dense global [cols][rows] with transposing
+// LDS reads: each lane gathers eight consecutive rows of one column (a matrix-core column
+// fragment, ld8_colblk) and writes them as one contiguous run.  Element-wise column reads
+// and column writes of such tiles hit few LDS banks.  NW waves; rows % 32 == 0,
+// cols % 16 == 0, lds * sizeof(T) % 8 == 0.
+template <typename T, int NW>
 __device__ __forceinline__ void tile_out_t(T* __restrict__ dst, const T* src, int rows, int cols, int lds) {
-  constexpr int V = V16<T>::N;
-  typedef typename V16<T>::type VT;
-  const int per = rows / V;
-  for (int idx = threadIdx.x; idx < cols * per; idx += blockDim.x) {
-    const int c = idx / per, r = (idx - c * per) * V;
-    VT vec;
-#pragma unroll
-    for (int e = 0; e < V; ++e) vec[e] = src[(r + e) * lds + c];
-    *reinterpret_cast<VT*>(dst + (size_t)c * rows + r) = vec;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const int nrb = rows / 32, nblk = nrb * (cols / 16);
+  for (int blk = wave; blk < nblk; blk += NW) {
+    const int rb = blk % nrb, cb = blk / nrb;
+    const Frag<T> f = ld8_colblk(src + (32 * rb) * lds + 16 * cb, lds);
+    *reinterpret_cast<decltype(f.v)*>(dst + (size_t)(16 * cb + col) * rows + 32 * rb + 8 * grp) = f.v;
   }
 }
 
@@ -347,7 +348,7 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh) {
     }
   }
   __syncthreads();
-  if constexpr (WANT_QST) tile_out_t<T>(reinterpret_cast<T*>(p.ops.QsT) + chunk * CP * DKP, sQ, CP, DKP, LDQ);
+  if constexpr (WANT_QST) tile_out_t<T, 4>(reinterpret_cast<T*>(p.ops.QsT) + chunk * CP * DKP, sQ, CP, DKP, LDQ);
 
   // ---- intra-chunk scores A, kept in registers until the LDS operands are released
   const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
@@ -356,8 +357,8 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh) {
   f32x4 accA[BPW];
 #pragma unroll
   for (int s = 0; s < BPW; ++s) accA[s] = zero4();
-  T* sKdT = reinterpret_cast<T*>(smem + Cfg::TILE);
-  T* sA = reinterpret_cast<T*>(smem + Cfg::TILE + Cfg::KDT);
+  T* sKd = reinterpret_cast<T*>(smem + Cfg::TILE);
+  T* sA = reinterpret_cast<T*>(smem + Cfg::TILE + Cfg::KD);
   if (fast) {
 #pragma unroll
     for (int s = 0; s < BPW; ++s) {
@@ -493,18 +494,18 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh) {
     for (int x = 0; x < NB; ++x) sA[(16 * x + rr) * LDC + 16 * x + cc] = from_f32<T>(cc <= rr ? acc_d[x] : 0.f);
   }
 
-  // ---- KdT = (k 2^{Gamma - b})^T into LDS
+  // ---- Kd = k 2^{Gamma - b} into LDS row by row; it leaves transposed (KdT)
   if (cs.active) {
 #pragma unroll
-    for (int e = 0; e < V; ++e) {
-      const float gam = sGam[c0 + e];
+    for (int u = 0; u < RPS; ++u) {
+      VT kd;
 #pragma unroll
-      for (int u = 0; u < RPS; ++u)
-        sKdT[(c0 + e) * LDC + r0 + u] = from_f32<T>(cs.kv[u][e] * fast_exp2(gam - cs.b[u][e]));
+      for (int e = 0; e < V; ++e) kd[e] = from_f32<T>(cs.kv[u][e] * fast_exp2(sGam[c0 + e] - cs.b[u][e]));
+      *reinterpret_cast<VT*>(sKd + (r0 + u) * LDQ + c0) = kd;
     }
   }
   __syncthreads();
-  tile_out<T>(reinterpret_cast<T*>(p.ops.KdT) + chunk * DKP * CP, sKdT, DKP, CP, LDC);
+  tile_out_t<T, 4>(reinterpret_cast<T*>(p.ops.KdT) + chunk * DKP * CP, sKd, CP, DKP, LDQ);
   tile_out<T>(reinterpret_cast<T*>(p.ops.A) + chunk * CP * CP, sA, CP, CP, LDC);
   if (tid < DKP) p.ops.Gam[chunk * DKP + tid] = sGam[tid];
 }
