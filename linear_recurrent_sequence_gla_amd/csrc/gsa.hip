@@ -61,9 +61,9 @@ struct GsaCfg {
 template <typename T, int MP, int CP>
 __global__ __launch_bounds__(256) void gsa_prep_kernel(GsaParams p) {
   using M = ChunkMap<T, MP, CP>;
-  constexpr int V = M::V, RPS = M::RPS, LDC = CP + V;
+  constexpr int V = M::V, RPS = M::RPS, LDM = MP + V;
   typedef typename V16<T>::type VT;
-  __shared__ __attribute__((aligned(16))) T sWdT[MP * LDC];
+  __shared__ __attribute__((aligned(16))) T sWd[CP * LDM];     // row by row; leaves transposed
   __shared__ float segtot[M::NSEG * MP];
   __shared__ float sGam[MP];
   __shared__ float red[8];
@@ -80,18 +80,19 @@ __global__ __launch_bounds__(256) void gsa_prep_kernel(GsaParams p) {
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
       const int r = r0 + u;
-      VT wv;
+      VT wv, wd;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const float w = -expm1f(cs.qv[u][e]);
         wv[e] = from_f32<T>(w);
-        sWdT[(c0 + e) * LDC + r] = from_f32<T>(w * fast_exp2(sGam[c0 + e] - cs.b[u][e]));
+        wd[e] = from_f32<T>(w * fast_exp2(sGam[c0 + e] - cs.b[u][e]));
       }
+      *reinterpret_cast<VT*>(sWd + r * LDM + c0) = wd;
       if (r < len && c0 < m) *reinterpret_cast<VT*>(Wg + (size_t)r * m + c0) = wv;
     }
   }
   __syncthreads();
-  tile_out<T>(reinterpret_cast<T*>(p.WdT) + chunk * MP * CP, sWdT, MP, CP, LDC);
+  tile_out_t<T, 4>(reinterpret_cast<T*>(p.WdT) + chunk * MP * CP, sWd, CP, MP, LDM);
   if (threadIdx.x < MP) p.Gam[chunk * MP + threadIdx.x] = sGam[threadIdx.x];
 }
 
@@ -319,9 +320,9 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
 template <typename T, int MP, int CP>
 __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
   using M = ChunkMap<T, MP, CP>;
-  constexpr int V = M::V, RPS = M::RPS, LDC = CP + V;
+  constexpr int V = M::V, RPS = M::RPS, LDM = MP + V;
   typedef typename V16<T>::type VT;
-  __shared__ __attribute__((aligned(16))) T sT[MP * LDC];
+  __shared__ __attribute__((aligned(16))) T sZs[CP * LDM];     // dZ 2^b row by row; leaves transposed
   __shared__ float segtot[M::NSEG * MP];
   __shared__ float sGam[MP];
   __shared__ float red[8];
@@ -374,11 +375,13 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
       float rs = 0.f;
       for (int c = 0; c < M::NCG; ++c) rs += rpart[c * CP + r];
       float dz[V];
+      VT zs;
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         dz[e] = p.act == kActSoftmax ? pv[u][e] * (dpv[u][e] - rs) : gsa_read_grad(pv[u][e], dpv[u][e], p.act);
-        sT[(c0 + e) * LDC + r] = from_f32<T>(dz[e] * fast_exp2(cs.b[u][e]));
+        zs[e] = from_f32<T>(dz[e] * fast_exp2(cs.b[u][e]));
       }
+      *reinterpret_cast<VT*>(sZs + r * LDM + c0) = zs;
       if (r < len && c0 < m) {
 #pragma unroll
         for (int e = 0; e < V; e += 4)
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
     }
   }
   __syncthreads();
-  tile_out<T>(reinterpret_cast<T*>(p.dZsT) + chunk * MP * CP, sT, MP, CP, LDC);
+  tile_out_t<T, 4>(reinterpret_cast<T*>(p.dZsT) + chunk * MP * CP, sZs, CP, MP, LDM);
 }
 
 // ----------------------------------------------------------------------------- pass 1 backward
