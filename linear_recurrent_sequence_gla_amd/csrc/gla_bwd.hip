@@ -445,9 +445,14 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
       for (int e = 0; e < V; ++e) sB[(r0 + u) * DKS + c0 + e] = cs.b[u][e];
     }
   }
-  // q, k and g of this tile are in registers as fp32 from here on: the next tile's go out
-  // (past the last tile, this tile's own again, so that no load is conditional)
-  issue(BwdTile(p, tn < ntiles ? tn : t, DKS));
+  // q, k and g of this tile are in registers as fp32 from here on: the next tile's go out.
+  // Past the last tile the loads still go out, so that none is conditional, but read only
+  // this tile's first row (cached) instead of a whole chunk.
+  {
+    BwdTile nx(p, tn < ntiles ? tn : t, DKS);
+    if (tn >= ntiles) nx.len = 1;
+    issue(nx);
+  }
   __syncthreads();
 
   // ---- epilogue: dq, dk; dg from the two in-chunk prefix sums and Z
