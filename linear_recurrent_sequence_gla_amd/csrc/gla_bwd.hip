@@ -244,331 +244,331 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   int t = blockIdx.x;
   issue(BwdTile(p, t, DKS));
   for (;;) {
-  tid = opaque_thread_index();           // per-lane addresses are formed anew for each tile
-  const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  const BwdTile tile(p, t, DKS);
-  const int tn = t + gridDim.x;                     // this workgroup's next tile
-  const int ch0 = tile.ch0, row0 = tile.row0, len = tile.len, kvalid = tile.kvalid;
-  const size_t chunk = tile.chunk, qbase = tile.qbase;
-  const T* qg = reinterpret_cast<const T*>(p.q) + qbase;
-  const T* kg = reinterpret_cast<const T*>(p.k) + qbase;
-  const T* dog = reinterpret_cast<const T*>(p.do_) + tile.vbase;
-  const T* vg = reinterpret_cast<const T*>(p.v) + tile.vbase;
-  const T* hs = reinterpret_cast<const T*>(p.Hs) + (chunk * DKP + ch0) * DVP;
-  const T* dhs = reinterpret_cast<const T*>(p.dHs) + (chunk * DKP + ch0) * DVP;
-  // the first Dv slice and (with dv) the chunk's A tile load while the gates are scanned
-  SliceStage<T, DKS, CP, WITH_DV> st;
-  st.load(dog, vg, hs, dhs, len, Dv, DVP, 0, kvalid, tid);
-  ATileStage<T, CP, NT> at;
-  if constexpr (WITH_DV) at.load(reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP, tid);
-  const float maxb = cs.finish(segtot, sGam, red, tid);
-  cs.kvals();                            // q is converted after the Dv loop, where it is first needed
-  const bool fast = maxb <= kSpanLimit;
-  const int c0 = cs.cg * V, r0 = cs.seg * RPS;
+    tid = opaque_thread_index();  // per-lane addresses are formed anew for each tile
+    const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+    const BwdTile tile(p, t, DKS);
+    const int tn = t + gridDim.x;  // this workgroup's next tile
+    const int ch0 = tile.ch0, row0 = tile.row0, len = tile.len, kvalid = tile.kvalid;
+    const size_t chunk = tile.chunk, qbase = tile.qbase;
+    const T* qg = reinterpret_cast<const T*>(p.q) + qbase;
+    const T* kg = reinterpret_cast<const T*>(p.k) + qbase;
+    const T* dog = reinterpret_cast<const T*>(p.do_) + tile.vbase;
+    const T* vg = reinterpret_cast<const T*>(p.v) + tile.vbase;
+    const T* hs = reinterpret_cast<const T*>(p.Hs) + (chunk * DKP + ch0) * DVP;
+    const T* dhs = reinterpret_cast<const T*>(p.dHs) + (chunk * DKP + ch0) * DVP;
+    // the first Dv slice and (with dv) the chunk's A tile load while the gates are scanned
+    SliceStage<T, DKS, CP, WITH_DV> st;
+    st.load(dog, vg, hs, dhs, len, Dv, DVP, 0, kvalid, tid);
+    ATileStage<T, CP, NT> at;
+    if constexpr (WITH_DV) at.load(reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP, tid);
+    const float maxb = cs.finish(segtot, sGam, red, tid);
+    cs.kvals();                            // q is converted after the Dv loop, where it is first needed
+    const bool fast = maxb <= kSpanLimit;
+    const int c0 = cs.cg * V, r0 = cs.seg * RPS;
 
-  if constexpr (WITH_DV) {
-    if (cs.active) {
+    if constexpr (WITH_DV) {
+      if (cs.active) {
 #pragma unroll
-      for (int u = 0; u < RPS; ++u) {
-        VT kd;
+        for (int u = 0; u < RPS; ++u) {
+          VT kd;
 #pragma unroll
-        for (int e = 0; e < V; ++e) kd[e] = from_f32<T>(cs.kv[u][e] * fast_exp2(sGam[c0 + e] - cs.b[u][e]));
-        *reinterpret_cast<VT*>(sKd + (r0 + u) * LDQ + c0) = kd;
+          for (int e = 0; e < V; ++e) kd[e] = from_f32<T>(cs.kv[u][e] * fast_exp2(sGam[c0 + e] - cs.b[u][e]));
+          *reinterpret_cast<VT*>(sKd + (r0 + u) * LDQ + c0) = kd;
+        }
+      }
+      at.store(sA, LDC, tid);
+    }
+    float zp[Cf::PH];
+#pragma unroll
+    for (int m = 0; m < Cf::PH; ++m) zp[m] = 0.f;
+    st.zdot(zp);
+    st.store(sdO, sV, sH, sdH, tid);
+    __syncthreads();
+
+    // The accumulators hold their blocks transposed (the products are formed with the operands
+    // swapped), so a lane owns four consecutive columns of one row and moves them to LDS with a
+    // single 8- or 16-byte write
+    f32x4 accA[PA], accQ[PQ], accK[PQ], accKI[PQ];
+#pragma unroll
+    for (int s = 0; s < PA; ++s) accA[s] = zero4();
+#pragma unroll
+    for (int s = 0; s < PQ; ++s) accQ[s] = accK[s] = accKI[s] = zero4();
+
+    for (int js = 0; js < ntile; ++js) {
+      st.load(dog, vg, hs, dhs, len, Dv, DVP, min(js + 1, ntile - 1), kvalid, tid);   // last: harmless reload
+#pragma unroll
+      for (int s = 0; s < PA; ++s) {       // dA += dO V^T
+        const int blk = wave + NW * s;
+        if (blk < NA_BLK) {
+          const int rb = blk / NBR, cb = blk % NBR;
+#pragma unroll
+          for (int kb = 0; kb < kDvTile / 32; ++kb)
+            mma(accA[s], ld8(sV + (16 * cb + col) * LDV + 32 * kb + 8 * grp), ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < PQ; ++s) {       // dQ += dO H^T ; dKI += V dH^T
+        const int blk = wave + NW * s;
+        if (blk < NQ_BLK) {
+          const int rb = blk / NIB, ib = blk % NIB;
+#pragma unroll
+          for (int kb = 0; kb < kDvTile / 32; ++kb) {
+            mma(accQ[s], ld8(sH + (16 * ib + col) * LDV + 32 * kb + 8 * grp), ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
+            mma(accKI[s], ld8(sdH + (16 * ib + col) * LDV + 32 * kb + 8 * grp), ld8(sV + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
+          }
+        }
+      }
+      if constexpr (WITH_DV) {             // dV = A^T dO + Kd dH for this slice
+#pragma unroll
+        for (int s = 0; s < PVb; ++s) {
+          const int blk = wave + NW * s;
+          if (blk < NV_BLK) {
+            const int cb = blk / NJB, jb = blk % NJB;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kr = 0; kr < CP / 32; ++kr)
+              mma(acc, ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV, lane),
+                  ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC, lane));
+#pragma unroll
+            for (int ki = 0; ki < DKS / 32; ++ki)
+              mma(acc, ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV, lane),
+                  ld8(sKd + (16 * cb + col) * LDQ + 32 * ki + 8 * grp));
+            // transposed block: this lane holds dV[16 cb + col][16 jb + 4 grp + e]
+            typename Vec4<T>::type dv4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dv4[e] = from_f32<T>(acc[e]);
+            *reinterpret_cast<typename Vec4<T>::type*>(sdV + (16 * cb + col) * LDV + 16 * jb + 4 * grp) = dv4;
+          }
+        }
+      }
+      __syncthreads();
+      // The next slice is staged before this slice's dv leaves, and on every path: after the
+      // last slice the reloaded copy goes to LDS that the intra phase overwrites, and adds
+      // nothing to Z.  The wait for its loads is explicit and comes first (the only older
+      // memory operations are the previous slice's dv stores); left to the compiler, it sinks
+      // the Z sums below the dv stores and then waits for those stores as well.
+      __builtin_amdgcn_s_waitcnt(0);
+      st.zdot(zp, js + 1 < ntile);
+      st.store(sdO, sV, sH, sdH, tid);
+      if constexpr (WITH_DV) {
+        T* dvg = reinterpret_cast<T*>(p.dv) + tile.vbase;
+        constexpr int PER_ROW = kDvTile / V;
+        for (int idx = tid; idx < CP * PER_ROW; idx += NT) {
+          const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+          const int jj = js * kDvTile + c;
+          if (r < len && jj < Dv)
+            *reinterpret_cast<VT*>(dvg + (size_t)r * Dv + jj) = *reinterpret_cast<const VT*>(sdV + r * LDV + c);
+        }
+      }
+      __syncthreads();
+    }
+    {  // Z_n = 2^Gamma rowsum(dH_{n+1} * H_n): reduce over the lanes that staged one state row
+      constexpr int PER_ROW = kDvTile / V;
+#pragma unroll
+      for (int m = 0; m < Cf::PH; ++m) {
+        float z = zp[m];
+#pragma unroll
+        for (int off = 1; off < PER_ROW; off <<= 1) z += __shfl_xor(z, off, 64);
+        const int idx = tid + NT * m, r = idx / PER_ROW;
+        if (idx < Cf::NH && idx % PER_ROW == 0) sZ[r] = r < kvalid ? z * fast_exp2(sGam[r]) : 0.f;
       }
     }
-    at.store(sA, LDC, tid);
-  }
-  float zp[Cf::PH];
-#pragma unroll
-  for (int m = 0; m < Cf::PH; ++m) zp[m] = 0.f;
-  st.zdot(zp);
-  st.store(sdO, sV, sH, sdH, tid);
-  __syncthreads();
 
-  // The accumulators hold their blocks transposed (the products are formed with the operands
-  // swapped), so a lane owns four consecutive columns of one row and moves them to LDS with a
-  // single 8- or 16-byte write
-  f32x4 accA[PA], accQ[PQ], accK[PQ], accKI[PQ];
-#pragma unroll
-  for (int s = 0; s < PA; ++s) accA[s] = zero4();
-#pragma unroll
-  for (int s = 0; s < PQ; ++s) accQ[s] = accK[s] = accKI[s] = zero4();
+    cs.qvals();
 
-  for (int js = 0; js < ntile; ++js) {
-    st.load(dog, vg, hs, dhs, len, Dv, DVP, min(js + 1, ntile - 1), kvalid, tid);   // last: harmless reload
+    // strictly lower dA -> LDS, the diagonal kept apart in fp32; on the factorised path also
+    // Qs and Ks (the phase-1 tiles are dead here).  The intra products read dA^T, Qs^T and Ks^T
+    // as column runs of these tiles through transposing LDS reads.
 #pragma unroll
-    for (int s = 0; s < PA; ++s) {       // dA += dO V^T
+    for (int s = 0; s < PA; ++s) {
       const int blk = wave + NW * s;
       if (blk < NA_BLK) {
         const int rb = blk / NBR, cb = blk % NBR;
+        // transposed block: this lane holds dA[16 rb + col][16 cb + 4 grp + e]
+        const int r = 16 * rb + col;
+        typename Vec4<T>::type a4;
 #pragma unroll
-        for (int kb = 0; kb < kDvTile / 32; ++kb)
-          mma(accA[s], ld8(sV + (16 * cb + col) * LDV + 32 * kb + 8 * grp), ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < PQ; ++s) {       // dQ += dO H^T ; dKI += V dH^T
-      const int blk = wave + NW * s;
-      if (blk < NQ_BLK) {
-        const int rb = blk / NIB, ib = blk % NIB;
-#pragma unroll
-        for (int kb = 0; kb < kDvTile / 32; ++kb) {
-          mma(accQ[s], ld8(sH + (16 * ib + col) * LDV + 32 * kb + 8 * grp), ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
-          mma(accKI[s], ld8(sdH + (16 * ib + col) * LDV + 32 * kb + 8 * grp), ld8(sV + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
+        for (int e = 0; e < 4; ++e) {
+          const int c = 16 * cb + 4 * grp + e;
+          a4[e] = from_f32<T>(c < r ? accA[s][e] : 0.f);
+          if (c == r) sDiag[r] = accA[s][e];
         }
+        *reinterpret_cast<typename Vec4<T>::type*>(sdA + r * LDC + 16 * cb + 4 * grp) = a4;
       }
     }
-    if constexpr (WITH_DV) {             // dV = A^T dO + Kd dH for this slice
+    if (fast && cs.active) {
 #pragma unroll
-      for (int s = 0; s < PVb; ++s) {
+      for (int u = 0; u < RPS; ++u) {
+        VT qs, ks;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          qs[e] = from_f32<T>(cs.qv[u][e] * fast_exp2(cs.b[u][e]));
+          ks[e] = from_f32<T>(cs.kv[u][e] * fast_exp2(-cs.b[u][e]));
+        }
+        *reinterpret_cast<VT*>(sQs + (r0 + u) * LDQ + c0) = qs;
+        *reinterpret_cast<VT*>(sKs + (r0 + u) * LDQ + c0) = ks;
+      }
+    }
+    __syncthreads();
+    if (fast) {                            // off-diagonal intra terms on MFMA
+#pragma unroll
+      for (int s = 0; s < PQ; ++s) {
         const int blk = wave + NW * s;
-        if (blk < NV_BLK) {
-          const int cb = blk / NJB, jb = blk % NJB;
-          f32x4 acc = zero4();
+        if (blk < NQ_BLK) {
+          const int rb = blk / NIB, ib = blk % NIB;
 #pragma unroll
-          for (int kr = 0; kr < CP / 32; ++kr)
-            mma(acc, ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV, lane),
-                ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC, lane));
-#pragma unroll
-          for (int ki = 0; ki < DKS / 32; ++ki)
-            mma(acc, ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV, lane),
-                ld8(sKd + (16 * cb + col) * LDQ + 32 * ki + 8 * grp));
-          // transposed block: this lane holds dV[16 cb + col][16 jb + 4 grp + e]
-          typename Vec4<T>::type dv4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dv4[e] = from_f32<T>(acc[e]);
-          *reinterpret_cast<typename Vec4<T>::type*>(sdV + (16 * cb + col) * LDV + 16 * jb + 4 * grp) = dv4;
+          for (int kc = 0; kc < CP / 32; ++kc) {
+            mma(accQ[s], ld8_colblk(sKs + (32 * kc) * LDQ + 16 * ib, LDQ, lane),
+                ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp));
+            mma(accK[s], ld8_colblk(sQs + (32 * kc) * LDQ + 16 * ib, LDQ, lane),
+                ld8_colblk(sdA + (32 * kc) * LDC + 16 * rb, LDC, lane));
+          }
         }
       }
     }
-    __syncthreads();
-    // The next slice is staged before this slice's dv leaves, and on every path: after the
-    // last slice the reloaded copy goes to LDS that the intra phase overwrites, and adds
-    // nothing to Z.  The wait for its loads is explicit and comes first (the only older
-    // memory operations are the previous slice's dv stores); left to the compiler, it sinks
-    // the Z sums below the dv stores and then waits for those stores as well.
-    __builtin_amdgcn_s_waitcnt(0);
-    st.zdot(zp, js + 1 < ntile);
-    st.store(sdO, sV, sH, sdH, tid);
-    if constexpr (WITH_DV) {
-      T* dvg = reinterpret_cast<T*>(p.dv) + tile.vbase;
-      constexpr int PER_ROW = kDvTile / V;
-      for (int idx = tid; idx < CP * PER_ROW; idx += NT) {
-        const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
-        const int jj = js * kDvTile + c;
-        if (r < len && jj < Dv)
-          *reinterpret_cast<VT*>(dvg + (size_t)r * Dv + jj) = *reinterpret_cast<const VT*>(sdV + r * LDV + c);
-      }
-    }
-    __syncthreads();
-  }
-  {  // Z_n = 2^Gamma rowsum(dH_{n+1} * H_n): reduce over the lanes that staged one state row
-    constexpr int PER_ROW = kDvTile / V;
-#pragma unroll
-    for (int m = 0; m < Cf::PH; ++m) {
-      float z = zp[m];
-#pragma unroll
-      for (int off = 1; off < PER_ROW; off <<= 1) z += __shfl_xor(z, off, 64);
-      const int idx = tid + NT * m, r = idx / PER_ROW;
-      if (idx < Cf::NH && idx % PER_ROW == 0) sZ[r] = r < kvalid ? z * fast_exp2(sGam[r]) : 0.f;
-    }
-  }
-
-  cs.qvals();
-
-  // strictly lower dA -> LDS, the diagonal kept apart in fp32; on the factorised path also
-  // Qs and Ks (the phase-1 tiles are dead here).  The intra products read dA^T, Qs^T and Ks^T
-  // as column runs of these tiles through transposing LDS reads.
-#pragma unroll
-  for (int s = 0; s < PA; ++s) {
-    const int blk = wave + NW * s;
-    if (blk < NA_BLK) {
-      const int rb = blk / NBR, cb = blk % NBR;
-      // transposed block: this lane holds dA[16 rb + col][16 cb + 4 grp + e]
-      const int r = 16 * rb + col;
-      typename Vec4<T>::type a4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = 16 * cb + 4 * grp + e;
-        a4[e] = from_f32<T>(c < r ? accA[s][e] : 0.f);
-        if (c == r) sDiag[r] = accA[s][e];
-      }
-      *reinterpret_cast<typename Vec4<T>::type*>(sdA + r * LDC + 16 * cb + 4 * grp) = a4;
-    }
-  }
-  if (fast && cs.active) {
-#pragma unroll
-    for (int u = 0; u < RPS; ++u) {
-      VT qs, ks;
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        qs[e] = from_f32<T>(cs.qv[u][e] * fast_exp2(cs.b[u][e]));
-        ks[e] = from_f32<T>(cs.kv[u][e] * fast_exp2(-cs.b[u][e]));
-      }
-      *reinterpret_cast<VT*>(sQs + (r0 + u) * LDQ + c0) = qs;
-      *reinterpret_cast<VT*>(sKs + (r0 + u) * LDQ + c0) = ks;
-    }
-  }
-  __syncthreads();
-  if (fast) {                            // off-diagonal intra terms on MFMA
+    __syncthreads();                       // phase-1 tiles are dead from here on
 #pragma unroll
     for (int s = 0; s < PQ; ++s) {
       const int blk = wave + NW * s;
       if (blk < NQ_BLK) {
         const int rb = blk / NIB, ib = blk % NIB;
-#pragma unroll
-        for (int kc = 0; kc < CP / 32; ++kc) {
-          mma(accQ[s], ld8_colblk(sKs + (32 * kc) * LDQ + 16 * ib, LDQ, lane),
-              ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp));
-          mma(accK[s], ld8_colblk(sQs + (32 * kc) * LDQ + 16 * ib, LDQ, lane),
-              ld8_colblk(sdA + (32 * kc) * LDC + 16 * rb, LDC, lane));
-        }
+        const int o = (16 * rb + col) * LDF + 16 * ib + 4 * grp;   // four consecutive channels
+        *reinterpret_cast<f32x4*>(sDQ + o) = accQ[s];
+        if (fast) *reinterpret_cast<f32x4*>(sDK + o) = accK[s];
+        *reinterpret_cast<f32x4*>(sDKI + o) = accKI[s];
       }
     }
-  }
-  __syncthreads();                       // phase-1 tiles are dead from here on
-#pragma unroll
-  for (int s = 0; s < PQ; ++s) {
-    const int blk = wave + NW * s;
-    if (blk < NQ_BLK) {
-      const int rb = blk / NIB, ib = blk % NIB;
-      const int o = (16 * rb + col) * LDF + 16 * ib + 4 * grp;   // four consecutive channels
-      *reinterpret_cast<f32x4*>(sDQ + o) = accQ[s];
-      if (fast) *reinterpret_cast<f32x4*>(sDK + o) = accK[s];
-      *reinterpret_cast<f32x4*>(sDKI + o) = accKI[s];
-    }
-  }
-  if (!fast && cs.active) {
-#pragma unroll
-    for (int u = 0; u < RPS; ++u) {
-#pragma unroll
-      for (int e = 0; e < V; ++e) sB[(r0 + u) * DKS + c0 + e] = cs.b[u][e];
-    }
-  }
-  // q, k and g of this tile are in registers as fp32 from here on: the next tile's go out.
-  // Past the last tile the loads still go out, so that none is conditional, but read only
-  // this tile's first row (cached) instead of a whole chunk.
-  {
-    BwdTile nx(p, tn < ntiles ? tn : t, DKS);
-    if (tn >= ntiles) nx.len = 1;
-    issue(nx);
-  }
-  __syncthreads();
-
-  // ---- epilogue: dq, dk; dg from the two in-chunk prefix sums and Z
-  float up[RPS][V], uk[RPS][V];          // q dq^nd - k dk'  (suffix-summed) ; k B (prefix-summed)
-  if (cs.active) {
-    T* dqg = reinterpret_cast<T*>(p.dq) + qbase;
-    T* dkg = reinterpret_cast<T*>(p.dk) + qbase;
-    // dq^nd and dk' per element; the path test is uniform and kept outside the element loops
-    // so that the fast path's LDS reads issue together
-    float dqn[RPS][V], dkp[RPS][V];
-    if (fast) {
+    if (!fast && cs.active) {
 #pragma unroll
       for (int u = 0; u < RPS; ++u) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-          const int o = (r0 + u) * LDF + c0 + e;
-          dqn[u][e] = sDQ[o] * fast_exp2(cs.b[u][e]);
-          dkp[u][e] = sDK[o] * fast_exp2(-cs.b[u][e]);
+        for (int e = 0; e < V; ++e) sB[(r0 + u) * DKS + c0 + e] = cs.b[u][e];
+      }
+    }
+    // q, k and g of this tile are in registers as fp32 from here on: the next tile's go out.
+    // Past the last tile the loads still go out, so that none is conditional, but read only
+    // this tile's first row (cached) instead of a whole chunk.
+    {
+      BwdTile nx(p, tn < ntiles ? tn : t, DKS);
+      if (tn >= ntiles) nx.len = 1;
+      issue(nx);
+    }
+    __syncthreads();
+
+    // ---- epilogue: dq, dk; dg from the two in-chunk prefix sums and Z
+    float up[RPS][V], uk[RPS][V];          // q dq^nd - k dk'  (suffix-summed) ; k B (prefix-summed)
+    if (cs.active) {
+      T* dqg = reinterpret_cast<T*>(p.dq) + qbase;
+      T* dkg = reinterpret_cast<T*>(p.dk) + qbase;
+      // dq^nd and dk' per element; the path test is uniform and kept outside the element loops
+      // so that the fast path's LDS reads issue together
+      float dqn[RPS][V], dkp[RPS][V];
+      if (fast) {
+#pragma unroll
+        for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const int o = (r0 + u) * LDF + c0 + e;
+            dqn[u][e] = sDQ[o] * fast_exp2(cs.b[u][e]);
+            dkp[u][e] = sDK[o] * fast_exp2(-cs.b[u][e]);
+          }
+        }
+      } else {
+        // exact off-diagonal intra terms: every exponent b_r - b_c has r > c
+        const int cend = c0 < kvalid ? len : 0;            // padded channels: q = k = 0
+#pragma unroll
+        for (int u = 0; u < RPS; ++u) {
+          const int r = r0 + u;
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            const int i = c0 + e;
+            const float bb = cs.b[u][e];
+            float iq = 0.f, ik = 0.f;
+            for (int c = 0; c < cend; ++c) {
+              if (c < r) iq += to_f32(sdA[r * LDC + c]) * to_f32(kg[(size_t)c * Dk + i]) * fast_exp2(bb - sB[c * DKS + i]);
+              if (c > r) ik += to_f32(sdA[c * LDC + r]) * to_f32(qg[(size_t)c * Dk + i]) * fast_exp2(sB[c * DKS + i] - bb);
+            }
+            dqn[u][e] = sDQ[r * LDF + i] * fast_exp2(bb) + iq;
+            dkp[u][e] = ik;
+          }
         }
       }
-    } else {
-      // exact off-diagonal intra terms: every exponent b_r - b_c has r > c
-      const int cend = c0 < kvalid ? len : 0;            // padded channels: q = k = 0
 #pragma unroll
       for (int u = 0; u < RPS; ++u) {
         const int r = r0 + u;
+        const float dgn = sDiag[r];
+        VT dqv, dkv;
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const int i = c0 + e;
           const float bb = cs.b[u][e];
-          float iq = 0.f, ik = 0.f;
-          for (int c = 0; c < cend; ++c) {
-            if (c < r) iq += to_f32(sdA[r * LDC + c]) * to_f32(kg[(size_t)c * Dk + i]) * fast_exp2(bb - sB[c * DKS + i]);
-            if (c > r) ik += to_f32(sdA[c * LDC + r]) * to_f32(qg[(size_t)c * Dk + i]) * fast_exp2(sB[c * DKS + i] - bb);
+          const float bk = sDKI[r * LDF + i] * fast_exp2(sGam[i] - bb);
+          const float qv = cs.qv[u][e], kv = cs.kv[u][e];
+          dqv[e] = from_f32<T>(dqn[u][e] + dgn * kv);
+          dkv[e] = from_f32<T>(dkp[u][e] + dgn * qv + bk);
+          up[u][e] = qv * dqn[u][e] - kv * dkp[u][e];
+          uk[u][e] = kv * bk;
+        }
+        if (r < len && c0 < kvalid) {
+          *reinterpret_cast<VT*>(dqg + (size_t)r * Dk + c0) = dqv;
+          *reinterpret_cast<VT*>(dkg + (size_t)r * Dk + c0) = dkv;
+        }
+      }
+      // in-segment scans: inclusive suffix of up, exclusive prefix of uk
+      float sp[V], sk[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) sp[e] = sk[e] = 0.f;
+#pragma unroll
+      for (int u = RPS - 1; u >= 0; --u) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          sp[e] += up[u][e];
+          up[u][e] = sp[e];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < RPS; ++u) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const float x = uk[u][e];
+          uk[u][e] = sk[e];
+          sk[e] += x;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        segtot[cs.seg * DKS + c0 + e] = sp[e];
+        segtot[(NSEG + cs.seg) * DKS + c0 + e] = sk[e];
+      }
+    }
+    __syncthreads();
+    // later segments' suffix totals of u, earlier segments' prefix totals of y
+    for (int t = tid; t < 2 * DKS; t += NT)
+      seg_scan_channel<NSEG>(segtot + (t < DKS ? 0 : NSEG * DKS), DKS, t < DKS ? t : t - DKS, t < DKS);
+    __syncthreads();
+    if (cs.active) {
+      float add[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        add[e] = sZ[c0 + e] + segtot[cs.seg * DKS + c0 + e] + segtot[(NSEG + cs.seg) * DKS + c0 + e];
+      float* dgg = p.dg + qbase;
+#pragma unroll
+      for (int u = 0; u < RPS; ++u) {
+        const int r = r0 + u;
+        if (r < len && c0 < kvalid) {
+#pragma unroll
+          for (int e = 0; e < V; e += 4) {
+            f32x4 w;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) w[x] = up[u][e + x] + uk[u][e + x] + add[e + x];
+            *reinterpret_cast<f32x4*>(dgg + (size_t)r * Dk + c0 + e) = w;
           }
-          dqn[u][e] = sDQ[r * LDF + i] * fast_exp2(bb) + iq;
-          dkp[u][e] = ik;
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < RPS; ++u) {
-      const int r = r0 + u;
-      const float dgn = sDiag[r];
-      VT dqv, dkv;
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        const int i = c0 + e;
-        const float bb = cs.b[u][e];
-        const float bk = sDKI[r * LDF + i] * fast_exp2(sGam[i] - bb);
-        const float qv = cs.qv[u][e], kv = cs.kv[u][e];
-        dqv[e] = from_f32<T>(dqn[u][e] + dgn * kv);
-        dkv[e] = from_f32<T>(dkp[u][e] + dgn * qv + bk);
-        up[u][e] = qv * dqn[u][e] - kv * dkp[u][e];
-        uk[u][e] = kv * bk;
-      }
-      if (r < len && c0 < kvalid) {
-        *reinterpret_cast<VT*>(dqg + (size_t)r * Dk + c0) = dqv;
-        *reinterpret_cast<VT*>(dkg + (size_t)r * Dk + c0) = dkv;
-      }
-    }
-    // in-segment scans: inclusive suffix of up, exclusive prefix of uk
-    float sp[V], sk[V];
-#pragma unroll
-    for (int e = 0; e < V; ++e) sp[e] = sk[e] = 0.f;
-#pragma unroll
-    for (int u = RPS - 1; u >= 0; --u) {
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        sp[e] += up[u][e];
-        up[u][e] = sp[e];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < RPS; ++u) {
-#pragma unroll
-      for (int e = 0; e < V; ++e) {
-        const float x = uk[u][e];
-        uk[u][e] = sk[e];
-        sk[e] += x;
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-      segtot[cs.seg * DKS + c0 + e] = sp[e];
-      segtot[(NSEG + cs.seg) * DKS + c0 + e] = sk[e];
-    }
-  }
-  __syncthreads();
-  // later segments' suffix totals of u, earlier segments' prefix totals of y
-  for (int t = tid; t < 2 * DKS; t += NT)
-    seg_scan_channel<NSEG>(segtot + (t < DKS ? 0 : NSEG * DKS), DKS, t < DKS ? t : t - DKS, t < DKS);
-  __syncthreads();
-  if (cs.active) {
-    float add[V];
-#pragma unroll
-    for (int e = 0; e < V; ++e)
-      add[e] = sZ[c0 + e] + segtot[cs.seg * DKS + c0 + e] + segtot[(NSEG + cs.seg) * DKS + c0 + e];
-    float* dgg = p.dg + qbase;
-#pragma unroll
-    for (int u = 0; u < RPS; ++u) {
-      const int r = r0 + u;
-      if (r < len && c0 < kvalid) {
-#pragma unroll
-        for (int e = 0; e < V; e += 4) {
-          f32x4 w;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) w[x] = up[u][e + x] + uk[u][e + x] + add[e + x];
-          *reinterpret_cast<f32x4*>(dgg + (size_t)r * Dk + c0 + e) = w;
-        }
-      }
-    }
-  }
-  if (tn >= ntiles) break;
-  t = tn;
-  __syncthreads();                       // the next tile's scan reuses segtot, sGam and red
+    if (tn >= ntiles) break;
+    t = tn;
+    __syncthreads();                       // the next tile's scan reuses segtot, sGam and red
   }
   __builtin_amdgcn_s_waitcnt(0);         // the last tile's repeated loads have landed
 }
