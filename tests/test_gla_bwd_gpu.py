@@ -109,6 +109,20 @@ def test_full_size_configs_sampled(gla, name, units, dht):
     check_bwd(gla, w, x, units=(b[:, None], h[None, :]), with_dht=dht)
 
 
+@pytest.mark.parametrize("shape", [
+    # (B, H, L, Dk, Dv): just over 256 chunk tiles, a ragged last chunk
+    (3, 3, 1850, 128, 64),      # 261 tiles of the whole-width kernel
+    (2, 5, 1700, 64, 128),      # 270 tiles of the Dk = 64 kernel
+], ids=lambda s: "x".join(map(str, s)))
+def test_workgroups_with_several_tiles(gla, shape):
+    """The chunk-gradient kernel's grid is persistent, one workgroup per CU: with more tiles
+    than workgroups, some workgroups run a second tile, whose q, k and g they loaded during the
+    first tile's epilogue, and the rest stop after one.  Every output is checked."""
+    B, H, L, Dk, Dv = shape
+    w = W.GlaWorkload(f"multi-tile-{Dk}", B, H, L, Dk, Dv, 64, "bf16", 77 + Dk, h0=True, gate_law="iid")
+    check_bwd(gla, w, W.gla_inputs(w))
+
+
 def test_deterministic(gla):
     import torch
     w = W.GlaWorkload("det", 2, 2, 500, 128, 256, 64, "bf16", 12, h0=True)
