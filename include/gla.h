@@ -286,7 +286,8 @@ int gsa_decode_step(const void* q, const void* k, const void* v, const void* g,
  * arrays give GLA_ERR_SHAPE (counts) or GLA_ERR_UNSUPPORTED (ngroups, scales).
  * The groups' GLA forwards run together, each kernel launched once for all groups, each
  * group with its own workspace slice.  A scale-1 group reads q, k, v and g in place; other
- * groups read pooled copies in the workspace. */
+ * groups read pooled copies in the workspace.  The branches' output kernel writes the held,
+ * weighted tokens straight into o (no pooled output is stored). */
 size_t msgla_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype,
                                  int ngroups, const int* scales, const int* heads);
 int msgla_fwd(const void* q, const void* k, const void* v, const void* g,

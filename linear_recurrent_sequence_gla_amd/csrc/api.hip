@@ -487,7 +487,6 @@ namespace {
 // ---------------------------------------------------------------- MS-GLA front end
 struct MsglaLayout {
   size_t pooled[kMsMaxGroups];   // per group: pooled q, k, g, then v (none at scale 1)
-  size_t op[kMsMaxGroups];       // per group: GLA outputs on the pooled sequence
   size_t h0g[kMsMaxGroups];      // per group: initial / final states, gathered from and
   size_t htg[kMsMaxGroups];      //   scattered to the group's heads of h0 / ht
   size_t gla[kMsMaxGroups];      // per group: GLA forward workspace (the groups run together)
@@ -523,8 +522,6 @@ MsglaLayout msgla_layout(int B, int L, int Dk, int Dv, int C, int dtype, int ngr
     const size_t st = align_up((size_t)B * heads[i] * Dk * Dv * 4);
     l.pooled[i] = off;
     if (scales[i] > 1) off += 3 * align_up(rows * Dk * es) + align_up(rows * Dv * es);
-    l.op[i] = off;
-    off += align_up(rows * Dv * es);
     l.h0g[i] = off;
     off += st;
     l.htg[i] = off;
@@ -791,7 +788,7 @@ int msgla_fwd(const void* q, const void* k, const void* v, const void* g, const 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   MsglaParams mp{};
-  mp.q = q; mp.k = k; mp.v = v; mp.g = g; mp.w = w; mp.o = o;
+  mp.q = q; mp.k = k; mp.v = v; mp.g = g;
   mp.B = B; mp.H = H; mp.L = L; mp.Dk = Dk; mp.Dv = Dv; mp.ngroups = ngroups;
   int hbeg = 0;
   bool pooled = false;
@@ -810,7 +807,6 @@ int msgla_fwd(const void* q, const void* k, const void* v, const void* g, const 
       mp.pooled_heads += G.nh;
       mp.max_pooled_len = std::max(mp.max_pooled_len, pooled_len(L, G.s));
     }
-    G.op = ws + lay.op[i];
     hbeg += heads[i];
   }
   hipError_t e = hipSuccess;
@@ -841,7 +837,11 @@ int msgla_fwd(const void* q, const void* k, const void* v, const void* g, const 
       p.q = G.qp; p.k = G.kp; p.v = G.vp; p.g = G.gp;
     }
     p.h0 = h0 ? h0g : nullptr;
-    p.o = G.op; p.ht = ht ? htg : nullptr;
+    p.o = nullptr; p.ht = ht ? htg : nullptr;
+    // the output kernel holds each pooled row over its tokens and applies the fusion weights
+    p.hold_o = o; p.hold_w = w;
+    p.hold_s = G.s; p.hold_L = L; p.hold_H = H; p.hold_h0 = G.h0; p.hold_nh = G.nh;
+    p.hold_ng = ngroups; p.hold_gi = i;
     p.BH = B * G.nh; p.L = Ls; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
     const OpsLayout ol = ops_layout((size_t)p.BH, N, CP, DKP, es, false);
     p.ops = carve_ops(ws + lay.gla[i], ol, false);
@@ -855,8 +855,7 @@ int msgla_fwd(const void* q, const void* k, const void* v, const void* g, const 
                          G.nh * head_bytes, B, hipMemcpyDeviceToDevice, hs) != hipSuccess)
       return GLA_ERR_HIP;
   }
-  e = dtype == GLA_BF16 ? launch_msgla_hold<bf16>(mp, hs) : launch_msgla_hold<float>(mp, hs);
-  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+  return GLA_OK;
 }
 
 }  // extern "C"

@@ -38,7 +38,8 @@ struct OutCfg {
 };
 
 // SEGC: the states come from a segmented walk without their carried part (FwdParams::seg_carry)
-template <typename T, int DKP, int CP, bool SEGC = false>
+// HOLD: O is written to the tokens that hold it (FwdParams::hold_o) instead of to p.o
+template <typename T, int DKP, int CP, bool SEGC = false, bool HOLD = false>
 __device__ __forceinline__ void fwd_out_block(const FwdParams& p, int ntile, int lin) {
   using W = OutCfg<T, DKP, CP>;
   constexpr int LDV = W::LDV, V = W::V, NBR = W::NBR, RBW = W::RBW;
@@ -169,13 +170,38 @@ __device__ __forceinline__ void fwd_out_block(const FwdParams& p, int ntile, int
     }
   }
   __syncthreads();
-  T* og = reinterpret_cast<T*>(p.o) + ((size_t)bh * L + row0) * Dv;
+  if constexpr (HOLD) {
+    // rows row0 .. row0 + len - 1 go to the tokens t with (t + 1) / s - 1 among them, scaled by
+    // the token's weight; chunk 0 also writes the zeros of the tokens before the first block
+    const int s = p.hold_s, Lf = p.hold_L;
+    const int t_beg = n == 0 ? 0 : (row0 + 1) * s - 1;
+    const int t_end = min((row0 + len + 1) * s - 1, Lf);
+    const int b = bh / p.hold_nh, h = p.hold_h0 + bh % p.hold_nh;
+    T* og = reinterpret_cast<T*>(p.hold_o) + ((size_t)b * p.hold_H + h) * Lf * Dv;
+    const float* wg = p.hold_w ? p.hold_w + (size_t)b * Lf * p.hold_ng + p.hold_gi : nullptr;
+    for (int idx = tid; idx < (t_end - t_beg) * PER_ROW; idx += 256) {
+      const int q = idx / PER_ROW, c = (idx - q * PER_ROW) * V;
+      const int t = t_beg + q, r = (t + 1) / s - 1 - row0, jj = tile * kDvTile + c;
+      if (jj < Dv) {
+        VT y = zero_vec<T>();
+        if (r >= 0) {
+          const float wt = wg ? wg[(size_t)t * p.hold_ng] : 1.f;
+          const VT x = *reinterpret_cast<const VT*>(sO + r * LDV + c);
 #pragma unroll
-  for (int m = 0; m < (CP * PER_ROW + 255) / 256; ++m) {
-    const int idx = tid + 256 * m, r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
-    const int j = tile * kDvTile + c;
-    if (idx < CP * PER_ROW && r < len && j < Dv)
-      *reinterpret_cast<VT*>(og + (size_t)r * Dv + j) = *reinterpret_cast<const VT*>(sO + r * LDV + c);
+          for (int e = 0; e < V; ++e) y[e] = from_f32<T>(wt * to_f32(x[e]));
+        }
+        *reinterpret_cast<VT*>(og + (size_t)t * Dv + jj) = y;
+      }
+    }
+  } else {
+    T* og = reinterpret_cast<T*>(p.o) + ((size_t)bh * L + row0) * Dv;
+#pragma unroll
+    for (int m = 0; m < (CP * PER_ROW + 255) / 256; ++m) {
+      const int idx = tid + 256 * m, r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
+      const int j = tile * kDvTile + c;
+      if (idx < CP * PER_ROW && r < len && j < Dv)
+        *reinterpret_cast<VT*>(og + (size_t)r * Dv + j) = *reinterpret_cast<const VT*>(sO + r * LDV + c);
+    }
   }
 }
 
@@ -187,10 +213,10 @@ __global__ __launch_bounds__(256) void gla_fwd_out(FwdParams p, int ntile) {
 }
 
 // several batches in one launch (see Batches): batch i owns blocks first[i] .. first[i+1] - 1
-template <typename T, int DKP, int CP>
+template <typename T, int DKP, int CP, bool HOLD>
 __global__ __launch_bounds__(256) void gla_fwd_out_batches(Batches<FwdParams> b, int ntile) {
   const int gi = b.find(blockIdx.x);
-  fwd_out_block<T, DKP, CP>(b.p[gi], ntile, blockIdx.x - b.first[gi]);
+  fwd_out_block<T, DKP, CP, false, HOLD>(b.p[gi], ntile, blockIdx.x - b.first[gi]);
 }
 
 template <typename T, int DKP, int CP>
@@ -256,7 +282,8 @@ hipError_t launch_gla_fwd_batches(const FwdParams* ps, int nb, hipStream_t s) {
     bp.first[0] = bo.first[0] = 0;
     for (int i = 0; i < nb; ++i) {
       const FwdParams& p = ps[i];
-      if (p.ops.QsT || p.Dk != ps[0].Dk || p.Dv != ps[0].Dv || p.C != ps[0].C) return hipErrorInvalidValue;
+      if (p.ops.QsT || p.Dk != ps[0].Dk || p.Dv != ps[0].Dv || p.C != ps[0].C || !p.hold_o != !ps[0].hold_o)
+        return hipErrorInvalidValue;
       bp.p[i] = PrepParams{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N, p.in};
       bw.p[i] = WalkIO{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, p.ht, p.Dk, p.Dv, p.L, p.C, p.N, 0, p.in};
       bo.p[i] = p;
@@ -268,7 +295,10 @@ hipError_t launch_gla_fwd_batches(const FwdParams* ps, int nb, hipStream_t s) {
     hipError_t e;
     if ((e = launch_prep_batches<T, DKP, CP, false>(bp, maxN, s)) != hipSuccess) return e;
     if ((e = launch_walk_store_batches<T, DKP, CP>(bw, BH, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((gla_fwd_out_batches<T, DKP, CP>), dim3(bo.first[nb]), dim3(256), 0, s, bo, ntile);
+    if (ps[0].hold_o)
+      hipLaunchKernelGGL((gla_fwd_out_batches<T, DKP, CP, true>), dim3(bo.first[nb]), dim3(256), 0, s, bo, ntile);
+    else
+      hipLaunchKernelGGL((gla_fwd_out_batches<T, DKP, CP, false>), dim3(bo.first[nb]), dim3(256), 0, s, bo, ntile);
     return hipGetLastError();
   }
 }

@@ -74,6 +74,14 @@ struct FwdParams {
   const float* seg_carry = nullptr;
   const float* seg_prefix = nullptr;
   int seg_len = 0, seg_n = 0;
+  // set for the batched output kernel by the multi-scale front end: instead of o, row j of
+  // this (pooled) sequence goes to the hold_s tokens t of hold_o with (t + 1) / hold_s - 1 == j,
+  // times hold_w[(b * hold_L + t) * hold_ng + hold_gi] (1 without weights), and the first
+  // hold_s - 1 tokens get zeros.  Sequence bh is batch bh / hold_nh, head hold_h0 + bh % hold_nh
+  // of hold_o [B][hold_H][hold_L][Dv].
+  void* hold_o = nullptr;
+  const float* hold_w = nullptr;
+  int hold_s = 1, hold_L = 0, hold_H = 0, hold_h0 = 0, hold_nh = 1, hold_ng = 1, hold_gi = 0;
 };
 
 struct BwdParams {
@@ -184,12 +192,9 @@ static_assert(kMsMaxGroups <= kMaxBatches, "the head groups run as one batched l
 struct MsglaGroup {
   int h0, nh, s;                  // first head, number of heads, pooling scale
   void *qp, *kp, *gp, *vp;        // pooled inputs [B][nh][ceil(L/s)][Dk or Dv] (T)
-  void* op;                       // pooled GLA outputs [B][nh][ceil(L/s)][Dv] (T)
 };
 struct MsglaParams {
   const void *q, *k, *v, *g;      // [B][H][L][Dk or Dv] (T)
-  const float* w;                 // [B][L][ngroups] fusion weights, or null for 1
-  void* o;                        // [B][H][L][Dv] (T)
   int B, H, L, Dk, Dv, ngroups;
   int pooled_heads;               // heads in groups with scale > 1
   int max_pooled_len;             // longest pooled sequence among those groups
@@ -197,8 +202,6 @@ struct MsglaParams {
 };
 template <typename T>
 hipError_t launch_msgla_pool(const MsglaParams& p, hipStream_t s);
-template <typename T>
-hipError_t launch_msgla_hold(const MsglaParams& p, hipStream_t s);
 
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per workgroup on gfx950
 

@@ -1,7 +1,8 @@
-// msgla.hip -- the multi-scale GLA (MS-GLA) front end: temporal pooling per head group, and
-// the causal hold with per-token fusion weights.  Between the two, each group's pooled
-// sequence runs through the GLA forward kernels unchanged (MS-GLA summary, section 3.4: static,
-// non-overlapping pooling keeps each branch a contiguous, shorter GLA sequence).
+// msgla.hip -- the multi-scale GLA (MS-GLA) front end's temporal pooling per head group.
+// Each group's pooled sequence then runs through the GLA forward kernels unchanged (MS-GLA
+// summary, section 3.4: static, non-overlapping pooling keeps each branch a contiguous,
+// shorter GLA sequence), and the forward's output kernel writes the causal hold with the
+// per-token fusion weights itself (FwdParams::hold_o).
 //
 //   pooling (section 3.1): block j of group scale s averages tokens j*s .. min(j*s+s, L) - 1
 //       of q, k, g and v (a trailing partial block averages only its real tokens), for the
@@ -11,7 +12,7 @@
 //       latest block it has fully seen (zero before the first completes), times the caller's
 //       weight w[b][t][group].
 //
-// Both kernels are plain HBM streams with 16-byte accesses and fp32 arithmetic; nothing here
+// The pooling is a plain HBM stream with 16-byte accesses and fp32 sums; nothing here
 // contracts, so there is no matrix-core work.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -19,16 +20,7 @@
 namespace gla {
 
 constexpr int kMsRowsPerBlock = 4;      // pooled rows per pooling workgroup
-constexpr int kMsTokPerBlock = 16;      // tokens per hold workgroup
 constexpr int kMsUnroll = 4;            // tokens whose loads are in flight together
-
-// head group of head h (groups hold consecutive heads, in order)
-__device__ __forceinline__ int ms_group_of(const MsglaParams& p, int h) {
-  int gi = 0;
-#pragma unroll 1
-  while (gi + 1 < p.ngroups && h >= p.grp[gi + 1].h0) ++gi;
-  return gi;
-}
 
 // grid (ceil(max pooled length / kMsRowsPerBlock), B * pooled heads): only the groups with a
 // scale above 1 are pooled; blocks past their group's pooled length return
@@ -96,36 +88,6 @@ __global__ __launch_bounds__(256) void msgla_pool_kernel(MsglaParams p) {
   }
 }
 
-// grid (ceil(L / kMsTokPerBlock), B*H)
-template <typename T>
-__global__ __launch_bounds__(256) void msgla_hold_kernel(MsglaParams p) {
-  typedef typename V16<T>::type VT;
-  constexpr int V = V16<T>::N;
-  const int bh = blockIdx.y, b = bh / p.H, h = bh - b * p.H;
-  const int gi = ms_group_of(p, h);
-  const MsglaGroup& G = p.grp[gi];
-  const int s = G.s, Ls = (p.L + s - 1) / s, hl = h - G.h0;
-  const int nv = p.Dv / V;
-  const int t0 = blockIdx.x * kMsTokPerBlock, toks = min(kMsTokPerBlock, p.L - t0);
-  const T* op = reinterpret_cast<const T*>(G.op) + (size_t)(b * G.nh + hl) * Ls * p.Dv;
-  T* o = reinterpret_cast<T*>(p.o) + (size_t)bh * p.L * p.Dv;
-  for (int idx = threadIdx.x; idx < toks * nv; idx += 256) {
-    const int r = idx / nv, col = (idx - r * nv) * V;
-    const int t = t0 + r, j = (t + 1) / s - 1;
-    const float wt = p.w ? p.w[((size_t)b * p.L + t) * p.ngroups + gi] : 1.f;
-    VT y;
-    if (j >= 0) {
-      const VT x = *reinterpret_cast<const VT*>(op + (size_t)j * p.Dv + col);
-#pragma unroll
-      for (int e = 0; e < V; ++e) y[e] = from_f32<T>(wt * to_f32(x[e]));
-    } else {
-#pragma unroll
-      for (int e = 0; e < V; ++e) y[e] = from_f32<T>(0.f);
-    }
-    *reinterpret_cast<VT*>(o + (size_t)t * p.Dv + col) = y;
-  }
-}
-
 template <typename T>
 hipError_t launch_msgla_pool(const MsglaParams& p, hipStream_t s) {
   if (p.pooled_heads == 0) return hipSuccess;
@@ -135,16 +97,7 @@ hipError_t launch_msgla_pool(const MsglaParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_msgla_hold(const MsglaParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((msgla_hold_kernel<T>), dim3((p.L + kMsTokPerBlock - 1) / kMsTokPerBlock, p.B * p.H),
-                     dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
 template hipError_t launch_msgla_pool<bf16>(const MsglaParams&, hipStream_t);
 template hipError_t launch_msgla_pool<float>(const MsglaParams&, hipStream_t);
-template hipError_t launch_msgla_hold<bf16>(const MsglaParams&, hipStream_t);
-template hipError_t launch_msgla_hold<float>(const MsglaParams&, hipStream_t);
 
 }  // namespace gla
