@@ -179,18 +179,27 @@ __device__ __forceinline__ void fwd_out_block(const FwdParams& p, int ntile, int
     const int b = bh / p.hold_nh, h = p.hold_h0 + bh % p.hold_nh;
     T* og = reinterpret_cast<T*>(p.hold_o) + ((size_t)b * p.hold_H + h) * Lf * Dv;
     const float* wg = p.hold_w ? p.hold_w + (size_t)b * Lf * p.hold_ng + p.hold_gi : nullptr;
-    for (int idx = tid; idx < (t_end - t_beg) * PER_ROW; idx += 256) {
-      const int q = idx / PER_ROW, c = (idx - q * PER_ROW) * V;
-      const int t = t_beg + q, r = (t + 1) / s - 1 - row0, jj = tile * kDvTile + c;
-      if (jj < Dv) {
-        VT y = zero_vec<T>();
-        if (r >= 0) {
-          const float wt = wg ? wg[(size_t)t * p.hold_ng] : 1.f;
-          const VT x = *reinterpret_cast<const VT*>(sO + r * LDV + c);
+    // the weights of 256 tokens at a time go to LDS with one load per thread, so that no
+    // store waits on a load of its own
+    __shared__ float sW[256];
+    for (int tb = t_beg; tb < t_end; tb += 256) {
+      const int nt = min(256, t_end - tb);
+      if (tb > t_beg) __syncthreads();   // the previous tokens' weights are read
+      if (tid < nt) sW[tid] = wg ? wg[(size_t)(tb + tid) * p.hold_ng] : 1.f;
+      __syncthreads();
+      for (int idx = tid; idx < nt * PER_ROW; idx += 256) {
+        const int q = idx / PER_ROW, c = (idx - q * PER_ROW) * V;
+        const int t = tb + q, r = (t + 1) / s - 1 - row0, jj = tile * kDvTile + c;
+        if (jj < Dv) {
+          VT y = zero_vec<T>();
+          if (r >= 0) {
+            const float wt = sW[q];
+            const VT x = *reinterpret_cast<const VT*>(sO + r * LDV + c);
 #pragma unroll
-          for (int e = 0; e < V; ++e) y[e] = from_f32<T>(wt * to_f32(x[e]));
+            for (int e = 0; e < V; ++e) y[e] = from_f32<T>(wt * to_f32(x[e]));
+          }
+          *reinterpret_cast<VT*>(og + (size_t)t * Dv + jj) = y;
         }
-        *reinterpret_cast<VT*>(og + (size_t)t * Dv + jj) = y;
       }
     }
   } else {
