@@ -45,8 +45,10 @@
  *     a *_workspace_bytes() query returns 0 for them.
  *   - Results are deterministic: no floating-point atomics are used, so two runs on the same
  *     inputs give bitwise-identical outputs.
- *   - The library is reentrant.  Its only global state is the compute-unit count of each
- *     device it has run on (read once; it picks the state walks' tile height).
+ *   - The library is reentrant.  Its only global state, kept per device it has run on and
+ *     read once, is the compute-unit count (it picks the state walks' tile height) and how
+ *     many chunk-gradient workgroups the device runs at once (the size of that kernel's
+ *     persistent grid).
  */
 #ifndef GLA_AMD_GLA_H
 #define GLA_AMD_GLA_H
