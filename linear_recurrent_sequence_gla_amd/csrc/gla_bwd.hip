@@ -296,48 +296,108 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
 
     for (int js = 0; js < ntile; ++js) {
       st.load(dog, vg, hs, dhs, len, Dv, DVP, min(js + 1, ntile - 1), kvalid, tid);   // last: harmless reload
+      // Where every wave owns the same number of blocks, its blocks of one product share one
+      // operand block (dA: the V block, dQ and dKI: the H and dH blocks, dV: the dO and dH
+      // column blocks), which is then read from LDS once per k step instead of once per block.
+      // Each accumulator still sums its k steps in the same order.
+      if constexpr (NA_BLK % NW == 0 && NW % NBR == 0) {   // dA += dO V^T
+        const int cb = wave % NBR, rb0 = wave / NBR;
 #pragma unroll
-      for (int s = 0; s < PA; ++s) {       // dA += dO V^T
-        const int blk = wave + NW * s;
-        if (blk < NA_BLK) {
-          const int rb = blk / NBR, cb = blk % NBR;
+        for (int kb = 0; kb < kDvTile / 32; ++kb) {
+          const Frag<T> fv = ld8(sV + (16 * cb + col) * LDV + 32 * kb + 8 * grp);
 #pragma unroll
-          for (int kb = 0; kb < kDvTile / 32; ++kb)
-            mma(accA[s], ld8(sV + (16 * cb + col) * LDV + 32 * kb + 8 * grp), ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
+          for (int s = 0; s < PA; ++s)
+            mma(accA[s], fv, ld8(sdO + (16 * (rb0 + (NW / NBR) * s) + col) * LDV + 32 * kb + 8 * grp));
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < PA; ++s) {       // dA += dO V^T
+          const int blk = wave + NW * s;
+          if (blk < NA_BLK) {
+            const int rb = blk / NBR, cb = blk % NBR;
+#pragma unroll
+            for (int kb = 0; kb < kDvTile / 32; ++kb)
+              mma(accA[s], ld8(sV + (16 * cb + col) * LDV + 32 * kb + 8 * grp), ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
+          }
         }
       }
+      if constexpr (NQ_BLK % NW == 0 && NW % NIB == 0) {   // dQ += dO H^T ; dKI += V dH^T
+        const int ib = wave % NIB, rb0 = wave / NIB;
 #pragma unroll
-      for (int s = 0; s < PQ; ++s) {       // dQ += dO H^T ; dKI += V dH^T
-        const int blk = wave + NW * s;
-        if (blk < NQ_BLK) {
-          const int rb = blk / NIB, ib = blk % NIB;
+        for (int kb = 0; kb < kDvTile / 32; ++kb) {
+          const Frag<T> fh = ld8(sH + (16 * ib + col) * LDV + 32 * kb + 8 * grp);
+          const Frag<T> fdh = ld8(sdH + (16 * ib + col) * LDV + 32 * kb + 8 * grp);
 #pragma unroll
-          for (int kb = 0; kb < kDvTile / 32; ++kb) {
-            mma(accQ[s], ld8(sH + (16 * ib + col) * LDV + 32 * kb + 8 * grp), ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
-            mma(accKI[s], ld8(sdH + (16 * ib + col) * LDV + 32 * kb + 8 * grp), ld8(sV + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
+          for (int s = 0; s < PQ; ++s) {
+            const int o = (16 * (rb0 + (NW / NIB) * s) + col) * LDV + 32 * kb + 8 * grp;
+            mma(accQ[s], fh, ld8(sdO + o));
+            mma(accKI[s], fdh, ld8(sV + o));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < PQ; ++s) {       // dQ += dO H^T ; dKI += V dH^T
+          const int blk = wave + NW * s;
+          if (blk < NQ_BLK) {
+            const int rb = blk / NIB, ib = blk % NIB;
+#pragma unroll
+            for (int kb = 0; kb < kDvTile / 32; ++kb) {
+              mma(accQ[s], ld8(sH + (16 * ib + col) * LDV + 32 * kb + 8 * grp), ld8(sdO + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
+              mma(accKI[s], ld8(sdH + (16 * ib + col) * LDV + 32 * kb + 8 * grp), ld8(sV + (16 * rb + col) * LDV + 32 * kb + 8 * grp));
+            }
           }
         }
       }
       if constexpr (WITH_DV) {             // dV = A^T dO + Kd dH for this slice
+        if constexpr (NV_BLK % NW == 0 && NW % NJB == 0) {
+          const int jb = wave % NJB, cb0 = wave / NJB;
+          f32x4 acc[PVb];
 #pragma unroll
-        for (int s = 0; s < PVb; ++s) {
-          const int blk = wave + NW * s;
-          if (blk < NV_BLK) {
-            const int cb = blk / NJB, jb = blk % NJB;
-            f32x4 acc = zero4();
+          for (int s = 0; s < PVb; ++s) acc[s] = zero4();
 #pragma unroll
-            for (int kr = 0; kr < CP / 32; ++kr)
-              mma(acc, ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV, lane),
-                  ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC, lane));
+          for (int kr = 0; kr < CP / 32; ++kr) {
+            const Frag<T> fo = ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV, lane);
 #pragma unroll
-            for (int ki = 0; ki < DKS / 32; ++ki)
-              mma(acc, ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV, lane),
-                  ld8(sKd + (16 * cb + col) * LDQ + 32 * ki + 8 * grp));
+            for (int s = 0; s < PVb; ++s)
+              mma(acc[s], fo, ld8_colblk(sA + (32 * kr) * LDC + 16 * (cb0 + (NW / NJB) * s), LDC, lane));
+          }
+#pragma unroll
+          for (int ki = 0; ki < DKS / 32; ++ki) {
+            const Frag<T> fd = ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV, lane);
+#pragma unroll
+            for (int s = 0; s < PVb; ++s)
+              mma(acc[s], fd, ld8(sKd + (16 * (cb0 + (NW / NJB) * s) + col) * LDQ + 32 * ki + 8 * grp));
+          }
+#pragma unroll
+          for (int s = 0; s < PVb; ++s) {
             // transposed block: this lane holds dV[16 cb + col][16 jb + 4 grp + e]
+            const int cb = cb0 + (NW / NJB) * s;
             typename Vec4<T>::type dv4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dv4[e] = from_f32<T>(acc[e]);
+            for (int e = 0; e < 4; ++e) dv4[e] = from_f32<T>(acc[s][e]);
             *reinterpret_cast<typename Vec4<T>::type*>(sdV + (16 * cb + col) * LDV + 16 * jb + 4 * grp) = dv4;
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < PVb; ++s) {
+            const int blk = wave + NW * s;
+            if (blk < NV_BLK) {
+              const int cb = blk / NJB, jb = blk % NJB;
+              f32x4 acc = zero4();
+#pragma unroll
+              for (int kr = 0; kr < CP / 32; ++kr)
+                mma(acc, ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV, lane),
+                    ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC, lane));
+#pragma unroll
+              for (int ki = 0; ki < DKS / 32; ++ki)
+                mma(acc, ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV, lane),
+                    ld8(sKd + (16 * cb + col) * LDQ + 32 * ki + 8 * grp));
+              // transposed block: this lane holds dV[16 cb + col][16 jb + 4 grp + e]
+              typename Vec4<T>::type dv4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) dv4[e] = from_f32<T>(acc[e]);
+              *reinterpret_cast<typename Vec4<T>::type*>(sdV + (16 * cb + col) * LDV + 16 * jb + 4 * grp) = dv4;
+            }
           }
         }
       }
