@@ -471,17 +471,34 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
     }
     __syncthreads();
     if (fast) {                            // off-diagonal intra terms on MFMA
+      if constexpr (NQ_BLK % NW == 0 && NW % NIB == 0) {
+        // as in the slice loop: the key block ib is fixed per wave, so its Ks and Qs column
+        // blocks are read once per k step
+        const int ib = wave % NIB, rb0 = wave / NIB;
 #pragma unroll
-      for (int s = 0; s < PQ; ++s) {
-        const int blk = wave + NW * s;
-        if (blk < NQ_BLK) {
-          const int rb = blk / NIB, ib = blk % NIB;
+        for (int kc = 0; kc < CP / 32; ++kc) {
+          const Frag<T> fks = ld8_colblk(sKs + (32 * kc) * LDQ + 16 * ib, LDQ, lane);
+          const Frag<T> fqs = ld8_colblk(sQs + (32 * kc) * LDQ + 16 * ib, LDQ, lane);
 #pragma unroll
-          for (int kc = 0; kc < CP / 32; ++kc) {
-            mma(accQ[s], ld8_colblk(sKs + (32 * kc) * LDQ + 16 * ib, LDQ, lane),
-                ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp));
-            mma(accK[s], ld8_colblk(sQs + (32 * kc) * LDQ + 16 * ib, LDQ, lane),
-                ld8_colblk(sdA + (32 * kc) * LDC + 16 * rb, LDC, lane));
+          for (int s = 0; s < PQ; ++s) {
+            const int rb = rb0 + (NW / NIB) * s;
+            mma(accQ[s], fks, ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp));
+            mma(accK[s], fqs, ld8_colblk(sdA + (32 * kc) * LDC + 16 * rb, LDC, lane));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < PQ; ++s) {
+          const int blk = wave + NW * s;
+          if (blk < NQ_BLK) {
+            const int rb = blk / NIB, ib = blk % NIB;
+#pragma unroll
+            for (int kc = 0; kc < CP / 32; ++kc) {
+              mma(accQ[s], ld8_colblk(sKs + (32 * kc) * LDQ + 16 * ib, LDQ, lane),
+                  ld8(sdA + (16 * rb + col) * LDC + 32 * kc + 8 * grp));
+              mma(accK[s], ld8_colblk(sQs + (32 * kc) * LDQ + 16 * ib, LDQ, lane),
+                  ld8_colblk(sdA + (32 * kc) * LDC + 16 * rb, LDC, lane));
+            }
           }
         }
       }
