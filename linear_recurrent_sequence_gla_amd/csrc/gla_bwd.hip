@@ -32,7 +32,7 @@
 //   4. gla_bwd_chunk: dA, dq, dk (+ dv when the whole key width fits one workgroup) on MFMA
 //      over 64-column slices of Dv, then an element-wise epilogue (gate scaling, diagonal
 //      terms, Z_n, the two in-chunk prefix sums of dg) with 16-byte stores
-//                                                              grid N x BH x (Dk slices)
+//                               N x BH x (Dk slices) tiles over a persistent grid, one per CU
 //   5. gla_bwd_dv (only when dv did not fit step 4)           grid N x BH x ceil(Dv/64)
 // Intra-chunk terms use the factorised form only on chunks whose gate span passes the same
 // check as the forward; other chunks form them exactly, element by element, in fp32.

@@ -77,7 +77,7 @@ struct PrepCfg {
   static constexpr size_t TILE = (size_t)CP * LDQ * sizeof(T);
   static constexpr size_t KD = TILE;                   // Kd [CP][DKP], copied out transposed
   static constexpr size_t ATILE = (size_t)CP * LDC * sizeof(T);
-  // fast path: sQ, sK (+ sQl, sKl); after the score product the same bytes hold KdT and A
+  // fast path: sQ, sK (+ sQl, sKl); after the score product the same bytes hold Kd and A
   static constexpr size_t FAST = (SPLIT ? 4 : 2) * TILE;
   static constexpr size_t SAFE = TILE + (size_t)3 * CP * 33 * 4 +
                                  (size_t)(SPLIT ? 2 : 1) * (CP + 16) * LDP * sizeof(T);
