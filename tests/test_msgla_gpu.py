@@ -51,6 +51,7 @@ SHAPES = [
     (1, 2, 10, 64, 64, 16, "bf16", (1, 16), (1, 1), True, True),        # a scale longer than L
     (2, 5, 257, 128, 128, 64, "bf16", (4, 1), (3, 2), False, True),      # coarse group first
     (2, 5, 190, 64, 128, 64, "bf16", (2, 1, 4), (1, 3, 1), True, True),  # in-place group in the middle
+    (1, 2, 1100, 64, 64, 64, "bf16", (1, 8), (1, 1), True, True),        # 512 held tokens per chunk
 ]
 
 
