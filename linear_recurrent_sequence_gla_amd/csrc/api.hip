@@ -211,8 +211,8 @@ const char* gla_status_str(int s) {
     case GLA_ERR_UNSUPPORTED:
       return "GLA_ERR_UNSUPPORTED: C must be 16/32/64/128, Dk and m multiples of 16 up to 256, "
              "Dv a multiple of 16 up to 512, B*H <= 65535, 16-byte aligned tensors; tiles that "
-             "exceed a CU's LDS are not supported (bf16: Dk > 128 with C = 128; fp32: C = 128, "
-             "or Dk > 128 with C = 64)";
+             "exceed a CU's LDS are not supported (bf16: Dk > 128 with C = 128; fp32: Dk > 128 "
+             "with C = 64, Dk > 64 with C = 128, and every backward with C = 128)";
     case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE: workspace NULL or smaller than the query returned";
     case GLA_ERR_ALIAS: return "GLA_ERR_ALIAS: an output overlaps an input, another output or the workspace";
     case GLA_ERR_HIP: return "GLA_ERR_HIP: a HIP kernel launch failed";
@@ -578,7 +578,7 @@ GsaLayout gsa_layout_of(int B, int H, int L, int Dk, int Dv, int m, int C, int d
     l.Hs2 = take(BH * N * MP * DvP * es);
   }
   if (grad) {
-    l.dP = take(tok * es);
+    l.dP = take(tok * 4);
     l.dW2 = take(tok * es);
     l.dg2 = take(tok * 4);
     l.dZ = take(tok * 4);
@@ -606,7 +606,7 @@ GsaParams gsa_params(const GsaLayout& lf, char* fb, bool saved, const GsaLayout&
   p.ops2 = carve_ops(fb + lf.ops2base, lf.ops2, saved);
   p.Hs2 = fb + lf.Hs2;
   if (gb) {
-    p.dP = gb + lg.dP; p.dW2 = gb + lg.dW2;
+    p.dP = reinterpret_cast<float*>(gb + lg.dP); p.dW2 = gb + lg.dW2;
     p.dg2 = reinterpret_cast<float*>(gb + lg.dg2); p.dZ = reinterpret_cast<float*>(gb + lg.dZ);
     p.dS1s = gb + lg.dS1s; p.dZsT = gb + lg.dZsT;
     p.dHs2 = gb + lg.dHs2;

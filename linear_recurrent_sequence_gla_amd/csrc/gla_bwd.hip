@@ -33,7 +33,7 @@
 //      over 64-column slices of Dv, then an element-wise epilogue (gate scaling, diagonal
 //      terms, Z_n, the two in-chunk prefix sums of dg) with 16-byte stores
 //                               N x BH x (Dk slices) tiles over a persistent grid, one per CU
-//   5. gla_bwd_dv (only when dv did not fit step 4)           grid N x BH x ceil(Dv/64)
+//   5. gla_bwd_dv (only when dv did not fit step 4)           grid N x BH
 // Intra-chunk terms use the factorised form only on chunks whose gate span passes the same
 // check as the forward; other chunks form them exactly, element by element, in fp32.
 #include "walks.hpp"
@@ -175,15 +175,31 @@ struct ATileStage {
   }
 };
 
-// Where tile t of the chunk kernel lies: chunk fastest, then b*h, then the key-width slice
-// (the order a grid (N, BH, DKP / DKS) gives its blocks).
+// Where tile t of the chunk kernel lies.  With the whole key width in one tile (NS = 1):
+// chunk fastest, then b*h.  With NS key-width slices, the slices of one chunk are 8 tiles
+// apart: workgroups are dealt to the 8 XCDs in turn, so the persistent grid's workgroups w and
+// w + 8 sit on one XCD and take their tiles at the same time; a chunk's dO and V rows, which
+// every slice reads, then come from HBM once and from that XCD's L2 for the other slices.
 struct BwdTile {
   int n, bh, ch0, row0, len, kvalid;
   size_t chunk, qbase, vbase;
-  __device__ __forceinline__ BwdTile(const BwdParams& p, int t, int DKS) {
-    n = t % p.N;
-    bh = t / p.N % p.BH;
-    ch0 = t / (p.N * p.BH) * DKS;
+  __device__ __forceinline__ BwdTile(const BwdParams& p, int t, int DKS, int NS) {
+    const int nc = p.N * p.BH, whole = nc / 8 * 8;
+    int c = t, s = 0;
+    if (NS > 1) {
+      if (t < whole * NS) {               // groups of 8 chunks: tile 8 (NS a + s) + x
+        const int x = t % 8, r = t / 8;
+        s = r % NS;
+        c = (r / NS) * 8 + x;
+      } else {                            // the last nc % 8 chunks, slice by slice
+        const int u = t - whole * NS, rem = nc - whole;
+        s = u / rem;
+        c = whole + u % rem;
+      }
+    }
+    n = c % p.N;
+    bh = c / p.N;
+    ch0 = s * DKS;
     row0 = n * p.C;
     len = min(p.C, p.L - row0);
     kvalid = min(DKS, p.Dk - ch0);
@@ -242,11 +258,11 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
             reinterpret_cast<const T*>(p.g) + u.qbase, Dk, Dk - u.ch0, u.len, tid);
   };
   int t = blockIdx.x;
-  issue(BwdTile(p, t, DKS));
+  issue(BwdTile(p, t, DKS, DKP / DKS));
   for (;;) {
     tid = opaque_thread_index();  // per-lane addresses are formed anew for each tile
     const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
-    const BwdTile tile(p, t, DKS);
+    const BwdTile tile(p, t, DKS, DKP / DKS);
     const int tn = t + gridDim.x;  // this workgroup's next tile
     const int ch0 = tile.ch0, row0 = tile.row0, len = tile.len, kvalid = tile.kvalid;
     const size_t chunk = tile.chunk, qbase = tile.qbase;
@@ -526,7 +542,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
     // Past the last tile the loads still go out, so that none is conditional, but read only
     // this tile's first row (cached) instead of a whole chunk.
     {
-      BwdTile nx(p, tn < ntiles ? tn : t, DKS);
+      BwdTile nx(p, tn < ntiles ? tn : t, DKS, DKP / DKS);
       if (tn >= ntiles) nx.len = 1;
       issue(nx);
     }
@@ -574,20 +590,30 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
       for (int u = 0; u < RPS; ++u) {
         const int r = r0 + u;
         const float dgn = sDiag[r];
-        VT dqv, dkv;
+        VT dkv;
+        float dqf[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const int i = c0 + e;
           const float bb = cs.b[u][e];
           const float bk = sDKI[r * LDF + i] * fast_exp2(sGam[i] - bb);
           const float qv = cs.qv[u][e], kv = cs.kv[u][e];
-          dqv[e] = from_f32<T>(dqn[u][e] + dgn * kv);
+          dqf[e] = dqn[u][e] + dgn * kv;
           dkv[e] = from_f32<T>(dkp[u][e] + dgn * qv + bk);
           up[u][e] = qv * dqn[u][e] - kv * dkp[u][e];
           uk[u][e] = kv * bk;
         }
         if (r < len && c0 < kvalid) {
-          *reinterpret_cast<VT*>(dqg + (size_t)r * Dk + c0) = dqv;
+          if (p.dq32) {
+            float* d32 = p.dq32 + qbase + (size_t)r * Dk + c0;
+#pragma unroll
+            for (int e = 0; e < V; e += 4) *reinterpret_cast<f32x4*>(d32 + e) = f32x4{dqf[e], dqf[e + 1], dqf[e + 2], dqf[e + 3]};
+          } else {
+            VT dqv;
+#pragma unroll
+            for (int e = 0; e < V; ++e) dqv[e] = from_f32<T>(dqf[e]);
+            *reinterpret_cast<VT*>(dqg + (size_t)r * Dk + c0) = dqv;
+          }
           *reinterpret_cast<VT*>(dkg + (size_t)r * Dk + c0) = dkv;
         }
       }
@@ -651,73 +677,160 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
 }
 
 // ======================================================================= dv (separate)
-template <typename T, int DKP, int CP>
-struct BwdDvCfg {
-  static constexpr int V = 16 / (int)sizeof(T);
-  static constexpr int LDC = CP + V, LDV = kDvTile + V;
-  static constexpr size_t AT = (size_t)CP * LDC * sizeof(T);
-  static constexpr size_t KT = (size_t)DKP * LDC * sizeof(T);
-  static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
-  static constexpr size_t HT = (size_t)DKP * LDV * sizeof(T);
-  static constexpr size_t BYTES = AT + KT + 2 * VT + HT;
-};
+// When the chunk-gradient kernel splits the key width (it does when dv does not fit its LDS:
+// Dk = 256, or C = 128), dv = A^T dO + Kd dH_{n+1} runs here.  One workgroup of 8 waves per
+// (chunk, b*h) stages the chunk's A and KdT tiles once and walks the 64-column Dv slices;
+// each slice's dO and dH loads are in flight while the previous slice's products run, as in
+// the chunk-gradient kernel.  Both products read their column operands with transposing LDS
+// reads (tiles with 32-byte row pads), and the accumulators hold dV transposed so that each
+// lane moves four consecutive columns of a row to LDS with one vector write.
+constexpr int kDvThreads = 512;
 
 template <typename T, int DKP, int CP>
-__global__ __launch_bounds__(256) void gla_bwd_dv(BwdParams p, int ntile) {
+struct BwdDvCfg {
+  static constexpr int NT = kDvThreads, NW = NT / 64;
+  static constexpr int V = 16 / (int)sizeof(T);
+  static constexpr int LDC = CP + 2 * V, LDV = kDvTile + 2 * V;
+  static constexpr size_t AT = (size_t)CP * LDC * sizeof(T);     // A   [CP][CP]
+  static constexpr size_t KT = (size_t)DKP * LDC * sizeof(T);    // KdT [DKP][CP]
+  static constexpr size_t OT = (size_t)CP * LDV * sizeof(T);     // dO slice, dV staging [CP][64]
+  static constexpr size_t HT = (size_t)DKP * LDV * sizeof(T);    // dH slice [DKP][64]
+  static constexpr size_t BYTES = AT + KT + 2 * OT + HT;
+  static constexpr int PER_ROW = kDvTile / V;
+  static constexpr int NO = CP * PER_ROW, NH = DKP * PER_ROW;    // 16-byte vectors per slice
+  static constexpr int PO = (NO + NT - 1) / NT, PH = (NH + NT - 1) / NT;
+  static constexpr int NA = CP * CP / V, NK = DKP * CP / V;
+  static constexpr int PA = (NA + NT - 1) / NT, PK = (NK + NT - 1) / NT;
+  static constexpr int NBR = CP / 16, NJB = kDvTile / 16, PVB = NBR * NJB / NW;   // dV blocks per wave
+  static_assert(NBR * NJB % NW == 0 && NW % NJB == 0, "every wave owns the same dV blocks of one column block");
+};
+
+// One Dv slice of dO (chunk rows) and dH_{n+1} (key rows) in flight: loads from clamped
+// in-bounds addresses, validity kept beside them and applied when the slice goes to LDS.
+template <typename T, int DKP, int CP>
+struct DvSlice {
   using Cf = BwdDvCfg<T, DKP, CP>;
-  constexpr int V = Cf::V, LDC = Cf::LDC, LDV = Cf::LDV;
-  constexpr int NBR = CP / 16;
+  typedef typename V16<T>::type VT;
+  VT o[Cf::PO], h[Cf::PH];
+  bool ook[Cf::PO];
+  __device__ __forceinline__ void load(const T* dog, const T* dhs, int len, int Dv, int DVP, int js, int tid) {
+#pragma unroll
+    for (int m = 0; m < Cf::PO; ++m) {
+      const int idx = tid + Cf::NT * m, r = idx / Cf::PER_ROW, c = (idx % Cf::PER_ROW) * Cf::V;
+      const int jj = js * kDvTile + c;
+      ook[m] = idx < Cf::NO && r < len && jj < Dv;
+      o[m] = *reinterpret_cast<const VT*>(dog + (size_t)min(r, len - 1) * Dv + min(jj, Dv - Cf::V));
+    }
+#pragma unroll
+    for (int m = 0; m < Cf::PH; ++m) {
+      const int idx = min(tid + Cf::NT * m, Cf::NH - 1), r = idx / Cf::PER_ROW, c = (idx % Cf::PER_ROW) * Cf::V;
+      h[m] = *reinterpret_cast<const VT*>(dhs + (size_t)r * DVP + js * kDvTile + c);
+    }
+  }
+  __device__ __forceinline__ void store(T* sdO, T* sdH, int tid) const {
+#pragma unroll
+    for (int m = 0; m < Cf::PO; ++m) {
+      const int idx = tid + Cf::NT * m, r = idx / Cf::PER_ROW, c = (idx % Cf::PER_ROW) * Cf::V;
+      if (Cf::NO % Cf::NT == 0 || idx < Cf::NO) *reinterpret_cast<VT*>(sdO + r * Cf::LDV + c) = ook[m] ? o[m] : zero_vec<T>();
+    }
+#pragma unroll
+    for (int m = 0; m < Cf::PH; ++m) {
+      const int idx = tid + Cf::NT * m, r = idx / Cf::PER_ROW, c = (idx % Cf::PER_ROW) * Cf::V;
+      if (Cf::NH % Cf::NT == 0 || idx < Cf::NH) *reinterpret_cast<VT*>(sdH + r * Cf::LDV + c) = h[m];
+    }
+  }
+};
+
+// grid N * BH: chunk n = blockIdx.x % N of sequence bh = blockIdx.x / N
+template <typename T, int DKP, int CP>
+__global__ __launch_bounds__(kDvThreads) void gla_bwd_dv(BwdParams p, int ntile) {
+  using Cf = BwdDvCfg<T, DKP, CP>;
+  constexpr int NT = Cf::NT, NW = Cf::NW, V = Cf::V, LDC = Cf::LDC, LDV = Cf::LDV;
+  constexpr int NJB = Cf::NJB, PVB = Cf::PVB, PER_ROW = Cf::PER_ROW;
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
   T* sA = reinterpret_cast<T*>(smem);
   T* sKdT = reinterpret_cast<T*>(smem + Cf::AT);
   T* sdO = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT);
-  T* sdV = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT + Cf::VT);
-  T* sdH = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT + 2 * Cf::VT);
+  T* sdV = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT + Cf::OT);
+  T* sdH = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT + 2 * Cf::OT);
 
-  const int n = blockIdx.x, bh = blockIdx.y, js = blockIdx.z;
+  const int n = blockIdx.x % p.N, bh = blockIdx.x / p.N;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
-  const int Dv = p.Dv, L = p.L, N = p.N;
+  const int Dv = p.Dv, L = p.L;
   const int DVP = ntile * kDvTile;
   const int row0 = n * p.C, len = min(p.C, L - row0);
-  const size_t chunk = (size_t)bh * N + n;
-  tile_in_dense<T>(sA, reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP, CP, CP, LDC);
-  tile_in_dense<T>(sKdT, reinterpret_cast<const T*>(p.ops.KdT) + chunk * DKP * CP, DKP, CP, LDC);
-  const T* dhs = reinterpret_cast<const T*>(p.dHs) + chunk * DKP * DVP + js * kDvTile;
+  const size_t chunk = (size_t)bh * p.N + n;
+  const T* dhs = reinterpret_cast<const T*>(p.dHs) + chunk * DKP * DVP;
   const T* dog = reinterpret_cast<const T*>(p.do_) + ((size_t)bh * L + row0) * Dv;
-  constexpr int PER_ROW = kDvTile / V;
-  for (int idx = tid; idx < DKP * PER_ROW; idx += 256) {
-    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
-    *reinterpret_cast<VT*>(sdH + r * LDV + c) = *reinterpret_cast<const VT*>(dhs + (size_t)r * DVP + c);
-  }
-  for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
-    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
-    const int jj = js * kDvTile + c;
-    *reinterpret_cast<VT*>(sdO + r * LDV + c) =
-        (r < len && jj < Dv) ? *reinterpret_cast<const VT*>(dog + (size_t)r * Dv + jj) : zero_vec<T>();
-  }
-  __syncthreads();
-#pragma unroll
-  for (int cb = 0; cb < NBR; ++cb) {
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int kr = 0; kr < CP / 32; ++kr)
-      mma(acc, ld8_colblk(sA + (32 * kr) * LDC + 16 * cb, LDC),
-          ld8_colblk(sdO + (32 * kr) * LDV + 16 * wave, LDV));
-#pragma unroll
-    for (int ki = 0; ki < DKP / 32; ++ki)
-      mma(acc, ld8_colblk(sKdT + (32 * ki) * LDC + 16 * cb, LDC),
-          ld8_colblk(sdH + (32 * ki) * LDV + 16 * wave, LDV));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sdV[(16 * cb + 4 * grp + e) * LDV + 16 * wave + col] = from_f32<T>(acc[e]);
-  }
-  __syncthreads();
   T* dvg = reinterpret_cast<T*>(p.dv) + ((size_t)bh * L + row0) * Dv;
-  for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
-    const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
-    const int jj = js * kDvTile + c;
-    if (r < len && jj < Dv)
-      *reinterpret_cast<VT*>(dvg + (size_t)r * Dv + jj) = *reinterpret_cast<const VT*>(sdV + r * LDV + c);
+
+  // the chunk's A and KdT tiles and the first slice, all in flight together
+  const T* Ag = reinterpret_cast<const T*>(p.ops.A) + chunk * CP * CP;
+  const T* Kg = reinterpret_cast<const T*>(p.ops.KdT) + chunk * DKP * CP;
+  VT av[Cf::PA], kv[Cf::PK];
+#pragma unroll
+  for (int m = 0; m < Cf::PA; ++m) av[m] = *reinterpret_cast<const VT*>(Ag + (size_t)min(tid + NT * m, Cf::NA - 1) * V);
+#pragma unroll
+  for (int m = 0; m < Cf::PK; ++m) kv[m] = *reinterpret_cast<const VT*>(Kg + (size_t)min(tid + NT * m, Cf::NK - 1) * V);
+  DvSlice<T, DKP, CP> st;
+  st.load(dog, dhs, len, Dv, DVP, 0, tid);
+#pragma unroll
+  for (int m = 0; m < Cf::PA; ++m) {
+    const int idx = tid + NT * m, r = idx / (CP / V), c = (idx % (CP / V)) * V;
+    if (Cf::NA % NT == 0 || idx < Cf::NA) *reinterpret_cast<VT*>(sA + r * LDC + c) = av[m];
+  }
+#pragma unroll
+  for (int m = 0; m < Cf::PK; ++m) {
+    const int idx = tid + NT * m, r = idx / (CP / V), c = (idx % (CP / V)) * V;
+    if (Cf::NK % NT == 0 || idx < Cf::NK) *reinterpret_cast<VT*>(sKdT + r * LDC + c) = kv[m];
+  }
+  st.store(sdO, sdH, tid);
+  __syncthreads();
+
+  // wave w owns column block jb = w % NJB of the slice and row blocks cb0 + (NW / NJB) s
+  const int jb = wave % NJB, cb0 = wave / NJB;
+  for (int js = 0; js < ntile; ++js) {
+    st.load(dog, dhs, len, Dv, DVP, min(js + 1, ntile - 1), tid);   // last: harmless reload
+    f32x4 acc[PVB];
+#pragma unroll
+    for (int s = 0; s < PVB; ++s) acc[s] = zero4();
+#pragma unroll
+    for (int kr = 0; kr < CP / 32; ++kr) {            // A^T dO
+      const Frag<T> fo = ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV, lane);
+#pragma unroll
+      for (int s = 0; s < PVB; ++s)
+        mma(acc[s], fo, ld8_colblk(sA + (32 * kr) * LDC + 16 * (cb0 + (NW / NJB) * s), LDC, lane));
+    }
+#pragma unroll
+    for (int ki = 0; ki < DKP / 32; ++ki) {           // Kd dH
+      const Frag<T> fd = ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV, lane);
+#pragma unroll
+      for (int s = 0; s < PVB; ++s)
+        mma(acc[s], fd, ld8_colblk(sKdT + (32 * ki) * LDC + 16 * (cb0 + (NW / NJB) * s), LDC, lane));
+    }
+#pragma unroll
+    for (int s = 0; s < PVB; ++s) {
+      // transposed block: this lane holds dV[16 cb + col][16 jb + 4 grp + e]
+      const int cb = cb0 + (NW / NJB) * s;
+      typename Vec4<T>::type dv4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dv4[e] = from_f32<T>(acc[s][e]);
+      *reinterpret_cast<typename Vec4<T>::type*>(sdV + (16 * cb + col) * LDV + 16 * jb + 4 * grp) = dv4;
+    }
+    __syncthreads();
+    // the next slice's loads are the youngest memory operations: wait for them, stage them,
+    // and send this slice's dv out of the staging tile
+    __builtin_amdgcn_s_waitcnt(0);
+    st.store(sdO, sdH, tid);
+#pragma unroll
+    for (int m = 0; m < Cf::PO; ++m) {
+      const int idx = tid + NT * m, r = idx / PER_ROW, c = (idx % PER_ROW) * V;
+      const int jj = js * kDvTile + c;
+      if ((Cf::NO % NT == 0 || idx < Cf::NO) && r < len && jj < Dv)
+        *reinterpret_cast<VT*>(dvg + (size_t)r * Dv + jj) = *reinterpret_cast<const VT*>(sdV + r * LDV + c);
+    }
+    __syncthreads();
   }
 }
 
@@ -786,7 +899,7 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     record_event(p.events, ev++, s);
     if constexpr (!P::FUSED) {
-      hipLaunchKernelGGL((gla_bwd_dv<T, DKP, CP>), dim3(p.N, p.BH, ntile), dim3(256), 0, s, p, ntile);
+      hipLaunchKernelGGL((gla_bwd_dv<T, DKP, CP>), dim3(p.N * p.BH), dim3(kDvThreads), 0, s, p, ntile);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       record_event(p.events, ev++, s);
     }

@@ -336,17 +336,19 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
   cs.load(gg, gg, gg, m, m, len);
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
   // P (fp32: the softmax's Jacobian keeps sum_s dZ = 0; Z for the element-wise read-outs) and
-  // dP, from clamped rows, in flight while the gates are scanned
-  f32x4 pl[RPS][V / 4];
-  VT dl[RPS];
+  // dP (fp32: dP - <dP, P> cancels when the slot memories are alike, so dP is not rounded to
+  // the input type first), from clamped rows, in flight while the gates are scanned
+  f32x4 pl[RPS][V / 4], dl[RPS][V / 4];
   {
     const int cc = (cs.active && c0 < m) ? c0 : 0;
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
       const size_t off = gbase + (size_t)min(r0 + u, len - 1) * m + cc;
 #pragma unroll
-      for (int e4 = 0; e4 < V / 4; ++e4) pl[u][e4] = *reinterpret_cast<const f32x4*>(p.Pf + off + 4 * e4);
-      dl[u] = *reinterpret_cast<const VT*>(reinterpret_cast<const T*>(p.dP) + off);
+      for (int e4 = 0; e4 < V / 4; ++e4) {
+        pl[u][e4] = *reinterpret_cast<const f32x4*>(p.Pf + off + 4 * e4);
+        dl[u][e4] = *reinterpret_cast<const f32x4*>(p.dP + off + 4 * e4);
+      }
     }
   }
   cs.finish(segtot, sGam, red);
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         pv[u][e] = ok ? pl[u][e >> 2][e & 3] : 0.f;
-        dpv[u][e] = ok ? to_f32(dl[u][e]) : 0.f;
+        dpv[u][e] = ok ? dl[u][e >> 2][e & 3] : 0.f;
         s += pv[u][e] * dpv[u][e];
       }
       rpart[cs.cg * CP + r] = s;
@@ -861,6 +863,7 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
     BwdParams b;
     b.q = p.P; b.k = p.W; b.v = p.v; b.g = p.g; b.do_ = p.do_; b.h0 = p.hv0; b.dht = p.dhvt;
     b.dq = p.dP; b.dk = p.dW2; b.dv = p.dv; b.dg = p.dg2; b.dh0 = p.dhv0;
+    b.dq32 = p.dP;     // dP stays fp32 for the read-out's backward
     b.BH = p.BH; b.L = p.L; b.Dk = p.m; b.Dv = p.Dv; b.C = p.C; b.N = p.N;
     b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.saved = p.saved != 0; b.events = LaunchEvents{nullptr, 0};
     if ((e = launch_gla_bwd<T, MP, CP>(b, s)) != hipSuccess) return e;

@@ -95,6 +95,9 @@ struct BwdParams {
   void* dHs;      // [BH][N][DKP][DvP] state gradient at chunk ends (T)
   bool saved;     // ops (with QsT) and Hs were left by a forward: skip recomputing them
   LaunchEvents events;
+  // if set, dq goes here in fp32 [BH][L][Dk] instead of to dq: GSA's pass 2, whose dq is the
+  // gradient of the read-out, which the softmax's Jacobian then reduces with cancellation
+  float* dq32 = nullptr;
 };
 
 // Gated slot attention: pass 1 runs on its own kernels, pass 2 on the GLA kernels.
@@ -114,7 +117,7 @@ struct GsaParams {
   void* P;        // [BH][L][m] slot softmax              (queries of pass 2) (T)
   float* Pf;      // [BH][L][m] fp32, backward only: the softmax P (its Jacobian needs P) or,
                   // for the element-wise read-outs, the scores Z (their derivative needs Z)
-  void* dP;       // [BH][L][m] gradient of P (backward)                       (T)
+  float* dP;      // [BH][L][m] gradient of P (backward), fp32
   void* dW2;      // [BH][L][m] pass-2 gradient of W (backward)                (T)
   float* dg2;     // [BH][L][m] pass-2 decay gradient (backward)
   float* dZ;      // [BH][L][m] gradient of the softmax input (backward)
