@@ -26,7 +26,9 @@
  *     Internal accumulation is float32; bf16 operands feed bf16 matrix cores.
  *   - Ownership: the caller owns every buffer.  The library never allocates device memory;
  *     scratch space is the caller's `workspace` of at least the size the matching
- *     *_workspace_bytes() query returns (its contents on entry do not matter).
+ *     *_workspace_bytes() query returns (its contents on entry do not matter).  The one
+ *     exception is gla_fwd_noalloc, whose scratch is a fixed 64 MiB array of the library's own
+ *     device memory (one per device, created with the library's code object).
  *   - Synchrony: arguments are validated on the host before anything is enqueued.  On any
  *     error the call returns a non-zero gla_status and enqueues nothing, so no output is
  *     touched.  On success all work is enqueued on `stream` (a hipStream_t, NULL = the null
@@ -46,9 +48,10 @@
  *   - Results are deterministic: no floating-point atomics are used, so two runs on the same
  *     inputs give bitwise-identical outputs.
  *   - The library is reentrant.  Its only global state, kept per device it has run on and
- *     read once, is the compute-unit count (it picks the state walks' tile height) and how
- *     many chunk-gradient workgroups the device runs at once (the size of that kernel's
- *     persistent grid).
+ *     read once, is the compute-unit count (it picks the state walks' tile height), how many
+ *     chunk-gradient workgroups the device runs at once (the size of that kernel's persistent
+ *     grid) and the address of gla_fwd_noalloc's scratch array (whose contents calls of that
+ *     entry point share).
  */
 #ifndef GLA_AMD_GLA_H
 #define GLA_AMD_GLA_H
@@ -67,7 +70,8 @@ typedef enum {
   GLA_ERR_UNSUPPORTED = 4, /* C, Dk, Dv or m outside the supported set                */
   GLA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the query returned       */
   GLA_ERR_ALIAS = 6,       /* an output overlaps an input or another output           */
-  GLA_ERR_HIP = 7          /* a HIP launch failed                                     */
+  GLA_ERR_HIP = 7,         /* a HIP launch failed                                     */
+  GLA_ERR_SCRATCH = 8      /* gla_fwd_noalloc: the sizes need more than its fixed scratch */
 } gla_status;
 
 typedef enum { GLA_F32 = 0, GLA_BF16 = 1 } gla_dtype;
@@ -105,6 +109,23 @@ int gla_fwd(const void* q, const void* k, const void* v, const void* g, const fl
             void* o, float* ht,
             int B, int H, int L, int Dk, int Dv, int C, int dtype,
             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- GLA forward, no allocation
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): gla_fwd with the same arguments, results and errors,
+ * minus the workspace.  Its scratch is a fixed buffer of gla_fwd_noalloc_max_workspace_bytes()
+ * = 64 MiB in the library's own device memory, one per device the library runs on, held until
+ * the process ends.  Sizes whose gla_fwd_workspace_bytes() exceeds it return GLA_ERR_SCRATCH
+ * before anything is enqueued.  The call never allocates or frees device memory.
+ *   - Every call on one device shares that device's buffer and leaves its contents behind;
+ *     nothing in it needs clearing between calls.  Calls that overlap on one device (other
+ *     streams, other host threads) race on it: order them, e.g. on one stream.
+ *   - The first call on a device looks the buffer's address up (hipGetSymbolAddress, no
+ *     allocation); make that first call outside graph capture. */
+size_t gla_fwd_noalloc_max_workspace_bytes(void);
+int gla_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                    void* o, float* ht,
+                    int B, int H, int L, int Dk, int Dv, int C, int dtype, void* stream);
 
 /* ---------------------------------------------------------------- GLA backward ---------
  * Gradients of sum(o * do_) + sum(ht * dht).  gla_bwd recomputes what it needs from the

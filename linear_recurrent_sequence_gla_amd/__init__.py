@@ -6,6 +6,8 @@ or PyTorch fallback: if the library is missing or cannot be loaded every call ra
 
 Entry points (same names as the C ABI):
     gla_fwd(q, k, v, g, C=64, h0=None, output_final_state=True) -> (o, ht)
+    gla_fwd_noalloc(q, k, v, g, C=64, h0=None, output_final_state=True) -> (o, ht)
+        (gla_fwd on the library's fixed scratch buffer; no workspace allocation)
     gla_bwd(q, k, v, g, do, C=64, h0=None, dht=None, want_dh0=False) -> (dq, dk, dv, dg, dh0)
     gla_fwd_save(q, k, v, g, C=64, h0=None, output_final_state=True) -> (o, ht, saved)
     gla_bwd_saved(q, k, v, g, do, saved, C=64, h0=None, dht=None, want_dh0=False)
@@ -30,7 +32,7 @@ from typing import Optional
 import torch  # imported first so the library binds to the HIP runtime torch already loaded
 
 __all__ = [
-    "lib", "lib_path", "GlaError", "gla_fwd", "gla_bwd", "gla_fwd_save", "gla_bwd_saved", "gla_decode_step",
+    "lib", "lib_path", "GlaError", "gla_fwd", "gla_fwd_noalloc", "gla_bwd", "gla_fwd_save", "gla_bwd_saved", "gla_decode_step",
     "gsa_fwd", "gsa_bwd", "gsa_decode_step", "gla_saved_bytes", "gla_bwd_saved_workspace_bytes",
     "gla_fwd_workspace_bytes", "gla_bwd_workspace_bytes", "gsa_fwd_workspace_bytes",
     "gsa_bwd_workspace_bytes", "EXPORTED_SYMBOLS", "GSA_ACTS", "msgla_fwd", "msgla_fwd_workspace_bytes",
@@ -63,6 +65,8 @@ _SIGS = {
     "gla_fwd": (_I, [_P] * 7 + [_I] * 7 + [_P, _Z, _P]),
     "gla_bwd_workspace_bytes": (_Z, [_I] * 7),
     "gla_bwd": (_I, [_P] * 12 + [_I] * 7 + [_P, _Z, _P]),
+    "gla_fwd_noalloc_max_workspace_bytes": (_Z, []),
+    "gla_fwd_noalloc": (_I, [_P] * 7 + [_I] * 7 + [_P]),
     "gla_fwd_profiled": (_I, [_P] * 7 + [_I] * 7 + [_P, _Z, _P, _P, _I]),
     "gla_bwd_profiled": (_I, [_P] * 12 + [_I] * 7 + [_P, _Z, _P, _P, _I]),
     "gla_bwd_launch_count": (_I, [_I] * 7),
@@ -207,6 +211,25 @@ def gla_fwd(q, k, v, g, C: int = 64, h0=None, output_final_state: bool = True, *
     ws = _workspace(nbytes, dev, workspace)
     _check(L_.gla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(o), _ptr(ht),
                       B, H, L, Dk, Dv, C, _DT[dt], _ptr(ws), ws.numel(), _stream(dev)))
+    return o, ht
+
+
+def gla_fwd_noalloc(q, k, v, g, C: int = 64, h0=None, output_final_state: bool = True, *,
+                    out=None, ht_out=None):
+    """gla_fwd whose scratch is the library's fixed per-device buffer: no workspace is
+    allocated by the library (pass out / ht_out to allocate nothing here either).  Sizes whose
+    forward workspace exceeds gla_fwd_noalloc_max_workspace_bytes() raise (GLA_ERR_SCRATCH)."""
+    B, H, L, Dk, Dv, dev, dt = _common(q, k, v, g)
+    if h0 is not None:
+        _need(h0, "h0", (B, H, Dk, Dv), torch.float32, dev)
+    o = out if out is not None else torch.empty((B, H, L, Dv), dtype=dt, device=dev)
+    _need(o, "out", (B, H, L, Dv), dt, dev)
+    ht = None
+    if output_final_state:
+        ht = ht_out if ht_out is not None else torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+        _need(ht, "ht_out", (B, H, Dk, Dv), torch.float32, dev)
+    _check(lib().gla_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(h0), _ptr(o), _ptr(ht),
+                                 B, H, L, Dk, Dv, C, _DT[dt], _stream(dev)))
     return o, ht
 
 

@@ -5,7 +5,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/gla.h"
 #include "common.hpp"
@@ -216,6 +218,9 @@ const char* gla_status_str(int s) {
     case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE: workspace NULL or smaller than the query returned";
     case GLA_ERR_ALIAS: return "GLA_ERR_ALIAS: an output overlaps an input, another output or the workspace";
     case GLA_ERR_HIP: return "GLA_ERR_HIP: a HIP kernel launch failed";
+    case GLA_ERR_SCRATCH:
+      return "GLA_ERR_SCRATCH: these sizes need more scratch memory than gla_fwd_noalloc's fixed "
+             "per-device buffer holds (64 MiB; gla_fwd_workspace_bytes gives the need)";
     default: return "unknown status";
   }
 }
@@ -363,6 +368,40 @@ int bwd_saved_impl(const void* q, const void* k, const void* v, const void* g, c
   return GLA_OK;
 }
 
+// ---------------------------------------------------------------- no-allocation forward
+// gla_fwd_noalloc's scratch: the forward workspace (chunk operands, chunk-start states and the
+// segmented walk's carries) lives in this fixed array of the library's own device memory
+// instead of a caller buffer.  Each device the library runs on holds its own copy until the
+// process ends.  Host code never passes the array's name to a kernel: the name is a host-side
+// stand-in, and the device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch, or null if it cannot be had.  The first call
+// on a device looks it up with that device current; later calls read the cached address.
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -380,6 +419,20 @@ int gla_fwd_profiled(const void* q, const void* k, const void* v, const void* g,
   if (!events || nevents < GLA_FWD_LAUNCHES + 1) return GLA_ERR_NULL_ARG;
   return fwd_impl(q, k, v, g, h0, o, ht, B, H, L, Dk, Dv, C, dtype, workspace, workspace_bytes, stream,
                   LaunchEvents{events, nevents});
+}
+
+size_t gla_fwd_noalloc_max_workspace_bytes(void) { return kNoAllocScratchBytes; }
+
+int gla_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const float* h0,
+                    void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype,
+                    void* stream) {
+  const int st = check_dims(B, H, L, Dk, Dv, C, dtype);
+  if (st != GLA_OK) return st;
+  if (fwd_ws_bytes(B, H, L, Dk, Dv, C, dtype) > kNoAllocScratchBytes) return GLA_ERR_SCRATCH;
+  void* ws = noalloc_scratch();
+  if (!ws) return GLA_ERR_HIP;
+  return fwd_impl(q, k, v, g, h0, o, ht, B, H, L, Dk, Dv, C, dtype, ws, kNoAllocScratchBytes, stream,
+                  LaunchEvents{nullptr, 0});
 }
 
 int gla_bwd(const void* q, const void* k, const void* v, const void* g, const float* h0,

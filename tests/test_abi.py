@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.gla_abi_version() >= 1
-    for code in range(8):
+    for code in range(9):
         s = lib.gla_status_str(code).decode()
         assert s.startswith("GLA_"), s
     assert lib.gla_status_str(99).decode() == "unknown status"
@@ -238,3 +238,16 @@ def test_msgla_validation(lib):
     assert lib.msgla_fwd(*N, 1, 4, 64, 64, 64, 64, 1, 1, None, I(4), None, 0, None) == 1
     assert lib.msgla_fwd_workspace_bytes(1, 4, 64, 64, 64, 64, 1, 2, I(1, 2), I(2, 1)) == 0
     assert lib.msgla_fwd_workspace_bytes(1, 4, 64, 64, 64, 64, 1, 2, I(1, 2), I(2, 2)) > 0
+
+
+def test_noalloc_validation(lib):
+    """gla_fwd_noalloc validates like gla_fwd and refuses sizes beyond its fixed scratch before
+    touching the device."""
+    assert lib.gla_fwd_noalloc_max_workspace_bytes() == 64 << 20
+    assert lib.gla_fwd_noalloc(*NOP, 1, 1, 64, 16, 16, 16, 5, None) == 3          # GLA_ERR_DTYPE
+    assert lib.gla_fwd_noalloc(*NOP, 1, 1, 0, 16, 16, 16, 1, None) == 2           # GLA_ERR_SHAPE
+    assert lib.gla_fwd_noalloc(*NOP, 1, 1, 64, 16, 16, 48, 1, None) == 4          # GLA_ERR_UNSUPPORTED
+    # the 340M-layer batch needs a ~110 MB forward workspace
+    assert lib.gla_fwd_workspace_bytes(8, 4, 2048, 128, 256, 64, 1) > (64 << 20)
+    assert lib.gla_fwd_noalloc(*NOP, 8, 4, 2048, 128, 256, 64, 1, None) == 8      # GLA_ERR_SCRATCH
+    assert lib.gla_status_str(8).decode().startswith("GLA_ERR_SCRATCH")
