@@ -2,7 +2,7 @@
 """Benchmark of the chunkwise GLA operator on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extras]
-    python bench.py --only {gla_1p3b,decode,gsa_decode,gsa,msgla,long_fwd} [--steps K] [--warmup W]
+    python bench.py --only {gla_1p3b,decode,gsa_decode,gsa,gsa_m128,msgla,long_fwd} [--steps K] [--warmup W]
         (one extra workload alone)
 
 One step is one pass of the training hot path over one batch of the 340M-layer workload
@@ -405,9 +405,11 @@ def _timed_steps(torch, fn, steps, warmup):
     return s.elapsed_time(e) / steps, [a.elapsed_time(b) for a, b in evs]
 
 
-def run_gsa(torch, m, steps=10, warmup=3, name="gsa_340m"):
+def run_gsa(torch, m, steps=10, warmup=3, name="gsa_340m", read_outs=None):
     """GSA fwd+bwd at its workload: gsa_fwd_save then gsa_bwd_saved (the training-step form, as
-    for GLA), with the recomputing gsa_fwd + gsa_bwd timed beside it."""
+    for GLA), with the recomputing gsa_fwd + gsa_bwd timed beside it, and (read_outs, by
+    default for the 64-slot workload only) the same step with each element-wise read-out."""
+    read_outs = (name == "gsa_340m") if read_outs is None else read_outs
     w = W.WORKLOADS[name]
     lib = m.lib()
     if lib.gsa_fwd_workspace_bytes(w.B, w.H, w.L, w.Dk, w.Dv, w.m, w.C, 1) == 0:
@@ -436,7 +438,7 @@ def run_gsa(torch, m, steps=10, warmup=3, name="gsa_340m"):
     ms_re, _ = _timed_steps(torch, recompute_step, steps, warmup)
     # the element-wise read-outs in place of the softmax (same saved-path step)
     acts = {a: round(_timed_steps(torch, lambda a=a: saved_step(a), steps, warmup)[0], 4)
-            for a in m.GSA_ACTS if a != "softmax"}
+            for a in m.GSA_ACTS if a != "softmax" and read_outs}
     alg = gsa_algorithmic(w.B, w.H, w.L, w.Dk, w.Dv, w.m, w.C)
     tflops = (alg["flops_fwd"] + alg["flops_bwd"]) / (ms * 1e-3) / 1e12
     nbytes = alg["bytes_fwd"] + alg["bytes_bwd"]
@@ -449,7 +451,7 @@ def run_gsa(torch, m, steps=10, warmup=3, name="gsa_340m"):
             "roofline_step": {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 2),
                               "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                               "frac": round(nbytes / (ms * 1e-3) / PEAK_HBM_BYTES, 4), "alg_bytes": nbytes},
-            "recomputing_ms_per_step": round(ms_re, 4), "read_out_ms_per_step": acts}
+            "recomputing_ms_per_step": round(ms_re, 4), **({"read_out_ms_per_step": acts} if acts else {})}
 
 
 def run_long_fwd(torch, m, steps=10, warmup=3):
@@ -669,7 +671,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-calib-mb", type=float, default=0.0,
                     help="also run one plain device copy of this many MB (counter calibration)")
-    ap.add_argument("--only", choices=["gla_1p3b", "decode", "gsa_decode", "gsa", "msgla", "long_fwd"],
+    ap.add_argument("--only", choices=["gla_1p3b", "decode", "gsa_decode", "gsa", "gsa_m128", "msgla", "long_fwd"],
                     help="run one extra workload alone and print its line (for profiling)")
     ap.add_argument("--summarize-stats")
     ap.add_argument("--summarize-pmc", nargs="+")
@@ -719,6 +721,7 @@ def main():
         fns = {"decode": lambda: run_decode(torch, m), "gsa_decode": lambda: run_gsa_decode(torch, m),
                "long_fwd": lambda: run_long_fwd(torch, m, args.steps, args.warmup),
                "gsa": lambda: run_gsa(torch, m, args.steps, args.warmup),
+               "gsa_m128": lambda: run_gsa(torch, m, args.steps, args.warmup, name="gsa_340m_m128"),
                "msgla": lambda: run_msgla(torch, m, args.steps, args.warmup),
                "gla_1p3b": lambda: c3_line(torch, m, args.steps, args.warmup)}
         print(json.dumps({args.only: fns[args.only]()}), flush=True)
@@ -764,6 +767,9 @@ def main():
         g = run_gsa(torch, m)
         if g is not None:
             ex["gsa"] = g
+        g = run_gsa(torch, m, name="gsa_340m_m128")
+        if g is not None:
+            ex["gsa_m128"] = g
         ex["msgla"] = run_msgla(torch, m)
         out["extras"] = ex
     if not args.no_cpu_baseline:

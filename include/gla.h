@@ -211,8 +211,11 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g,
                     int B, int H, int Dk, int Dv, int dtype, void* stream);
 
 /* ---------------------------------------------------------------- GSA forward ----------
- * Supported: C in {16, 32, 64}; m a multiple of 16 up to 64; Dk a multiple of 16 up to 256;
- * Dv a multiple of 16 up to 512 (others: GLA_ERR_UNSUPPORTED).  act: a gsa_act value.
+ * Supported: C in {16, 32, 64}; m a multiple of 16 up to 128; Dk a multiple of 16 up to 256;
+ * Dv a multiple of 16 up to 512 (others: GLA_ERR_UNSUPPORTED).  The backward (gsa_bwd,
+ * gsa_fwd_save, gsa_bwd_saved) needs its pass-1 tiles in a CU's LDS: with m > 64 it takes
+ * C in {16, 32}, and float32 takes m <= 64 with C in {16, 32} (gsa_fwd takes the rest).
+ * act: a gsa_act value.
  *   q, k : [B,H,L,Dk] dtype;  v : [B,H,L,Dv] dtype;  g : [B,H,L,m] dtype slot log-gates
  *   hk0  : [B,H,Dk,m] float32 initial pass-1 state or NULL;  hv0 : [B,H,m,Dv] or NULL
  *   o    : [B,H,L,Dv] dtype

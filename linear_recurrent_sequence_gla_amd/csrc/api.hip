@@ -591,11 +591,11 @@ int check_gsa(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, bool
   if (dtype != GLA_F32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;
   if (B < 1 || H < 1 || L < 1 || Dk < 1 || Dv < 1 || m < 1 || C < 1) return GLA_ERR_SHAPE;
   if (C != 16 && C != 32 && C != 64) return GLA_ERR_UNSUPPORTED;
-  if (m % 16 != 0 || m > 64 || Dk % 16 != 0 || Dk > 256 || Dv % 16 != 0 || Dv > 512) return GLA_ERR_UNSUPPORTED;
+  if (m % 16 != 0 || m > 128 || Dk % 16 != 0 || Dk > 256 || Dv % 16 != 0 || Dv > 512) return GLA_ERR_UNSUPPORTED;
   if ((int64_t)B * H > 65535 || (int64_t)L * Dv > INT32_MAX / 2 || (int64_t)L * Dk > INT32_MAX / 2)
     return GLA_ERR_UNSUPPORTED;
   const int es = esize_of(dtype), MP = pad_dk(m), CP = pad_c(C);
-  if (!gsa_config_fits(es, MP, CP) || !fwd_config_fits(es, MP, CP)) return GLA_ERR_UNSUPPORTED;
+  if (!gsa_config_fits(es, MP, CP, bwd) || !fwd_config_fits(es, MP, CP)) return GLA_ERR_UNSUPPORTED;
   if (bwd && !bwd_config_fits(es, MP, CP)) return GLA_ERR_UNSUPPORTED;
   return GLA_OK;
 }
@@ -673,6 +673,8 @@ GsaParams gsa_params(const GsaLayout& lf, char* fb, bool saved, const GsaLayout&
     if (MP == 32 && CP == 64) return LAUNCH<TT, 32, 64>(__VA_ARGS__);                          \
     if (MP == 64 && CP == 32) return LAUNCH<TT, 64, 32>(__VA_ARGS__);                          \
     if (MP == 64 && CP == 64) return LAUNCH<TT, 64, 64>(__VA_ARGS__);                          \
+    if (MP == 128 && CP == 32) return LAUNCH<TT, 128, 32>(__VA_ARGS__);                        \
+    if (MP == 128 && CP == 64) return LAUNCH<TT, 128, 64>(__VA_ARGS__);                        \
   } while (0)
 
 hipError_t dispatch_gsa(bool bwd, int dtype, int MP, int CP, const GsaParams& p, hipStream_t s) {

@@ -820,15 +820,21 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
 }
 
 // ----------------------------------------------------------------------------- launchers
+// The forward needs the read-out kernel's LDS and the walks; the backward also the pass-1
+// backward kernel's, whose three fp32 [CP][MP] tiles and phase region rule out m > 64 at
+// C = 64 (about 237 KB at m = 128).
+template <typename T, int MP, int CP>
+constexpr bool gsa_fwd_fits() {
+  return GsaCfg<T, MP, CP>::P_BYTES <= kMaxLds && walk_fits<T, MP, CP>();
+}
 template <typename T, int MP, int CP>
 constexpr bool gsa_fits() {
-  return GsaCfg<T, MP, CP>::P_BYTES <= kMaxLds && GsaCfg<T, MP, CP>::B_BYTES <= kMaxLds &&
-         walk_fits<T, MP, CP>();
+  return gsa_fwd_fits<T, MP, CP>() && GsaCfg<T, MP, CP>::B_BYTES <= kMaxLds;
 }
 
 template <typename T, int MP, int CP>
 hipError_t launch_gsa_fwd(const GsaParams& p, hipStream_t s) {
-  if constexpr (!gsa_fits<T, MP, CP>()) {
+  if constexpr (!gsa_fwd_fits<T, MP, CP>()) {
     return hipErrorNotSupported;
   } else {
     hipError_t e;
@@ -877,12 +883,14 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
   }
 }
 
-bool gsa_config_fits(int esize, int MP, int CP) {
+bool gsa_config_fits(int esize, int MP, int CP, bool bwd) {
   bool ok = false;
 #define GSA_FIT(TT, M_, C_) \
-  if (esize == (int)sizeof(TT) && MP == M_ && CP == C_) ok = gsa_fits<TT, M_, C_>();
+  if (esize == (int)sizeof(TT) && MP == M_ && CP == C_) ok = bwd ? gsa_fits<TT, M_, C_>() : gsa_fwd_fits<TT, M_, C_>();
   GSA_FIT(bf16, 32, 32) GSA_FIT(bf16, 32, 64) GSA_FIT(bf16, 64, 32) GSA_FIT(bf16, 64, 64)
+  GSA_FIT(bf16, 128, 32) GSA_FIT(bf16, 128, 64)
   GSA_FIT(float, 32, 32) GSA_FIT(float, 32, 64) GSA_FIT(float, 64, 32) GSA_FIT(float, 64, 64)
+  GSA_FIT(float, 128, 32) GSA_FIT(float, 128, 64)
 #undef GSA_FIT
   return ok;
 }
@@ -891,6 +899,8 @@ bool gsa_config_fits(int esize, int MP, int CP) {
   template hipError_t launch_gsa_fwd<TT, M_, C_>(const GsaParams&, hipStream_t); \
   template hipError_t launch_gsa_bwd<TT, M_, C_>(const GsaParams&, hipStream_t);
 GSA_INST(bf16, 32, 32) GSA_INST(bf16, 32, 64) GSA_INST(bf16, 64, 32) GSA_INST(bf16, 64, 64)
+GSA_INST(bf16, 128, 32) GSA_INST(bf16, 128, 64)
 GSA_INST(float, 32, 32) GSA_INST(float, 32, 64) GSA_INST(float, 64, 32) GSA_INST(float, 64, 64)
+GSA_INST(float, 128, 32) GSA_INST(float, 128, 64)
 
 }  // namespace gla

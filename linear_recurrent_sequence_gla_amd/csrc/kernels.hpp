@@ -212,7 +212,7 @@ template <typename T, int MP, int CP>
 hipError_t launch_gsa_fwd(const GsaParams& p, hipStream_t s);
 template <typename T, int MP, int CP>
 hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s);
-bool gsa_config_fits(int esize, int MP, int CP);
+bool gsa_config_fits(int esize, int MP, int CP, bool bwd);   // bwd: the backward's kernels too
 
 // Kernel launches per call (for the profiled entry points).
 constexpr int GLA_FWD_LAUNCHES = 3;

@@ -543,19 +543,40 @@ __global__ __launch_bounds__(256) void seg_fixup_kernel(SegParams q) {
   }
 }
 
+// Tile height of a segmented walk.  The segments supply the parallelism, so the tile is the
+// tallest that fits: for the same number of resident workgroups the chunks then split into more
+// segments, each a shorter chain of sequential steps, and each chunk's source rows are fetched
+// by fewer workgroups.  64-row tiles run 8 waves, 32- and 16-row tiles 4; PER_CU is how many
+// workgroups a CU's LDS holds.
+template <typename T, int SP, int CP, int RT>
+struct SegTileCfg {
+  static constexpr int NW = RT == 64 ? 8 : 4;
+  static constexpr size_t BYTES = WalkIOCfg<T, RT, CP, 2, 64 * NW>::BYTES;
+  static constexpr bool OK = RT <= SP && SP % RT == 0 && BYTES <= kMaxLds;
+  static constexpr int PER_CU = OK ? (int)(kMaxLds / BYTES) : 0;
+};
+template <typename T, int SP, int CP>
+struct SegTile {
+  static constexpr int RT = SegTileCfg<T, SP, CP, 64>::OK ? 64 : SegTileCfg<T, SP, CP, 32>::OK ? 32 : 16;
+  using Cf = SegTileCfg<T, SP, CP, RT>;
+};
+
 // Segments of a sequence for a forward walk of BH sequences of N chunks, given room for up to
-// seg_max: enough to give the CUs about two 16-row workgroups each, at least 8 chunks per
-// segment; 1 (no split) when the plain walk already fills the device.
+// seg_max: split only when even the 16-row plain walk leaves CUs idle; then as many segments as
+// the resident workgroups of the segmented tile allow, at least 8 chunks each.  1 = no split.
 template <typename T, int SP, int CP>
 int walk_segments(int BH, int Ds, int N, int seg_max) {
   using P = WalkPlan<T, SP, CP>;
-  if constexpr (!P::NARROW) {
+  using S = typename SegTile<T, SP, CP>::Cf;
+  if constexpr (!P::NARROW || !S::OK) {
     return 1;
   } else {
     const int cus = device_cu_count();
-    const int grid16 = (Ds + kDvTile - 1) / kDvTile * (SP / 16) * BH;
+    const int ntile = (Ds + kDvTile - 1) / kDvTile;
+    const int grid16 = ntile * (SP / 16) * BH;
     if (cus <= 0 || seg_max < 2 || grid16 >= cus) return 1;
-    int ns = min(min(seg_max, kMaxSeg), max(1, 2 * cus / grid16));
+    const int grid = ntile * (SP / SegTile<T, SP, CP>::RT) * BH;    // one segment's workgroups
+    int ns = min(min(seg_max, kMaxSeg), max(1, S::PER_CU * cus / grid));
     ns = min(ns, N / 8);
     if (ns < 2) return 1;
     const int len = (N + ns - 1) / ns;
@@ -573,15 +594,16 @@ template <typename T, int SP, int CP>
 hipError_t launch_walk_store_segmented(WalkIO w, int BH, int nseg, float* seg_end, float* carry, float* prefix,
                                        float* total, bool fixup, hipStream_t s) {
   using P = WalkPlan<T, SP, CP>;
-  if constexpr (!P::NARROW) {
+  constexpr int RT = SegTile<T, SP, CP>::RT, NW = SegTile<T, SP, CP>::Cf::NW;
+  if constexpr (!P::NARROW || !SegTile<T, SP, CP>::Cf::OK) {
     return hipErrorNotSupported;
   } else {
     const int ntile = (w.Ds + kDvTile - 1) / kDvTile, DsP = ntile * kDvTile;
     w.nseg = nseg;
     w.seg_len = (w.N + nseg - 1) / nseg;
     w.seg_end = seg_end;
-    hipLaunchKernelGGL((walk_kernel<T, SP, 16, CP, 2, false, 4>), dim3(ntile * (SP / 16) * BH * nseg), dim3(256), 0,
-                       s, w, ntile);
+    hipLaunchKernelGGL((walk_kernel<T, SP, RT, CP, 2, false, NW>), dim3(ntile * (SP / RT) * BH * nseg), dim3(64 * NW),
+                       0, s, w, ntile);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SegParams q{w.gam, seg_end, carry, prefix, total, w.states, w.fin, w.N, nseg, w.seg_len, w.rows, w.Ds, DsP};

@@ -80,6 +80,55 @@ def test_small_shapes(gla, shape):
     check_gsa(gla, w, W.gsa_inputs(w), with_state=h0, with_dstate=dht)
 
 
+WIDE_SHAPES = [
+    # (B, H, L, Dk, Dv, m, C, dtype, h0, dht): more than 64 slots
+    (1, 2, 150, 64, 64, 128, 32, "bf16", True, True),
+    (2, 1, 77, 32, 48, 96, 16, "bf16", True, True),
+    (1, 1, 130, 128, 128, 80, 32, "bf16", False, True),
+    (1, 2, 200, 64, 96, 112, 32, "bf16", True, False),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_wide_slot_counts(gla, shape):
+    """Slot counts up to 128 (the GSA summary's ablation doubles m from 64 to 128), forward and
+    backward at the chunk sizes whose kernels hold them."""
+    B, H, L, Dk, Dv, m, C, dt, h0, dht = shape
+    w = W.GsaWorkload("wide", B, H, L, Dk, Dv, m, C, dt, 700 + L + m, h0=True)
+    check_gsa(gla, w, W.gsa_inputs(w), with_state=h0, with_dstate=dht)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 150, 64, 64, 128, 64, "bf16"), (1, 2, 100, 64, 96, 128, 64, "f32"),
+                                   (1, 1, 90, 48, 64, 64, 64, "f32")], ids=lambda s: "x".join(map(str, s)))
+def test_forward_only_shapes(gla, shape):
+    """Shapes whose forward fits but whose pass-1 backward does not (more than 64 slots at
+    C = 64; fp32 with 64 slots at C = 64): the forward matches the oracle, and the backward and
+    the saving forward are refused before anything runs."""
+    import torch
+    B, H, L, Dk, Dv, m, C, dt = shape
+    w = W.GsaWorkload("fwd-only", B, H, L, Dk, Dv, m, C, dt, 720 + L + m, h0=True)
+    x = W.gsa_inputs(w)
+    check_gsa(gla, w, x, backward=False)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    assert gla.gsa_bwd_workspace_bytes(B, H, L, Dk, Dv, m, C, tdt) == 0
+    assert gla.gsa_saved_bytes(B, H, L, Dk, Dv, m, C, tdt) == 0
+    args = [dev(x[n], dt) for n in ("q", "k", "v", "g")]
+    with pytest.raises(gla.GlaError):
+        gla.gsa_bwd(*args, dev(x["do"], dt), C=C)
+
+
+def test_full_size_m128_sampled(gla):
+    """The GSA layer with 128 slots (B=8, H=4, L=2048, Dk=Dv=128, C=32) through the saved path,
+    as the benchmark runs it, sampled units; and its forward at C = 64."""
+    w = W.WORKLOADS["gsa_340m_m128"]
+    x = W.gsa_inputs(w)
+    units = (np.array([1, 6])[:, None], np.array([2])[None, :])
+    check_gsa(gla, w, x, units=units, with_state=False, with_dstate=False, saved=True)
+    w64 = W.GsaWorkload("gsa_340m_m128_c64", 8, 4, 2048, 128, 128, 128, 64, "bf16", 1007)
+    check_gsa(gla, w64, x, units=(np.array([3])[:, None], np.array([0, 3])[None, :]), with_state=False,
+              backward=False)
+
+
 @pytest.mark.parametrize("gval", [-3.0, -30.0])
 def test_extreme_gates(gla, gval):
     """Strong forgetting on every other slot (normal gates on the rest): every chunk fails the

@@ -117,6 +117,9 @@ WORKLOADS = {
     "gla_long": GlaWorkload("gla_long", 1, 4, 20480, 128, 256, 64, "bf16", 1004, bias_frac=0.1),
     "decode": DecodeWorkload("decode", 1024, 64, 4, 128, 256, "bf16", 1004),
     "gsa_340m": GsaWorkload("gsa_340m", 8, 4, 2048, 128, 128, 64, 64, "bf16", 1005),
+    # the GSA layer with 128 slots (the GSA summary's slot-count ablation); chunk 32, the
+    # largest at which the backward's kernels fit 128 slots
+    "gsa_340m_m128": GsaWorkload("gsa_340m_m128", 8, 4, 2048, 128, 128, 128, 32, "bf16", 1007),
     # GSA recurrent inference at the GSA layer's dimensions with the decode batch
     "gsa_decode": GsaDecodeWorkload("gsa_decode", 1024, 64, 4, 128, 128, 64, "bf16", 1006),
 }
