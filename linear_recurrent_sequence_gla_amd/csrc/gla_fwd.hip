@@ -246,9 +246,11 @@ hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
     WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, p.ht, p.Dk, p.Dv, p.L, p.C, p.N, 0, p.in};
     // few, long sequences: the walk runs in segments and the output kernel adds each state's
     // carried part as it stages it (these states serve only that kernel)
-    const int nseg = p.seg_ws ? walk_segments<T, DKP, CP>(p.BH, p.Dv, p.N, p.seg_max) : 1;
+    const int nseg = p.seg_ws && !p.states_ready ? walk_segments<T, DKP, CP>(p.BH, p.Dv, p.N, p.seg_max) : 1;
     FwdParams po = p;
-    if (nseg >= 2) {
+    if (p.states_ready) {
+      // the caller's walk already left the chunk-start states (GSA's pass 2)
+    } else if (nseg >= 2) {
       const size_t part = (size_t)p.BH * p.seg_max * DKP * ((p.Dv + kDvTile - 1) / kDvTile * kDvTile);
       float* prefix = p.seg_ws + 2 * part;
       float* total = prefix + (size_t)p.BH * p.N * DKP;

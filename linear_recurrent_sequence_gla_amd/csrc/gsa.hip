@@ -13,7 +13,8 @@
 // Pass 2 is exactly GLA with queries p, keys w, values v and the same gates, so it runs on the
 // GLA kernels (gla_fwd.hip / gla_bwd.hip) with p and w materialised as [B,H,L,m] tensors.  Pass
 // 1 runs here.  Its transposed state S1^T [m x Dk] is row-gated (keys w, values k), so it
-// rides the generic state walks of walks.hpp.  In chunk form (b = chunk-local log2 prefix sum
+// rides the generic state walks of walks.hpp; pass 2's state walk has the same decayed keys
+// and decays, so the two forward walks run as one launch (launch_gsa_walks).  In chunk form (b = chunk-local log2 prefix sum
 // of g, E = 2^b, Ei = 2^-b, Eg = 2^{Gamma-b}, QK = mask(Q K^T) with c <= r):
 //   Z = E * (QK (W*Ei) + Q S1_n)                                    (then P = softmax(Z))
 //   dQK = mask((dZ*E)(W*Ei)^T),  dq = dQK K + (dZ*E) S1_n^T
@@ -483,9 +484,12 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
       for (int e = 0; e < V; ++e) {
         const float w = -expm1f(cs.qv[u][e]);
         const float dz = ok ? dzv[u][e >> 2][e & 3] : 0.f;
-        sB[r * LDF + c0 + e] = cs.b[u][e];
-        sW[r * LDF + c0 + e] = w;
-        sdZ[r * LDF + c0 + e] = dz;
+        // on the factorised path the tiles hold the decayed operands W Ei and dZ E, which every
+        // product there takes; the exact path reads the raw values
+        const float bb = cs.b[u][e];
+        sB[r * LDF + c0 + e] = bb;
+        sW[r * LDF + c0 + e] = fast ? w * fast_exp2(-bb) : w;
+        sdZ[r * LDF + c0 + e] = fast ? dz * fast_exp2(bb) : dz;
         dsum[u] += p.act == kActSoftmax ? -dz * (1.f - w) : dz * w;
       }
     }
@@ -511,7 +515,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 16 * rb + col, s = 32 * ks + 8 * grp + e;
-        dze[ks][e] = sdZ[r * LDF + s] * fast_exp2(sB[r * LDF + s]);
+        dze[ks][e] = fast ? sdZ[r * LDF + s] : sdZ[r * LDF + s] * fast_exp2(sB[r * LDF + s]);
       }
     }
   }
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
               const int s = 32 * ks + 8 * grp + e, c = 16 * cb + col;
-              xb[e] = sW[c * LDF + s] * fast_exp2(-sB[c * LDF + s]);
+              xb[e] = sW[c * LDF + s];                                   // W Ei
             }
             mma3(acc, hilo<T>(dze[ks]), hilo<T>(xb));
           }
@@ -577,7 +581,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int s = 32 * ks + 8 * grp + e, r = 16 * rb + col;
-        xw[e] = sW[r * LDF + s] * fast_exp2(sGam[s] - sB[r * LDF + s]);
+        xw[e] = fast ? sW[r * LDF + s] * fast_exp2(sGam[s]) : sW[r * LDF + s] * fast_exp2(sGam[s] - sB[r * LDF + s]);
       }
       fZ[ks] = frag_of<T>(dze[ks]);
       fG[ks] = frag_of<T>(xw);
@@ -715,9 +719,9 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
           for (int e = 0; e < 8; ++e) {
             const int kk = 32 * kc + 8 * grp + e, r = 16 * rb + col, s = 16 * sb + col;
             xa[e] = kk < r ? sQK[r * LDQK + kk] : 0.f;                      // QK' row r
-            xb[e] = sW[kk * LDF + s] * fast_exp2(-sB[kk * LDF + s]);       // (W Ei)[c][s]
+            xb[e] = sW[kk * LDF + s];                                       // (W Ei)[c][s]
             xt[e] = kk > r ? sQK[kk * LDQK + r] : 0.f;                      // QK'^T row c = r
-            xd[e] = sdZ[kk * LDF + s] * fast_exp2(sB[kk * LDF + s]);       // (dZ E)[r'][s]
+            xd[e] = sdZ[kk * LDF + s];                                      // (dZ E)[r'][s]
           }
           mma3(zi, hilo<T>(xa), hilo<T>(xb));
           mma3(w1, hilo<T>(xt), hilo<T>(xd));
@@ -727,10 +731,11 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + 4 * grp + e, s = 16 * sb + col;
         const float br = sB[r * LDF + s];
+        const float eb = fast_exp2(br), eib = fast_exp2(-br);
         float zip, dw1p;
         if (fast) {
-          zip = fast_exp2(br) * zi[e];
-          dw1p = fast_exp2(-br) * w1[e];
+          zip = eb * zi[e];
+          dw1p = eib * w1[e];
         } else {
           zip = 0.f;
           dw1p = 0.f;
@@ -738,9 +743,10 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
           for (int c = r + 1; c < CP; ++c)
             dw1p += sQK[c * LDQK + r] * sdZ[c * LDF + s] * fast_exp2(sB[c * LDF + s] - br);
         }
-        const float znd = zip + fast_exp2(br) * accZe[sh][e];
+        const float znd = zip + eb * accZe[sh][e];
         const float b1 = fast_exp2(sGam[s] - br) * accB1[sh][e];
-        const float dz = sdZ[r * LDF + s], w = sW[r * LDF + s];
+        const float dz = fast ? sdZ[r * LDF + s] * eib : sdZ[r * LDF + s];
+        const float w = fast ? sW[r * LDF + s] * eb : sW[r * LDF + s];
         sU[r * LDF + s] = dz * znd - w * dw1p;
         sY[r * LDF + s] = w * b1;
         sD[r * LDF + s] = dw1p + sQK[r * LDQK + r] * dz + b1;
@@ -832,6 +838,20 @@ constexpr bool gsa_fits() {
   return gsa_fwd_fits<T, MP, CP>() && GsaCfg<T, MP, CP>::B_BYTES <= kMaxLds;
 }
 
+// Both passes' state walks in one launch.  Pass 2's decayed keys are the pass-1 walk's matrix
+// WdT = (w 2^{Gamma-b})^T and its chunk decays are Gamma, so the two walks share the matrix and
+// differ only in their source (k for pass 1's transposed slot keys, v for pass 2's slot
+// values), their states and their end states.
+template <typename T, int MP, int CP>
+hipError_t launch_gsa_walks(const GsaParams& p, float* hkt, float* hvt, hipStream_t s) {
+  Batches<WalkIO> b{};
+  b.n = 2;
+  b.p[0] = WalkIO{p.WdT, p.k, p.Gam, p.S1s, p.hk0, hkt, p.m, p.Dk, p.L, p.C, p.N, 1};
+  b.p[1] = WalkIO{p.WdT, p.v, p.Gam, p.Hs2, p.hv0, hvt, p.m, p.Dv, p.L, p.C, p.N, 0};
+  const int BH[2] = {p.BH, p.BH};
+  return launch_walk_store_batches<T, MP, CP>(b, BH, s);
+}
+
 template <typename T, int MP, int CP>
 hipError_t launch_gsa_fwd(const GsaParams& p, hipStream_t s) {
   if constexpr (!gsa_fwd_fits<T, MP, CP>()) {
@@ -840,14 +860,14 @@ hipError_t launch_gsa_fwd(const GsaParams& p, hipStream_t s) {
     hipError_t e;
     hipLaunchKernelGGL((gsa_prep_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    WalkIO w1{p.WdT, p.k, p.Gam, p.S1s, p.hk0, p.hkt, p.m, p.Dk, p.L, p.C, p.N, 1};
-    if ((e = launch_walk_store<T, MP, CP>(w1, p.BH, s)) != hipSuccess) return e;
+    if ((e = launch_gsa_walks<T, MP, CP>(p, p.hkt, p.hvt, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // pass 2: its chunk operands and outputs on the states the walk above left
     FwdParams f;
     f.q = p.P; f.k = p.W; f.v = p.v; f.g = p.g; f.h0 = p.hv0; f.o = p.o; f.ht = p.hvt;
     f.BH = p.BH; f.L = p.L; f.Dk = p.m; f.Dv = p.Dv; f.C = p.C; f.N = p.N;
-    f.ops = p.ops2; f.Hs = p.Hs2; f.events = LaunchEvents{nullptr, 0};
+    f.ops = p.ops2; f.Hs = p.Hs2; f.states_ready = true; f.events = LaunchEvents{nullptr, 0};
     return launch_gla_fwd<T, MP, CP>(f, s);
   }
 }
@@ -858,20 +878,21 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
     return hipErrorNotSupported;
   } else {
     hipError_t e;
-    if (!p.saved) {   // recompute the forward's tensors
+    if (!p.saved) {   // recompute the forward's tensors, as the saving forward leaves them
       hipLaunchKernelGGL((gsa_prep_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      WalkIO w1{p.WdT, p.k, p.Gam, p.S1s, p.hk0, nullptr, p.m, p.Dk, p.L, p.C, p.N, 1};
-      if ((e = launch_walk_store<T, MP, CP>(w1, p.BH, s)) != hipSuccess) return e;
+      if ((e = launch_gsa_walks<T, MP, CP>(p, nullptr, nullptr, s)) != hipSuccess) return e;
       hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
+      PrepParams pp{p.P, p.W, p.g, p.ops2, p.L, p.m, p.C, p.N};
+      if ((e = launch_prep<T, MP, CP, true>(pp, p.BH, s)) != hipSuccess) return e;
     }
     BwdParams b;
     b.q = p.P; b.k = p.W; b.v = p.v; b.g = p.g; b.do_ = p.do_; b.h0 = p.hv0; b.dht = p.dhvt;
     b.dq = p.dP; b.dk = p.dW2; b.dv = p.dv; b.dg = p.dg2; b.dh0 = p.dhv0;
     b.dq32 = p.dP;     // dP stays fp32 for the read-out's backward
     b.BH = p.BH; b.L = p.L; b.Dk = p.m; b.Dv = p.Dv; b.C = p.C; b.N = p.N;
-    b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.saved = p.saved != 0; b.events = LaunchEvents{nullptr, 0};
+    b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.saved = true; b.events = LaunchEvents{nullptr, 0};
     if ((e = launch_gla_bwd<T, MP, CP>(b, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((gsa_dz_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;

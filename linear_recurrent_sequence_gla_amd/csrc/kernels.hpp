@@ -61,6 +61,7 @@ struct FwdParams {
   int BH, L, Dk, Dv, C, N;
   ChunkOps ops;   // ops.QsT != nullptr: the preparation also writes Qs^T (kept for a backward)
   void* Hs;       // [BH][N][DKP][DvP] chunk-start states (T), written by the state walk
+  bool states_ready = false;   // Hs (and ht) already hold the walk's result: no walk is run
   LaunchEvents events;
   SeqView in;     // input sequences read by the launch
   // optional scratch for a segmented state walk (walks.hpp), room for seg_max segments:

@@ -374,11 +374,12 @@ __global__ __launch_bounds__(64 * NW) void walk_kernel(WalkIO w, int ntile) {
   walk_tile<T, SP, RT, CP, G, REV, NW>(w, ntile, xcd_remap(blockIdx.x, gridDim.x));
 }
 
-// several batches in one launch (see Batches): batch i owns blocks first[i] .. first[i+1] - 1
+// several batches in one launch (see Batches): batch i owns blocks first[i] .. first[i+1] - 1;
+// each batch has its own source width Ds (so its own count of 64-column tiles)
 template <typename T, int SP, int RT, int CP, int G, bool REV, int NW>
-__global__ __launch_bounds__(64 * NW) void walk_batches(Batches<WalkIO> b, int ntile) {
+__global__ __launch_bounds__(64 * NW) void walk_batches(Batches<WalkIO> b) {
   const int gi = b.find(blockIdx.x);
-  walk_tile<T, SP, RT, CP, G, REV, NW>(b.p[gi], ntile, blockIdx.x - b.first[gi]);
+  walk_tile<T, SP, RT, CP, G, REV, NW>(b.p[gi], (b.p[gi].Ds + kDvTile - 1) / kDvTile, blockIdx.x - b.first[gi]);
 }
 
 template <typename T, int SP, int CP, bool REV>
@@ -416,11 +417,10 @@ hipError_t launch_walk_store_batches(Batches<WalkIO> b, const int* BH, hipStream
   if constexpr (!P::OK) {
     return hipErrorNotSupported;
   } else {
-    const int ntile = (b.p[0].Ds + kDvTile - 1) / kDvTile;
     b.first[0] = 0;
-    for (int i = 0; i < b.n; ++i) b.first[i + 1] = b.first[i] + ntile * (SP / P::RT) * BH[i];
-    hipLaunchKernelGGL((walk_batches<T, SP, P::RT, CP, P::G, false, 4>), dim3(b.first[b.n]), dim3(256), 0, s, b,
-                       ntile);
+    for (int i = 0; i < b.n; ++i)
+      b.first[i + 1] = b.first[i] + (b.p[i].Ds + kDvTile - 1) / kDvTile * (SP / P::RT) * BH[i];
+    hipLaunchKernelGGL((walk_batches<T, SP, P::RT, CP, P::G, false, 4>), dim3(b.first[b.n]), dim3(256), 0, s, b);
     return hipGetLastError();
   }
 }
