@@ -76,14 +76,13 @@ bool any_alias(const Range* outs, int nout, const Range* ins, int nin) {
 
 // Chunk-operand region of the workspace (shared by forward and backward).
 struct OpsLayout {
-  size_t qs, qst, kdt, a, gam, total;
+  size_t qs, kdt, a, gam, total;
 };
 
-OpsLayout ops_layout(size_t BH, size_t N, size_t CP, size_t DKP, size_t es, bool want_qst) {
+OpsLayout ops_layout(size_t BH, size_t N, size_t CP, size_t DKP, size_t es) {
   OpsLayout l{};
   size_t off = 0;
   l.qs = off;  off += align_up(BH * N * CP * DKP * es);
-  l.qst = off; if (want_qst) off += align_up(BH * N * CP * DKP * es);
   l.kdt = off; off += align_up(BH * N * CP * DKP * es);
   l.a = off;   off += align_up(BH * N * CP * CP * es);
   l.gam = off; off += align_up(BH * N * DKP * 4);
@@ -91,10 +90,9 @@ OpsLayout ops_layout(size_t BH, size_t N, size_t CP, size_t DKP, size_t es, bool
   return l;
 }
 
-ChunkOps carve_ops(char* ws, const OpsLayout& l, bool want_qst) {
+ChunkOps carve_ops(char* ws, const OpsLayout& l) {
   ChunkOps o;
   o.Qs = ws + l.qs;
-  o.QsT = want_qst ? ws + l.qst : nullptr;
   o.KdT = ws + l.kdt;
   o.A = ws + l.a;
   o.Gam = reinterpret_cast<float*>(ws + l.gam);
@@ -155,7 +153,7 @@ size_t fwd_seg_bytes(int B, int H, int L, int Dk, int Dv, int C) {
 size_t fwd_ws_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype, bool seg = true) {
   const size_t BH = (size_t)B * H, CP = pad_c(C), DKP = pad_dk(Dk), N = (L + C - 1) / C;
   const size_t es = esize_of(dtype);
-  return ops_layout(BH, N, CP, DKP, es, false).total + align_up(BH * N * DKP * pad_dv(Dv) * es) +
+  return ops_layout(BH, N, CP, DKP, es).total + align_up(BH * N * DKP * pad_dv(Dv) * es) +
          (seg ? fwd_seg_bytes(B, H, L, Dk, Dv, C) : 0);
 }
 
@@ -164,8 +162,8 @@ struct BwdLayout {
   size_t hs, dhs, total;
 };
 
-// What gla_fwd_save leaves for gla_bwd_saved: the chunk operands (with Qs^T) and the
-// chunk-start states.  The saved-state backward's own workspace holds only dH.
+// What gla_fwd_save leaves for gla_bwd_saved: the chunk operands and the chunk-start
+// states.  The saved-state backward's own workspace holds only dH.
 struct SavedLayout {
   OpsLayout ops;
   size_t hs, total;
@@ -175,7 +173,7 @@ SavedLayout saved_layout(int B, int H, int L, int Dk, int Dv, int C, int dtype) 
   const size_t BH = (size_t)B * H, CP = pad_c(C), DKP = pad_dk(Dk), N = (L + C - 1) / C;
   const size_t es = esize_of(dtype), DVP = pad_dv(Dv);
   SavedLayout l;
-  l.ops = ops_layout(BH, N, CP, DKP, es, true);
+  l.ops = ops_layout(BH, N, CP, DKP, es);
   l.hs = l.ops.total;
   l.total = l.hs + align_up(BH * N * DKP * DVP * es);
   return l;
@@ -190,7 +188,7 @@ BwdLayout bwd_layout(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
   const size_t BH = (size_t)B * H, CP = pad_c(C), DKP = pad_dk(Dk), N = (L + C - 1) / C;
   const size_t es = esize_of(dtype), DVP = pad_dv(Dv);
   BwdLayout l;
-  l.ops = ops_layout(BH, N, CP, DKP, es, true);
+  l.ops = ops_layout(BH, N, CP, DKP, es);
   size_t off = l.ops.total;
   l.hs = off;    off += align_up(BH * N * DKP * DVP * es);
   l.dhs = off;   off += align_up(BH * N * DKP * DVP * es);
@@ -259,8 +257,8 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* g, const f
   FwdParams p;
   p.q = q; p.k = k; p.v = v; p.g = g; p.h0 = h0; p.o = o; p.ht = ht;
   p.BH = (int)BH; p.L = L; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
-  const OpsLayout ol = ops_layout(BH, N, CP, DKP, es, false);
-  p.ops = carve_ops(static_cast<char*>(workspace), ol, false);
+  const OpsLayout ol = ops_layout(BH, N, CP, DKP, es);
+  p.ops = carve_ops(static_cast<char*>(workspace), ol);
   p.Hs = static_cast<char*>(workspace) + ol.total;
   if (fwd_seg_bytes(B, H, L, Dk, Dv, C) > 0) {
     p.seg_ws = reinterpret_cast<float*>(static_cast<char*>(p.Hs) + align_up(BH * N * DKP * pad_dv(Dv) * es));
@@ -291,7 +289,7 @@ int fwd_save_impl(const void* q, const void* k, const void* v, const void* g, co
   FwdParams p;
   p.q = q; p.k = k; p.v = v; p.g = g; p.h0 = h0; p.o = o; p.ht = ht;
   p.BH = (int)BH; p.L = L; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
-  p.ops = carve_ops(static_cast<char*>(saved), lay.ops, true);
+  p.ops = carve_ops(static_cast<char*>(saved), lay.ops);
   p.Hs = static_cast<char*>(saved) + lay.hs;
   p.events = ev;
   if (dispatch_fwd(dtype, DKP, CP, p, static_cast<hipStream_t>(stream)) != hipSuccess) return GLA_ERR_HIP;
@@ -322,7 +320,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* g, const f
   p.q = q; p.k = k; p.v = v; p.g = g; p.do_ = do_; p.h0 = h0; p.dht = dht;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dh0 = dh0;
   p.BH = (int)BH; p.L = L; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
-  p.ops = carve_ops(ws, lay.ops, true);
+  p.ops = carve_ops(ws, lay.ops);
   p.Hs = ws + lay.hs;
   p.dHs = ws + lay.dhs;
   p.saved = false;
@@ -359,7 +357,7 @@ int bwd_saved_impl(const void* q, const void* k, const void* v, const void* g, c
   p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dh0 = dh0;
   p.BH = (int)BH; p.L = L; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
   char* sv = const_cast<char*>(static_cast<const char*>(saved));   // read only on this path
-  p.ops = carve_ops(sv, lay.ops, true);
+  p.ops = carve_ops(sv, lay.ops);
   p.Hs = sv + lay.hs;
   p.dHs = workspace;
   p.saved = true;
@@ -601,12 +599,12 @@ int check_gsa(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, bool
 }
 
 struct GsaLayout {
-  size_t W, P, Pf, dP, dW2, dg2, dZ, WdT, Gam, S1s, dS1s, dZsT, ops2base, Hs2, dHs2, total;
+  size_t W, P, Pf, dP, dW2, dg2, dZ, WdT, Gam, S1s, dS1s, dZs, ops2base, Hs2, dHs2, total;
   OpsLayout ops2;
 };
 
 // Parts of the GSA device memory.  FWD: the forward's own tensors.  SAVED: those plus what only
-// the backward reads (the fp32 read-out Pf, pass 2's Qs^T operand) -- what gsa_fwd_save leaves
+// the backward reads (the fp32 read-out Pf) -- what gsa_fwd_save leaves
 // for gsa_bwd_saved.  GRAD: the backward's gradient buffers.  gsa_bwd keeps SAVED and GRAD in
 // one workspace.
 enum { kGsaFwd = 1, kGsaSaved = 2, kGsaGrad = 4 };
@@ -626,7 +624,7 @@ GsaLayout gsa_layout_of(int B, int H, int L, int Dk, int Dv, int m, int C, int d
     l.Gam = take(BH * N * MP * 4);
     l.S1s = take(BH * N * MP * DkP * es);
     if (saved) l.Pf = take(tok * 4);
-    l.ops2 = ops_layout(BH, N, CP, MP, es, saved);
+    l.ops2 = ops_layout(BH, N, CP, MP, es);
     l.ops2base = take(l.ops2.total);
     l.Hs2 = take(BH * N * MP * DvP * es);
   }
@@ -636,7 +634,7 @@ GsaLayout gsa_layout_of(int B, int H, int L, int Dk, int Dv, int m, int C, int d
     l.dg2 = take(tok * 4);
     l.dZ = take(tok * 4);
     l.dS1s = take(BH * N * MP * DkP * es);
-    l.dZsT = take(BH * N * MP * CP * es);
+    l.dZs = take(BH * N * CP * MP * es);
     l.dHs2 = take(BH * N * MP * DvP * es);
   }
   l.total = off;
@@ -656,12 +654,12 @@ GsaParams gsa_params(const GsaLayout& lf, char* fb, bool saved, const GsaLayout&
   p.W = fb + lf.W; p.P = fb + lf.P; p.WdT = fb + lf.WdT; p.Gam = reinterpret_cast<float*>(fb + lf.Gam);
   p.S1s = fb + lf.S1s;
   if (saved) p.Pf = reinterpret_cast<float*>(fb + lf.Pf);
-  p.ops2 = carve_ops(fb + lf.ops2base, lf.ops2, saved);
+  p.ops2 = carve_ops(fb + lf.ops2base, lf.ops2);
   p.Hs2 = fb + lf.Hs2;
   if (gb) {
     p.dP = reinterpret_cast<float*>(gb + lg.dP); p.dW2 = gb + lg.dW2;
     p.dg2 = reinterpret_cast<float*>(gb + lg.dg2); p.dZ = reinterpret_cast<float*>(gb + lg.dZ);
-    p.dS1s = gb + lg.dS1s; p.dZsT = gb + lg.dZsT;
+    p.dS1s = gb + lg.dS1s; p.dZs = gb + lg.dZs;
     p.dHs2 = gb + lg.dHs2;
   }
   return p;
@@ -898,8 +896,8 @@ int msgla_fwd(const void* q, const void* k, const void* v, const void* g, const 
     p.hold_s = G.s; p.hold_L = L; p.hold_H = H; p.hold_h0 = G.h0; p.hold_nh = G.nh;
     p.hold_ng = ngroups; p.hold_gi = i;
     p.BH = B * G.nh; p.L = Ls; p.Dk = Dk; p.Dv = Dv; p.C = C; p.N = N;
-    const OpsLayout ol = ops_layout((size_t)p.BH, N, CP, DKP, es, false);
-    p.ops = carve_ops(ws + lay.gla[i], ol, false);
+    const OpsLayout ol = ops_layout((size_t)p.BH, N, CP, DKP, es);
+    p.ops = carve_ops(ws + lay.gla[i], ol);
     p.Hs = ws + lay.gla[i] + ol.total;
     p.events = LaunchEvents{nullptr, 0};
   }

@@ -25,7 +25,7 @@
 // in-chunk prefix sums.
 //
 // Launches:
-//   1. gla_prep_kernel (also writes QsT)                      grid N x BH
+//   1. gla_prep_kernel                                        grid N x BH
 //   2. walk_store: forward state walk storing H_n               grid ceil(Dv/64) * BH
 //   3. walk_reverse: reverse walk storing dH_{n+1}              grid ceil(Dv/64) * BH
 //      (walks.hpp; state slices in fp32 MFMA accumulators)
@@ -884,13 +884,13 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
     const int ntile = (p.Dv + kDvTile - 1) / kDvTile;
     if (!p.saved) {   // recompute the chunk operands and the forward states
       PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N};
-      if ((e = launch_prep<T, DKP, CP, true>(pp, p.BH, s)) != hipSuccess) return e;
+      if ((e = launch_prep<T, DKP, CP>(pp, p.BH, s)) != hipSuccess) return e;
       record_event(p.events, ev++, s);
       WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, nullptr, p.Dk, p.Dv, p.L, p.C, p.N, 0};
       if ((e = launch_walk_store<T, DKP, CP>(wf, p.BH, s)) != hipSuccess) return e;
       record_event(p.events, ev++, s);
     }
-    WalkIO wr{p.ops.QsT, p.do_, p.ops.Gam, p.dHs, p.dht, p.dh0, p.Dk, p.Dv, p.L, p.C, p.N, 0};
+    WalkIO wr{p.ops.Qs, p.do_, p.ops.Gam, p.dHs, p.dht, p.dh0, p.Dk, p.Dv, p.L, p.C, p.N, 0};
     if ((e = launch_walk_reverse<T, DKP, CP>(wr, p.BH, s)) != hipSuccess) return e;
     record_event(p.events, ev++, s);
     const int ntiles = p.N * p.BH * (DKP / P::DKS);

@@ -240,7 +240,7 @@ hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
   } else {
     PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N, p.in};
     record_event(p.events, 0, s);
-    hipError_t e = p.ops.QsT ? launch_prep<T, DKP, CP, true>(pp, p.BH, s) : launch_prep<T, DKP, CP, false>(pp, p.BH, s);
+    hipError_t e = launch_prep<T, DKP, CP>(pp, p.BH, s);
     if (e != hipSuccess) return e;
     record_event(p.events, 1, s);
     WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, p.ht, p.Dk, p.Dv, p.L, p.C, p.N, 0, p.in};
@@ -293,7 +293,7 @@ hipError_t launch_gla_fwd_batches(const FwdParams* ps, int nb, hipStream_t s) {
     bp.first[0] = bo.first[0] = 0;
     for (int i = 0; i < nb; ++i) {
       const FwdParams& p = ps[i];
-      if (p.ops.QsT || p.Dk != ps[0].Dk || p.Dv != ps[0].Dv || p.C != ps[0].C || !p.hold_o != !ps[0].hold_o)
+      if (p.Dk != ps[0].Dk || p.Dv != ps[0].Dv || p.C != ps[0].C || !p.hold_o != !ps[0].hold_o)
         return hipErrorInvalidValue;
       bp.p[i] = PrepParams{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N, p.in};
       bw.p[i] = WalkIO{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, p.ht, p.Dk, p.Dv, p.L, p.C, p.N, 0, p.in};
@@ -304,7 +304,7 @@ hipError_t launch_gla_fwd_batches(const FwdParams* ps, int nb, hipStream_t s) {
       bo.first[i + 1] = bo.first[i] + ntile * p.N * p.BH;
     }
     hipError_t e;
-    if ((e = launch_prep_batches<T, DKP, CP, false>(bp, maxN, s)) != hipSuccess) return e;
+    if ((e = launch_prep_batches<T, DKP, CP>(bp, maxN, s)) != hipSuccess) return e;
     if ((e = launch_walk_store_batches<T, DKP, CP>(bw, BH, s)) != hipSuccess) return e;
     if (ps[0].hold_o)
       hipLaunchKernelGGL((gla_fwd_out_batches<T, DKP, CP, true>), dim3(bo.first[nb]), dim3(256), 0, s, bo, ntile);

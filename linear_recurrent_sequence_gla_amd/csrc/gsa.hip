@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
   using M = ChunkMap<T, MP, CP>;
   constexpr int V = M::V, RPS = M::RPS, LDM = MP + V;
   typedef typename V16<T>::type VT;
-  __shared__ __attribute__((aligned(16))) T sZs[CP * LDM];     // dZ 2^b row by row; leaves transposed
+  __shared__ __attribute__((aligned(16))) T sZs[CP * LDM];     // dZ 2^b, staged to leave in 16-byte rows
   __shared__ float segtot[M::NSEG * MP];
   __shared__ float sGam[MP];
   __shared__ float red[8];
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
     }
   }
   __syncthreads();
-  tile_out_t<T, 4>(reinterpret_cast<T*>(p.dZsT) + chunk * MP * CP, sZs, CP, MP, LDM);
+  tile_out<T>(reinterpret_cast<T*>(p.dZs) + chunk * CP * MP, sZs, CP, MP, LDM);
 }
 
 // ----------------------------------------------------------------------------- pass 1 backward
@@ -885,7 +885,7 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
       hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       PrepParams pp{p.P, p.W, p.g, p.ops2, p.L, p.m, p.C, p.N};
-      if ((e = launch_prep<T, MP, CP, true>(pp, p.BH, s)) != hipSuccess) return e;
+      if ((e = launch_prep<T, MP, CP>(pp, p.BH, s)) != hipSuccess) return e;
     }
     BwdParams b;
     b.q = p.P; b.k = p.W; b.v = p.v; b.g = p.g; b.do_ = p.do_; b.h0 = p.hv0; b.dht = p.dhvt;
@@ -896,7 +896,7 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
     if ((e = launch_gla_bwd<T, MP, CP>(b, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((gsa_dz_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    WalkIO w1r{p.dZsT, p.q, p.Gam, p.dS1s, p.dhkt, p.dhk0, p.m, p.Dk, p.L, p.C, p.N, 1};
+    WalkIO w1r{p.dZs, p.q, p.Gam, p.dS1s, p.dhkt, p.dhk0, p.m, p.Dk, p.L, p.C, p.N, 1};
     if ((e = launch_walk_reverse<T, MP, CP>(w1r, p.BH, s)) != hipSuccess) return e;
     const int ntk = p.DkP / kDvTile;
     hipLaunchKernelGGL((gsa_pass1_bwd_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(kP1Threads), 0, s, p, ntk);

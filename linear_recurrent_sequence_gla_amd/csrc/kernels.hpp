@@ -37,7 +37,6 @@ struct Batches {
 // consumers need no bounds checks: CP = padded chunk rows, DKP = padded key width.
 struct ChunkOps {
   void* Qs;     // [BH][N][CP][DKP]  q * 2^{b}            (T)
-  void* QsT;    // [BH][N][DKP][CP]  same, transposed      (T) or nullptr
   void* KdT;    // [BH][N][DKP][CP]  (k * 2^{Gamma - b})^T (T)
   void* A;      // [BH][N][CP][CP]   masked intra-chunk scores (T)
   float* Gam;   // [BH][N][DKP]      chunk log2-decay Gamma (f32)
@@ -59,7 +58,7 @@ struct FwdParams {
   void* o;
   float* ht;
   int BH, L, Dk, Dv, C, N;
-  ChunkOps ops;   // ops.QsT != nullptr: the preparation also writes Qs^T (kept for a backward)
+  ChunkOps ops;
   void* Hs;       // [BH][N][DKP][DvP] chunk-start states (T), written by the state walk
   bool states_ready = false;   // Hs (and ht) already hold the walk's result: no walk is run
   LaunchEvents events;
@@ -94,7 +93,7 @@ struct BwdParams {
   ChunkOps ops;
   void* Hs;       // [BH][N][DKP][DvP] state at chunk starts (T)
   void* dHs;      // [BH][N][DKP][DvP] state gradient at chunk ends (T)
-  bool saved;     // ops (with QsT) and Hs were left by a forward: skip recomputing them
+  bool saved;     // ops and Hs were left by a forward: skip recomputing them
   LaunchEvents events;
   // if set, dq goes here in fp32 [BH][L][Dk] instead of to dq: GSA's pass 2, whose dq is the
   // gradient of the read-out, which the softmax's Jacobian then reduces with cancellation
@@ -111,7 +110,7 @@ struct GsaParams {
   float *dg, *dhk0, *dhv0;
   int BH, L, Dk, DkP, Dv, m, C, N;
   int act;        // read-out between the passes (GsaAct)
-  int saved;      // backward: W, P, Pf, WdT, Gam, S1s, ops2 (with QsT) and Hs2 were left by a
+  int saved;      // backward: W, P, Pf, WdT, Gam, S1s, ops2 and Hs2 were left by a
                   // saving forward, so the backward does not recompute them
   // workspace
   void* W;        // [BH][L][m] write weights 1 - exp(g)   (keys of pass 2)   (T)
@@ -126,7 +125,7 @@ struct GsaParams {
   float* Gam;     // [BH][N][MP]
   void* S1s;      // [BH][N][MP][DkP] pass-1 state S1^T at chunk starts        (T)
   void* dS1s;     // [BH][N][MP][DkP] its gradient at chunk ends (backward)    (T)
-  void* dZsT;     // [BH][N][MP][CP] (dZ 2^b)^T (backward)                     (T)
+  void* dZs;      // [BH][N][CP][MP] dZ 2^b, chunk-padded (backward)           (T)
   ChunkOps ops2;  // pass-2 GLA chunk operands
   void *Hs2, *dHs2;
 };

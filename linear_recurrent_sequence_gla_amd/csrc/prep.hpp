@@ -7,7 +7,7 @@
 //   KdT    = (k * 2^{Gamma - b})^T     (the key decayed to the chunk end; transposed)
 //   A[r,c] = sum_i q_r[i] k_c[i] 2^{b_r[i] - b_c[i]} for c <= r, else 0
 // which are the inputs of the state walk (Gamma, KdT), the chunk outputs (Qs, A) and, for
-// the backward, the reverse state walk (QsT).  The decomposition into chunks with a
+// the backward, the reverse state walk (Gamma, Qs).  The decomposition into chunks with a
 // sequential state pass between them and a parallel causal block inside each chunk follows
 // the chunkwise training form (MS-GLA summary, section 2.1; GLA visual companion, "Why
 // chunking and SRAM locality matter").
@@ -288,7 +288,7 @@ struct ChunkScan {
   }
 };
 
-template <typename T, int DKP, int CP, bool WANT_QST>
+template <typename T, int DKP, int CP>
 __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh) {
   using Cfg = PrepCfg<T, DKP, CP>;
   using M = ChunkMap<T, DKP, CP>;
@@ -348,7 +348,6 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh) {
     }
   }
   __syncthreads();
-  if constexpr (WANT_QST) tile_out_t<T, 4>(reinterpret_cast<T*>(p.ops.QsT) + chunk * CP * DKP, sQ, CP, DKP, LDQ);
 
   // ---- intra-chunk scores A, kept in registers until the LDS operands are released
   const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
@@ -511,37 +510,37 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh) {
 }
 
 // grid (N, BH): chunk n of sequence bh
-template <typename T, int DKP, int CP, bool WANT_QST>
+template <typename T, int DKP, int CP>
 __global__ __launch_bounds__(256, 2) void gla_prep_kernel(PrepParams p) {
-  prep_chunk<T, DKP, CP, WANT_QST>(p, blockIdx.x, blockIdx.y);
+  prep_chunk<T, DKP, CP>(p, blockIdx.x, blockIdx.y);
 }
 
 // grid (max N, total sequences): blockIdx.y runs over the batches' sequences back to back;
 // blocks past a batch's own chunk count return at once
-template <typename T, int DKP, int CP, bool WANT_QST>
+template <typename T, int DKP, int CP>
 __global__ __launch_bounds__(256, 2) void gla_prep_batches(Batches<PrepParams> b) {
   const int gi = b.find(blockIdx.y);
   const PrepParams& p = b.p[gi];
   if ((int)blockIdx.x >= p.N) return;
-  prep_chunk<T, DKP, CP, WANT_QST>(p, blockIdx.x, blockIdx.y - b.first[gi]);
+  prep_chunk<T, DKP, CP>(p, blockIdx.x, blockIdx.y - b.first[gi]);
 }
 
-template <typename T, int DKP, int CP, bool WANT_QST>
+template <typename T, int DKP, int CP>
 hipError_t launch_prep(const PrepParams& p, int BH, hipStream_t s) {
   if constexpr (PrepCfg<T, DKP, CP>::BYTES > kMaxLds) {
     return hipErrorNotSupported;
   } else {
-    hipLaunchKernelGGL((gla_prep_kernel<T, DKP, CP, WANT_QST>), dim3(p.N, BH), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gla_prep_kernel<T, DKP, CP>), dim3(p.N, BH), dim3(256), 0, s, p);
     return hipGetLastError();
   }
 }
 
-template <typename T, int DKP, int CP, bool WANT_QST>
+template <typename T, int DKP, int CP>
 hipError_t launch_prep_batches(const Batches<PrepParams>& b, int maxN, hipStream_t s) {
   if constexpr (PrepCfg<T, DKP, CP>::BYTES > kMaxLds) {
     return hipErrorNotSupported;
   } else {
-    hipLaunchKernelGGL((gla_prep_batches<T, DKP, CP, WANT_QST>), dim3(maxN, b.first[b.n]), dim3(256), 0, s, b);
+    hipLaunchKernelGGL((gla_prep_batches<T, DKP, CP>), dim3(maxN, b.first[b.n]), dim3(256), 0, s, b);
     return hipGetLastError();
   }
 }

@@ -7,9 +7,12 @@
 //   reverse walk   D_N = init;  for n = N-1..0:      store D_{n+1} (at index n),
 //                               D_n = Diag(2^{Gamma_n}) D_{n+1} + M_n X_n ;    fin = D_0
 //
-// with M_n = mat[n] a per-chunk [SP][CP] matrix (the decayed keys transposed for the forward
-// walk, the decayed queries transposed for the reverse walk) and X_n the chunk's rows of a
-// token tensor src [L][Ds] (values for the forward walk, output gradients for the reverse).
+// with M_n = mat[n] a per-chunk [SP][CP] matrix and X_n the chunk's rows of a token tensor
+// src [L][Ds] (values for the forward walk, output gradients for the reverse).  The forward
+// walk reads M_n as stored ([SP][CP]: the decayed keys transposed); the reverse walk reads its
+// transpose as stored ([CP][SP]: the decayed queries, chunk rows first, exactly as the output
+// kernels use them) and takes M_n from it with transposing LDS reads, so no transposed copy of
+// the queries is ever written.
 // GLA: rows = key channels.  GSA: rows = slots for both passes (pass 1 walks the transposed
 // slot-key memory, whose values are the keys).  The chunked structure -- sequential
 // inter-chunk updates, state written only at chunk boundaries -- is the chunkwise training
@@ -36,7 +39,7 @@
 namespace gla {
 
 struct WalkIO {
-  const void* mat;     // [BH][N][SP][CP] per-chunk matrix (T)
+  const void* mat;     // [BH][N][SP][CP] per-chunk matrix (T); reverse walks: [BH][N][CP][SP]
   const void* src;     // [BH][L][Ds] token tensor (T)
   const float* gam;    // [BH][N][SP] chunk log2-decay per state row
   void* states;        // [BH][N][SP][DsP] stored states / state gradients (T)
@@ -58,8 +61,10 @@ constexpr int kWalkDepth = 2;   // chunk groups whose operands are in flight ahe
 template <typename T, int RT, int CP, int G = 1, int NT = 256>
 struct WalkIOCfg {
   static constexpr int V = 16 / (int)sizeof(T);
-  static constexpr int LDA = CP + V, LDV = kDvTile + V;
-  static constexpr size_t KT = (size_t)RT * LDA * sizeof(T);
+  // per-chunk matrix tile: [RT][LDA] as stored for a forward walk, [CP][LDM] (chunk rows
+  // first) for a reverse walk; the slot has room for either, so both directions share a plan
+  static constexpr int LDA = CP + V, LDM = RT + V, LDV = kDvTile + V;
+  static constexpr size_t KT = (size_t)(RT * LDA > CP * LDM ? RT * LDA : CP * LDM) * sizeof(T);
   static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
   static constexpr size_t GT = (size_t)RT * 4;
   static constexpr size_t SLOT = KT + VT + GT;            // one chunk's operands
@@ -120,23 +125,31 @@ constexpr bool walk_fits() {
 // beside it; masking happens when the registers are written to LDS, after the data has
 // arrived.  This keeps branches and register rewrites away from loads in flight, so the
 // compiler can leave several chunks' loads outstanding.
-template <typename T, int RT, int CP, int NT>
+// ROWM: the chunk's matrix is stored chunk rows first ([CP][SP]; mat points at this tile's
+// first column and the rows are SP apart), else as [RT][CP] rows (row stride CP).
+template <typename T, int RT, int CP, int NT, bool ROWM, int SP>
 struct WalkIOStage {
   using W = WalkIOCfg<T, RT, CP, 1, NT>;
   typedef typename V16<T>::type VT;
+  static constexpr int MPR = ROWM ? RT / W::V : CP / W::V;   // matrix vectors per stored row
   VT kt[W::PKd], v[W::PV];
   bool vok[W::PV];
   f32x4 gam;
 
-  // mat: [RT][CP] rows of this chunk's matrix (row stride CP); src: [L][Ds] of this (b,h);
-  // gam_chunk: this tile's RT decay values.
+  // mat: this tile's part of the chunk's matrix; src: [L][Ds] of this (b,h); gam_chunk: this
+  // tile's RT decay values.
   __device__ __forceinline__ void load(const T* mat, const T* src, int row0, int len, int Ds, int tile,
                                        const float* gam_chunk) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < W::PKd; ++m) {
       const int idx = min(tid + NT * m, W::NK - 1);
-      kt[m] = *reinterpret_cast<const VT*>(mat + (size_t)idx * W::V);
+      if constexpr (ROWM) {
+        const int r = idx / MPR, c = (idx - r * MPR) * W::V;
+        kt[m] = *reinterpret_cast<const VT*>(mat + (size_t)r * SP + c);
+      } else {
+        kt[m] = *reinterpret_cast<const VT*>(mat + (size_t)idx * W::V);
+      }
     }
     constexpr int PER_ROW = kDvTile / W::V;
 #pragma unroll
@@ -157,8 +170,8 @@ struct WalkIOStage {
     for (int m = 0; m < W::PKd; ++m) {
       const int idx = tid + NT * m;
       if (W::NK % NT == 0 || idx < W::NK) {
-        const int r = idx / (CP / W::V), c = (idx - r * (CP / W::V)) * W::V;
-        *reinterpret_cast<VT*>(sKT + r * W::LDA + c) = kt[m];
+        const int r = idx / MPR, c = (idx - r * MPR) * W::V;
+        *reinterpret_cast<VT*>(sKT + r * (ROWM ? W::LDM : W::LDA) + c) = kt[m];
       }
     }
     constexpr int PER_ROW = kDvTile / W::V;
@@ -207,8 +220,8 @@ __device__ __forceinline__ size_t walk_state_index(const WalkIO& w, int bh, int 
 
 // T^T = X^T M^T on fresh accumulators (M and X from LDS): one chunk's state increment over
 // the RW rows from row ri and the 16 columns from cj, with lane (col, grp) holding
-// T[ri + 16 ib + col][cj + 4 grp + e] in Tm[ib][e].
-template <typename T, int RT, int CP, int RW>
+// T[ri + 16 ib + col][cj + 4 grp + e] in Tm[ib][e].  ROWM: sKT holds M^T ([CP][LDM]).
+template <typename T, int RT, int CP, int RW, bool ROWM>
 __device__ __forceinline__ void walk_product(f32x4 (&Tm)[RW / 16], const T* sKT, const T* sV, int ri, int cj) {
   using W = WalkIOCfg<T, RT, CP>;
   const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
@@ -221,8 +234,12 @@ __device__ __forceinline__ void walk_product(f32x4 (&Tm)[RW / 16], const T* sKT,
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib)
-      mma(Tm[ib], Yv[cb], ld8(sKT + (ri + 16 * ib + col) * W::LDA + 32 * cb + 8 * grp));
+    for (int ib = 0; ib < NIB; ++ib) {
+      if constexpr (ROWM)
+        mma(Tm[ib], Yv[cb], ld8_colblk(sKT + (32 * cb) * W::LDM + ri + 16 * ib, W::LDM));
+      else
+        mma(Tm[ib], Yv[cb], ld8(sKT + (ri + 16 * ib + col) * W::LDA + 32 * cb + 8 * grp));
+    }
   }
 }
 
@@ -233,7 +250,7 @@ __device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
   constexpr int NT = 64 * NW, RW = RT * 4 / NW;
   static_assert(NW == 4 || NW == 8, "four column waves, one or two row groups");
   using W = WalkIOCfg<T, RT, CP, G, NT>;
-  using Stage = WalkIOStage<T, RT, CP, NT>;
+  using Stage = WalkIOStage<T, RT, CP, NT, REV, SP>;
   constexpr int LDV = W::LDV, NIB = RW / 16, NRT = SP / RT, R = kWalkDepth;
   __shared__ __attribute__((aligned(16))) char smem[W::BYTES];
 
@@ -255,7 +272,7 @@ __device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
   const int j0 = tile * kDvTile + cw + 4 * grp;             // this lane's four columns
   typedef typename Vec4<T>::type V4T;
   const T* src = reinterpret_cast<const T*>(w.src) + (size_t)w.in(bh) * L * Ds;
-  const T* mat = reinterpret_cast<const T*>(w.mat) + ((size_t)bh * NT_ * SP + i0) * CP;
+  const T* mat = reinterpret_cast<const T*>(w.mat) + (size_t)bh * NT_ * SP * CP + (REV ? i0 : i0 * CP);
   const float* gam = w.gam + (size_t)bh * NT_ * SP + i0;
   T* out = reinterpret_cast<T*>(w.states) + ((size_t)bh * NT_ * SP + i0) * DsP + tile * kDvTile;
 
@@ -305,7 +322,7 @@ __device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
     load(st[r], kg + R);                         // st[r] (group kg) is already in LDS
     f32x4 Tm[G][NIB];
 #pragma unroll
-    for (int g = 0; g < G; ++g) walk_product<T, RT, CP, RW>(Tm[g], sKT(b, g), sV(b, g), ri, cw);
+    for (int g = 0; g < G; ++g) walk_product<T, RT, CP, RW, REV>(Tm[g], sKT(b, g), sV(b, g), ri, cw);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int k = kg * G + g;
