@@ -51,9 +51,13 @@ struct WalkIO {
   // parallel, the first from init and the others from zero.  Each segment then leaves its end
   // state in seg_end ([BH][nseg][SP][DsP] fp32) instead of writing fin; the stored states of
   // later segments lack the part carried in from before the segment (the segment kernels
-  // further down add it).
+  // further down add it).  The first column tile's workgroups also write, per row, the
+  // segment's log2-decay before each chunk (seg_prefix [BH][N][SP]) and in all
+  // (seg_total [BH][nseg][SP]).
   int nseg = 1, seg_len = 0;
   float* seg_end = nullptr;
+  float* seg_prefix = nullptr;
+  float* seg_total = nullptr;
 };
 
 constexpr int kWalkDepth = 2;   // chunk groups whose operands are in flight ahead of use
@@ -283,6 +287,12 @@ __device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
   auto sHo = [&](int b, int g) { return reinterpret_cast<T*>(smem + 2 * W::STAGE + (b * G + g) * W::HT); };
   auto chunk_of = [&](int k) { return REV ? N - 1 - k : c0 + k; };   // the k-th chunk visited
 
+  // segmented walk: the lanes of the first column wave of the first column tile keep the
+  // running log2-decay of their rows over the segment's chunks
+  const bool keep_pre = !REV && w.nseg > 1 && tile == 0 && (wave & 3) == 0 && grp == 0;
+  float run[NIB];
+#pragma unroll
+  for (int ib = 0; ib < NIB; ++ib) run[ib] = 0.f;
   f32x4 S[NIB];
 #pragma unroll
   for (int ib = 0; ib < NIB; ++ib) {
@@ -329,6 +339,13 @@ __device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
       if (!CHECK || k < N) {
         const float* gg = sG(b, g);
         T* ho = sHo(b, g) + (ri + col) * LDV + cw + 4 * grp;
+        if (!REV && keep_pre) {
+#pragma unroll
+          for (int ib = 0; ib < NIB; ++ib) {
+            w.seg_prefix[((size_t)bh * NT_ + chunk_of(k)) * SP + i0 + ri + 16 * ib + col] = run[ib];
+            run[ib] += gg[ri + 16 * ib + col];
+          }
+        }
 #pragma unroll
         for (int ib = 0; ib < NIB; ++ib) {
           V4T hv;
@@ -370,6 +387,10 @@ __device__ __forceinline__ void walk_tile(const WalkIO& w, int ntile, int lin) {
   }
   for (; kg < NG; kg += R) round_checked(kg);
   if (w.nseg > 1) {
+    if (keep_pre) {
+#pragma unroll
+      for (int ib = 0; ib < NIB; ++ib) w.seg_total[((size_t)bh * w.nseg + seg) * SP + i0 + ri + 16 * ib + col] = run[ib];
+    }
     float* e_out = w.seg_end + (((size_t)bh * w.nseg + seg) * SP + i0 + ri) * DsP;
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib)
@@ -455,9 +476,9 @@ hipError_t launch_walk_store(const WalkIO& w, int BH, hipStream_t s) {
 // with H_n^seg what the segment's own walk stored, P_n the log2-decay of the segment's chunks
 // before n (per row) and X_s the true state at the segment's start:
 //     X_1 = E_0,   X_{s+1} = Diag(2^{D_s}) X_s + E_s,   final state = X_nseg,
-// E_s being the segment's own end state and D_s its total log2-decay.  seg_prefix_kernel forms
-// P and D, seg_carry_kernel X and the final state, and seg_fixup_kernel adds the carried part
-// to the stored states.
+// E_s being the segment's own end state and D_s its total log2-decay.  The segmented walk
+// itself forms P and D, seg_carry_kernel X and the final state, and seg_fixup_kernel adds the
+// carried part to the stored states.
 struct SegParams {
   const float* gam;       // [BH][N][SP] chunk log2-decay per row
   const float* seg_end;   // [BH][nseg][SP][DsP] each segment's own end state (fp32)
@@ -469,40 +490,6 @@ struct SegParams {
   int N, nseg, seg_len, rows, Ds, DsP;
 };
 constexpr int kMaxSeg = 8;
-constexpr int kSegRounds = 16;     // 16-chunk rounds whose decay loads are in flight together
-
-// grid (BH, SP / 16, nseg): P_n for 16 rows over one segment, and D_s.  Thread (row r, lane l)
-// takes chunks l, l + 16, ... of the segment; each round of 16 chunks is scanned across the
-// 16 lanes of a row with shuffles.
-template <int SP>
-__global__ __launch_bounds__(256) void seg_prefix_kernel(SegParams q) {
-  const int bh = blockIdx.x, i = blockIdx.y * 16 + (threadIdx.x >> 4), sg = blockIdx.z, l = threadIdx.x & 15;
-  const int c0 = sg * q.seg_len, c1 = min(q.N, c0 + q.seg_len);
-  const float* gam = q.gam + (size_t)bh * q.N * SP + i;
-  float* pre = q.prefix + (size_t)bh * q.N * SP + i;
-  float run = 0.f;                                 // decay of the rounds before
-  for (int base = c0; base < c1; base += 16 * kSegRounds) {
-    float gv[kSegRounds];
-#pragma unroll
-    for (int t = 0; t < kSegRounds; ++t) {
-      const int n = base + 16 * t + l;
-      gv[t] = n < c1 ? gam[(size_t)n * SP] : 0.f;
-    }
-#pragma unroll
-    for (int t = 0; t < kSegRounds; ++t) {
-      float x = gv[t];                             // inclusive scan over the row's 16 lanes
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float y = __shfl_up(x, o, 16);
-        if (l >= o) x += y;
-      }
-      const int n = base + 16 * t + l;
-      if (n < c1) pre[(size_t)n * SP] = run + x - gv[t];
-      run += __shfl(x, 15, 16);
-    }
-  }
-  if (l == 0) q.total[((size_t)bh * q.nseg + sg) * SP + i] = run;
-}
 
 // grid (BH, SP / 16, DsP / 64): the carries for 16 rows and 64 columns, four columns a thread
 template <int SP>
@@ -601,8 +588,8 @@ int walk_segments(int BH, int Ds, int N, int seg_max) {
   }
 }
 
-// The forward walk in nseg segments (nseg from walk_segments, >= 2), then the decay prefixes,
-// the carries and the fix-up: w.states and w.fin end as the plain walk would leave them.
+// The forward walk in nseg segments (nseg from walk_segments, >= 2; it also leaves the decay
+// prefixes and totals), then the carries and the fix-up: w.states and w.fin end as the plain walk would leave them.
 // Scratch: seg_end and carry [BH][nseg][SP][DsP] fp32, prefix [BH][N][SP] fp32, total
 // [BH][nseg][SP] fp32.
 // fixup = false leaves the stored states without their carried part, for a consumer that adds
@@ -619,13 +606,13 @@ hipError_t launch_walk_store_segmented(WalkIO w, int BH, int nseg, float* seg_en
     w.nseg = nseg;
     w.seg_len = (w.N + nseg - 1) / nseg;
     w.seg_end = seg_end;
+    w.seg_prefix = prefix;
+    w.seg_total = total;
     hipLaunchKernelGGL((walk_kernel<T, SP, RT, CP, 2, false, NW>), dim3(ntile * (SP / RT) * BH * nseg), dim3(64 * NW),
                        0, s, w, ntile);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SegParams q{w.gam, seg_end, carry, prefix, total, w.states, w.fin, w.N, nseg, w.seg_len, w.rows, w.Ds, DsP};
-    hipLaunchKernelGGL((seg_prefix_kernel<SP>), dim3(BH, SP / 16, nseg), dim3(256), 0, s, q);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((seg_carry_kernel<SP>), dim3(BH, SP / 16, ntile), dim3(256), 0, s, q);
     if ((e = hipGetLastError()) != hipSuccess || !fixup) return e;
     hipLaunchKernelGGL((seg_fixup_kernel<T, SP>), dim3(w.N - w.seg_len, BH), dim3(256), 0, s, q);
