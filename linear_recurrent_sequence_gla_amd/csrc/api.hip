@@ -79,13 +79,14 @@ struct OpsLayout {
   size_t qs, kdt, a, gam, total;
 };
 
-OpsLayout ops_layout(size_t BH, size_t N, size_t CP, size_t DKP, size_t es) {
+// kd_gam = false: no room for KdT and Gam (GSA's pass 2 uses pass 1's WdT and Gamma)
+OpsLayout ops_layout(size_t BH, size_t N, size_t CP, size_t DKP, size_t es, bool kd_gam = true) {
   OpsLayout l{};
   size_t off = 0;
   l.qs = off;  off += align_up(BH * N * CP * DKP * es);
-  l.kdt = off; off += align_up(BH * N * CP * DKP * es);
+  l.kdt = off; if (kd_gam) off += align_up(BH * N * CP * DKP * es);
   l.a = off;   off += align_up(BH * N * CP * CP * es);
-  l.gam = off; off += align_up(BH * N * DKP * 4);
+  l.gam = off; if (kd_gam) off += align_up(BH * N * DKP * 4);
   l.total = off;
   return l;
 }
@@ -624,7 +625,7 @@ GsaLayout gsa_layout_of(int B, int H, int L, int Dk, int Dv, int m, int C, int d
     l.Gam = take(BH * N * MP * 4);
     l.S1s = take(BH * N * MP * DkP * es);
     if (saved) l.Pf = take(tok * 4);
-    l.ops2 = ops_layout(BH, N, CP, MP, es);
+    l.ops2 = ops_layout(BH, N, CP, MP, es, false);
     l.ops2base = take(l.ops2.total);
     l.Hs2 = take(BH * N * MP * DvP * es);
   }
@@ -655,6 +656,8 @@ GsaParams gsa_params(const GsaLayout& lf, char* fb, bool saved, const GsaLayout&
   p.S1s = fb + lf.S1s;
   if (saved) p.Pf = reinterpret_cast<float*>(fb + lf.Pf);
   p.ops2 = carve_ops(fb + lf.ops2base, lf.ops2);
+  p.ops2.KdT = p.WdT;   // pass 2's decayed keys and chunk decays are pass 1's
+  p.ops2.Gam = p.Gam;
   p.Hs2 = fb + lf.Hs2;
   if (gb) {
     p.dP = reinterpret_cast<float*>(gb + lg.dP); p.dW2 = gb + lg.dW2;

@@ -240,7 +240,7 @@ hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
   } else {
     PrepParams pp{p.q, p.k, p.g, p.ops, p.L, p.Dk, p.C, p.N, p.in};
     record_event(p.events, 0, s);
-    hipError_t e = launch_prep<T, DKP, CP>(pp, p.BH, s);
+    hipError_t e = p.ops_ready ? hipSuccess : launch_prep<T, DKP, CP>(pp, p.BH, s);
     if (e != hipSuccess) return e;
     record_event(p.events, 1, s);
     WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, p.ht, p.Dk, p.Dv, p.L, p.C, p.N, 0, p.in};

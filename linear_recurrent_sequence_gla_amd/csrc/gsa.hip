@@ -129,13 +129,18 @@ struct SliceRegs {
 };
 
 // ----------------------------------------------------------------------------- pass 1 forward
-// Z = E * (QK (W Ei) + Q S1_n), P = softmax_slots(Z), written as the [L][m] queries of pass 2.
+// Z = E * (QK (W Ei) + Q S1_n), P = softmax_slots(Z), written as the [L][m] queries of pass 2,
+// together with pass 2's chunk operands, which are what the GLA preparation would form from
+// the queries P (as stored), the keys w and the same gates:
+//   Qs2 = P 2^b,   A2[r][c] = sum_s P[r][s] w[c][s] 2^{b_r[s] - b_c[s]}  (c <= r, else 0)
+// on the factorised path as (P E)(W Ei)^T on hi/lo matrix-core products, on the exact path
+// element by element.  Pass 2's decayed keys and chunk decays are WdT and Gamma themselves.
 template <typename T, int MP, int CP>
 __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
   using G = GsaCfg<T, MP, CP>;
   using M = ChunkMap<T, MP, CP>;
   constexpr int V = M::V, RPS = M::RPS;
-  constexpr int LDF = G::LDF, LDQK = G::LDQK, LDS = G::LDS, LDM = G::LDM, NRB = G::NRB, NSB = G::NSB;
+  constexpr int LDF = G::LDF, LDQK = G::LDQK, LDS = G::LDS, LDM = G::LDM, LDC = G::LDC, NRB = G::NRB, NSB = G::NSB;
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[G::P_BYTES];
   float* sB = reinterpret_cast<float*>(smem);
@@ -146,6 +151,7 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
   T* sS1 = sk + CP * LDS;
   float* sQK = reinterpret_cast<float*>(reg);  // after it
   T* sP = reinterpret_cast<T*>(reg + G::QKT);
+  T* sA2 = reinterpret_cast<T*>(reg);          // once the scores are formed: A2 [CP][LDC]
   float* segtot = reinterpret_cast<float*>(smem + 2 * G::FT + G::P_REGION);
   float* sGam = segtot + M::NSEG * MP;
   float* red = sGam + MP;
@@ -306,13 +312,68 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
       }
     }
   }
-  __syncthreads();
+  __syncthreads();   // P staged; sQK dead
+
+  // ---- A2 (rows past the chunk's end are zero, as are columns there: w = 0)
+  if (rbv) {
+    HiLo<T> fpe[MP / 32];                     // P E on this lane's operand row, once per wave
+    if (fast) {
+#pragma unroll
+      for (int ks = 0; ks < MP / 32; ++ks) {
+        float xa[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 16 * rb + col, sl = 32 * ks + 8 * grp + e;
+          xa[e] = to_f32(sP[r * LDM + sl]) * fast_exp2(sB[r * LDF + sl]);
+        }
+        fpe[ks] = hilo<T>(xa);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < NRB; ++cb) {
+      f32x4 acc = zero4();
+      if (cb <= rb) {
+        if (fast) {
+#pragma unroll
+          for (int ks = 0; ks < MP / 32; ++ks) {
+            float xb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xb[e] = sW[(16 * cb + col) * LDF + 32 * ks + 8 * grp + e];   // W Ei
+            mma3(acc, fpe[ks], hilo<T>(xb));
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
+            float x = 0.f;
+            if (c <= r)
+              for (int sl = 0; sl < m; ++sl)
+                x += to_f32(sP[r * LDM + sl]) * sW[c * LDF + sl] * fast_exp2(sB[r * LDF + sl] - sB[c * LDF + sl]);
+            acc[e] = x;
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
+        sA2[r * LDC + c] = from_f32<T>(c <= r && r < len ? acc[e] : 0.f);
+      }
+    }
+  }
   T* Pg = reinterpret_cast<T*>(p.P) + gbase;
+  T* Qg2 = reinterpret_cast<T*>(p.ops2.Qs) + chunk * CP * MP;
   constexpr int PER_ROW = MP / V;
   for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
     const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
-    if (r < len && c < m) *reinterpret_cast<VT*>(Pg + (size_t)r * m + c) = *reinterpret_cast<const VT*>(sP + r * LDM + c);
+    const VT pv = *reinterpret_cast<const VT*>(sP + r * LDM + c);
+    if (r < len && c < m) *reinterpret_cast<VT*>(Pg + (size_t)r * m + c) = pv;
+    VT qs;
+#pragma unroll
+    for (int e = 0; e < V; ++e) qs[e] = from_f32<T>(r < len ? to_f32(pv[e]) * fast_exp2(sB[r * LDF + c + e]) : 0.f);
+    *reinterpret_cast<VT*>(Qg2 + (size_t)r * MP + c) = qs;
   }
+  __syncthreads();
+  tile_out<T>(reinterpret_cast<T*>(p.ops2.A) + chunk * CP * CP, sA2, CP, CP, LDC);
 }
 
 // ----------------------------------------------------------------------------- read-out backward
@@ -863,11 +924,11 @@ hipError_t launch_gsa_fwd(const GsaParams& p, hipStream_t s) {
     if ((e = launch_gsa_walks<T, MP, CP>(p, p.hkt, p.hvt, s)) != hipSuccess) return e;
     hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // pass 2: its chunk operands and outputs on the states the walk above left
+    // pass 2's outputs from the chunk operands gsa_p left and the states the walk above left
     FwdParams f;
     f.q = p.P; f.k = p.W; f.v = p.v; f.g = p.g; f.h0 = p.hv0; f.o = p.o; f.ht = p.hvt;
     f.BH = p.BH; f.L = p.L; f.Dk = p.m; f.Dv = p.Dv; f.C = p.C; f.N = p.N;
-    f.ops = p.ops2; f.Hs = p.Hs2; f.states_ready = true; f.events = LaunchEvents{nullptr, 0};
+    f.ops = p.ops2; f.Hs = p.Hs2; f.states_ready = true; f.ops_ready = true; f.events = LaunchEvents{nullptr, 0};
     return launch_gla_fwd<T, MP, CP>(f, s);
   }
 }
@@ -884,8 +945,6 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
       if ((e = launch_gsa_walks<T, MP, CP>(p, nullptr, nullptr, s)) != hipSuccess) return e;
       hipLaunchKernelGGL((gsa_p_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      PrepParams pp{p.P, p.W, p.g, p.ops2, p.L, p.m, p.C, p.N};
-      if ((e = launch_prep<T, MP, CP>(pp, p.BH, s)) != hipSuccess) return e;
     }
     BwdParams b;
     b.q = p.P; b.k = p.W; b.v = p.v; b.g = p.g; b.do_ = p.do_; b.h0 = p.hv0; b.dht = p.dhvt;

@@ -61,6 +61,7 @@ struct FwdParams {
   ChunkOps ops;
   void* Hs;       // [BH][N][DKP][DvP] chunk-start states (T), written by the state walk
   bool states_ready = false;   // Hs (and ht) already hold the walk's result: no walk is run
+  bool ops_ready = false;      // ops.Qs and ops.A already hold the chunk operands: no preparation
   LaunchEvents events;
   SeqView in;     // input sequences read by the launch
   // optional scratch for a segmented state walk (walks.hpp), room for seg_max segments:
@@ -126,7 +127,7 @@ struct GsaParams {
   void* S1s;      // [BH][N][MP][DkP] pass-1 state S1^T at chunk starts        (T)
   void* dS1s;     // [BH][N][MP][DkP] its gradient at chunk ends (backward)    (T)
   void* dZs;      // [BH][N][CP][MP] dZ 2^b, chunk-padded (backward)           (T)
-  ChunkOps ops2;  // pass-2 GLA chunk operands
+  ChunkOps ops2;  // pass-2 GLA chunk operands: Qs and A from gsa_p; KdT and Gam are WdT and Gam
   void *Hs2, *dHs2;
 };
 
