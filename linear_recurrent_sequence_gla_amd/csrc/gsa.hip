@@ -51,9 +51,9 @@ struct GsaCfg {
   static constexpr size_t P_REGION = cmax(2 * ST_C + ST_M, QKT + (size_t)CP * LDM * sizeof(T));
   static constexpr size_t P_BYTES = 2 * FT + P_REGION + (size_t)(M::NSEG * MP + MP + 8) * 4;
   // gsa_pass1_bwd: sB, sW, sdZ, then {sdQK + slices} aliased by {sQK + three fp32 tiles}; the
-  // tail holds the scan totals, Gamma, Z1, the block-max scratch and the dQK diagonal
+  // tail holds the scan totals, Gamma, Z1, the block-max scratch and the dQK and QK diagonals
   static constexpr size_t B_REGION = cmax(QKT + 4 * ST_C + 2 * ST_M, QKT + 3 * FT);
-  static constexpr size_t B_BYTES = 3 * FT + B_REGION + (size_t)(2 * M::NSEG * MP + 2 * MP + 8 + CP) * 4;
+  static constexpr size_t B_BYTES = 3 * FT + B_REGION + (size_t)(2 * M::NSEG * MP + 2 * MP + 8 + 2 * CP) * 4;
 };
 
 // ----------------------------------------------------------------------------- prep
@@ -495,6 +495,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
   float* sZ1 = sGam + MP;
   float* red = sZ1 + MP;
   float* sDiag = red + 8;
+  float* sQKd = sDiag + CP;                                 // diagonal of QK
 
   const int n = blockIdx.x, bh = blockIdx.y, m = p.m, Dk = p.Dk, DkP = p.DkP;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
@@ -759,8 +760,10 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
       if (cb >= NRB) break;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        // the strictly lower part (what the intra products take), the diagonal apart
         const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
-        sQK[r * LDQK + c] = c <= r ? accQK[ch][e] : 0.f;
+        sQK[r * LDQK + c] = c < r ? accQK[ch][e] : 0.f;
+        if (c == r) sQKd[r] = accQK[ch][e];
       }
     }
   }
@@ -779,9 +782,9 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int kk = 32 * kc + 8 * grp + e, r = 16 * rb + col, s = 16 * sb + col;
-            xa[e] = kk < r ? sQK[r * LDQK + kk] : 0.f;                      // QK' row r
+            xa[e] = sQK[r * LDQK + kk];                                     // QK' row r
             xb[e] = sW[kk * LDF + s];                                       // (W Ei)[c][s]
-            xt[e] = kk > r ? sQK[kk * LDQK + r] : 0.f;                      // QK'^T row c = r
+            xt[e] = sQK[kk * LDQK + r];                                     // QK'^T row c = r
             xd[e] = sdZ[kk * LDF + s];                                      // (dZ E)[r'][s]
           }
           mma3(zi, hilo<T>(xa), hilo<T>(xb));
@@ -810,7 +813,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
         const float w = fast ? sW[r * LDF + s] * eb : sW[r * LDF + s];
         sU[r * LDF + s] = dz * znd - w * dw1p;
         sY[r * LDF + s] = w * b1;
-        sD[r * LDF + s] = dw1p + sQK[r * LDQK + r] * dz + b1;
+        sD[r * LDF + s] = dw1p + sQKd[r] * dz + b1;
       }
     }
   }
