@@ -50,10 +50,17 @@ struct GsaCfg {
   // once the Dk loop is done.  Under 80 KB for bf16, so that two workgroups share a CU.
   static constexpr size_t P_REGION = cmax(2 * ST_C + ST_M, QKT + (size_t)CP * LDM * sizeof(T));
   static constexpr size_t P_BYTES = 2 * FT + P_REGION + (size_t)(M::NSEG * MP + MP + 8) * 4;
-  // gsa_pass1_bwd: sB, sW, sdZ, then {sdQK + slices} aliased by {sQK + three fp32 tiles}; the
-  // tail holds the scan totals, Gamma, Z1, the block-max scratch and the dQK and QK diagonals
-  static constexpr size_t B_REGION = cmax(QKT + 4 * ST_C + 2 * ST_M, QKT + 3 * FT);
-  static constexpr size_t B_BYTES = 3 * FT + B_REGION + (size_t)(2 * M::NSEG * MP + 2 * MP + 8 + 2 * CP) * 4;
+  // gsa_pass1_bwd: sB (fp32), the split tiles W Ei and dZ E, then {dQK (T) + slices} aliased by
+  // {split QK + three fp32 tiles}; the tail holds the scan totals, Gamma, Z1, the block-max
+  // scratch and the dQK and QK diagonals.  Split tiles hold hi and lo parts of T (lo only for
+  // 16-bit T) with 32-byte row pads, so that transposing reads of them are free of conflicts.
+  static constexpr bool SPLIT = sizeof(T) == 2;
+  static constexpr int LDH = MP + 2 * V;        // split [CP][MP] tiles
+  static constexpr int LDQ2 = CP + 2 * V;       // split [CP][CP] QK and T dQK tiles
+  static constexpr size_t HPAIR = (SPLIT ? 2 : 1) * (size_t)CP * LDH * sizeof(T);
+  static constexpr size_t QPAIR = (SPLIT ? 2 : 1) * (size_t)CP * LDQ2 * sizeof(T);
+  static constexpr size_t B_REGION = cmax(QPAIR + 4 * ST_C + 2 * ST_M, QPAIR + 3 * FT);
+  static constexpr size_t B_BYTES = FT + 2 * HPAIR + B_REGION + (size_t)(2 * M::NSEG * MP + 2 * MP + 8 + 2 * CP) * 4;
 };
 
 // ----------------------------------------------------------------------------- prep
@@ -457,6 +464,63 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
   tile_out<T>(reinterpret_cast<T*>(p.dZs) + chunk * CP * MP, sZs, CP, MP, LDM);
 }
 
+// An fp32 [rows][ld] tile kept in LDS as hi = T(x) and, for 16-bit T, lo = T(x - hi): the
+// matrix-core operands come from it whole, by rows (ld8) or by columns (transposing reads),
+// with no splitting at the point of use; a single value reads back as hi + lo.
+template <typename T>
+struct SplitTile {
+  static constexpr bool SPLIT = sizeof(T) == 2;
+  T* hi;
+  T* lo;
+  int ld;
+  __device__ __forceinline__ float get(int r, int c) const {
+    float x = to_f32(hi[r * ld + c]);
+    if constexpr (SPLIT) x += to_f32(lo[r * ld + c]);
+    return x;
+  }
+  // the 8 values of row r from column c0 (c0 a multiple of 8)
+  __device__ __forceinline__ void get8(int r, int c0, float (&x)[8]) const {
+    const Frag<T> h = ld8(hi + r * ld + c0);
+    Frag<T> l;
+    if constexpr (SPLIT) l = ld8(lo + r * ld + c0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = to_f32(h.v[e]) + (SPLIT ? to_f32(l.v[e]) : 0.f);
+  }
+  // V consecutive values of row r from column c0, as 16-byte stores
+  template <int NV>
+  __device__ __forceinline__ void put(int r, int c0, const float (&x)[NV]) const {
+    typedef typename V16<T>::type VT;
+    static_assert(NV == V16<T>::N, "one 16-byte vector");
+    VT h, l;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      h[e] = from_f32<T>(x[e]);
+      l[e] = from_f32<T>(x[e] - to_f32(h[e]));
+    }
+    *reinterpret_cast<VT*>(hi + r * ld + c0) = h;
+    if constexpr (SPLIT) *reinterpret_cast<VT*>(lo + r * ld + c0) = l;
+  }
+  __device__ __forceinline__ void put1(int r, int c, float x) const {
+    const T h = from_f32<T>(x);
+    hi[r * ld + c] = h;
+    if constexpr (SPLIT) lo[r * ld + c] = from_f32<T>(x - to_f32(h));
+  }
+  // operand row r, k-run from column k0 (lane layout of ld8)
+  __device__ __forceinline__ HiLo<T> row(int r, int k0) const {
+    HiLo<T> f;
+    f.hi = ld8(hi + r * ld + k0);
+    if constexpr (SPLIT) f.lo = ld8(lo + r * ld + k0);
+    return f;
+  }
+  // operand column n0 + col, k-run down rows k0 .. k0 + 31 (lane layout of ld8_colblk)
+  __device__ __forceinline__ HiLo<T> col(int k0, int n0) const {
+    HiLo<T> f;
+    f.hi = ld8_colblk(hi + k0 * ld + n0, ld);
+    if constexpr (SPLIT) f.lo = ld8_colblk(lo + k0 * ld + n0, ld);
+    return f;
+  }
+};
+
 // ----------------------------------------------------------------------------- pass 1 backward
 // Eight waves: the two waves (rb, 0) and (rb, 1) of 16-row block rb split its column blocks by
 // parity, so each holds half the accumulators and a CU runs two waves per SIMD.  The scans
@@ -469,28 +533,32 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
   using M = ChunkMap<T, MP, CP>;
   constexpr int NT = kP1Threads;
   constexpr int V = M::V, RPS = M::RPS, NSEG = M::NSEG, NCG = M::NCG;
-  constexpr int LDF = G::LDF, LDQK = G::LDQK, LDS = G::LDS, NRB = G::NRB, NSB = G::NSB;
+  constexpr int LDF = G::LDF, LDS = G::LDS, NRB = G::NRB, NSB = G::NSB;
   constexpr int NRH = (NRB + 1) / 2, NSH = NSB / 2, NIH = kDvTile / 32;   // column blocks per half
   typedef typename V16<T>::type VT;
   using SC = SliceRegs<T, CP, NT>;
   using SM = SliceRegs<T, MP, NT>;
   __shared__ __attribute__((aligned(16))) char smem[G::B_BYTES];
+  constexpr int LDH = G::LDH, LDQ2 = G::LDQ2;
   float* sB = reinterpret_cast<float*>(smem);
-  float* sW = sB + CP * LDF;
-  float* sdZ = sW + CP * LDF;
-  char* reg = smem + 3 * G::FT;
-  float* sdQK = reinterpret_cast<float*>(reg);             // until the Dk loop
-  T* sq = reinterpret_cast<T*>(reg + G::QKT);
+  auto split_at = [&](char* base, int rows, int ld) {
+    return SplitTile<T>{reinterpret_cast<T*>(base), reinterpret_cast<T*>(base) + rows * ld, ld};
+  };
+  const SplitTile<T> tW = split_at(smem + G::FT, CP, LDH);                 // W Ei (fast) or W
+  const SplitTile<T> tZ = split_at(smem + G::FT + G::HPAIR, CP, LDH);      // dZ E (fast) or dZ
+  char* reg = smem + G::FT + 2 * G::HPAIR;
+  T* sdQK = reinterpret_cast<T*>(reg);                     // until the Dk loop
+  T* sq = reinterpret_cast<T*>(reg + G::QPAIR);
   T* sk = sq + CP * LDS;
   T* sS1 = sk + CP * LDS;
   T* sdS1 = sS1 + MP * LDS;
   T* sDQ = sdS1 + MP * LDS;
   T* sDK = sDQ + CP * LDS;
-  float* sQK = reinterpret_cast<float*>(reg);              // after the Dk loop
-  float* sU = sQK + CP * LDQK;
+  const SplitTile<T> tQK = split_at(reg, CP, LDQ2);        // after the Dk loop: strictly lower QK
+  float* sU = reinterpret_cast<float*>(reg + G::QPAIR);
   float* sY = sU + CP * LDF;
   float* sD = sY + CP * LDF;
-  float* segtot = reinterpret_cast<float*>(smem + 3 * G::FT + G::B_REGION);
+  float* segtot = reinterpret_cast<float*>(smem + G::FT + 2 * G::HPAIR + G::B_REGION);
   float* sGam = segtot + 2 * NSEG * MP;
   float* sZ1 = sGam + MP;
   float* red = sZ1 + MP;
@@ -542,6 +610,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
     for (int u = 0; u < RPS; ++u) {
       const int r = r0 + u;
       const bool ok = r < len && c0 < m;
+      float xw[V], xz[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const float w = -expm1f(cs.qv[u][e]);
@@ -550,10 +619,12 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
         // product there takes; the exact path reads the raw values
         const float bb = cs.b[u][e];
         sB[r * LDF + c0 + e] = bb;
-        sW[r * LDF + c0 + e] = fast ? w * fast_exp2(-bb) : w;
-        sdZ[r * LDF + c0 + e] = fast ? dz * fast_exp2(bb) : dz;
+        xw[e] = fast ? w * fast_exp2(-bb) : w;
+        xz[e] = fast ? dz * fast_exp2(bb) : dz;
         dsum[u] += p.act == kActSoftmax ? -dz * (1.f - w) : dz * w;
       }
+      tW.put(r, c0, xw);
+      tZ.put(r, c0, xz);
     }
   }
 #pragma unroll
@@ -570,14 +641,19 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
   const bool rbv = rb < NRB;
 
   // (dZ E) on this lane's operand row 16 rb + col: the row operand of dQK and of dq's state term
-  float dze[MP / 32][8];
+  HiLo<T> dze[MP / 32];
   if (rbv) {
 #pragma unroll
     for (int ks = 0; ks < MP / 32; ++ks) {
+      const int r = 16 * rb + col, s0 = 32 * ks + 8 * grp;
+      if (fast) {
+        dze[ks] = tZ.row(r, s0);
+      } else {
+        float x[8];
+        tZ.get8(r, s0, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = 16 * rb + col, s = 32 * ks + 8 * grp + e;
-        dze[ks][e] = fast ? sdZ[r * LDF + s] : sdZ[r * LDF + s] * fast_exp2(sB[r * LDF + s]);
+        for (int e = 0; e < 8; ++e) x[e] *= fast_exp2(sB[r * LDF + s0 + e]);
+        dze[ks] = hilo<T>(x);
       }
     }
   }
@@ -592,15 +668,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
       if (cb <= rb) {
         if (fast) {
 #pragma unroll
-          for (int ks = 0; ks < MP / 32; ++ks) {
-            float xb[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int s = 32 * ks + 8 * grp + e, c = 16 * cb + col;
-              xb[e] = sW[c * LDF + s];                                   // W Ei
-            }
-            mma3(acc, hilo<T>(dze[ks]), hilo<T>(xb));
-          }
+          for (int ks = 0; ks < MP / 32; ++ks) mma3(acc, dze[ks], tW.row(16 * cb + col, 32 * ks + 8 * grp));   // W Ei
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -608,7 +676,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
             float x = 0.f;
             if (c < r)
               for (int s = 0; s < m; ++s)
-                x += sdZ[r * LDF + s] * sW[c * LDF + s] * fast_exp2(sB[r * LDF + s] - sB[c * LDF + s]);
+                x += tZ.get(r, s) * tW.get(c, s) * fast_exp2(sB[r * LDF + s] - sB[c * LDF + s]);
             acc[e] = x;
           }
         }
@@ -616,7 +684,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
-        sdQK[r * LDQK + c] = c < r ? acc[e] : c == r ? sDiag[r] : 0.f;
+        sdQK[r * LDQ2 + c] = from_f32<T>(c < r ? acc[e] : c == r ? sDiag[r] : 0.f);
       }
     }
   }
@@ -628,24 +696,17 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
   if (rbv) {
 #pragma unroll
     for (int kc = 0; kc < CP / 32; ++kc) {
-      float xa[8], xt[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xa[e] = sdQK[(16 * rb + col) * LDQK + 32 * kc + 8 * grp + e];
-        xt[e] = sdQK[(32 * kc + 8 * grp + e) * LDQK + 16 * rb + col];
-      }
-      fA[kc] = frag_of<T>(xa);
-      fT[kc] = frag_of<T>(xt);
+      fA[kc] = ld8(sdQK + (16 * rb + col) * LDQ2 + 32 * kc + 8 * grp);
+      fT[kc] = ld8_colblk(sdQK + (32 * kc) * LDQ2 + 16 * rb, LDQ2);
     }
 #pragma unroll
     for (int ks = 0; ks < MP / 32; ++ks) {
+      const int r = 16 * rb + col, s0 = 32 * ks + 8 * grp;
       float xw[8];
+      tW.get8(r, s0, xw);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int s = 32 * ks + 8 * grp + e, r = 16 * rb + col;
-        xw[e] = fast ? sW[r * LDF + s] * fast_exp2(sGam[s]) : sW[r * LDF + s] * fast_exp2(sGam[s] - sB[r * LDF + s]);
-      }
-      fZ[ks] = frag_of<T>(dze[ks]);
+      for (int e = 0; e < 8; ++e) xw[e] *= fast ? fast_exp2(sGam[s0 + e]) : fast_exp2(sGam[s0 + e] - sB[r * LDF + s0 + e]);
+      fZ[ks] = dze[ks].hi;
       fG[ks] = frag_of<T>(xw);
     }
   }
@@ -752,7 +813,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
     const int idx = tid + NT * j, zs = idx / SM::PER_ROW;
     if (SM::has(j) && idx % SM::PER_ROW == 0) sZ1[zs] = zs < m ? z1[j] * fast_exp2(sGam[zs]) : 0.f;
   }
-  __syncthreads();   // slices and dQK dead: sQK and the dg tiles take their bytes
+  __syncthreads();   // slices and dQK dead: the QK tile and the dg tiles take their bytes
   if (rbv) {
 #pragma unroll
     for (int ch = 0; ch < NRH; ++ch) {
@@ -762,7 +823,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
       for (int e = 0; e < 4; ++e) {
         // the strictly lower part (what the intra products take), the diagonal apart
         const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
-        sQK[r * LDQK + c] = c < r ? accQK[ch][e] : 0.f;
+        tQK.put1(r, c, c < r ? accQK[ch][e] : 0.f);
         if (c == r) sQKd[r] = accQK[ch][e];
       }
     }
@@ -778,17 +839,9 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
       if (fast) {
 #pragma unroll
         for (int kc = 0; kc < CP / 32; ++kc) {
-          float xa[8], xb[8], xt[8], xd[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int kk = 32 * kc + 8 * grp + e, r = 16 * rb + col, s = 16 * sb + col;
-            xa[e] = sQK[r * LDQK + kk];                                     // QK' row r
-            xb[e] = sW[kk * LDF + s];                                       // (W Ei)[c][s]
-            xt[e] = sQK[kk * LDQK + r];                                     // QK'^T row c = r
-            xd[e] = sdZ[kk * LDF + s];                                      // (dZ E)[r'][s]
-          }
-          mma3(zi, hilo<T>(xa), hilo<T>(xb));
-          mma3(w1, hilo<T>(xt), hilo<T>(xd));
+          // QK' row r against (W Ei) column s; QK' column r against (dZ E) column s
+          mma3(zi, tQK.row(16 * rb + col, 32 * kc + 8 * grp), tW.col(32 * kc, 16 * sb));
+          mma3(w1, tQK.col(32 * kc, 16 * rb), tZ.col(32 * kc, 16 * sb));
         }
       }
 #pragma unroll
@@ -803,14 +856,14 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
         } else {
           zip = 0.f;
           dw1p = 0.f;
-          for (int c = 0; c < r; ++c) zip += sQK[r * LDQK + c] * sW[c * LDF + s] * fast_exp2(br - sB[c * LDF + s]);
+          for (int c = 0; c < r; ++c) zip += tQK.get(r, c) * tW.get(c, s) * fast_exp2(br - sB[c * LDF + s]);
           for (int c = r + 1; c < CP; ++c)
-            dw1p += sQK[c * LDQK + r] * sdZ[c * LDF + s] * fast_exp2(sB[c * LDF + s] - br);
+            dw1p += tQK.get(c, r) * tZ.get(c, s) * fast_exp2(sB[c * LDF + s] - br);
         }
         const float znd = zip + eb * accZe[sh][e];
         const float b1 = fast_exp2(sGam[s] - br) * accB1[sh][e];
-        const float dz = fast ? sdZ[r * LDF + s] * eib : sdZ[r * LDF + s];
-        const float w = fast ? sW[r * LDF + s] * eb : sW[r * LDF + s];
+        const float dz = fast ? tZ.get(r, s) * eib : tZ.get(r, s);
+        const float w = fast ? tW.get(r, s) * eb : tW.get(r, s);
         sU[r * LDF + s] = dz * znd - w * dw1p;
         sY[r * LDF + s] = w * b1;
         sD[r * LDF + s] = dw1p + sQKd[r] * dz + b1;
