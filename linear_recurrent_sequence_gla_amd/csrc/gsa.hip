@@ -37,19 +37,13 @@ struct GsaCfg {
   using M = ChunkMap<T, MP, CP>;
   static constexpr int V = 16 / (int)sizeof(T);
   static constexpr int LDF = MP + 4;            // fp32 [CP][MP] tiles
-  static constexpr int LDQK = CP + 4;           // fp32 [CP][CP] tiles
   static constexpr int LDS = kDvTile + V;       // 64-wide T slices
   static constexpr int LDM = MP + V;            // T [CP][MP] staging
   static constexpr int LDC = CP + V;            // T [MP][CP] tiles
   static constexpr int NRB = CP / 16, NSB = MP / 16;
   static constexpr size_t FT = (size_t)CP * LDF * 4;
-  static constexpr size_t QKT = (size_t)CP * LDQK * 4;
   static constexpr size_t ST_C = (size_t)CP * LDS * sizeof(T);
   static constexpr size_t ST_M = (size_t)MP * LDS * sizeof(T);
-  // gsa_p: sB, sW, then the slices (q, k, S1^T), which sQK and the P staging tile replace
-  // once the Dk loop is done.  Under 80 KB for bf16, so that two workgroups share a CU.
-  static constexpr size_t P_REGION = cmax(2 * ST_C + ST_M, QKT + (size_t)CP * LDM * sizeof(T));
-  static constexpr size_t P_BYTES = 2 * FT + P_REGION + (size_t)(M::NSEG * MP + MP + 8) * 4;
   // gsa_pass1_bwd: sB (fp32), the split tiles W Ei and dZ E, then {dQK (T) + slices} aliased by
   // {split QK + three fp32 tiles}; the tail holds the scan totals, Gamma, Z1, the block-max
   // scratch and the dQK and QK diagonals.  Split tiles hold hi and lo parts of T (lo only for
@@ -60,6 +54,11 @@ struct GsaCfg {
   static constexpr size_t HPAIR = (SPLIT ? 2 : 1) * (size_t)CP * LDH * sizeof(T);
   static constexpr size_t QPAIR = (SPLIT ? 2 : 1) * (size_t)CP * LDQ2 * sizeof(T);
   static constexpr size_t B_REGION = cmax(QPAIR + 4 * ST_C + 2 * ST_M, QPAIR + 3 * FT);
+  // gsa_p: sB (fp32), the split tile W Ei, then the slices (q, k, S1^T), which the split QK
+  // tile and the P staging tile replace once the Dk loop is done.  Under 80 KB for bf16 at
+  // m = 64, so that two workgroups share a CU.
+  static constexpr size_t P_REGION = cmax(2 * ST_C + ST_M, QPAIR + (size_t)CP * LDM * sizeof(T));
+  static constexpr size_t P_BYTES = FT + HPAIR + P_REGION + (size_t)(M::NSEG * MP + MP + 8) * 4;
   static constexpr size_t B_BYTES = FT + 2 * HPAIR + B_REGION + (size_t)(2 * M::NSEG * MP + 2 * MP + 8 + 2 * CP) * 4;
 };
 
@@ -135,6 +134,63 @@ struct SliceRegs {
   }
 };
 
+// An fp32 [rows][ld] tile kept in LDS as hi = T(x) and, for 16-bit T, lo = T(x - hi): the
+// matrix-core operands come from it whole, by rows (ld8) or by columns (transposing reads),
+// with no splitting at the point of use; a single value reads back as hi + lo.
+template <typename T>
+struct SplitTile {
+  static constexpr bool SPLIT = sizeof(T) == 2;
+  T* hi;
+  T* lo;
+  int ld;
+  __device__ __forceinline__ float get(int r, int c) const {
+    float x = to_f32(hi[r * ld + c]);
+    if constexpr (SPLIT) x += to_f32(lo[r * ld + c]);
+    return x;
+  }
+  // the 8 values of row r from column c0 (c0 a multiple of 8)
+  __device__ __forceinline__ void get8(int r, int c0, float (&x)[8]) const {
+    const Frag<T> h = ld8(hi + r * ld + c0);
+    Frag<T> l;
+    if constexpr (SPLIT) l = ld8(lo + r * ld + c0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = to_f32(h.v[e]) + (SPLIT ? to_f32(l.v[e]) : 0.f);
+  }
+  // V consecutive values of row r from column c0, as 16-byte stores
+  template <int NV>
+  __device__ __forceinline__ void put(int r, int c0, const float (&x)[NV]) const {
+    typedef typename V16<T>::type VT;
+    static_assert(NV == V16<T>::N, "one 16-byte vector");
+    VT h, l;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      h[e] = from_f32<T>(x[e]);
+      l[e] = from_f32<T>(x[e] - to_f32(h[e]));
+    }
+    *reinterpret_cast<VT*>(hi + r * ld + c0) = h;
+    if constexpr (SPLIT) *reinterpret_cast<VT*>(lo + r * ld + c0) = l;
+  }
+  __device__ __forceinline__ void put1(int r, int c, float x) const {
+    const T h = from_f32<T>(x);
+    hi[r * ld + c] = h;
+    if constexpr (SPLIT) lo[r * ld + c] = from_f32<T>(x - to_f32(h));
+  }
+  // operand row r, k-run from column k0 (lane layout of ld8)
+  __device__ __forceinline__ HiLo<T> row(int r, int k0) const {
+    HiLo<T> f;
+    f.hi = ld8(hi + r * ld + k0);
+    if constexpr (SPLIT) f.lo = ld8(lo + r * ld + k0);
+    return f;
+  }
+  // operand column n0 + col, k-run down rows k0 .. k0 + 31 (lane layout of ld8_colblk)
+  __device__ __forceinline__ HiLo<T> col(int k0, int n0) const {
+    HiLo<T> f;
+    f.hi = ld8_colblk(hi + k0 * ld + n0, ld);
+    if constexpr (SPLIT) f.lo = ld8_colblk(lo + k0 * ld + n0, ld);
+    return f;
+  }
+};
+
 // ----------------------------------------------------------------------------- pass 1 forward
 // Z = E * (QK (W Ei) + Q S1_n), P = softmax_slots(Z), written as the [L][m] queries of pass 2,
 // together with pass 2's chunk operands, which are what the GLA preparation would form from
@@ -147,19 +203,22 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
   using G = GsaCfg<T, MP, CP>;
   using M = ChunkMap<T, MP, CP>;
   constexpr int V = M::V, RPS = M::RPS;
-  constexpr int LDF = G::LDF, LDQK = G::LDQK, LDS = G::LDS, LDM = G::LDM, LDC = G::LDC, NRB = G::NRB, NSB = G::NSB;
+  constexpr int LDF = G::LDF, LDS = G::LDS, LDM = G::LDM, LDC = G::LDC, NRB = G::NRB, NSB = G::NSB;
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[G::P_BYTES];
   float* sB = reinterpret_cast<float*>(smem);
-  float* sW = sB + CP * LDF;                  // Ws = W 2^-b (fast) or W (exact path)
-  char* reg = smem + 2 * G::FT;
+  auto split_at = [&](char* base, int rows, int ld) {
+    return SplitTile<T>{reinterpret_cast<T*>(base), reinterpret_cast<T*>(base) + rows * ld, ld};
+  };
+  const SplitTile<T> tW = split_at(smem + G::FT, CP, G::LDH);   // Ws = W 2^-b (fast) or W (exact path)
+  char* reg = smem + G::FT + G::HPAIR;
   T* sq = reinterpret_cast<T*>(reg);          // during the Dk loop
   T* sk = sq + CP * LDS;
   T* sS1 = sk + CP * LDS;
-  float* sQK = reinterpret_cast<float*>(reg);  // after it
-  T* sP = reinterpret_cast<T*>(reg + G::QKT);
+  const SplitTile<T> tQK = split_at(reg, CP, G::LDQ2);   // after it: masked QK
+  T* sP = reinterpret_cast<T*>(reg + G::QPAIR);
   T* sA2 = reinterpret_cast<T*>(reg);          // once the scores are formed: A2 [CP][LDC]
-  float* segtot = reinterpret_cast<float*>(smem + 2 * G::FT + G::P_REGION);
+  float* segtot = reinterpret_cast<float*>(smem + G::FT + G::HPAIR + G::P_REGION);
   float* sGam = segtot + M::NSEG * MP;
   float* red = sGam + MP;
 
@@ -185,13 +244,15 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
     const int c0 = cs.cg * V, r0 = cs.seg * RPS;
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
+      float xw[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const float bb = cs.b[u][e];
         const float w = -expm1f(cs.qv[u][e]);
         sB[(r0 + u) * LDF + c0 + e] = bb;
-        sW[(r0 + u) * LDF + c0 + e] = fast ? w * fast_exp2(-bb) : w;
+        xw[e] = fast ? w * fast_exp2(-bb) : w;
       }
+      tW.put(r0 + u, c0, xw);
     }
   }
   const int rb = wave;                        // this wave's 16 chunk rows
@@ -225,14 +286,14 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
       }
     }
   }
-  __syncthreads();   // sQK and sP take the slices' bytes
+  __syncthreads();   // the QK tile and sP take the slices' bytes
   if (rbv) {
 #pragma unroll
     for (int cb = 0; cb < NRB; ++cb) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rb + 4 * grp + e, c = 16 * cb + col;
-        sQK[r * LDQK + c] = c <= r ? accQK[cb][e] : 0.f;
+        tQK.put1(r, c, c <= r ? accQK[cb][e] : 0.f);
       }
     }
   }
@@ -246,15 +307,7 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
       for (int sb = 0; sb < NSB; ++sb) {
         f32x4 acc = zero4();
 #pragma unroll
-        for (int kc = 0; kc < CP / 32; ++kc) {
-          float xa[8], xb[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            xa[e] = sQK[(16 * rb + col) * LDQK + 32 * kc + 8 * grp + e];
-            xb[e] = sW[(32 * kc + 8 * grp + e) * LDF + 16 * sb + col];
-          }
-          mma3(acc, hilo<T>(xa), hilo<T>(xb));
-        }
+        for (int kc = 0; kc < CP / 32; ++kc) mma3(acc, tQK.row(16 * rb + col, 32 * kc + 8 * grp), tW.col(32 * kc, 16 * sb));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * rb + 4 * grp + e, s = 16 * sb + col;
@@ -269,7 +322,7 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
           const int r = 16 * rb + 4 * grp + e, s = 16 * sb + col;
           const float br = sB[r * LDF + s];
           float zi = 0.f;
-          for (int c = 0; c <= r; ++c) zi += sQK[r * LDQK + c] * sW[c * LDF + s] * fast_exp2(br - sB[c * LDF + s]);
+          for (int c = 0; c <= r; ++c) zi += tQK.get(r, c) * tW.get(c, s) * fast_exp2(br - sB[c * LDF + s]);
           z[sb][e] = zi + fast_exp2(br) * accZe[sb][e];
         }
       }
@@ -319,7 +372,7 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
       }
     }
   }
-  __syncthreads();   // P staged; sQK dead
+  __syncthreads();   // P staged; the QK tile dead
 
   // ---- A2 (rows past the chunk's end are zero, as are columns there: w = 0)
   if (rbv) {
@@ -342,12 +395,7 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
       if (cb <= rb) {
         if (fast) {
 #pragma unroll
-          for (int ks = 0; ks < MP / 32; ++ks) {
-            float xb[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xb[e] = sW[(16 * cb + col) * LDF + 32 * ks + 8 * grp + e];   // W Ei
-            mma3(acc, fpe[ks], hilo<T>(xb));
-          }
+          for (int ks = 0; ks < MP / 32; ++ks) mma3(acc, fpe[ks], tW.row(16 * cb + col, 32 * ks + 8 * grp));   // W Ei
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -355,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
             float x = 0.f;
             if (c <= r)
               for (int sl = 0; sl < m; ++sl)
-                x += to_f32(sP[r * LDM + sl]) * sW[c * LDF + sl] * fast_exp2(sB[r * LDF + sl] - sB[c * LDF + sl]);
+                x += to_f32(sP[r * LDM + sl]) * tW.get(c, sl) * fast_exp2(sB[r * LDF + sl] - sB[c * LDF + sl]);
             acc[e] = x;
           }
         }
@@ -463,63 +511,6 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
   __syncthreads();
   tile_out<T>(reinterpret_cast<T*>(p.dZs) + chunk * CP * MP, sZs, CP, MP, LDM);
 }
-
-// An fp32 [rows][ld] tile kept in LDS as hi = T(x) and, for 16-bit T, lo = T(x - hi): the
-// matrix-core operands come from it whole, by rows (ld8) or by columns (transposing reads),
-// with no splitting at the point of use; a single value reads back as hi + lo.
-template <typename T>
-struct SplitTile {
-  static constexpr bool SPLIT = sizeof(T) == 2;
-  T* hi;
-  T* lo;
-  int ld;
-  __device__ __forceinline__ float get(int r, int c) const {
-    float x = to_f32(hi[r * ld + c]);
-    if constexpr (SPLIT) x += to_f32(lo[r * ld + c]);
-    return x;
-  }
-  // the 8 values of row r from column c0 (c0 a multiple of 8)
-  __device__ __forceinline__ void get8(int r, int c0, float (&x)[8]) const {
-    const Frag<T> h = ld8(hi + r * ld + c0);
-    Frag<T> l;
-    if constexpr (SPLIT) l = ld8(lo + r * ld + c0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = to_f32(h.v[e]) + (SPLIT ? to_f32(l.v[e]) : 0.f);
-  }
-  // V consecutive values of row r from column c0, as 16-byte stores
-  template <int NV>
-  __device__ __forceinline__ void put(int r, int c0, const float (&x)[NV]) const {
-    typedef typename V16<T>::type VT;
-    static_assert(NV == V16<T>::N, "one 16-byte vector");
-    VT h, l;
-#pragma unroll
-    for (int e = 0; e < NV; ++e) {
-      h[e] = from_f32<T>(x[e]);
-      l[e] = from_f32<T>(x[e] - to_f32(h[e]));
-    }
-    *reinterpret_cast<VT*>(hi + r * ld + c0) = h;
-    if constexpr (SPLIT) *reinterpret_cast<VT*>(lo + r * ld + c0) = l;
-  }
-  __device__ __forceinline__ void put1(int r, int c, float x) const {
-    const T h = from_f32<T>(x);
-    hi[r * ld + c] = h;
-    if constexpr (SPLIT) lo[r * ld + c] = from_f32<T>(x - to_f32(h));
-  }
-  // operand row r, k-run from column k0 (lane layout of ld8)
-  __device__ __forceinline__ HiLo<T> row(int r, int k0) const {
-    HiLo<T> f;
-    f.hi = ld8(hi + r * ld + k0);
-    if constexpr (SPLIT) f.lo = ld8(lo + r * ld + k0);
-    return f;
-  }
-  // operand column n0 + col, k-run down rows k0 .. k0 + 31 (lane layout of ld8_colblk)
-  __device__ __forceinline__ HiLo<T> col(int k0, int n0) const {
-    HiLo<T> f;
-    f.hi = ld8_colblk(hi + k0 * ld + n0, ld);
-    if constexpr (SPLIT) f.lo = ld8_colblk(lo + k0 * ld + n0, ld);
-    return f;
-  }
-};
 
 // ----------------------------------------------------------------------------- pass 1 backward
 // Eight waves: the two waves (rb, 0) and (rb, 1) of 16-row block rb split its column blocks by
