@@ -438,6 +438,18 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
       }
       __syncthreads();
     }
+    // GSA's pass 2 with the read-out's backward fused: the read-out's input (fp32) for the
+    // epilogue, in flight through the intra phase
+    f32x4 rdl[RPS][V / 4];
+    if (p.dz) {
+      const int cc = (cs.active && c0 < kvalid) ? c0 : 0;
+#pragma unroll
+      for (int u = 0; u < RPS; ++u) {
+        const float* src = p.rd + qbase + (size_t)min(r0 + u, len - 1) * Dk + cc;
+#pragma unroll
+        for (int e4 = 0; e4 < V / 4; ++e4) rdl[u][e4] = *reinterpret_cast<const f32x4*>(src + 4 * e4);
+      }
+    }
     {  // Z_n = 2^Gamma rowsum(dH_{n+1} * H_n): reduce over the lanes that staged one state row
       constexpr int PER_ROW = kDvTile / V;
 #pragma unroll
@@ -603,8 +615,38 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
           up[u][e] = qv * dqn[u][e] - kv * dkp[u][e];
           uk[u][e] = kv * bk;
         }
+        if (p.dz) {
+          // the read-out's backward: dq here is dP, the gradient of the read-out's output, and
+          // dZ = P (dP - <dP, P>) over the row's slots for the softmax (the row's channel groups
+          // are NCG consecutive lanes), else f'(Z) dP; dZ 2^b also goes out chunk-padded for
+          // the pass-1 reverse walk
+          const bool ok = r < len && c0 < kvalid;
+          float rv[V], sdot = 0.f;
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            rv[e] = ok ? rdl[u][e >> 2][e & 3] : 0.f;
+            sdot += rv[e] * dqf[e];
+          }
+#pragma unroll
+          for (int o = 1; o < M::NCG; o <<= 1) sdot += __shfl_xor(sdot, o, 64);
+          float dzv[V];
+          VT zs;
+#pragma unroll
+          for (int e = 0; e < V; ++e) {
+            dzv[e] = p.act == kActSoftmax ? rv[e] * (dqf[e] - sdot) : gsa_read_grad(rv[e], dqf[e], p.act);
+            zs[e] = from_f32<T>(dzv[e] * fast_exp2(cs.b[u][e]));
+          }
+          *reinterpret_cast<VT*>(reinterpret_cast<T*>(p.dzs) + (chunk * CP + r) * DKP + ch0 + c0) = zs;
+          if (ok) {
+            float* d = p.dz + qbase + (size_t)r * Dk + c0;
+#pragma unroll
+            for (int e = 0; e < V; e += 4) *reinterpret_cast<f32x4*>(d + e) = f32x4{dzv[e], dzv[e + 1], dzv[e + 2], dzv[e + 3]};
+          }
+        }
         if (r < len && c0 < kvalid) {
-          if (p.dq32) {
+          if (p.dz) {
+            // dq itself is not kept
+          } else if (p.dq32) {
             float* d32 = p.dq32 + qbase + (size_t)r * Dk + c0;
 #pragma unroll
             for (int e = 0; e < V; e += 4) *reinterpret_cast<f32x4*>(d32 + e) = f32x4{dqf[e], dqf[e + 1], dqf[e + 2], dqf[e + 3]};
@@ -871,6 +913,22 @@ struct BwdPlan {
                              walk_fits<T, DKP, CP>() &&
                              (FUSED || BwdDvCfg<T, DKP, CP>::BYTES <= kMaxLds);
 };
+
+template <typename T, int DKP, int CP>
+constexpr int bwd_key_slices() {
+  return BwdPlan<T, DKP, CP>::OK ? DKP / BwdPlan<T, DKP, CP>::DKS : 0;
+}
+
+int gla_bwd_key_slices(int esize, int DKP, int CP) {
+#define GLA_BWD_SLICES(TT, D, C_) \
+  if (esize == (int)sizeof(TT) && DKP == D && CP == C_) return bwd_key_slices<TT, D, C_>();
+  GLA_BWD_SLICES(bf16, 32, 32) GLA_BWD_SLICES(bf16, 32, 64) GLA_BWD_SLICES(bf16, 64, 32)
+  GLA_BWD_SLICES(bf16, 64, 64) GLA_BWD_SLICES(bf16, 128, 32) GLA_BWD_SLICES(bf16, 128, 64)
+  GLA_BWD_SLICES(float, 32, 32) GLA_BWD_SLICES(float, 32, 64) GLA_BWD_SLICES(float, 64, 32)
+  GLA_BWD_SLICES(float, 64, 64) GLA_BWD_SLICES(float, 128, 32) GLA_BWD_SLICES(float, 128, 64)
+#undef GLA_BWD_SLICES
+  return 0;
+}
 
 template <typename T, int DKP, int CP>
 hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {

@@ -996,12 +996,21 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
     BwdParams b;
     b.q = p.P; b.k = p.W; b.v = p.v; b.g = p.g; b.do_ = p.do_; b.h0 = p.hv0; b.dht = p.dhvt;
     b.dq = p.dP; b.dk = p.dW2; b.dv = p.dv; b.dg = p.dg2; b.dh0 = p.dhv0;
-    b.dq32 = p.dP;     // dP stays fp32 for the read-out's backward
     b.BH = p.BH; b.L = p.L; b.Dk = p.m; b.Dv = p.Dv; b.C = p.C; b.N = p.N;
     b.ops = p.ops2; b.Hs = p.Hs2; b.dHs = p.dHs2; b.saved = true; b.events = LaunchEvents{nullptr, 0};
+    // the read-out's backward needs each row's whole slot width: in the chunk kernel's epilogue
+    // when one tile holds it, else in its own kernel on the fp32 dP
+    const bool fuse_dz = gla_bwd_key_slices((int)sizeof(T), MP, CP) == 1;
+    if (fuse_dz) {
+      b.rd = p.Pf; b.dz = p.dZ; b.dzs = p.dZs; b.act = p.act;
+    } else {
+      b.dq32 = p.dP;   // dP stays fp32 for the read-out's backward
+    }
     if ((e = launch_gla_bwd<T, MP, CP>(b, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((gsa_dz_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!fuse_dz) {
+      hipLaunchKernelGGL((gsa_dz_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(256), 0, s, p);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     WalkIO w1r{p.dZs, p.q, p.Gam, p.dS1s, p.dhkt, p.dhk0, p.m, p.Dk, p.L, p.C, p.N, 1};
     if ((e = launch_walk_reverse<T, MP, CP>(w1r, p.BH, s)) != hipSuccess) return e;
     const int ntk = p.DkP / kDvTile;

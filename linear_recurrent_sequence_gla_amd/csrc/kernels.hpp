@@ -99,6 +99,14 @@ struct BwdParams {
   // if set, dq goes here in fp32 [BH][L][Dk] instead of to dq: GSA's pass 2, whose dq is the
   // gradient of the read-out, which the softmax's Jacobian then reduces with cancellation
   float* dq32 = nullptr;
+  // if set (GSA's pass 2 with its whole slot width in one chunk tile: gla_bwd_key_slices == 1),
+  // the read-out's backward runs in the chunk kernel's epilogue: from dq = dP and the fp32
+  // read-out input rd (P for the softmax, the scores Z otherwise) it writes dz = dZ (fp32
+  // [BH][L][Dk]) and dzs = dZ 2^b ([BH][N][CP][DKP], T, chunk-padded), and no dq
+  const float* rd = nullptr;
+  float* dz = nullptr;
+  void* dzs = nullptr;
+  int act = 0;
 };
 
 // Gated slot attention: pass 1 runs on its own kernels, pass 2 on the GLA kernels.
@@ -150,6 +158,9 @@ template <typename T, int DKP, int CP>
 hipError_t launch_gla_fwd_batches(const FwdParams* ps, int nb, hipStream_t s);
 template <typename T, int DKP, int CP>
 hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s);
+// key-width slices of the backward's chunk tiles for a (type size, padded key width, padded
+// chunk) configuration; 0 = unsupported
+int gla_bwd_key_slices(int esize, int DKP, int CP);
 template <typename T>
 hipError_t launch_gla_decode(const DecodeParams& p, hipStream_t s);
 
