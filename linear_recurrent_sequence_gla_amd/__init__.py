@@ -40,7 +40,8 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-lib_path = os.path.join(_HERE, "libgla_amd.so")
+# GLA_AMD_LIB: another build of the same library (the host-AddressSanitizer one, for instance)
+lib_path = os.environ.get("GLA_AMD_LIB") or os.path.join(_HERE, "libgla_amd.so")
 
 GLA_F32, GLA_BF16 = 0, 1
 _DT = {torch.float32: GLA_F32, torch.bfloat16: GLA_BF16}
