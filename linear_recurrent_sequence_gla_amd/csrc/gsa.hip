@@ -60,6 +60,9 @@ struct GsaCfg {
   static constexpr size_t P_REGION = cmax(2 * ST_C + ST_M, QPAIR + (size_t)CP * LDM * sizeof(T));
   static constexpr size_t P_BYTES = FT + HPAIR + P_REGION + (size_t)(M::NSEG * MP + MP + 8) * 4;
   static constexpr size_t B_BYTES = FT + 2 * HPAIR + B_REGION + (size_t)(2 * M::NSEG * MP + 2 * MP + 8 + 2 * CP) * 4;
+  // the pass-1 backward walks its tiles in a persistent loop, carrying the next tile's gates
+  // and dZ (more slots: one tile per workgroup, where the loop's registers would spill)
+  static constexpr bool P1_PERSIST = MP <= 64;
 };
 
 // ----------------------------------------------------------------------------- prep
@@ -115,20 +118,21 @@ struct SliceRegs {
   typedef typename V16<T>::type VT;
   VT x[N];
   // item j of this thread exists (always, when the items divide evenly over the threads)
-  __device__ __forceinline__ static bool has(int j) { return ITEMS % NT == 0 || (int)threadIdx.x + NT * j < ITEMS; }
-  __device__ __forceinline__ void load(const T* src, size_t ld, int nrows, int col0, int ncols) {
+  // tid: the thread's index (threadIdx.x, or an opaque copy of it in a persistent loop)
+  __device__ __forceinline__ static bool has(int j, int tid = threadIdx.x) { return ITEMS % NT == 0 || tid + NT * j < ITEMS; }
+  __device__ __forceinline__ void load(const T* src, size_t ld, int nrows, int col0, int ncols, int tid = threadIdx.x) {
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const int idx = min((int)threadIdx.x + NT * j, ITEMS - 1), r = idx / PER_ROW;
+      const int idx = min(tid + NT * j, ITEMS - 1), r = idx / PER_ROW;
       const int c = col0 + (idx % PER_ROW) * V;
       x[j] = *reinterpret_cast<const VT*>(src + (size_t)min(r, nrows - 1) * ld + min(c, ncols - V));
     }
   }
-  __device__ __forceinline__ void store(T* dst, int lds, int nrows, int col0, int ncols) const {
+  __device__ __forceinline__ void store(T* dst, int lds, int nrows, int col0, int ncols, int tid = threadIdx.x) const {
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const int idx = threadIdx.x + NT * j, r = idx / PER_ROW, c = (idx % PER_ROW) * V;
-      if (has(j))
+      const int idx = tid + NT * j, r = idx / PER_ROW, c = (idx % PER_ROW) * V;
+      if (has(j, tid))
         *reinterpret_cast<VT*>(dst + r * lds + c) = (r < nrows && col0 + c < ncols) ? x[j] : zero_vec<T>();
     }
   }
@@ -183,10 +187,10 @@ struct SplitTile {
     return f;
   }
   // operand column n0 + col, k-run down rows k0 .. k0 + 31 (lane layout of ld8_colblk)
-  __device__ __forceinline__ HiLo<T> col(int k0, int n0) const {
+  __device__ __forceinline__ HiLo<T> col(int k0, int n0, int lane = threadIdx.x & 63) const {
     HiLo<T> f;
-    f.hi = ld8_colblk(hi + k0 * ld + n0, ld);
-    if constexpr (SPLIT) f.lo = ld8_colblk(lo + k0 * ld + n0, ld);
+    f.hi = ld8_colblk(hi + k0 * ld + n0, ld, lane);
+    if constexpr (SPLIT) f.lo = ld8_colblk(lo + k0 * ld + n0, ld, lane);
     return f;
   }
 };
@@ -519,7 +523,7 @@ __global__ __launch_bounds__(256) void gsa_dz_kernel(GsaParams p) {
 constexpr int kP1Threads = 512;
 
 template <typename T, int MP, int CP>
-__global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, int ntk) {
+__global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, int ntk, int ntiles) {
   using G = GsaCfg<T, MP, CP>;
   using M = ChunkMap<T, MP, CP>;
   constexpr int NT = kP1Threads;
@@ -556,41 +560,58 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
   float* sDiag = red + 8;
   float* sQKd = sDiag + CP;                                 // diagonal of QK
 
-  const int n = blockIdx.x, bh = blockIdx.y, m = p.m, Dk = p.Dk, DkP = p.DkP;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int m = p.m, Dk = p.Dk, DkP = p.DkP;
+
+  // The grid is persistent: workgroup w takes tiles w, w + gridDim.x, ... (tile = chunk
+  // tile % N of sequence tile / N).  A tile's gates and dZ, which its gate scan and first phase
+  // wait for, go out during the previous tile's gate-gradient phase; past the last tile they
+  // still go out, unconditionally, but read one cached row of that tile.
+  ChunkScan<T, MP, CP, false> cs;
+  f32x4 dzv[RPS][V / 4];                 // dZ in the scan's layout
+  auto issue = [&](int tt, bool past, int tid) {
+    const int nn = tt % p.N, rr0 = nn * p.C;
+    const int ll = past ? 1 : min(p.C, p.L - rr0);
+    const size_t gb = ((size_t)(tt / p.N) * p.L + rr0) * m;
+    const T* g0 = reinterpret_cast<const T*>(p.g) + gb;
+    cs.load(g0, g0, g0, m, m, ll, tid);
+    const int cc = (cs.active && cs.cg * V < m) ? cs.cg * V : 0;
+#pragma unroll
+    for (int u = 0; u < RPS; ++u) {
+      const float* src = p.dZ + gb + (size_t)min(cs.seg * RPS + u, ll - 1) * m + cc;
+#pragma unroll
+      for (int e4 = 0; e4 < V / 4; ++e4) dzv[u][e4] = *reinterpret_cast<const f32x4*>(src + 4 * e4);
+    }
+  };
+  // With more than 64 slots the persistent loop would spill: there each workgroup takes one
+  // tile (the launch gives one workgroup per tile) and the loop body runs once.
+  constexpr bool PERSIST = GsaCfg<T, MP, CP>::P1_PERSIST;
+  int tile_t = blockIdx.x;
+  issue(tile_t, false, threadIdx.x);
+  for (;;) {
+  // the thread index through an opaque move, once per tile: per-lane addresses are then formed
+  // inside each tile instead of being hoisted out of the loop and held across it
+  const int tid = opaque_thread_index(), wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int tile_n = tile_t + gridDim.x;
+  const int n = tile_t % p.N, bh = tile_t / p.N;
   const int row0 = n * p.C, len = min(p.C, p.L - row0);
   const size_t chunk = (size_t)bh * p.N + n;
   const size_t gbase = ((size_t)bh * p.L + row0) * m;
   const size_t kbase = ((size_t)bh * p.L + row0) * Dk;
-  const T* gg = reinterpret_cast<const T*>(p.g) + gbase;
   const T* qg = reinterpret_cast<const T*>(p.q) + kbase;
   const T* kg = reinterpret_cast<const T*>(p.k) + kbase;
   const T* s1 = reinterpret_cast<const T*>(p.S1s) + chunk * MP * DkP;
   const T* ds1 = reinterpret_cast<const T*>(p.dS1s) + chunk * MP * DkP;
   T* dqg = reinterpret_cast<T*>(p.dq) + kbase;
   T* dkg = reinterpret_cast<T*>(p.dk) + kbase;
-
-  ChunkScan<T, MP, CP, false> cs;
-  cs.load(gg, gg, gg, m, m, len);
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
-  // dZ in the scan's layout and the first Dk slice: in flight while the gates are scanned
-  f32x4 dzv[RPS][V / 4];
-  {
-    const int cc = (cs.active && c0 < m) ? c0 : 0;
-#pragma unroll
-    for (int u = 0; u < RPS; ++u) {
-      const float* src = p.dZ + gbase + (size_t)min(r0 + u, len - 1) * m + cc;
-#pragma unroll
-      for (int e4 = 0; e4 < V / 4; ++e4) dzv[u][e4] = *reinterpret_cast<const f32x4*>(src + 4 * e4);
-    }
-  }
+  // the first Dk slice: in flight while the gates are scanned
   SC rq, rk;
   SM rs, rd;
-  rq.load(qg, Dk, len, 0, Dk);
-  rk.load(kg, Dk, len, 0, Dk);
-  rs.load(s1, DkP, MP, 0, DkP);
-  rd.load(ds1, DkP, MP, 0, DkP);
-  const bool fast = cs.finish(segtot, sGam, red) <= kSpanLimit;
+  rq.load(qg, Dk, len, 0, Dk, tid);
+  rk.load(kg, Dk, len, 0, Dk, tid);
+  rs.load(s1, DkP, MP, 0, DkP, tid);
+  rd.load(ds1, DkP, MP, 0, DkP, tid);
+  const bool fast = cs.finish(segtot, sGam, red, tid) <= kSpanLimit;
   // diagonal of dQK, sum_s dZ w per row.  For the softmax it equals -sum_s dZ alpha, since
   // sum_s dZ = 0 (its Jacobian); that form scales with alpha instead of cancelling.
   float dsum[RPS];
@@ -688,7 +709,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
 #pragma unroll
     for (int kc = 0; kc < CP / 32; ++kc) {
       fA[kc] = ld8(sdQK + (16 * rb + col) * LDQ2 + 32 * kc + 8 * grp);
-      fT[kc] = ld8_colblk(sdQK + (32 * kc) * LDQ2 + 16 * rb, LDQ2);
+      fT[kc] = ld8_colblk(sdQK + (32 * kc) * LDQ2 + 16 * rb, LDQ2, lane);
     }
 #pragma unroll
     for (int ks = 0; ks < MP / 32; ++ks) {
@@ -714,22 +735,22 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
   for (int j = 0; j < SM::N; ++j) z1[j] = 0.f;
   for (int ds = 0; ds < ntk; ++ds) {
     __syncthreads();
-    rq.store(sq, LDS, len, ds * kDvTile, Dk);
-    rk.store(sk, LDS, len, ds * kDvTile, Dk);
-    rs.store(sS1, LDS, MP, ds * kDvTile, DkP);
-    rd.store(sdS1, LDS, MP, ds * kDvTile, DkP);
+    rq.store(sq, LDS, len, ds * kDvTile, Dk, tid);
+    rk.store(sk, LDS, len, ds * kDvTile, Dk, tid);
+    rs.store(sS1, LDS, MP, ds * kDvTile, DkP, tid);
+    rd.store(sdS1, LDS, MP, ds * kDvTile, DkP, tid);
 #pragma unroll
     for (int j = 0; j < SM::N; ++j) {
-      if (SM::has(j)) {
+      if (SM::has(j, tid)) {
 #pragma unroll
         for (int e = 0; e < V; ++e) z1[j] += to_f32(rs.x[j][e]) * to_f32(rd.x[j][e]);
       }
     }
     if (ds + 1 < ntk) {
-      rq.load(qg, Dk, len, (ds + 1) * kDvTile, Dk);
-      rk.load(kg, Dk, len, (ds + 1) * kDvTile, Dk);
-      rs.load(s1, DkP, MP, (ds + 1) * kDvTile, DkP);
-      rd.load(ds1, DkP, MP, (ds + 1) * kDvTile, DkP);
+      rq.load(qg, Dk, len, (ds + 1) * kDvTile, Dk, tid);
+      rk.load(kg, Dk, len, (ds + 1) * kDvTile, Dk, tid);
+      rs.load(s1, DkP, MP, (ds + 1) * kDvTile, DkP, tid);
+      rd.load(ds1, DkP, MP, (ds + 1) * kDvTile, DkP, tid);
     }
     __syncthreads();
     if (rbv) {
@@ -756,13 +777,13 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
         f32x4 aq = zero4(), ak = zero4();
 #pragma unroll
         for (int kc = 0; kc < CP / 32; ++kc) {
-          mma(aq, fA[kc], ld8_colblk(sk + (32 * kc) * LDS + 16 * ib, LDS));
-          mma(ak, fT[kc], ld8_colblk(sq + (32 * kc) * LDS + 16 * ib, LDS));
+          mma(aq, fA[kc], ld8_colblk(sk + (32 * kc) * LDS + 16 * ib, LDS, lane));
+          mma(ak, fT[kc], ld8_colblk(sq + (32 * kc) * LDS + 16 * ib, LDS, lane));
         }
 #pragma unroll
         for (int ks = 0; ks < MP / 32; ++ks) {
-          mma(aq, fZ[ks], ld8_colblk(sS1 + (32 * ks) * LDS + 16 * ib, LDS));
-          mma(ak, fG[ks], ld8_colblk(sdS1 + (32 * ks) * LDS + 16 * ib, LDS));
+          mma(aq, fZ[ks], ld8_colblk(sS1 + (32 * ks) * LDS + 16 * ib, LDS, lane));
+          mma(ak, fG[ks], ld8_colblk(sdS1 + (32 * ks) * LDS + 16 * ib, LDS, lane));
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -802,7 +823,7 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
 #pragma unroll
     for (int o = 1; o < SM::PER_ROW; o <<= 1) z1[j] += __shfl_xor(z1[j], o, 64);
     const int idx = tid + NT * j, zs = idx / SM::PER_ROW;
-    if (SM::has(j) && idx % SM::PER_ROW == 0) sZ1[zs] = zs < m ? z1[j] * fast_exp2(sGam[zs]) : 0.f;
+    if (SM::has(j, tid) && idx % SM::PER_ROW == 0) sZ1[zs] = zs < m ? z1[j] * fast_exp2(sGam[zs]) : 0.f;
   }
   __syncthreads();   // slices and dQK dead: the QK tile and the dg tiles take their bytes
   if (rbv) {
@@ -831,8 +852,8 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
 #pragma unroll
         for (int kc = 0; kc < CP / 32; ++kc) {
           // QK' row r against (W Ei) column s; QK' column r against (dZ E) column s
-          mma3(zi, tQK.row(16 * rb + col, 32 * kc + 8 * grp), tW.col(32 * kc, 16 * sb));
-          mma3(w1, tQK.col(32 * kc, 16 * rb), tZ.col(32 * kc, 16 * sb));
+          mma3(zi, tQK.row(16 * rb + col, 32 * kc + 8 * grp), tW.col(32 * kc, 16 * sb, lane));
+          mma3(w1, tQK.col(32 * kc, 16 * rb, lane), tZ.col(32 * kc, 16 * sb, lane));
         }
       }
 #pragma unroll
@@ -862,6 +883,8 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
     }
   }
   __syncthreads();
+  // the gates and dZ of this workgroup's next tile (dzv and the raw gates are dead here)
+  if constexpr (PERSIST) issue(tile_n < ntiles ? tile_n : tile_t, tile_n >= ntiles, tid);
 
   // ---- dg: in-chunk suffix of u, exclusive prefix of y, Z1, pass-2 part, -alpha dW
   float up[RPS][V], yk[RPS][V];
@@ -931,6 +954,32 @@ __global__ __launch_bounds__(kP1Threads) void gsa_pass1_bwd_kernel(GsaParams p, 
       }
     }
   }
+  if (!PERSIST || tile_n >= ntiles) break;
+  tile_t = tile_n;
+  __syncthreads();                       // the next tile's scan reuses the tail and the tiles
+  }
+  __builtin_amdgcn_s_waitcnt(0);         // the last tile's repeated loads have landed
+}
+
+// Resident workgroups of the pass-1 backward on the current device (its persistent grid),
+// cached per device id.
+template <typename T, int MP, int CP>
+int p1_slots() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gsa_pass1_bwd_kernel<T, MP, CP>, kP1Threads, 0) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int cus = device_cu_count();
+  const int n = (cus > 0 ? cus : 256) * per_cu;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // ----------------------------------------------------------------------------- launchers
@@ -1013,8 +1062,9 @@ hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s) {
     }
     WalkIO w1r{p.dZs, p.q, p.Gam, p.dS1s, p.dhkt, p.dhk0, p.m, p.Dk, p.L, p.C, p.N, 1};
     if ((e = launch_walk_reverse<T, MP, CP>(w1r, p.BH, s)) != hipSuccess) return e;
-    const int ntk = p.DkP / kDvTile;
-    hipLaunchKernelGGL((gsa_pass1_bwd_kernel<T, MP, CP>), dim3(p.N, p.BH), dim3(kP1Threads), 0, s, p, ntk);
+    const int ntk = p.DkP / kDvTile, ntiles = p.N * p.BH;
+    const int grid = GsaCfg<T, MP, CP>::P1_PERSIST ? imin(ntiles, p1_slots<T, MP, CP>()) : ntiles;
+    hipLaunchKernelGGL((gsa_pass1_bwd_kernel<T, MP, CP>), dim3(grid), dim3(kP1Threads), 0, s, p, ntk, ntiles);
     return hipGetLastError();
   }
 }
