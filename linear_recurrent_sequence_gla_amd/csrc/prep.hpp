@@ -35,6 +35,7 @@
 // locally; segment totals are combined through LDS.  Qs leaves straight from registers with
 // 16-byte stores; KdT and A are staged in LDS so their stores are 16-byte and coalesced.
 #pragma once
+#include <atomic>
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -74,6 +75,9 @@ struct PrepCfg {
   static constexpr int NP = NB * (NB - 1) / 2;         // off-diagonal sub-block pairs
   static constexpr int PPW = (NP + 3) / 4;             // pairs per wave
   static constexpr bool SPLIT = sizeof(T) == 2;        // hi/lo operands ("Precision of A")
+  // the persistent loop (next chunk's loads carried through a chunk) fits the registers except
+  // for fp32 with the widest keys
+  static constexpr bool PERSIST = sizeof(T) == 2 || DKP <= 128;
   static constexpr size_t TILE = (size_t)CP * LDQ * sizeof(T);
   static constexpr size_t KD = TILE;                   // Kd [CP][DKP], copied out transposed
   static constexpr size_t ATILE = (size_t)CP * LDC * sizeof(T);
@@ -288,8 +292,38 @@ struct ChunkScan {
   }
 };
 
+// Compute units of the current device, cached per device id.
+inline int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+// Issue the loads of chunk n of sequence bh (q, k, g) into cs; past = true reads only the
+// chunk's first row (a harmless, cached reload: the loads of a persistent loop's last round are
+// issued unconditionally)
 template <typename T, int DKP, int CP>
-__device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh) {
+__device__ __forceinline__ void prep_issue(const PrepParams& p, int n, int bh, ChunkScan<T, DKP, CP>& cs,
+                                           bool past) {
+  const int row0 = n * p.C;
+  const int len = past ? 1 : min(p.C, p.L - row0);
+  const size_t base = ((size_t)p.in(bh) * p.L + row0) * p.Dk;
+  cs.load(reinterpret_cast<const T*>(p.q) + base, reinterpret_cast<const T*>(p.k) + base,
+          reinterpret_cast<const T*>(p.g) + base, p.Dk, p.Dk, len);
+}
+
+// One chunk, whose loads the caller has issued into cs.  Once q and k are converted (the raw
+// vectors dead), next() runs: a persistent caller issues its next chunk's loads there, so they
+// are in flight while this chunk is computed.
+template <typename T, int DKP, int CP, typename Next>
+__device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, ChunkScan<T, DKP, CP>& cs, Next&& next) {
   using Cfg = PrepCfg<T, DKP, CP>;
   using M = ChunkMap<T, DKP, CP>;
   constexpr int V = M::V, RPS = M::RPS;
@@ -308,9 +342,10 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh) {
   const size_t base = ((size_t)p.in(bh) * p.L + row0) * Dk;
   const size_t chunk = (size_t)bh * p.N + n;
 
-  ChunkScan<T, DKP, CP> cs;
-  const float maxb = cs.run(reinterpret_cast<const T*>(p.q) + base, reinterpret_cast<const T*>(p.k) + base,
-                            reinterpret_cast<const T*>(p.g) + base, Dk, Dk, len, segtot, sGam, red);
+  const float maxb = cs.finish(segtot, sGam, red);
+  cs.kvals();
+  cs.qvals();
+  next();
   const bool fast = maxb <= kSpanLimit;
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
 
@@ -509,10 +544,29 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh) {
   if (tid < DKP) p.ops.Gam[chunk * DKP + tid] = sGam[tid];
 }
 
-// grid (N, BH): chunk n of sequence bh
+// Persistent grid over the ntiles = N * BH chunks (tile t: chunk t % N of sequence t / N):
+// workgroup w takes tiles w, w + gridDim.x, ..., each tile's loads in flight during the
+// previous tile's computation
 template <typename T, int DKP, int CP>
-__global__ __launch_bounds__(256, 2) void gla_prep_kernel(PrepParams p) {
-  prep_chunk<T, DKP, CP>(p, blockIdx.x, blockIdx.y);
+__global__ __launch_bounds__(256, 2) void gla_prep_kernel(PrepParams p, int ntiles) {
+  ChunkScan<T, DKP, CP> cs;
+  int t = blockIdx.x;
+  prep_issue(p, t % p.N, t / p.N, cs, false);
+  if constexpr (!PrepCfg<T, DKP, CP>::PERSIST) {    // one chunk per workgroup
+    prep_chunk<T, DKP, CP>(p, t % p.N, t / p.N, cs, [] {});
+    return;
+  }
+  for (;;) {
+    const int tn = t + gridDim.x;
+    prep_chunk<T, DKP, CP>(p, t % p.N, t / p.N, cs, [&] {
+      const int u = tn < ntiles ? tn : t;
+      prep_issue(p, u % p.N, u / p.N, cs, tn >= ntiles);
+    });
+    if (tn >= ntiles) break;
+    t = tn;
+    __syncthreads();                     // the next chunk's scan reuses the LDS
+  }
+  __builtin_amdgcn_s_waitcnt(0);         // the last round's repeated loads have landed
 }
 
 // grid (max N, total sequences): blockIdx.y runs over the batches' sequences back to back;
@@ -522,7 +576,9 @@ __global__ __launch_bounds__(256, 2) void gla_prep_batches(Batches<PrepParams> b
   const int gi = b.find(blockIdx.y);
   const PrepParams& p = b.p[gi];
   if ((int)blockIdx.x >= p.N) return;
-  prep_chunk<T, DKP, CP>(p, blockIdx.x, blockIdx.y - b.first[gi]);
+  ChunkScan<T, DKP, CP> cs;
+  prep_issue(p, blockIdx.x, blockIdx.y - b.first[gi], cs, false);
+  prep_chunk<T, DKP, CP>(p, blockIdx.x, blockIdx.y - b.first[gi], cs, [] {});
 }
 
 template <typename T, int DKP, int CP>
@@ -530,7 +586,9 @@ hipError_t launch_prep(const PrepParams& p, int BH, hipStream_t s) {
   if constexpr (PrepCfg<T, DKP, CP>::BYTES > kMaxLds) {
     return hipErrorNotSupported;
   } else {
-    hipLaunchKernelGGL((gla_prep_kernel<T, DKP, CP>), dim3(p.N, BH), dim3(256), 0, s, p);
+    const int ntiles = p.N * BH, cus = device_cu_count();
+    const int grid = PrepCfg<T, DKP, CP>::PERSIST && cus > 0 ? imin(ntiles, 2 * cus) : ntiles;   // two per CU
+    hipLaunchKernelGGL((gla_prep_kernel<T, DKP, CP>), dim3(grid), dim3(256), 0, s, p, ntiles);
     return hipGetLastError();
   }
 }

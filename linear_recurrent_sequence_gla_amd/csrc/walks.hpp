@@ -105,20 +105,6 @@ struct WalkPlan {
   static constexpr bool NARROW = OK && RT == 32 && WalkIOCfg<T, 16, CP, 2>::BYTES <= kMaxLds;
 };
 
-// Compute units of the current device, cached per device id.
-inline int device_cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-  if (dev < 64) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
-  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
 template <typename T, int SP, int CP>
 constexpr bool walk_fits() {
   return WalkPlan<T, SP, CP>::OK;
