@@ -210,10 +210,12 @@ const char* gla_status_str(int s) {
     case GLA_ERR_SHAPE: return "GLA_ERR_SHAPE: a size is smaller than 1";
     case GLA_ERR_DTYPE: return "GLA_ERR_DTYPE: dtype must be GLA_F32 (0) or GLA_BF16 (1)";
     case GLA_ERR_UNSUPPORTED:
-      return "GLA_ERR_UNSUPPORTED: C must be 16/32/64/128, Dk and m multiples of 16 up to 256, "
-             "Dv a multiple of 16 up to 512, B*H <= 65535, 16-byte aligned tensors; tiles that "
-             "exceed a CU's LDS are not supported (bf16: Dk > 128 with C = 128; fp32: Dk > 128 "
-             "with C = 64, Dk > 64 with C = 128, and every backward with C = 128)";
+      return "GLA_ERR_UNSUPPORTED: C must be 16/32/64/128, Dk a multiple of 16 up to 256, "
+             "Dv a multiple of 16 up to 512, GSA slots m a multiple of 16 up to 128, B*H <= 65535, "
+             "16-byte aligned tensors; tiles that exceed a CU's LDS are not supported (bf16: "
+             "Dk > 128 with C = 128; fp32: Dk > 128 with C = 64, Dk > 64 with C = 128, and every "
+             "backward with C = 128; chunked GSA: C <= 64, and its backward C <= 32 when m > 64, "
+             "fp32 m <= 64 with C <= 32)";
     case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE: workspace NULL or smaller than the query returned";
     case GLA_ERR_ALIAS: return "GLA_ERR_ALIAS: an output overlaps an input, another output or the workspace";
     case GLA_ERR_HIP: return "GLA_ERR_HIP: a HIP kernel launch failed";
