@@ -621,8 +621,10 @@ GsaLayout gsa_layout_of(int B, int H, int L, int Dk, int Dv, int m, int C, int d
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
   if (fwd) {
-    l.W = take(tok * es);
-    l.P = take(tok * es);
+    if (saved) {   // W and P as [L][m] tensors serve only pass 2's backward
+      l.W = take(tok * es);
+      l.P = take(tok * es);
+    }
     l.WdT = take(BH * N * MP * CP * es);
     l.Gam = take(BH * N * MP * 4);
     l.S1s = take(BH * N * MP * DkP * es);
@@ -654,7 +656,9 @@ GsaParams gsa_params(const GsaLayout& lf, char* fb, bool saved, const GsaLayout&
                      int Dk, int Dv, int m, int C) {
   GsaParams p{};
   p.BH = B * H; p.L = L; p.Dk = Dk; p.DkP = pad_dv(Dk); p.Dv = Dv; p.m = m; p.C = C; p.N = (L + C - 1) / C;
-  p.W = fb + lf.W; p.P = fb + lf.P; p.WdT = fb + lf.WdT; p.Gam = reinterpret_cast<float*>(fb + lf.Gam);
+  p.W = saved ? fb + lf.W : nullptr;   // the forward alone needs neither
+  p.P = saved ? fb + lf.P : nullptr;
+  p.WdT = fb + lf.WdT; p.Gam = reinterpret_cast<float*>(fb + lf.Gam);
   p.S1s = fb + lf.S1s;
   if (saved) p.Pf = reinterpret_cast<float*>(fb + lf.Pf);
   p.ops2 = carve_ops(fb + lf.ops2base, lf.ops2);

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void gsa_prep_kernel(GsaParams p) {
   cs.run(gg, gg, gg, m, m, len, segtot, sGam, red);
   const int c0 = cs.cg * V, r0 = cs.seg * RPS;
   if (cs.active) {
-    T* Wg = reinterpret_cast<T*>(p.W) + gbase;
+    T* Wg = p.W ? reinterpret_cast<T*>(p.W) + gbase : nullptr;
 #pragma unroll
     for (int u = 0; u < RPS; ++u) {
       const int r = r0 + u;
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void gsa_prep_kernel(GsaParams p) {
         wd[e] = from_f32<T>(w * fast_exp2(sGam[c0 + e] - cs.b[u][e]));
       }
       *reinterpret_cast<VT*>(sWd + r * LDM + c0) = wd;
-      if (r < len && c0 < m) *reinterpret_cast<VT*>(Wg + (size_t)r * m + c0) = wv;
+      if (Wg && r < len && c0 < m) *reinterpret_cast<VT*>(Wg + (size_t)r * m + c0) = wv;
     }
   }
   __syncthreads();
@@ -419,13 +419,13 @@ __global__ __launch_bounds__(256, 2) void gsa_p_kernel(GsaParams p) {
       }
     }
   }
-  T* Pg = reinterpret_cast<T*>(p.P) + gbase;
+  T* Pg = p.P ? reinterpret_cast<T*>(p.P) + gbase : nullptr;   // null: the forward alone
   T* Qg2 = reinterpret_cast<T*>(p.ops2.Qs) + chunk * CP * MP;
   constexpr int PER_ROW = MP / V;
   for (int idx = tid; idx < CP * PER_ROW; idx += 256) {
     const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
     const VT pv = *reinterpret_cast<const VT*>(sP + r * LDM + c);
-    if (r < len && c < m) *reinterpret_cast<VT*>(Pg + (size_t)r * m + c) = pv;
+    if (Pg && r < len && c < m) *reinterpret_cast<VT*>(Pg + (size_t)r * m + c) = pv;
     VT qs;
 #pragma unroll
     for (int e = 0; e < V; ++e) qs[e] = from_f32<T>(r < len ? to_f32(pv[e]) * fast_exp2(sB[r * LDF + c + e]) : 0.f);

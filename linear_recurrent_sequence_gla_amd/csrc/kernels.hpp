@@ -122,8 +122,9 @@ struct GsaParams {
   int saved;      // backward: W, P, Pf, WdT, Gam, S1s, ops2 and Hs2 were left by a
                   // saving forward, so the backward does not recompute them
   // workspace
-  void* W;        // [BH][L][m] write weights 1 - exp(g)   (keys of pass 2)   (T)
-  void* P;        // [BH][L][m] slot softmax              (queries of pass 2) (T)
+  void* W;        // [BH][L][m] write weights 1 - exp(g)   (keys of pass 2)   (T), or null
+  void* P;        // [BH][L][m] slot softmax              (queries of pass 2) (T), or null
+                  // (W and P serve only pass 2's backward: the forward alone writes neither)
   float* Pf;      // [BH][L][m] fp32, backward only: the softmax P (its Jacobian needs P) or,
                   // for the element-wise read-outs, the scores Z (their derivative needs Z)
   float* dP;      // [BH][L][m] gradient of P (backward), fp32
