@@ -209,7 +209,9 @@ struct BwdTile {
   }
 };
 
-template <typename T, int DKS, int CP, bool WITH_DV>
+// RD: GSA's pass 2 with the read-out's backward in the epilogue (p.dz, p.rd, p.dzs, p.act set);
+// a separate instance, so that the plain GLA backward carries none of its registers
+template <typename T, int DKS, int CP, bool WITH_DV, bool RD>
 __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DKP, int ntile, int ntiles) {
   using Cf = BwdChunkCfg<T, DKS, CP, WITH_DV>;
   constexpr int NT = Cf::NT, NW = NT / 64;
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
     // GSA's pass 2 with the read-out's backward fused: the read-out's input (fp32) for the
     // epilogue, in flight through the intra phase
     f32x4 rdl[RPS][V / 4];
-    if (p.dz) {
+    if constexpr (RD) {
       const int cc = (cs.active && c0 < kvalid) ? c0 : 0;
 #pragma unroll
       for (int u = 0; u < RPS; ++u) {
@@ -615,7 +617,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
           up[u][e] = qv * dqn[u][e] - kv * dkp[u][e];
           uk[u][e] = kv * bk;
         }
-        if (p.dz) {
+        if constexpr (RD) {
           // the read-out's backward: dq here is dP, the gradient of the read-out's output, and
           // dZ = P (dP - <dP, P>) over the row's slots for the softmax (the row's channel groups
           // are NCG consecutive lanes), else f'(Z) dP; dZ 2^b also goes out chunk-padded for
@@ -644,7 +646,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
           }
         }
         if (r < len && c0 < kvalid) {
-          if (p.dz) {
+          if constexpr (RD) {
             // dq itself is not kept
           } else if (p.dq32) {
             float* d32 = p.dq32 + qbase + (size_t)r * Dk + c0;
@@ -879,7 +881,7 @@ __global__ __launch_bounds__(kDvThreads) void gla_bwd_dv(BwdParams p, int ntile)
 // ======================================================================= plan + launch
 // Workgroups of the persistent chunk kernel that the device runs at once (CUs times the
 // workgroups one CU holds), cached per device; 0 cannot happen (at least one per CU).
-template <typename T, int DKS, int CP, bool WITH_DV>
+template <typename T, int DKS, int CP, bool WITH_DV, bool RD>
 int bwd_chunk_slots() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -889,7 +891,7 @@ int bwd_chunk_slots() {
     if (c > 0) return c;
   }
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gla_bwd_chunk<T, DKS, CP, WITH_DV>, kBwdThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gla_bwd_chunk<T, DKS, CP, WITH_DV, RD>, kBwdThreads, 0) !=
           hipSuccess || per_cu < 1)
     per_cu = 1;
   const int cus = device_cu_count();
@@ -952,8 +954,19 @@ hipError_t launch_gla_bwd(const BwdParams& p, hipStream_t s) {
     if ((e = launch_walk_reverse<T, DKP, CP>(wr, p.BH, s)) != hipSuccess) return e;
     record_event(p.events, ev++, s);
     const int ntiles = p.N * p.BH * (DKP / P::DKS);
-    hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED>), dim3(imin(ntiles, bwd_chunk_slots<T, P::DKS, CP, P::FUSED>())),
-                       dim3(kBwdThreads), 0, s, p, DKP, ntile, ntiles);
+    if (p.dz) {   // GSA's pass 2 with the read-out's backward: one key-width slice only
+      if constexpr (P::DKS == DKP && DKP <= 128) {   // GSA pads at most 128 slots
+        hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED, true>),
+                           dim3(imin(ntiles, bwd_chunk_slots<T, P::DKS, CP, P::FUSED, true>())), dim3(kBwdThreads), 0, s,
+                           p, DKP, ntile, ntiles);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    } else {
+      hipLaunchKernelGGL((gla_bwd_chunk<T, P::DKS, CP, P::FUSED, false>),
+                         dim3(imin(ntiles, bwd_chunk_slots<T, P::DKS, CP, P::FUSED, false>())), dim3(kBwdThreads), 0, s,
+                         p, DKP, ntile, ntiles);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     record_event(p.events, ev++, s);
     if constexpr (!P::FUSED) {
