@@ -221,6 +221,12 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   constexpr int NBR = CP / 16, NIB = DKS / 16, NJB = kDvTile / 16;
   constexpr int NA_BLK = NBR * NBR, NQ_BLK = NBR * NIB, NV_BLK = NBR * NJB;
   constexpr int PA = (NA_BLK + NW - 1) / NW, PQ = (NQ_BLK + NW - 1) / NW, PVb = (NV_BLK + NW - 1) / NW;
+  // Square blocking: where the [C][DKS] products split into 2 x 2 blocks per wave (two row blocks,
+  // two key blocks) and dA into the same two row blocks, a wave reads two dO, two V, two H and two
+  // dH fragments per k step for its eight products instead of four, four, one and one -- and
+  // its dA blocks reuse the two dO fragments.  Otherwise a wave owns one key block and every row.
+  constexpr bool SQ2 = NBR % 2 == 0 && NIB % 2 == 0 && (NBR / 2) * (NIB / 2) == NW && PQ == 4 && PA == 2 &&
+                       NIB / 2 == NBR;
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
   T* sdA = reinterpret_cast<T*>(smem);                            // strictly lower dA
@@ -264,6 +270,12 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   for (;;) {
     tid = opaque_thread_index();  // per-lane addresses are formed anew for each tile
     const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+    // block s of this wave's [C][DKS] products and of its dA (rows rb, key or column block)
+    const int rp = wave / (NIB > 1 ? NIB / 2 : 1), ip = wave % (NIB > 1 ? NIB / 2 : 1);   // SQ2 only
+    auto q_rb = [&](int s) { return SQ2 ? 2 * rp + (s >> 1) : (wave + NW * s) / NIB; };
+    auto q_ib = [&](int s) { return SQ2 ? 2 * ip + (s & 1) : (wave + NW * s) % NIB; };
+    auto a_rb = [&](int s) { return SQ2 ? 2 * rp + s : (wave + NW * s) / NBR; };
+    auto a_cb = [&](int s) { return SQ2 ? ip : (wave + NW * s) % NBR; };
     const BwdTile tile(p, t, DKS, DKP / DKS);
     const int tn = t + gridDim.x;  // this workgroup's next tile
     const int ch0 = tile.ch0, row0 = tile.row0, len = tile.len, kvalid = tile.kvalid;
@@ -318,7 +330,27 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
       // operand block (dA: the V block, dQ and dKI: the H and dH blocks, dV: the dO and dH
       // column blocks), which is then read from LDS once per k step instead of once per block.
       // Each accumulator still sums its k steps in the same order.
-      if constexpr (NA_BLK % NW == 0 && NW % NBR == 0) {   // dA += dO V^T
+      if constexpr (SQ2) {                 // dA += dO V^T ; dQ += dO H^T ; dKI += V dH^T
+#pragma unroll
+        for (int kb = 0; kb < kDvTile / 32; ++kb) {
+          const int ko = 32 * kb + 8 * grp;
+          const Frag<T> o0 = ld8(sdO + (32 * rp + col) * LDV + ko), o1 = ld8(sdO + (32 * rp + 16 + col) * LDV + ko);
+          const Frag<T> v0 = ld8(sV + (32 * rp + col) * LDV + ko), v1 = ld8(sV + (32 * rp + 16 + col) * LDV + ko);
+          const Frag<T> h0 = ld8(sH + (32 * ip + col) * LDV + ko), h1 = ld8(sH + (32 * ip + 16 + col) * LDV + ko);
+          const Frag<T> d0 = ld8(sdH + (32 * ip + col) * LDV + ko), d1 = ld8(sdH + (32 * ip + 16 + col) * LDV + ko);
+          const Frag<T> vc = ld8(sV + (16 * ip + col) * LDV + ko);
+          mma(accA[0], vc, o0);
+          mma(accA[1], vc, o1);
+          mma(accQ[0], h0, o0);
+          mma(accQ[1], h1, o0);
+          mma(accQ[2], h0, o1);
+          mma(accQ[3], h1, o1);
+          mma(accKI[0], d0, v0);
+          mma(accKI[1], d1, v0);
+          mma(accKI[2], d0, v1);
+          mma(accKI[3], d1, v1);
+        }
+      } else if constexpr (NA_BLK % NW == 0 && NW % NBR == 0) {   // dA += dO V^T
         const int cb = wave % NBR, rb0 = wave / NBR;
 #pragma unroll
         for (int kb = 0; kb < kDvTile / 32; ++kb) {
@@ -339,7 +371,9 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
           }
         }
       }
-      if constexpr (NQ_BLK % NW == 0 && NW % NIB == 0) {   // dQ += dO H^T ; dKI += V dH^T
+      if constexpr (SQ2) {
+        // done above
+      } else if constexpr (NQ_BLK % NW == 0 && NW % NIB == 0) {   // dQ += dO H^T ; dKI += V dH^T
         const int ib = wave % NIB, rb0 = wave / NIB;
 #pragma unroll
         for (int kb = 0; kb < kDvTile / 32; ++kb) {
@@ -471,9 +505,8 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
     // as column runs of these tiles through transposing LDS reads.
 #pragma unroll
     for (int s = 0; s < PA; ++s) {
-      const int blk = wave + NW * s;
-      if (blk < NA_BLK) {
-        const int rb = blk / NBR, cb = blk % NBR;
+      if (SQ2 || wave + NW * s < NA_BLK) {
+        const int rb = a_rb(s), cb = a_cb(s);
         // transposed block: this lane holds dA[16 rb + col][16 cb + 4 grp + e]
         const int r = 16 * rb + col;
         typename Vec4<T>::type a4;
@@ -501,7 +534,29 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
     }
     __syncthreads();
     if (fast) {                            // off-diagonal intra terms on MFMA
-      if constexpr (NQ_BLK % NW == 0 && NW % NIB == 0) {
+      if constexpr (SQ2) {
+        // the wave's two key blocks' Ks and Qs column blocks and its two row blocks' dA rows
+        // and dA columns, each read once per k step
+#pragma unroll
+        for (int kc = 0; kc < CP / 32; ++kc) {
+          const Frag<T> ks0 = ld8_colblk(sKs + (32 * kc) * LDQ + 32 * ip, LDQ, lane);
+          const Frag<T> ks1 = ld8_colblk(sKs + (32 * kc) * LDQ + 32 * ip + 16, LDQ, lane);
+          const Frag<T> qs0 = ld8_colblk(sQs + (32 * kc) * LDQ + 32 * ip, LDQ, lane);
+          const Frag<T> qs1 = ld8_colblk(sQs + (32 * kc) * LDQ + 32 * ip + 16, LDQ, lane);
+          const Frag<T> ar0 = ld8(sdA + (32 * rp + col) * LDC + 32 * kc + 8 * grp);
+          const Frag<T> ar1 = ld8(sdA + (32 * rp + 16 + col) * LDC + 32 * kc + 8 * grp);
+          const Frag<T> ac0 = ld8_colblk(sdA + (32 * kc) * LDC + 32 * rp, LDC, lane);
+          const Frag<T> ac1 = ld8_colblk(sdA + (32 * kc) * LDC + 32 * rp + 16, LDC, lane);
+          mma(accQ[0], ks0, ar0);
+          mma(accQ[1], ks1, ar0);
+          mma(accQ[2], ks0, ar1);
+          mma(accQ[3], ks1, ar1);
+          mma(accK[0], qs0, ac0);
+          mma(accK[1], qs1, ac0);
+          mma(accK[2], qs0, ac1);
+          mma(accK[3], qs1, ac1);
+        }
+      } else if constexpr (NQ_BLK % NW == 0 && NW % NIB == 0) {
         // as in the slice loop: the key block ib is fixed per wave, so its Ks and Qs column
         // blocks are read once per k step
         const int ib = wave % NIB, rb0 = wave / NIB;
@@ -536,9 +591,8 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
     __syncthreads();                       // phase-1 tiles are dead from here on
 #pragma unroll
     for (int s = 0; s < PQ; ++s) {
-      const int blk = wave + NW * s;
-      if (blk < NQ_BLK) {
-        const int rb = blk / NIB, ib = blk % NIB;
+      if (SQ2 || wave + NW * s < NQ_BLK) {
+        const int rb = q_rb(s), ib = q_ib(s);
         const int o = (16 * rb + col) * LDF + 16 * ib + 4 * grp;   // four consecutive channels
         *reinterpret_cast<f32x4*>(sDQ + o) = accQ[s];
         if (fast) *reinterpret_cast<f32x4*>(sDK + o) = accK[s];
