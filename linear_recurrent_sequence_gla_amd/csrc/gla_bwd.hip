@@ -47,7 +47,7 @@ constexpr int kBwdThreads = 512;
 
 // LDS phases of the chunk kernel:
 //   front   sdA [CP][CP] (written after the Dv loop, read to the end), diag of dA (fp32)
-//   phase 1 (Dv loop)    sKd, sA (with dv) and the Dv slice tiles dO, V, H, dH (+ dV)
+//   phase 1 (Dv loop)    sKd, sA (with dv) and the Dv slice tiles dO, V, H, dH
 //   phase 2 (intra)      Qs, Ks [CP][DKS] for the intra-chunk products
 //   phase 3 (epilogue)   three fp32 [CP][DKS] gradient tiles; on the exact path b takes the
 //                        place of the (unused) intra dk tile
@@ -56,7 +56,7 @@ constexpr size_t chunk_bwd_bytes(int es, int DKS, int CP, bool dv, int nseg) {  
   const size_t LDQ = DKS + 2 * V, LDC = CP + 2 * V, LDV = kDvTile + 2 * V, LDF = DKS + 4;
   const size_t QT = CP * LDQ * es, CT = CP * LDC * es, VT = CP * LDV * es, HT = DKS * LDV * es;
   const size_t FT = CP * LDF * 4;
-  const size_t ph1 = (dv ? QT + CT : 0) + 2 * VT + 2 * HT + (dv ? VT : 0);
+  const size_t ph1 = (dv ? QT + CT : 0) + 2 * VT + 2 * HT;
   const size_t ph2 = 2 * QT;
   const size_t ph3 = 3 * FT;
   const size_t mx = ph1 > ph2 ? (ph1 > ph3 ? ph1 : ph3) : (ph2 > ph3 ? ph2 : ph3);
@@ -76,7 +76,7 @@ struct BwdChunkCfg {
   static constexpr size_t VT = (size_t)CP * LDV * sizeof(T);
   static constexpr size_t HT = (size_t)DKS * LDV * sizeof(T);
   static constexpr size_t FT = (size_t)CP * LDF * 4;
-  static constexpr size_t PH1 = (WITH_DV ? QT + CT : 0) + 2 * VT + 2 * HT + (WITH_DV ? VT : 0);
+  static constexpr size_t PH1 = (WITH_DV ? QT + CT : 0) + 2 * VT + 2 * HT;
   static constexpr size_t PH2 = 2 * QT;
   static constexpr size_t PH3 = 3 * FT;
   static constexpr size_t MAIN = CT + cmax(cmax(PH1, PH2), PH3);
@@ -89,6 +89,9 @@ struct BwdChunkCfg {
 // Loads are unconditional from clamped in-bounds addresses; each vector's validity is kept
 // beside it and applied once the data is used, so no branch or register rewrite touches a
 // load in flight and the next slice's loads overlap the current slice's matrix work.
+// where the chunk kernel's lanes outside a ragged chunk or the value width write their dv
+__device__ __attribute__((aligned(16))) char g_dv_sink[16];
+
 template <typename T, int DKS, int CP, bool WITH_DV>
 struct SliceStage {
   using Cf = BwdChunkCfg<T, DKS, CP, WITH_DV>;
@@ -238,7 +241,6 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   T* sV = sdO + CP * LDV;
   T* sH = sV + CP * LDV;
   T* sdH = sH + DKS * LDV;
-  T* sdV = sdH + DKS * LDV;                                       // WITH_DV only
   // phase 2 (aliases phase 1)
   T* sQs = reinterpret_cast<T*>(rmain);                           // q 2^b   [CP][DKS]
   T* sKs = sQs + CP * LDQ;                                        // k 2^-b
@@ -284,6 +286,14 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
     const T* kg = reinterpret_cast<const T*>(p.k) + qbase;
     const T* dog = reinterpret_cast<const T*>(p.do_) + tile.vbase;
     const T* vg = reinterpret_cast<const T*>(p.v) + tile.vbase;
+    // dv goes out straight from the accumulators, four consecutive columns of one row per lane;
+    // a lane outside the chunk or the value width writes to a sink instead, so that every lane
+    // stores and the wait for the next slice's loads can leave these stores in flight
+    typedef typename Vec4<T>::type DV4;
+    auto dv_dst = [&](int r, int c) -> DV4* {
+      T* dvg = reinterpret_cast<T*>(p.dv) + tile.vbase;
+      return r < len && c < Dv ? reinterpret_cast<DV4*>(dvg + (size_t)r * Dv + c) : reinterpret_cast<DV4*>(g_dv_sink);
+    };
     const T* hs = reinterpret_cast<const T*>(p.Hs) + (chunk * DKP + ch0) * DVP;
     const T* dhs = reinterpret_cast<const T*>(p.dHs) + (chunk * DKP + ch0) * DVP;
     // the first Dv slice and (with dv) the chunk's A tile load while the gates are scanned
@@ -427,7 +437,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
             typename Vec4<T>::type dv4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) dv4[e] = from_f32<T>(acc[s][e]);
-            *reinterpret_cast<typename Vec4<T>::type*>(sdV + (16 * cb + col) * LDV + 16 * jb + 4 * grp) = dv4;
+            *dv_dst(16 * cb + col, js * kDvTile + 16 * jb + 4 * grp) = dv4;
           }
         } else {
 #pragma unroll
@@ -448,30 +458,17 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
               typename Vec4<T>::type dv4;
 #pragma unroll
               for (int e = 0; e < 4; ++e) dv4[e] = from_f32<T>(acc[e]);
-              *reinterpret_cast<typename Vec4<T>::type*>(sdV + (16 * cb + col) * LDV + 16 * jb + 4 * grp) = dv4;
+              *dv_dst(16 * cb + col, js * kDvTile + 16 * jb + 4 * grp) = dv4;
             }
           }
         }
       }
       __syncthreads();
-      // The next slice is staged before this slice's dv leaves, and on every path: after the
-      // last slice the reloaded copy goes to LDS that the intra phase overwrites, and adds
-      // nothing to Z.  The wait for its loads is explicit and comes first (the only older
-      // memory operations are the previous slice's dv stores); left to the compiler, it sinks
-      // the Z sums below the dv stores and then waits for those stores as well.
-      __builtin_amdgcn_s_waitcnt(0);
+      // The next slice is staged on every path: after the last slice the reloaded copy goes to
+      // LDS that the intra phase overwrites, and adds nothing to Z.  Its loads are older than
+      // this slice's dv stores, so the wait for them leaves the stores in flight.
       st.zdot(zp, js + 1 < ntile);
       st.store(sdO, sV, sH, sdH, tid);
-      if constexpr (WITH_DV) {
-        T* dvg = reinterpret_cast<T*>(p.dv) + tile.vbase;
-        constexpr int PER_ROW = kDvTile / V;
-        for (int idx = tid; idx < CP * PER_ROW; idx += NT) {
-          const int r = idx / PER_ROW, c = (idx - r * PER_ROW) * V;
-          const int jj = js * kDvTile + c;
-          if (r < len && jj < Dv)
-            *reinterpret_cast<VT*>(dvg + (size_t)r * Dv + jj) = *reinterpret_cast<const VT*>(sdV + r * LDV + c);
-        }
-      }
       __syncthreads();
     }
     // GSA's pass 2 with the read-out's backward fused: the read-out's input (fp32) for the
