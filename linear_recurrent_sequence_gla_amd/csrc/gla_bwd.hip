@@ -230,6 +230,11 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
   // its dA blocks reuse the two dO fragments.  Otherwise a wave owns one key block and every row.
   constexpr bool SQ2 = NBR % 2 == 0 && NIB % 2 == 0 && (NBR / 2) * (NIB / 2) == NW && PQ == 4 && PA == 2 &&
                        NIB / 2 == NBR;
+  // Row sharing: where a wave's dQ and dKI blocks are its row blocks rb0, rb0 + NW / NIB, ... of
+  // one key block and its dA blocks the same row blocks of one column block (NIB == NBR), the
+  // three products run in one k loop and read each dO and V row fragment once
+  constexpr bool ROWS = !SQ2 && NIB == NBR && PQ == PA && NQ_BLK % NW == 0 && NW % NIB == 0 &&
+                        NA_BLK % NW == 0;
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
   T* sdA = reinterpret_cast<T*>(smem);                            // strictly lower dA
@@ -360,6 +365,23 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
           mma(accKI[2], d0, v1);
           mma(accKI[3], d1, v1);
         }
+      } else if constexpr (ROWS) {          // dA += dO V^T ; dQ += dO H^T ; dKI += V dH^T
+        const int ib = wave % NIB, rb0 = wave / NIB;
+#pragma unroll
+        for (int kb = 0; kb < kDvTile / 32; ++kb) {
+          const int ko = 32 * kb + 8 * grp;
+          const Frag<T> fh = ld8(sH + (16 * ib + col) * LDV + ko);
+          const Frag<T> fdh = ld8(sdH + (16 * ib + col) * LDV + ko);
+          const Frag<T> vc = ld8(sV + (16 * ib + col) * LDV + ko);     // dA's column block is ib
+#pragma unroll
+          for (int s = 0; s < PQ; ++s) {
+            const int o = (16 * (rb0 + (NW / NIB) * s) + col) * LDV + ko;
+            const Frag<T> fo = ld8(sdO + o);
+            mma(accA[s], vc, fo);
+            mma(accQ[s], fh, fo);
+            mma(accKI[s], fdh, ld8(sV + o));
+          }
+        }
       } else if constexpr (NA_BLK % NW == 0 && NW % NBR == 0) {   // dA += dO V^T
         const int cb = wave % NBR, rb0 = wave / NBR;
 #pragma unroll
@@ -381,7 +403,7 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
           }
         }
       }
-      if constexpr (SQ2) {
+      if constexpr (SQ2 || ROWS) {
         // done above
       } else if constexpr (NQ_BLK % NW == 0 && NW % NIB == 0) {   // dQ += dO H^T ; dKI += V dH^T
         const int ib = wave % NIB, rb0 = wave / NIB;
