@@ -796,11 +796,12 @@ __global__ __launch_bounds__(kBwdThreads) void gla_bwd_chunk(BwdParams p, int DK
 // ======================================================================= dv (separate)
 // When the chunk-gradient kernel splits the key width (it does when dv does not fit its LDS:
 // Dk = 256, or C = 128), dv = A^T dO + Kd dH_{n+1} runs here.  One workgroup of 8 waves per
-// (chunk, b*h) stages the chunk's A and KdT tiles once and walks the 64-column Dv slices;
-// each slice's dO and dH loads are in flight while the previous slice's products run, as in
-// the chunk-gradient kernel.  Both products read their column operands with transposing LDS
-// reads (tiles with 32-byte row pads), and the accumulators hold dV transposed so that each
-// lane moves four consecutive columns of a row to LDS with one vector write.
+// (chunk, b*h) stages the chunk's A and KdT tiles once, from which each wave keeps the A^T and
+// Kd fragments of its blocks in registers, and walks the 64-column Dv slices; each slice's dO
+// and dH loads are in flight while the previous slice's products run, as in the chunk-gradient
+// kernel.  Column operands are read with transposing LDS reads (tiles with 32-byte row pads),
+// and the accumulators hold dV transposed, so that each lane stores four consecutive columns of
+// a row straight to memory.
 constexpr int kDvThreads = 512;
 
 template <typename T, int DKP, int CP>
@@ -810,9 +811,9 @@ struct BwdDvCfg {
   static constexpr int LDC = CP + 2 * V, LDV = kDvTile + 2 * V;
   static constexpr size_t AT = (size_t)CP * LDC * sizeof(T);     // A   [CP][CP]
   static constexpr size_t KT = (size_t)DKP * LDC * sizeof(T);    // KdT [DKP][CP]
-  static constexpr size_t OT = (size_t)CP * LDV * sizeof(T);     // dO slice, dV staging [CP][64]
+  static constexpr size_t OT = (size_t)CP * LDV * sizeof(T);     // dO slice [CP][64]
   static constexpr size_t HT = (size_t)DKP * LDV * sizeof(T);    // dH slice [DKP][64]
-  static constexpr size_t BYTES = AT + KT + 2 * OT + HT;
+  static constexpr size_t BYTES = AT + KT + OT + HT;
   static constexpr int PER_ROW = kDvTile / V;
   static constexpr int NO = CP * PER_ROW, NH = DKP * PER_ROW;    // 16-byte vectors per slice
   static constexpr int PO = (NO + NT - 1) / NT, PH = (NH + NT - 1) / NT;
@@ -863,14 +864,13 @@ template <typename T, int DKP, int CP>
 __global__ __launch_bounds__(kDvThreads) void gla_bwd_dv(BwdParams p, int ntile) {
   using Cf = BwdDvCfg<T, DKP, CP>;
   constexpr int NT = Cf::NT, NW = Cf::NW, V = Cf::V, LDC = Cf::LDC, LDV = Cf::LDV;
-  constexpr int NJB = Cf::NJB, PVB = Cf::PVB, PER_ROW = Cf::PER_ROW;
+  constexpr int NJB = Cf::NJB, PVB = Cf::PVB;
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[Cf::BYTES];
   T* sA = reinterpret_cast<T*>(smem);
   T* sKdT = reinterpret_cast<T*>(smem + Cf::AT);
   T* sdO = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT);
-  T* sdV = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT + Cf::OT);
-  T* sdH = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT + 2 * Cf::OT);
+  T* sdH = reinterpret_cast<T*>(smem + Cf::AT + Cf::KT + Cf::OT);
 
   const int n = blockIdx.x % p.N, bh = blockIdx.x / p.N;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
@@ -905,8 +905,21 @@ __global__ __launch_bounds__(kDvThreads) void gla_bwd_dv(BwdParams p, int ntile)
   st.store(sdO, sdH, tid);
   __syncthreads();
 
-  // wave w owns column block jb = w % NJB of the slice and row blocks cb0 + (NW / NJB) s
+  // wave w owns column block jb = w % NJB of the slice and row blocks cb0 + (NW / NJB) s.  Its
+  // A^T and Kd fragments are the same for every slice: they stay in registers, and each slice
+  // reads only its dO and dH column fragments from LDS
   const int jb = wave % NJB, cb0 = wave / NJB;
+  Frag<T> fa[CP / 32][PVB], fk[DKP / 32][PVB];
+#pragma unroll
+  for (int kr = 0; kr < CP / 32; ++kr) {
+#pragma unroll
+    for (int s = 0; s < PVB; ++s) fa[kr][s] = ld8_colblk(sA + (32 * kr) * LDC + 16 * (cb0 + (NW / NJB) * s), LDC, lane);
+  }
+#pragma unroll
+  for (int ki = 0; ki < DKP / 32; ++ki) {
+#pragma unroll
+    for (int s = 0; s < PVB; ++s) fk[ki][s] = ld8_colblk(sKdT + (32 * ki) * LDC + 16 * (cb0 + (NW / NJB) * s), LDC, lane);
+  }
   for (int js = 0; js < ntile; ++js) {
     st.load(dog, dhs, len, Dv, DVP, min(js + 1, ntile - 1), tid);   // last: harmless reload
     f32x4 acc[PVB];
@@ -916,37 +929,28 @@ __global__ __launch_bounds__(kDvThreads) void gla_bwd_dv(BwdParams p, int ntile)
     for (int kr = 0; kr < CP / 32; ++kr) {            // A^T dO
       const Frag<T> fo = ld8_colblk(sdO + (32 * kr) * LDV + 16 * jb, LDV, lane);
 #pragma unroll
-      for (int s = 0; s < PVB; ++s)
-        mma(acc[s], fo, ld8_colblk(sA + (32 * kr) * LDC + 16 * (cb0 + (NW / NJB) * s), LDC, lane));
+      for (int s = 0; s < PVB; ++s) mma(acc[s], fo, fa[kr][s]);
     }
 #pragma unroll
     for (int ki = 0; ki < DKP / 32; ++ki) {           // Kd dH
       const Frag<T> fd = ld8_colblk(sdH + (32 * ki) * LDV + 16 * jb, LDV, lane);
 #pragma unroll
-      for (int s = 0; s < PVB; ++s)
-        mma(acc[s], fd, ld8_colblk(sKdT + (32 * ki) * LDC + 16 * (cb0 + (NW / NJB) * s), LDC, lane));
+      for (int s = 0; s < PVB; ++s) mma(acc[s], fd, fk[ki][s]);
     }
+    // dv straight from the accumulators (this lane holds dV[16 cb + col][16 jb + 4 grp + e]);
+    // lanes outside the chunk or the value width write to a sink, so every lane stores and the
+    // wait for the next slice's loads, which are older, leaves these stores in flight
 #pragma unroll
     for (int s = 0; s < PVB; ++s) {
-      // transposed block: this lane holds dV[16 cb + col][16 jb + 4 grp + e]
-      const int cb = cb0 + (NW / NJB) * s;
+      const int r = 16 * (cb0 + (NW / NJB) * s) + col, c = js * kDvTile + 16 * jb + 4 * grp;
       typename Vec4<T>::type dv4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) dv4[e] = from_f32<T>(acc[s][e]);
-      *reinterpret_cast<typename Vec4<T>::type*>(sdV + (16 * cb + col) * LDV + 16 * jb + 4 * grp) = dv4;
+      *reinterpret_cast<typename Vec4<T>::type*>(r < len && c < Dv ? dvg + (size_t)r * Dv + c
+                                                                   : reinterpret_cast<T*>(g_dv_sink)) = dv4;
     }
     __syncthreads();
-    // the next slice's loads are the youngest memory operations: wait for them, stage them,
-    // and send this slice's dv out of the staging tile
-    __builtin_amdgcn_s_waitcnt(0);
     st.store(sdO, sdH, tid);
-#pragma unroll
-    for (int m = 0; m < Cf::PO; ++m) {
-      const int idx = tid + NT * m, r = idx / PER_ROW, c = (idx % PER_ROW) * V;
-      const int jj = js * kDvTile + c;
-      if ((Cf::NO % NT == 0 || idx < Cf::NO) && r < len && jj < Dv)
-        *reinterpret_cast<VT*>(dvg + (size_t)r * Dv + jj) = *reinterpret_cast<const VT*>(sdV + r * LDV + c);
-    }
     __syncthreads();
   }
 }
