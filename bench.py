@@ -179,8 +179,12 @@ def _stats(vals_ms):
 
 
 def run_gla(torch, m, steps, warmup, name=WORKLOAD):
-    """Training steps (gla_fwd_save then gla_bwd_saved) on one GLA workload, per-step and
-    per-kernel durations from HIP events the library records on the launch stream."""
+    """Training steps (gla_fwd_save then gla_bwd_saved) on one GLA workload.  Three timed
+    passes over the same `steps` steps: the mean step time with nothing recorded between the
+    steps (the headline: an event at each kernel boundary costs about 2.5 us of the stream's
+    time, some 20 us per step); each step's duration, from an event before and after it; and
+    each kernel's duration, from the HIP events the library records at its kernel boundaries
+    on the launch stream."""
     import ctypes
     w = W.WORKLOADS[name]
     B, H, L, Dk, Dv, C = w.B, w.H, w.L, w.Dk, w.Dv, w.C
@@ -214,18 +218,15 @@ def run_gla(torch, m, steps, warmup, name=WORKLOAD):
 
     for k in range(warmup):
         step(k=k)
+    ms, step_ms = _timed_steps(torch, lambda k: step(k=k), steps, 0, indexed=True)
     ef = [_events(torch, 4) for _ in range(steps)]
     eb = [_events(torch, 4) for _ in range(steps)]                 # room for the most launches
     hf = [_handles(e) for e in ef]
     hb = [_handles(e) for e in eb]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
     for k in range(steps):
         step(hf[k], hb[k], k)
-    end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
     names_f = ["fwd.prep", "fwd.walk", "fwd.out"]
     names_b = ["bwd.walk_rev", "bwd.chunk", "bwd.dv"][:nb]
     kt = {}
@@ -233,7 +234,6 @@ def run_gla(torch, m, steps, warmup, name=WORKLOAD):
         kt[nme] = [ef[k][i].elapsed_time(ef[k][i + 1]) for k in range(steps)]
     for i, nme in enumerate(names_b):
         kt[nme] = [eb[k][i].elapsed_time(eb[k][i + 1]) for k in range(steps)]
-    step_ms = [ef[k][0].elapsed_time(eb[k][nb]) for k in range(steps)]
     return {"w": w, "x": x, "ms": ms, "step_ms": step_ms, "kernel_ms": kt}
 
 
@@ -388,19 +388,26 @@ def run_gsa_decode(torch, m, T=None, sets=24):
                        cold, warm, sets, BH * state / 1e6)
 
 
-def _timed_steps(torch, fn, steps, warmup):
-    """Mean over one timed region of `steps` calls, and each call's duration (events)."""
-    for _ in range(warmup):
-        fn()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
+def _timed_steps(torch, fn, steps, warmup, indexed=False):
+    """The mean over one timed region of `steps` calls with nothing recorded between them, and
+    each call's duration from a second pass with an event before and after every call (those
+    events take stream time of their own, so they stay out of the mean).  With indexed, fn
+    takes the call's index."""
+    call = (lambda k: fn(k)) if indexed else (lambda k: fn())
+    for k in range(warmup):
+        call(k)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     s.record()
-    for a, b in evs:
-        a.record()
-        fn()
-        b.record()
+    for k in range(steps):
+        call(k)
     e.record()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for k, (a, b) in enumerate(evs):
+        a.record()
+        call(k)
+        b.record()
     torch.cuda.synchronize()
     return s.elapsed_time(e) / steps, [a.elapsed_time(b) for a, b in evs]
 
@@ -477,17 +484,11 @@ def run_long_fwd(torch, m, steps=10, warmup=3):
                 P(ws), ws.numel(), stream)
         m._check(lib.gla_fwd_profiled(*args, h, 4) if h else lib.gla_fwd(*args))
 
-    for _ in range(warmup):
-        fwd()
+    ms, per = _timed_steps(torch, fwd, steps, warmup)   # no events recorded between kernels
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for k in range(steps):
+    for k in range(steps):                              # each kernel's duration
         fwd(hs[k])
-    e.record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / steps
-    per = [evs[k][0].elapsed_time(evs[k][3]) for k in range(steps)]
     kt = {nme: [evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]
           for i, nme in enumerate(("prep", "walk", "out"))}
     alg = algorithmic(w.B, w.H, w.L, w.Dk, w.Dv, w.C)
