@@ -412,7 +412,7 @@ def _timed_steps(torch, fn, steps, warmup, indexed=False):
     return s.elapsed_time(e) / steps, [a.elapsed_time(b) for a, b in evs]
 
 
-def run_gsa(torch, m, steps=10, warmup=3, name="gsa_340m", read_outs=None):
+def run_gsa(torch, m, steps=20, warmup=100, name="gsa_340m", read_outs=None):
     """GSA fwd+bwd at its workload: gsa_fwd_save then gsa_bwd_saved (the training-step form, as
     for GLA), with the recomputing gsa_fwd + gsa_bwd timed beside it, and (read_outs, by
     default for the 64-slot workload only) the same step with each element-wise read-out."""
@@ -461,7 +461,7 @@ def run_gsa(torch, m, steps=10, warmup=3, name="gsa_340m", read_outs=None):
             "recomputing_ms_per_step": round(ms_re, 4), **({"read_out_ms_per_step": acts} if acts else {})}
 
 
-def run_long_fwd(torch, m, steps=10, warmup=3):
+def run_long_fwd(torch, m, steps=20, warmup=200):
     """The long-sequence forward (B=1, H=4, L=20480, Dk=128, Dv=256, C=64): few sequences, so
     the sequential state walk over 320 chunks sets the time."""
     import ctypes
@@ -508,7 +508,7 @@ def run_long_fwd(torch, m, steps=10, warmup=3):
                          "unit": "GB/s", "frac": round(ach / (PEAK_HBM_BYTES / 1e9), 4), "alg_bytes": kbytes[dom]}}
 
 
-def run_msgla(torch, m, steps=10, warmup=3):
+def run_msgla(torch, m, steps=20, warmup=200):
     """MS-GLA {1, 2, 4} forward on the 340M-layer shape, head budget split 2/1/1, with fusion
     weights; plain gla_fwd on the same inputs is timed beside it."""
     w = W.WORKLOADS["gla_340m"]
@@ -666,8 +666,10 @@ KERNEL_SYMBOLS = {"fwd.prep": "gla_prep_kernel", "fwd.walk": "walk_kernel", "fwd
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU's clocks ramp up over the first 10-15 ms of work after an idle spell: the default
+    # warm-up (about 20 ms of steps at the 340M shape) lets the timed steps run at steady clocks
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-calib-mb", type=float, default=0.0,
