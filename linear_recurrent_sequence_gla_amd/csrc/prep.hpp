@@ -64,20 +64,26 @@ struct ChunkMap {
   static constexpr int ACTIVE = NCG * NSEG;            // threads with work (<= NT)
 };
 
+// Threads of the preparation kernel: 256 (4 waves), two workgroups to a CU; 512 (8 waves) for
+// 16-bit inputs with 256-channel keys and chunks of at most 64 rows, whose 136 KB of LDS leave
+// room for one workgroup per CU: 256 threads would then keep only four waves on a CU, each
+// carrying eight rows of the chunk (1.3B-layer shape: 61 -> 47 us).  At 128 channels the
+// 512-thread form measured no faster than two 256-thread workgroups per CU.
+template <typename T, int DKP, int CP>
+constexpr int prep_threads() { return sizeof(T) == 2 && CP <= 64 && DKP >= 256 ? 512 : 256; }
+
 template <typename T, int DKP, int CP>
 struct PrepCfg {
-  using M = ChunkMap<T, DKP, CP>;
+  static constexpr int NT = prep_threads<T, DKP, CP>(), NW = NT / 64;
+  using M = ChunkMap<T, DKP, CP, NT>;
   static constexpr int PK = 16 / (int)sizeof(T);       // 16-byte row padding, in elements
   static constexpr int LDQ = DKP + PK;                 // row stride of the [CP][DKP] tiles
   static constexpr int LDC = CP + PK;                  // row stride of the [CP][CP] score tile
   static constexpr int LDP = 32 + PK;                  // row stride of the safe-path slice tiles
   static constexpr int NB = CP / 16;                   // 16-row sub-chunks per chunk
   static constexpr int NP = NB * (NB - 1) / 2;         // off-diagonal sub-block pairs
-  static constexpr int PPW = (NP + 3) / 4;             // pairs per wave
+  static constexpr int PPW = (NP + NW - 1) / NW;       // pairs per wave
   static constexpr bool SPLIT = sizeof(T) == 2;        // hi/lo operands ("Precision of A")
-  // the persistent loop (next chunk's loads carried through a chunk) fits the registers except
-  // for fp32 with the widest keys
-  static constexpr bool PERSIST = sizeof(T) == 2 || DKP <= 128;
   static constexpr size_t TILE = (size_t)CP * LDQ * sizeof(T);
   static constexpr size_t KD = TILE;                   // Kd [CP][DKP], copied out transposed
   static constexpr size_t ATILE = (size_t)CP * LDC * sizeof(T);
@@ -85,9 +91,18 @@ struct PrepCfg {
   static constexpr size_t FAST = (SPLIT ? 4 : 2) * TILE;
   static constexpr size_t SAFE = TILE + (size_t)3 * CP * 33 * 4 +
                                  (size_t)(SPLIT ? 2 : 1) * (CP + 16) * LDP * sizeof(T);
-  static constexpr size_t MAIN = cmax(cmax(FAST, SAFE), TILE + KD + ATILE);
-  static constexpr size_t MISC = (size_t)(M::NSEG * DKP + DKP + 8) * 4;
+  // the gate scan's segment totals ([NSEG][DKP] fp32) use the main region, which is free
+  // while a chunk's gates are scanned; Gamma and the block-max scratch stay apart
+  static constexpr size_t MAIN = cmax(cmax(cmax(FAST, SAFE), TILE + KD + ATILE), (size_t)M::NSEG * DKP * 4);
+  static constexpr size_t MISC = (size_t)(DKP + 8) * 4;
   static constexpr size_t BYTES = MAIN + MISC;
+  // A persistent grid (each chunk's loads in flight during the previous chunk's work) for
+  // 256-thread workgroups, except fp32 with the widest keys, whose registers cannot carry the
+  // next chunk's loads; and for 512-thread workgroups only where a CU holds one of them: two
+  // share a CU otherwise and overlap one another's loads and work, in 128 registers that leave
+  // no room for a second chunk's loads.
+  static constexpr bool PERSIST = NT == 512 ? BYTES > kMaxLds / 2 : (sizeof(T) == 2 || DKP <= 128);
+  static constexpr int MIN_WAVES = NT == 512 && !PERSIST ? 4 : 2;   // per SIMD, for the registers
 };
 
 // Copy a [rows][cols] tile (LDS row stride lds) to dense global memory, 16 bytes per access.
@@ -310,7 +325,7 @@ inline int device_cu_count() {
 // chunk's first row (a harmless, cached reload: the loads of a persistent loop's last round are
 // issued unconditionally)
 template <typename T, int DKP, int CP>
-__device__ __forceinline__ void prep_issue(const PrepParams& p, int n, int bh, ChunkScan<T, DKP, CP>& cs,
+__device__ __forceinline__ void prep_issue(const PrepParams& p, int n, int bh, ChunkScan<T, DKP, CP, true, prep_threads<T, DKP, CP>()>& cs,
                                            bool past) {
   const int row0 = n * p.C;
   const int len = past ? 1 : min(p.C, p.L - row0);
@@ -323,16 +338,17 @@ __device__ __forceinline__ void prep_issue(const PrepParams& p, int n, int bh, C
 // vectors dead), next() runs: a persistent caller issues its next chunk's loads there, so they
 // are in flight while this chunk is computed.
 template <typename T, int DKP, int CP, typename Next>
-__device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, ChunkScan<T, DKP, CP>& cs, Next&& next) {
+__device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh,
+                                           ChunkScan<T, DKP, CP, true, prep_threads<T, DKP, CP>()>& cs, Next&& next) {
   using Cfg = PrepCfg<T, DKP, CP>;
-  using M = ChunkMap<T, DKP, CP>;
-  constexpr int V = M::V, RPS = M::RPS;
+  using M = typename Cfg::M;
+  constexpr int V = M::V, RPS = M::RPS, NT = Cfg::NT, NW = Cfg::NW;
   constexpr int LDQ = Cfg::LDQ, LDC = Cfg::LDC, LDP = Cfg::LDP;
   constexpr int NB = Cfg::NB, NP = Cfg::NP, PPW = Cfg::PPW;
   typedef typename V16<T>::type VT;
   __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
-  float* segtot = reinterpret_cast<float*>(smem + Cfg::MAIN);
-  float* sGam = segtot + M::NSEG * DKP;
+  float* segtot = reinterpret_cast<float*>(smem);              // during the scan only
+  float* sGam = reinterpret_cast<float*>(smem + Cfg::MAIN);
   float* red = sGam + DKP;
 
   const int tid = threadIdx.x;
@@ -387,7 +403,7 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
   // ---- intra-chunk scores A, kept in registers until the LDS operands are released
   const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
   constexpr int NBLK = NB * NB;
-  constexpr int BPW = (NBLK + 3) / 4;        // score blocks per wave
+  constexpr int BPW = (NBLK + NW - 1) / NW;  // score blocks per wave
   f32x4 accA[BPW];
 #pragma unroll
   for (int s = 0; s < BPW; ++s) accA[s] = zero4();
@@ -396,7 +412,7 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
   if (fast) {
 #pragma unroll
     for (int s = 0; s < BPW; ++s) {
-      const int blk = wave + 4 * s;
+      const int blk = wave + NW * s;
       const int rb = blk / NB, cb = blk % NB;
       if (blk < NBLK && cb <= rb) {
 #pragma unroll
@@ -414,7 +430,7 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
     __syncthreads();   // score operands released: KdT and A reuse their bytes
 #pragma unroll
     for (int s = 0; s < BPW; ++s) {
-      const int blk = wave + 4 * s;
+      const int blk = wave + NW * s;
       if (blk < NBLK) {
         const int rb = blk / NB, cb = blk % NB;
 #pragma unroll
@@ -439,7 +455,8 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
     float acc_d[NB];
 #pragma unroll
     for (int x = 0; x < NB; ++x) acc_d[x] = 0.f;
-    const int rr = tid >> 4, cc = tid & 15;
+    const int rr = tid >> 4, cc = tid & 15;   // diagonal sub-block element (the first 256 threads)
+    const bool dgl = tid < 256;
     for (int sl = 0; sl < DKP / 32; ++sl) {
       __syncthreads();
       if (cs.active && c0 >= 32 * sl && c0 < 32 * sl + 32) {
@@ -456,7 +473,7 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
       }
       __syncthreads();
       // diagonal sub-blocks, element by element: exponent b_r - b_c <= 0 for c <= r
-      if (cc <= rr) {
+      if (dgl && cc <= rr) {
 #pragma unroll
         for (int x = 0; x < NB; ++x) {
           const int r = 16 * x + rr, c = 16 * x + cc;
@@ -469,7 +486,7 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
       // off-diagonal sub-blocks against reference row eps_y = b[16y + 15]
       for (int y = 0; y < NB - 1; ++y) {
         __syncthreads();
-        for (int e = tid; e < CP * 32; e += 256) {
+        for (int e = tid; e < CP * 32; e += NT) {
           const int r = e >> 5, ii = e & 31;
           const float eps = sbs[(16 * y + 15) * 33 + ii];
           if (r >= 16 * (y + 1)) {
@@ -489,7 +506,7 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
         __syncthreads();
 #pragma unroll
         for (int s = 0; s < PPW; ++s) {
-          const int pidx = wave + 4 * s;
+          const int pidx = wave + NW * s;
           if (pidx < NP) {
             int x, yy;
             pair_decode(pidx, x, yy);
@@ -509,7 +526,7 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
     __syncthreads();   // safe-path scratch released: KdT and A reuse its bytes
 #pragma unroll
     for (int s = 0; s < PPW; ++s) {
-      const int pidx = wave + 4 * s;
+      const int pidx = wave + NW * s;
       if (pidx < NP) {
         int x, y;
         pair_decode(pidx, x, y);
@@ -517,15 +534,17 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
         for (int e = 0; e < 4; ++e) sA[(16 * x + 4 * grp + e) * LDC + 16 * y + col] = from_f32<T>(acc_off[s][e]);
       }
     }
-    for (int blk = wave; blk < NBLK; blk += 4) {
+    for (int blk = wave; blk < NBLK; blk += NW) {
       const int rb = blk / NB, cb = blk % NB;
       if (cb > rb) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sA[(16 * rb + 4 * grp + e) * LDC + 16 * cb + col] = from_f32<T>(0.f);
       }
     }
+    if (dgl) {
 #pragma unroll
-    for (int x = 0; x < NB; ++x) sA[(16 * x + rr) * LDC + 16 * x + cc] = from_f32<T>(cc <= rr ? acc_d[x] : 0.f);
+      for (int x = 0; x < NB; ++x) sA[(16 * x + rr) * LDC + 16 * x + cc] = from_f32<T>(cc <= rr ? acc_d[x] : 0.f);
+    }
   }
 
   // ---- Kd = k 2^{Gamma - b} into LDS row by row; it leaves transposed (KdT)
@@ -539,7 +558,7 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
     }
   }
   __syncthreads();
-  tile_out_t<T, 4>(reinterpret_cast<T*>(p.ops.KdT) + chunk * DKP * CP, sKd, CP, DKP, LDQ);
+  tile_out_t<T, NW>(reinterpret_cast<T*>(p.ops.KdT) + chunk * DKP * CP, sKd, CP, DKP, LDQ);
   tile_out<T>(reinterpret_cast<T*>(p.ops.A) + chunk * CP * CP, sA, CP, CP, LDC);
   if (tid < DKP) p.ops.Gam[chunk * DKP + tid] = sGam[tid];
 }
@@ -548,8 +567,8 @@ __device__ __forceinline__ void prep_chunk(const PrepParams& p, int n, int bh, C
 // workgroup w takes tiles w, w + gridDim.x, ..., each tile's loads in flight during the
 // previous tile's computation
 template <typename T, int DKP, int CP>
-__global__ __launch_bounds__(256, 2) void gla_prep_kernel(PrepParams p, int ntiles) {
-  ChunkScan<T, DKP, CP> cs;
+__global__ __launch_bounds__((PrepCfg<T, DKP, CP>::NT), (PrepCfg<T, DKP, CP>::MIN_WAVES)) void gla_prep_kernel(PrepParams p, int ntiles) {
+  ChunkScan<T, DKP, CP, true, prep_threads<T, DKP, CP>()> cs;
   int t = blockIdx.x;
   prep_issue(p, t % p.N, t / p.N, cs, false);
   if constexpr (!PrepCfg<T, DKP, CP>::PERSIST) {    // one chunk per workgroup
@@ -572,13 +591,34 @@ __global__ __launch_bounds__(256, 2) void gla_prep_kernel(PrepParams p, int ntil
 // grid (max N, total sequences): blockIdx.y runs over the batches' sequences back to back;
 // blocks past a batch's own chunk count return at once
 template <typename T, int DKP, int CP>
-__global__ __launch_bounds__(256, 2) void gla_prep_batches(Batches<PrepParams> b) {
+__global__ __launch_bounds__((PrepCfg<T, DKP, CP>::NT), (PrepCfg<T, DKP, CP>::MIN_WAVES)) void gla_prep_batches(Batches<PrepParams> b) {
   const int gi = b.find(blockIdx.y);
   const PrepParams& p = b.p[gi];
   if ((int)blockIdx.x >= p.N) return;
-  ChunkScan<T, DKP, CP> cs;
+  ChunkScan<T, DKP, CP, true, prep_threads<T, DKP, CP>()> cs;
   prep_issue(p, blockIdx.x, blockIdx.y - b.first[gi], cs, false);
   prep_chunk<T, DKP, CP>(p, blockIdx.x, blockIdx.y - b.first[gi], cs, [] {});
+}
+
+// Workgroups of the persistent preparation kernel the device runs at once (CUs times the
+// workgroups one CU holds), cached per device
+template <typename T, int DKP, int CP>
+int prep_slots() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gla_prep_kernel<T, DKP, CP>, PrepCfg<T, DKP, CP>::NT, 0) !=
+          hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int cus = device_cu_count();
+  const int n = (cus > 0 ? cus : 256) * per_cu;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 template <typename T, int DKP, int CP>
@@ -586,9 +626,9 @@ hipError_t launch_prep(const PrepParams& p, int BH, hipStream_t s) {
   if constexpr (PrepCfg<T, DKP, CP>::BYTES > kMaxLds) {
     return hipErrorNotSupported;
   } else {
-    const int ntiles = p.N * BH, cus = device_cu_count();
-    const int grid = PrepCfg<T, DKP, CP>::PERSIST && cus > 0 ? imin(ntiles, 2 * cus) : ntiles;   // two per CU
-    hipLaunchKernelGGL((gla_prep_kernel<T, DKP, CP>), dim3(grid), dim3(256), 0, s, p, ntiles);
+    const int ntiles = p.N * BH;
+    const int grid = PrepCfg<T, DKP, CP>::PERSIST ? imin(ntiles, prep_slots<T, DKP, CP>()) : ntiles;
+    hipLaunchKernelGGL((gla_prep_kernel<T, DKP, CP>), dim3(grid), dim3(PrepCfg<T, DKP, CP>::NT), 0, s, p, ntiles);
     return hipGetLastError();
   }
 }
@@ -598,7 +638,7 @@ hipError_t launch_prep_batches(const Batches<PrepParams>& b, int maxN, hipStream
   if constexpr (PrepCfg<T, DKP, CP>::BYTES > kMaxLds) {
     return hipErrorNotSupported;
   } else {
-    hipLaunchKernelGGL((gla_prep_batches<T, DKP, CP>), dim3(maxN, b.first[b.n]), dim3(256), 0, s, b);
+    hipLaunchKernelGGL((gla_prep_batches<T, DKP, CP>), dim3(maxN, b.first[b.n]), dim3(PrepCfg<T, DKP, CP>::NT), 0, s, b);
     return hipGetLastError();
   }
 }
