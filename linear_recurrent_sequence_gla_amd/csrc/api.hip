@@ -263,6 +263,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* g, const f
   const OpsLayout ol = ops_layout(BH, N, CP, DKP, es);
   p.ops = carve_ops(static_cast<char*>(workspace), ol);
   p.Hs = static_cast<char*>(workspace) + ol.total;
+  p.keep_states = false;
   if (fwd_seg_bytes(B, H, L, Dk, Dv, C) > 0) {
     p.seg_ws = reinterpret_cast<float*>(static_cast<char*>(p.Hs) + align_up(BH * N * DKP * pad_dv(Dv) * es));
     p.seg_max = fwd_seg_max(B, H, L, Dk, Dv, C);

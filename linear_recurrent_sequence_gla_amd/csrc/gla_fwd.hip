@@ -15,7 +15,7 @@
 // the state update, so it is short per step and every matrix product of the outputs runs at
 // full occupancy.  A forward that keeps its activations for the backward leaves the states
 // where the backward finds them.
-#include "walks.hpp"
+#include "walk_out.hpp"
 
 namespace gla {
 
@@ -243,6 +243,22 @@ hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
     hipError_t e = p.ops_ready ? hipSuccess : launch_prep<T, DKP, CP>(pp, p.BH, s);
     if (e != hipSuccess) return e;
     record_event(p.events, 1, s);
+    // Enough sequences to give every CU a workgroup of 32 value columns: the walk and the
+    // outputs run as one kernel (walk_out.hpp), which writes the states only if they are kept;
+    // its time is recorded as the walk's and the output kernel's as zero.  Kept states need
+    // whole 64-column tiles: their padding columns, which the backward reads, are not written.
+    if constexpr (walk_out_fits<T, DKP, CP>()) {
+      const int cus = device_cu_count();
+      const int cols = p.keep_states ? kDvTile : kWoCols;
+      if (!p.states_ready && !p.hold_o && p.Dv % cols == 0 && cus > 0 && p.Dv / kWoCols * p.BH >= cus) {
+        FwdParams pf = p;
+        if (!p.keep_states) pf.Hs = nullptr;
+        if ((e = launch_walk_out<T, DKP, CP>(pf, s)) != hipSuccess) return e;
+        record_event(p.events, 2, s);
+        record_event(p.events, 3, s);
+        return hipSuccess;
+      }
+    }
     WalkIO wf{p.ops.KdT, p.v, p.ops.Gam, p.Hs, p.h0, p.ht, p.Dk, p.Dv, p.L, p.C, p.N, 0, p.in};
     // few, long sequences: the walk runs in segments and the output kernel adds each state's
     // carried part as it stages it (these states serve only that kernel)

@@ -62,6 +62,7 @@ struct FwdParams {
   void* Hs;       // [BH][N][DKP][DvP] chunk-start states (T), written by the state walk
   bool states_ready = false;   // Hs (and ht) already hold the walk's result: no walk is run
   bool ops_ready = false;      // ops.Qs and ops.A already hold the chunk operands: no preparation
+  bool keep_states = true;     // Hs must hold the chunk-start states afterwards (else it is scratch)
   LaunchEvents events;
   SeqView in;     // input sequences read by the launch
   // optional scratch for a segmented state walk (walks.hpp), room for seg_max segments:

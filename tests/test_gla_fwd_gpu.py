@@ -74,6 +74,25 @@ def test_small_shapes(gla, shape):
     check_fwd(gla, w, W.gla_inputs(w, with_grad=False))
 
 
+# Enough sequences that the 32-column tiles give each CU of a 256-CU device a workgroup: the
+# walk and the outputs run as one kernel, which keeps no states for gla_fwd
+FUSED_SHAPES = [
+    # (B, H, L, Dk, Dv, C, dtype, h0)
+    (64, 4, 100, 128, 32, 64, "bf16", True),     # ragged last chunk
+    (32, 4, 200, 112, 64, 64, "bf16", False),    # padded key rows, no initial state
+    (16, 4, 129, 128, 128, 64, "bf16", True),    # last chunk of one row (odd chunk count)
+    (64, 4, 64, 128, 32, 64, "bf16", True),      # one chunk
+    (64, 4, 128, 128, 32, 64, "bf16", True),     # two chunks
+]
+
+
+@pytest.mark.parametrize("shape", FUSED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_fused_walk_output_shapes(gla, shape):
+    B, H, L, Dk, Dv, C, dt, h0 = shape
+    w = W.GlaWorkload("fused", B, H, L, Dk, Dv, C, dt, 91 + L + Dk, h0=h0, gate_law="iid")
+    check_fwd(gla, w, W.gla_inputs(w, with_grad=False))
+
+
 @pytest.mark.parametrize("C", [16, 32, 64, 128])
 def test_chunk_size_independence(gla, C):
     """Same inputs, every chunk size: each result matches the oracle (and so each other)."""

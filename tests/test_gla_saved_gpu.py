@@ -58,6 +58,12 @@ SHAPES = [
     (1, 2, 1, 128, 64, 64, "bf16", True, True),
     (2, 2, 90, 48, 32, 16, "f32", True, True),
     (1, 2, 70, 128, 96, 64, "f32", True, True),
+    # the walk and the outputs as one kernel (32-column tiles filling a 256-CU device), which
+    # keeps the states for the backward; with 32 value columns (states padded to 64) the plain
+    # walk keeps them instead
+    (32, 4, 100, 128, 64, 64, "bf16", True, True),
+    (64, 4, 100, 128, 32, 64, "bf16", True, True),
+    (16, 4, 129, 128, 128, 64, "bf16", True, False),
 ]
 
 
@@ -84,11 +90,13 @@ def test_full_size_config_sampled(gla):
     check_saved(gla, w, x, units=units, with_dht=False)
 
 
-def test_matches_recomputing_backward(gla):
+@pytest.mark.parametrize("B,H", [(2, 2), (16, 4)], ids=["walk", "fused-walk-output"])
+def test_matches_recomputing_backward(gla, B, H):
     """gla_bwd_saved and gla_bwd agree to within rounding (they differ only in how the
-    chunk-start states were accumulated)."""
+    chunk-start states were accumulated: at B=16, H=4 the saving forward runs the walk and the
+    outputs as one kernel, the recomputing backward the plain walk)."""
     import torch
-    w = W.GlaWorkload("saved-vs-bwd", 2, 2, 257, 128, 128, 64, "bf16", 423, h0=True, gate_law="iid")
+    w = W.GlaWorkload("saved-vs-bwd", B, H, 257, 128, 128, 64, "bf16", 423, h0=True, gate_law="iid")
     x = W.gla_inputs(w)
     q, k, v, g, do = (dev(x[n], "bf16") for n in ("q", "k", "v", "g", "do"))
     h0, dht = dev(x["h0"]), dev(x["dht"])
