@@ -94,6 +94,7 @@ def kernel_alg_bytes(B, H, L, Dk, Dv, s=2):
         "fwd.prep": u * s * 3 * Dk,                            # q, k, g
         "fwd.walk": u * s * Dv,                                # v (states are workspace)
         "fwd.out": u * s * 2 * Dv,                             # v in, o out
+        "fwd.walk_out": u * s * 2 * Dv,                        # v in, o out (walk and outputs fused)
         "bwd.prep": u * s * 3 * Dk,                            # q, k, g (self-contained backward)
         "bwd.walk_fwd": u * s * Dv,                            # v
         "bwd.walk_rev": u * s * Dv,                            # do
@@ -227,7 +228,9 @@ def run_gla(torch, m, steps, warmup, name=WORKLOAD):
     for k in range(steps):
         step(hf[k], hb[k], k)
     torch.cuda.synchronize()
-    names_f = ["fwd.prep", "fwd.walk", "fwd.out"]
+    # the state walk and the chunk outputs run as one kernel where gla_fwd_launch_count says 2
+    fused = lib.gla_fwd_launch_count(B, H, L, Dk, Dv, C, 1, 1) == 2
+    names_f = ["fwd.prep", "fwd.walk_out"] if fused else ["fwd.prep", "fwd.walk", "fwd.out"]
     names_b = ["bwd.walk_rev", "bwd.chunk", "bwd.dv"][:nb]
     kt = {}
     for i, nme in enumerate(names_f):
@@ -489,14 +492,16 @@ def run_long_fwd(torch, m, steps=20, warmup=200):
     for k in range(steps):                              # each kernel's duration
         fwd(hs[k])
     torch.cuda.synchronize()
+    fused = lib.gla_fwd_launch_count(w.B, w.H, w.L, w.Dk, w.Dv, w.C, 1, 0) == 2
     kt = {nme: [evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(steps)]
-          for i, nme in enumerate(("prep", "walk", "out"))}
+          for i, nme in enumerate(("prep", "walk_out") if fused else ("prep", "walk", "out"))}
     alg = algorithmic(w.B, w.H, w.L, w.Dk, w.Dv, w.C)
     tflops = alg["flops_fwd"] / (ms * 1e-3) / 1e12
     kmean = {k: float(np.mean(v)) for k, v in kt.items()}
     dom = max(kmean, key=kmean.get)
     u = w.B * w.H * w.L
-    kbytes = {"prep": u * 2 * 3 * w.Dk, "walk": u * 2 * w.Dv + w.B * w.H * w.Dk * w.Dv * 4, "out": u * 2 * 2 * w.Dv}
+    kbytes = {"prep": u * 2 * 3 * w.Dk, "walk": u * 2 * w.Dv + w.B * w.H * w.Dk * w.Dv * 4, "out": u * 2 * 2 * w.Dv,
+              "walk_out": u * 2 * 2 * w.Dv + w.B * w.H * w.Dk * w.Dv * 4}
     ach = kbytes[dom] / (kmean[dom] * 1e-3) / 1e9
     return {"workload": f"gla_long forward B={w.B} H={w.H} L={w.L} Dk={w.Dk} Dv={w.Dv} C={w.C}, final state kept",
             "ms": round(ms, 4), "ms_median": round(float(np.median(per)), 4), "ms_min": round(float(np.min(per)), 4),
@@ -657,6 +662,7 @@ def traffic_for(kernel):
 
 
 KERNEL_SYMBOLS = {"fwd.prep": "gla_prep_kernel", "fwd.walk": "walk_kernel", "fwd.out": "gla_fwd_out",
+                  "fwd.walk_out": "walk_out_kernel",
                   "bwd.prep": "gla_prep_kernel",
                   "bwd.walk_fwd": "walk_kernel", "bwd.walk_rev": "walk_kernel", "bwd.chunk": "gla_bwd_chunk",
                   "bwd.dv": "gla_bwd_dv"}

@@ -146,7 +146,8 @@ int gla_bwd(const void* q, const void* k, const void* v, const void* g, const fl
 /* ---------------------------------------------------------------- profiling ------------
  * Same as gla_fwd / gla_bwd, and additionally records caller-created hipEvent_t handles on
  * `stream` at kernel boundaries: events[0] before the first kernel, events[i] after the i-th
- * (gla_fwd launches 3 kernels: chunk preparation, state walk, chunk outputs; gla_bwd launches
+ * (gla_fwd launches 3 kernels: chunk preparation, state walk, chunk outputs, or 2 of them per
+ * gla_fwd_launch_count(), events[2] and events[3] then both after the second; gla_bwd launches
  * gla_bwd_launch_count() kernels: chunk preparation, forward state walk, reverse state walk,
  * chunk gradients, and a value-gradient kernel when the key width is split).  nevents must
  * be at least 4 (forward) or 6 (backward), else GLA_ERR_NULL_ARG.  The events are owned by the caller and are only
@@ -162,6 +163,13 @@ int gla_bwd_profiled(const void* q, const void* k, const void* v, const void* g,
                      void* workspace, size_t workspace_bytes, void* stream, void** events, int nevents);
 /* Number of kernels gla_bwd launches for these sizes (0 if unsupported). */
 int gla_bwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype);
+/* Kernel phases of gla_fwd (keep_states = 0) or gla_fwd_save (keep_states = 1) for these sizes
+ * on the current device: 3 (chunk preparation, state walk, chunk outputs), or 2 where the state
+ * walk and the chunk outputs run as one kernel (bf16, Dk in 97..128, C in 33..64, B*H*Dv/32 at
+ * least the device's compute units, and Dv a multiple of 32, or of 64 with keep_states); 0 if
+ * unsupported.  With 2, the profiled entry points record events[2] and events[3] both after
+ * the fused kernel.  Pure host query: nothing is enqueued. */
+int gla_fwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype, int keep_states);
 
 /* ---------------------------------------------------------------- GLA saved activations --
  * A training step runs the forward and then the backward on the same q, k, v, g, h0.  The

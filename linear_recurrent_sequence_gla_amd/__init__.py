@@ -71,6 +71,7 @@ _SIGS = {
     "gla_fwd_profiled": (_I, [_P] * 7 + [_I] * 7 + [_P, _Z, _P, _P, _I]),
     "gla_bwd_profiled": (_I, [_P] * 12 + [_I] * 7 + [_P, _Z, _P, _P, _I]),
     "gla_bwd_launch_count": (_I, [_I] * 7),
+    "gla_fwd_launch_count": (_I, [_I] * 8),
     "gla_saved_bytes": (_Z, [_I] * 7),
     "gla_bwd_saved_workspace_bytes": (_Z, [_I] * 7),
     "gla_fwd_save": (_I, [_P] * 7 + [_I] * 7 + [_P, _Z, _P, _P, _I]),

@@ -489,6 +489,13 @@ int gla_bwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype) 
   return bwd_launch_count(esize_of(dtype), pad_dk(Dk), pad_c(C));
 }
 
+int gla_fwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype, int keep_states) {
+  if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
+  const int es = esize_of(dtype), DKP = pad_dk(Dk), CP = pad_c(C);
+  if (keep_states && !bwd_config_fits(es, DKP, CP)) return 0;
+  return fwd_fused(es, DKP, CP, B * H, Dv, keep_states != 0) ? 2 : 3;
+}
+
 int gla_decode_step(const void* q, const void* k, const void* v, const void* g, float* state,
                     void* o, int B, int H, int Dk, int Dv, int dtype, void* stream) {
   if (dtype != GLA_F32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;

@@ -245,12 +245,9 @@ hipError_t launch_gla_fwd(const FwdParams& p, hipStream_t s) {
     record_event(p.events, 1, s);
     // Enough sequences to give every CU a workgroup of 32 value columns: the walk and the
     // outputs run as one kernel (walk_out.hpp), which writes the states only if they are kept;
-    // its time is recorded as the walk's and the output kernel's as zero.  Kept states need
-    // whole 64-column tiles: their padding columns, which the backward reads, are not written.
+    // its time is recorded as the walk's and the output kernel's as zero
     if constexpr (walk_out_fits<T, DKP, CP>()) {
-      const int cus = device_cu_count();
-      const int cols = p.keep_states ? kDvTile : kWoCols;
-      if (!p.states_ready && !p.hold_o && p.Dv % cols == 0 && cus > 0 && p.Dv / kWoCols * p.BH >= cus) {
+      if (!p.states_ready && !p.hold_o && walk_out_applies(p.BH, p.Dv, p.keep_states)) {
         FwdParams pf = p;
         if (!p.keep_states) pf.Hs = nullptr;
         if ((e = launch_walk_out<T, DKP, CP>(pf, s)) != hipSuccess) return e;
@@ -328,6 +325,15 @@ hipError_t launch_gla_fwd_batches(const FwdParams* ps, int nb, hipStream_t s) {
       hipLaunchKernelGGL((gla_fwd_out_batches<T, DKP, CP, false>), dim3(bo.first[nb]), dim3(256), 0, s, bo, ntile);
     return hipGetLastError();
   }
+}
+
+bool fwd_fused(int esize, int DKP, int CP, int BH, int Dv, bool keep_states) {
+  bool fits = false;
+#define GLA_FUSED_CASE(D, C_) \
+  if (esize == (int)sizeof(bf16) && DKP == D && CP == C_) fits = walk_out_fits<bf16, D, C_>();
+  GLA_FUSED_CASE(128, 64)
+#undef GLA_FUSED_CASE
+  return fits && walk_out_applies(BH, Dv, keep_states);
 }
 
 bool fwd_config_fits(int esize, int DKP, int CP) {

@@ -235,6 +235,8 @@ int bwd_launch_count(int esize, int DKP, int CP);   // self-contained backward; 
 
 // Whether every kernel of the forward fits the LDS of a CU for this (dtype size, DKP, CP).
 bool fwd_config_fits(int esize, int DKP, int CP);
+// whether the forward runs its state walk and chunk outputs as one kernel (walk_out.hpp)
+bool fwd_fused(int esize, int DKP, int CP, int BH, int Dv, bool keep_states);
 // Same for the backward kernels.
 bool bwd_config_fits(int esize, int DKP, int CP);
 

@@ -284,6 +284,16 @@ constexpr bool walk_out_fits() {
   return WalkOutCfg<T, DKP, CP>::OK;
 }
 
+// Whether a forward of BH sequences of Dv value columns runs the fused kernel (on a shape it
+// fits): when its 32-column tiles give every CU of the current device a workgroup.  Kept
+// states need whole 64-column tiles: their padding columns, which the backward reads, are not
+// written.
+inline bool walk_out_applies(int BH, int Dv, bool keep_states) {
+  const int cus = device_cu_count();
+  const int cols = keep_states ? kDvTile : kWoCols;
+  return Dv % cols == 0 && cus > 0 && (long long)(Dv / kWoCols) * BH >= cus;
+}
+
 // The fused walk and outputs for p (p.Hs null: states not kept); the caller has checked
 // walk_out_fits and that Dv is a multiple of 32.
 template <typename T, int DKP, int CP>

@@ -97,6 +97,12 @@ def test_workspace_sizes(lib):
     assert lib.gla_fwd_workspace_bytes(1, 1, 64, 16, 16, 48, 1) == 0
     assert lib.gla_bwd_launch_count(B, H, L, Dk, Dv, C, 1) == 4
     assert lib.gla_bwd_launch_count(4, 4, 4096, 256, 512, 64, 1) == 5
+    # the forward's kernel phases: 3, or 2 where the walk and the outputs run as one kernel,
+    # which depends on the device's compute units (none here: 3)
+    assert lib.gla_fwd_launch_count(B, H, L, Dk, Dv, C, 1, 0) in (2, 3)
+    assert lib.gla_fwd_launch_count(B, H, L, Dk, Dv, C, 1, 1) in (2, 3)
+    assert lib.gla_fwd_launch_count(1, 1, 64, 16, 16, 64, 0, 0) == 3     # fp32: never fused
+    assert lib.gla_fwd_launch_count(1, 1, 64, 16, 16, 48, 1, 0) == 0     # unsupported chunk size
 
 
 def test_forward_workspace_keeps_room_for_a_segmented_walk(lib):

@@ -93,6 +93,18 @@ def test_fused_walk_output_shapes(gla, shape):
     check_fwd(gla, w, W.gla_inputs(w, with_grad=False))
 
 
+def test_fused_launch_count(gla):
+    """gla_fwd_launch_count reports the fused walk-output kernel exactly where 32-column tiles
+    give every compute unit a workgroup (and 64-column multiples when the states are kept)."""
+    import torch
+    lib = gla.lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for B, H, Dv, keep in ((8, 4, 256, 1), (8, 4, 256, 0), (64, 4, 32, 0), (64, 4, 32, 1), (1, 2, 256, 0)):
+        fused = B * H * Dv // 32 >= cus and Dv % (64 if keep else 32) == 0
+        assert lib.gla_fwd_launch_count(B, H, 2048, 128, Dv, 64, 1, keep) == (2 if fused else 3), (B, H, Dv, keep)
+    assert lib.gla_fwd_launch_count(64, 4, 2048, 128, 256, 64, 0, 0) == 3      # fp32: never fused
+
+
 @pytest.mark.parametrize("C", [16, 32, 64, 128])
 def test_chunk_size_independence(gla, C):
     """Same inputs, every chunk size: each result matches the oracle (and so each other)."""
