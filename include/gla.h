@@ -165,7 +165,7 @@ int gla_bwd_profiled(const void* q, const void* k, const void* v, const void* g,
 int gla_bwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype);
 /* Kernel phases of gla_fwd (keep_states = 0) or gla_fwd_save (keep_states = 1) for these sizes
  * on the current device: 3 (chunk preparation, state walk, chunk outputs), or 2 where the state
- * walk and the chunk outputs run as one kernel (bf16, Dk in 97..128, C in 33..64, B*H*Dv/32 at
+ * walk and the chunk outputs run as one kernel (bf16, Dk in 65..128, C = 64, B*H*Dv/32 at
  * least the device's compute units, and Dv a multiple of 32, or of 64 with keep_states); 0 if
  * unsupported.  With 2, the profiled entry points record events[2] and events[3] both after
  * the fused kernel.  Pure host query: nothing is enqueued. */

@@ -80,6 +80,7 @@ FUSED_SHAPES = [
     # (B, H, L, Dk, Dv, C, dtype, h0)
     (64, 4, 100, 128, 32, 64, "bf16", True),     # ragged last chunk
     (32, 4, 200, 112, 64, 64, "bf16", False),    # padded key rows, no initial state
+    (64, 4, 150, 80, 32, 64, "bf16", True),      # 48 padded key rows
     (16, 4, 129, 128, 128, 64, "bf16", True),    # last chunk of one row (odd chunk count)
     (64, 4, 64, 128, 32, 64, "bf16", True),      # one chunk
     (64, 4, 128, 128, 32, 64, "bf16", True),     # two chunks
