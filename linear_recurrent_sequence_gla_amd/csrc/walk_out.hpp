@@ -207,10 +207,10 @@ __global__ __launch_bounds__(kWoThreads) void walk_out_kernel(FwdParams p, int n
   if (hs) state_out(0, 0);
 
   // Step k (register stage r = k % 2, LDS buffers b = k % 2): the next-but-one chunk's loads
-  // into the register stage whose tiles went to LDS in the previous step, T_k and O_k from
-  // the staged tiles (O_k into its LDS tile), the fold into H_{k+1} (its bf16 copy into the
-  // other buffer), chunk k+1's tiles into the other buffer, one barrier, O_k and H_{k+1} out.
-  // LAST: the final step, whose H_N is not a chunk-start state.
+  // into the register stage whose tiles went to LDS in the previous step, T_k from the staged
+  // tiles, the fold into H_{k+1} (its bf16 copy into the other buffer), O_k from the staged
+  // tiles and H_k's copy (into its LDS tile), chunk k+1's tiles into the other buffer, one
+  // barrier, O_k and H_{k+1} out.  LAST: the final step, whose H_N is not a chunk-start state.
   auto body = [&](auto rc, int k, auto lc) {
     constexpr int r = decltype(rc)::value;
     constexpr bool LAST = decltype(lc)::value;
@@ -227,6 +227,14 @@ __global__ __launch_bounds__(kWoThreads) void walk_out_kernel(FwdParams p, int n
       for (int cb = 0; cb < W::NCB; ++cb)
         mma(Tm[ib], Yv[cb], ld8(sKT(b) + (ri + 16 * ib + col) * LDA + 32 * cb + 8 * grp));
     }
+    const float* gg = sG(b);
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+      const float dec = fast_exp2(gg[ri + 16 * ib + col]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[ib][e] = dec * S[ib][e] + Tm[ib][e];
+    }
+    put_state(b ^ 1);
     // O_k^T block: X = H_k column run (out column), Y = Qs_k / A_k row (out row)
     f32x4 O = zero4();
     const int ro = 16 * rbo + col;
@@ -241,14 +249,6 @@ __global__ __launch_bounds__(kWoThreads) void walk_out_kernel(FwdParams p, int n
       for (int e = 0; e < 4; ++e) o4[e] = from_f32<T>(O[e]);
       *reinterpret_cast<V4T*>(sO(b) + ro * LDV + cw + 4 * grp) = o4;
     }
-    const float* gg = sG(b);
-#pragma unroll
-    for (int ib = 0; ib < NIB; ++ib) {
-      const float dec = fast_exp2(gg[ri + 16 * ib + col]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[ib][e] = dec * S[ib][e] + Tm[ib][e];
-    }
-    put_state(b ^ 1);
     st[r ^ 1].store(sKT(b ^ 1), sV(b ^ 1), sQ(b ^ 1), sA(b ^ 1), sG(b ^ 1), tid);
     __syncthreads();
     out_tile(b, k);
