@@ -83,6 +83,7 @@ FUSED_SHAPES = [
     (64, 4, 150, 80, 32, 64, "bf16", True),      # 48 padded key rows
     (16, 4, 129, 128, 128, 64, "bf16", True),    # last chunk of one row (odd chunk count)
     (64, 4, 64, 128, 32, 64, "bf16", True),      # one chunk
+    (64, 4, 1, 128, 32, 64, "bf16", True),       # one token
     (64, 4, 128, 128, 32, 64, "bf16", True),     # two chunks
 ]
 

@@ -64,6 +64,7 @@ SHAPES = [
     (32, 4, 100, 128, 64, 64, "bf16", True, True),
     (64, 4, 100, 128, 32, 64, "bf16", True, True),
     (16, 4, 129, 128, 128, 64, "bf16", True, False),
+    (32, 4, 1, 128, 64, 64, "bf16", True, True),     # one token
 ]
 
 
