@@ -190,7 +190,8 @@ int gla_fwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype, 
  *   64, pad(Dk) = 32, 64, 128 or 256), about 130 MB at B=8, H=4, L=2048, Dk=128, Dv=256.
  * workspace (gla_bwd_saved): at least gla_bwd_saved_workspace_bytes() bytes.
  * events / nevents: optional (NULL, 0) launch-boundary events as for gla_*_profiled:
- *   gla_fwd_save launches 3 kernels (nevents >= 4), gla_bwd_saved launches
+ *   gla_fwd_save launches 3 kernels, or 2 per gla_fwd_launch_count(..., 1) (nevents >= 4 either
+ *   way), gla_bwd_saved launches
  *   gla_bwd_launch_count() - 2 kernels (nevents >= 4).
  * Sizes, dtypes, alignment and errors as for gla_bwd (the saved path supports the sizes the
  * backward supports); `saved` must not overlap any input or output (GLA_ERR_ALIAS). */

@@ -1,6 +1,6 @@
 // gla_fwd.hip -- chunkwise GLA forward on gfx950.
 //
-// Three launches per call:
+// Three kernel phases per call:
 //   1. gla_prep_kernel  (grid N x BH): per chunk, the decayed operands Qs, KdT, Gamma and the
 //      masked intra-chunk scores A (prep.hpp).  Fully parallel over chunks.
 //   2. state walk       (walks.hpp): the only sequential part -- H_{n+1} = Diag(2^Gamma_n) H_n
@@ -13,8 +13,9 @@
 // inter-chunk updates, parallel intra-chunk computation.  The chunk-start states cost one
 // write and one read of B*H*N*Dk*Dv elements; in exchange the sequential walk carries only
 // the state update, so it is short per step and every matrix product of the outputs runs at
-// full occupancy.  A forward that keeps its activations for the backward leaves the states
-// where the backward finds them.
+// full occupancy.  Where 32-column tiles give every CU a workgroup, phases 2 and 3 run as one
+// kernel instead (walk_out.hpp), which never reads the states back.  A forward that keeps its
+// activations for the backward leaves the states where the backward finds them.
 #include "walk_out.hpp"
 
 namespace gla {

@@ -228,7 +228,8 @@ template <typename T, int MP, int CP>
 hipError_t launch_gsa_bwd(const GsaParams& p, hipStream_t s);
 bool gsa_config_fits(int esize, int MP, int CP, bool bwd);   // bwd: the backward's kernels too
 
-// Kernel launches per call (for the profiled entry points).
+// Kernel phases per call (for the profiled entry points; the forward's walk and outputs may be
+// one kernel, whose events then bracket both phases).
 constexpr int GLA_FWD_LAUNCHES = 3;
 constexpr int GLA_BWD_MAX_LAUNCHES = 5;
 int bwd_launch_count(int esize, int DKP, int CP);   // self-contained backward; 2 fewer when saved
