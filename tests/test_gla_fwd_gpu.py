@@ -107,6 +107,38 @@ def test_fused_launch_count(gla):
     assert lib.gla_fwd_launch_count(64, 4, 2048, 128, 256, 64, 0, 0) == 3      # fp32: never fused
 
 
+def test_fused_profiled_events(gla):
+    """gla_fwd_profiled on a fused shape: the same outputs as gla_fwd, and its events bracket
+    the preparation and the fused kernel, with nothing between events[2] and events[3]."""
+    import ctypes
+    import torch
+    lib = gla.lib()
+    B, H, L, Dk, Dv, C = 64, 4, 100, 128, 32, 64
+    if lib.gla_fwd_launch_count(B, H, L, Dk, Dv, C, 1, 0) != 2:
+        pytest.skip("the fused walk-output kernel does not apply on this device")
+    w = W.GlaWorkload("fused-ev", B, H, L, Dk, Dv, C, "bf16", 95, h0=True, gate_law="iid")
+    x = W.gla_inputs(w, with_grad=False)
+    q, k, v, g = (dev(x[n], "bf16") for n in ("q", "k", "v", "g"))
+    h0 = dev(x["h0"])
+    o_ref, ht_ref = gla.gla_fwd(q, k, v, g, C=C, h0=h0)
+    o, ht = torch.empty_like(o_ref), torch.empty_like(ht_ref)
+    ws = torch.empty(lib.gla_fwd_workspace_bytes(B, H, L, Dk, Dv, C, 1), dtype=torch.uint8, device="cuda")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    handles = (ctypes.c_void_p * 4)(*[e.cuda_event for e in evs])
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = lib.gla_fwd_profiled(P(q), P(k), P(v), P(g), P(h0), P(o), P(ht), B, H, L, Dk, Dv, C, 1, P(ws), ws.numel(),
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), handles, 4)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(ht, ht_ref)
+    t = [evs[i].elapsed_time(evs[i + 1]) for i in range(3)]
+    print(f"  prep {t[0] * 1e3:.1f} us, walk+out {t[1] * 1e3:.1f} us, after {t[2] * 1e3:.1f} us", flush=True)
+    assert t[0] > 0 and t[1] > 0 and t[2] * 1e3 < 10.0      # nothing runs between events[2] and [3]
+
+
 @pytest.mark.parametrize("C", [16, 32, 64, 128])
 def test_chunk_size_independence(gla, C):
     """Same inputs, every chunk size: each result matches the oracle (and so each other)."""
