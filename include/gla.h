@@ -40,9 +40,11 @@
  *     gla_decode_step, which is updated in place.
  *   - Supported sizes: B, H >= 1; L >= 1 (any value; the last chunk may be partial);
  *     C in {16, 32, 64, 128}; Dk and m multiples of 16 up to 256; Dv a multiple of 16 up to
- *     512; B*H <= 65535; every tensor 16-byte aligned.  Chunk tiles must fit a CU's LDS:
- *     bf16 excludes Dk > 128 with C = 128; float32 (a parity dtype) excludes Dk > 128 with
- *     C = 64, Dk > 64 with C = 128 and, for the backward, every Dk with C = 128.  Other
+ *     512; B*H <= 65535; every tensor 16-byte aligned.  The result does not depend on C, a
+ *     tiling choice: where the requested C's chunk tiles do not fit a CU's LDS (bf16 with
+ *     Dk > 128 and C = 128; float32 with Dk > 128 and C = 64, Dk > 64 and C = 128, and every
+ *     backward with C = 128), the call runs with the largest smaller C whose tiles fit, the
+ *     same for a saving forward and its backward, and the sizes queried follow it.  Other
  *     values return GLA_ERR_UNSUPPORTED (shape errors such as L < 1 return GLA_ERR_SHAPE);
  *     a *_workspace_bytes() query returns 0 for them.
  *   - Results are deterministic: no floating-point atomics are used, so two runs on the same
@@ -220,10 +222,11 @@ int gla_decode_step(const void* q, const void* k, const void* v, const void* g,
                     int B, int H, int Dk, int Dv, int dtype, void* stream);
 
 /* ---------------------------------------------------------------- GSA forward ----------
- * Supported: C in {16, 32, 64}; m a multiple of 16 up to 128; Dk a multiple of 16 up to 256;
- * Dv a multiple of 16 up to 512 (others: GLA_ERR_UNSUPPORTED).  The backward (gsa_bwd,
- * gsa_fwd_save, gsa_bwd_saved) needs its pass-1 tiles in a CU's LDS: with m > 64 it takes
- * C in {16, 32}, and float32 takes m <= 64 with C in {16, 32} (gsa_fwd takes the rest).
+ * Supported: C in {16, 32, 64, 128}; m a multiple of 16 up to 128; Dk a multiple of 16 up to
+ * 256; Dv a multiple of 16 up to 512 (others: GLA_ERR_UNSUPPORTED).  As for GLA, C is a tiling
+ * choice: the GSA kernels tile chunks of at most 64 rows, and the backward (gsa_bwd,
+ * gsa_fwd_save, gsa_bwd_saved) of at most 32 with m > 64 (and of float32 with m = 64), so a
+ * larger C runs at the largest that fits.  float32 with m > 64 has a forward only.
  * act: a gsa_act value.
  *   q, k : [B,H,L,Dk] dtype;  v : [B,H,L,Dv] dtype;  g : [B,H,L,m] dtype slot log-gates
  *   hk0  : [B,H,Dk,m] float32 initial pass-1 state or NULL;  hv0 : [B,H,m,Dv] or NULL

@@ -52,6 +52,25 @@ int check_dims(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
   return GLA_OK;
 }
 
+// The chunk size the kernels tile a call with.  The operator's result does not depend on the
+// chunk size (chunks only regroup the same recurrence: sequential state passing between them,
+// the parallel form inside), so where the requested size's tiles do not fit a CU's LDS the call
+// runs with the largest smaller supported size whose tiles do, and computes the same outputs to
+// rounding.  bwd: the backward's kernels must fit too (backward, saving forward and their
+// sizes, so that a saving forward and its backward agree).  A size nothing fits under comes
+// back unchanged, for the checks to refuse.
+int gla_tile_c(int Dk, int C, int dtype, bool bwd) {
+  if (!valid_c(C) || (dtype != GLA_F32 && dtype != GLA_BF16) || Dk < 1 || Dk > 256) return C;
+  const int es = esize_of(dtype), DKP = pad_dk(Dk);
+  for (int c = C; c >= 16; c /= 2) {
+    const int CP = pad_c(c);
+    if (DKP == 256 && CP == 128) continue;
+    if (!fwd_config_fits(es, DKP, CP) || (bwd && !bwd_config_fits(es, DKP, CP))) continue;
+    return c;
+  }
+  return C;
+}
+
 struct Range {
   const void* p;
   size_t bytes;
@@ -227,11 +246,13 @@ const char* gla_status_str(int s) {
 }
 
 size_t gla_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  C = gla_tile_c(Dk, C, dtype, false);
   if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
   return fwd_ws_bytes(B, H, L, Dk, Dv, C, dtype);
 }
 
 size_t gla_bwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  C = gla_tile_c(Dk, C, dtype, true);
   if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
   if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return 0;
   return bwd_layout(B, H, L, Dk, Dv, C, dtype).total;
@@ -244,6 +265,7 @@ namespace {
 int fwd_impl(const void* q, const void* k, const void* v, const void* g, const float* h0,
              void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype,
              void* workspace, size_t workspace_bytes, void* stream, LaunchEvents ev) {
+  C = gla_tile_c(Dk, C, dtype, false);
   int st = check_dims(B, H, L, Dk, Dv, C, dtype);
   if (st != GLA_OK) return st;
   if (!q || !k || !v || !g || !o) return GLA_ERR_NULL_ARG;
@@ -276,6 +298,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const void* g, const f
 int fwd_save_impl(const void* q, const void* k, const void* v, const void* g, const float* h0,
                   void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype,
                   void* saved, size_t saved_bytes, void* stream, LaunchEvents ev) {
+  C = gla_tile_c(Dk, C, dtype, true);
   int st = check_dims(B, H, L, Dk, Dv, C, dtype);
   if (st != GLA_OK) return st;
   if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return GLA_ERR_UNSUPPORTED;
@@ -304,6 +327,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const void* g, const f
              const void* do_, const float* dht, void* dq, void* dk, void* dv, float* dg,
              float* dh0, int B, int H, int L, int Dk, int Dv, int C, int dtype,
              void* workspace, size_t workspace_bytes, void* stream, LaunchEvents ev) {
+  C = gla_tile_c(Dk, C, dtype, true);
   int st = check_dims(B, H, L, Dk, Dv, C, dtype);
   if (st != GLA_OK) return st;
   if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return GLA_ERR_UNSUPPORTED;
@@ -338,6 +362,7 @@ int bwd_saved_impl(const void* q, const void* k, const void* v, const void* g, c
                    float* dh0, int B, int H, int L, int Dk, int Dv, int C, int dtype,
                    const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
                    void* stream, LaunchEvents ev) {
+  C = gla_tile_c(Dk, C, dtype, true);
   int st = check_dims(B, H, L, Dk, Dv, C, dtype);
   if (st != GLA_OK) return st;
   if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return GLA_ERR_UNSUPPORTED;
@@ -428,6 +453,7 @@ size_t gla_fwd_noalloc_max_workspace_bytes(void) { return kNoAllocScratchBytes; 
 int gla_fwd_noalloc(const void* q, const void* k, const void* v, const void* g, const float* h0,
                     void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype,
                     void* stream) {
+  C = gla_tile_c(Dk, C, dtype, false);
   const int st = check_dims(B, H, L, Dk, Dv, C, dtype);
   if (st != GLA_OK) return st;
   if (fwd_ws_bytes(B, H, L, Dk, Dv, C, dtype) > kNoAllocScratchBytes) return GLA_ERR_SCRATCH;
@@ -455,12 +481,14 @@ int gla_bwd_profiled(const void* q, const void* k, const void* v, const void* g,
 }
 
 size_t gla_saved_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  C = gla_tile_c(Dk, C, dtype, true);
   if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
   if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return 0;
   return saved_layout(B, H, L, Dk, Dv, C, dtype).total;
 }
 
 size_t gla_bwd_saved_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  C = gla_tile_c(Dk, C, dtype, true);
   if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
   if (!bwd_config_fits(esize_of(dtype), pad_dk(Dk), pad_c(C))) return 0;
   return bwd_saved_ws_bytes(B, H, L, Dk, Dv, C, dtype);
@@ -485,11 +513,13 @@ int gla_bwd_saved(const void* q, const void* k, const void* v, const void* g, co
 }
 
 int gla_bwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype) {
+  C = gla_tile_c(Dk, C, dtype, true);
   if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
   return bwd_launch_count(esize_of(dtype), pad_dk(Dk), pad_c(C));
 }
 
 int gla_fwd_launch_count(int B, int H, int L, int Dk, int Dv, int C, int dtype, int keep_states) {
+  C = gla_tile_c(Dk, C, dtype, keep_states != 0);
   if (check_dims(B, H, L, Dk, Dv, C, dtype) != GLA_OK) return 0;
   const int es = esize_of(dtype), DKP = pad_dk(Dk), CP = pad_c(C);
   if (keep_states && !bwd_config_fits(es, DKP, CP)) return 0;
@@ -596,6 +626,22 @@ MsglaLayout msgla_layout(int B, int L, int Dk, int Dv, int C, int dtype, int ngr
 }
 
 // ---------------------------------------------------------------- gated slot attention
+// As gla_tile_c, for GSA, whose kernels tile chunks of at most 64 rows: a requested C whose
+// tiles do not fit (C = 128 always; more than 64 slots with C = 64 in the backward) runs at the
+// largest smaller chunk size that fits, with the same results to rounding.
+int gsa_tile_c(int m, int C, int dtype, bool bwd) {
+  if (!valid_c(C) || (dtype != GLA_F32 && dtype != GLA_BF16) || m < 16 || m > 128 || m % 16 != 0) return C;
+  const int es = esize_of(dtype), MP = pad_dk(m);
+  for (int c = C; c >= 16; c /= 2) {
+    if (c > 64) continue;
+    const int CP = pad_c(c);
+    if (!gsa_config_fits(es, MP, CP, bwd) || !fwd_config_fits(es, MP, CP) || (bwd && !bwd_config_fits(es, MP, CP)))
+      continue;
+    return c;
+  }
+  return C;
+}
+
 int check_gsa(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, bool bwd) {
   if (dtype != GLA_F32 && dtype != GLA_BF16) return GLA_ERR_DTYPE;
   if (B < 1 || H < 1 || L < 1 || Dk < 1 || Dv < 1 || m < 1 || C < 1) return GLA_ERR_SHAPE;
@@ -708,21 +754,25 @@ hipError_t dispatch_gsa(bool bwd, int dtype, int MP, int CP, const GsaParams& p,
 extern "C" {
 
 size_t gsa_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype) {
+  C = gsa_tile_c(m, C, dtype, false);
   if (check_gsa(B, H, L, Dk, Dv, m, C, dtype, false) != GLA_OK) return 0;
   return gsa_layout(B, H, L, Dk, Dv, m, C, dtype, false).total;
 }
 
 size_t gsa_bwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype) {
+  C = gsa_tile_c(m, C, dtype, true);
   if (check_gsa(B, H, L, Dk, Dv, m, C, dtype, true) != GLA_OK) return 0;
   return gsa_layout(B, H, L, Dk, Dv, m, C, dtype, true).total;
 }
 
 size_t gsa_saved_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype) {
+  C = gsa_tile_c(m, C, dtype, true);
   if (check_gsa(B, H, L, Dk, Dv, m, C, dtype, true) != GLA_OK) return 0;
   return gsa_layout_of(B, H, L, Dk, Dv, m, C, dtype, kGsaSaved).total;
 }
 
 size_t gsa_bwd_saved_workspace_bytes(int B, int H, int L, int Dk, int Dv, int m, int C, int dtype) {
+  C = gsa_tile_c(m, C, dtype, true);
   if (check_gsa(B, H, L, Dk, Dv, m, C, dtype, true) != GLA_OK) return 0;
   return gsa_layout_of(B, H, L, Dk, Dv, m, C, dtype, kGsaGrad).total;
 }
@@ -736,6 +786,7 @@ namespace {
 int gsa_fwd_impl(const void* q, const void* k, const void* v, const void* g, const float* hk0, const float* hv0,
                  void* o, float* hkt, float* hvt, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype,
                  int act, void* mem, size_t mem_bytes, void* stream, bool saving) {
+  C = gsa_tile_c(m, C, dtype, saving);
   int st = check_gsa(B, H, L, Dk, Dv, m, C, dtype, saving);
   if (st != GLA_OK) return st;
   if (!valid_act(act)) return GLA_ERR_UNSUPPORTED;
@@ -763,6 +814,7 @@ int gsa_bwd_impl(const void* q, const void* k, const void* v, const void* g, con
                  const void* do_, const float* dhkt, const float* dhvt, void* dq, void* dk, void* dv, float* dg,
                  float* dhk0, float* dhv0, int B, int H, int L, int Dk, int Dv, int m, int C, int dtype, int act,
                  const void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream) {
+  C = gsa_tile_c(m, C, dtype, true);
   int st = check_gsa(B, H, L, Dk, Dv, m, C, dtype, true);
   if (st != GLA_OK) return st;
   if (!valid_act(act)) return GLA_ERR_UNSUPPORTED;
@@ -834,6 +886,7 @@ int gsa_bwd_saved(const void* q, const void* k, const void* v, const void* g, co
 
 size_t msgla_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int dtype, int ngroups,
                                  const int* scales, const int* heads) {
+  C = gla_tile_c(Dk, C, dtype, false);
   if (check_msgla(B, H, L, Dk, Dv, C, dtype, ngroups, scales, heads) != GLA_OK) return 0;
   return msgla_layout(B, L, Dk, Dv, C, dtype, ngroups, scales, heads).total;
 }
@@ -841,6 +894,7 @@ size_t msgla_fwd_workspace_bytes(int B, int H, int L, int Dk, int Dv, int C, int
 int msgla_fwd(const void* q, const void* k, const void* v, const void* g, const float* h0, const float* w,
               void* o, float* ht, int B, int H, int L, int Dk, int Dv, int C, int dtype, int ngroups,
               const int* scales, const int* heads, void* workspace, size_t workspace_bytes, void* stream) {
+  C = gla_tile_c(Dk, C, dtype, false);
   int st = check_msgla(B, H, L, Dk, Dv, C, dtype, ngroups, scales, heads);
   if (st != GLA_OK) return st;
   if (!q || !k || !v || !g || !o) return GLA_ERR_NULL_ARG;

@@ -60,10 +60,14 @@ def test_dtype_shape_unsupported(lib):
     assert fwd(lib, Dk=24) == 4
     assert fwd(lib, Dk=512) == 4
     assert fwd(lib, Dv=520) == 4
-    assert fwd(lib, Dk=256, C=128) == 4               # LDS limit (bf16)
-    assert fwd(lib, Dk=128, C=128, dt=0) == 4         # LDS limit (fp32)
+    # chunk sizes whose tiles exceed a CU's LDS run at a smaller chunk (the result does not
+    # depend on C): accepted, so these calls get as far as their NULL pointers
+    assert fwd(lib, Dk=256, C=128) == 1               # bf16: runs at C = 64
+    assert fwd(lib, Dk=128, C=128, dt=0) == 1         # fp32: runs at C = 64
     assert lib.gla_fwd_workspace_bytes(1, 1, 64, 64, 16, 128, 0) > 0        # fp32 forward fits
-    assert lib.gla_bwd_workspace_bytes(1, 1, 64, 64, 16, 128, 0) == 0       # its backward does not
+    assert lib.gla_bwd_workspace_bytes(1, 1, 64, 64, 16, 128, 0) == lib.gla_bwd_workspace_bytes(1, 1, 64, 64, 16, 64, 0)
+    assert lib.gla_saved_bytes(1, 1, 300, 256, 64, 128, 1) == lib.gla_saved_bytes(1, 1, 300, 256, 64, 64, 1) > 0
+    assert lib.gla_fwd_workspace_bytes(1, 1, 300, 256, 64, 128, 1) == lib.gla_fwd_workspace_bytes(1, 1, 300, 256, 64, 64, 1)
     assert fwd(lib, B=70000) == 4                     # grid limit
 
 
@@ -127,7 +131,7 @@ def test_saved_path_sizes_and_validation(lib):
     assert lib.gla_saved_bytes(B, H, L, Dk, Dv, C, 1) == ops + states
     assert lib.gla_bwd_saved_workspace_bytes(B, H, L, Dk, Dv, C, 1) == states
     assert lib.gla_saved_bytes(1, 1, 64, 16, 16, 48, 1) == 0          # unsupported C
-    assert lib.gla_saved_bytes(1, 1, 64, 256, 64, 128, 1) == 0        # LDS limit
+    assert lib.gla_saved_bytes(1, 1, 64, 256, 64, 128, 1) > 0         # runs at C = 64
     q, k, v, g, o = (ctypes.c_void_p(0x10000000 + i * 0x1000000) for i in range(5))
     need = lib.gla_saved_bytes(1, 1, 64, 16, 16, 16, 1)
     assert lib.gla_fwd_save(q, k, v, g, None, o, None, 1, 1, 64, 16, 16, 16, 1, None, 0, None, None, 0) == 5
@@ -158,6 +162,11 @@ def test_gsa_saved_path_sizes_and_validation(lib):
     assert sv > lib.gsa_fwd_workspace_bytes(B, H, L, Dk, Dv, m, C, 1) > 0
     assert sv + gw == lib.gsa_bwd_workspace_bytes(B, H, L, Dk, Dv, m, C, 1)
     assert lib.gsa_saved_bytes(1, 1, 64, 16, 16, 16, 48, 1) == 0       # unsupported C
+    # chunk sizes beyond the GSA tiles run at a smaller chunk: C = 128 at 64, and the backward
+    # with more than 64 slots at 32
+    assert lib.gsa_fwd_workspace_bytes(B, H, L, Dk, Dv, m, 128, 1) == lib.gsa_fwd_workspace_bytes(B, H, L, Dk, Dv, m, 64, 1)
+    assert lib.gsa_saved_bytes(B, H, L, Dk, Dv, 128, 64, 1) == lib.gsa_saved_bytes(B, H, L, Dk, Dv, 128, 32, 1) > 0
+    assert lib.gsa_saved_bytes(B, H, L, Dk, Dv, 128, 128, 0) == 0        # fp32, 128 slots: no backward
     q, k, v, g, o = (ctypes.c_void_p(0x10000000 + i * 0x1000000) for i in range(5))
     need = lib.gsa_saved_bytes(1, 1, 64, 16, 16, 16, 16, 1)
     base = [q, k, v, g, None, None, o, None, None, 1, 1, 64, 16, 16, 16, 16, 1, 0]

@@ -63,6 +63,10 @@ SHAPES = [
     (2, 2, 90, 48, 32, 16, "f32", True, True),
     (1, 2, 70, 128, 96, 64, "f32", True, True),
     (1, 1, 140, 64, 64, 64, "f32", False, True),
+    # chunk sizes whose tiles exceed a CU's LDS: the call runs at a smaller chunk (same result)
+    (1, 2, 300, 256, 64, 128, "bf16", True, True),    # at C = 64
+    (1, 2, 200, 64, 48, 128, "f32", True, True),      # the fp32 backward at C = 64
+    (1, 1, 150, 256, 32, 64, "f32", True, True),      # fp32 with 256-channel keys at C = 32
 ]
 
 

@@ -98,12 +98,30 @@ def test_wide_slot_counts(gla, shape):
     check_gsa(gla, w, W.gsa_inputs(w), with_state=h0, with_dstate=dht)
 
 
-@pytest.mark.parametrize("shape", [(1, 2, 150, 64, 64, 128, 64, "bf16"), (1, 2, 100, 64, 96, 128, 64, "f32"),
-                                   (1, 1, 90, 48, 64, 64, 64, "f32")], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("shape", [
+    # (B, H, L, Dk, Dv, m, C, dtype, h0, dht)
+    (1, 2, 150, 64, 64, 128, 64, "bf16", True, True),   # backward at C = 32
+    (1, 1, 90, 48, 64, 64, 64, "f32", True, True),      # fp32 backward at C = 32
+    (1, 2, 150, 64, 64, 64, 128, "bf16", True, True),   # C = 128: forward and backward at 64
+    (1, 2, 130, 64, 96, 128, 128, "bf16", False, True),  # C = 128 with 128 slots: 64, and 32 backward
+], ids=lambda s: "x".join(map(str, s)))
+def test_chunk_sizes_beyond_the_tiles(gla, shape):
+    """A chunk size whose GSA tiles exceed a CU's LDS runs at the largest smaller one whose
+    tiles fit (the result does not depend on the chunk size): forward and backward, through
+    both entry-point pairs, match the oracle."""
+    B, H, L, Dk, Dv, m, C, dt, h0, dht = shape
+    w = W.GsaWorkload("tile-c", B, H, L, Dk, Dv, m, C, dt, 740 + L + m, h0=True)
+    x = W.gsa_inputs(w)
+    check_gsa(gla, w, x, with_state=h0, with_dstate=dht)
+    check_gsa(gla, w, x, with_state=h0, with_dstate=dht, saved=True)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 100, 64, 96, 128, 64, "f32"), (1, 2, 100, 64, 96, 128, 128, "f32")],
+                         ids=lambda s: "x".join(map(str, s)))
 def test_forward_only_shapes(gla, shape):
-    """Shapes whose forward fits but whose pass-1 backward does not (more than 64 slots at
-    C = 64; fp32 with 64 slots at C = 64): the forward matches the oracle, and the backward and
-    the saving forward are refused before anything runs."""
+    """fp32 with more than 64 slots: no chunk size holds the pass-1 backward's tiles.  The
+    forward matches the oracle, and the backward and the saving forward are refused before
+    anything runs."""
     import torch
     B, H, L, Dk, Dv, m, C, dt = shape
     w = W.GsaWorkload("fwd-only", B, H, L, Dk, Dv, m, C, dt, 720 + L + m, h0=True)
