@@ -100,6 +100,16 @@ def test_mixed_safe_and_fast_chunks(gla):
     check_bwd(gla, w, x)
 
 
+def test_mixed_safe_and_fast_chunks_wide_keys(gla):
+    """256-channel keys (512-thread preparation, split key width in the chunk kernel, separate
+    dv kernel) with chunks on both intra-chunk paths."""
+    w = W.GlaWorkload("mixed-wide", 1, 2, 256, 256, 64, 64, "bf16", 13, h0=True)
+    x = W.gla_inputs(w)
+    x["g"][:, :, 64:128] = -2.0
+    x["g"][:, 1, 200:210, :7] = -40.0
+    check_bwd(gla, w, x)
+
+
 @pytest.mark.parametrize("name,units,dht", [
     ("gla_340m", (np.array([0, 7]), np.array([1, 2])), False),
     ("gla_340m", (np.array([3]), np.array([0])), True),

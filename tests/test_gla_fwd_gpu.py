@@ -164,6 +164,17 @@ def test_mixed_safe_and_fast_chunks(gla):
     check_fwd(gla, w, x)
 
 
+@pytest.mark.parametrize("C", [32, 64])
+def test_mixed_safe_and_fast_chunks_wide_keys(gla, C):
+    """As above with 256-channel keys, whose preparation kernel runs 512 threads (persistent at
+    C = 64, one chunk per workgroup at C = 32), on both intra-chunk paths."""
+    w = W.GlaWorkload("mixed-wide", 1, 2, 256, 256, 64, C, "bf16", 12, h0=True)
+    x = W.gla_inputs(w, with_grad=False)
+    x["g"][:, :, 64:128] = -2.0
+    x["g"][:, 1, 200:210, :7] = -40.0
+    check_fwd(gla, w, x)
+
+
 def test_large_negative_gate_is_finite(gla):
     w = W.GlaWorkload("neg", 1, 1, 100, 32, 32, 32, "bf16", 11, h0=True)
     x = W.gla_inputs(w, with_grad=False)
