@@ -12,16 +12,16 @@
 // Per chunk n, in order within one step:
 //   T_n   = Kd_n^T V_n                 (from LDS: the chunk's staged KdT and V tiles)
 //   O_n   = Qs_n H_n + A_n V_n         (H_n, and the chunk's staged Qs and A tiles, from LDS;
-//                                       O_n leaves through LDS in 16-byte pieces)
+//                                       O_n leaves through LDS, 8 bytes per thread)
 //   H_n+1 = Diag(2^Gamma_n) H_n + T_n  (fp32 accumulators; its bf16 copy goes to LDS for the
 //                                       next chunk's O and, if kept, to memory)
 // O_n needs every key row of H_n, which four waves write, so the bf16 copy of H_n is written
 // one step earlier (after the fold that produces it), and the staged tiles, the copy and the
 // output tile are double-buffered: one barrier per chunk.  Every tile moves between memory and
-// LDS in whole 16-byte vectors of consecutive threads: Qs and A row fragments read by each
-// lane straight from memory (as the unfused output kernel does) cost about 40 us at the 340M
-// shape here, where each step waits for them, and so did 8-byte output stores from the
-// accumulators.
+// LDS in whole runs of consecutive threads.  A first form read each lane's Qs and A row
+// fragments straight from memory (as the unfused output kernel does) and stored the outputs
+// from the accumulators, four elements of one row per lane: 84 us at the 340M shape against
+// 58 us as built, since every step waits for those loads.
 //
 // Layout: 8 waves; wave w owns state columns 16 (w % 2) .. +15 and rows DKP/4 (w / 2) .. +
 // DKP/4 - 1, and the 16 x 16 output block (rows 16 (w / 2), columns 16 (w % 2)).  The
